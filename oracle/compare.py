@@ -1,0 +1,105 @@
+"""Tolerance rule for judging GPU outputs against the float64 oracle.
+
+Test infrastructure only.  The headline bound is max-abs 1e-5 for fp32
+storage and 2e-2 for fp16/bf16 storage.  Two outputs cannot meet a bare
+max-abs bound at every magnitude, and take a wider clause derived from the
+arithmetic; every use of the wider clause is counted in the report:
+
+* elementwise outputs stored in T (y, z, dx): the value must be stored in T,
+  so half a storage step of T is unavoidable.  Pass iff
+  |o - r| <= max(atol_T, 0.5 * ulp_T(r) * (1 + 2^-8)); the (1 + 2^-8) covers
+  the fp32 error of the value before it is rounded.  Half a step exceeds atol
+  only for bf16 |r| >= 8, fp16 |r| >= 32 and fp32 |r| >= 256.
+* column sums (dgamma, dbeta, float32): pass iff |o - r| <= atol_T or
+  |o - r| <= 0.5 * ulp_f32(r) + ceil(log2 rows) * 2^-24 * S_j, with
+  S_j = sum_r |term_rj|: the rounding of a float32 result plus the error
+  bound of a balanced summation tree over `rows` terms ("GPU Performance
+  from First Principles", §7.4: a tree sum rounds each term log2(n) times).
+* mean / rstd (float32): pass iff |o - r| <= 1e-5 * max(1, |r|).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F32, F16, BF16 = 0, 1, 2
+ATOL = {F32: 1e-5, F16: 2e-2, BF16: 2e-2}
+_BITS = {F32: (24, -126), F16: (11, -14), BF16: (8, -126)}
+
+
+def ulp(r, fmt) -> np.ndarray:
+    """Spacing of the storage format at each |r| (subnormal spacing below)."""
+    p, emin = _BITS[fmt]
+    a = np.abs(np.asarray(r, dtype=np.float64))
+    _, k = np.frexp(a)
+    e = np.maximum(k.astype(np.int64) - 1, emin)
+    e = np.where(a == 0, emin, e)
+    return np.ldexp(1.0, (e - (p - 1)).astype(np.int64))
+
+
+@dataclass
+class Report:
+    name: str
+    ok: bool
+    max_abs: float
+    worst_index: tuple
+    n: int
+    n_wide: int = 0          # elements that needed the wider clause
+    n_fail: int = 0
+    details: list = field(default_factory=list)
+
+    def __str__(self):
+        return (f"{self.name}: ok={self.ok} max_abs={self.max_abs:.3e} "
+                f"n={self.n} wide={self.n_wide} fail={self.n_fail} "
+                f"worst={self.worst_index}")
+
+
+def _finish(name, out, ref, err, tol, atol):
+    both_nan = np.isnan(out) & np.isnan(ref)
+    err = np.where(both_nan, 0.0, err)
+    bad = ~(err <= tol)
+    n_wide = int(np.count_nonzero((err > atol) & ~bad))
+    if err.size:
+        idx = np.unravel_index(int(np.nanargmax(np.where(np.isnan(err), np.inf, err))),
+                               err.shape)
+        mx = float(err[idx])
+    else:
+        idx, mx = (), 0.0
+    details = []
+    if bad.any():
+        for i in np.argwhere(bad)[:8]:
+            t = tuple(int(v) for v in i)
+            details.append((t, float(out[t]), float(ref[t]), float(tol[t])))
+    return Report(name, not bad.any(), mx, tuple(int(v) for v in idx), int(err.size),
+                  n_wide, int(np.count_nonzero(bad)), details)
+
+
+def check_elementwise(name, out, ref, fmt) -> Report:
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    atol = ATOL[fmt]
+    tol = np.maximum(atol, 0.5 * ulp(ref, fmt) * (1.0 + 2.0 ** -8))
+    err = np.abs(out - ref)
+    return _finish(name, out, ref, err, tol, atol)
+
+
+def check_colsum(name, out, ref, abs_sum, rows: int, fmt) -> Report:
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    s = np.asarray(abs_sum, dtype=np.float64)
+    atol = ATOL[fmt]
+    depth = math.ceil(math.log2(max(rows, 2)))
+    tol = np.maximum(atol, 0.5 * ulp(ref, F32) + depth * 2.0 ** -24 * s)
+    err = np.abs(out - ref)
+    return _finish(name, out, ref, err, tol, atol)
+
+
+def check_stats(name, out, ref) -> Report:
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    tol = 1e-5 * np.maximum(1.0, np.abs(ref))
+    err = np.abs(out - ref)
+    return _finish(name, out, ref, err, tol, 1e-5)
