@@ -249,6 +249,28 @@ void orc_ln_bwd_dx_hw4(const double* dy, const double* x, const double* gamma,
     }
 }
 
+void orc_ln_bwd_dx_scale(const double* dy, const double* x, const double* gamma,
+                         const double* mean, const double* rstd,
+                         int64_t rows, int64_t m, double* scale) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* dyr = dy + r * m;
+        const double* xr = x + r * m;
+        double mu = mean[r], rs = rstd[r];
+        double abs_g = 0.0, abs_gxhat = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            double g = gamma[j] * dyr[j];
+            double xhat = (xr[j] - mu) * rs;
+            abs_g += fabs(g);
+            abs_gxhat += fabs(g * xhat);
+        }
+        for (int64_t j = 0; j < m; ++j) {
+            double g = gamma[j] * dyr[j];
+            double xhat = (xr[j] - mu) * rs;
+            scale[r * m + j] = rs * (fabs(g) + (abs_g + fabs(xhat) * abs_gxhat) / (double)m);
+        }
+    }
+}
+
 void orc_ln_bwd_dx_slides(const double* dy, const double* x,
                           const double* gamma, const double* mean,
                           const double* rstd, int64_t rows, int64_t m,

@@ -102,6 +102,15 @@ void orc_ln_bwd_dx_hw4(const double* dy, const double* x, const double* gamma,
                        const double* mean, const double* rstd,
                        int64_t rows, int64_t m, double* dx);
 
+/* Magnitude of the terms that form each dx_j in the x-hat form:
+ * scale_j = r * (|g_j| + (sum_k |g_k| + |xhat_j| * sum_k |g_k xhat_k|) / m).
+ * A float32 evaluation of dx_j rounds quantities of at most this size, so its
+ * error is bounded by a small multiple of 2^-24 * scale_j (used by the
+ * tolerance rule, not by the result). */
+void orc_ln_bwd_dx_scale(const double* dy, const double* x, const double* gamma,
+                         const double* mean, const double* rstd,
+                         int64_t rows, int64_t m, double* scale);
+
 /* LayerNorm backward dx, the slides form ([L11] §2.1):
  * dx = g/sigma + alpha*sum g + beta*sum g*x with
  * alpha = ((x - mu)*mu - sigma^2)/(m sigma^3), beta = (mu - x)/(m sigma^3),

@@ -59,7 +59,7 @@ def _load():
     lib.orc_dropout_keep.argtypes = [ctypes.c_uint64, ctypes.c_float, i64, i64, u8p]
     lib.orc_bias_dropout_residual.argtypes = [dp, dp, dp, u8p, ctypes.c_float,
                                               i64, i64, dp]
-    for name in ("orc_ln_bwd_dx_hw4", "orc_ln_bwd_dx_slides"):
+    for name in ("orc_ln_bwd_dx_hw4", "orc_ln_bwd_dx_slides", "orc_ln_bwd_dx_scale"):
         getattr(lib, name).argtypes = [dp, dp, dp, dp, dp, i64, i64, dp]
     lib.orc_ln_bwd_params.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, dp, dp]
     _lib = lib
@@ -182,6 +182,17 @@ def ln_bwd_dx(dy, x, gamma, mean, rstd, form: str = "hw4") -> np.ndarray:
     return dx
 
 
+def ln_bwd_dx_scale(dy, x, gamma, mean, rstd) -> np.ndarray:
+    """Per-element magnitude of the terms of dx (for the float32 error bound)."""
+    dy, x = _d(dy), _d(x)
+    rows, m = _shape2(x)
+    g, mu, rs = _d(gamma), _d(mean), _d(rstd)
+    out = np.empty_like(x)
+    _load().orc_ln_bwd_dx_scale(_ptr(dy), _ptr(x), _ptr(g), _ptr(mu), _ptr(rs), rows, m,
+                                _ptr(out))
+    return out
+
+
 def ln_bwd_params(dy, x, mean, rstd):
     """-> (dgamma, dbeta, sum|dy*xhat|, sum|dy|) column sums in float64."""
     dy, x = _d(dy), _d(x)
@@ -196,4 +207,4 @@ def ln_bwd_params(dy, x, mean, rstd):
 __all__ = ["F32", "F16", "BF16", "build", "round_to", "round_scalar", "ln_fwd",
            "row_stats_welford", "var_naive_f32", "var_chan_f32", "philox4x32_10",
            "dropout_threshold", "dropout_keep", "bias_dropout_residual",
-           "ln_bwd_dx", "ln_bwd_params"]
+           "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params"]

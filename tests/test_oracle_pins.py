@@ -390,3 +390,15 @@ def test_fused_prologue_definition(orc):
     # p = 0 keeps everything: z = residual + x + bias
     z0 = orc.bias_dropout_residual(x, bias, res, np.ones_like(keep), 0.0)
     assert np.array_equal(z0, res + (x + bias))
+
+
+def test_dx_term_scale_bounds_dx(orc):
+    # |dx_j| = r |g_j - (A + xhat_j B)/m| <= r (|g_j| + (sum|g| + |xhat_j| sum|g xhat|)/m)
+    rng = np.random.default_rng(12)
+    x, dy = _rows(rng, 20, 50, mean=2.0), _rows(rng, 20, 50)
+    gamma = rng.uniform(0.5, 1.5, 50)
+    _, mean, rstd = orc.ln_fwd(x, gamma, np.zeros(50), 1e-5)
+    dx = orc.ln_bwd_dx(dy, x, gamma, mean, rstd)
+    scale = orc.ln_bwd_dx_scale(dy, x, gamma, mean, rstd)
+    assert np.all(np.abs(dx) <= scale * (1 + 1e-12))
+    assert np.all(scale <= 10 * rstd[:, None] * (np.abs(gamma * dy) + 10))
