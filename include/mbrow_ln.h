@@ -1,0 +1,180 @@
+/*
+ * mbrow_ln.h -- C ABI of the fused LayerNorm library for AMD MI355X (gfx950).
+ *
+ * Sources ("the pages"):
+ *   [L10]  "Accelerating Transformer on GPU (I): Kernel Fusion and LightSeq
+ *          Inference" (CMU 11-868 lecture-10 notes)
+ *   [L11]  "Accelerating Transformer on GPU (II): Training with LightSeq2"
+ *          (CMU 11-868 lecture-11 notes)
+ *   [BLOG] "AI infra 学习记录(2): 从 LayerNorm 算子熟悉常见的算子优化方法"
+ *   [LLMC] "02 · llmc/ 的 CUDA kernel 层" (llm.c CUDA kernel walk-through)
+ *
+ * Common conventions for every entry point
+ * ----------------------------------------
+ * Layout.  Every tensor of shape [rows, cols] is row-major and contiguous
+ *   (row r starts at element r*cols).  gamma, beta and bias are [cols].
+ *   mean, rstd are [rows] float32; dgamma, dbeta are [cols] float32.
+ *   Storage type T of the [rows, cols] tensors and of gamma/beta/bias is
+ *   given by `dt`; all arithmetic is float32 (the pages compute norms in
+ *   FP32 and store FP16/BF16, [L10] §4.2).  Results are rounded to T with
+ *   round-to-nearest-even.
+ * Pointers.  All data pointers are DEVICE pointers (hipMalloc'd or equivalent)
+ *   owned by the caller.  The library never allocates, frees or retains a
+ *   pointer after the call returns.  No alignment is required: 16-byte
+ *   aligned bases with cols*sizeof(T) a multiple of 16 take the vector path,
+ *   anything else a per-element path with identical results.
+ * Aliasing.  Only the exact in-place forms y == x (ln_fwd) and dx == dy
+ *   (ln_bwd_dx) are allowed; any other overlap of an output with an input
+ *   or another output is undefined.
+ * Streams.  All work is enqueued on `stream` (NULL = the null stream).  No
+ *   call synchronises, allocates, memsets or copies, so every call may be
+ *   captured into a HIP graph.  Outputs are valid once the stream has
+ *   reached the enqueued work.
+ * Errors.  Every call returns an ln_status_t.  All arguments are checked on
+ *   the host before anything is enqueued, so a call that returns an error
+ *   other than LN_ERR_HIP has written nothing.  rows == 0 is a no-op that
+ *   returns LN_OK.  Launch failures are reported as LN_ERR_HIP.  No call
+ *   prints, exits or throws.
+ * Determinism.  Every output is bitwise reproducible from run to run on the
+ *   same device for the same inputs and shape; dgamma/dbeta use a fixed
+ *   partition of rows (a pure function of rows and cols) and a fixed-order
+ *   fold, never floating-point atomics ([L11] §2.4 and [L10] §5.1 note that
+ *   atomic accumulation order varies from run to run).
+ */
+#ifndef MBROW_LN_H
+#define MBROW_LN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LN_F32 = 0, LN_F16 = 1, LN_BF16 = 2 } ln_dtype_t;
+
+typedef enum {
+    LN_OK = 0,
+    LN_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    LN_ERR_SHAPE = 2,       /* rows < 0 or cols <= 0                           */
+    LN_ERR_DTYPE = 3,       /* unknown ln_dtype_t                              */
+    LN_ERR_PARAM = 4,       /* eps < 0 or NaN; p outside [0, 1) or NaN         */
+    LN_ERR_WORKSPACE = 5,   /* workspace smaller than ln_bwd_workspace_bytes   */
+    LN_ERR_UNSUPPORTED = 6, /* cols above LN_MAX_COLS for this dtype, or an
+                               aliasing form the call does not allow          */
+    LN_ERR_HIP = 7          /* a HIP launch or query failed                    */
+} ln_status_t;
+
+/* Widest row each storage type supports (the whole row is held on chip). */
+#define LN_MAX_COLS_F32 32768
+#define LN_MAX_COLS_16BIT 65536
+
+/*
+ * LayerNorm forward.  For each row r with m = cols:
+ *   mu = (1/m) sum_j x_j,  var = (1/m) sum_j (x_j - mu)^2,
+ *   rstd = 1/sqrt(var + eps),  y_j = gamma_j * (x_j - mu) * rstd + beta_j.
+ * [L11] §2.1 (xhat, sigma = sqrt(var + eps), save mu and r = 1/sigma);
+ * [L10] §4.2 (population variance, one reduction); [BLOG] §2.1 gives the
+ * same argument list (input, output, gamma, beta, rows, cols, eps).
+ *   x     [rows, cols] T, input.
+ *   gamma [cols] T, beta [cols] T.
+ *   y     [rows, cols] T, output; may equal x.
+ *   mean, rstd  [rows] float32 outputs, each may be NULL (inference keeps
+ *         no intermediates, [L10] §6.3).
+ *   eps   >= 0, added to the variance inside the square root.
+ */
+ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta,
+                   void* y, float* mean, float* rstd,
+                   int64_t rows, int64_t cols, float eps, ln_dtype_t dt,
+                   hipStream_t stream);
+
+/*
+ * Fused bias + dropout + residual + LayerNorm forward ([L10] §2.3: add the
+ * bias, apply dropout, add the residual, in one kernel; [LLMC] §3.2: the
+ * residual sum is written out and normalised in the same kernel).
+ *   t = x + bias;  keep = mask(seed, r, j, p);
+ *   z = residual + (keep ? t / (1 - p) : 0)     (inverted dropout);
+ *   residual_out = round_T(z);  then LayerNorm of the stored residual_out,
+ *   exactly as ln_fwd(residual_out) would compute it.
+ * The mask is a pure function of (seed, row, column, p), so a backward pass
+ * regenerates it from the seed instead of storing it ([L11] §3.3):
+ *   key = (seed & 0xffffffff, seed >> 32), counter = (col >> 3,
+ *   row & 0xffffffff, row >> 32, 0), w = Philox4x32-10(counter, key)
+ *   (Salmon et al., SC'11); u = 16-bit half (col & 1) of word (col & 7) >> 1;
+ *   keep iff u >= floor(p * 65536 + 0.5) evaluated in double from float p.
+ *   x, residual  [rows, cols] T inputs;  bias, gamma, beta [cols] T.
+ *   residual_out [rows, cols] T output (z).   y [rows, cols] T output.
+ *   mean, rstd   [rows] float32 outputs of the LayerNorm of z, nullable.
+ *   mask_out     [rows, cols] uint8 output (1 = kept), nullable; debugging
+ *                and tests only, the mask never needs to be stored.
+ *   p in [0, 1): dropout probability; seed: 64-bit mask seed.
+ */
+ln_status_t bias_dropout_residual_ln_fwd(
+    const void* x, const void* bias, const void* residual,
+    const void* gamma, const void* beta, void* residual_out, void* y,
+    float* mean, float* rstd, uint8_t* mask_out,
+    int64_t rows, int64_t cols, float eps, float p, uint64_t seed,
+    ln_dtype_t dt, hipStream_t stream);
+
+/*
+ * Bytes of float32 workspace the backward needs for the per-partition
+ * column partials of dgamma and dbeta: P * 2 * cols * 4, where the number of
+ * row partitions P depends only on (rows, cols).  Returns 0 for rows <= 0 or
+ * cols <= 0.  ([L11] §2.4: split the rows into P ranges, one partial sum per
+ * range, then a second small kernel adds the P partials.)
+ */
+size_t ln_bwd_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * LayerNorm backward, input gradient, with both row sums in one reduction
+ * ([L11] §2.1 "HW4" form, §2.2 one synchronisation):
+ *   g_j = gamma_j * dy_j,  xhat_j = (x_j - mean) * rstd,
+ *   A = sum_j g_j,  B = sum_j g_j * xhat_j,
+ *   dx_j = rstd * (g_j - (A + xhat_j * B) / cols).
+ *   dy, x [rows, cols] T inputs;  gamma [cols] T;
+ *   mean, rstd [rows] float32 as saved by the forward;
+ *   dx [rows, cols] T output; may equal dy.
+ *   workspace  float32 device buffer or NULL.  When non-NULL the same pass
+ *              also writes the stage-1 column partials of dgamma/dbeta
+ *              (dgamma = sum_rows dy * xhat, dbeta = sum_rows dy, [L11]
+ *              §2.1/§2.4) into it; finish them with
+ *              ln_bwd_dgamma_dbeta(..., partials_ready = 1, ...).
+ *   workspace_bytes  its size; must be >= ln_bwd_workspace_bytes(rows, cols)
+ *              when workspace is non-NULL.
+ */
+ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma,
+                      const float* mean, const float* rstd, void* dx,
+                      float* workspace, size_t workspace_bytes,
+                      int64_t rows, int64_t cols, ln_dtype_t dt,
+                      hipStream_t stream);
+
+/*
+ * LayerNorm backward, parameter gradients (column sums over rows, [L11]
+ * §2.1 and §2.4): dgamma_j = sum_r dy_rj * xhat_rj, dbeta_j = sum_r dy_rj,
+ * as float32, by a deterministic two-stage reduction: P per-partition
+ * partials, then a fixed-order fold.
+ *   partials_ready = 1: the workspace already holds the partials written by
+ *     ln_bwd_dx for the same (rows, cols); only the fold runs, and dy, x,
+ *     mean, rstd may be NULL.
+ *   partials_ready = 0: stage 1 runs here first (reads dy, x, mean, rstd);
+ *     the result is bitwise identical to the ln_bwd_dx path.
+ *   dgamma, dbeta [cols] float32 outputs.
+ *   workspace / workspace_bytes as for ln_bwd_dx (required here).
+ */
+ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x,
+                                const float* mean, const float* rstd,
+                                float* dgamma, float* dbeta,
+                                float* workspace, size_t workspace_bytes,
+                                int partials_ready, int64_t rows,
+                                int64_t cols, ln_dtype_t dt,
+                                hipStream_t stream);
+
+/* Static English description of a status code (never NULL). */
+const char* ln_status_string(ln_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,1 +1,217 @@
-"""Fused LayerNorm forward/backward for AMD MI355X (gfx950)."""
+"""Fused LayerNorm forward/backward for AMD MI355X (gfx950).
+
+A thin binding over the C ABI of ``libmbrow_ln.so`` (declared in
+``include/mbrow_ln.h``): it checks tensor placement and layout, allocates
+outputs with torch when the caller passes none, and hands raw device pointers
+and the current HIP stream to the library.  Every step of the computation
+runs in the library's HIP kernels; there is no fallback.  Calling any op
+without the built library raises ``RuntimeError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmbrow_ln.so")
+
+LN_F32, LN_F16, LN_BF16 = 0, 1, 2
+_DTYPES = {torch.float32: LN_F32, torch.float16: LN_F16, torch.bfloat16: LN_BF16}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(the HIP library is required; there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    L.ln_status_string.restype = ctypes.c_char_p
+    L.ln_status_string.argtypes = [i32]
+    L.ln_fwd.restype = i32
+    L.ln_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    L.bias_dropout_residual_ln_fwd.restype = i32
+    L.bias_dropout_residual_ln_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               i64, i64, f32, f32, ctypes.c_uint64, i32, vp]
+    L.ln_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.ln_bwd_workspace_bytes.argtypes = [i64, i64]
+    L.ln_bwd_dx.restype = i32
+    L.ln_bwd_dx.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, vp]
+    L.ln_bwd_dgamma_dbeta.restype = i32
+    L.ln_bwd_dgamma_dbeta.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i32,
+                                      i64, i64, i32, vp]
+    L.ln_debug_force_path.restype = i32
+    L.ln_debug_force_path.argtypes = [i32, i32, i32]
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return lib().ln_status_string(int(code)).decode()
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise RuntimeError(status_string(code))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _mat(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() < 1:
+        raise ValueError(f"{name} must have a last (row) dimension")
+    cols = t.shape[-1]
+    rows = t.numel() // cols if cols else 0
+    return rows, cols
+
+
+def _vec(t: torch.Tensor, cols: int, dtype, name: str):
+    if not t.is_cuda or not t.is_contiguous() or t.numel() != cols or t.dtype != dtype:
+        raise ValueError(f"{name} must be a contiguous GPU tensor of {cols} {dtype} values")
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if (not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape)
+            or t.dtype != dtype):
+        raise ValueError(f"{name} must be a contiguous GPU tensor {tuple(shape)} {dtype}")
+    return t
+
+
+def ln_fwd(x, gamma, beta, eps: float = 1e-5, *, y=None, mean=None, rstd=None,
+           stats: bool = True):
+    """LayerNorm over the last dimension -> (y, mean, rstd) (stats None if not kept)."""
+    rows, cols = _mat(x, "x")
+    _vec(gamma, cols, x.dtype, "gamma")
+    _vec(beta, cols, x.dtype, "beta")
+    y = _out(y, x.shape, x.dtype, x.device, "y")
+    if stats:
+        mean = _out(mean, (rows,), torch.float32, x.device, "mean")
+        rstd = _out(rstd, (rows,), torch.float32, x.device, "rstd")
+    if rows == 0:
+        return y, mean, rstd
+    _check(lib().ln_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd),
+                        rows, cols, float(eps), _dt(x), _stream(x)))
+    return y, mean, rstd
+
+
+def bias_dropout_residual_ln_fwd(x, bias, residual, gamma, beta, p: float, seed: int,
+                                 eps: float = 1e-5, *, residual_out=None, y=None, mean=None,
+                                 rstd=None, mask_out=None, stats: bool = True,
+                                 want_mask: bool = False):
+    """z = residual + dropout(x + bias); y = LayerNorm(z) -> (z, y, mean, rstd, mask)."""
+    rows, cols = _mat(x, "x")
+    if residual.shape != x.shape or residual.dtype != x.dtype:
+        raise ValueError("residual must match x")
+    _mat(residual, "residual")
+    for t, n in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        _vec(t, cols, x.dtype, n)
+    residual_out = _out(residual_out, x.shape, x.dtype, x.device, "residual_out")
+    y = _out(y, x.shape, x.dtype, x.device, "y")
+    if stats:
+        mean = _out(mean, (rows,), torch.float32, x.device, "mean")
+        rstd = _out(rstd, (rows,), torch.float32, x.device, "rstd")
+    if want_mask or mask_out is not None:
+        mask_out = _out(mask_out, x.shape, torch.uint8, x.device, "mask_out")
+    if rows == 0:
+        return residual_out, y, mean, rstd, mask_out
+    _check(lib().bias_dropout_residual_ln_fwd(
+        _ptr(x), _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(residual_out),
+        _ptr(y), _ptr(mean), _ptr(rstd), _ptr(mask_out), rows, cols, float(eps), float(p),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, _dt(x), _stream(x)))
+    return residual_out, y, mean, rstd, mask_out
+
+
+def ln_bwd_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().ln_bwd_workspace_bytes(int(rows), int(cols)))
+
+
+def workspace(rows: int, cols: int, device) -> torch.Tensor:
+    """A float32 workspace of the size the backward needs."""
+    n = ln_bwd_workspace_bytes(rows, cols) // 4
+    return torch.empty(max(n, 1), dtype=torch.float32, device=device)
+
+
+def ln_bwd_dx(dy, x, gamma, mean, rstd, *, dx=None, workspace=None):
+    """dx of LayerNorm; with `workspace` also writes the dgamma/dbeta partials."""
+    rows, cols = _mat(x, "x")
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x")
+    _mat(dy, "dy")
+    _vec(gamma, cols, x.dtype, "gamma")
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        _vec(t, rows, torch.float32, n)
+    dx = _out(dx, x.shape, x.dtype, x.device, "dx")
+    ws_bytes = 0
+    if workspace is not None:
+        if workspace.dtype != torch.float32 or not workspace.is_cuda:
+            raise ValueError("workspace must be a float32 GPU tensor")
+        ws_bytes = workspace.numel() * 4
+    if rows == 0:
+        return dx
+    _check(lib().ln_bwd_dx(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx),
+                           _ptr(workspace), ws_bytes, rows, cols, _dt(x), _stream(x)))
+    return dx
+
+
+def ln_bwd_dgamma_dbeta(workspace, rows: int, cols: int, dtype, *, partials_ready: bool,
+                        dy=None, x=None, mean=None, rstd=None, dgamma=None, dbeta=None):
+    """dgamma, dbeta (float32): fold the partials, after stage 1 unless ready."""
+    device = workspace.device
+    dgamma = _out(dgamma, (cols,), torch.float32, device, "dgamma")
+    dbeta = _out(dbeta, (cols,), torch.float32, device, "dbeta")
+    if not partials_ready:
+        r, c = _mat(x, "x")
+        if (r, c) != (rows, cols) or dy.shape != x.shape:
+            raise ValueError("dy/x must be [rows, cols]")
+    if workspace.dtype != torch.float32:
+        raise ValueError("workspace must be float32")
+    if rows == 0:
+        return dgamma.zero_(), dbeta.zero_()
+    _check(lib().ln_bwd_dgamma_dbeta(
+        _ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
+        workspace.numel() * 4, 1 if partials_ready else 0, int(rows), int(cols),
+        _DTYPES[dtype], _stream(workspace)))
+    return dgamma, dbeta
+
+
+def ln_bwd(dy, x, gamma, mean, rstd, *, dx=None, workspace_buf=None, dgamma=None, dbeta=None):
+    """Whole LayerNorm backward: dx with fused partials, then the fold."""
+    rows, cols = _mat(x, "x")
+    ws = workspace_buf if workspace_buf is not None else workspace(rows, cols, x.device)
+    dx = ln_bwd_dx(dy, x, gamma, mean, rstd, dx=dx, workspace=ws)
+    dgamma, dbeta = ln_bwd_dgamma_dbeta(ws, rows, cols, x.dtype, partials_ready=True,
+                                        dgamma=dgamma, dbeta=dbeta)
+    return dx, dgamma, dbeta
+
+
+def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,
+                     scalar: bool = False) -> None:
+    """Test-only: force the row layout of later calls (0 restores the default)."""
+    _check(lib().ln_debug_force_path(int(lanes_per_row), int(slots_per_lane),
+                                     1 if scalar else 0))

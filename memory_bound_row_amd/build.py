@@ -1,0 +1,65 @@
+"""Build libmbrow_ln.so (HIP, gfx950) in-tree with hipcc.
+
+Each kernel file is compiled once per storage type in parallel; the objects
+go to ``_build/`` next to this file and the library to
+``memory_bound_row_amd/libmbrow_ln.so``.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libmbrow_ln.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    # no packed-FP32 instructions in any kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+UNITS = (
+    [("ln_fwd.hip", ["-DMBROW_DT=%d" % d], "ln_fwd_%d.o" % d) for d in range(3)]
+    + [("ln_bwd.hip", ["-DMBROW_DT=%d" % d], "ln_bwd_%d.o" % d) for d in range(3)]
+    + [("ln_fold.hip", [], "ln_fold.o"), ("ln_api.cpp", [], "ln_api.o")]
+)
+
+
+def _compile(unit):
+    src, defs, obj = unit
+    out = os.path.join(BUILD, obj)
+    cmd = [HIPCC, *COMMON, *defs, "-c", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
+    return out
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, UNITS))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

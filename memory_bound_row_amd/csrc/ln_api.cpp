@@ -1,0 +1,316 @@
+// ln_api.cpp -- the C ABI declared in include/mbrow_ln.h: argument checks,
+// path selection and launches on the caller's stream.  Everything that can
+// be rejected is rejected here, on the host, before anything is enqueued.
+#include "mbrow_ln.h"
+#include "mbrow_ln_debug.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "ln_launch.hpp"
+
+namespace mbrow {
+
+hipError_t launch_fwd_f32(const Path&, bool, const FwdArgs&, hipStream_t);
+hipError_t launch_fwd_f16(const Path&, bool, const FwdArgs&, hipStream_t);
+hipError_t launch_fwd_bf16(const Path&, bool, const FwdArgs&, hipStream_t);
+hipError_t launch_bwd_f32(const Path&, BwdMode, const BwdArgs&, hipStream_t);
+hipError_t launch_bwd_f16(const Path&, BwdMode, const BwdArgs&, hipStream_t);
+hipError_t launch_bwd_bf16(const Path&, BwdMode, const BwdArgs&, hipStream_t);
+
+hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_fwd_f32(p, fused, a, s);
+    case Dt::F16: return launch_fwd_f16(p, fused, a, s);
+    default: return launch_fwd_bf16(p, fused, a, s);
+    }
+}
+
+hipError_t launch_bwd(Dt dt, const Path& p, BwdMode mode, const BwdArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_bwd_f32(p, mode, a, s);
+    case Dt::F16: return launch_bwd_f16(p, mode, a, s);
+    default: return launch_bwd_bf16(p, mode, a, s);
+    }
+}
+
+int elems_per_slot(Dt dt) { return dt == Dt::F32 ? 4 : 8; }
+
+// Instances compiled in ln_fwd.hip / ln_bwd.hip.
+static bool have_instance(int g, int v) {
+    switch (g) {
+    case 16: case 32: return v == 1;
+    case 64: return v >= 1 && v <= 8;
+    case 128: case 256: case 512: return v == 4;
+    case 1024: return v == 4 || v == 8;
+    default: return false;
+    }
+}
+
+static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0};
+
+Path pick_path(Dt dt, int64_t cols, bool vec) {
+    const int E = elems_per_slot(dt);
+    const int64_t ns = (cols + E - 1) / E;
+    Path p;
+    p.vec = vec && g_force_scalar.load(std::memory_order_relaxed) == 0;
+    const int fg = g_force_g.load(std::memory_order_relaxed);
+    const int fv = g_force_v.load(std::memory_order_relaxed);
+    if (fg > 0 && (int64_t)fg * fv >= ns) {
+        p.g = fg;
+        p.v = fv;
+        return p;
+    }
+    if (ns <= 16) {
+        p.g = 16; p.v = 1;
+    } else if (ns <= 32) {
+        p.g = 32; p.v = 1;
+    } else {
+        // One wave per row while each lane holds at most 32 values (8 fp32
+        // slots or 4 16-bit slots); wider rows spread over 2..16 waves.
+        const int64_t vmax = (E == 4) ? 8 : 4;
+        if (ns <= 64 * vmax) {
+            p.g = 64;
+            p.v = (int)((ns + 63) / 64);
+        } else if (ns <= 1024 * 4) {
+            p.g = 128;
+            while ((int64_t)p.g * 4 < ns) p.g *= 2;
+            p.v = 4;
+        } else {
+            p.g = 1024;
+            p.v = 8;
+        }
+    }
+    return p;
+}
+
+int64_t bwd_partitions(int64_t rows, int64_t cols) {
+    (void)cols;
+    const int64_t kParts = 256;
+    return rows < kParts ? rows : kParts;
+}
+
+}  // namespace mbrow
+
+using namespace mbrow;
+
+namespace {
+
+constexpr int64_t kMaxRows = std::numeric_limits<int32_t>::max();
+
+bool valid_dtype(ln_dtype_t dt) { return dt == LN_F32 || dt == LN_F16 || dt == LN_BF16; }
+
+size_t elem_bytes(ln_dtype_t dt) { return dt == LN_F32 ? 4 : 2; }
+
+int64_t max_cols(ln_dtype_t dt) { return dt == LN_F32 ? LN_MAX_COLS_F32 : LN_MAX_COLS_16BIT; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const void* p;
+    size_t bytes;
+    bool tensor2d;   // a [rows, cols] tensor (may be updated in place)
+};
+
+bool overlaps(const Span& a, const Span& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Outputs may not overlap each other; an output may coincide exactly with a
+// [rows, cols] input (in place) and must otherwise be disjoint from inputs.
+ln_status_t check_aliasing(const Span* outs, int nout, const Span* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j])) return LN_ERR_UNSUPPORTED;
+        for (int j = 0; j < nin; ++j) {
+            if (!overlaps(outs[i], ins[j])) continue;
+            const bool exact = outs[i].p == ins[j].p && outs[i].bytes == ins[j].bytes &&
+                               outs[i].tensor2d && ins[j].tensor2d;
+            if (!exact) return LN_ERR_UNSUPPORTED;
+        }
+    }
+    return LN_OK;
+}
+
+ln_status_t check_shape(int64_t rows, int64_t cols, ln_dtype_t dt) {
+    if (!valid_dtype(dt)) return LN_ERR_DTYPE;
+    if (rows < 0 || cols <= 0) return LN_ERR_SHAPE;
+    if (cols > max_cols(dt) || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
+    return LN_OK;
+}
+
+ln_status_t from_hip(hipError_t e) { return e == hipSuccess ? LN_OK : LN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ln_status_string(ln_status_t status) {
+    switch (status) {
+    case LN_OK: return "LN_OK: success";
+    case LN_ERR_NULL: return "LN_ERR_NULL: a required pointer is NULL";
+    case LN_ERR_SHAPE: return "LN_ERR_SHAPE: rows must be >= 0 and cols > 0";
+    case LN_ERR_DTYPE: return "LN_ERR_DTYPE: unknown storage dtype";
+    case LN_ERR_PARAM: return "LN_ERR_PARAM: eps must be >= 0; p must be in [0, 1)";
+    case LN_ERR_WORKSPACE: return "LN_ERR_WORKSPACE: workspace missing or too small";
+    case LN_ERR_UNSUPPORTED:
+        return "LN_ERR_UNSUPPORTED: shape too large or buffers overlap in a way the call "
+               "does not allow";
+    case LN_ERR_HIP: return "LN_ERR_HIP: a HIP launch failed";
+    default: return "unknown ln_status_t";
+    }
+}
+
+size_t ln_bwd_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)bwd_partitions(rows, cols) * 2u * (size_t)cols * sizeof(float);
+}
+
+ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
+                   float* rstd, int64_t rows, int64_t cols, float eps, ln_dtype_t dt,
+                   hipStream_t stream) {
+    if (!x || !gamma || !beta || !y) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    if (!(eps >= 0.0f) || std::isinf(eps)) return LN_ERR_PARAM;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float);
+    const Span outs[] = {{y, tb, true}, {mean, sb, false}, {rstd, sb, false}};
+    const Span ins[] = {{x, tb, true}, {gamma, vb, false}, {beta, vb, false}};
+    st = check_aliasing(outs, 3, ins, 3);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(x) && aligned16(y) && aligned16(gamma) && aligned16(beta) &&
+                     (cols * (int64_t)es) % 16 == 0;
+    FwdArgs a{};
+    a.x = x; a.gamma = gamma; a.beta = beta; a.y = y; a.mean = mean; a.rstd = rstd;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.eps = eps;
+    return from_hip(launch_fwd(d, pick_path(d, cols, vec), false, a, stream));
+}
+
+ln_status_t bias_dropout_residual_ln_fwd(const void* x, const void* bias, const void* residual,
+                                         const void* gamma, const void* beta, void* residual_out,
+                                         void* y, float* mean, float* rstd, uint8_t* mask_out,
+                                         int64_t rows, int64_t cols, float eps, float p,
+                                         uint64_t seed, ln_dtype_t dt, hipStream_t stream) {
+    if (!x || !bias || !residual || !gamma || !beta || !residual_out || !y) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    if (!(eps >= 0.0f) || std::isinf(eps)) return LN_ERR_PARAM;
+    if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float);
+    const Span outs[] = {{residual_out, tb, true}, {y, tb, true}, {mean, sb, false},
+                         {rstd, sb, false}, {mask_out, (size_t)rows * (size_t)cols, false}};
+    const Span ins[] = {{x, tb, true}, {residual, tb, true}, {bias, vb, false},
+                        {gamma, vb, false}, {beta, vb, false}};
+    st = check_aliasing(outs, 5, ins, 5);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(x) && aligned16(bias) && aligned16(residual) &&
+                     aligned16(gamma) && aligned16(beta) && aligned16(residual_out) &&
+                     aligned16(y) && (cols * (int64_t)es) % 16 == 0;
+    FwdArgs a{};
+    a.x = x; a.bias = bias; a.residual = residual; a.gamma = gamma; a.beta = beta;
+    a.residual_out = residual_out; a.y = y; a.mean = mean; a.rstd = rstd; a.mask_out = mask_out;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.eps = eps;
+    a.thr = (uint32_t)std::floor((double)p * 65536.0 + 0.5);
+    a.scale = (float)(1.0 / (1.0 - (double)p));
+    a.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    a.seed_hi = (uint32_t)(seed >> 32);
+    return from_hip(launch_fwd(d, pick_path(d, cols, vec), true, a, stream));
+}
+
+ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const float* mean,
+                      const float* rstd, void* dx, float* workspace, size_t workspace_bytes,
+                      int64_t rows, int64_t cols, ln_dtype_t dt, hipStream_t stream) {
+    if (!dy || !x || !gamma || !mean || !rstd || !dx) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    const size_t need = ln_bwd_workspace_bytes(rows, cols);
+    if (workspace && workspace_bytes < need) return LN_ERR_WORKSPACE;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float);
+    const Span outs[] = {{dx, tb, true}, {workspace, workspace ? need : 0, false}};
+    const Span ins[] = {{dy, tb, true}, {x, tb, true}, {gamma, vb, false},
+                        {mean, sb, false}, {rstd, sb, false}};
+    st = check_aliasing(outs, 2, ins, 5);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(dy) && aligned16(x) && aligned16(gamma) && aligned16(dx) &&
+                     (cols * (int64_t)es) % 16 == 0;
+    BwdArgs a{};
+    a.dy = dy; a.x = x; a.gamma = gamma; a.mean = mean; a.rstd = rstd; a.dx = dx;
+    a.ws = workspace;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.parts = bwd_partitions(rows, cols);
+    a.inv_m = (float)(1.0 / (double)cols);
+    const BwdMode mode = workspace ? BwdMode::DX_PARTIALS : BwdMode::DX;
+    return from_hip(launch_bwd(d, pick_path(d, cols, vec), mode, a, stream));
+}
+
+ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean,
+                                const float* rstd, float* dgamma, float* dbeta, float* workspace,
+                                size_t workspace_bytes, int partials_ready, int64_t rows,
+                                int64_t cols, ln_dtype_t dt, hipStream_t stream) {
+    if (!dgamma || !dbeta || !workspace) return LN_ERR_NULL;
+    if (!partials_ready && (!dy || !x || !mean || !rstd)) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    const size_t need = ln_bwd_workspace_bytes(rows, cols);
+    if (workspace_bytes < need) return LN_ERR_WORKSPACE;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float), cb = (size_t)cols * sizeof(float);
+    const Span outs[] = {{dgamma, cb, false}, {dbeta, cb, false},
+                         {partials_ready ? nullptr : workspace, need, false}};
+    const Span ins[] = {{dy, tb, true}, {x, tb, true}, {mean, sb, false}, {rstd, sb, false},
+                        {partials_ready ? workspace : nullptr, need, false}};
+    st = check_aliasing(outs, 3, ins, 5);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const int64_t parts = bwd_partitions(rows, cols);
+    if (!partials_ready) {
+        const bool vec = aligned16(dy) && aligned16(x) && (cols * (int64_t)es) % 16 == 0;
+        BwdArgs a{};
+        a.dy = dy; a.x = x; a.mean = mean; a.rstd = rstd; a.ws = workspace;
+        a.rows = rows; a.m = cols;
+        a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+        a.parts = parts;
+        a.inv_m = (float)(1.0 / (double)cols);
+        st = from_hip(launch_bwd(d, pick_path(d, cols, vec), BwdMode::PARTIALS, a, stream));
+        if (st != LN_OK) return st;
+    }
+    return from_hip(launch_fold(workspace, parts, cols, dgamma, dbeta, stream));
+}
+
+ln_status_t ln_debug_force_path(int lanes_per_row, int slots_per_lane, int scalar) {
+    if (lanes_per_row != 0 && !have_instance(lanes_per_row, slots_per_lane))
+        return LN_ERR_UNSUPPORTED;
+    g_force_g.store(lanes_per_row, std::memory_order_relaxed);
+    g_force_v.store(lanes_per_row ? slots_per_lane : 0, std::memory_order_relaxed);
+    g_force_scalar.store(scalar ? 1 : 0, std::memory_order_relaxed);
+    return LN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,339 @@
+// ln_device.hpp -- device-side building blocks of the fused LayerNorm kernels
+// for gfx950 (CDNA4, wave64).
+//
+// Sources ("the pages"):
+//   [L10]  "Accelerating Transformer on GPU (I): Kernel Fusion and LightSeq
+//          Inference" (CMU 11-868 lecture-10 notes)
+//   [L11]  "Accelerating Transformer on GPU (II): Training with LightSeq2"
+//   [BLOG] "AI infra 学习记录(2): 从 LayerNorm 算子熟悉常见的算子优化方法"
+//   [LLMC] "02 · llmc/ 的 CUDA kernel 层"
+//
+// Contents: storage-type traits (16-byte slot load/unpack/pack/store with
+// round-to-nearest-even), the lane -> slot -> column map shared by every
+// kernel, wave-level reductions built on DPP / ds_swizzle / readlane, the
+// shifted (count, sum, M2) merge used for row statistics, and Philox4x32-10.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// No implicit multiply-add contraction anywhere in the kernels: every fused
+// multiply-add is written out with fmaf, so that two kernels that share an
+// expression round it identically (the partials of the fused and standalone
+// dgamma/dbeta paths must match bit for bit) and so that symmetric merges
+// stay symmetric.
+#pragma clang fp contract(off)
+
+namespace mbrow {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Storage types.  A "slot" is 16 bytes of a row: E consecutive elements.
+// ---------------------------------------------------------------------------
+struct StF32 {
+    static constexpr int E = 4;
+    static constexpr int BYTES = 4;
+    __device__ static inline float to_f(uint32_t bits) { return __uint_as_float(bits); }
+    __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+    }
+    __device__ static inline u32x4 pack(const float* f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+        return v;
+    }
+    __device__ static inline float load1(const void* p, int64_t i) {
+        return static_cast<const float*>(p)[i];
+    }
+    __device__ static inline void store1(void* p, int64_t i, float f) {
+        static_cast<float*>(p)[i] = f;
+    }
+    // value as it would be stored (RNE to T), back in float
+    __device__ static inline float round(float f) { return f; }
+};
+
+struct StBF16 {
+    static constexpr int E = 8;
+    static constexpr int BYTES = 2;
+    __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(v[i] << 16);
+            f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    }
+    __device__ static inline uint32_t pack2(float a, float b) {
+        bf16x2 h = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32, RNE
+        return __builtin_bit_cast(uint32_t, h);
+    }
+    __device__ static inline u32x4 pack(const float* f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = pack2(f[2 * i], f[2 * i + 1]);
+        return v;
+    }
+    __device__ static inline float load1(const void* p, int64_t i) {
+        uint32_t b = static_cast<const uint16_t*>(p)[i];
+        return __uint_as_float(b << 16);
+    }
+    __device__ static inline void store1(void* p, int64_t i, float f) {
+        static_cast<__bf16*>(p)[i] = (__bf16)f;
+    }
+    __device__ static inline float round(float f) { return (float)(__bf16)f; }
+};
+
+struct StF16 {
+    static constexpr int E = 8;
+    static constexpr int BYTES = 2;
+    __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // copy the word out first: a bit_cast applied directly to the
+            // vector element v[i] is miscompiled (every i reads element 0)
+            const uint32_t word = v[i];
+            f16x2 h = __builtin_bit_cast(f16x2, word);
+            f[2 * i] = (float)h[0];
+            f[2 * i + 1] = (float)h[1];
+        }
+    }
+    __device__ static inline uint32_t pack2(float a, float b) {
+        f16x2 h = {(_Float16)a, (_Float16)b};  // v_cvt_f16_f32, RNE
+        return __builtin_bit_cast(uint32_t, h);
+    }
+    __device__ static inline u32x4 pack(const float* f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = pack2(f[2 * i], f[2 * i + 1]);
+        return v;
+    }
+    __device__ static inline float load1(const void* p, int64_t i) {
+        return (float)static_cast<const _Float16*>(p)[i];
+    }
+    __device__ static inline void store1(void* p, int64_t i, float f) {
+        static_cast<_Float16*>(p)[i] = (_Float16)f;
+    }
+    __device__ static inline float round(float f) { return (float)(_Float16)f; }
+};
+
+// ---------------------------------------------------------------------------
+// Slot access.  VEC: one 16-byte access per slot (row starts 16-byte
+// aligned, cols*sizeof(T) a multiple of 16).  Otherwise one access per
+// element, each predicated on its column.  Streaming tensors use
+// nontemporal accesses; gamma/beta/bias (re-read by every row) do not.
+// ---------------------------------------------------------------------------
+template <class S, bool VEC, bool NT>
+__device__ inline void load_slot(const void* base, int64_t row_off, int64_t col0,
+                                 int64_t m, bool valid, float* f) {
+    if constexpr (VEC) {
+        if (valid) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(
+                static_cast<const char*>(base) + (row_off + col0) * S::BYTES);
+            u32x4 v;
+            if constexpr (NT) v = __builtin_nontemporal_load(p);
+            else v = *p;
+            S::unpack(v, f);
+        } else {
+#pragma unroll
+            for (int e = 0; e < S::E; ++e) f[e] = 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < S::E; ++e)
+            f[e] = (valid && col0 + e < m) ? S::load1(base, row_off + col0 + e) : 0.0f;
+    }
+}
+
+template <class S, bool VEC, bool NT>
+__device__ inline void store_slot(void* base, int64_t row_off, int64_t col0, int64_t m,
+                                  bool valid, const float* f) {
+    if (!valid) return;
+    if constexpr (VEC) {
+        u32x4* p = reinterpret_cast<u32x4*>(static_cast<char*>(base) +
+                                            (row_off + col0) * S::BYTES);
+        u32x4 v = S::pack(f);
+        if constexpr (NT) __builtin_nontemporal_store(v, p);
+        else *p = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < S::E; ++e)
+            if (col0 + e < m) S::store1(base, row_off + col0 + e, f[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level data movement (wave64).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ inline float swz_xor16(float v) {
+    // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 (stays inside 32 lanes)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+__device__ inline float lane_read(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+constexpr int DPP_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within 8
+constexpr int DPP_MIRROR = 0x140;       // lane i <-> 15-i within 16
+
+// Partner of the butterfly step at distance D (lanes stay in their group of
+// 2D): quad permutes for 1 and 2, mirrors for 4 and 8, swizzle for 16.  The
+// mirrors pair each lane with one in the other half of its group, which is
+// all a symmetric merge needs.
+template <int D>
+__device__ inline float partner(float v) {
+    if constexpr (D == 1) return dpp<DPP_XOR1>(v);
+    else if constexpr (D == 2) return dpp<DPP_XOR2>(v);
+    else if constexpr (D == 4) return dpp<DPP_HALF_MIRROR>(v);
+    else if constexpr (D == 8) return dpp<DPP_MIRROR>(v);
+    else return swz_xor16(v);
+}
+
+// Sum over aligned groups of G lanes (G = 1..64), result in every lane of the
+// group.  Adds are commutative, so both partners of a step compute the same
+// bits and every lane ends with the identical sum.
+template <int G>
+__device__ inline float group_sum(float v) {
+    if constexpr (G >= 2) v = v + partner<1>(v);
+    if constexpr (G >= 4) v = v + partner<2>(v);
+    if constexpr (G >= 8) v = v + partner<4>(v);
+    if constexpr (G >= 16) v = v + partner<8>(v);
+    if constexpr (G >= 32) v = v + partner<16>(v);
+    if constexpr (G >= 64) v = lane_read(v, 0) + lane_read(v, 32);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics.  Each lane holds (n, s, q): its element count, the sum of
+// its values minus a shift c shared by the whole group, and the sum of
+// squared deviations from its own mean.  Two such states with the same shift
+// merge as ([L10] §4.2, the Chan et al. pairwise update, written with sums):
+//   n = na + nb,  s = sa + sb,  q = qa + qb + (nb*sa - na*sb)^2 / (na*nb*n).
+// Every operation is commutative in (a, b) and no product is contracted, so
+// both partners of a butterfly step get the same bits.  The shift keeps the
+// sums small when the row mean is large compared with its spread ([L10]
+// §4.2: E[x^2] - E[x]^2 collapses at mean 1e4).
+// ---------------------------------------------------------------------------
+struct Stats {
+    float n, s, q;
+};
+
+__device__ inline Stats merge(const Stats& a, const Stats& b) {
+    if (a.n == 0.0f) return b;
+    if (b.n == 0.0f) return a;
+    Stats r;
+    r.n = a.n + b.n;
+    r.s = a.s + b.s;
+    float d = b.n * a.s - a.n * b.s;
+    float w = (a.n * b.n) * r.n;
+    r.q = (a.q + b.q) + (d * d) / w;
+    return r;
+}
+
+template <int D>
+__device__ inline Stats merge_step(const Stats& a) {
+    Stats b{partner<D>(a.n), partner<D>(a.s), partner<D>(a.q)};
+    // merge(a, b) and merge(b, a) coincide bit for bit: sums and products are
+    // commutative, and fl(p - q) = -fl(q - p) under round-to-nearest-even, so
+    // d differs only in sign and d*d is identical.
+    return merge(a, b);
+}
+
+template <int G>
+__device__ inline Stats group_stats(Stats st) {
+    if constexpr (G >= 2) st = merge_step<1>(st);
+    if constexpr (G >= 4) st = merge_step<2>(st);
+    if constexpr (G >= 8) st = merge_step<4>(st);
+    if constexpr (G >= 16) st = merge_step<8>(st);
+    if constexpr (G >= 32) st = merge_step<16>(st);
+    if constexpr (G >= 64) {
+        Stats lo{lane_read(st.n, 0), lane_read(st.s, 0), lane_read(st.q, 0)};
+        Stats hi{lane_read(st.n, 32), lane_read(st.s, 32), lane_read(st.q, 32)};
+        st = merge(lo, hi);
+    }
+    return st;
+}
+
+// Re-express a state whose values were shifted by cb relative to shift ca.
+__device__ inline Stats reshift(const Stats& b, float cb, float ca) {
+    Stats r = b;
+    r.s = b.s + b.n * (cb - ca);
+    return r;
+}
+
+// Broadcast lane (group base) value to every lane of its group of G lanes.
+template <int G>
+__device__ inline float group_broadcast_first(float v, int lane) {
+    if constexpr (G >= 64) {
+        return lane_read(v, 0);
+    } else if constexpr (G == 32) {
+        float a = lane_read(v, 0), b = lane_read(v, 32);
+        return lane < 32 ? a : b;
+    } else if constexpr (G == 16) {
+        float a = lane_read(v, 0), b = lane_read(v, 16);
+        float c = lane_read(v, 32), d = lane_read(v, 48);
+        float lo = lane < 16 ? a : b, hi = lane < 48 ? c : d;
+        return lane < 32 ? lo : hi;
+    } else {
+        return __shfl(v, lane & ~(G - 1), 64);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): 10 rounds of two
+// 32x32->64 multiplies and xors with a Weyl-sequence key schedule.
+// ---------------------------------------------------------------------------
+__device__ inline u32x4 philox4x32_10(u32x4 ctr, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = (uint64_t)ctr[0] * 0xD2511F53u;
+        uint64_t p2 = (uint64_t)ctr[2] * 0xCD9E8D57u;
+        u32x4 nx;
+        nx[0] = (uint32_t)(p2 >> 32) ^ ctr[1] ^ k0;
+        nx[1] = (uint32_t)p2;
+        nx[2] = (uint32_t)(p0 >> 32) ^ ctr[3] ^ k1;
+        nx[3] = (uint32_t)p0;
+        ctr = nx;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return ctr;
+}
+
+// Keep bits of the E columns col0 .. col0+E-1 of one row (all in the same
+// group of 8 columns): bit e set iff the 16-bit uniform of column col0+e is
+// >= thr.  Counter (col >> 3, row lo, row hi, 0); key (seed lo, seed hi);
+// column k = col & 7 of the group takes half (k & 1) of word k >> 1.
+template <int E>
+__device__ inline uint32_t keep_bits(int64_t row, int64_t col0, uint32_t seed_lo,
+                                     uint32_t seed_hi, uint32_t thr) {
+    if (thr == 0u) return (1u << E) - 1u;  // u >= 0 always: keep every column
+    u32x4 c;
+    c[0] = (uint32_t)((uint64_t)col0 >> 3);
+    c[1] = (uint32_t)((uint64_t)row & 0xffffffffu);
+    c[2] = (uint32_t)((uint64_t)row >> 32);
+    c[3] = 0u;
+    u32x4 w = philox4x32_10(c, seed_lo, seed_hi);
+    uint32_t bits = 0;
+    // E == 8: the slot is a whole group of 8 columns.  E == 4: it is the low
+    // or the high half of one (col0 & 4), i.e. words 0-1 or words 2-3.
+    const bool high = (E == 4) && ((col0 & 4) != 0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        uint32_t word = high ? w[2 + (e >> 1)] : w[e >> 1];
+        uint32_t u = (e & 1) ? (word >> 16) : (word & 0xffffu);
+        bits |= (u >= thr ? 1u : 0u) << e;
+    }
+    return bits;
+}
+
+}  // namespace mbrow

@@ -1,0 +1,90 @@
+"""Shared steps of the GPU parity tests: run the HIP library through its
+binding, run the float64 oracle on the same stored values, compare under the
+tolerance rule of oracle/compare.py."""
+import sys
+
+import numpy as np
+import torch
+
+import memory_bound_row_amd as mb
+from memory_bound_row_amd import synth
+from oracle import compare as cmp
+
+FMT = {torch.float32: cmp.F32, torch.float16: cmp.F16, torch.bfloat16: cmp.BF16}
+EPS = 1e-5
+
+
+def case(msg: str) -> None:
+    """Name the case on stderr before its GPU work starts."""
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def dev(d: dict) -> dict:
+    return {k: v.to("cuda") for k, v in d.items()}
+
+
+def f64(t) -> np.ndarray:
+    return synth.as_f64(t)
+
+
+def assert_reports(*reports):
+    bad = [r for r in reports if not r.ok]
+    msg = "\n".join(str(r) + (f" first failures: {r.details}" if r.details else "")
+                    for r in reports)
+    assert not bad, msg
+    return reports
+
+
+def check_fwd(orc, x, gamma, beta, y, mean, rstd, fmt, eps=EPS, name="fwd"):
+    y_ref, mu_ref, rs_ref = orc.ln_fwd(f64(x).reshape(-1, x.shape[-1]), f64(gamma),
+                                       f64(beta), eps)
+    reps = [cmp.check_elementwise(f"{name}.y", f64(y).reshape(y_ref.shape), y_ref, fmt)]
+    if mean is not None:
+        reps.append(cmp.check_stats(f"{name}.mean", f64(mean), mu_ref))
+        reps.append(cmp.check_stats(f"{name}.rstd", f64(rstd), rs_ref))
+    return assert_reports(*reps)
+
+
+def check_bwd(orc, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, fmt, name="bwd"):
+    """Reference dx, dgamma, dbeta from the stored inputs and the stored fp32
+    mean/rstd the GPU read."""
+    rows, cols = x.shape[0], x.shape[-1]
+    dy64, x64 = f64(dy).reshape(rows, cols), f64(x).reshape(rows, cols)
+    mu64, rs64 = f64(mean), f64(rstd)
+    reps = []
+    if dx is not None:
+        dx_ref = orc.ln_bwd_dx(dy64, x64, f64(gamma), mu64, rs64)
+        scale = orc.ln_bwd_dx_scale(dy64, x64, f64(gamma), mu64, rs64)
+        reps.append(cmp.check_elementwise(f"{name}.dx", f64(dx).reshape(rows, cols),
+                                          dx_ref, fmt, term_scale=scale, row_len=cols))
+    if dgamma is not None:
+        dg, db, sg, sb = orc.ln_bwd_params(dy64, x64, mu64, rs64)
+        reps.append(cmp.check_colsum(f"{name}.dgamma", f64(dgamma), dg, sg, rows, fmt))
+        reps.append(cmp.check_colsum(f"{name}.dbeta", f64(dbeta), db, sb, rows, fmt))
+    return assert_reports(*reps)
+
+
+def check_fused(orc, inp, p, seed, z, y, mean, rstd, mask, fmt, eps=EPS, name="fused"):
+    rows, cols = inp["x"].shape
+    keep = orc.dropout_keep(seed, p, rows, cols)
+    reps = []
+    if mask is not None:
+        m = mask.cpu().numpy()
+        n_diff = int(np.count_nonzero(m != keep))
+        assert n_diff == 0, f"{name}: {n_diff} mask bits differ from the oracle"
+    z_ref = orc.bias_dropout_residual(f64(inp["x"]), f64(inp["bias"]), f64(inp["residual"]),
+                                      keep, p)
+    reps.append(cmp.check_elementwise(f"{name}.z", f64(z), z_ref, fmt))
+    # the LayerNorm runs on z as stored
+    reps += list(check_fwd(orc, z, inp["gamma"], inp["beta"], y, mean, rstd, fmt, eps,
+                           name=f"{name}.ln"))
+    return assert_reports(*reps)
+
+
+def run_fwd_bwd(rows, cols, dtype, seed=0, x_mean=0.0, x_std=1.0):
+    inp = dev(synth.layer_inputs(rows, cols, dtype, seed=seed, x_mean=x_mean, x_std=x_std,
+                                 names=("x", "gamma", "beta", "dy")))
+    y, mean, rstd = mb.ln_fwd(inp["x"], inp["gamma"], inp["beta"], EPS)
+    dx, dg, db = mb.ln_bwd(inp["dy"], inp["x"], inp["gamma"], mean, rstd)
+    torch.cuda.synchronize()
+    return inp, y, mean, rstd, dx, dg, db

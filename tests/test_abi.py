@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the public
+headers declare, and rejects every invalid argument on the host (before any
+HIP call, so these run without a GPU)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import memory_bound_row_amd as mb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+LN_OK, LN_ERR_NULL, LN_ERR_SHAPE, LN_ERR_DTYPE, LN_ERR_PARAM = 0, 1, 2, 3, 4
+LN_ERR_WORKSPACE, LN_ERR_UNSUPPORTED, LN_ERR_HIP = 5, 6, 7
+F32, F16, BF16 = 0, 1, 2
+
+# fake but non-NULL device addresses: validation never dereferences them
+A, B, C, D, E, F, G, H = (0x10000000 * k for k in range(1, 9))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mb.lib()
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(?:ln_status_t|size_t|const char\s*\*)\s*(\w+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert {"ln_fwd", "bias_dropout_residual_ln_fwd", "ln_bwd_dx", "ln_bwd_dgamma_dbeta",
+            "ln_bwd_workspace_bytes", "ln_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(8):
+        s = mb.status_string(code)
+        assert s and s != "unknown ln_status_t"
+    assert mb.status_string(99) == "unknown ln_status_t"
+
+
+def test_workspace_bytes(L):
+    assert L.ln_bwd_workspace_bytes(0, 10) == 0
+    assert L.ln_bwd_workspace_bytes(10, 0) == 0
+    assert L.ln_bwd_workspace_bytes(-1, 10) == 0
+    # P = min(rows, 256) partitions of [2, cols] float32
+    assert L.ln_bwd_workspace_bytes(8192, 1280) == 256 * 2 * 1280 * 4
+    assert L.ln_bwd_workspace_bytes(64, 768) == 64 * 2 * 768 * 4
+    assert L.ln_bwd_workspace_bytes(1, 7) == 1 * 2 * 7 * 4
+
+
+def fwd(L, x=A, g=B, b=C, y=D, mean=None, rstd=None, rows=4, cols=8, eps=1e-5, dt=BF16):
+    return L.ln_fwd(x, g, b, y, mean, rstd, rows, cols, eps, dt, None)
+
+
+def test_ln_fwd_validation(L):
+    assert fwd(L, x=None) == LN_ERR_NULL
+    assert fwd(L, g=None) == LN_ERR_NULL
+    assert fwd(L, b=None) == LN_ERR_NULL
+    assert fwd(L, y=None) == LN_ERR_NULL
+    assert fwd(L, rows=-1) == LN_ERR_SHAPE
+    assert fwd(L, cols=0) == LN_ERR_SHAPE
+    assert fwd(L, cols=-3) == LN_ERR_SHAPE
+    assert fwd(L, dt=3) == LN_ERR_DTYPE
+    assert fwd(L, dt=-1) == LN_ERR_DTYPE
+    assert fwd(L, eps=-1e-6) == LN_ERR_PARAM
+    assert fwd(L, eps=float("nan")) == LN_ERR_PARAM
+    assert fwd(L, eps=float("inf")) == LN_ERR_PARAM
+    assert fwd(L, cols=32769, dt=F32) == LN_ERR_UNSUPPORTED
+    assert fwd(L, cols=65537, dt=BF16) == LN_ERR_UNSUPPORTED
+    assert fwd(L, rows=2 ** 31) == LN_ERR_UNSUPPORTED
+    assert fwd(L, rows=0) == LN_OK            # no-op, nothing enqueued
+    # y may be x exactly, but not a partial overlap of it
+    assert fwd(L, rows=0, y=A) == LN_OK
+    assert fwd(L, y=A + 2) == LN_ERR_UNSUPPORTED
+    # outputs must not overlap parameters or each other
+    assert fwd(L, y=B) == LN_ERR_UNSUPPORTED
+    assert fwd(L, mean=E, rstd=E) == LN_ERR_UNSUPPORTED
+    assert fwd(L, mean=D + 8) == LN_ERR_UNSUPPORTED
+
+
+def fused(L, x=A, bias=B, res=C, g=D, b=E, z=F, y=G, mean=None, rstd=None, mask=None,
+          rows=4, cols=8, eps=1e-5, p=0.1, seed=0, dt=BF16):
+    return L.bias_dropout_residual_ln_fwd(x, bias, res, g, b, z, y, mean, rstd, mask,
+                                          rows, cols, eps, p, seed, dt, None)
+
+
+def test_fused_fwd_validation(L):
+    for k in ("x", "bias", "res", "g", "b", "z", "y"):
+        assert fused(L, **{k: None}) == LN_ERR_NULL, k
+    assert fused(L, rows=-5) == LN_ERR_SHAPE
+    assert fused(L, cols=0) == LN_ERR_SHAPE
+    assert fused(L, dt=7) == LN_ERR_DTYPE
+    assert fused(L, p=-0.1) == LN_ERR_PARAM
+    assert fused(L, p=1.0) == LN_ERR_PARAM
+    assert fused(L, p=float("nan")) == LN_ERR_PARAM
+    assert fused(L, eps=-1.0) == LN_ERR_PARAM
+    assert fused(L, rows=0) == LN_OK
+    assert fused(L, rows=0, z=C, y=A) == LN_OK                 # in place
+    assert fused(L, z=G) == LN_ERR_UNSUPPORTED                  # z and y alias
+    assert fused(L, z=B) == LN_ERR_UNSUPPORTED                  # z over bias
+    assert fused(L, mask=A) == LN_ERR_UNSUPPORTED               # mask over x
+
+
+def bwd_dx(L, dy=A, x=B, g=C, mean=D, rstd=E, dx=F, ws=None, wsb=0, rows=4, cols=8, dt=BF16):
+    return L.ln_bwd_dx(dy, x, g, mean, rstd, dx, ws, wsb, rows, cols, dt, None)
+
+
+def test_bwd_dx_validation(L):
+    for k in ("dy", "x", "g", "mean", "rstd", "dx"):
+        assert bwd_dx(L, **{k: None}) == LN_ERR_NULL, k
+    assert bwd_dx(L, rows=-1) == LN_ERR_SHAPE
+    assert bwd_dx(L, cols=0) == LN_ERR_SHAPE
+    assert bwd_dx(L, dt=5) == LN_ERR_DTYPE
+    need = L.ln_bwd_workspace_bytes(4, 8)
+    assert bwd_dx(L, ws=G, wsb=need - 1) == LN_ERR_WORKSPACE
+    assert bwd_dx(L, rows=0) == LN_OK
+    assert bwd_dx(L, rows=0, dx=A) == LN_OK                     # dx == dy in place
+    assert bwd_dx(L, dx=A + 4) == LN_ERR_UNSUPPORTED
+    assert bwd_dx(L, ws=A, wsb=need) == LN_ERR_UNSUPPORTED      # workspace over dy
+
+
+def dgdb(L, dy=A, x=B, mean=C, rstd=D, dg=E, db=F, ws=G, wsb=None, ready=0, rows=4, cols=8,
+         dt=BF16):
+    if wsb is None:
+        wsb = L.ln_bwd_workspace_bytes(rows, cols)
+    return L.ln_bwd_dgamma_dbeta(dy, x, mean, rstd, dg, db, ws, wsb, ready, rows, cols, dt,
+                                 None)
+
+
+def test_dgamma_dbeta_validation(L):
+    for k in ("dg", "db", "ws"):
+        assert dgdb(L, **{k: None}) == LN_ERR_NULL, k
+    for k in ("dy", "x", "mean", "rstd"):
+        assert dgdb(L, **{k: None}) == LN_ERR_NULL, k
+        assert dgdb(L, rows=0, ready=1, **{k: None}) == LN_OK, k
+    assert dgdb(L, wsb=L.ln_bwd_workspace_bytes(4, 8) - 4) == LN_ERR_WORKSPACE
+    assert dgdb(L, rows=-2) == LN_ERR_SHAPE
+    assert dgdb(L, dt=9) == LN_ERR_DTYPE
+    assert dgdb(L, dg=F) == LN_ERR_UNSUPPORTED                  # dgamma over dbeta
+
+
+def test_debug_force_path_validation(L):
+    assert L.ln_debug_force_path(48, 1, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(64, 9, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(128, 2, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(64, 3, 0) == LN_OK
+    assert L.ln_debug_force_path(0, 0, 0) == LN_OK
