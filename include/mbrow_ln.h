@@ -23,9 +23,11 @@
  *   pointer after the call returns.  No alignment is required: 16-byte
  *   aligned bases with cols*sizeof(T) a multiple of 16 take the vector path,
  *   anything else a per-element path with identical results.
- * Aliasing.  Only the exact in-place forms y == x (ln_fwd) and dx == dy
- *   (ln_bwd_dx) are allowed; any other overlap of an output with an input
- *   or another output is undefined.
+ * Aliasing.  An output [rows, cols] tensor may be exactly one of the call's
+ *   [rows, cols] inputs (in place: y == x, residual_out == residual,
+ *   dx == dy, ...); every row is read completely before any of it is
+ *   written.  Any other overlap of an output with an input or with another
+ *   output is rejected with LN_ERR_UNSUPPORTED.
  * Streams.  All work is enqueued on `stream` (NULL = the null stream).  No
  *   call synchronises, allocates, memsets or copies, so every call may be
  *   captured into a HIP graph.  Outputs are valid once the stream has
@@ -61,14 +63,14 @@ typedef enum {
     LN_ERR_DTYPE = 3,       /* unknown ln_dtype_t                              */
     LN_ERR_PARAM = 4,       /* eps < 0 or NaN; p outside [0, 1) or NaN         */
     LN_ERR_WORKSPACE = 5,   /* workspace smaller than ln_bwd_workspace_bytes   */
-    LN_ERR_UNSUPPORTED = 6, /* cols above LN_MAX_COLS for this dtype, or an
-                               aliasing form the call does not allow          */
+    LN_ERR_UNSUPPORTED = 6, /* cols above LN_MAX_COLS, or an aliasing form
+                               the call does not allow                        */
     LN_ERR_HIP = 7          /* a HIP launch or query failed                    */
 } ln_status_t;
 
-/* Widest row each storage type supports (the whole row is held on chip). */
-#define LN_MAX_COLS_F32 32768
-#define LN_MAX_COLS_16BIT 65536
+/* Widest row supported, for every storage type (the whole row is held in
+ * registers of one workgroup). */
+#define LN_MAX_COLS 16384
 
 /*
  * LayerNorm forward.  For each row r with m = cols:

@@ -20,16 +20,25 @@ extern "C" {
  * Force the row layout of every later call in this process:
  *   lanes_per_row  16, 32, 64, 128, 256, 512 or 1024; 0 restores the
  *                  library's own choice (and ignores slots_per_lane).
- *   slots_per_lane 16-byte slots per lane: 1 for 16/32 lanes, 1-8 for 64,
- *                  4 for 128-512, 4 or 8 for 1024.
+ *   slots_per_lane 16-byte slots per lane.  Built layouts: fp32 16x{1,2,4,8},
+ *                  32x1-8, 64x1-8, {128,256,512,1024}x4; fp16/bf16
+ *                  16x{1,2,4}, 32x1-5, 64x1-5, {128,256,512}x4.
  *   scalar         non-zero forces per-element loads and stores.
- * A forced layout applies only to calls whose row fits it
- * (lanes_per_row * slots_per_lane slots); other calls use the library's own
- * choice.  Returns LN_ERR_UNSUPPORTED (and changes nothing) for a layout the
- * library was not built with.  Not thread-safe with respect to concurrent
+ * A forced layout applies only to calls whose dtype has it built and whose
+ * row fits it (lanes_per_row * slots_per_lane slots); other calls use the
+ * library's own choice.  Returns LN_ERR_UNSUPPORTED (and changes nothing)
+ * for a layout no dtype was built with.  Not thread-safe with respect to concurrent
  * calls that expect a particular layout.
  */
 ln_status_t ln_debug_force_path(int lanes_per_row, int slots_per_lane, int scalar);
+
+/*
+ * Force the grid of the persistent forward kernels: workgroups_per_cu > 0
+ * launches that many workgroups per compute unit, -1 one workgroup per block
+ * of rows (no persistence), 0 restores the occupancy-derived default.
+ * Results do not depend on it.
+ */
+ln_status_t ln_debug_force_grid(int workgroups_per_cu);
 
 #ifdef __cplusplus
 }

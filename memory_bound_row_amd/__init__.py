@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
                                       i64, i64, i32, vp]
     L.ln_debug_force_path.restype = i32
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
+    L.ln_debug_force_grid.restype = i32
+    L.ln_debug_force_grid.argtypes = [i32]
     _lib = L
     return L
 
@@ -215,3 +217,8 @@ def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,
     """Test-only: force the row layout of later calls (0 restores the default)."""
     _check(lib().ln_debug_force_path(int(lanes_per_row), int(slots_per_lane),
                                      1 if scalar else 0))
+
+
+def debug_force_grid(workgroups_per_cu: int = 0) -> None:
+    """Test-only: persistent-grid size of the forward (0 default, -1 one per block)."""
+    _check(lib().ln_debug_force_grid(int(workgroups_per_cu)))

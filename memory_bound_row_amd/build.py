@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -34,13 +35,30 @@ UNITS = (
 )
 
 
+def _spilling_kernels(remarks: str):
+    """Kernels whose resource-usage remarks report VGPR spills or scratch."""
+    bad = []
+    for block in re.split(r"remark: Function Name: ", remarks)[1:]:
+        name = block.split()[0]
+        spill = re.search(r"VGPRs Spill: (\d+)", block)
+        scratch = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", block)
+        if (spill and int(spill.group(1))) or (scratch and int(scratch.group(1))):
+            bad.append(name)
+    return bad
+
+
 def _compile(unit):
     src, defs, obj = unit
     out = os.path.join(BUILD, obj)
-    cmd = [HIPCC, *COMMON, *defs, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *COMMON, *defs, "-Rpass-analysis=kernel-resource-usage",
+           "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
+    # every kernel must fit in registers: a spilling instance is a build error
+    bad = _spilling_kernels(r.stderr)
+    if bad:
+        raise RuntimeError("%s: kernels spill registers:\n  %s" % (src, "\n  ".join(bad)))
     return out
 
 

@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
+#include <unordered_map>
 
 #include "ln_launch.hpp"
 
@@ -39,51 +41,119 @@ hipError_t launch_bwd(Dt dt, const Path& p, BwdMode mode, const BwdArgs& a, hipS
 int elems_per_slot(Dt dt) { return dt == Dt::F32 ? 4 : 8; }
 
 // Instances compiled in ln_fwd.hip / ln_bwd.hip.
-static bool have_instance(int g, int v) {
-    switch (g) {
-    case 16: case 32: return v == 1;
-    case 64: return v >= 1 && v <= 8;
-    case 128: case 256: case 512: return v == 4;
-    case 1024: return v == 4 || v == 8;
-    default: return false;
+static bool have_instance(bool f32, int g, int v) {
+#define MBROW_HAVE(GG, VV) if (g == GG && v == VV) return true;
+    if (f32) {
+        MBROW_LAYOUTS_F32(MBROW_HAVE)
+    } else {
+        MBROW_LAYOUTS_16(MBROW_HAVE)
     }
+#undef MBROW_HAVE
+    return false;
 }
 
-static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0};
+static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0}, g_force_grid{0};
 
-Path pick_path(Dt dt, int64_t cols, bool vec) {
-    const int E = elems_per_slot(dt);
-    const int64_t ns = (cols + E - 1) / E;
+// Row layout: among the candidate layouts, the one with the fewest unused
+// slots; ties go to the earlier candidate.
+static Path pick(bool f32, int64_t ns, bool vec, const int (*prefer)[2], int nprefer,
+                 bool need_prefetch = false) {
     Path p;
     p.vec = vec && g_force_scalar.load(std::memory_order_relaxed) == 0;
     const int fg = g_force_g.load(std::memory_order_relaxed);
     const int fv = g_force_v.load(std::memory_order_relaxed);
-    if (fg > 0 && (int64_t)fg * fv >= ns) {
+    if (fg > 0 && (int64_t)fg * fv >= ns && have_instance(f32, fg, fv)) {
         p.g = fg;
         p.v = fv;
         return p;
     }
-    if (ns <= 16) {
-        p.g = 16; p.v = 1;
-    } else if (ns <= 32) {
-        p.g = 32; p.v = 1;
-    } else {
-        // One wave per row while each lane holds at most 32 values (8 fp32
-        // slots or 4 16-bit slots); wider rows spread over 2..16 waves.
-        const int64_t vmax = (E == 4) ? 8 : 4;
-        if (ns <= 64 * vmax) {
-            p.g = 64;
-            p.v = (int)((ns + 63) / 64);
-        } else if (ns <= 1024 * 4) {
-            p.g = 128;
-            while ((int64_t)p.g * 4 < ns) p.g *= 2;
-            p.v = 4;
-        } else {
-            p.g = 1024;
-            p.v = 8;
+    int64_t best = -1;
+    for (int k = 0; k < nprefer; ++k) {
+        const int64_t cap = (int64_t)prefer[k][0] * prefer[k][1];
+        if (cap < ns) continue;
+        if (need_prefetch && !bwd_prefetch(prefer[k][0], prefer[k][1], f32 ? 4 : 8, true))
+            continue;
+        const int64_t waste = cap - ns;
+        if (best < 0 || waste < best) {
+            best = waste;
+            p.g = prefer[k][0];
+            p.v = prefer[k][1];
         }
     }
+    if (best < 0) {
+        if (need_prefetch) return pick(f32, ns, vec, prefer, nprefer, false);
+        p.g = f32 ? 1024 : 512;   // wider than every layout: callers cap cols
+        p.v = 4;
+    }
     return p;
+}
+
+// Candidate layouts in order of preference for equal waste.  Within a wave a
+// lane holds at most 32 values of a row in the forward (8 fp32 or 4-5 16-bit
+// slots) and at most 40 in the backward, which also keeps two column
+// accumulators per value; wider rows spread over several waves.
+static const int kFwd32[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
+                                {32, 4}, {64, 3}, {32, 5}, {32, 6}, {64, 4}, {32, 7}, {32, 8},
+                                {64, 5}, {64, 6}, {64, 7}, {64, 8}, {128, 4}, {256, 4},
+                                {512, 4}, {1024, 4}};
+static const int kFwd16[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
+                                {32, 4}, {64, 3}, {32, 5}, {64, 4}, {128, 4}, {256, 4},
+                                {512, 4}};
+static const int kBwd32[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
+                                {32, 4}, {64, 3}, {32, 5}, {32, 6}, {64, 4}, {64, 5}, {64, 6},
+                                {128, 4}, {256, 4}, {512, 4}, {1024, 4}};
+static const int kBwd16[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
+                                {32, 4}, {64, 3}, {32, 5}, {128, 4}, {256, 4}, {512, 4}};
+
+#define MBROW_N(a) (int)(sizeof(a) / sizeof(a[0]))
+
+Path pick_path(Dt dt, int64_t cols, bool vec) {
+    const int E = elems_per_slot(dt);
+    const int64_t ns = (cols + E - 1) / E;
+    return E == 4 ? pick(true, ns, vec, kFwd32, MBROW_N(kFwd32))
+                  : pick(false, ns, vec, kFwd16, MBROW_N(kFwd16));
+}
+
+// With column partials, a layout that can double-buffer its rows beside the
+// accumulators wins over one that wastes fewer slots; the partials-only pass
+// makes the same choice, so both accumulate in the same order.
+Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool partials) {
+    const int E = elems_per_slot(dt);
+    const int64_t ns = (cols + E - 1) / E;
+    return E == 4 ? pick(true, ns, vec, kBwd32, MBROW_N(kBwd32), partials)
+                  : pick(false, ns, vec, kBwd16, MBROW_N(kBwd16), partials);
+}
+
+int64_t persistent_grid(const void* kernel, int threads, int64_t blocks) {
+    const int forced = g_force_grid.load(std::memory_order_relaxed);
+    if (forced < 0) return blocks;
+    static std::mutex mu;
+    static std::unordered_map<const void*, int> per_cu;   // resident workgroups per CU
+    static int cus = 0;
+    int n = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (cus == 0) {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                    hipSuccess || cus <= 0)
+                cus = 0;
+        }
+        auto it = per_cu.find(kernel);
+        if (it == per_cu.end()) {
+            int b = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, threads, 0) !=
+                    hipSuccess || b <= 0)
+                b = 0;
+            it = per_cu.emplace(kernel, b).first;
+        }
+        n = it->second;
+    }
+    if (cus <= 0 || n <= 0) return blocks;   // unknown: one workgroup per block
+    const int64_t per = forced > 0 ? forced : n;
+    const int64_t g = (int64_t)cus * per;
+    return g < blocks ? g : blocks;
 }
 
 int64_t bwd_partitions(int64_t rows, int64_t cols) {
@@ -104,7 +174,7 @@ bool valid_dtype(ln_dtype_t dt) { return dt == LN_F32 || dt == LN_F16 || dt == L
 
 size_t elem_bytes(ln_dtype_t dt) { return dt == LN_F32 ? 4 : 2; }
 
-int64_t max_cols(ln_dtype_t dt) { return dt == LN_F32 ? LN_MAX_COLS_F32 : LN_MAX_COLS_16BIT; }
+int64_t max_cols(ln_dtype_t) { return LN_MAX_COLS; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -194,6 +264,7 @@ ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, 
     a.rows = rows; a.m = cols;
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.eps = eps;
+    a.inv_m = (float)(1.0 / (double)cols);
     return from_hip(launch_fwd(d, pick_path(d, cols, vec), false, a, stream));
 }
 
@@ -228,6 +299,7 @@ ln_status_t bias_dropout_residual_ln_fwd(const void* x, const void* bias, const 
     a.rows = rows; a.m = cols;
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.eps = eps;
+    a.inv_m = (float)(1.0 / (double)cols);
     a.thr = (uint32_t)std::floor((double)p * 65536.0 + 0.5);
     a.scale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
@@ -264,7 +336,8 @@ ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const fl
     a.parts = bwd_partitions(rows, cols);
     a.inv_m = (float)(1.0 / (double)cols);
     const BwdMode mode = workspace ? BwdMode::DX_PARTIALS : BwdMode::DX;
-    return from_hip(launch_bwd(d, pick_path(d, cols, vec), mode, a, stream));
+    return from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec, workspace != nullptr), mode, a,
+                               stream));
 }
 
 ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean,
@@ -298,14 +371,21 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
         a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
         a.parts = parts;
         a.inv_m = (float)(1.0 / (double)cols);
-        st = from_hip(launch_bwd(d, pick_path(d, cols, vec), BwdMode::PARTIALS, a, stream));
+        st = from_hip(
+            launch_bwd(d, pick_bwd_path(d, cols, vec, true), BwdMode::PARTIALS, a, stream));
         if (st != LN_OK) return st;
     }
     return from_hip(launch_fold(workspace, parts, cols, dgamma, dbeta, stream));
 }
 
+ln_status_t ln_debug_force_grid(int workgroups_per_cu) {
+    g_force_grid.store(workgroups_per_cu, std::memory_order_relaxed);
+    return LN_OK;
+}
+
 ln_status_t ln_debug_force_path(int lanes_per_row, int slots_per_lane, int scalar) {
-    if (lanes_per_row != 0 && !have_instance(lanes_per_row, slots_per_lane))
+    if (lanes_per_row != 0 && !have_instance(true, lanes_per_row, slots_per_lane) &&
+        !have_instance(false, lanes_per_row, slots_per_lane))
         return LN_ERR_UNSUPPORTED;
     g_force_g.store(lanes_per_row, std::memory_order_relaxed);
     g_force_v.store(lanes_per_row ? slots_per_lane : 0, std::memory_order_relaxed);

@@ -37,7 +37,7 @@ using St = StBF16;
 
 template <int G>
 struct BwdGeometry {
-    static constexpr int NT = G <= 512 ? 512 : G;    // threads per workgroup (multiple of G)
+    static constexpr int NT = bwd_threads(G);        // threads per workgroup (multiple of G)
     static constexpr int NG = NT / G;                // row groups per workgroup
     static constexpr int NW = NT / 64;               // waves per workgroup
     static constexpr int WPR = G > 64 ? G / 64 : 1;  // waves per row
@@ -49,12 +49,16 @@ struct BwdGeometry {
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+template <int V>
+struct BwdRowBuf {
+    u32x4 x[V], d[V];
+    float mu, rs;
+};
+
 template <class S, int G, int V, bool VEC, int MODE>
 __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     constexpr int E = S::E;
-    constexpr int NT = BwdGeometry<G>::NT;
     constexpr int NG = BwdGeometry<G>::NG;
-    constexpr int NW = BwdGeometry<G>::NW;
     constexpr int WPR = BwdGeometry<G>::WPR;
     constexpr int NU = BwdGeometry<G>::NU;
     constexpr int UT = BwdGeometry<G>::UT;
@@ -62,23 +66,22 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     constexpr bool PART = MODE != (int)BwdMode::DX;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
     const int lg = tid % G;
     const int grp = tid / G;
+    const int m = (int)a.m;
+    const int nslots = (int)a.nslots;
 
     const int64_t part = blockIdx.x;
     const int64_t r0 = part * a.rows / a.parts;
     const int64_t r1 = (part + 1) * a.rows / a.parts;
 
+    // slot i of this lane covers columns (i*G + lg)*E .. +E-1
     bool ok[V];
-    int64_t col0[V];
-    float ga[V][E];
+    u32x4 gp[V];   // gamma, packed in T
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const int64_t s = (int64_t)i * G + lg;
-        ok[i] = s < a.nslots;
-        col0[i] = s * E;
-        if constexpr (DX) load_slot<S, VEC, false>(a.gamma, 0, col0[i], a.m, ok[i], ga[i]);
+        ok[i] = i * G + lg < nslots;
+        if constexpr (DX) gp[i] = load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
     }
     float acc_g[V][E], acc_b[V][E];
     if constexpr (PART) {
@@ -89,37 +92,63 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     }
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
-    // Every row group runs the same number of iterations (a row past the
-    // partition end is skipped but still takes part in the barriers of a
-    // multi-wave row).
-    int it = 0;
-    for (int64_t base = r0; base < r1; base += NG, ++it) {
+    auto load_row = [&](BwdRowBuf<V>& b, int64_t base) {
         const int64_t row = base + grp;
-        const bool row_ok = row < r1;
-        const int64_t roff = row_ok ? row * a.m : 0;
-        float x[V][E], d[V][E];
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            load_slot<S, VEC, true>(a.dy, roff, col0[i], a.m, ok[i] && row_ok, d[i]);
-            load_slot<S, VEC, true>(a.x, roff, col0[i], a.m, ok[i] && row_ok, x[i]);
-        }
-        const float mu = row_ok ? a.mean[row] : 0.0f;
-        const float rs = row_ok ? a.rstd[row] : 0.0f;
-        float xh[V][E];
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-#pragma unroll
-            for (int e = 0; e < E; ++e) xh[i][e] = (x[i][e] - mu) * rs;
-        if constexpr (DX) {
-            float A = 0.0f, B = 0.0f;
-            float g[V][E];
+        const bool rok = row < r1;
+        const int64_t r = rok ? row : 0;
+        if constexpr (VEC) {
+            const u32x4* pd = lane_slots<S>(a.dy, r, m, lg);
+            const u32x4* px = lane_slots<S>(a.x, r, m, lg);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
+                b.d[i] = nt_load(pd + i * G, ok[i] && rok);
+                b.x[i] = nt_load(px + i * G, ok[i] && rok);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                load_elems<S>(a.dy, r, m, (i * G + lg) * E, ok[i] && rok, f);
+                b.d[i] = S::pack(f);
+                load_elems<S>(a.x, r, m, (i * G + lg) * E, ok[i] && rok, f);
+                b.x[i] = S::pack(f);
+            }
+        }
+        b.mu = rok ? a.mean[row] : 0.0f;
+        b.rs = rok ? a.rstd[row] : 0.0f;
+    };
+
+    // Pass 1 forms x-hat and g slot by slot from the packed row and
+    // accumulates the two row sums; pass 2 forms them again for dx (and the
+    // column partials) instead of keeping them in registers.  The partials
+    // use the same expressions in every mode, so the fused and the
+    // partials-only passes produce the same bits.
+    auto process = [&](const BwdRowBuf<V>& b, int64_t base, int it) {
+        const int64_t row = base + grp;
+        const bool rok = row < r1;
+        const int64_t r = rok ? row : 0;
+        const float mu = b.mu, rs = b.rs;
+        if constexpr (DX) keep_packed(gp);
+        u32x4 xr[V], dr[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            xr[i] = b.x[i];
+            dr[i] = b.d[i];
+        }
+        if constexpr (DX) {
+            float A = 0.0f, B = 0.0f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float x[E], d[E], ga[E];
+                S::unpack(xr[i], x);
+                S::unpack(dr[i], d);
+                S::unpack(gp[i], ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    g[i][e] = ga[i][e] * d[i][e];   // zero outside the row
-                    A += g[i][e];
-                    B = fmaf(g[i][e], xh[i][e], B);
+                    const float xh = (x[e] - mu) * rs;
+                    const float g = ga[e] * d[e];   // zero outside the row
+                    A += g;
+                    B = fmaf(g, xh, B);
                 }
             }
             if constexpr (G <= 64) {
@@ -143,26 +172,82 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                     B += red[buf][grp][k][1];
                 }
             }
+            keep_packed(xr);
+            keep_packed(dr);
+            keep_packed(gp);
+            u32x4* pdx = VEC ? lane_slots<S>(a.dx, r, m, lg) : nullptr;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                float out[E];
+                float x[E], d[E], ga[E], out[E];
+                S::unpack(xr[i], x);
+                S::unpack(dr[i], d);
+                S::unpack(gp[i], ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float t = fmaf(xh[i][e], B, A) * a.inv_m;
-                    out[e] = rs * (g[i][e] - t);
+                    const float xh = (x[e] - mu) * rs;
+                    const float g = ga[e] * d[e];
+                    const float t = fmaf(xh, B, A) * a.inv_m;
+                    out[e] = rs * (g - t);
+                    if constexpr (PART) {
+                        acc_g[i][e] = fmaf(d[e], xh, acc_g[i][e]);
+                        acc_b[i][e] = acc_b[i][e] + d[e];
+                    }
                 }
-                store_slot<S, VEC, true>(a.dx, roff, col0[i], a.m, ok[i] && row_ok, out);
+                if constexpr (VEC) {
+                    if (ok[i] && rok) __builtin_nontemporal_store(S::pack(out), pdx + i * G);
+                } else {
+                    store_elems<S>(a.dx, r, m, (i * G + lg) * E, ok[i] && rok, out);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float x[E], d[E];
+                S::unpack(xr[i], x);
+                S::unpack(dr[i], d);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float xh = (x[e] - mu) * rs;
+                    acc_g[i][e] = fmaf(d[e], xh, acc_g[i][e]);
+                    acc_b[i][e] = acc_b[i][e] + d[e];
+                }
             }
         }
-        if constexpr (PART) {
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    acc_g[i][e] = fmaf(d[i][e], xh[i][e], acc_g[i][e]);
-                    acc_b[i][e] = acc_b[i][e] + d[i][e];
-                }
-            }
+    };
+
+    // Walk over the partition's rows, double-buffered: the next rows' loads
+    // are issued before the current rows are reduced, so each wave keeps
+    // memory busy while it computes.  Every row group runs the same number
+    // of iterations (a row past the partition end is skipped but still takes
+    // part in the barriers of a multi-wave row), and each lane sees its rows
+    // in ascending order, so the column partials are summed in a fixed order.
+    int64_t base = r0;
+    int it = 0;
+    // Prefetch needs a second row buffer; without room for it beside the
+    // column accumulators the walk is single-buffered.
+    constexpr bool PF = bwd_prefetch(G, V, E, PART);
+    if constexpr (PF) {
+        BwdRowBuf<V> b0, b1;
+        if (base < r1) load_row(b0, base);
+        while (base < r1) {
+            int64_t nxt = base + NG;
+            if (nxt < r1) load_row(b1, nxt);
+            process(b0, base, it++);
+            base = nxt;
+            if (base >= r1) break;
+            nxt = base + NG;
+            if (nxt < r1) load_row(b0, nxt);
+            process(b1, base, it++);
+            base = nxt;
+        }
+    } else {
+        // single buffer: 1024-lane rows (16 waves per row already keep loads
+        // in flight and the 128-VGPR budget has no room for a second
+        // buffer), and lanes with many column accumulators
+        BwdRowBuf<V> b0;
+        for (; base < r1; base += NG) {
+            load_row(b0, base);
+            process(b0, base, it++);
         }
     }
 
@@ -182,50 +267,62 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 }
             }
         }
-        // Fold the units (waves, or multi-wave row groups) through LDS in a
-        // fixed tree, one slot at a time to bound the LDS footprint: at each
-        // level unit u + h hands its sums to unit u.
+        // Fold the units (waves, or multi-wave row groups) whose lanes own the
+        // same columns: every unit writes its sums to LDS, one barrier, then
+        // the whole workgroup adds them in unit order (0, 1, ...) and writes
+        // the workgroup's partial.  Slots go through LDS in chunks of CH so
+        // the footprint stays at 64 KB.
+        constexpr int CH = (NU * 2 * E * UT * 4 <= 65536) ? ((65536 / (NU * 2 * E * UT * 4)) < V ? (65536 / (NU * 2 * E * UT * 4)) : V) : 1;
         const int unit = tid / UT;
         const int pos = tid % UT;
-        if constexpr (NU > 1) {
-            __shared__ float tree[NU / 2][2][E][UT];
+        float* pg = a.ws + (part * 2 + 0) * a.m;
+        float* pb = a.ws + (part * 2 + 1) * a.m;
+        if constexpr (NU == 1) {
+            // one unit: each lane writes its own columns
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-#pragma unroll
-                for (int h = NU / 2; h >= 1; h /= 2) {
-                    if (unit >= h && unit < 2 * h) {
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            tree[unit - h][0][e][pos] = acc_g[i][e];
-                            tree[unit - h][1][e][pos] = acc_b[i][e];
-                        }
-                    }
-                    __syncthreads();
-                    if (unit < h) {
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            acc_g[i][e] = acc_g[i][e] + tree[unit][0][e][pos];
-                            acc_b[i][e] = acc_b[i][e] + tree[unit][1][e][pos];
-                        }
-                    }
-                    __syncthreads();
-                }
-            }
-        }
-        // Unit 0 holds the workgroup's partial; for G < 64 its first row
-        // group writes it.
-        const bool writer = (G <= 64) ? (tid < G) : (unit == 0);
-        if (writer) {
-            float* pg = a.ws + (part * 2 + 0) * a.m;
-            float* pb = a.ws + (part * 2 + 1) * a.m;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                if (!ok[i]) continue;
+                const int col0 = (i * G + lg) * E;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    if (col0[i] + e < a.m) {
-                        pg[col0[i] + e] = acc_g[i][e];
-                        pb[col0[i] + e] = acc_b[i][e];
+                    if (ok[i] && col0 + e < m) {
+                        pg[col0 + e] = acc_g[i][e];
+                        pb[col0 + e] = acc_b[i][e];
+                    }
+                }
+            }
+        } else {
+            __shared__ float stage[NU][2][CH * E][UT];
+            // positions of one chunk: (kind, value k of the chunk, lane pos)
+            constexpr int NPOS = 2 * CH * E * UT;
+#pragma unroll
+            for (int i0 = 0; i0 < V; i0 += CH) {
+                if (i0 > 0) __syncthreads();   // previous chunk fully read
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    if (i0 + c < V) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            stage[unit][0][c * E + e][pos] = acc_g[i0 + c][e];
+                            stage[unit][1][c * E + e][pos] = acc_b[i0 + c][e];
+                        }
+                    }
+                }
+                __syncthreads();
+                for (int q = tid; q < NPOS; q += BwdGeometry<G>::NT) {
+                    const int p = q % UT;
+                    const int k = (q / UT) % (CH * E);
+                    const int kind = q / (UT * CH * E);
+                    const int i = i0 + k / E;
+                    const int e = k % E;
+                    // lane p of a unit owns slot i*G + p (G <= 64: p < G is
+                    // one row group's copy; larger p are duplicates)
+                    const int s = i * G + p;
+                    const int col = s * E + e;
+                    if (i < V && (G > 64 || p < G) && s < nslots && col < m) {
+                        float t = stage[0][kind][k][p];
+#pragma unroll
+                        for (int u = 1; u < NU; ++u) t = t + stage[u][kind][k][p];
+                        (kind == 0 ? pg : pb)[col] = t;
                     }
                 }
             }
@@ -244,21 +341,11 @@ template <bool VEC, int MODE>
 static hipError_t dispatch(const Path& p, const BwdArgs& a, hipStream_t s) {
 #define MBROW_CASE(GG, VV) \
     if (p.g == GG && p.v == VV) return launch_one<GG, VV, VEC, MODE>(a, s);
-    MBROW_CASE(16, 1)
-    MBROW_CASE(32, 1)
-    MBROW_CASE(64, 1)
-    MBROW_CASE(64, 2)
-    MBROW_CASE(64, 3)
-    MBROW_CASE(64, 4)
-    MBROW_CASE(64, 5)
-    MBROW_CASE(64, 6)
-    MBROW_CASE(64, 7)
-    MBROW_CASE(64, 8)
-    MBROW_CASE(128, 4)
-    MBROW_CASE(256, 4)
-    MBROW_CASE(512, 4)
-    MBROW_CASE(1024, 4)
-    MBROW_CASE(1024, 8)
+#if MBROW_DT == 0
+    MBROW_LAYOUTS_F32(MBROW_CASE)
+#else
+    MBROW_LAYOUTS_16(MBROW_CASE)
+#endif
 #undef MBROW_CASE
     return hipErrorInvalidValue;
 }

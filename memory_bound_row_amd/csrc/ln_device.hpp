@@ -122,46 +122,68 @@ struct StF16 {
 
 // ---------------------------------------------------------------------------
 // Slot access.  VEC: one 16-byte access per slot (row starts 16-byte
-// aligned, cols*sizeof(T) a multiple of 16).  Otherwise one access per
-// element, each predicated on its column.  Streaming tensors use
-// nontemporal accesses; gamma/beta/bias (re-read by every row) do not.
+// aligned, cols*sizeof(T) a multiple of 16); a lane keeps one pointer to its
+// first slot of the row and reaches slot i at the constant offset i*G*16
+// bytes, which the load/store instruction folds into its immediate.
+// Otherwise one access per element, each predicated on its column.
+// Streaming tensors use nontemporal accesses; gamma/beta/bias (re-read by
+// every row) use ordinary cached loads.
 // ---------------------------------------------------------------------------
-template <class S, bool VEC, bool NT>
-__device__ inline void load_slot(const void* base, int64_t row_off, int64_t col0,
-                                 int64_t m, bool valid, float* f) {
+template <class S>
+__device__ __forceinline__ const u32x4* lane_slots(const void* base, int64_t row, int m,
+                                                   int lg) {
+    return reinterpret_cast<const u32x4*>(static_cast<const char*>(base) +
+                                          row * (int64_t)m * S::BYTES) + lg;
+}
+template <class S>
+__device__ __forceinline__ u32x4* lane_slots(void* base, int64_t row, int m, int lg) {
+    return reinterpret_cast<u32x4*>(static_cast<char*>(base) + row * (int64_t)m * S::BYTES) + lg;
+}
+
+__device__ __forceinline__ u32x4 nt_load(const u32x4* p, bool ok) {
+    return ok ? __builtin_nontemporal_load(p) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Per-element path: E elements of row `row` starting at column col0 (< m
+// checked per element), unpacked to float; outside the row reads as 0.
+template <class S>
+__device__ inline void load_elems(const void* base, int64_t row, int m, int col0, bool ok,
+                                  float* f) {
+    const int64_t off = row * (int64_t)m;
+#pragma unroll
+    for (int e = 0; e < S::E; ++e) f[e] = (ok && col0 + e < m) ? S::load1(base, off + col0 + e) : 0.0f;
+}
+template <class S>
+__device__ inline void store_elems(void* base, int64_t row, int m, int col0, bool ok,
+                                   const float* f) {
+    const int64_t off = row * (int64_t)m;
+#pragma unroll
+    for (int e = 0; e < S::E; ++e)
+        if (ok && col0 + e < m) S::store1(base, off + col0 + e, f[e]);
+}
+
+// One slot of a [cols] parameter vector, packed in T (cached load).
+template <class S, bool VEC>
+__device__ __forceinline__ u32x4 load_param(const void* base, int s, int m, bool ok) {
     if constexpr (VEC) {
-        if (valid) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(
-                static_cast<const char*>(base) + (row_off + col0) * S::BYTES);
-            u32x4 v;
-            if constexpr (NT) v = __builtin_nontemporal_load(p);
-            else v = *p;
-            S::unpack(v, f);
-        } else {
-#pragma unroll
-            for (int e = 0; e < S::E; ++e) f[e] = 0.0f;
-        }
+        return ok ? reinterpret_cast<const u32x4*>(base)[s] : u32x4{0u, 0u, 0u, 0u};
     } else {
-#pragma unroll
-        for (int e = 0; e < S::E; ++e)
-            f[e] = (valid && col0 + e < m) ? S::load1(base, row_off + col0 + e) : 0.0f;
+        float f[S::E];
+        load_elems<S>(base, 0, m, s * S::E, ok, f);
+        return S::pack(f);   // exact: the values are representable in T
     }
 }
 
-template <class S, bool VEC, bool NT>
-__device__ inline void store_slot(void* base, int64_t row_off, int64_t col0, int64_t m,
-                                  bool valid, const float* f) {
-    if (!valid) return;
-    if constexpr (VEC) {
-        u32x4* p = reinterpret_cast<u32x4*>(static_cast<char*>(base) +
-                                            (row_off + col0) * S::BYTES);
-        u32x4 v = S::pack(f);
-        if constexpr (NT) __builtin_nontemporal_store(v, p);
-        else *p = v;
-    } else {
+// Keep a packed register array packed: the empty asm tells the compiler the
+// values may have changed, so unpacking them is not hoisted out of a loop
+// (which would hold the unpacked floats, twice the registers, across it).
+template <int N>
+__device__ __forceinline__ void keep_packed(u32x4 (&v)[N]) {
 #pragma unroll
-        for (int e = 0; e < S::E; ++e)
-            if (col0 + e < m) S::store1(base, row_off + col0 + e, f[e]);
+    for (int i = 0; i < N; ++i) {
+        uint32_t a0 = v[i][0], a1 = v[i][1], a2 = v[i][2], a3 = v[i][3];
+        asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+        v[i] = u32x4{a0, a1, a2, a3};
     }
 }
 
@@ -314,11 +336,11 @@ __device__ inline u32x4 philox4x32_10(u32x4 ctr, uint32_t k0, uint32_t k1) {
 // >= thr.  Counter (col >> 3, row lo, row hi, 0); key (seed lo, seed hi);
 // column k = col & 7 of the group takes half (k & 1) of word k >> 1.
 template <int E>
-__device__ inline uint32_t keep_bits(int64_t row, int64_t col0, uint32_t seed_lo,
+__device__ inline uint32_t keep_bits(int64_t row, int col0, uint32_t seed_lo,
                                      uint32_t seed_hi, uint32_t thr) {
     if (thr == 0u) return (1u << E) - 1u;  // u >= 0 always: keep every column
     u32x4 c;
-    c[0] = (uint32_t)((uint64_t)col0 >> 3);
+    c[0] = (uint32_t)col0 >> 3;
     c[1] = (uint32_t)((uint64_t)row & 0xffffffffu);
     c[2] = (uint32_t)((uint64_t)row >> 32);
     c[3] = 0u;

@@ -2,21 +2,28 @@
 // LayerNorm forward for gfx950.  Compiled once per storage type
 // (-DMBROW_DT=0 fp32, 1 fp16, 2 bf16).
 //
-// One row is owned by a group of G lanes: G <= 64 lanes of one wave
-// (64/G rows per wave), or G/64 waves of one workgroup.  Lane l of a group
-// owns the 16-byte slots l, l+G, l+2G, ... of the row, so consecutive lanes
-// touch consecutive 16 bytes and every load and store of a wave is fully
-// coalesced ("AI infra 学习记录(2)" §2.4: 16-byte accesses cut instructions,
-// not bytes).  The whole row stays in VGPRs between the statistics and the
-// affine pass, so HBM is read once and written once ("AI infra 学习记录(2)"
-// §4: keep x on chip instead of reading it twice).
+// Layout.  One row is owned by a group of G lanes: G <= 64 lanes of one wave
+// (64/G rows per wave) or G/64 waves of one workgroup.  Lane l of a group owns
+// the 16-byte slots l, l+G, l+2G, ... of the row, so consecutive lanes touch
+// consecutive 16 bytes and every wave-wide load and store is fully coalesced
+// ("AI infra 学习记录(2)" §2.4: 16-byte accesses cut instructions, not bytes).
+// The whole row stays in VGPRs between the statistics and the affine pass,
+// so HBM is read once and written once ("AI infra 学习记录(2)" §4).
 //
-// Statistics take one reduction ("Accelerating Transformer on GPU (I)"
-// §4.2: one synchronisation instead of two, without the cancellation of
-// E[x^2] - E[x]^2): every lane reduces its own values exactly in registers
-// to (count, shifted sum, M2), then the group merges those states with the
-// Chan update through DPP / swizzle / readlane; a multi-wave row adds one LDS
-// exchange and one barrier.
+// Schedule.  The grid is persistent (about as many workgroups as fit on the
+// chip at once); each workgroup walks row blocks with a stride of the grid
+// and double-buffers them: the loads of the next block are issued before the
+// current block is reduced and written, so memory traffic and ALU work of
+// each wave overlap.
+//
+// Statistics ("Accelerating Transformer on GPU (I)" §4.2).  Values are
+// shifted by the first value c of the group's part of the row, so sums stay
+// small when the mean is large compared with the spread (the page's
+// E[x^2] - E[x]^2 collapse at mean 1e4).  Within a wave the mean and then the
+// sum of squared deviations are exact two-pass sums over registers, each
+// reduced by one DPP/swizzle butterfly with no barrier.  A multi-wave row
+// merges the per-wave (count, sum, M2) states with the Chan update after one
+// LDS exchange, so it takes a single barrier.
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 
@@ -40,164 +47,254 @@ using St = StBF16;
 template <int G>
 struct Geometry {
     static constexpr int NT = G <= 256 ? 256 : G;   // threads per workgroup
-    static constexpr int ROWS = NT / G;              // rows per workgroup
+    static constexpr int ROWS = NT / G;              // rows per block
     static constexpr int WPR = G > 64 ? G / 64 : 1;  // waves per row
+};
+
+// Raw 16-byte slots of one row of the streaming inputs.
+template <int V, bool FUSED>
+struct RowBuf {
+    u32x4 x[V];
+    u32x4 r[FUSED ? V : 1];
 };
 
 template <class S, int G, int V, bool VEC, bool FUSED>
 __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
     constexpr int E = S::E;
-    constexpr int NT = Geometry<G>::NT;
     constexpr int ROWS = Geometry<G>::ROWS;
     constexpr int WPR = Geometry<G>::WPR;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int lg = tid % G;
     const int rloc = tid / G;
-    const int64_t row = (int64_t)blockIdx.x * ROWS + rloc;
-    const bool row_ok = row < a.rows;
-    const int64_t roff = row_ok ? row * a.m : 0;
+    const int m = (int)a.m;
+    const int nslots = (int)a.nslots;
+    const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
 
-    float v[V][E];      // the values being normalised (x, or the stored z)
-    float ga[V][E], be[V][E];
+    // slot i of this lane covers columns (i*G + lg)*E .. +E-1
     bool ok[V];
-    int64_t col0[V];
+    // gamma, beta, bias stay packed in T and are unpacked where used
+    u32x4 gp[V], bp[V], bip[FUSED ? V : 1];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const int64_t s = (int64_t)i * G + lg;
-        ok[i] = row_ok && s < a.nslots;
-        col0[i] = s * E;
-        load_slot<S, VEC, true>(a.x, roff, col0[i], a.m, ok[i], v[i]);
+        const int s = i * G + lg;
+        ok[i] = s < nslots;
+        gp[i] = load_param<S, VEC>(a.gamma, s, m, ok[i]);
+        bp[i] = load_param<S, VEC>(a.beta, s, m, ok[i]);
+        if constexpr (FUSED) bip[i] = load_param<S, VEC>(a.bias, s, m, ok[i]);
     }
-    if constexpr (FUSED) {
-        float r[V][E], b[V][E];
+
+    auto load_row = [&](RowBuf<V, FUSED>& b, int64_t blk) {
+        const int64_t row = blk * ROWS + rloc;
+        const bool rok = row < a.rows;
+        const int64_t r = rok ? row : 0;
+        if constexpr (VEC) {
+            const u32x4* px = lane_slots<S>(a.x, r, m, lg);
+            const u32x4* pr = FUSED ? lane_slots<S>(a.residual, r, m, lg) : nullptr;
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            load_slot<S, VEC, true>(a.residual, roff, col0[i], a.m, ok[i], r[i]);
-            load_slot<S, VEC, false>(a.bias, 0, col0[i], a.m, ok[i], b[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            if (!ok[i]) continue;
-            const uint32_t bits = keep_bits<E>(row, col0[i], a.seed_lo, a.seed_hi, a.thr);
-            float z[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float t = v[i][e] + b[i][e];
-                const float d = ((bits >> e) & 1u) ? t * a.scale : 0.0f;
-                z[e] = r[i][e] + d;
+            for (int i = 0; i < V; ++i) {
+                b.x[i] = nt_load(px + i * G, ok[i] && rok);
+                if constexpr (FUSED) b.r[i] = nt_load(pr + i * G, ok[i] && rok);
             }
-            // z is stored in T; the LayerNorm runs on the stored value.
-            if constexpr (VEC) {
-                u32x4 zp = S::pack(z);
-                u32x4* p = reinterpret_cast<u32x4*>(static_cast<char*>(a.residual_out) +
-                                                    (roff + col0[i]) * S::BYTES);
-                __builtin_nontemporal_store(zp, p);
-                S::unpack(zp, v[i]);
-            } else {
+        } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    v[i][e] = S::round(z[e]);
-                    if (col0[i] + e < a.m) S::store1(a.residual_out, roff + col0[i] + e, z[e]);
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                load_elems<S>(a.x, r, m, (i * G + lg) * E, ok[i] && rok, f);
+                b.x[i] = S::pack(f);
+                if constexpr (FUSED) {
+                    load_elems<S>(a.residual, r, m, (i * G + lg) * E, ok[i] && rok, f);
+                    b.r[i] = S::pack(f);
                 }
             }
-            if (a.mask_out) {
+        }
+    };
+
+    __shared__ float lds[2][ROWS][WPR][4];
+
+    // The row is kept packed in T (16-bit types: half the registers) and
+    // unpacked again by each pass over it.
+    auto process = [&](const RowBuf<V, FUSED>& b, int64_t blk, int it) {
+        const int64_t row = blk * ROWS + rloc;
+        const bool rok = row < a.rows;
+        const int64_t r = rok ? row : 0;
+        keep_packed(gp);
+        keep_packed(bp);
+        u32x4 zp[V];   // the values being normalised, packed (x, or the stored z)
+        if constexpr (FUSED) {
+            keep_packed(bip);
+            u32x4* pz = VEC ? lane_slots<S>(a.residual_out, r, m, lg) : nullptr;
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (col0[i] + e < a.m)
-                        a.mask_out[roff + col0[i] + e] = (uint8_t)((bits >> e) & 1u);
+            for (int i = 0; i < V; ++i) {
+                const bool sok = ok[i] && rok;
+                const int col0 = (i * G + lg) * E;
+                float xv[E], rv[E], bv[E];
+                S::unpack(b.x[i], xv);
+                S::unpack(b.r[i], rv);
+                S::unpack(bip[i], bv);
+                const uint32_t bits = sok ? keep_bits<E>(row, col0, a.seed_lo, a.seed_hi, a.thr) : 0u;
+                float z[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float t = xv[e] + bv[e];
+                    const float d = ((bits >> e) & 1u) ? t * a.scale : 0.0f;
+                    z[e] = rv[e] + d;
+                }
+                // z is stored in T; the LayerNorm runs on the stored value.
+                zp[i] = S::pack(z);
+                if constexpr (VEC) {
+                    if (sok) __builtin_nontemporal_store(zp[i], pz + i * G);
+                } else {
+                    store_elems<S>(a.residual_out, r, m, col0, sok, z);
+                }
+                if (a.mask_out && sok) {
+                    const int64_t off = r * (int64_t)m;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (col0 + e < m) a.mask_out[off + col0 + e] = (uint8_t)((bits >> e) & 1u);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) zp[i] = b.x[i];
+        }
+        // element e of slot i lies in the row
+        auto inside = [&](int i, int e) { return ok[i] && (VEC || (i * G + lg) * E + e < m); };
+
+        // shift: first value of this wave's part of the row
+        float first[E];
+        S::unpack(zp[0], first);
+        const float c = (G <= 64) ? group_broadcast_first<(G <= 64 ? G : 64)>(first[0], lane)
+                                  : lane_read(first[0], 0);
+        // pass 1: sum of shifted values (elements outside the row contribute 0)
+        keep_packed(zp);
+        float s_l = 0.0f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float v[E];
+            S::unpack(zp[i], v);
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_l += inside(i, e) ? v[e] - c : 0.0f;
+        }
+        // pass 2: sum of squared deviations from a mean m_l
+        auto sq_dev = [&](float m_l) {
+            keep_packed(zp);
+            float q_l = 0.0f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float v[E];
+                S::unpack(zp[i], v);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = inside(i, e) ? (v[e] - c) - m_l : 0.0f;
+                    q_l = fmaf(d, d, q_l);
+                }
+            }
+            return q_l;
+        };
+        float mu, var;   // mean of (v - c) for this wave's shift, variance
+        if constexpr (G <= 64) {
+            mu = group_sum<G>(s_l) * a.inv_m;
+            var = group_sum<G>(sq_dev(mu)) * a.inv_m;
+        } else {
+            // this wave's exact state, then one exchange and a fixed-order
+            // Chan merge (wave 0, 1, ...) done identically by every lane
+            float n_l = 0.0f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                if constexpr (VEC) {
+                    n_l += ok[i] ? (float)E : 0.0f;
+                } else {
+                    const int left = m - (i * G + lg) * E;
+                    n_l += ok[i] ? (float)(left < E ? left : E) : 0.0f;
+                }
+            }
+            const float n_w = group_sum<64>(n_l);
+            const float s_w = group_sum<64>(s_l);
+            const float mu_w = n_w > 0.0f ? s_w / n_w : 0.0f;
+            const float q_w = group_sum<64>(sq_dev(mu_w));
+            const int w = lg / 64;
+            const int buf = it & 1;   // double buffer: one barrier per block
+            if (lane == 0) {
+                lds[buf][rloc][w][0] = n_w;
+                lds[buf][rloc][w][1] = s_w;
+                lds[buf][rloc][w][2] = q_w;
+                lds[buf][rloc][w][3] = c;
+            }
+            __syncthreads();
+            const float c0 = lds[buf][rloc][0][3];
+            Stats tot{lds[buf][rloc][0][0], lds[buf][rloc][0][1], lds[buf][rloc][0][2]};
+#pragma unroll
+            for (int k = 1; k < WPR; ++k) {
+                Stats sk{lds[buf][rloc][k][0], lds[buf][rloc][k][1], lds[buf][rloc][k][2]};
+                tot = merge(tot, reshift(sk, lds[buf][rloc][k][3], c0));
+            }
+            // mean relative to this wave's own shift c
+            mu = tot.s / tot.n - (c - c0);
+            var = tot.q / tot.n;
+        }
+        const float rs = 1.0f / sqrtf(var + a.eps);
+        if (lg == 0 && rok) {
+            if (a.mean) a.mean[row] = c + mu;
+            if (a.rstd) a.rstd[row] = rs;
+        }
+        // pass 3: normalise and apply the affine map
+        keep_packed(zp);
+        u32x4* py = VEC ? lane_slots<S>(a.y, r, m, lg) : nullptr;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float v[E], ga[E], be[E], out[E];
+            S::unpack(zp[i], v);
+            S::unpack(gp[i], ga);
+            S::unpack(bp[i], be);
+#pragma unroll
+            for (int e = 0; e < E; ++e) out[e] = fmaf(((v[e] - c) - mu) * rs, ga[e], be[e]);
+            if constexpr (VEC) {
+                if (ok[i] && rok) __builtin_nontemporal_store(S::pack(out), py + i * G);
+            } else {
+                store_elems<S>(a.y, r, m, (i * G + lg) * E, ok[i] && rok, out);
             }
         }
-    }
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        load_slot<S, VEC, false>(a.gamma, 0, col0[i], a.m, ok[i], ga[i]);
-        load_slot<S, VEC, false>(a.beta, 0, col0[i], a.m, ok[i], be[i]);
-    }
+    };
 
-    // Shift: the first value of the wave's part of the row (lane 0 of the
-    // group, or of the wave for a multi-wave row), common to every lane that
-    // merges with it.
-    float c;
-    if constexpr (G <= 64) c = group_broadcast_first<G>(v[0][0], lane);
-    else c = lane_read(v[0][0], 0);
-
-    // This lane's exact local state: count, sum of (v - c), and M2 about its
-    // own mean (two passes over registers).
-    float n_l = 0.0f, s_l = 0.0f;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool in = ok[i] && (VEC || col0[i] + e < a.m);
-            if (in) {
-                n_l += 1.0f;
-                s_l += v[i][e] - c;
-            }
+    // Persistent walk over row blocks, uniform per workgroup so the barrier
+    // of a multi-wave row is reached by all.  Double-buffered (the next
+    // block's loads are in flight while this one is reduced) except for
+    // 1024-lane rows, whose 16 waves already keep enough loads in flight and
+    // whose 128-VGPR budget has no room for a second buffer.
+    int64_t blk = blockIdx.x;
+    const int64_t step = gridDim.x;
+    int it = 0;
+    if constexpr (Geometry<G>::NT <= 512) {
+        RowBuf<V, FUSED> b0, b1;
+        if (blk < nblk) load_row(b0, blk);
+        while (blk < nblk) {
+            int64_t nxt = blk + step;
+            if (nxt < nblk) load_row(b1, nxt);
+            process(b0, blk, it++);
+            blk = nxt;
+            if (blk >= nblk) break;
+            nxt = blk + step;
+            if (nxt < nblk) load_row(b0, nxt);
+            process(b1, blk, it++);
+            blk = nxt;
         }
-    }
-    const float mu_l = n_l > 0.0f ? s_l / n_l : 0.0f;
-    float q_l = 0.0f;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool in = ok[i] && (VEC || col0[i] + e < a.m);
-            const float d = (v[i][e] - c) - mu_l;
-            if (in) q_l = fmaf(d, d, q_l);
-        }
-    }
-    Stats st{n_l, s_l, q_l};
-    if constexpr (G <= 64) {
-        st = group_stats<G>(st);
     } else {
-        // One wave-level merge, then one LDS exchange between the WPR waves
-        // of the row and a fixed-order merge (wave 0, 1, ...) in every lane.
-        __shared__ float lds[ROWS][WPR][4];
-        st = group_stats<64>(st);
-        const int w = (tid % G) / 64;
-        if (lane == 0) {
-            lds[rloc][w][0] = st.n;
-            lds[rloc][w][1] = st.s;
-            lds[rloc][w][2] = st.q;
-            lds[rloc][w][3] = c;
+        RowBuf<V, FUSED> b0;
+        for (; blk < nblk; blk += step) {
+            load_row(b0, blk);
+            process(b0, blk, it++);
         }
-        __syncthreads();
-        const float c0 = lds[rloc][0][3];
-        Stats tot{lds[rloc][0][0], lds[rloc][0][1], lds[rloc][0][2]};
-#pragma unroll
-        for (int k = 1; k < WPR; ++k) {
-            Stats sk{lds[rloc][k][0], lds[rloc][k][1], lds[rloc][k][2]};
-            tot = merge(tot, reshift(sk, lds[rloc][k][3], c0));
-        }
-        st = tot;
-        c = c0;
-    }
-    const float mu_s = st.s / st.n;          // mean of (v - c)
-    const float var = st.q / st.n;
-    const float rs = 1.0f / sqrtf(var + a.eps);
-    if (lg == 0 && row_ok) {
-        if (a.mean) a.mean[row] = c + mu_s;
-        if (a.rstd) a.rstd[row] = rs;
-    }
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        float out[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float xh = ((v[i][e] - c) - mu_s) * rs;
-            out[e] = fmaf(xh, ga[i][e], be[i][e]);
-        }
-        store_slot<S, VEC, true>(a.y, roff, col0[i], a.m, ok[i], out);
     }
 }
 
 template <int G, int V, bool VEC, bool FUSED>
 static hipError_t launch_one(const FwdArgs& a, hipStream_t s) {
     using Geo = Geometry<G>;
-    const int64_t blocks = (a.rows + Geo::ROWS - 1) / Geo::ROWS;
-    hipLaunchKernelGGL((ln_fwd_kernel<St, G, V, VEC, FUSED>), dim3((unsigned)blocks),
-                       dim3(Geo::NT), 0, s, a);
+    auto kern = ln_fwd_kernel<St, G, V, VEC, FUSED>;
+    const int64_t nblk = (a.rows + Geo::ROWS - 1) / Geo::ROWS;
+    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), Geo::NT, nblk);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Geo::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -205,21 +302,11 @@ template <bool VEC, bool FUSED>
 static hipError_t dispatch(const Path& p, const FwdArgs& a, hipStream_t s) {
 #define MBROW_CASE(GG, VV) \
     if (p.g == GG && p.v == VV) return launch_one<GG, VV, VEC, FUSED>(a, s);
-    MBROW_CASE(16, 1)
-    MBROW_CASE(32, 1)
-    MBROW_CASE(64, 1)
-    MBROW_CASE(64, 2)
-    MBROW_CASE(64, 3)
-    MBROW_CASE(64, 4)
-    MBROW_CASE(64, 5)
-    MBROW_CASE(64, 6)
-    MBROW_CASE(64, 7)
-    MBROW_CASE(64, 8)
-    MBROW_CASE(128, 4)
-    MBROW_CASE(256, 4)
-    MBROW_CASE(512, 4)
-    MBROW_CASE(1024, 4)
-    MBROW_CASE(1024, 8)
+#if MBROW_DT == 0
+    MBROW_LAYOUTS_F32(MBROW_CASE)
+#else
+    MBROW_LAYOUTS_16(MBROW_CASE)
+#endif
 #undef MBROW_CASE
     return hipErrorInvalidValue;
 }

@@ -18,6 +18,21 @@ struct Path {
     bool vec = true;
 };
 
+// Row layouts compiled into the library, per storage size: (lanes per row,
+// 16-byte slots per lane).  Each list holds only layouts whose kernels fit in
+// registers without spilling (the build checks this); the widest covers
+// 16384 columns.
+#define MBROW_LAYOUTS_F32(X)                                                \
+    X(16, 1) X(16, 2) X(16, 4) X(16, 8)                                     \
+    X(32, 1) X(32, 2) X(32, 3) X(32, 4) X(32, 5) X(32, 6) X(32, 7) X(32, 8) \
+    X(64, 1) X(64, 2) X(64, 3) X(64, 4) X(64, 5) X(64, 6) X(64, 7) X(64, 8) \
+    X(128, 4) X(256, 4) X(512, 4) X(1024, 4)
+#define MBROW_LAYOUTS_16(X)                                                 \
+    X(16, 1) X(16, 2) X(16, 4)                                              \
+    X(32, 1) X(32, 2) X(32, 3) X(32, 4) X(32, 5)                            \
+    X(64, 1) X(64, 2) X(64, 3) X(64, 4) X(64, 5)                            \
+    X(128, 4) X(256, 4) X(512, 4)
+
 struct FwdArgs {
     const void* x;
     const void* bias;
@@ -33,6 +48,7 @@ struct FwdArgs {
     int64_t m;
     int64_t nslots;   // ceil(m / E)
     float eps;
+    float inv_m;      // 1 / m
     float scale;      // 1 / (1 - p)
     uint32_t thr;     // keep iff 16-bit uniform >= thr
     uint32_t seed_lo;
@@ -56,14 +72,30 @@ struct BwdArgs {
 
 enum class BwdMode : int { DX = 0, DX_PARTIALS = 1, PARTIALS = 2 };
 
+// Threads per workgroup of the backward for G lanes per row.
+constexpr int bwd_threads(int g) { return g <= 512 ? 512 : g; }
+
+// Whether the backward double-buffers its rows: the second row buffer
+// (V * 8 registers) must fit beside the column accumulators (2 per value when
+// partials are on) and packed gamma within an estimated 120 registers.
+constexpr bool bwd_prefetch(int g, int v, int e, bool partials) {
+    return bwd_threads(g) <= 512 && (partials ? 2 * v * e : 0) + 2 * v * 8 + v * 4 <= 120;
+}
+
 // Row partitions of the dgamma/dbeta stage-1 pass: a pure function of
 // (rows, cols).  Every partition owns at least one row.
 int64_t bwd_partitions(int64_t rows, int64_t cols);
 
 // Path selection from (dtype, cols, alignment); honours the test-only
 // override set through ln_debug_force_path.
-Path pick_path(Dt dt, int64_t cols, bool vec);
+Path pick_path(Dt dt, int64_t cols, bool vec);        // forward
+Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool partials);   // backward
 int elems_per_slot(Dt dt);
+
+// Workgroups for a persistent launch of `kernel` with `threads` threads per
+// workgroup over `blocks` units of work: as many as are resident on the
+// device at once (occupancy x CUs), never more than `blocks`.
+int64_t persistent_grid(const void* kernel, int threads, int64_t blocks);
 
 // Kernel launches; return hipSuccess or the launch error.
 hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStream_t s);

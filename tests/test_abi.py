@@ -77,8 +77,9 @@ def test_ln_fwd_validation(L):
     assert fwd(L, eps=-1e-6) == LN_ERR_PARAM
     assert fwd(L, eps=float("nan")) == LN_ERR_PARAM
     assert fwd(L, eps=float("inf")) == LN_ERR_PARAM
-    assert fwd(L, cols=32769, dt=F32) == LN_ERR_UNSUPPORTED
-    assert fwd(L, cols=65537, dt=BF16) == LN_ERR_UNSUPPORTED
+    assert fwd(L, cols=16385, dt=F32) == LN_ERR_UNSUPPORTED
+    assert fwd(L, cols=16385, dt=BF16) == LN_ERR_UNSUPPORTED
+    assert fwd(L, cols=16384, dt=F16, rows=0) == LN_OK
     assert fwd(L, rows=2 ** 31) == LN_ERR_UNSUPPORTED
     assert fwd(L, rows=0) == LN_OK            # no-op, nothing enqueued
     # y may be x exactly, but not a partial overlap of it
@@ -155,5 +156,6 @@ def test_debug_force_path_validation(L):
     assert L.ln_debug_force_path(48, 1, 0) == LN_ERR_UNSUPPORTED
     assert L.ln_debug_force_path(64, 9, 0) == LN_ERR_UNSUPPORTED
     assert L.ln_debug_force_path(128, 2, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(1024, 8, 0) == LN_ERR_UNSUPPORTED
     assert L.ln_debug_force_path(64, 3, 0) == LN_OK
     assert L.ln_debug_force_path(0, 0, 0) == LN_OK

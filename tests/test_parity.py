@@ -136,8 +136,12 @@ def test_rows_beyond_partitions(orc):
 # Every row layout on the same shapes (test-only path forcing)
 # ----------------------------------------------------------------------------
 
-LAYOUTS = [(16, 1), (32, 1)] + [(64, v) for v in range(1, 9)] + \
-    [(128, 4), (256, 4), (512, 4), (1024, 4), (1024, 8)]
+# the layouts built for each storage size (fp32; fp16/bf16)
+LAYOUTS_F32 = [(16, v) for v in (1, 2, 4, 8)] + [(32, v) for v in range(1, 9)] + \
+    [(64, v) for v in range(1, 9)] + [(128, 4), (256, 4), (512, 4), (1024, 4)]
+LAYOUTS_16 = [(16, v) for v in (1, 2, 4)] + [(32, v) for v in range(1, 6)] + \
+    [(64, v) for v in range(1, 6)] + [(128, 4), (256, 4), (512, 4)]
+LAYOUTS = sorted(set(LAYOUTS_F32) | set(LAYOUTS_16))
 
 
 @pytest.mark.parametrize("scalar", [False, True], ids=["vec", "scalar"])
@@ -146,7 +150,8 @@ def test_forced_layouts(orc, g, v, scalar):
     for dtype, cols in ((torch.float32, 60), (torch.bfloat16, 120), (torch.float32, 1000),
                         (torch.bfloat16, 1000), (torch.float16, 4096)):
         e = 4 if dtype == torch.float32 else 8
-        if g * v * e < cols:
+        built = LAYOUTS_F32 if dtype == torch.float32 else LAYOUTS_16
+        if g * v * e < cols or (g, v) not in built:
             continue
         rows = 19
         case(f"forced g={g} v={v} scalar={scalar} {dtype} {rows}x{cols}")
@@ -201,3 +206,25 @@ def test_zero_rows_is_noop():
     g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
     y, mean, rstd = mb.ln_fwd(x, g, g, EPS)
     assert y.shape == (0, 64) and mean.shape == (0,)
+
+
+@pytest.mark.parametrize("grid", [1, 2, -1])
+def test_grid_size_does_not_change_results(grid):
+    # the persistent forward walks row blocks with the grid's stride; any
+    # grid must give the same bits
+    rows, cols, dtype = 3000, 1280, torch.bfloat16
+    case(f"grid {grid} fused fwd {dtype} {rows}x{cols}")
+    inp = dev(synth.layer_inputs(rows, cols, dtype, seed=13))
+    ref = mb.bias_dropout_residual_ln_fwd(inp["x"], inp["bias"], inp["residual"], inp["gamma"],
+                                          inp["beta"], 0.1, 5, EPS)
+    ref_plain = mb.ln_fwd(inp["x"], inp["gamma"], inp["beta"], EPS)
+    mb.debug_force_grid(grid)
+    try:
+        got = mb.bias_dropout_residual_ln_fwd(inp["x"], inp["bias"], inp["residual"],
+                                              inp["gamma"], inp["beta"], 0.1, 5, EPS)
+        got_plain = mb.ln_fwd(inp["x"], inp["gamma"], inp["beta"], EPS)
+        torch.cuda.synchronize()
+    finally:
+        mb.debug_force_grid(0)
+    for a, b in zip(ref[:4] + ref_plain, got[:4] + got_plain):
+        assert torch.equal(a, b)
