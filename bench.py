@@ -56,6 +56,9 @@ def parse():
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--warm-cache", action="store_true",
                     help="one buffer set, backward on the forward's fresh z (cache-resident)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "this benchmark into profiles/traffic.json and exit")
     return ap.parse_args()
 
 
@@ -81,6 +84,68 @@ def load_traffic(kernel: str, src_hash: str):
     if not k or k.get("source_hash") != src_hash:
         return None
     return k.get("hbm_bytes_per_launch")
+
+
+COPY_BYTES = 256 * 1024 * 1024   # calibration copy: 256 MiB read, 256 MiB written
+
+
+def _read_counters(path: str) -> dict:
+    """rocprofv3 counter_collection.csv -> {kernel name: [values per dispatch]}."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "")
+            try:
+                val = float(row.get("Counter_Value", "nan"))
+            except ValueError:
+                continue
+            out.setdefault(name, []).append(val)
+    return out
+
+
+def pmc_summary(fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per launch of each library kernel from FETCH_SIZE/WRITE_SIZE
+    (KiB per dispatch), scaled so that the calibration copy of COPY_BYTES reads
+    and writes exactly COPY_BYTES."""
+    fetch, write = _read_counters(fetch_csv), _read_counters(write_csv)
+
+    def copy_kib(d):
+        best = 0.0
+        for name, vals in d.items():
+            if "copy" in name.lower():
+                best = max(best, max(vals))
+        return best
+    fcopy, wcopy = copy_kib(fetch), copy_kib(write)
+    if fcopy <= 0 or wcopy <= 0:
+        raise SystemExit("no calibration copy kernel found in the counter files")
+    fscale, wscale = COPY_BYTES / (fcopy * 1024), COPY_BYTES / (wcopy * 1024)
+    src_hash = kernel_source_hash()
+    kernels = {}
+    for name in fetch:
+        if "mbrow" not in name:
+            continue
+        f_kib = sum(fetch[name]) / len(fetch[name])
+        w_kib = sum(write.get(name, [0.0])) / max(1, len(write.get(name, [0.0])))
+        short = ("ln_fwd_kernel(fused)" if "ln_fwd_kernel" in name and "true>" in name
+                 else "ln_fwd_kernel" if "ln_fwd_kernel" in name
+                 else "ln_bwd_kernel(dx+partials)" if "ln_bwd_kernel" in name
+                 else name.split("(")[0].replace("mbrow::", ""))
+        kernels[short] = {
+            "kernel_name": name,
+            "fetch_bytes_per_launch": round(f_kib * 1024 * fscale),
+            "write_bytes_per_launch": round(w_kib * 1024 * wscale),
+            "hbm_bytes_per_launch": round(f_kib * 1024 * fscale + w_kib * 1024 * wscale),
+            "dispatches": len(fetch[name]),
+            "source_hash": src_hash,
+        }
+    rec = {"copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": fcopy, "write_kib": wcopy,
+                                "fetch_scale": fscale, "write_scale": wscale},
+           "kernels": kernels}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(inp_cpu, target_s: float):
@@ -114,6 +179,9 @@ def cpu_baseline(inp_cpu, target_s: float):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method's rows "
               "shard across GPUs with no communication except a [2, cols] dgamma/dbeta "
@@ -191,6 +259,13 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end) / n        # ms per item
 
+    # attainable bandwidth: a plain copy of the forward's input size, rotated
+    # like the step, and a large copy (also the PMC calibration kernel)
+    ms_copy = timed(capture(lambda i: sets[i % S]["y"].copy_(sets[i % S]["x"]), K), K)
+    big_src = torch.empty(COPY_BYTES // 2, dtype=dtype, device=dev)
+    big_dst = torch.empty_like(big_src)
+    ms_bigcopy = timed(capture(lambda i: big_dst.copy_(big_src), 4), 4)
+
     g_step = capture(step, K)
     ms_step = timed(g_step, K)
     # per-kernel launches over the same rotation, for the roofline
@@ -231,6 +306,8 @@ def main():
         "bytes_per_step": nbytes["step"],
         "kernel_us": {"fused_fwd": round(ms_fwd * 1e3, 3), "bwd_dx_partials": round(ms_bwd * 1e3, 3),
                       "fold": round(ms_fold * 1e3, 3)},
+        "copy_GBps": {"21MB_rotated": round(2 * ROWS * COLS * 2 / (ms_copy * 1e-3) / 1e9, 1),
+                      "256MiB": round(2 * COPY_BYTES / (ms_bigcopy * 1e-3) / 1e9, 1)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -304,7 +304,9 @@ ln_status_t bias_dropout_residual_ln_fwd(const void* x, const void* bias, const 
     a.scale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
-    return from_hip(launch_fwd(d, pick_path(d, cols, vec), true, a, stream));
+    st = from_hip(launch_fwd(d, pick_path(d, cols, vec), true, a, stream));
+    if (st == LN_OK && mask_out) st = from_hip(launch_dropout_mask(a, stream));
+    return st;
 }
 
 ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const float* mean,

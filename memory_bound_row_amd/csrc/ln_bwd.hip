@@ -83,13 +83,16 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         ok[i] = i * G + lg < nslots;
         if constexpr (DX) gp[i] = load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
     }
-    float acc_g[V][E], acc_b[V][E];
-    if constexpr (PART) {
+    // Column accumulators.  With 32-lane rows the two row groups of a wave
+    // own the same columns; elements e and e + E/2 of each slot are summed
+    // over both rows with one lane swap, the lower half of the wave keeping
+    // the first and the upper half the second, so a lane carries half the
+    // columns.
+    constexpr bool SPLIT = PART && G == 32;
+    constexpr int KA = PART ? bwd_accumulators(G, V, E) : 1;
+    float acc_g[KA], acc_b[KA];
 #pragma unroll
-        for (int i = 0; i < V; ++i)
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc_g[i][e] = acc_b[i][e] = 0.0f;
-    }
+    for (int k = 0; k < KA; ++k) acc_g[k] = acc_b[k] = 0.0f;
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
     auto load_row = [&](BwdRowBuf<V>& b, int64_t base) {
@@ -135,6 +138,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             xr[i] = b.x[i];
             dr[i] = b.d[i];
         }
+        float c1 = 0.0f, c2 = 0.0f;
         if constexpr (DX) {
             float A = 0.0f, B = 0.0f;
 #pragma unroll
@@ -172,55 +176,59 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                     B += red[buf][grp][k][1];
                 }
             }
-            keep_packed(xr);
-            keep_packed(dr);
-            keep_packed(gp);
-            u32x4* pdx = VEC ? lane_slots<S>(a.dx, r, m, lg) : nullptr;
+            // dx = rstd * (g - (A + xhat * B) / m) = rstd * (g - (c1 + xhat * c2));
+            // g - (...) cancels exactly where it should (a one-column row
+            // gets dx = 0)
+            c1 = A * a.inv_m;
+            c2 = B * a.inv_m;
+        }
+        // Pass 2, slot by slot: dx (when formed) and the column partials.
+        // The partials use the same expressions whether or not dx is formed,
+        // so the fused and the partials-only passes give the same bits.
+        keep_packed(xr);
+        keep_packed(dr);
+        if constexpr (DX) keep_packed(gp);
+        u32x4* pdx = (DX && VEC) ? lane_slots<S>(a.dx, r, m, lg) : nullptr;
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float x[E], d[E], ga[E], out[E];
-                S::unpack(xr[i], x);
-                S::unpack(dr[i], d);
+        for (int i = 0; i < V; ++i) {
+            float x[E], d[E], xh[E];
+            S::unpack(xr[i], x);
+            S::unpack(dr[i], d);
+#pragma unroll
+            for (int e = 0; e < E; ++e) xh[e] = (x[e] - mu) * rs;
+            if constexpr (DX) {
+                float ga[E], out[E];
                 S::unpack(gp[i], ga);
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float xh = (x[e] - mu) * rs;
-                    const float g = ga[e] * d[e];
-                    const float t = fmaf(xh, B, A) * a.inv_m;
-                    out[e] = rs * (g - t);
-                    if constexpr (PART) {
-                        acc_g[i][e] = fmaf(d[e], xh, acc_g[i][e]);
-                        acc_b[i][e] = acc_b[i][e] + d[e];
-                    }
-                }
+                for (int e = 0; e < E; ++e) out[e] = rs * (ga[e] * d[e] - fmaf(xh[e], c2, c1));
                 if constexpr (VEC) {
                     if (ok[i] && rok) __builtin_nontemporal_store(S::pack(out), pdx + i * G);
                 } else {
                     store_elems<S>(a.dx, r, m, (i * G + lg) * E, ok[i] && rok, out);
                 }
             }
-        } else {
+            if constexpr (SPLIT) {
+                // element e of the slot pairs with e + E/2: the lower half of
+                // the wave keeps the first, the upper half the second
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float x[E], d[E];
-                S::unpack(xr[i], x);
-                S::unpack(dr[i], d);
+                for (int e = 0; e < E / 2; ++e) {
+                    const int k = i * (E / 2) + e;
+                    acc_g[k] = acc_g[k] + halves_sum_swap(d[e] * xh[e], d[e + E / 2] * xh[e + E / 2]);
+                    acc_b[k] = acc_b[k] + halves_sum_swap(d[e], d[e + E / 2]);
+                }
+            } else if constexpr (PART) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float xh = (x[e] - mu) * rs;
-                    acc_g[i][e] = fmaf(d[e], xh, acc_g[i][e]);
-                    acc_b[i][e] = acc_b[i][e] + d[e];
+                    acc_g[i * E + e] = fmaf(d[e], xh[e], acc_g[i * E + e]);
+                    acc_b[i * E + e] = acc_b[i * E + e] + d[e];
                 }
             }
+            // keep the scheduler from interleaving slots (it would hold
+            // several slots' temporaries at once)
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Walk over the partition's rows, double-buffered: the next rows' loads
-    // are issued before the current rows are reduced, so each wave keeps
-    // memory busy while it computes.  Every row group runs the same number
-    // of iterations (a row past the partition end is skipped but still takes
-    // part in the barriers of a multi-wave row), and each lane sees its rows
-    // in ascending order, so the column partials are summed in a fixed order.
     int64_t base = r0;
     int it = 0;
     // Prefetch needs a second row buffer; without room for it beside the
@@ -252,76 +260,78 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     }
 
     if constexpr (PART) {
-        if constexpr (G <= 32) {
-            // Fold the row groups of each wave: lanes l, l+G, ... own the same
-            // columns.  Adds are commutative, so partners agree bit for bit.
+        if constexpr (G == 16) {
+            // Fold the four row groups of each wave: lanes l, l+16, l+32, l+48
+            // own the same columns.  Adds are commutative, so partners agree
+            // bit for bit and every group ends with the wave's sums.
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    float& ag = acc_g[i][e];
-                    float& ab = acc_b[i][e];
-                    if constexpr (G <= 16) { ag = ag + partner<16>(ag); ab = ab + partner<16>(ab); }
-                    ag = ag + xor32(ag);
-                    ab = ab + xor32(ab);
-                }
+            for (int k = 0; k < KA; ++k) {
+                acc_g[k] = acc_g[k] + partner<16>(acc_g[k]);
+                acc_b[k] = acc_b[k] + partner<16>(acc_b[k]);
+                acc_g[k] = acc_g[k] + xor32(acc_g[k]);
+                acc_b[k] = acc_b[k] + xor32(acc_b[k]);
             }
         }
-        // Fold the units (waves, or multi-wave row groups) whose lanes own the
-        // same columns: every unit writes its sums to LDS, one barrier, then
-        // the whole workgroup adds them in unit order (0, 1, ...) and writes
-        // the workgroup's partial.  Slots go through LDS in chunks of CH so
-        // the footprint stays at 64 KB.
-        constexpr int CH = (NU * 2 * E * UT * 4 <= 65536) ? ((65536 / (NU * 2 * E * UT * 4)) < V ? (65536 / (NU * 2 * E * UT * 4)) : V) : 1;
+        // Column of accumulator k held by lane `pos` of a unit (a wave for
+        // G <= 64, a row group otherwise), or -1 when that lane only holds a
+        // copy of another lane's sums or the column is outside the row.
+        auto column = [&](int k, int pos) -> int {
+            int q = k, lane_in_group = pos;
+            if constexpr (SPLIT) {
+                // accumulator k = i*(E/2) + e: element e of slot i (lower
+                // half of the wave) or element e + E/2 (upper half)
+                q = (k / (E / 2)) * E + k % (E / 2) + (pos >= 32 ? E / 2 : 0);
+                lane_in_group = pos & 31;
+            } else if constexpr (G <= 64) {
+                if (pos >= G) return -1;
+            }
+            const int slot = (q / E) * G + lane_in_group;
+            const int col = slot * E + q % E;
+            return (slot < nslots && col < m) ? col : -1;
+        };
+        // Fold the units whose lanes own the same columns: every unit writes
+        // its sums to LDS, one barrier, then the whole workgroup adds them in
+        // unit order (0, 1, ...) and writes the workgroup's partial.
+        // Accumulators go through LDS in chunks of CH so the footprint stays
+        // at 64 KB.
+        constexpr int PER_K = NU * 2 * UT * 4;   // bytes of one accumulator index
+        constexpr int CH = (65536 / PER_K) < KA ? (65536 / PER_K < 1 ? 1 : 65536 / PER_K) : KA;
         const int unit = tid / UT;
         const int pos = tid % UT;
         float* pg = a.ws + (part * 2 + 0) * a.m;
         float* pb = a.ws + (part * 2 + 1) * a.m;
         if constexpr (NU == 1) {
-            // one unit: each lane writes its own columns
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                const int col0 = (i * G + lg) * E;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    if (ok[i] && col0 + e < m) {
-                        pg[col0 + e] = acc_g[i][e];
-                        pb[col0 + e] = acc_b[i][e];
-                    }
+            for (int k = 0; k < KA; ++k) {
+                const int col = column(k, pos);
+                if (col >= 0) {
+                    pg[col] = acc_g[k];
+                    pb[col] = acc_b[k];
                 }
             }
         } else {
-            __shared__ float stage[NU][2][CH * E][UT];
-            // positions of one chunk: (kind, value k of the chunk, lane pos)
-            constexpr int NPOS = 2 * CH * E * UT;
+            __shared__ float stage[NU][2][CH][UT];
+            constexpr int NPOS = 2 * CH * UT;
 #pragma unroll
-            for (int i0 = 0; i0 < V; i0 += CH) {
-                if (i0 > 0) __syncthreads();   // previous chunk fully read
+            for (int k0 = 0; k0 < KA; k0 += CH) {
+                if (k0 > 0) __syncthreads();   // previous chunk fully read
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
-                    if (i0 + c < V) {
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            stage[unit][0][c * E + e][pos] = acc_g[i0 + c][e];
-                            stage[unit][1][c * E + e][pos] = acc_b[i0 + c][e];
-                        }
+                    if (k0 + c < KA) {
+                        stage[unit][0][c][pos] = acc_g[k0 + c];
+                        stage[unit][1][c][pos] = acc_b[k0 + c];
                     }
                 }
                 __syncthreads();
                 for (int q = tid; q < NPOS; q += BwdGeometry<G>::NT) {
                     const int p = q % UT;
-                    const int k = (q / UT) % (CH * E);
-                    const int kind = q / (UT * CH * E);
-                    const int i = i0 + k / E;
-                    const int e = k % E;
-                    // lane p of a unit owns slot i*G + p (G <= 64: p < G is
-                    // one row group's copy; larger p are duplicates)
-                    const int s = i * G + p;
-                    const int col = s * E + e;
-                    if (i < V && (G > 64 || p < G) && s < nslots && col < m) {
-                        float t = stage[0][kind][k][p];
+                    const int c = (q / UT) % CH;
+                    const int kind = q / (UT * CH);
+                    const int col = (k0 + c < KA) ? column(k0 + c, p) : -1;
+                    if (col >= 0) {
+                        float t = stage[0][kind][c][p];
 #pragma unroll
-                        for (int u = 1; u < NU; ++u) t = t + stage[u][kind][k][p];
+                        for (int u = 1; u < NU; ++u) t = t + stage[u][kind][c][p];
                         (kind == 0 ? pg : pb)[col] = t;
                     }
                 }

@@ -17,6 +17,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 // No implicit multiply-add contraction anywhere in the kernels: every fused
 // multiply-add is written out with fmaf, so that two kernels that share an
 // expression round it identically (the partials of the fused and standalone
@@ -27,6 +30,17 @@
 namespace mbrow {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Call f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time
+// indices, e.g. to pick a packed element).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -55,6 +69,8 @@ struct StF32 {
     }
     // value as it would be stored (RNE to T), back in float
     __device__ static inline float round(float f) { return f; }
+    template <int e>
+    __device__ static inline float elem(const u32x4& v) { return __uint_as_float(v[e]); }
 };
 
 struct StBF16 {
@@ -85,6 +101,11 @@ struct StBF16 {
         static_cast<__bf16*>(p)[i] = (__bf16)f;
     }
     __device__ static inline float round(float f) { return (float)(__bf16)f; }
+    template <int e>
+    __device__ static inline float elem(const u32x4& v) {
+        const uint32_t w = v[e / 2];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
 };
 
 struct StF16 {
@@ -118,6 +139,12 @@ struct StF16 {
         static_cast<_Float16*>(p)[i] = (_Float16)f;
     }
     __device__ static inline float round(float f) { return (float)(_Float16)f; }
+    template <int e>
+    __device__ static inline float elem(const u32x4& v) {
+        const uint32_t w = v[e / 2];
+        f16x2 h = __builtin_bit_cast(f16x2, w);
+        return (float)h[e & 1];
+    }
 };
 
 // ---------------------------------------------------------------------------
@@ -197,6 +224,14 @@ __device__ inline float dpp(float v) {
 __device__ inline float swz_xor16(float v) {
     // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 (stays inside 32 lanes)
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+// gfx950 v_permlane32_swap: the upper 32 lanes of x trade places with the
+// lower 32 lanes of y; returns (x', y') = ([x_lo, y_lo], [x_hi, y_hi]).  So
+// x' + y' holds x_lo + x_hi in the lower half and y_lo + y_hi in the upper.
+__device__ inline float halves_sum_swap(float x, float y) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ inline float lane_read(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));

@@ -147,12 +147,6 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
                 } else {
                     store_elems<S>(a.residual_out, r, m, col0, sok, z);
                 }
-                if (a.mask_out && sok) {
-                    const int64_t off = r * (int64_t)m;
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        if (col0 + e < m) a.mask_out[off + col0 + e] = (uint8_t)((bits >> e) & 1u);
-                }
             }
         } else {
 #pragma unroll
@@ -288,6 +282,30 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
     }
 }
 
+#if MBROW_DT == 0
+// The dropout keep mask of a [rows, m] tensor as bytes (1 = kept), from the
+// same function of (seed, row, column, p) the fused forward uses.  Tests and
+// debugging only: the forward never stores the mask.  (One copy, in the fp32
+// unit: it does not depend on the storage type.)
+__global__ __launch_bounds__(256) void ln_dropout_mask_kernel(uint8_t* __restrict__ mask,
+                                                              int64_t rows, int m, uint32_t thr,
+                                                              uint32_t seed_lo,
+                                                              uint32_t seed_hi) {
+    const int groups = (m + 7) / 8;   // 8-column groups per row
+    const int64_t total = rows * groups;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = q / groups;
+        const int col0 = (int)(q - row * groups) * 8;
+        const uint32_t bits = keep_bits<8>(row, col0, seed_lo, seed_hi, thr);
+        uint8_t* dst = mask + row * (int64_t)m + col0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col0 + e < m) dst[e] = (uint8_t)((bits >> e) & 1u);
+    }
+}
+#endif
+
 template <int G, int V, bool VEC, bool FUSED>
 static hipError_t launch_one(const FwdArgs& a, hipStream_t s) {
     using Geo = Geometry<G>;
@@ -310,6 +328,18 @@ static hipError_t dispatch(const Path& p, const FwdArgs& a, hipStream_t s) {
 #undef MBROW_CASE
     return hipErrorInvalidValue;
 }
+
+#if MBROW_DT == 0
+hipError_t launch_dropout_mask(const FwdArgs& a, hipStream_t s) {
+    const int64_t groups = (a.m + 7) / 8;
+    const int64_t total = a.rows * groups;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(ln_dropout_mask_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       a.mask_out, a.rows, (int)a.m, a.thr, a.seed_lo, a.seed_hi);
+    return hipGetLastError();
+}
+#endif
 
 #define MBROW_CAT2(a, b) a##b
 #define MBROW_CAT(a, b) MBROW_CAT2(a, b)

@@ -43,7 +43,7 @@ struct FwdArgs {
     void* y;
     float* mean;
     float* rstd;
-    uint8_t* mask_out;
+    uint8_t* mask_out;  // only read by the mask kernel
     int64_t rows;
     int64_t m;
     int64_t nslots;   // ceil(m / E)
@@ -75,11 +75,17 @@ enum class BwdMode : int { DX = 0, DX_PARTIALS = 1, PARTIALS = 2 };
 // Threads per workgroup of the backward for G lanes per row.
 constexpr int bwd_threads(int g) { return g <= 512 ? 512 : g; }
 
+// Column accumulators per lane and kind in the backward: one per value of
+// the lane's row slots, or half as many for 32-lane rows, whose two row
+// groups per wave split the columns between the wave's halves.
+constexpr int bwd_accumulators(int g, int v, int e) { return g == 32 ? v * e / 2 : v * e; }
+
 // Whether the backward double-buffers its rows: the second row buffer
-// (V * 8 registers) must fit beside the column accumulators (2 per value when
-// partials are on) and packed gamma within an estimated 120 registers.
+// (V * 8 registers) must fit beside the column accumulators (two kinds when
+// partials are on) and packed gamma within an estimated 130 registers.
 constexpr bool bwd_prefetch(int g, int v, int e, bool partials) {
-    return bwd_threads(g) <= 512 && (partials ? 2 * v * e : 0) + 2 * v * 8 + v * 4 <= 120;
+    return bwd_threads(g) <= 512 &&
+           (partials ? 2 * bwd_accumulators(g, v, e) : 0) + 2 * v * 8 + v * 4 <= 130;
 }
 
 // Row partitions of the dgamma/dbeta stage-1 pass: a pure function of
@@ -100,6 +106,7 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t blocks);
 // Kernel launches; return hipSuccess or the launch error.
 hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(Dt dt, const Path& p, BwdMode mode, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dropout_mask(const FwdArgs& a, hipStream_t s);   // a.mask_out, rows, m, thr, seed
 hipError_t launch_fold(const float* ws, int64_t parts, int64_t m, float* dgamma,
                        float* dbeta, hipStream_t s);
 
