@@ -77,12 +77,20 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
 
     // slot i of this lane covers columns (i*G + lg)*E .. +E-1
     bool ok[V];
-    u32x4 gp[V];   // gamma, packed in T
+    // gamma, packed in T: kept in registers, except with 32-lane rows and
+    // partials, where the registers go to the second row buffer and gamma is
+    // re-read (from cache) where used
+    constexpr bool GREG = !(PART && G == 32);
+    u32x4 gp[GREG ? V : 1];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         ok[i] = i * G + lg < nslots;
-        if constexpr (DX) gp[i] = load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
+        if constexpr (DX && GREG) gp[i] = load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
     }
+    auto gamma_slot = [&](int i) -> u32x4 {
+        if constexpr (GREG) return gp[i];
+        else return load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
+    };
     // Column accumulators.  With 32-lane rows the two row groups of a wave
     // own the same columns; elements e and e + E/2 of each slot are summed
     // over both rows with one lane swap, the lower half of the wave keeping
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         const bool rok = row < r1;
         const int64_t r = rok ? row : 0;
         const float mu = b.mu, rs = b.rs;
-        if constexpr (DX) keep_packed(gp);
+        if constexpr (DX && GREG) keep_packed(gp);
         u32x4 xr[V], dr[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) {
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 float x[E], d[E], ga[E];
                 S::unpack(xr[i], x);
                 S::unpack(dr[i], d);
-                S::unpack(gp[i], ga);
+                S::unpack(gamma_slot(i), ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float xh = (x[e] - mu) * rs;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         // so the fused and the partials-only passes give the same bits.
         keep_packed(xr);
         keep_packed(dr);
-        if constexpr (DX) keep_packed(gp);
+        if constexpr (DX && GREG) keep_packed(gp);
         u32x4* pdx = (DX && VEC) ? lane_slots<S>(a.dx, r, m, lg) : nullptr;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             for (int e = 0; e < E; ++e) xh[e] = (x[e] - mu) * rs;
             if constexpr (DX) {
                 float ga[E], out[E];
-                S::unpack(gp[i], ga);
+                S::unpack(gamma_slot(i), ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e) out[e] = rs * (ga[e] * d[e] - fmaf(xh[e], c2, c1));
                 if constexpr (VEC) {
@@ -241,11 +249,13 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             int64_t nxt = base + NG;
             if (nxt < r1) load_row(b1, nxt);
             process(b0, base, it++);
+            __builtin_amdgcn_sched_barrier(0);
             base = nxt;
             if (base >= r1) break;
             nxt = base + NG;
             if (nxt < r1) load_row(b0, nxt);
             process(b1, base, it++);
+            __builtin_amdgcn_sched_barrier(0);
             base = nxt;
         }
     } else {

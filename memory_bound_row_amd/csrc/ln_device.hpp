@@ -355,9 +355,10 @@ __device__ inline u32x4 philox4x32_10(u32x4 ctr, uint32_t k0, uint32_t k1) {
         uint64_t p0 = (uint64_t)ctr[0] * 0xD2511F53u;
         uint64_t p2 = (uint64_t)ctr[2] * 0xCD9E8D57u;
         u32x4 nx;
-        nx[0] = (uint32_t)(p2 >> 32) ^ ctr[1] ^ k0;
+        // three-input xor in one v_bitop3_b32 (truth table 0x96)
+        nx[0] = __builtin_amdgcn_bitop3_b32((uint32_t)(p2 >> 32), ctr[1], k0, 0x96);
         nx[1] = (uint32_t)p2;
-        nx[2] = (uint32_t)(p0 >> 32) ^ ctr[3] ^ k1;
+        nx[2] = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), ctr[3], k1, 0x96);
         nx[3] = (uint32_t)p0;
         ctr = nx;
         k0 += 0x9E3779B9u;

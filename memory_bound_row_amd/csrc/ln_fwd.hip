@@ -121,6 +121,32 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
         keep_packed(gp);
         keep_packed(bp);
         u32x4 zp[V];   // the values being normalised, packed (x, or the stored z)
+        // element e of slot i lies in the row
+        auto inside = [&](int i, int e) { return ok[i] && (VEC || (i * G + lg) * E + e < m); };
+        // Shift: the first value of this wave's part of the row.  Pass 1: the
+        // sum of the shifted values of the row (outside elements count 0; on
+        // the vector path a slot is wholly inside or outside).
+        float c = 0.0f, s_l = 0.0f;
+        auto add_slot = [&](int i, const float* v) {
+            if constexpr (VEC) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) ss += v[e] - c;
+                s_l += ok[i] ? ss : 0.0f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) s_l += inside(i, e) ? v[e] - c : 0.0f;
+            }
+        };
+        // fp32 rows are shifted so a large mean cannot swamp the sums; 16-bit
+        // rows hold at most 11 significant bits, and fp32 sums of them stay
+        // accurate far beyond their storage step, so they are not shifted
+        auto set_shift = [&](const float* v0) {
+            if constexpr (S::BYTES == 4) {
+                c = (G <= 64) ? group_broadcast_first<(G <= 64 ? G : 64)>(v0[0], lane)
+                              : lane_read(v0[0], 0);
+            }
+        };
         if constexpr (FUSED) {
             keep_packed(bip);
             u32x4* pz = VEC ? lane_slots<S>(a.residual_out, r, m, lg) : nullptr;
@@ -147,28 +173,22 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
                 } else {
                     store_elems<S>(a.residual_out, r, m, col0, sok, z);
                 }
+                float v[E];
+                S::unpack(zp[i], v);
+                if (i == 0) set_shift(v);
+                add_slot(i, v);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < V; ++i) zp[i] = b.x[i];
-        }
-        // element e of slot i lies in the row
-        auto inside = [&](int i, int e) { return ok[i] && (VEC || (i * G + lg) * E + e < m); };
-
-        // shift: first value of this wave's part of the row
-        float first[E];
-        S::unpack(zp[0], first);
-        const float c = (G <= 64) ? group_broadcast_first<(G <= 64 ? G : 64)>(first[0], lane)
-                                  : lane_read(first[0], 0);
-        // pass 1: sum of shifted values (elements outside the row contribute 0)
-        keep_packed(zp);
-        float s_l = 0.0f;
+            keep_packed(zp);
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            float v[E];
-            S::unpack(zp[i], v);
-#pragma unroll
-            for (int e = 0; e < E; ++e) s_l += inside(i, e) ? v[e] - c : 0.0f;
+            for (int i = 0; i < V; ++i) {
+                float v[E];
+                S::unpack(zp[i], v);
+                if (i == 0) set_shift(v);
+                add_slot(i, v);
+            }
         }
         // pass 2: sum of squared deviations from a mean m_l
         auto sq_dev = [&](float m_l) {
@@ -178,10 +198,20 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
             for (int i = 0; i < V; ++i) {
                 float v[E];
                 S::unpack(zp[i], v);
+                if constexpr (VEC) {
+                    float qq = 0.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float d = inside(i, e) ? (v[e] - c) - m_l : 0.0f;
-                    q_l = fmaf(d, d, q_l);
+                    for (int e = 0; e < E; ++e) {
+                        const float d = (v[e] - c) - m_l;
+                        qq = fmaf(d, d, qq);
+                    }
+                    q_l += ok[i] ? qq : 0.0f;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float d = inside(i, e) ? (v[e] - c) - m_l : 0.0f;
+                        q_l = fmaf(d, d, q_l);
+                    }
                 }
             }
             return q_l;

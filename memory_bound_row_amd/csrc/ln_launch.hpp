@@ -85,7 +85,8 @@ constexpr int bwd_accumulators(int g, int v, int e) { return g == 32 ? v * e / 2
 // partials are on) and packed gamma within an estimated 130 registers.
 constexpr bool bwd_prefetch(int g, int v, int e, bool partials) {
     return bwd_threads(g) <= 512 &&
-           (partials ? 2 * bwd_accumulators(g, v, e) : 0) + 2 * v * 8 + v * 4 <= 130;
+           (partials ? 2 * bwd_accumulators(g, v, e) : 0) + 2 * v * 8 +
+                   ((partials && g == 32) ? 0 : v * 4) <= 130;
 }
 
 // Row partitions of the dgamma/dbeta stage-1 pass: a pure function of
