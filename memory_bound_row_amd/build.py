@@ -25,7 +25,7 @@ COMMON = [
     # no packed-FP32 instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
-    "-I", INCLUDE, "-I", CSRC,
+    "-I", INCLUDE,
 ]
 
 UNITS = (
@@ -47,11 +47,11 @@ def _spilling_kernels(remarks: str):
     return bad
 
 
-def _compile(unit):
+def _compile(unit, build_dir=BUILD, extra=(), csrc=CSRC):
     src, defs, obj = unit
-    out = os.path.join(BUILD, obj)
-    cmd = [HIPCC, *COMMON, *defs, "-Rpass-analysis=kernel-resource-usage",
-           "-c", os.path.join(CSRC, src), "-o", out]
+    out = os.path.join(build_dir, obj)
+    cmd = [HIPCC, *COMMON, "-I", csrc, *extra, *defs, "-Rpass-analysis=kernel-resource-usage",
+           "-c", os.path.join(csrc, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
@@ -62,20 +62,23 @@ def _compile(unit):
     return out
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, extra_flags=(), out_lib: str = LIB,
+          build_dir: str = BUILD, csrc: str = CSRC) -> str:
+    """Compile every unit of `csrc` and link `out_lib`; `extra_flags` go to
+    every hipcc compile."""
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, UNITS))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda u: _compile(u, build_dir, tuple(extra_flags), csrc), UNITS))
+    tmp = out_lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out_lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":

@@ -87,6 +87,20 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         ok[i] = i * G + lg < nslots;
         if constexpr (DX && GREG) gp[i] = load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
     }
+    // vector path: the lane's byte offset of each slot in its wave's row view
+    uint32_t vo[VEC ? V : 1];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) vo[i] = slot_offset<S, G>(tid, i, m, ok[i]);
+    }
+    const int wrow = wave_first_row<G>(tid);
+    // the rows of the block starting at `base` that this wave touches, within
+    // the partition (uniform across the wave)
+    auto view = [&](const void* t, int64_t base) {
+        const int64_t row0 = base + wrow;
+        const int64_t left = r1 - row0;
+        return row_view<S>(t, row0, left < WaveRows<G>::N ? left : WaveRows<G>::N, m);
+    };
     auto gamma_slot = [&](int i) -> u32x4 {
         if constexpr (GREG) return gp[i];
         else return load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
@@ -108,12 +122,12 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         const bool rok = row < r1;
         const int64_t r = rok ? row : 0;
         if constexpr (VEC) {
-            const u32x4* pd = lane_slots<S>(a.dy, r, m, lg);
-            const u32x4* px = lane_slots<S>(a.x, r, m, lg);
+            const rsrc_t vd = view(a.dy, base);
+            const rsrc_t vx = view(a.x, base);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                b.d[i] = nt_load(pd + i * G, ok[i] && rok);
-                b.x[i] = nt_load(px + i * G, ok[i] && rok);
+                b.d[i] = buf_load_nt(vd, vo[i]);
+                b.x[i] = buf_load_nt(vx, vo[i]);
             }
         } else {
 #pragma unroll
@@ -196,7 +210,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         keep_packed(xr);
         keep_packed(dr);
         if constexpr (DX && GREG) keep_packed(gp);
-        u32x4* pdx = (DX && VEC) ? lane_slots<S>(a.dx, r, m, lg) : nullptr;
+        const rsrc_t vdx = view(DX ? a.dx : a.dy, base);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             float x[E], d[E], xh[E];
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) out[e] = rs * (ga[e] * d[e] - fmaf(xh[e], c2, c1));
                 if constexpr (VEC) {
-                    if (ok[i] && rok) __builtin_nontemporal_store(S::pack(out), pdx + i * G);
+                    buf_store_nt(S::pack(out), vdx, vo[i]);
                 } else {
                     store_elems<S>(a.dx, r, m, (i * G + lg) * E, ok[i] && rok, out);
                 }
@@ -282,69 +296,58 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 acc_b[k] = acc_b[k] + xor32(acc_b[k]);
             }
         }
-        // Column of accumulator k held by lane `pos` of a unit (a wave for
-        // G <= 64, a row group otherwise), or -1 when that lane only holds a
-        // copy of another lane's sums or the column is outside the row.
-        auto column = [&](int k, int pos) -> int {
-            int q = k, lane_in_group = pos;
-            if constexpr (SPLIT) {
-                // accumulator k = i*(E/2) + e: element e of slot i (lower
-                // half of the wave) or element e + E/2 (upper half)
-                q = (k / (E / 2)) * E + k % (E / 2) + (pos >= 32 ? E / 2 : 0);
-                lane_in_group = pos & 31;
-            } else if constexpr (G <= 64) {
-                if (pos >= G) return -1;
-            }
-            const int slot = (q / E) * G + lane_in_group;
-            const int col = slot * E + q % E;
-            return (slot < nslots && col < m) ? col : -1;
-        };
-        // Fold the units whose lanes own the same columns: every unit writes
-        // its sums to LDS, one barrier, then the whole workgroup adds them in
-        // unit order (0, 1, ...) and writes the workgroup's partial.
-        // Accumulators go through LDS in chunks of CH so the footprint stays
-        // at 64 KB.
-        constexpr int PER_K = NU * 2 * UT * 4;   // bytes of one accumulator index
-        constexpr int CH = (65536 / PER_K) < KA ? (65536 / PER_K < 1 ? 1 : 65536 / PER_K) : KA;
+        // Fold the units whose lanes own the same columns (the waves of the
+        // workgroup for G <= 64, its row groups otherwise): every unit stages
+        // its sums in LDS, one barrier, then the workgroup adds them in unit
+        // order (0, 1, ...) column by column, consecutive threads taking
+        // consecutive columns, and writes the workgroup's partial.  The
+        // accumulators go through LDS in chunks of CI slot indices so the
+        // footprint stays within 64 KB.
+        constexpr int KPI = SPLIT ? E / 2 : E;                  // accumulators per slot index
+        constexpr int KF = 65536 / (NU * 2 * UT * 4);           // floats per lane that fit
+        constexpr int CI = (KF - 1) / KPI < 1 ? 1 : ((KF - 1) / KPI < V ? (KF - 1) / KPI : V);
+        constexpr int CK = CI * KPI + 1;                        // padded lane stride
+        constexpr int CW = CI * G * E;                          // columns per chunk
+        static_assert(NU * 2 * UT * CK * 4 <= 65536, "stage exceeds 64 KB");
+        __shared__ float stage[NU][2][UT][CK];
         const int unit = tid / UT;
         const int pos = tid % UT;
         float* pg = a.ws + (part * 2 + 0) * a.m;
         float* pb = a.ws + (part * 2 + 1) * a.m;
-        if constexpr (NU == 1) {
 #pragma unroll
-            for (int k = 0; k < KA; ++k) {
-                const int col = column(k, pos);
-                if (col >= 0) {
-                    pg[col] = acc_g[k];
-                    pb[col] = acc_b[k];
+        for (int i0 = 0; i0 < V; i0 += CI) {
+            if (i0 > 0) __syncthreads();   // previous chunk fully read
+#pragma unroll
+            for (int c = 0; c < CI * KPI; ++c) {
+                const int k = i0 * KPI + c;
+                if (k < KA) {
+                    stage[unit][0][pos][c] = acc_g[k];
+                    stage[unit][1][pos][c] = acc_b[k];
                 }
             }
-        } else {
-            __shared__ float stage[NU][2][CH][UT];
-            constexpr int NPOS = 2 * CH * UT;
-#pragma unroll
-            for (int k0 = 0; k0 < KA; k0 += CH) {
-                if (k0 > 0) __syncthreads();   // previous chunk fully read
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    if (k0 + c < KA) {
-                        stage[unit][0][c][pos] = acc_g[k0 + c];
-                        stage[unit][1][c][pos] = acc_b[k0 + c];
-                    }
+            __syncthreads();
+            const int col0 = i0 * G * E;
+            for (int q = tid; q < 2 * CW; q += BwdGeometry<G>::NT) {
+                const int kind = q >= CW;
+                const int cl = q - kind * CW;
+                const int col = col0 + cl;
+                if (col >= m) continue;
+                // lane and accumulator holding column col: slot col/E, element col%E
+                const int sl = cl / E, ee = cl % E;
+                const int il = sl / G, lig = sl % G;
+                int c, p;
+                if constexpr (SPLIT) {
+                    // element ee < E/2 in the lower half of the wave, else the upper
+                    c = il * KPI + ee % KPI;
+                    p = lig + (ee / KPI) * 32;
+                } else {
+                    c = il * E + ee;
+                    p = lig;
                 }
-                __syncthreads();
-                for (int q = tid; q < NPOS; q += BwdGeometry<G>::NT) {
-                    const int p = q % UT;
-                    const int c = (q / UT) % CH;
-                    const int kind = q / (UT * CH);
-                    const int col = (k0 + c < KA) ? column(k0 + c, p) : -1;
-                    if (col >= 0) {
-                        float t = stage[0][kind][c][p];
+                float t = stage[0][kind][p][c];
 #pragma unroll
-                        for (int u = 1; u < NU; ++u) t = t + stage[u][kind][c][p];
-                        (kind == 0 ? pg : pb)[col] = t;
-                    }
-                }
+                for (int u = 1; u < NU; ++u) t = t + stage[u][kind][p][c];
+                (kind == 0 ? pg : pb)[col] = t;
             }
         }
     }

@@ -148,27 +148,62 @@ struct StF16 {
 };
 
 // ---------------------------------------------------------------------------
-// Slot access.  VEC: one 16-byte access per slot (row starts 16-byte
-// aligned, cols*sizeof(T) a multiple of 16); a lane keeps one pointer to its
-// first slot of the row and reaches slot i at the constant offset i*G*16
-// bytes, which the load/store instruction folds into its immediate.
+// Slot access.  VEC (row starts 16-byte aligned, cols*sizeof(T) a multiple
+// of 16): one 16-byte buffer access per slot.  A wave addresses its rows
+// through a buffer resource based at its first row whose size covers only
+// the rows that exist, so the hardware range check returns 0 for a load and
+// drops a store past the end of the tensor: no branch and no zeroing per
+// access.  A lane's byte offset of slot i is fixed for the whole kernel;
+// slots past the end of a row are given kOob, outside every view.
 // Otherwise one access per element, each predicated on its column.
 // Streaming tensors use nontemporal accesses; gamma/beta/bias (re-read by
 // every row) use ordinary cached loads.
 // ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;        // beyond any view (views are < 2^31 bytes)
+constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
+constexpr int kNt = 2;                        // nontemporal cache policy
+
+// View of rows [row0, row0 + nrows) of a [rows, m] tensor; nrows <= 0 gives
+// an empty view (every access out of range).  row0 and nrows must be
+// uniform across the wave.
 template <class S>
-__device__ __forceinline__ const u32x4* lane_slots(const void* base, int64_t row, int m,
-                                                   int lg) {
-    return reinterpret_cast<const u32x4*>(static_cast<const char*>(base) +
-                                          row * (int64_t)m * S::BYTES) + lg;
+__device__ __forceinline__ rsrc_t row_view(const void* base, int64_t row0, int64_t nrows, int m) {
+    const int64_t n = nrows > 0 ? nrows : 0;
+    char* p = const_cast<char*>(static_cast<const char*>(base)) + row0 * (int64_t)m * S::BYTES;
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)(n * m * S::BYTES), kRsrcWord3);
 }
-template <class S>
-__device__ __forceinline__ u32x4* lane_slots(void* base, int64_t row, int m, int lg) {
-    return reinterpret_cast<u32x4*>(static_cast<char*>(base) + row * (int64_t)m * S::BYTES) + lg;
+__device__ __forceinline__ u32x4 buf_load_nt(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNt);
+}
+__device__ __forceinline__ u32x4 buf_load(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_nt(u32x4 v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNt);
 }
 
-__device__ __forceinline__ u32x4 nt_load(const u32x4* p, bool ok) {
-    return ok ? __builtin_nontemporal_load(p) : u32x4{0u, 0u, 0u, 0u};
+// Rows of one wave: a group of G <= 64 lanes owns one row, so a wave spans
+// 64/G consecutive rows; wider rows span G/64 waves.
+template <int G>
+struct WaveRows {
+    static constexpr int N = G <= 64 ? 64 / G : 1;
+};
+
+// The wave's first row within its block of NT/G rows (wave-uniform).
+template <int G>
+__device__ __forceinline__ int wave_first_row(int tid) {
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    return G <= 64 ? w * (64 / G) : w / (G / 64);
+}
+
+// Byte offset of slot i of this lane within its wave's row view, or kOob for
+// a slot past the end of the row.
+template <class S, int G>
+__device__ __forceinline__ uint32_t slot_offset(int tid, int i, int m, bool ok) {
+    const int lg = tid % G;
+    const uint32_t row_in_wave = G <= 64 ? (uint32_t)((tid & 63) / G) : 0u;
+    return ok ? row_in_wave * (uint32_t)m * S::BYTES + (uint32_t)(i * G + lg) * 16u : kOob;
 }
 
 // Per-element path: E elements of row `row` starting at column col0 (< m
@@ -193,7 +228,8 @@ __device__ inline void store_elems(void* base, int64_t row, int m, int col0, boo
 template <class S, bool VEC>
 __device__ __forceinline__ u32x4 load_param(const void* base, int s, int m, bool ok) {
     if constexpr (VEC) {
-        return ok ? reinterpret_cast<const u32x4*>(base)[s] : u32x4{0u, 0u, 0u, 0u};
+        // slots past the end of the vector fall outside the view and read 0
+        return buf_load(row_view<S>(base, 0, 1, m), (uint32_t)s * 16u);
     } else {
         float f[S::E];
         load_elems<S>(base, 0, m, s * S::E, ok, f);
@@ -367,31 +403,32 @@ __device__ inline u32x4 philox4x32_10(u32x4 ctr, uint32_t k0, uint32_t k1) {
     return ctr;
 }
 
-// Keep bits of the E columns col0 .. col0+E-1 of one row (all in the same
-// group of 8 columns): bit e set iff the 16-bit uniform of column col0+e is
-// >= thr.  Counter (col >> 3, row lo, row hi, 0); key (seed lo, seed hi);
-// column k = col & 7 of the group takes half (k & 1) of word k >> 1.
-template <int E>
-__device__ inline uint32_t keep_bits(int64_t row, int col0, uint32_t seed_lo,
-                                     uint32_t seed_hi, uint32_t thr) {
-    if (thr == 0u) return (1u << E) - 1u;  // u >= 0 always: keep every column
+// Dropout uniforms of the 8-column group holding column col0 of a row:
+// Philox4x32-10 with counter (col >> 3, row lo, row hi, 0) and key
+// (seed lo, seed hi); column k = col & 7 of the group takes the 16-bit half
+// (k & 1) of word k >> 1.  With thr == 0 every column is kept, so the
+// generator is skipped and every half reads 0xffff.
+__device__ inline u32x4 dropout_words(int64_t row, int col0, uint32_t seed_lo, uint32_t seed_hi,
+                                      uint32_t thr) {
+    if (thr == 0u) return u32x4{~0u, ~0u, ~0u, ~0u};
     u32x4 c;
     c[0] = (uint32_t)col0 >> 3;
     c[1] = (uint32_t)((uint64_t)row & 0xffffffffu);
     c[2] = (uint32_t)((uint64_t)row >> 32);
     c[3] = 0u;
-    u32x4 w = philox4x32_10(c, seed_lo, seed_hi);
-    uint32_t bits = 0;
-    // E == 8: the slot is a whole group of 8 columns.  E == 4: it is the low
-    // or the high half of one (col0 & 4), i.e. words 0-1 or words 2-3.
+    return philox4x32_10(c, seed_lo, seed_hi);
+}
+
+// Whether element e of a slot of E columns starting at col0 is kept (its
+// 16-bit uniform is >= thr), from the words of its 8-column group.  E == 8:
+// the slot is the whole group; E == 4: the low or the high half of one
+// (col0 & 4), i.e. words 0-1 or words 2-3.
+template <int E>
+__device__ __forceinline__ bool kept(const u32x4& w, int col0, int e, uint32_t thr) {
     const bool high = (E == 4) && ((col0 & 4) != 0);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        uint32_t word = high ? w[2 + (e >> 1)] : w[e >> 1];
-        uint32_t u = (e & 1) ? (word >> 16) : (word & 0xffffu);
-        bits |= (u >= thr ? 1u : 0u) << e;
-    }
-    return bits;
+    const uint32_t word = high ? w[2 + (e >> 1)] : w[e >> 1];
+    const uint32_t u = (e & 1) ? (word >> 16) : (word & 0xffffu);
+    return u >= thr;
 }
 
 }  // namespace mbrow

@@ -73,28 +73,51 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
 
     // slot i of this lane covers columns (i*G + lg)*E .. +E-1
     bool ok[V];
-    // gamma, beta, bias stay packed in T and are unpacked where used
-    u32x4 gp[V], bp[V], bip[FUSED ? V : 1];
+    // The fused kernel keeps gamma, beta and bias packed in T in registers
+    // across rows; the plain one re-reads gamma and beta (from cache) for
+    // every row, which leaves room for more resident waves and measured
+    // faster there.
+    constexpr bool PREG = FUSED;
+    u32x4 gp[PREG ? V : 1], bp[PREG ? V : 1], bip[PREG ? V : 1];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int s = i * G + lg;
         ok[i] = s < nslots;
-        gp[i] = load_param<S, VEC>(a.gamma, s, m, ok[i]);
-        bp[i] = load_param<S, VEC>(a.beta, s, m, ok[i]);
-        if constexpr (FUSED) bip[i] = load_param<S, VEC>(a.bias, s, m, ok[i]);
+        if constexpr (PREG) {
+            gp[i] = load_param<S, VEC>(a.gamma, s, m, ok[i]);
+            bp[i] = load_param<S, VEC>(a.beta, s, m, ok[i]);
+            bip[i] = load_param<S, VEC>(a.bias, s, m, ok[i]);
+        }
     }
+    auto param = [&](const void* base, const u32x4* regs, int i) -> u32x4 {
+        if constexpr (PREG) return regs[i];
+        else return load_param<S, VEC>(base, i * G + lg, m, ok[i]);
+    };
+    // vector path: the lane's byte offset of each slot in its wave's row view
+    uint32_t vo[VEC ? V : 1];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) vo[i] = slot_offset<S, G>(tid, i, m, ok[i]);
+    }
+    const int wrow = wave_first_row<G>(tid);
+    // the rows of block blk that this wave touches (uniform across the wave)
+    auto view = [&](const void* base, int64_t blk) {
+        const int64_t row0 = blk * ROWS + wrow;
+        const int64_t left = a.rows - row0;
+        return row_view<S>(base, row0, left < WaveRows<G>::N ? left : WaveRows<G>::N, m);
+    };
 
     auto load_row = [&](RowBuf<V, FUSED>& b, int64_t blk) {
         const int64_t row = blk * ROWS + rloc;
         const bool rok = row < a.rows;
         const int64_t r = rok ? row : 0;
         if constexpr (VEC) {
-            const u32x4* px = lane_slots<S>(a.x, r, m, lg);
-            const u32x4* pr = FUSED ? lane_slots<S>(a.residual, r, m, lg) : nullptr;
+            const rsrc_t vx = view(a.x, blk);
+            const rsrc_t vr = view(FUSED ? a.residual : a.x, blk);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                b.x[i] = nt_load(px + i * G, ok[i] && rok);
-                if constexpr (FUSED) b.r[i] = nt_load(pr + i * G, ok[i] && rok);
+                b.x[i] = buf_load_nt(vx, vo[i]);
+                if constexpr (FUSED) b.r[i] = buf_load_nt(vr, vo[i]);
             }
         } else {
 #pragma unroll
@@ -112,44 +135,25 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
 
     __shared__ float lds[2][ROWS][WPR][4];
 
-    // The row is kept packed in T (16-bit types: half the registers) and
-    // unpacked again by each pass over it.
+    // The streaming inputs of a block stay packed in T (16-bit types: half
+    // the registers) until the block is processed; the values being
+    // normalised are unpacked once and then held as floats through the
+    // three passes.
     auto process = [&](const RowBuf<V, FUSED>& b, int64_t blk, int it) {
         const int64_t row = blk * ROWS + rloc;
         const bool rok = row < a.rows;
         const int64_t r = rok ? row : 0;
-        keep_packed(gp);
-        keep_packed(bp);
-        u32x4 zp[V];   // the values being normalised, packed (x, or the stored z)
+        if constexpr (PREG) {
+            keep_packed(gp);
+            keep_packed(bp);
+        }
+        // the values being normalised: x, or the stored z (as rounded to T)
+        float v[V][E];
         // element e of slot i lies in the row
         auto inside = [&](int i, int e) { return ok[i] && (VEC || (i * G + lg) * E + e < m); };
-        // Shift: the first value of this wave's part of the row.  Pass 1: the
-        // sum of the shifted values of the row (outside elements count 0; on
-        // the vector path a slot is wholly inside or outside).
-        float c = 0.0f, s_l = 0.0f;
-        auto add_slot = [&](int i, const float* v) {
-            if constexpr (VEC) {
-                float ss = 0.0f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) ss += v[e] - c;
-                s_l += ok[i] ? ss : 0.0f;
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) s_l += inside(i, e) ? v[e] - c : 0.0f;
-            }
-        };
-        // fp32 rows are shifted so a large mean cannot swamp the sums; 16-bit
-        // rows hold at most 11 significant bits, and fp32 sums of them stay
-        // accurate far beyond their storage step, so they are not shifted
-        auto set_shift = [&](const float* v0) {
-            if constexpr (S::BYTES == 4) {
-                c = (G <= 64) ? group_broadcast_first<(G <= 64 ? G : 64)>(v0[0], lane)
-                              : lane_read(v0[0], 0);
-            }
-        };
         if constexpr (FUSED) {
-            keep_packed(bip);
-            u32x4* pz = VEC ? lane_slots<S>(a.residual_out, r, m, lg) : nullptr;
+            if constexpr (PREG) keep_packed(bip);
+            const rsrc_t vz = view(a.residual_out, blk);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 const bool sok = ok[i] && rok;
@@ -157,69 +161,78 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
                 float xv[E], rv[E], bv[E];
                 S::unpack(b.x[i], xv);
                 S::unpack(b.r[i], rv);
-                S::unpack(bip[i], bv);
-                const uint32_t bits = sok ? keep_bits<E>(row, col0, a.seed_lo, a.seed_hi, a.thr) : 0u;
+                S::unpack(param(a.bias, bip, i), bv);
+                // (slots outside the tensor are never stored, so their
+                // uniforms do not matter)
+                const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
                 float z[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float t = xv[e] + bv[e];
-                    const float d = ((bits >> e) & 1u) ? t * a.scale : 0.0f;
-                    z[e] = rv[e] + d;
+                    // z = r + keep * (x + bias) / (1 - p), the scaling and the
+                    // residual add rounded once
+                    const float t = kept<E>(w, col0, e, a.thr) ? xv[e] + bv[e] : 0.0f;
+                    z[e] = fmaf(t, a.scale, rv[e]);
                 }
                 // z is stored in T; the LayerNorm runs on the stored value.
-                zp[i] = S::pack(z);
+                const u32x4 zp = S::pack(z);
                 if constexpr (VEC) {
-                    if (sok) __builtin_nontemporal_store(zp[i], pz + i * G);
+                    buf_store_nt(zp, vz, vo[i]);
                 } else {
                     store_elems<S>(a.residual_out, r, m, col0, sok, z);
                 }
-                float v[E];
-                S::unpack(zp[i], v);
-                if (i == 0) set_shift(v);
-                add_slot(i, v);
+                S::unpack(zp, v[i]);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < V; ++i) zp[i] = b.x[i];
-            keep_packed(zp);
+            for (int i = 0; i < V; ++i) S::unpack(b.x[i], v[i]);
+        }
+        // Shift c: the first value of this wave's part of the row.  fp32 rows
+        // are shifted so a large mean cannot swamp the sums; 16-bit rows hold
+        // at most 11 significant bits, and fp32 sums of them stay accurate far
+        // beyond their storage step, so they are not shifted (c = 0).
+        float c = 0.0f;
+        if constexpr (S::BYTES == 4) {
+            c = (G <= 64) ? group_broadcast_first<(G <= 64 ? G : 64)>(v[0][0], lane)
+                          : lane_read(v[0][0], 0);
+        }
+        // pass 1: the sum of the shifted values (outside elements count 0; on
+        // the vector path a slot is wholly inside or outside)
+        float s_l = 0.0f;
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float v[E];
-                S::unpack(zp[i], v);
-                if (i == 0) set_shift(v);
-                add_slot(i, v);
+        for (int i = 0; i < V; ++i) {
+            if constexpr (VEC) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) ss += v[i][e] - c;
+                s_l += ok[i] ? ss : 0.0f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) s_l += inside(i, e) ? v[i][e] - c : 0.0f;
             }
         }
-        // pass 2: sum of squared deviations from a mean m_l
-        auto sq_dev = [&](float m_l) {
-            keep_packed(zp);
+        // pass 2: the sum of squared deviations from a mean m_l of the shifted
+        // values; with `keep` the deviations replace the values in place
+        // (the last pass needs exactly them)
+        auto sq_dev = [&](float m_l, bool keep) {
             float q_l = 0.0f;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                float v[E];
-                S::unpack(zp[i], v);
-                if constexpr (VEC) {
-                    float qq = 0.0f;
+                float qq = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const float d = (v[e] - c) - m_l;
-                        qq = fmaf(d, d, qq);
-                    }
-                    q_l += ok[i] ? qq : 0.0f;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const float d = inside(i, e) ? (v[e] - c) - m_l : 0.0f;
-                        q_l = fmaf(d, d, q_l);
-                    }
+                for (int e = 0; e < E; ++e) {
+                    const float d = (VEC || inside(i, e)) ? (v[i][e] - c) - m_l : 0.0f;
+                    if (keep) v[i][e] = d;
+                    if constexpr (VEC) qq = fmaf(d, d, qq);
+                    else q_l = fmaf(d, d, q_l);
                 }
+                if constexpr (VEC) q_l += ok[i] ? qq : 0.0f;
             }
             return q_l;
         };
         float mu, var;   // mean of (v - c) for this wave's shift, variance
         if constexpr (G <= 64) {
             mu = group_sum<G>(s_l) * a.inv_m;
-            var = group_sum<G>(sq_dev(mu)) * a.inv_m;
+            var = group_sum<G>(sq_dev(mu, true)) * a.inv_m;
         } else {
             // this wave's exact state, then one exchange and a fixed-order
             // Chan merge (wave 0, 1, ...) done identically by every lane
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
             const float n_w = group_sum<64>(n_l);
             const float s_w = group_sum<64>(s_l);
             const float mu_w = n_w > 0.0f ? s_w / n_w : 0.0f;
-            const float q_w = group_sum<64>(sq_dev(mu_w));
+            const float q_w = group_sum<64>(sq_dev(mu_w, false));
             const int w = lg / 64;
             const int buf = it & 1;   // double buffer: one barrier per block
             if (lane == 0) {
@@ -256,25 +269,27 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
             // mean relative to this wave's own shift c
             mu = tot.s / tot.n - (c - c0);
             var = tot.q / tot.n;
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[i][e] = (v[i][e] - c) - mu;
         }
         const float rs = 1.0f / sqrtf(var + a.eps);
         if (lg == 0 && rok) {
             if (a.mean) a.mean[row] = c + mu;
             if (a.rstd) a.rstd[row] = rs;
         }
-        // pass 3: normalise and apply the affine map
-        keep_packed(zp);
-        u32x4* py = VEC ? lane_slots<S>(a.y, r, m, lg) : nullptr;
+        // pass 3: normalise the deviations (now in v) and apply the affine map
+        const rsrc_t vy = view(a.y, blk);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            float v[E], ga[E], be[E], out[E];
-            S::unpack(zp[i], v);
-            S::unpack(gp[i], ga);
-            S::unpack(bp[i], be);
+            float ga[E], be[E], out[E];
+            S::unpack(param(a.gamma, gp, i), ga);
+            S::unpack(param(a.beta, bp, i), be);
 #pragma unroll
-            for (int e = 0; e < E; ++e) out[e] = fmaf(((v[e] - c) - mu) * rs, ga[e], be[e]);
+            for (int e = 0; e < E; ++e) out[e] = fmaf(v[i][e] * rs, ga[e], be[e]);
             if constexpr (VEC) {
-                if (ok[i] && rok) __builtin_nontemporal_store(S::pack(out), py + i * G);
+                buf_store_nt(S::pack(out), vy, vo[i]);
             } else {
                 store_elems<S>(a.y, r, m, (i * G + lg) * E, ok[i] && rok, out);
             }
@@ -327,11 +342,11 @@ __global__ __launch_bounds__(256) void ln_dropout_mask_kernel(uint8_t* __restric
          q += (int64_t)gridDim.x * blockDim.x) {
         const int64_t row = q / groups;
         const int col0 = (int)(q - row * groups) * 8;
-        const uint32_t bits = keep_bits<8>(row, col0, seed_lo, seed_hi, thr);
+        const u32x4 w = dropout_words(row, col0, seed_lo, seed_hi, thr);
         uint8_t* dst = mask + row * (int64_t)m + col0;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (col0 + e < m) dst[e] = (uint8_t)((bits >> e) & 1u);
+            if (col0 + e < m) dst[e] = kept<8>(w, col0, e, thr) ? 1 : 0;
     }
 }
 #endif
