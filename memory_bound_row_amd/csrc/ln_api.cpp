@@ -54,10 +54,12 @@ static bool have_instance(bool f32, int g, int v) {
 
 static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0}, g_force_grid{0};
 
-// Row layout: among the candidate layouts, the one with the fewest unused
-// slots; ties go to the earlier candidate.
+// Row layout: among the candidate layouts, the one with the fewest slots
+// (used or not); ties go to the earlier candidate.  With `wave_rows`, slots
+// of a layout whose row is not exactly one wave (G != 64) count 5/4: one row
+// per wave measured faster in the backward even with some lanes idle.
 static Path pick(bool f32, int64_t ns, bool vec, const int (*prefer)[2], int nprefer,
-                 bool need_prefetch = false) {
+                 bool wave_rows = false) {
     Path p;
     p.vec = vec && g_force_scalar.load(std::memory_order_relaxed) == 0;
     const int fg = g_force_g.load(std::memory_order_relaxed);
@@ -71,27 +73,24 @@ static Path pick(bool f32, int64_t ns, bool vec, const int (*prefer)[2], int npr
     for (int k = 0; k < nprefer; ++k) {
         const int64_t cap = (int64_t)prefer[k][0] * prefer[k][1];
         if (cap < ns) continue;
-        if (need_prefetch && !bwd_prefetch(prefer[k][0], prefer[k][1], f32 ? 4 : 8, true))
-            continue;
-        const int64_t waste = cap - ns;
-        if (best < 0 || waste < best) {
-            best = waste;
+        const int64_t cost = wave_rows ? cap * (prefer[k][0] == 64 ? 4 : 5) : cap;
+        if (best < 0 || cost < best) {
+            best = cost;
             p.g = prefer[k][0];
             p.v = prefer[k][1];
         }
     }
     if (best < 0) {
-        if (need_prefetch) return pick(f32, ns, vec, prefer, nprefer, false);
         p.g = f32 ? 1024 : 512;   // wider than every layout: callers cap cols
         p.v = 4;
     }
     return p;
 }
 
-// Candidate layouts in order of preference for equal waste.  Within a wave a
-// lane holds at most 32 values of a row in the forward (8 fp32 or 4-5 16-bit
-// slots) and at most 40 in the backward, which also keeps two column
-// accumulators per value; wider rows spread over several waves.
+// Candidate layouts in order of preference for equal cost.  Within a wave a
+// lane holds at most 32 fp32 or 40 16-bit values of a row (8 or 5 slots; the
+// backward also keeps two column accumulators per value); wider rows spread
+// over several waves.
 static const int kFwd32[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
                                 {32, 4}, {64, 3}, {32, 5}, {32, 6}, {64, 4}, {32, 7}, {32, 8},
                                 {64, 5}, {64, 6}, {64, 7}, {64, 8}, {128, 4}, {256, 4},
@@ -100,10 +99,12 @@ static const int kFwd16[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32
                                 {32, 4}, {64, 3}, {32, 5}, {64, 4}, {128, 4}, {256, 4},
                                 {512, 4}};
 static const int kBwd32[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
-                                {32, 4}, {64, 3}, {32, 5}, {32, 6}, {64, 4}, {64, 5}, {64, 6},
-                                {128, 4}, {256, 4}, {512, 4}, {1024, 4}};
+                                {32, 4}, {64, 3}, {32, 5}, {32, 6}, {64, 4}, {32, 7}, {32, 8},
+                                {64, 5}, {64, 6}, {64, 7}, {64, 8}, {128, 4}, {256, 4},
+                                {512, 4}, {1024, 4}};
 static const int kBwd16[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
-                                {32, 4}, {64, 3}, {32, 5}, {128, 4}, {256, 4}, {512, 4}};
+                                {32, 4}, {64, 3}, {32, 5}, {64, 4}, {64, 5}, {128, 4}, {256, 4},
+                                {512, 4}};
 
 #define MBROW_N(a) (int)(sizeof(a) / sizeof(a[0]))
 
@@ -120,8 +121,9 @@ Path pick_path(Dt dt, int64_t cols, bool vec) {
 Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool partials) {
     const int E = elems_per_slot(dt);
     const int64_t ns = (cols + E - 1) / E;
-    return E == 4 ? pick(true, ns, vec, kBwd32, MBROW_N(kBwd32), partials)
-                  : pick(false, ns, vec, kBwd16, MBROW_N(kBwd16), partials);
+    (void)partials;
+    return E == 4 ? pick(true, ns, vec, kBwd32, MBROW_N(kBwd32), true)
+                  : pick(false, ns, vec, kBwd16, MBROW_N(kBwd16), true);
 }
 
 int64_t persistent_grid(const void* kernel, int threads, int64_t blocks) {

@@ -8,13 +8,19 @@
 // both, and dx = rstd*(g - (A + xhat*B)/m).
 //
 // dgamma/dbeta (§2.4 of the same page): a column sum over rows cannot use the
-// row-per-group layout directly; rows are split into P contiguous ranges,
-// one workgroup per range.  Each lane accumulates dy*xhat and dy for the
-// columns it owns, row after row in ascending order; the row groups of the
-// workgroup are folded in a fixed tree (in-wave swizzles, then LDS); the
-// workgroup writes one [2][m] partial.  A second small kernel adds the P
-// partials in a fixed order.  No floating-point atomics anywhere, so every
-// run gives the same bits.
+// row-per-group layout directly; the rows are split into P partitions, one
+// workgroup each.  The row blocks are dealt to the partitions in turn, so
+// the workgroups stream through the tensor side by side.  Each lane
+// accumulates dy*xhat and dy for the columns it owns, block after block;
+// the row groups of the workgroup are folded in a fixed tree (in-wave lane
+// exchanges, then LDS); the workgroup writes one [2][m] partial.  A second
+// small kernel adds the P partials in a fixed order.  No floating-point
+// atomics anywhere, so every run gives the same bits.
+//
+// Schedule.  One row block at a time per workgroup, its loads issued
+// together at the top of the iteration; all P workgroups are resident, so
+// the memory system sees P blocks in flight.  (Measured: prefetching the
+// next block as well slows this kernel down on gfx950.)
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 
@@ -49,12 +55,6 @@ struct BwdGeometry {
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
-template <int V>
-struct BwdRowBuf {
-    u32x4 x[V], d[V];
-    float mu, rs;
-};
-
 template <class S, int G, int V, bool VEC, int MODE>
 __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     constexpr int E = S::E;
@@ -71,21 +71,21 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     const int m = (int)a.m;
     const int nslots = (int)a.nslots;
 
+    // Partition `part` owns the blocks of NG consecutive rows starting at
+    // rows part*NG, (part + P)*NG, (part + 2P)*NG, ...: the workgroups walk
+    // the tensor side by side, one window of P*NG rows at a time.
     const int64_t part = blockIdx.x;
-    const int64_t r0 = part * a.rows / a.parts;
-    const int64_t r1 = (part + 1) * a.rows / a.parts;
+    const int64_t first = part * NG;
+    const int64_t stride = a.parts * NG;
 
-    // slot i of this lane covers columns (i*G + lg)*E .. +E-1
+    // slot i of this lane covers columns (i*G + lg)*E .. +E-1; gamma stays
+    // packed in T in registers
     bool ok[V];
-    // gamma, packed in T: kept in registers, except with 32-lane rows and
-    // partials, where the registers go to the second row buffer and gamma is
-    // re-read (from cache) where used
-    constexpr bool GREG = !(PART && G == 32);
-    u32x4 gp[GREG ? V : 1];
+    u32x4 gp[DX ? V : 1];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         ok[i] = i * G + lg < nslots;
-        if constexpr (DX && GREG) gp[i] = load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
+        if constexpr (DX) gp[i] = load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
     }
     // vector path: the lane's byte offset of each slot in its wave's row view
     uint32_t vo[VEC ? V : 1];
@@ -94,72 +94,54 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         for (int i = 0; i < V; ++i) vo[i] = slot_offset<S, G>(tid, i, m, ok[i]);
     }
     const int wrow = wave_first_row<G>(tid);
-    // the rows of the block starting at `base` that this wave touches, within
-    // the partition (uniform across the wave)
+    // the rows of the block starting at `base` that this wave touches
+    // (uniform across the wave)
     auto view = [&](const void* t, int64_t base) {
         const int64_t row0 = base + wrow;
-        const int64_t left = r1 - row0;
+        const int64_t left = a.rows - row0;
         return row_view<S>(t, row0, left < WaveRows<G>::N ? left : WaveRows<G>::N, m);
     };
-    auto gamma_slot = [&](int i) -> u32x4 {
-        if constexpr (GREG) return gp[i];
-        else return load_param<S, VEC>(a.gamma, i * G + lg, m, ok[i]);
-    };
-    // Column accumulators.  With 32-lane rows the two row groups of a wave
-    // own the same columns; elements e and e + E/2 of each slot are summed
-    // over both rows with one lane swap, the lower half of the wave keeping
-    // the first and the upper half the second, so a lane carries half the
-    // columns.
-    constexpr bool SPLIT = PART && G == 32;
-    constexpr int KA = PART ? bwd_accumulators(G, V, E) : 1;
+
+    // Column accumulators: one per value of the lane's slots and kind.
+    constexpr int KA = PART ? V * E : 1;
     float acc_g[KA], acc_b[KA];
 #pragma unroll
     for (int k = 0; k < KA; ++k) acc_g[k] = acc_b[k] = 0.0f;
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
-    auto load_row = [&](BwdRowBuf<V>& b, int64_t base) {
+    // One block at a time: its loads, then pass 1 (x-hat and g formed slot
+    // by slot from the packed row, the two row sums), then pass 2 (x-hat
+    // and g formed again for dx and the column partials).  The partials use
+    // the same expressions in every mode, so the fused and the partials-only
+    // passes produce the same bits.  The walk is uniform per workgroup, so
+    // the barrier of a multi-wave row is reached by all.
+    int it = 0;
+    for (int64_t base = first; base < a.rows; base += stride, ++it) {
         const int64_t row = base + grp;
-        const bool rok = row < r1;
-        const int64_t r = rok ? row : 0;
+        const bool rok = row < a.rows;
+        const int64_t r = rok ? row : 0;   // rows past the end read row 0's statistics
+        u32x4 xr[V], dr[V];
         if constexpr (VEC) {
+            // rows past the end read 0 and are never stored
             const rsrc_t vd = view(a.dy, base);
             const rsrc_t vx = view(a.x, base);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                b.d[i] = buf_load_nt(vd, vo[i]);
-                b.x[i] = buf_load_nt(vx, vo[i]);
+                dr[i] = buf_load_nt(vd, vo[i]);
+                xr[i] = buf_load_nt(vx, vo[i]);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 float f[E];
                 load_elems<S>(a.dy, r, m, (i * G + lg) * E, ok[i] && rok, f);
-                b.d[i] = S::pack(f);
+                dr[i] = S::pack(f);
                 load_elems<S>(a.x, r, m, (i * G + lg) * E, ok[i] && rok, f);
-                b.x[i] = S::pack(f);
+                xr[i] = S::pack(f);
             }
         }
-        b.mu = rok ? a.mean[row] : 0.0f;
-        b.rs = rok ? a.rstd[row] : 0.0f;
-    };
-
-    // Pass 1 forms x-hat and g slot by slot from the packed row and
-    // accumulates the two row sums; pass 2 forms them again for dx (and the
-    // column partials) instead of keeping them in registers.  The partials
-    // use the same expressions in every mode, so the fused and the
-    // partials-only passes produce the same bits.
-    auto process = [&](const BwdRowBuf<V>& b, int64_t base, int it) {
-        const int64_t row = base + grp;
-        const bool rok = row < r1;
-        const int64_t r = rok ? row : 0;
-        const float mu = b.mu, rs = b.rs;
-        if constexpr (DX && GREG) keep_packed(gp);
-        u32x4 xr[V], dr[V];
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            xr[i] = b.x[i];
-            dr[i] = b.d[i];
-        }
+        const float mu = a.mean[r], rs = a.rstd[r];
+        if constexpr (DX) keep_packed(gp);
         float c1 = 0.0f, c2 = 0.0f;
         if constexpr (DX) {
             float A = 0.0f, B = 0.0f;
@@ -168,7 +150,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 float x[E], d[E], ga[E];
                 S::unpack(xr[i], x);
                 S::unpack(dr[i], d);
-                S::unpack(gamma_slot(i), ga);
+                S::unpack(gp[i], ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float xh = (x[e] - mu) * rs;
@@ -184,7 +166,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 A = group_sum<64>(A);
                 B = group_sum<64>(B);
                 const int w = lg / 64;
-                const int buf = it & 1;   // double buffer: one barrier per row
+                const int buf = it & 1;   // double buffer: one barrier per block
                 if (lane == 0) {
                     red[buf][grp][w][0] = A;
                     red[buf][grp][w][1] = B;
@@ -204,12 +186,9 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             c1 = A * a.inv_m;
             c2 = B * a.inv_m;
         }
-        // Pass 2, slot by slot: dx (when formed) and the column partials.
-        // The partials use the same expressions whether or not dx is formed,
-        // so the fused and the partials-only passes give the same bits.
         keep_packed(xr);
         keep_packed(dr);
-        if constexpr (DX && GREG) keep_packed(gp);
+        if constexpr (DX) keep_packed(gp);
         const rsrc_t vdx = view(DX ? a.dx : a.dy, base);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
@@ -220,7 +199,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             for (int e = 0; e < E; ++e) xh[e] = (x[e] - mu) * rs;
             if constexpr (DX) {
                 float ga[E], out[E];
-                S::unpack(gamma_slot(i), ga);
+                S::unpack(gp[i], ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e) out[e] = rs * (ga[e] * d[e] - fmaf(xh[e], c2, c1));
                 if constexpr (VEC) {
@@ -229,16 +208,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                     store_elems<S>(a.dx, r, m, (i * G + lg) * E, ok[i] && rok, out);
                 }
             }
-            if constexpr (SPLIT) {
-                // element e of the slot pairs with e + E/2: the lower half of
-                // the wave keeps the first, the upper half the second
-#pragma unroll
-                for (int e = 0; e < E / 2; ++e) {
-                    const int k = i * (E / 2) + e;
-                    acc_g[k] = acc_g[k] + halves_sum_swap(d[e] * xh[e], d[e + E / 2] * xh[e + E / 2]);
-                    acc_b[k] = acc_b[k] + halves_sum_swap(d[e], d[e + E / 2]);
-                }
-            } else if constexpr (PART) {
+            if constexpr (PART) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     acc_g[i * E + e] = fmaf(d[e], xh[e], acc_g[i * E + e]);
@@ -249,45 +219,14 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             // several slots' temporaries at once)
             __builtin_amdgcn_sched_barrier(0);
         }
-    };
-
-    int64_t base = r0;
-    int it = 0;
-    // Prefetch needs a second row buffer; without room for it beside the
-    // column accumulators the walk is single-buffered.
-    constexpr bool PF = bwd_prefetch(G, V, E, PART);
-    if constexpr (PF) {
-        BwdRowBuf<V> b0, b1;
-        if (base < r1) load_row(b0, base);
-        while (base < r1) {
-            int64_t nxt = base + NG;
-            if (nxt < r1) load_row(b1, nxt);
-            process(b0, base, it++);
-            __builtin_amdgcn_sched_barrier(0);
-            base = nxt;
-            if (base >= r1) break;
-            nxt = base + NG;
-            if (nxt < r1) load_row(b0, nxt);
-            process(b1, base, it++);
-            __builtin_amdgcn_sched_barrier(0);
-            base = nxt;
-        }
-    } else {
-        // single buffer: 1024-lane rows (16 waves per row already keep loads
-        // in flight and the 128-VGPR budget has no room for a second
-        // buffer), and lanes with many column accumulators
-        BwdRowBuf<V> b0;
-        for (; base < r1; base += NG) {
-            load_row(b0, base);
-            process(b0, base, it++);
-        }
     }
 
     if constexpr (PART) {
+        // Rows of one wave that own the same columns are folded inside the
+        // wave first: lanes l, l+16, l+32, l+48 (16-lane rows) or l, l+32
+        // (32-lane rows).  Adds are commutative, so partners agree bit for
+        // bit and every row group ends with the wave's sums.
         if constexpr (G == 16) {
-            // Fold the four row groups of each wave: lanes l, l+16, l+32, l+48
-            // own the same columns.  Adds are commutative, so partners agree
-            // bit for bit and every group ends with the wave's sums.
 #pragma unroll
             for (int k = 0; k < KA; ++k) {
                 acc_g[k] = acc_g[k] + partner<16>(acc_g[k]);
@@ -295,18 +234,23 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 acc_g[k] = acc_g[k] + xor32(acc_g[k]);
                 acc_b[k] = acc_b[k] + xor32(acc_b[k]);
             }
+        } else if constexpr (G == 32) {
+#pragma unroll
+            for (int k = 0; k < KA; ++k) {
+                acc_g[k] = halves_sum_swap(acc_g[k], acc_g[k]);
+                acc_b[k] = halves_sum_swap(acc_b[k], acc_b[k]);
+            }
         }
-        // Fold the units whose lanes own the same columns (the waves of the
+        // Then the units whose lanes own the same columns (the waves of the
         // workgroup for G <= 64, its row groups otherwise): every unit stages
         // its sums in LDS, one barrier, then the workgroup adds them in unit
         // order (0, 1, ...) column by column, consecutive threads taking
         // consecutive columns, and writes the workgroup's partial.  The
         // accumulators go through LDS in chunks of CI slot indices so the
         // footprint stays within 64 KB.
-        constexpr int KPI = SPLIT ? E / 2 : E;                  // accumulators per slot index
         constexpr int KF = 65536 / (NU * 2 * UT * 4);           // floats per lane that fit
-        constexpr int CI = (KF - 1) / KPI < 1 ? 1 : ((KF - 1) / KPI < V ? (KF - 1) / KPI : V);
-        constexpr int CK = CI * KPI + 1;                        // padded lane stride
+        constexpr int CI = (KF - 1) / E < 1 ? 1 : ((KF - 1) / E < V ? (KF - 1) / E : V);
+        constexpr int CK = CI * E + 1;                          // padded lane stride
         constexpr int CW = CI * G * E;                          // columns per chunk
         static_assert(NU * 2 * UT * CK * 4 <= 65536, "stage exceeds 64 KB");
         __shared__ float stage[NU][2][UT][CK];
@@ -318,8 +262,8 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         for (int i0 = 0; i0 < V; i0 += CI) {
             if (i0 > 0) __syncthreads();   // previous chunk fully read
 #pragma unroll
-            for (int c = 0; c < CI * KPI; ++c) {
-                const int k = i0 * KPI + c;
+            for (int c = 0; c < CI * E; ++c) {
+                const int k = i0 * E + c;
                 if (k < KA) {
                     stage[unit][0][pos][c] = acc_g[k];
                     stage[unit][1][pos][c] = acc_b[k];
@@ -332,21 +276,14 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 const int cl = q - kind * CW;
                 const int col = col0 + cl;
                 if (col >= m) continue;
-                // lane and accumulator holding column col: slot col/E, element col%E
+                // lane (of the first row group) and accumulator holding
+                // column col: slot col/E, element col%E
                 const int sl = cl / E, ee = cl % E;
                 const int il = sl / G, lig = sl % G;
-                int c, p;
-                if constexpr (SPLIT) {
-                    // element ee < E/2 in the lower half of the wave, else the upper
-                    c = il * KPI + ee % KPI;
-                    p = lig + (ee / KPI) * 32;
-                } else {
-                    c = il * E + ee;
-                    p = lig;
-                }
-                float t = stage[0][kind][p][c];
+                const int c = il * E + ee;
+                float t = stage[0][kind][lig][c];
 #pragma unroll
-                for (int u = 1; u < NU; ++u) t = t + stage[u][kind][p][c];
+                for (int u = 1; u < NU; ++u) t = t + stage[u][kind][lig][c];
                 (kind == 0 ? pg : pb)[col] = t;
             }
         }

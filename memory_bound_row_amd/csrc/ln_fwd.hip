@@ -74,9 +74,9 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
     // slot i of this lane covers columns (i*G + lg)*E .. +E-1
     bool ok[V];
     // The fused kernel keeps gamma, beta and bias packed in T in registers
-    // across rows; the plain one re-reads gamma and beta (from cache) for
-    // every row, which leaves room for more resident waves and measured
-    // faster there.
+    // across rows.  The plain one re-reads gamma and beta (from cache) in
+    // its last pass: measured clearly faster on gfx950, although the wait
+    // for such a load also covers the prefetched next block.
     constexpr bool PREG = FUSED;
     u32x4 gp[PREG ? V : 1], bp[PREG ? V : 1], bip[PREG ? V : 1];
 #pragma unroll
@@ -300,21 +300,25 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
     // of a multi-wave row is reached by all.  Double-buffered (the next
     // block's loads are in flight while this one is reduced) except for
     // 1024-lane rows, whose 16 waves already keep enough loads in flight and
-    // whose 128-VGPR budget has no room for a second buffer.
+    // whose 128-VGPR budget has no room for a second buffer.  The next
+    // block's loads are issued unconditionally (past the last block they
+    // read nothing): a conditional prefetch would make the wait for the
+    // current block also wait for the prefetch, since loads retire in order
+    // and the wait must hold on the path without it.
     int64_t blk = blockIdx.x;
     const int64_t step = gridDim.x;
     int it = 0;
     if constexpr (Geometry<G>::NT <= 512) {
         RowBuf<V, FUSED> b0, b1;
-        if (blk < nblk) load_row(b0, blk);
+        load_row(b0, blk);
         while (blk < nblk) {
             int64_t nxt = blk + step;
-            if (nxt < nblk) load_row(b1, nxt);
+            load_row(b1, nxt);
             process(b0, blk, it++);
             blk = nxt;
             if (blk >= nblk) break;
             nxt = blk + step;
-            if (nxt < nblk) load_row(b0, nxt);
+            load_row(b0, nxt);
             process(b1, blk, it++);
             blk = nxt;
         }

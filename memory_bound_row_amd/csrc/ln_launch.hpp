@@ -75,22 +75,9 @@ enum class BwdMode : int { DX = 0, DX_PARTIALS = 1, PARTIALS = 2 };
 // Threads per workgroup of the backward for G lanes per row.
 constexpr int bwd_threads(int g) { return g <= 512 ? 512 : g; }
 
-// Column accumulators per lane and kind in the backward: one per value of
-// the lane's row slots, or half as many for 32-lane rows, whose two row
-// groups per wave split the columns between the wave's halves.
-constexpr int bwd_accumulators(int g, int v, int e) { return g == 32 ? v * e / 2 : v * e; }
-
-// Whether the backward double-buffers its rows: the second row buffer
-// (V * 8 registers) must fit beside the column accumulators (two kinds when
-// partials are on) and packed gamma within an estimated 130 registers.
-constexpr bool bwd_prefetch(int g, int v, int e, bool partials) {
-    return bwd_threads(g) <= 512 &&
-           (partials ? 2 * bwd_accumulators(g, v, e) : 0) + 2 * v * 8 +
-                   ((partials && g == 32) ? 0 : v * 4) <= 130;
-}
-
 // Row partitions of the dgamma/dbeta stage-1 pass: a pure function of
-// (rows, cols).  Every partition owns at least one row.
+// (rows, cols).  Partition p owns the blocks of rows p, p + P, p + 2P, ...
+// of the backward's row blocks; a partition without rows writes zeros.
 int64_t bwd_partitions(int64_t rows, int64_t cols);
 
 // Path selection from (dtype, cols, alignment); honours the test-only
