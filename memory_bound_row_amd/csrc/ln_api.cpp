@@ -115,13 +115,11 @@ Path pick_path(Dt dt, int64_t cols, bool vec) {
                   : pick(false, ns, vec, kFwd16, MBROW_N(kFwd16));
 }
 
-// With column partials, a layout that can double-buffer its rows beside the
-// accumulators wins over one that wastes fewer slots; the partials-only pass
-// makes the same choice, so both accumulate in the same order.
-Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool partials) {
+// The same choice with and without partials, so the fused and the
+// partials-only passes accumulate in the same order.
+Path pick_bwd_path(Dt dt, int64_t cols, bool vec) {
     const int E = elems_per_slot(dt);
     const int64_t ns = (cols + E - 1) / E;
-    (void)partials;
     return E == 4 ? pick(true, ns, vec, kBwd32, MBROW_N(kBwd32), true)
                   : pick(false, ns, vec, kBwd16, MBROW_N(kBwd16), true);
 }
@@ -340,7 +338,7 @@ ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const fl
     a.parts = bwd_partitions(rows, cols);
     a.inv_m = (float)(1.0 / (double)cols);
     const BwdMode mode = workspace ? BwdMode::DX_PARTIALS : BwdMode::DX;
-    return from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec, workspace != nullptr), mode, a,
+    return from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec), mode, a,
                                stream));
 }
 
@@ -376,7 +374,7 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
         a.parts = parts;
         a.inv_m = (float)(1.0 / (double)cols);
         st = from_hip(
-            launch_bwd(d, pick_bwd_path(d, cols, vec, true), BwdMode::PARTIALS, a, stream));
+            launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::PARTIALS, a, stream));
         if (st != LN_OK) return st;
     }
     return from_hip(launch_fold(workspace, parts, cols, dgamma, dbeta, stream));

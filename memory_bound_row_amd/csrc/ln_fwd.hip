@@ -16,12 +16,14 @@
 // current block is reduced and written, so memory traffic and ALU work of
 // each wave overlap.
 //
-// Statistics ("Accelerating Transformer on GPU (I)" §4.2).  Values are
+// Statistics ("Accelerating Transformer on GPU (I)" §4.2).  fp32 values are
 // shifted by the first value c of the group's part of the row, so sums stay
 // small when the mean is large compared with the spread (the page's
-// E[x^2] - E[x]^2 collapse at mean 1e4).  Within a wave the mean and then the
-// sum of squared deviations are exact two-pass sums over registers, each
-// reduced by one DPP/swizzle butterfly with no barrier.  A multi-wave row
+// E[x^2] - E[x]^2 collapse at mean 1e4); 16-bit values carry few enough
+// significant bits that fp32 sums of them need no shift.  The values are
+// unpacked once per row and held as floats through the passes; within a wave
+// the mean and then the sum of squared deviations are exact two-pass sums
+// over registers, each reduced by one DPP/swizzle butterfly with no barrier.  A multi-wave row
 // merges the per-wave (count, sum, M2) states with the Chan update after one
 // LDS exchange, so it takes a single barrier.
 #include "ln_device.hpp"

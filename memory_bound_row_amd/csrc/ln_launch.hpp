@@ -83,7 +83,7 @@ int64_t bwd_partitions(int64_t rows, int64_t cols);
 // Path selection from (dtype, cols, alignment); honours the test-only
 // override set through ln_debug_force_path.
 Path pick_path(Dt dt, int64_t cols, bool vec);        // forward
-Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool partials);   // backward
+Path pick_bwd_path(Dt dt, int64_t cols, bool vec);   // backward
 int elems_per_slot(Dt dt);
 
 // Workgroups for a persistent launch of `kernel` with `threads` threads per
