@@ -56,6 +56,13 @@ def parse():
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--warm-cache", action="store_true",
                     help="one buffer set, backward on the forward's fresh z (cache-resident)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the step, measure the other workloads (decode-shaped "
+                         "launch cost, 64x768 fp32, 16384x1024 bf16 backward, wide/ragged "
+                         "rows) and print one JSON line each")
+    ap.add_argument("--no-cpp-launch", action="store_true",
+                    help="with --configs: skip the C++ launch-loop child process (for runs "
+                         "under a profiler, whose preloaded library the child inherits)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "this benchmark into profiles/traffic.json and exit")
@@ -148,6 +155,44 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(rec, indent=1))
 
 
+def capture(fn, n):
+    """HIP graph of fn(0) .. fn(n-1) captured on a side stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)                                      # warm the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    return g
+
+
+def timed(g, n):
+    """Milliseconds per item of one replay of graph g holding n items
+    (after one untimed replay), between HIP events."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def plain_bytes(rows: int, cols: int, s: int) -> dict:
+    """Algorithmic bytes of ln_fwd and of the backward (dx, dgamma, dbeta)."""
+    fwd = 2 * rows * cols * s + 2 * cols * s + 8 * rows
+    bwd = 3 * rows * cols * s + cols * s + 8 * rows + 8 * cols
+    return {"fwd": fwd, "bwd": bwd, "step": fwd + bwd}
+
+
 def cpu_baseline(inp_cpu, target_s: float):
     """The float64 oracle, as it stands, on the host: the same step on the
     same stored values (single thread)."""
@@ -177,10 +222,135 @@ def cpu_baseline(inp_cpu, target_s: float):
             "rows_per_s": round(rows_s * reps / t_total, 1)}
 
 
+def configs_report(cpp_launch: bool = True) -> None:
+    """Figures of the workloads other than the step, one JSON line each:
+      * decode-shaped fp16 ln_fwd, 1 and 8 rows x 4096, 10^4 back-to-back
+        calls without saved statistics: microseconds per call from a C++
+        loop (the `launch_bench` tool, run first as a child process), a
+        Python loop through the binding, and a HIP graph of the calls;
+      * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
+      * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
+      * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
+        forward + backward (each pass moves more than the cache holds)."""
+    import subprocess
+    tool = os.path.join(ROOT, "memory_bound_row_amd", "launch_bench")
+    if not os.path.exists(tool):
+        raise RuntimeError(f"{tool} is not built (run the package build)")
+    cpp = {1: {}, 8: {}}
+    for rows in ((1, 8) if cpp_launch else ()):
+        r = subprocess.run([tool, str(rows), "4096", "10000", "1"], capture_output=True,
+                           text=True, timeout=300)
+        if r.returncode != 0:
+            raise RuntimeError(f"launch_bench failed: {r.stderr.strip()}")
+        cpp[rows] = json.loads(r.stdout)
+
+    import torch
+    import memory_bound_row_amd as mb
+    from memory_bound_row_amd import synth
+    torch.cuda.init()
+    dev = torch.device("cuda", 0)
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    # decode-shaped launch cost
+    n = 10000
+    for rows in (1, 8):
+        inp = {k: v.to(dev) for k, v in
+               synth.layer_inputs(rows, 4096, torch.float16, x_mean=3.0, x_std=2.0,
+                                  names=("x", "gamma", "beta")).items()}
+        y = torch.empty_like(inp["x"])
+
+        def call(i, inp=inp, y=y):
+            mb.ln_fwd(inp["x"], inp["gamma"], inp["beta"], EPS, y=y, stats=False)
+
+        for i in range(200):
+            call(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            call(i)
+        torch.cuda.synchronize()
+        py_us = (time.perf_counter() - t0) / n * 1e6
+        g_us = timed(capture(call, n), n) * 1e3
+        b = plain_bytes(rows, 4096, 2)["fwd"] - 8 * rows
+        emit({"workload": f"decode-shaped fp16 LayerNorm forward, {rows}x4096, no saved stats",
+              "calls": n, "bytes_per_call": b,
+              "cpp_loop_us": cpp[rows].get("cpp_loop_us"), "cpp_graph_us": cpp[rows].get("graph_us"),
+              "python_loop_us": round(py_us, 3), "torch_graph_us": round(g_us, 3)})
+
+    def fwd_bwd(rows, cols, dtype, sets, iters, label, fwd=True):
+        s = torch.tensor([], dtype=dtype).element_size()
+        inp = synth.layer_inputs(rows, cols, dtype, names=("x", "gamma", "beta", "dy"))
+        gamma, beta = inp["gamma"].to(dev), inp["beta"].to(dev)
+        st = []
+        for _ in range(sets):
+            a = {"x": inp["x"].to(dev), "dy": inp["dy"].to(dev)}
+            a["y"] = torch.empty_like(a["x"])
+            a["dx"] = torch.empty_like(a["x"])
+            a["mean"] = torch.empty(rows, dtype=torch.float32, device=dev)
+            a["rstd"] = torch.empty(rows, dtype=torch.float32, device=dev)
+            st.append(a)
+        del inp
+        ws = mb.workspace(rows, cols, dev)
+        dg = torch.empty(cols, dtype=torch.float32, device=dev)
+        db = torch.empty(cols, dtype=torch.float32, device=dev)
+
+        def f(i):
+            a = st[i % sets]
+            mb.ln_fwd(a["x"], gamma, beta, EPS, y=a["y"], mean=a["mean"], rstd=a["rstd"])
+
+        def bw(i):
+            a = st[(i + sets // 2) % sets]
+            mb.ln_bwd_dx(a["dy"], a["x"], gamma, a["mean"], a["rstd"], dx=a["dx"],
+                         workspace=ws)
+            mb.ln_bwd_dgamma_dbeta(ws, rows, cols, dtype, partials_ready=True, dgamma=dg,
+                                   dbeta=db)
+
+        def both(i):
+            if fwd:
+                f(i)
+            bw(i)
+
+        for i in range(sets):
+            f(i)
+        torch.cuda.synchronize()
+        pb = plain_bytes(rows, cols, s)
+        ms = timed(capture(both, iters), iters)
+        rec = {"workload": label, "rows": rows, "cols": cols, "storage": str(dtype)[6:],
+               "buffer_sets": sets, "iters": iters}
+        nb = pb["step"] if fwd else pb["bwd"]
+        rec["bytes_per_pass"] = nb
+        rec["us_per_pass"] = round(ms * 1e3, 3)
+        rec["GBps"] = round(nb / (ms * 1e-3) / 1e9, 1)
+        rec["pct_of_hbm_peak"] = round(100.0 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
+        if fwd:
+            msf = timed(capture(f, iters), iters)
+            rec["fwd_us"] = round(msf * 1e3, 3)
+            rec["fwd_GBps"] = round(pb["fwd"] / (msf * 1e-3) / 1e9, 1)
+        msb = timed(capture(bw, iters), iters)
+        rec["bwd_fold_us"] = round(msb * 1e3, 3)
+        rec["bwd_GBps"] = round(pb["bwd"] / (msb * 1e-3) / 1e9, 1)
+        emit(rec)
+        del st, ws
+        torch.cuda.empty_cache()
+
+    fwd_bwd(64, 768, torch.float32, 1, 1000,
+            "LayerNorm forward + backward fp32 64x768 (launch-bound)")
+    fwd_bwd(16384, 1024, torch.bfloat16, 4, 100,
+            "LayerNorm backward (dx, dgamma, dbeta) bf16 16384x1024, rotated", fwd=False)
+    for dtype in (torch.float32, torch.bfloat16):
+        for rows, cols in ((4096, 16384), (65536, 1000)):
+            fwd_bwd(rows, cols, dtype, 2, 20, "LayerNorm forward + backward, wide/ragged rows")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.configs:
+        configs_report(cpp_launch=not args.no_cpp_launch)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method's rows "
@@ -234,31 +404,6 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    def capture(fn, n):
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            fn(0)                                  # warm the capture stream
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        return g
-
-    def timed(g, n):
-        g.replay()                                 # untimed replay
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        g.replay()
-        end.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / n        # ms per item
-
     # attainable bandwidth: a plain copy of the forward's input size, rotated
     # like the step, and a large copy (also the PMC calibration kernel)
     ms_copy = timed(capture(lambda i: sets[i % S]["y"].copy_(sets[i % S]["x"]), K), K)
@@ -272,6 +417,20 @@ def main():
     ms_fwd = timed(capture(lambda i: fwd(sets[i % S]), K), K)
     ms_bwd = timed(capture(lambda i: bwd(sets[(i + S // 2) % S]), K), K)
     ms_fold = timed(capture(lambda i: fold(), K), K)
+
+    # the same step with the plain forward (ln_fwd of x, no bias/dropout/
+    # residual), whose backward reads x
+    def plain_step(i):
+        a = sets[i % S]
+        mb.ln_fwd(a["x"], shared["gamma"], shared["beta"], EPS, y=a["y"], mean=a["mean"],
+                  rstd=a["rstd"])
+        b = sets[(i + S // 2) % S]
+        mb.ln_bwd_dx(b["dy"], b["x"], shared["gamma"], b["mean"], b["rstd"], dx=b["dx"],
+                     workspace=ws)
+        fold()
+
+    ms_plain = timed(capture(plain_step, K), K)
+    pb = plain_bytes(ROWS, COLS, 2)["step"]
 
     nbytes = algorithmic_bytes(ROWS, COLS, 2)
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
@@ -308,6 +467,11 @@ def main():
                       "fold": round(ms_fold * 1e3, 3)},
         "copy_GBps": {"21MB_rotated": round(2 * ROWS * COLS * 2 / (ms_copy * 1e-3) / 1e9, 1),
                       "256MiB": round(2 * COPY_BYTES / (ms_bigcopy * 1e-3) / 1e9, 1)},
+        "plain_fwd_step": {"workload": "ln_fwd then the same backward and fold, 8192x1280 bf16",
+                           "bytes_per_step": pb, "ms_per_step": round(ms_plain, 5),
+                           "GBps": round(pb / (ms_plain * 1e-3) / 1e9, 1),
+                           "pct_of_hbm_peak": round(100.0 * pb / (ms_plain * 1e-3) / 1e9
+                                                    / HBM_PEAK_GBPS, 2)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -18,6 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmbrow_ln.so")
+LAUNCH_BENCH = os.path.join(HERE, "launch_bench")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [
@@ -78,7 +79,24 @@ def build(jobs: int | None = None, verbose: bool = False, extra_flags=(), out_li
     os.replace(tmp, out_lib)
     if verbose:
         print("built", out_lib)
+    if out_lib == LIB:
+        build_launch_bench(verbose)
     return out_lib
+
+
+def build_launch_bench(verbose: bool = False) -> str:
+    """The host-side launch-cost tool (``launch_bench``), linked against the
+    library next to it."""
+    tmp = LAUNCH_BENCH + ".tmp"
+    cmd = [HIPCC, *COMMON, os.path.join(CSRC, "launch_bench.cpp"), "-o", tmp,
+           "-L", HERE, "-lmbrow_ln", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("launch_bench build failed:\n%s\n%s" % (r.stdout, r.stderr))
+    os.replace(tmp, LAUNCH_BENCH)
+    if verbose:
+        print("built", LAUNCH_BENCH)
+    return LAUNCH_BENCH
 
 
 if __name__ == "__main__":

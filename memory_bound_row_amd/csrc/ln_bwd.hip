@@ -109,12 +109,10 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     for (int k = 0; k < KA; ++k) acc_g[k] = acc_b[k] = 0.0f;
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
-    // One block at a time: its loads, then pass 1 (x-hat and g formed slot
-    // by slot from the packed row, the two row sums), then pass 2 (x-hat
-    // and g formed again for dx and the column partials).  The partials use
-    // the same expressions in every mode, so the fused and the partials-only
-    // passes produce the same bits.  The walk is uniform per workgroup, so
-    // the barrier of a multi-wave row is reached by all.
+    // One block at a time: its loads, the block unpacked once, pass 1 (the
+    // two row sums), pass 2 (dx and the column partials).  The walk is
+    // uniform per workgroup, so the barrier of a multi-wave row is reached
+    // by all.
     int it = 0;
     for (int64_t base = first; base < a.rows; base += stride, ++it) {
         const int64_t row = base + grp;
@@ -141,67 +139,75 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             }
         }
         const float mu = a.mean[r], rs = a.rstd[r];
-        if constexpr (DX) keep_packed(gp);
+        // (the per-element path has no registers to spare for gamma unpacked
+        // across blocks)
+        if constexpr (DX && !VEC) keep_packed(gp);
+        // The block is unpacked once: x becomes x - mean in place, dy stays.
+        float xm[V][E], d[V][E];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            S::unpack(xr[i], xm[i]);
+            S::unpack(dr[i], d[i]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) xm[i][e] = xm[i][e] - mu;
+        }
         float c1 = 0.0f, c2 = 0.0f;
         if constexpr (DX) {
-            float A = 0.0f, B = 0.0f;
+            // A = sum g, B = sum g * xhat = rstd * sum g * (x - mean)
+            float A = 0.0f, Bm = 0.0f;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                float x[E], d[E], ga[E];
-                S::unpack(xr[i], x);
-                S::unpack(dr[i], d);
+                float ga[E];
                 S::unpack(gp[i], ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float xh = (x[e] - mu) * rs;
-                    const float g = ga[e] * d[e];   // zero outside the row
+                    const float g = ga[e] * d[i][e];   // zero outside the row
                     A += g;
-                    B = fmaf(g, xh, B);
+                    Bm = fmaf(g, xm[i][e], Bm);
                 }
             }
             if constexpr (G <= 64) {
                 A = group_sum<G>(A);
-                B = group_sum<G>(B);
+                Bm = group_sum<G>(Bm);
             } else {
                 A = group_sum<64>(A);
-                B = group_sum<64>(B);
+                Bm = group_sum<64>(Bm);
                 const int w = lg / 64;
                 const int buf = it & 1;   // double buffer: one barrier per block
                 if (lane == 0) {
                     red[buf][grp][w][0] = A;
-                    red[buf][grp][w][1] = B;
+                    red[buf][grp][w][1] = Bm;
                 }
                 __syncthreads();
                 A = red[buf][grp][0][0];
-                B = red[buf][grp][0][1];
+                Bm = red[buf][grp][0][1];
 #pragma unroll
                 for (int k = 1; k < WPR; ++k) {
                     A += red[buf][grp][k][0];
-                    B += red[buf][grp][k][1];
+                    Bm += red[buf][grp][k][1];
                 }
             }
             // dx = rstd * (g - (A + xhat * B) / m) = rstd * (g - (c1 + xhat * c2));
             // g - (...) cancels exactly where it should (a one-column row
             // gets dx = 0)
             c1 = A * a.inv_m;
-            c2 = B * a.inv_m;
+            c2 = (Bm * rs) * a.inv_m;
         }
-        keep_packed(xr);
-        keep_packed(dr);
-        if constexpr (DX) keep_packed(gp);
+        // Pass 2, slot by slot: dx (when formed) and the column partials.
+        // The partials use the same expressions in every mode, so the fused
+        // and the partials-only passes produce the same bits.
         const rsrc_t vdx = view(DX ? a.dx : a.dy, base);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            float x[E], d[E], xh[E];
-            S::unpack(xr[i], x);
-            S::unpack(dr[i], d);
+            float xh[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) xh[e] = (x[e] - mu) * rs;
+            for (int e = 0; e < E; ++e) xh[e] = xm[i][e] * rs;
             if constexpr (DX) {
                 float ga[E], out[E];
                 S::unpack(gp[i], ga);
 #pragma unroll
-                for (int e = 0; e < E; ++e) out[e] = rs * (ga[e] * d[e] - fmaf(xh[e], c2, c1));
+                for (int e = 0; e < E; ++e)
+                    out[e] = rs * (ga[e] * d[i][e] - fmaf(xh[e], c2, c1));
                 if constexpr (VEC) {
                     buf_store_nt(S::pack(out), vdx, vo[i]);
                 } else {
@@ -211,13 +217,10 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             if constexpr (PART) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    acc_g[i * E + e] = fmaf(d[e], xh[e], acc_g[i * E + e]);
-                    acc_b[i * E + e] = acc_b[i * E + e] + d[e];
+                    acc_g[i * E + e] = fmaf(d[i][e], xh[e], acc_g[i * E + e]);
+                    acc_b[i * E + e] = acc_b[i * E + e] + d[i][e];
                 }
             }
-            // keep the scheduler from interleaving slots (it would hold
-            // several slots' temporaries at once)
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
