@@ -227,6 +227,24 @@ void orc_bias_dropout_residual(const double* x, const double* bias,
 /* Backward ([L11] §2.1, §2.4).                                              */
 /* ------------------------------------------------------------------------ */
 
+void orc_dropout_residual_bwd(const double* dz, const uint8_t* keep, float p,
+                              int64_t rows, int64_t m, double* dx,
+                              double* dbias, double* sbias) {
+    double q = 1.0 - (double)p;
+    for (int64_t j = 0; j < m; ++j) {
+        dbias[j] = 0.0;
+        if (sbias) sbias[j] = 0.0;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t j = 0; j < m; ++j) {
+            int64_t i = r * m + j;
+            dx[i] = keep[i] ? dz[i] / q : 0.0;
+            dbias[j] += dx[i];
+            if (sbias) sbias[j] += fabs(dx[i]);
+        }
+    }
+}
+
 void orc_ln_bwd_dx_hw4(const double* dy, const double* x, const double* gamma,
                        const double* mean, const double* rstd,
                        int64_t rows, int64_t m, double* dx) {

@@ -95,6 +95,19 @@ void orc_bias_dropout_residual(const double* x, const double* bias,
                                const double* residual, const uint8_t* keep,
                                float p, int64_t rows, int64_t m, double* z);
 
+/* Backward of the bias + dropout + residual prologue ([L10] §2.3 order: bias
+ * add, dropout, residual add; [L11] §3.3: the mask is regenerated from the
+ * seed instead of stored).  With z = residual + keep * (x + bias) / (1 - p)
+ * and dz the gradient reaching z (the LayerNorm's dx plus any gradient from
+ * z's other uses), by the chain rule:
+ *   dresidual = dz (the caller keeps dz);
+ *   dx_j = keep_j ? dz_j / (1 - p) : 0;
+ *   dbias_j = sum over rows of dx_rj (row order); sbias_j = sum of |dx_rj|
+ * (sbias may be NULL). */
+void orc_dropout_residual_bwd(const double* dz, const uint8_t* keep, float p,
+                              int64_t rows, int64_t m, double* dx,
+                              double* dbias, double* sbias);
+
 /* LayerNorm backward dx, the x-hat form ([L11] §2.1, "HW4" form):
  * g = gamma*dy, xhat = (x - mu)*r, A = sum g, B = sum g*xhat,
  * dx = r * (g - (A + xhat*B)/m). */

@@ -62,6 +62,7 @@ def _load():
     for name in ("orc_ln_bwd_dx_hw4", "orc_ln_bwd_dx_slides", "orc_ln_bwd_dx_scale"):
         getattr(lib, name).argtypes = [dp, dp, dp, dp, dp, i64, i64, dp]
     lib.orc_ln_bwd_params.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, dp, dp]
+    lib.orc_dropout_residual_bwd.argtypes = [dp, u8p, ctypes.c_float, i64, i64, dp, dp, dp]
     _lib = lib
     return lib
 
@@ -204,7 +205,23 @@ def ln_bwd_params(dy, x, mean, rstd):
     return dg, db, sg, sb
 
 
+def dropout_residual_bwd(dz, keep, p: float):
+    """Backward of z = residual + keep*(x + bias)/(1 - p) given dz:
+    (dx, dbias, sbias); dresidual is dz itself."""
+    dz = _d(dz)
+    rows, m = _shape2(dz)
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    if keep.shape != dz.shape:
+        raise ValueError("keep must match dz")
+    dx = np.empty_like(dz)
+    db = np.empty(m)
+    sb = np.empty(m)
+    _load().orc_dropout_residual_bwd(_ptr(dz), _ptr(keep, ctypes.c_uint8), ctypes.c_float(p),
+                                     rows, m, _ptr(dx), _ptr(db), _ptr(sb))
+    return dx, db, sb
+
+
 __all__ = ["F32", "F16", "BF16", "build", "round_to", "round_scalar", "ln_fwd",
            "row_stats_welford", "var_naive_f32", "var_chan_f32", "philox4x32_10",
            "dropout_threshold", "dropout_keep", "bias_dropout_residual",
-           "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params"]
+           "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params", "dropout_residual_bwd"]

@@ -234,6 +234,61 @@ def test_backward_finite_differences(orc, m):
             assert abs(fdp - grad[j]) <= 1e-12 * max(1.0, abs(grad[j])), (which, j)
 
 
+# --------------------------------------------------------------------------
+# Backward of the bias + dropout + residual prologue: the chain rule through
+# the composed forward ("Accelerating Transformer on GPU (I)" §2.3 order),
+# pinned by central finite differences of a scalar loss that uses both y and
+# z (z also feeds the residual stream)
+# --------------------------------------------------------------------------
+
+def _fused_loss(orc, x, bias, res, keep, p, gamma, beta, dy, dzx, eps):
+    z = orc.bias_dropout_residual(x, bias, res, keep, p)
+    y, _, _ = orc.ln_fwd(z, gamma, beta, eps)
+    return float(np.sum(dy * y) + np.sum(dzx * z))
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+def test_dropout_residual_backward_finite_differences(orc, m):
+    rng = np.random.default_rng(300 + m)
+    rows, p, eps = 3, 0.3, 1e-5
+    x, res, dy, dzx = (_rows(rng, rows, m) for _ in range(4))
+    bias = rng.normal(0.0, 0.5, m)
+    gamma = rng.uniform(0.5, 1.5, m)
+    beta = rng.normal(0.0, 0.1, m)
+    keep = (rng.uniform(size=(rows, m)) >= p).astype(np.uint8)
+    keep[0, 0], keep[-1, -1] = 0, 1            # both cases present
+    z = orc.bias_dropout_residual(x, bias, res, keep, p)
+    _, mean, rstd = orc.ln_fwd(z, gamma, beta, eps)
+    dz = orc.ln_bwd_dx(dy, z, gamma, mean, rstd) + dzx
+    dx, dbias, sbias = orc.dropout_residual_bwd(dz, keep, p)
+
+    def loss(xx=x, rr=res, bb=bias):
+        return _fused_loss(orc, xx, bb, rr, keep, p, gamma, beta, dy, dzx, eps)
+
+    scale = max(1.0, np.max(np.abs(dx)), np.max(np.abs(dz)))
+    for r in range(rows):
+        for j in range(m):
+            for name, arr, grad in (("x", x, dx), ("residual", res, dz)):
+                h = 1e-6 * max(1.0, abs(arr[r, j]))
+                ap, am = arr.copy(), arr.copy()
+                ap[r, j] += h
+                am[r, j] -= h
+                kw_p = {"xx": ap} if name == "x" else {"rr": ap}
+                kw_m = {"xx": am} if name == "x" else {"rr": am}
+                fd = (loss(**kw_p) - loss(**kw_m)) / (2 * h)
+                assert abs(fd - grad[r, j]) <= 1e-7 * scale, (name, r, j, fd, grad[r, j])
+    for j in range(m):
+        h = 1e-6 * max(1.0, abs(bias[j]))
+        bp, bm = bias.copy(), bias.copy()
+        bp[j] += h
+        bm[j] -= h
+        fd = (loss(bb=bp) - loss(bb=bm)) / (2 * h)
+        assert abs(fd - dbias[j]) <= 1e-7 * max(1.0, np.max(np.abs(dbias))), (j, fd, dbias[j])
+    # dropped positions get exactly no gradient; the absolute sums bound the sums
+    assert np.all(dx[keep == 0] == 0.0)
+    assert np.all(sbias >= np.abs(dbias))
+
+
 @pytest.mark.parametrize("m", [64, 768, 1280])
 def test_backward_two_forms_agree(orc, m):
     # The x-hat ("HW4") form and the slides' alpha/beta form: algebraically
