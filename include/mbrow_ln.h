@@ -71,6 +71,10 @@ typedef enum {
 /* Widest row supported, for every storage type (the whole row is held in
  * registers of one workgroup). */
 #define LN_MAX_COLS 16384
+/* Widest row of bias_dropout_residual_ln_bwd, for every storage type (its
+ * three column accumulators per value need the registers of twice as many
+ * lanes). */
+#define LN_MAX_COLS_DROPOUT_BWD 8192
 
 /*
  * LayerNorm forward.  For each row r with m = cols:
@@ -171,6 +175,49 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x,
                                 int partials_ready, int64_t rows,
                                 int64_t cols, ln_dtype_t dt,
                                 hipStream_t stream);
+
+/*
+ * Bytes of float32 workspace bias_dropout_residual_ln_bwd needs: P * 3 * cols
+ * * 4 (dgamma, dbeta and dbias partials per partition), with the same P as
+ * ln_bwd_workspace_bytes.  Returns 0 for rows <= 0 or cols <= 0.
+ */
+size_t bias_dropout_residual_ln_bwd_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Backward of bias_dropout_residual_ln_fwd in one pass over the rows: the
+ * LayerNorm backward as in ln_bwd_dx / ln_bwd_dgamma_dbeta, then the
+ * prologue's backward by the chain rule through
+ * z = residual + keep * (x + bias) / (1 - p), with the forward's mask
+ * regenerated from (seed, row, column, p) instead of stored ([L11] §3.3;
+ * [L10] §2.3 for the order bias add, dropout, residual add):
+ *   dz        = dx of the LayerNorm (from dy) + dz_extra;
+ *   dresidual = dz;
+ *   dx_j      = keep_j ? dz_j / (1 - p) : 0;
+ *   dbias_j   = sum over rows of dx_j (before rounding to T), dgamma_j =
+ *               sum dy * xhat, dbeta_j = sum dy, by the same deterministic
+ *               two-stage reduction ([L11] §2.4).
+ * dz is formed in float32; dresidual and dx are rounded from it.
+ *   dy        [rows, cols] T: gradient of y.
+ *   dz_extra  [rows, cols] T or NULL: gradient reaching z from its other
+ *             uses (the residual stream); NULL adds nothing.
+ *   z         [rows, cols] T: residual_out of the forward.
+ *   gamma [cols] T;  mean, rstd [rows] float32 as saved by the forward.
+ *   p, seed   the forward's dropout probability and seed.
+ *   dresidual, dx  [rows, cols] T outputs; each may equal exactly one of dy,
+ *             dz_extra, z (in place), but not each other.
+ *   dgamma, dbeta, dbias  [cols] float32 outputs.
+ *   workspace float32 device buffer of at least
+ *             bias_dropout_residual_ln_bwd_workspace_bytes(rows, cols).
+ * Errors as for the other calls; p outside [0, 1) is LN_ERR_PARAM; rows wider
+ * than LN_MAX_COLS_DROPOUT_BWD are LN_ERR_UNSUPPORTED.
+ */
+ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, const void* z,
+                                         const void* gamma, const float* mean,
+                                         const float* rstd, void* dresidual, void* dx,
+                                         float* dgamma, float* dbeta, float* dbias,
+                                         float* workspace, size_t workspace_bytes,
+                                         int64_t rows, int64_t cols, float p, uint64_t seed,
+                                         ln_dtype_t dt, hipStream_t stream);
 
 /* Static English description of a status code (never NULL). */
 const char* ln_status_string(ln_status_t status);

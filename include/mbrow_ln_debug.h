@@ -22,11 +22,14 @@ extern "C" {
  *                  library's own choice (and ignores slots_per_lane).
  *   slots_per_lane 16-byte slots per lane.  Built layouts: fp32 16x{1,2,4,8},
  *                  32x1-8, 64x1-8, {128,256,512,1024}x4; fp16/bf16
- *                  16x{1,2,4}, 32x1-5, 64x1-5, {128,256,512}x4.
+ *                  16x{1,2,4}, 32x1-5, 64x1-5, {128,256,512}x4.  The prologue
+ *                  backward (bias_dropout_residual_ln_bwd) has its own set:
+ *                  fp32 16x{1,2,4}, 32x1-4, 64x1-6, {128,256,512}x4;
+ *                  fp16/bf16 16x{1,2}, 32x1-3, 64x1-3, {128,256,512}x2.
  *   scalar         non-zero forces per-element loads and stores.
- * A forced layout applies only to calls whose dtype has it built and whose
- * row fits it (lanes_per_row * slots_per_lane slots); other calls use the
- * library's own choice.  Returns LN_ERR_UNSUPPORTED (and changes nothing)
+ * A forced layout applies only to calls that have it built for their dtype
+ * and whose row fits it (lanes_per_row * slots_per_lane slots); other calls
+ * use the library's own choice.  Returns LN_ERR_UNSUPPORTED (and changes nothing)
  * for a layout no dtype was built with.  Not thread-safe with respect to concurrent
  * calls that expect a particular layout.
  */

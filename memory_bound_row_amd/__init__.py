@@ -48,6 +48,12 @@ def lib() -> ctypes.CDLL:
     L.ln_bwd_dgamma_dbeta.restype = i32
     L.ln_bwd_dgamma_dbeta.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i32,
                                       i64, i64, i32, vp]
+    L.bias_dropout_residual_ln_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.bias_dropout_residual_ln_bwd_workspace_bytes.argtypes = [i64, i64]
+    L.bias_dropout_residual_ln_bwd.restype = i32
+    L.bias_dropout_residual_ln_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               ctypes.c_size_t, i64, i64, f32, ctypes.c_uint64,
+                                               i32, vp]
     L.ln_debug_force_path.restype = i32
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
     L.ln_debug_force_grid.restype = i32
@@ -210,6 +216,51 @@ def ln_bwd(dy, x, gamma, mean, rstd, *, dx=None, workspace_buf=None, dgamma=None
     dgamma, dbeta = ln_bwd_dgamma_dbeta(ws, rows, cols, x.dtype, partials_ready=True,
                                         dgamma=dgamma, dbeta=dbeta)
     return dx, dgamma, dbeta
+
+
+def bias_dropout_residual_ln_bwd_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().bias_dropout_residual_ln_bwd_workspace_bytes(int(rows), int(cols)))
+
+
+def dropout_workspace(rows: int, cols: int, device) -> torch.Tensor:
+    """A float32 workspace of the size bias_dropout_residual_ln_bwd needs."""
+    n = bias_dropout_residual_ln_bwd_workspace_bytes(rows, cols) // 4
+    return torch.empty(max(n, 1), dtype=torch.float32, device=device)
+
+
+def bias_dropout_residual_ln_bwd(dy, z, gamma, mean, rstd, p: float, seed: int, *,
+                                 dz_extra=None, dresidual=None, dx=None, dgamma=None,
+                                 dbeta=None, dbias=None, workspace=None):
+    """Backward of bias_dropout_residual_ln_fwd -> (dresidual, dx, dgamma, dbeta, dbias).
+
+    dz = LayerNorm dx (from dy) + dz_extra; dresidual = dz; dx = mask * dz / (1 - p)
+    with the forward's mask regenerated from (seed, p); dbias = column sums of dx."""
+    rows, cols = _mat(z, "z")
+    for t, n in ((dy, "dy"), (dz_extra, "dz_extra")):
+        if t is not None and (t.shape != z.shape or t.dtype != z.dtype):
+            raise ValueError(f"{n} must match z")
+        if t is not None:
+            _mat(t, n)
+    _vec(gamma, cols, z.dtype, "gamma")
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        _vec(t, rows, torch.float32, n)
+    dresidual = _out(dresidual, z.shape, z.dtype, z.device, "dresidual")
+    dx = _out(dx, z.shape, z.dtype, z.device, "dx")
+    dgamma = _out(dgamma, (cols,), torch.float32, z.device, "dgamma")
+    dbeta = _out(dbeta, (cols,), torch.float32, z.device, "dbeta")
+    dbias = _out(dbias, (cols,), torch.float32, z.device, "dbias")
+    if workspace is None:
+        workspace = dropout_workspace(rows, cols, z.device)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda:
+        raise ValueError("workspace must be a float32 GPU tensor")
+    if rows == 0:
+        return dresidual, dx, dgamma.zero_(), dbeta.zero_(), dbias.zero_()
+    _check(lib().bias_dropout_residual_ln_bwd(
+        _ptr(dy), _ptr(dz_extra), _ptr(z), _ptr(gamma), _ptr(mean), _ptr(rstd),
+        _ptr(dresidual), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dbias), _ptr(workspace),
+        workspace.numel() * 4, rows, cols, float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, _dt(z),
+        _stream(z)))
+    return dresidual, dx, dgamma, dbeta, dbias
 
 
 def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,

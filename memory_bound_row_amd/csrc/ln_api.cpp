@@ -58,13 +58,22 @@ static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0}, g_force_g
 // (used or not); ties go to the earlier candidate.  With `wave_rows`, slots
 // of a layout whose row is not exactly one wave (G != 64) count 5/4: one row
 // per wave measured faster in the backward even with some lanes idle.
+static bool in_list(const int (*list)[2], int n, int g, int v) {
+    for (int k = 0; k < n; ++k)
+        if (list[k][0] == g && list[k][1] == v) return true;
+    return false;
+}
+
+// `only_listed`: a forced layout applies only if it is one of the candidates
+// (the prologue backward is compiled for its own list).
 static Path pick(bool f32, int64_t ns, bool vec, const int (*prefer)[2], int nprefer,
-                 bool wave_rows = false) {
+                 bool wave_rows = false, bool only_listed = false) {
     Path p;
     p.vec = vec && g_force_scalar.load(std::memory_order_relaxed) == 0;
     const int fg = g_force_g.load(std::memory_order_relaxed);
     const int fv = g_force_v.load(std::memory_order_relaxed);
-    if (fg > 0 && (int64_t)fg * fv >= ns && have_instance(f32, fg, fv)) {
+    const bool known = only_listed ? in_list(prefer, nprefer, fg, fv) : have_instance(f32, fg, fv);
+    if (fg > 0 && (int64_t)fg * fv >= ns && known) {
         p.g = fg;
         p.v = fv;
         return p;
@@ -102,6 +111,11 @@ static const int kBwd32[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32
                                 {32, 4}, {64, 3}, {32, 5}, {32, 6}, {64, 4}, {32, 7}, {32, 8},
                                 {64, 5}, {64, 6}, {64, 7}, {64, 8}, {128, 4}, {256, 4},
                                 {512, 4}, {1024, 4}};
+static const int kDrop32[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
+                                 {32, 4}, {64, 3}, {64, 4}, {64, 5}, {64, 6}, {128, 4},
+                                 {256, 4}, {512, 4}};
+static const int kDrop16[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
+                                 {64, 3}, {128, 2}, {256, 2}, {512, 2}};
 static const int kBwd16[][2] = {{16, 1}, {32, 1}, {16, 2}, {32, 2}, {64, 1}, {32, 3}, {64, 2},
                                 {32, 4}, {64, 3}, {32, 5}, {64, 4}, {64, 5}, {128, 4}, {256, 4},
                                 {512, 4}};
@@ -116,10 +130,14 @@ Path pick_path(Dt dt, int64_t cols, bool vec) {
 }
 
 // The same choice with and without partials, so the fused and the
-// partials-only passes accumulate in the same order.
-Path pick_bwd_path(Dt dt, int64_t cols, bool vec) {
+// partials-only passes accumulate in the same order.  The prologue backward
+// (`dropout`) chooses among the layouts compiled for it.
+Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool dropout) {
     const int E = elems_per_slot(dt);
     const int64_t ns = (cols + E - 1) / E;
+    if (dropout)
+        return E == 4 ? pick(true, ns, vec, kDrop32, MBROW_N(kDrop32), true, true)
+                      : pick(false, ns, vec, kDrop16, MBROW_N(kDrop16), true, true);
     return E == 4 ? pick(true, ns, vec, kBwd32, MBROW_N(kBwd32), true)
                   : pick(false, ns, vec, kBwd16, MBROW_N(kBwd16), true);
 }
@@ -238,6 +256,11 @@ const char* ln_status_string(ln_status_t status) {
 size_t ln_bwd_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
     return (size_t)bwd_partitions(rows, cols) * 2u * (size_t)cols * sizeof(float);
+}
+
+size_t bias_dropout_residual_ln_bwd_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)bwd_partitions(rows, cols) * 3u * (size_t)cols * sizeof(float);
 }
 
 ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
@@ -377,7 +400,61 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
             launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::PARTIALS, a, stream));
         if (st != LN_OK) return st;
     }
-    return from_hip(launch_fold(workspace, parts, cols, dgamma, dbeta, stream));
+    FoldOut out{};
+    out.p[0] = dgamma;
+    out.p[1] = dbeta;
+    return from_hip(launch_fold(workspace, parts, cols, 2, out, stream));
+}
+
+ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, const void* z,
+                                         const void* gamma, const float* mean,
+                                         const float* rstd, void* dresidual, void* dx,
+                                         float* dgamma, float* dbeta, float* dbias,
+                                         float* workspace, size_t workspace_bytes, int64_t rows,
+                                         int64_t cols, float p, uint64_t seed, ln_dtype_t dt,
+                                         hipStream_t stream) {
+    if (!dy || !z || !gamma || !mean || !rstd || !dresidual || !dx || !dgamma || !dbeta ||
+        !dbias || !workspace)
+        return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    if (cols > LN_MAX_COLS_DROPOUT_BWD) return LN_ERR_UNSUPPORTED;
+    if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
+    const size_t need = bias_dropout_residual_ln_bwd_workspace_bytes(rows, cols);
+    if (workspace_bytes < need) return LN_ERR_WORKSPACE;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float), cb = (size_t)cols * sizeof(float);
+    const Span outs[] = {{dresidual, tb, true}, {dx, tb, true}, {dgamma, cb, false},
+                         {dbeta, cb, false}, {dbias, cb, false}, {workspace, need, false}};
+    const Span ins[] = {{dy, tb, true}, {dz_extra, dz_extra ? tb : 0, true}, {z, tb, true},
+                        {gamma, vb, false}, {mean, sb, false}, {rstd, sb, false}};
+    st = check_aliasing(outs, 6, ins, 6);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(dy) && (!dz_extra || aligned16(dz_extra)) && aligned16(z) &&
+                     aligned16(gamma) && aligned16(dresidual) && aligned16(dx) &&
+                     (cols * (int64_t)es) % 16 == 0;
+    BwdArgs a{};
+    a.dy = dy; a.x = z; a.gamma = gamma; a.mean = mean; a.rstd = rstd; a.dx = dresidual;
+    a.dz_extra = dz_extra; a.dx_in = dx; a.ws = workspace;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.parts = bwd_partitions(rows, cols);
+    a.inv_m = (float)(1.0 / (double)cols);
+    a.thr = (uint32_t)std::floor((double)p * 65536.0 + 0.5);
+    a.scale = (float)(1.0 / (1.0 - (double)p));
+    a.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    a.seed_hi = (uint32_t)(seed >> 32);
+    st = from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec, true), BwdMode::DROPOUT, a, stream));
+    if (st != LN_OK) return st;
+    FoldOut out{};
+    out.p[0] = dgamma;
+    out.p[1] = dbeta;
+    out.p[2] = dbias;
+    return from_hip(launch_fold(workspace, a.parts, cols, 3, out, stream));
 }
 
 ln_status_t ln_debug_force_grid(int workgroups_per_cu) {
@@ -386,8 +463,9 @@ ln_status_t ln_debug_force_grid(int workgroups_per_cu) {
 }
 
 ln_status_t ln_debug_force_path(int lanes_per_row, int slots_per_lane, int scalar) {
-    if (lanes_per_row != 0 && !have_instance(true, lanes_per_row, slots_per_lane) &&
-        !have_instance(false, lanes_per_row, slots_per_lane))
+    const int g = lanes_per_row, v = slots_per_lane;
+    if (g != 0 && !have_instance(true, g, v) && !have_instance(false, g, v) &&
+        !in_list(kDrop32, MBROW_N(kDrop32), g, v) && !in_list(kDrop16, MBROW_N(kDrop16), g, v))
         return LN_ERR_UNSUPPORTED;
     g_force_g.store(lanes_per_row, std::memory_order_relaxed);
     g_force_v.store(lanes_per_row ? slots_per_lane : 0, std::memory_order_relaxed);

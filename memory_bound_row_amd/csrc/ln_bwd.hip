@@ -64,6 +64,8 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     constexpr int UT = BwdGeometry<G>::UT;
     constexpr bool DX = MODE != (int)BwdMode::PARTIALS;
     constexpr bool PART = MODE != (int)BwdMode::DX;
+    constexpr bool DROP = MODE == (int)BwdMode::DROPOUT;   // prologue backward too
+    constexpr int NK = DROP ? 3 : 2;                        // kinds of column partials
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int lg = tid % G;
@@ -102,11 +104,17 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         return row_view<S>(t, row0, left < WaveRows<G>::N ? left : WaveRows<G>::N, m);
     };
 
-    // Column accumulators: one per value of the lane's slots and kind.
+    // Column accumulators: one per value of the lane's slots and kind
+    // (dgamma, dbeta, and dbias in the prologue mode).
     constexpr int KA = PART ? V * E : 1;
-    float acc_g[KA], acc_b[KA];
+    float acc[NK][KA];
 #pragma unroll
-    for (int k = 0; k < KA; ++k) acc_g[k] = acc_b[k] = 0.0f;
+    for (int k = 0; k < KA; ++k) acc[0][k] = acc[1][k] = 0.0f;
+    if constexpr (DROP) {
+#pragma unroll
+        for (int k = 0; k < KA; ++k) acc[NK - 1][k] = 0.0f;
+    }
+    const bool has_extra = DROP && a.dz_extra != nullptr;   // uniform
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
     // One block at a time: its loads, the block unpacked once, pass 1 (the
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         const int64_t row = base + grp;
         const bool rok = row < a.rows;
         const int64_t r = rok ? row : 0;   // rows past the end read row 0's statistics
-        u32x4 xr[V], dr[V];
+        u32x4 xr[V], dr[V], er[DROP ? V : 1];
         if constexpr (VEC) {
             // rows past the end read 0 and are never stored
             const rsrc_t vd = view(a.dy, base);
@@ -128,6 +136,13 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 dr[i] = buf_load_nt(vd, vo[i]);
                 xr[i] = buf_load_nt(vx, vo[i]);
             }
+            if constexpr (DROP) {
+                if (has_extra) {
+                    const rsrc_t ve = view(a.dz_extra, base);
+#pragma unroll
+                    for (int i = 0; i < V; ++i) er[i] = buf_load_nt(ve, vo[i]);
+                }
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < V; ++i) {
@@ -136,34 +151,62 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 dr[i] = S::pack(f);
                 load_elems<S>(a.x, r, m, (i * G + lg) * E, ok[i] && rok, f);
                 xr[i] = S::pack(f);
+                if constexpr (DROP) {
+                    if (has_extra) {
+                        load_elems<S>(a.dz_extra, r, m, (i * G + lg) * E, ok[i] && rok, f);
+                        er[i] = S::pack(f);
+                    }
+                }
             }
         }
         const float mu = a.mean[r], rs = a.rstd[r];
-        // (the per-element path has no registers to spare for gamma unpacked
-        // across blocks)
-        if constexpr (DX && !VEC) keep_packed(gp);
+        // (the per-element path and multi-wave rows of the prologue backward
+        // have no registers to spare for gamma unpacked across blocks)
+        if constexpr (DX && (!VEC || (DROP && G > 64))) keep_packed(gp);
         // The block is unpacked once: x becomes x - mean in place, dy stays.
-        float xm[V][E], d[V][E];
+        // (Multi-wave rows of the prologue backward have no registers to
+        // spare for that: they keep the block packed and unpack it in each
+        // pass.)
+        constexpr bool ONCE = !(DROP && G > 64);
+        float xm_[ONCE ? V : 1][E], d_[ONCE ? V : 1][E];
+        if constexpr (ONCE) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            S::unpack(xr[i], xm[i]);
-            S::unpack(dr[i], d[i]);
+            for (int i = 0; i < V; ++i) {
+                S::unpack(xr[i], xm_[i]);
+                S::unpack(dr[i], d_[i]);
 #pragma unroll
-            for (int e = 0; e < E; ++e) xm[i][e] = xm[i][e] - mu;
+                for (int e = 0; e < E; ++e) xm_[i][e] = xm_[i][e] - mu;
+            }
         }
+        // x - mean and dy of slot i
+        auto slot = [&](int i, float* xm, float* d) {
+            if constexpr (ONCE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    xm[e] = xm_[i][e];
+                    d[e] = d_[i][e];
+                }
+            } else {
+                S::unpack(xr[i], xm);
+                S::unpack(dr[i], d);
+#pragma unroll
+                for (int e = 0; e < E; ++e) xm[e] = xm[e] - mu;
+            }
+        };
         float c1 = 0.0f, c2 = 0.0f;
         if constexpr (DX) {
             // A = sum g, B = sum g * xhat = rstd * sum g * (x - mean)
             float A = 0.0f, Bm = 0.0f;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                float ga[E];
+                float ga[E], xm[E], d[E];
                 S::unpack(gp[i], ga);
+                slot(i, xm, d);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float g = ga[e] * d[i][e];   // zero outside the row
+                    const float g = ga[e] * d[e];   // zero outside the row
                     A += g;
-                    Bm = fmaf(g, xm[i][e], Bm);
+                    Bm = fmaf(g, xm[e], Bm);
                 }
             }
             if constexpr (G <= 64) {
@@ -197,28 +240,58 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         // The partials use the same expressions in every mode, so the fused
         // and the partials-only passes produce the same bits.
         const rsrc_t vdx = view(DX ? a.dx : a.dy, base);
+        const rsrc_t vdi = view(DROP ? a.dx_in : a.dy, base);
+        if constexpr (!ONCE) {
+            keep_packed(xr);
+            keep_packed(dr);
+        }
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            float xh[E];
+            const int col0 = (i * G + lg) * E;
+            float xh[E], xm[E], d[E];
+            slot(i, xm, d);
 #pragma unroll
-            for (int e = 0; e < E; ++e) xh[e] = xm[i][e] * rs;
+            for (int e = 0; e < E; ++e) xh[e] = xm[e] * rs;
             if constexpr (DX) {
                 float ga[E], out[E];
                 S::unpack(gp[i], ga);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    out[e] = rs * (ga[e] * d[i][e] - fmaf(xh[e], c2, c1));
+                    out[e] = rs * (ga[e] * d[e] - fmaf(xh[e], c2, c1));
+                if constexpr (DROP) {
+                    // dz = the LayerNorm's dx + the gradient from z's other
+                    // uses; dresidual = dz; dx of the prologue = keep * dz /
+                    // (1 - p) with the forward's mask regenerated; dbias sums it
+                    if (has_extra) {
+                        float ez[E];
+                        S::unpack(er[i], ez);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) out[e] = out[e] + ez[e];
+                    }
+                    const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                    float din[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        din[e] = kept<E>(w, col0, e, a.thr) ? out[e] * a.scale : 0.0f;
+                        acc[2][i * E + e] = acc[2][i * E + e] + din[e];
+                    }
+                    if constexpr (VEC) {
+                        buf_store_nt(S::pack(din), vdi, vo[i]);
+                    } else {
+                        store_elems<S>(a.dx_in, r, m, col0, ok[i] && rok, din);
+                    }
+                }
                 if constexpr (VEC) {
                     buf_store_nt(S::pack(out), vdx, vo[i]);
                 } else {
-                    store_elems<S>(a.dx, r, m, (i * G + lg) * E, ok[i] && rok, out);
+                    store_elems<S>(a.dx, r, m, col0, ok[i] && rok, out);
                 }
             }
             if constexpr (PART) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    acc_g[i * E + e] = fmaf(d[i][e], xh[e], acc_g[i * E + e]);
-                    acc_b[i * E + e] = acc_b[i * E + e] + d[i][e];
+                    acc[0][i * E + e] = fmaf(d[e], xh[e], acc[0][i * E + e]);
+                    acc[1][i * E + e] = acc[1][i * E + e] + d[e];
                 }
             }
         }
@@ -229,19 +302,17 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         // wave first: lanes l, l+16, l+32, l+48 (16-lane rows) or l, l+32
         // (32-lane rows).  Adds are commutative, so partners agree bit for
         // bit and every row group ends with the wave's sums.
-        if constexpr (G == 16) {
+#pragma unroll
+        for (int kind = 0; kind < NK; ++kind) {
 #pragma unroll
             for (int k = 0; k < KA; ++k) {
-                acc_g[k] = acc_g[k] + partner<16>(acc_g[k]);
-                acc_b[k] = acc_b[k] + partner<16>(acc_b[k]);
-                acc_g[k] = acc_g[k] + xor32(acc_g[k]);
-                acc_b[k] = acc_b[k] + xor32(acc_b[k]);
-            }
-        } else if constexpr (G == 32) {
-#pragma unroll
-            for (int k = 0; k < KA; ++k) {
-                acc_g[k] = halves_sum_swap(acc_g[k], acc_g[k]);
-                acc_b[k] = halves_sum_swap(acc_b[k], acc_b[k]);
+                float& v = acc[kind][k];
+                if constexpr (G == 16) {
+                    v = v + partner<16>(v);
+                    v = v + xor32(v);
+                } else if constexpr (G == 32) {
+                    v = halves_sum_swap(v, v);
+                }
             }
         }
         // Then the units whose lanes own the same columns (the waves of the
@@ -251,16 +322,29 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         // consecutive columns, and writes the workgroup's partial.  The
         // accumulators go through LDS in chunks of CI slot indices so the
         // footprint stays within 64 KB.
-        constexpr int KF = 65536 / (NU * 2 * UT * 4);           // floats per lane that fit
+        constexpr int KF = 65536 / (NU * NK * UT * 4);          // floats per lane that fit
         constexpr int CI = (KF - 1) / E < 1 ? 1 : ((KF - 1) / E < V ? (KF - 1) / E : V);
         constexpr int CK = CI * E + 1;                          // padded lane stride
         constexpr int CW = CI * G * E;                          // columns per chunk
-        static_assert(NU * 2 * UT * CK * 4 <= 65536, "stage exceeds 64 KB");
-        __shared__ float stage[NU][2][UT][CK];
+        float* const pw = a.ws + part * NK * a.m;   // this partition's [NK][m] partial
+        constexpr bool DIRECT = NU == 1 && NK * UT * CK * 4 > 65536;
+        if constexpr (DIRECT) {
+            // one unit too wide to stage: every column is held by exactly
+            // one lane, which writes it
+#pragma unroll
+            for (int k = 0; k < KA; ++k) {
+                const int col = ((k / E) * G + lg) * E + k % E;
+                if ((k / E) * G + lg < nslots && col < m) {
+#pragma unroll
+                    for (int kind = 0; kind < NK; ++kind) pw[kind * a.m + col] = acc[kind][k];
+                }
+            }
+            return;
+        }
+        static_assert(DIRECT || NU * NK * UT * CK * 4 <= 65536, "stage exceeds 64 KB");
+        __shared__ float stage[DIRECT ? 1 : NU][NK][DIRECT ? 1 : UT][DIRECT ? 1 : CK];
         const int unit = tid / UT;
         const int pos = tid % UT;
-        float* pg = a.ws + (part * 2 + 0) * a.m;
-        float* pb = a.ws + (part * 2 + 1) * a.m;
 #pragma unroll
         for (int i0 = 0; i0 < V; i0 += CI) {
             if (i0 > 0) __syncthreads();   // previous chunk fully read
@@ -268,14 +352,14 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             for (int c = 0; c < CI * E; ++c) {
                 const int k = i0 * E + c;
                 if (k < KA) {
-                    stage[unit][0][pos][c] = acc_g[k];
-                    stage[unit][1][pos][c] = acc_b[k];
+#pragma unroll
+                    for (int kind = 0; kind < NK; ++kind) stage[unit][kind][pos][c] = acc[kind][k];
                 }
             }
             __syncthreads();
             const int col0 = i0 * G * E;
-            for (int q = tid; q < 2 * CW; q += BwdGeometry<G>::NT) {
-                const int kind = q >= CW;
+            for (int q = tid; q < NK * CW; q += BwdGeometry<G>::NT) {
+                const int kind = q / CW;
                 const int cl = q - kind * CW;
                 const int col = col0 + cl;
                 if (col >= m) continue;
@@ -287,7 +371,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 float t = stage[0][kind][lig][c];
 #pragma unroll
                 for (int u = 1; u < NU; ++u) t = t + stage[u][kind][lig][c];
-                (kind == 0 ? pg : pb)[col] = t;
+                pw[kind * a.m + col] = t;
             }
         }
     }
@@ -304,11 +388,19 @@ template <bool VEC, int MODE>
 static hipError_t dispatch(const Path& p, const BwdArgs& a, hipStream_t s) {
 #define MBROW_CASE(GG, VV) \
     if (p.g == GG && p.v == VV) return launch_one<GG, VV, VEC, MODE>(a, s);
+    if constexpr (MODE == (int)BwdMode::DROPOUT) {
 #if MBROW_DT == 0
-    MBROW_LAYOUTS_F32(MBROW_CASE)
+        MBROW_LAYOUTS_DROP_F32(MBROW_CASE)
 #else
-    MBROW_LAYOUTS_16(MBROW_CASE)
+        MBROW_LAYOUTS_DROP_16(MBROW_CASE)
 #endif
+    } else {
+#if MBROW_DT == 0
+        MBROW_LAYOUTS_F32(MBROW_CASE)
+#else
+        MBROW_LAYOUTS_16(MBROW_CASE)
+#endif
+    }
 #undef MBROW_CASE
     return hipErrorInvalidValue;
 }
@@ -318,7 +410,8 @@ static hipError_t dispatch_mode(const Path& p, BwdMode mode, const BwdArgs& a, h
     switch (mode) {
     case BwdMode::DX: return dispatch<VEC, 0>(p, a, s);
     case BwdMode::DX_PARTIALS: return dispatch<VEC, 1>(p, a, s);
-    default: return dispatch<VEC, 2>(p, a, s);
+    case BwdMode::PARTIALS: return dispatch<VEC, 2>(p, a, s);
+    default: return dispatch<VEC, 3>(p, a, s);
     }
 }
 

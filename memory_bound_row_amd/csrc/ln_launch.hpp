@@ -57,20 +57,40 @@ struct FwdArgs {
 
 struct BwdArgs {
     const void* dy;
-    const void* x;
+    const void* x;          // the LayerNorm input (z of the fused forward)
     const void* gamma;
     const float* mean;
     const float* rstd;
-    void* dx;
-    float* ws;        // [P][2][m] partials
+    void* dx;               // LayerNorm dx; with the prologue: dresidual = dz
+    const void* dz_extra;   // prologue mode: gradient reaching z from its other uses, or NULL
+    void* dx_in;            // prologue mode: gradient of the prologue's x
+    float* ws;              // [P][K][m] partials (K = 2, or 3 with dbias)
     int64_t rows;
     int64_t m;
     int64_t nslots;
     int64_t parts;    // P
     float inv_m;
+    float scale;      // prologue mode: 1 / (1 - p)
+    uint32_t thr;     // prologue mode: keep iff 16-bit uniform >= thr
+    uint32_t seed_lo;
+    uint32_t seed_hi;
 };
 
-enum class BwdMode : int { DX = 0, DX_PARTIALS = 1, PARTIALS = 2 };
+// DROPOUT: dx of the LayerNorm plus the backward of the bias + dropout +
+// residual prologue, with partials of dgamma, dbeta and dbias.
+enum class BwdMode : int { DX = 0, DX_PARTIALS = 1, PARTIALS = 2, DROPOUT = 3 };
+
+// Row layouts of the prologue backward: three column accumulators per value
+// leave room for fewer values per lane (multi-wave 16-bit rows take 2 slots
+// per lane), and none for 1024-lane rows (128 registers per lane), so rows
+// stop at 8192 columns there (512 lanes).
+#define MBROW_LAYOUTS_DROP_F32(X)                                           \
+    X(16, 1) X(16, 2) X(16, 4) X(32, 1) X(32, 2) X(32, 3) X(32, 4)          \
+    X(64, 1) X(64, 2) X(64, 3) X(64, 4) X(64, 5) X(64, 6)                   \
+    X(128, 4) X(256, 4) X(512, 4)
+#define MBROW_LAYOUTS_DROP_16(X)                                            \
+    X(16, 1) X(16, 2) X(32, 1) X(32, 2) X(32, 3)                            \
+    X(64, 1) X(64, 2) X(64, 3) X(128, 2) X(256, 2) X(512, 2)
 
 // Threads per workgroup of the backward for G lanes per row.
 constexpr int bwd_threads(int g) { return g <= 512 ? 512 : g; }
@@ -83,7 +103,7 @@ int64_t bwd_partitions(int64_t rows, int64_t cols);
 // Path selection from (dtype, cols, alignment); honours the test-only
 // override set through ln_debug_force_path.
 Path pick_path(Dt dt, int64_t cols, bool vec);        // forward
-Path pick_bwd_path(Dt dt, int64_t cols, bool vec);   // backward
+Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool dropout = false);   // backward
 int elems_per_slot(Dt dt);
 
 // Workgroups for a persistent launch of `kernel` with `threads` threads per
@@ -95,7 +115,11 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t blocks);
 hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(Dt dt, const Path& p, BwdMode mode, const BwdArgs& a, hipStream_t s);
 hipError_t launch_dropout_mask(const FwdArgs& a, hipStream_t s);   // a.mask_out, rows, m, thr, seed
-hipError_t launch_fold(const float* ws, int64_t parts, int64_t m, float* dgamma,
-                       float* dbeta, hipStream_t s);
+// Fold of [P][kinds][m] partials (kinds = 2 or 3) into out[0..kinds-1].
+struct FoldOut {
+    float* p[3];
+};
+hipError_t launch_fold(const float* ws, int64_t parts, int64_t m, int kinds, FoldOut out,
+                       hipStream_t s);
 
 }  // namespace mbrow

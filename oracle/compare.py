@@ -96,13 +96,19 @@ def check_elementwise(name, out, ref, fmt, term_scale=None, row_len: int = 1) ->
     return _finish(name, out, ref, err, tol, atol)
 
 
-def check_colsum(name, out, ref, abs_sum, rows: int, fmt) -> Report:
+def check_colsum(name, out, ref, abs_sum, rows: int, fmt, term_err=None) -> Report:
+    """Column sums: |o - r| <= atol, or <= half an fp32 step + the rounding of
+    a depth-ceil(log2 rows) summation of |terms| (abs_sum).  `term_err`, when
+    given, is the per-column sum of the error bounds of the summed terms
+    themselves (terms that the GPU forms in float32 before summing them)."""
     out = np.asarray(out, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     s = np.asarray(abs_sum, dtype=np.float64)
     atol = ATOL[fmt]
     depth = math.ceil(math.log2(max(rows, 2)))
     tol = np.maximum(atol, 0.5 * ulp(ref, F32) + depth * 2.0 ** -24 * s)
+    if term_err is not None:
+        tol = tol + np.asarray(term_err, dtype=np.float64)
     err = np.abs(out - ref)
     return _finish(name, out, ref, err, tol, atol)
 

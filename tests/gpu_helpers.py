@@ -81,6 +81,44 @@ def check_fused(orc, inp, p, seed, z, y, mean, rstd, mask, fmt, eps=EPS, name="f
     return assert_reports(*reps)
 
 
+def check_dropout_bwd(orc, dy, dz_extra, z, gamma, mean, rstd, p, seed, dres, dx, dgamma,
+                      dbeta, dbias, fmt, name="drop_bwd"):
+    """Reference of the prologue backward from the stored inputs: dz = the
+    LayerNorm's dx + dz_extra, dresidual = dz, dx = keep * dz / (1 - p),
+    dbias = column sums of dx; dgamma, dbeta as for the LayerNorm backward.
+    The GPU forms dz in float32 (the dx clause of the tolerance rule, plus one
+    rounding of the dz_extra add) and scales it by 1/(1 - p) before rounding;
+    dbias sums those float32 values."""
+    import math
+    rows, cols = z.shape[0], z.shape[-1]
+    dy64, z64 = f64(dy).reshape(rows, cols), f64(z).reshape(rows, cols)
+    mu64, rs64, g64 = f64(mean), f64(rstd), f64(gamma)
+    ez64 = np.zeros_like(dy64) if dz_extra is None else f64(dz_extra).reshape(rows, cols)
+    dz = orc.ln_bwd_dx(dy64, z64, g64, mu64, rs64) + ez64
+    scale = orc.ln_bwd_dx_scale(dy64, z64, g64, mu64, rs64) + np.abs(ez64)
+    keep = orc.dropout_keep(seed, p, rows, cols)
+    dx_ref, dbias_ref, sbias = orc.dropout_residual_bwd(dz, keep, p)
+    s = 1.0 / (1.0 - np.float64(np.float32(p)))
+    dx_scale = scale * s * keep
+    k = 4 + math.ceil(math.log2(max(cols, 2)))
+    bias_err = np.sum(k * 2.0 ** -24 * dx_scale, axis=0)
+    dg, db, sg, sb = orc.ln_bwd_params(dy64, z64, mu64, rs64)
+    reps = [
+        cmp.check_elementwise(f"{name}.dresidual", f64(dres).reshape(rows, cols), dz, fmt,
+                              term_scale=scale, row_len=cols),
+        cmp.check_elementwise(f"{name}.dx", f64(dx).reshape(rows, cols), dx_ref, fmt,
+                              term_scale=dx_scale, row_len=cols),
+        cmp.check_colsum(f"{name}.dgamma", f64(dgamma), dg, sg, rows, fmt),
+        cmp.check_colsum(f"{name}.dbeta", f64(dbeta), db, sb, rows, fmt),
+        cmp.check_colsum(f"{name}.dbias", f64(dbias), dbias_ref, sbias, rows, fmt,
+                         term_err=bias_err),
+    ]
+    # dropped positions carry exactly no gradient
+    dropped = f64(dx).reshape(rows, cols)[keep == 0]
+    assert np.all(dropped == 0.0), f"{name}: nonzero dx at dropped positions"
+    return assert_reports(*reps)
+
+
 def run_fwd_bwd(rows, cols, dtype, seed=0, x_mean=0.0, x_std=1.0):
     inp = dev(synth.layer_inputs(rows, cols, dtype, seed=seed, x_mean=x_mean, x_std=x_std,
                                  names=("x", "gamma", "beta", "dy")))

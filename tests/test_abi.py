@@ -17,7 +17,7 @@ LN_ERR_WORKSPACE, LN_ERR_UNSUPPORTED, LN_ERR_HIP = 5, 6, 7
 F32, F16, BF16 = 0, 1, 2
 
 # fake but non-NULL device addresses: validation never dereferences them
-A, B, C, D, E, F, G, H = (0x10000000 * k for k in range(1, 9))
+A, B, C, D, E, F, G, H, I, J, K, M = (0x10000000 * k for k in range(1, 13))
 
 
 @pytest.fixture(scope="module")
@@ -38,7 +38,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
     assert {"ln_fwd", "bias_dropout_residual_ln_fwd", "ln_bwd_dx", "ln_bwd_dgamma_dbeta",
-            "ln_bwd_workspace_bytes", "ln_status_string"} <= set(names)
+            "ln_bwd_workspace_bytes", "ln_status_string", "bias_dropout_residual_ln_bwd",
+            "bias_dropout_residual_ln_bwd_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -155,7 +156,52 @@ def test_dgamma_dbeta_validation(L):
 def test_debug_force_path_validation(L):
     assert L.ln_debug_force_path(48, 1, 0) == LN_ERR_UNSUPPORTED
     assert L.ln_debug_force_path(64, 9, 0) == LN_ERR_UNSUPPORTED
-    assert L.ln_debug_force_path(128, 2, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(128, 3, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(128, 2, 0) == LN_OK          # prologue-backward layout
+    assert L.ln_debug_force_path(0, 0, 0) == LN_OK
     assert L.ln_debug_force_path(1024, 8, 0) == LN_ERR_UNSUPPORTED
     assert L.ln_debug_force_path(64, 3, 0) == LN_OK
     assert L.ln_debug_force_path(0, 0, 0) == LN_OK
+
+
+def test_dropout_bwd_workspace_bytes(L):
+    f = L.bias_dropout_residual_ln_bwd_workspace_bytes
+    assert f(0, 10) == 0 and f(10, 0) == 0 and f(-1, 10) == 0
+    # the same P partitions as the LayerNorm backward, three kinds of partials
+    assert f(8192, 1280) == 256 * 3 * 1280 * 4
+    assert f(64, 768) == 64 * 3 * 768 * 4
+    assert f(5, 7) * 2 == L.ln_bwd_workspace_bytes(5, 7) * 3
+
+
+def drop_bwd(L, dy=A, ez=None, z=B, g=C, mean=D, rstd=E, dres=F, dx=G, dg=H, db=I, dbias=J,
+             ws=K, wsb=None, rows=4, cols=8, p=0.1, seed=0, dt=BF16):
+    if wsb is None:
+        wsb = L.bias_dropout_residual_ln_bwd_workspace_bytes(rows, cols)
+    return L.bias_dropout_residual_ln_bwd(dy, ez, z, g, mean, rstd, dres, dx, dg, db, dbias,
+                                          ws, wsb, rows, cols, p, seed, dt, None)
+
+
+def test_dropout_bwd_validation(L):
+    for k in ("dy", "z", "g", "mean", "rstd", "dres", "dx", "dg", "db", "dbias", "ws"):
+        assert drop_bwd(L, **{k: None}) == LN_ERR_NULL, k
+    assert drop_bwd(L, rows=0) == LN_OK                       # dz_extra may be NULL
+    assert drop_bwd(L, rows=0, ez=M) == LN_OK
+    assert drop_bwd(L, rows=-1) == LN_ERR_SHAPE
+    assert drop_bwd(L, cols=0) == LN_ERR_SHAPE
+    assert drop_bwd(L, dt=5) == LN_ERR_DTYPE
+    for p in (-0.1, 1.0, float("nan")):
+        assert drop_bwd(L, p=p) == LN_ERR_PARAM, p
+    for dt in (F32, F16, BF16):
+        assert drop_bwd(L, cols=8193, dt=dt) == LN_ERR_UNSUPPORTED, dt
+        assert drop_bwd(L, cols=8192, rows=0, dt=dt) == LN_OK, dt
+    need = L.bias_dropout_residual_ln_bwd_workspace_bytes(4, 8)
+    assert drop_bwd(L, wsb=need - 4) == LN_ERR_WORKSPACE
+    assert drop_bwd(L, wsb=L.ln_bwd_workspace_bytes(4, 8)) == LN_ERR_WORKSPACE
+    # in place on one input each is allowed (checked on an empty call) ...
+    assert drop_bwd(L, rows=0, dres=A, dx=B) == LN_OK
+    # ... but the two outputs may not coincide, or partially overlap inputs
+    assert drop_bwd(L, dres=G) == LN_ERR_UNSUPPORTED
+    assert drop_bwd(L, dres=A + 2) == LN_ERR_UNSUPPORTED
+    assert drop_bwd(L, dbias=H) == LN_ERR_UNSUPPORTED             # dbias over dgamma
+    assert drop_bwd(L, ws=B) == LN_ERR_UNSUPPORTED                # workspace over z
+    assert drop_bwd(L, rows=0, dx=M, ez=M) == LN_OK               # in place on dz_extra
