@@ -228,6 +228,8 @@ def configs_report(cpp_launch: bool = True) -> None:
         calls without saved statistics: microseconds per call from a C++
         loop (the `launch_bench` tool, run first as a child process), a
         Python loop through the binding, and a HIP graph of the calls;
+      * the fused backward of the whole layer (bias_dropout_residual_ln_bwd)
+        at 8192x1280 bf16, alone and after the fused forward;
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
@@ -334,6 +336,66 @@ def configs_report(cpp_launch: bool = True) -> None:
         emit(rec)
         del st, ws
         torch.cuda.empty_cache()
+
+    # the backward of the whole fused layer: LayerNorm dx + the prologue's
+    # backward (dresidual, dx with the regenerated mask, dgamma/dbeta/dbias),
+    # alone and after the fused forward (a training layer), rotated past the
+    # cache
+    R, C, S = ROWS, COLS, 8
+    dt16 = torch.bfloat16
+    inp = synth.layer_inputs(R, C, dt16, seed=SEED)
+    ez_cpu = synth.layer_inputs(R, C, dt16, seed=SEED + 1, names=("dy",))["dy"]
+    sh = {k: inp[k].to(dev) for k in ("bias", "gamma", "beta")}
+    st = []
+    for _ in range(S):
+        a = {k: inp[k].to(dev) for k in ("x", "residual", "dy")}
+        a["ez"] = ez_cpu.to(dev)
+        for k in ("z", "y", "dres", "dxin"):
+            a[k] = torch.empty((R, C), dtype=dt16, device=dev)
+        a["mean"] = torch.empty(R, dtype=torch.float32, device=dev)
+        a["rstd"] = torch.empty(R, dtype=torch.float32, device=dev)
+        st.append(a)
+    del inp
+    wsd = mb.dropout_workspace(R, C, dev)
+    pg = [torch.empty(C, dtype=torch.float32, device=dev) for _ in range(3)]
+
+    def lfwd(i):
+        a = st[i % S]
+        mb.bias_dropout_residual_ln_fwd(a["x"], sh["bias"], a["residual"], sh["gamma"],
+                                        sh["beta"], P_DROP, SEED, EPS, residual_out=a["z"],
+                                        y=a["y"], mean=a["mean"], rstd=a["rstd"])
+
+    def lbwd(i):
+        a = st[(i + S // 2) % S]
+        mb.bias_dropout_residual_ln_bwd(a["dy"], a["z"], sh["gamma"], a["mean"], a["rstd"],
+                                        P_DROP, SEED, dz_extra=a["ez"], dresidual=a["dres"],
+                                        dx=a["dxin"], dgamma=pg[0], dbeta=pg[1], dbias=pg[2],
+                                        workspace=wsd)
+
+    def layer(i):
+        lfwd(i)
+        lbwd(i)
+
+    for i in range(S):
+        lfwd(i)
+    torch.cuda.synchronize()
+    n = 200
+    ms_b = timed(capture(lbwd, n), n)
+    ms_l = timed(capture(layer, n), n)
+    bb = 5 * R * C * 2 + C * 2 + 8 * R + 12 * C
+    lb = algorithmic_bytes(R, C, 2)["fused_fwd"] + bb
+    emit({"workload": "fused backward of bias+dropout(p=0.1)+residual+LayerNorm "
+                      "(dz_extra given), 8192x1280 bf16, rotated",
+          "bytes_per_pass": bb, "us_per_pass": round(ms_b * 1e3, 3),
+          "GBps": round(bb / (ms_b * 1e-3) / 1e9, 1),
+          "pct_of_hbm_peak": round(100.0 * bb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)})
+    emit({"workload": "training layer: fused forward + fused backward (p=0.1), "
+                      "8192x1280 bf16, rotated",
+          "bytes_per_pass": lb, "us_per_pass": round(ms_l * 1e3, 3),
+          "GBps": round(lb / (ms_l * 1e-3) / 1e9, 1),
+          "pct_of_hbm_peak": round(100.0 * lb / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)})
+    del st, wsd
+    torch.cuda.empty_cache()
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")
