@@ -337,3 +337,57 @@ void orc_ln_bwd_params(const double* dy, const double* x, const double* mean,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Attention softmax ([L10] §4.1, [L11] §3).                                 */
+/* ------------------------------------------------------------------------ */
+
+void orc_attn_softmax_fwd(const double* x, const double* mask, int64_t rows_per_mask,
+                          int64_t rows, int64_t m, double scale, int causal, double* y) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * m;
+        const double* mr = mask ? mask + (r / rows_per_mask) * m : NULL;
+        double* yr = y + r * m;
+        int64_t q = r % m;
+        /* scaled and masked scores, kept in y for the two passes below */
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < m; ++j) {
+            double t = scale * xr[j] + (mr ? mr[j] : 0.0);
+            if (causal && j > q) t = -INFINITY;
+            yr[j] = t;
+            if (t > mx) mx = t;
+        }
+        if (mx == -INFINITY) {
+            for (int64_t j = 0; j < m; ++j) yr[j] = 0.0;
+            continue;
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            double e = exp(yr[j] - mx);
+            yr[j] = e;
+            sum += e;
+        }
+        for (int64_t j = 0; j < m; ++j) yr[j] = yr[j] / sum;
+    }
+}
+
+void orc_attn_softmax_bwd(const double* dy, const double* y, const uint8_t* keep, float p,
+                          int64_t rows, int64_t m, double scale, double* dx) {
+    double q = 1.0 - (double)p;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* dyr = dy + r * m;
+        const double* yr = y + r * m;
+        double s = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            int64_t i = r * m + j;
+            double g = keep ? (keep[i] ? dyr[j] / q : 0.0) : dyr[j];
+            dx[i] = g;               /* g, kept for the second pass */
+            s += g * yr[j];
+        }
+        for (int64_t j = 0; j < m; ++j) {
+            int64_t i = r * m + j;
+            dx[i] = scale * yr[j] * (dx[i] - s);
+        }
+    }
+}
+

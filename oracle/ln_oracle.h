@@ -142,6 +142,25 @@ void orc_ln_bwd_params(const double* dy, const double* x, const double* mean,
                        double* dgamma, double* dbeta,
                        double* sgamma, double* sbeta);
 
+/* Attention softmax forward ([L10] §4.1: per row, scale, add the mask, the
+ * row maximum, exp of the difference, the row sum, divide), one row at a
+ * time in double:
+ *   t_j = scale * x_j + (mask ? mask[(r / rows_per_mask) * m + j] : 0);
+ *   causal: t_j = -inf for keys j > q, q = r mod m (square score blocks);
+ *   mx = max_j t_j; y_j = exp(t_j - mx) / sum_k exp(t_k - mx).
+ * A row whose every key is masked (mx = -inf) gives y = 0. */
+void orc_attn_softmax_fwd(const double* x, const double* mask, int64_t rows_per_mask,
+                          int64_t rows, int64_t m, double scale, int causal, double* y);
+
+/* Attention softmax backward fused with the dropout backward ([L11] §3: the
+ * Jacobian y_i (delta_ij - y_j) times a vector needs one dot product; the
+ * dropout backward is applied first, in registers):
+ *   g_j = keep ? (keep_j ? dy_j / (1 - p) : 0) : dy_j;   s = sum_j g_j y_j;
+ *   dx_j = scale * y_j * (g_j - s).
+ * keep may be NULL (no dropout). */
+void orc_attn_softmax_bwd(const double* dy, const double* y, const uint8_t* keep, float p,
+                          int64_t rows, int64_t m, double scale, double* dx);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,10 @@ def _load():
         getattr(lib, name).argtypes = [dp, dp, dp, dp, dp, i64, i64, dp]
     lib.orc_ln_bwd_params.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, dp, dp]
     lib.orc_dropout_residual_bwd.argtypes = [dp, u8p, ctypes.c_float, i64, i64, dp, dp, dp]
+    lib.orc_attn_softmax_fwd.argtypes = [dp, dp, i64, i64, i64, ctypes.c_double, ctypes.c_int,
+                                         dp]
+    lib.orc_attn_softmax_bwd.argtypes = [dp, dp, u8p, ctypes.c_float, i64, i64, ctypes.c_double,
+                                         dp]
     _lib = lib
     return lib
 
@@ -221,7 +225,41 @@ def dropout_residual_bwd(dz, keep, p: float):
     return dx, db, sb
 
 
+
+def attn_softmax_fwd(x, scale: float = 1.0, mask=None, rows_per_mask: int = 1,
+                     causal: bool = False) -> np.ndarray:
+    """Row softmax of scale*x + mask (mask row r // rows_per_mask), causal over
+    square blocks (q = r mod cols); fully masked rows give 0."""
+    x = _d(x)
+    rows, m = _shape2(x)
+    mk = None
+    if mask is not None:
+        mk = _d(mask)
+        if mk.ndim != 2 or mk.shape[1] != m or mk.shape[0] * int(rows_per_mask) < rows:
+            raise ValueError("mask must be [ceil(rows / rows_per_mask), cols]")
+    y = np.empty_like(x)
+    _load().orc_attn_softmax_fwd(_ptr(x), None if mk is None else _ptr(mk), int(rows_per_mask),
+                                 rows, m, float(scale), 1 if causal else 0, _ptr(y))
+    return y
+
+
+def attn_softmax_bwd(dy, y, keep=None, p: float = 0.0, scale: float = 1.0) -> np.ndarray:
+    """dx of the attention softmax, after the dropout backward (keep, p)."""
+    dy, y = _d(dy), _d(y)
+    rows, m = _shape2(y)
+    kp = None
+    if keep is not None:
+        kp = np.ascontiguousarray(keep, dtype=np.uint8)
+        if kp.shape != y.shape:
+            raise ValueError("keep must match y")
+    dx = np.empty_like(y)
+    _load().orc_attn_softmax_bwd(_ptr(dy), _ptr(y), None if kp is None else _ptr(kp, ctypes.c_uint8),
+                                 ctypes.c_float(p), rows, m, float(scale), _ptr(dx))
+    return dx
+
+
 __all__ = ["F32", "F16", "BF16", "build", "round_to", "round_scalar", "ln_fwd",
            "row_stats_welford", "var_naive_f32", "var_chan_f32", "philox4x32_10",
            "dropout_threshold", "dropout_keep", "bias_dropout_residual",
-           "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params", "dropout_residual_bwd"]
+           "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params", "dropout_residual_bwd",
+           "attn_softmax_fwd", "attn_softmax_bwd"]

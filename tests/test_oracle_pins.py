@@ -457,3 +457,93 @@ def test_dx_term_scale_bounds_dx(orc):
     scale = orc.ln_bwd_dx_scale(dy, x, gamma, mean, rstd)
     assert np.all(np.abs(dx) <= scale * (1 + 1e-12))
     assert np.all(scale <= 10 * rstd[:, None] * (np.abs(gamma * dy) + 10))
+
+
+# --------------------------------------------------------------------------
+# Attention softmax: "Accelerating Transformer on GPU (I)" §4.1 (forward:
+# scale, mask, max, exp, sum, divide) and "(II)" §3 (backward, fused with
+# the dropout backward)
+# --------------------------------------------------------------------------
+
+def test_softmax_backward_worked_example(orc):
+    g = _golden_kv("softmax_backward_example.txt")
+    y, dy = np.array([g["y"]]), np.array([g["dy"]])
+    dx = orc.attn_softmax_bwd(dy, y)
+    assert np.allclose(dx[0], g["dx"], rtol=0, atol=1e-15)
+    assert abs(float(np.sum(dy * y)) - g["s"][0]) < 1e-15
+    assert abs(float(np.sum(dx))) < 1e-15          # the page's check: the sum is 0
+
+
+def test_softmax_forward_matches_library(orc):
+    from scipy.special import softmax
+    rng = np.random.default_rng(21)
+    for m in (1, 2, 7, 64, 1000):
+        x = _rows(rng, 5, m, std=3.0)
+        for scale in (1.0, 0.125):
+            y = orc.attn_softmax_fwd(x, scale=scale)
+            ref = softmax(scale * x, axis=1)
+            assert np.allclose(y, ref, rtol=1e-13, atol=1e-300), (m, scale)
+            assert np.allclose(np.sum(y, axis=1), 1.0, rtol=0, atol=1e-13)
+
+
+def test_softmax_forward_shift_invariance_and_large_scores(orc):
+    rng = np.random.default_rng(22)
+    x = _rows(rng, 4, 33)
+    y = orc.attn_softmax_fwd(x)
+    # softmax ignores a constant added to the row; huge scores do not overflow
+    # because the row maximum is subtracted first
+    assert np.allclose(orc.attn_softmax_fwd(x + 1000.0), y, rtol=1e-12, atol=1e-15)
+    big = orc.attn_softmax_fwd(np.array([[1000.0, 999.0, -1000.0]]))
+    e = np.exp(-1.0)
+    assert np.allclose(big[0], [1 / (1 + e), e / (1 + e), 0.0], rtol=1e-14, atol=1e-300)
+
+
+def test_softmax_forward_masks(orc):
+    from scipy.special import softmax
+    rng = np.random.default_rng(23)
+    m = 16
+    x = _rows(rng, 2 * m, m)                       # two square blocks
+    y = orc.attn_softmax_fwd(x, causal=True)
+    for r in range(2 * m):
+        q = r % m
+        assert np.all(y[r, q + 1:] == 0.0)
+        assert np.allclose(y[r, :q + 1], softmax(x[r, :q + 1]), rtol=1e-13, atol=1e-300)
+    # an additive mask row per 8 rows; -inf removes a key, a finite value shifts it
+    mask = np.zeros((4, m))
+    mask[1, 3] = -np.inf
+    mask[2, :] = 5.0
+    y = orc.attn_softmax_fwd(x, mask=mask, rows_per_mask=8)
+    assert np.all(y[8:16, 3] == 0.0)
+    assert np.allclose(y[16:24], softmax(x[16:24], axis=1), rtol=1e-13)
+    # a row with every key masked gives zeros
+    mask[3, :] = -np.inf
+    y = orc.attn_softmax_fwd(x, mask=mask, rows_per_mask=8)
+    assert np.all(y[24:32] == 0.0)
+
+
+def _softmax_loss(orc, x, dy, keep, p, scale):
+    y = orc.attn_softmax_fwd(x, scale=scale)
+    yd = np.where(keep == 1, y / (1.0 - np.float64(np.float32(p))), 0.0)
+    return float(np.sum(dy * yd))
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 8])
+def test_softmax_backward_finite_differences(orc, m):
+    rng = np.random.default_rng(400 + m)
+    rows, p, scale = 3, 0.25, 0.7
+    x, dy = _rows(rng, rows, m), _rows(rng, rows, m)
+    keep = (rng.uniform(size=(rows, m)) >= p).astype(np.uint8)
+    y = orc.attn_softmax_fwd(x, scale=scale)
+    dx = orc.attn_softmax_bwd(dy, y, keep=keep, p=p, scale=scale)
+    for r in range(rows):
+        for j in range(m):
+            h = 1e-6 * max(1.0, abs(x[r, j]))
+            xp, xm = x.copy(), x.copy()
+            xp[r, j] += h
+            xm[r, j] -= h
+            fd = (_softmax_loss(orc, xp, dy, keep, p, scale)
+                  - _softmax_loss(orc, xm, dy, keep, p, scale)) / (2 * h)
+            assert abs(fd - dx[r, j]) <= 1e-8 * max(1.0, np.max(np.abs(dx))), (r, j)
+    # each row of dx sums to 0 (softmax ignores a constant added to its input)
+    assert np.allclose(np.sum(dx, axis=1), 0.0, atol=1e-14)
+
