@@ -219,6 +219,44 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
                                          int64_t rows, int64_t cols, float p, uint64_t seed,
                                          ln_dtype_t dt, hipStream_t stream);
 
+/*
+ * Attention softmax forward over rows of `cols` scores ([L10] §4.1: per row,
+ * scale, add the mask, subtract the row maximum, exp, divide by the row sum;
+ * one row per group of lanes, held in registers):
+ *   t_j = scale * x_j + mask[r / rows_per_mask][j]   (mask NULL: no term);
+ *   causal = 1: t_j = -inf for keys j > q, q = r mod cols (rows are square
+ *               [L, L] score blocks one after another; keys past the query
+ *               are not read);
+ *   y_j = exp(t_j - max t) / sum_k exp(t_k - max t); a row whose every key
+ *   is masked gives y = 0.
+ *   y_dropped_j = keep_j ? y_j / (1 - p) : 0 with the same mask function of
+ *   (seed, row, column, p) as bias_dropout_residual_ln_fwd; NULL skips it.
+ *   x [rows, cols] T input;  mask [ceil(rows / rows_per_mask), cols] T or
+ *   NULL;  y [rows, cols] T output (may equal x);  y_dropped [rows, cols] T
+ *   output or NULL (may equal x, not y).
+ * scale must be finite; causal 0 or 1; p in [0, 1); rows_per_mask >= 1 when
+ * mask is given.  Arithmetic in float32 (exp by the device's exp2).
+ */
+ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
+                             void* y_dropped, int64_t rows, int64_t cols, float scale,
+                             int causal, float p, uint64_t seed, ln_dtype_t dt,
+                             hipStream_t stream);
+
+/*
+ * Attention softmax backward fused with the attention-dropout backward
+ * ([L11] §3: the dropout backward in registers first, then one dot product
+ * per row):  g_j = keep_j ? dy_j / (1 - p) : 0 (the forward's mask
+ * regenerated; p = 0 keeps all), s = sum_j g_j * y_j,
+ * dx_j = scale * y_j * (g_j - s).
+ *   dy [rows, cols] T: gradient of y_dropped (of y when p = 0).
+ *   y  [rows, cols] T: the forward's y.   dx [rows, cols] T output (may equal
+ *   dy or y).  causal = 1 skips reading the keys past the query (y = 0
+ *   there, so dx = 0).
+ */
+ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
+                             int64_t cols, float scale, int causal, float p, uint64_t seed,
+                             ln_dtype_t dt, hipStream_t stream);
+
 /* Static English description of a status code (never NULL). */
 const char* ln_status_string(ln_status_t status);
 

@@ -54,6 +54,11 @@ def lib() -> ctypes.CDLL:
     L.bias_dropout_residual_ln_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                ctypes.c_size_t, i64, i64, f32, ctypes.c_uint64,
                                                i32, vp]
+    L.attn_softmax_fwd.restype = i32
+    L.attn_softmax_fwd.argtypes = [vp, vp, i64, vp, vp, i64, i64, f32, i32, f32,
+                                   ctypes.c_uint64, i32, vp]
+    L.attn_softmax_bwd.restype = i32
+    L.attn_softmax_bwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, f32, ctypes.c_uint64, i32, vp]
     L.ln_debug_force_path.restype = i32
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
     L.ln_debug_force_grid.restype = i32
@@ -261,6 +266,44 @@ def bias_dropout_residual_ln_bwd(dy, z, gamma, mean, rstd, p: float, seed: int, 
         workspace.numel() * 4, rows, cols, float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, _dt(z),
         _stream(z)))
     return dresidual, dx, dgamma, dbeta, dbias
+
+
+def attn_softmax_fwd(x, scale: float = 1.0, *, mask=None, rows_per_mask: int = 1,
+                     causal: bool = False, p: float = 0.0, seed: int = 0, y=None,
+                     y_dropped=None, want_dropped: bool = False):
+    """Row softmax of scale*x + mask (+ causal mask) -> (y, y_dropped or None)."""
+    rows, cols = _mat(x, "x")
+    if mask is not None:
+        mrows = (rows + rows_per_mask - 1) // max(rows_per_mask, 1)
+        if (not mask.is_cuda or not mask.is_contiguous() or mask.dtype != x.dtype
+                or mask.numel() != mrows * cols):
+            raise ValueError(f"mask must be a contiguous GPU tensor [{mrows}, {cols}] {x.dtype}")
+    y = _out(y, x.shape, x.dtype, x.device, "y")
+    if want_dropped or y_dropped is not None:
+        y_dropped = _out(y_dropped, x.shape, x.dtype, x.device, "y_dropped")
+    if rows == 0:
+        return y, y_dropped
+    _check(lib().attn_softmax_fwd(_ptr(x), _ptr(mask), int(rows_per_mask), _ptr(y),
+                                  _ptr(y_dropped), rows, cols, float(scale),
+                                  1 if causal else 0, float(p),
+                                  int(seed) & 0xFFFFFFFFFFFFFFFF, _dt(x), _stream(x)))
+    return y, y_dropped
+
+
+def attn_softmax_bwd(dy, y, scale: float = 1.0, *, causal: bool = False, p: float = 0.0,
+                     seed: int = 0, dx=None):
+    """dx of the attention softmax after the dropout backward (mask from seed, p)."""
+    rows, cols = _mat(y, "y")
+    if dy.shape != y.shape or dy.dtype != y.dtype:
+        raise ValueError("dy must match y")
+    _mat(dy, "dy")
+    dx = _out(dx, y.shape, y.dtype, y.device, "dx")
+    if rows == 0:
+        return dx
+    _check(lib().attn_softmax_bwd(_ptr(dy), _ptr(y), _ptr(dx), rows, cols, float(scale),
+                                  1 if causal else 0, float(p),
+                                  int(seed) & 0xFFFFFFFFFFFFFFFF, _dt(y), _stream(y)))
+    return dx
 
 
 def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,

@@ -21,6 +21,17 @@ hipError_t launch_fwd_bf16(const Path&, bool, const FwdArgs&, hipStream_t);
 hipError_t launch_bwd_f32(const Path&, BwdMode, const BwdArgs&, hipStream_t);
 hipError_t launch_bwd_f16(const Path&, BwdMode, const BwdArgs&, hipStream_t);
 hipError_t launch_bwd_bf16(const Path&, BwdMode, const BwdArgs&, hipStream_t);
+hipError_t launch_softmax_f32(const Path&, bool, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_f16(const Path&, bool, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_bf16(const Path&, bool, const SmArgs&, hipStream_t);
+
+hipError_t launch_softmax(Dt dt, const Path& p, bool backward, const SmArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_softmax_f32(p, backward, a, s);
+    case Dt::F16: return launch_softmax_f16(p, backward, a, s);
+    default: return launch_softmax_bf16(p, backward, a, s);
+    }
+}
 
 hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStream_t s) {
     switch (dt) {
@@ -127,6 +138,18 @@ Path pick_path(Dt dt, int64_t cols, bool vec) {
     const int64_t ns = (cols + E - 1) / E;
     return E == 4 ? pick(true, ns, vec, kFwd32, MBROW_N(kFwd32))
                   : pick(false, ns, vec, kFwd16, MBROW_N(kFwd16));
+}
+
+static const int kSm32[][2] = {{16, 1}, {16, 2}, {16, 4}, {32, 2}, {32, 4}, {64, 2}, {64, 4},
+                               {64, 8}, {128, 4}, {256, 4}, {512, 4}, {1024, 4}};
+static const int kSm16[][2] = {{16, 1}, {16, 2}, {32, 1}, {32, 2}, {64, 1}, {64, 2}, {64, 4},
+                               {128, 4}, {256, 4}, {512, 4}};
+
+Path pick_softmax_path(Dt dt, int64_t cols, bool vec) {
+    const int E = elems_per_slot(dt);
+    const int64_t ns = (cols + E - 1) / E;
+    return E == 4 ? pick(true, ns, vec, kSm32, MBROW_N(kSm32), false, true)
+                  : pick(false, ns, vec, kSm16, MBROW_N(kSm16), false, true);
 }
 
 // The same choice with and without partials, so the fused and the
@@ -457,6 +480,75 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
     return from_hip(launch_fold(workspace, a.parts, cols, 3, out, stream));
 }
 
+ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
+                             void* y_dropped, int64_t rows, int64_t cols, float scale,
+                             int causal, float p, uint64_t seed, ln_dtype_t dt,
+                             hipStream_t stream) {
+    if (!x || !y) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    if (!std::isfinite(scale) || (causal != 0 && causal != 1)) return LN_ERR_PARAM;
+    if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
+    if (mask && rows_per_mask < 1) return LN_ERR_PARAM;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es;
+    const int64_t mrows = mask ? (rows + rows_per_mask - 1) / rows_per_mask : 0;
+    const Span outs[] = {{y, tb, true}, {y_dropped, y_dropped ? tb : 0, true}};
+    const Span ins[] = {{x, tb, true}, {mask, (size_t)mrows * (size_t)cols * es, false}};
+    st = check_aliasing(outs, 2, ins, 2);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(x) && aligned16(y) && (!mask || aligned16(mask)) &&
+                     (!y_dropped || aligned16(y_dropped)) && (cols * (int64_t)es) % 16 == 0;
+    SmArgs a{};
+    a.x = x; a.mask = mask; a.out = y; a.out2 = y_dropped;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.rows_per_mask = mask ? rows_per_mask : 1;
+    a.scale = scale;
+    a.causal = causal;
+    a.thr = (uint32_t)std::floor((double)p * 65536.0 + 0.5);
+    a.pscale = (float)(1.0 / (1.0 - (double)p));
+    a.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    a.seed_hi = (uint32_t)(seed >> 32);
+    return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec), false, a, stream));
+}
+
+ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
+                             int64_t cols, float scale, int causal, float p, uint64_t seed,
+                             ln_dtype_t dt, hipStream_t stream) {
+    if (!dy || !y || !dx) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    if (!std::isfinite(scale) || (causal != 0 && causal != 1)) return LN_ERR_PARAM;
+    if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es;
+    const Span outs[] = {{dx, tb, true}};
+    const Span ins[] = {{dy, tb, true}, {y, tb, true}};
+    st = check_aliasing(outs, 1, ins, 2);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(dy) && aligned16(y) && aligned16(dx) &&
+                     (cols * (int64_t)es) % 16 == 0;
+    SmArgs a{};
+    a.x = dy; a.y = y; a.out = dx;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.rows_per_mask = 1;
+    a.scale = scale;
+    a.causal = causal;
+    a.thr = (uint32_t)std::floor((double)p * 65536.0 + 0.5);
+    a.pscale = (float)(1.0 / (1.0 - (double)p));
+    a.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    a.seed_hi = (uint32_t)(seed >> 32);
+    return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec), true, a, stream));
+}
+
 ln_status_t ln_debug_force_grid(int workgroups_per_cu) {
     g_force_grid.store(workgroups_per_cu, std::memory_order_relaxed);
     return LN_OK;
@@ -465,7 +557,8 @@ ln_status_t ln_debug_force_grid(int workgroups_per_cu) {
 ln_status_t ln_debug_force_path(int lanes_per_row, int slots_per_lane, int scalar) {
     const int g = lanes_per_row, v = slots_per_lane;
     if (g != 0 && !have_instance(true, g, v) && !have_instance(false, g, v) &&
-        !in_list(kDrop32, MBROW_N(kDrop32), g, v) && !in_list(kDrop16, MBROW_N(kDrop16), g, v))
+        !in_list(kDrop32, MBROW_N(kDrop32), g, v) && !in_list(kDrop16, MBROW_N(kDrop16), g, v) &&
+        !in_list(kSm32, MBROW_N(kSm32), g, v) && !in_list(kSm16, MBROW_N(kSm16), g, v))
         return LN_ERR_UNSUPPORTED;
     g_force_g.store(lanes_per_row, std::memory_order_relaxed);
     g_force_v.store(lanes_per_row ? slots_per_lane : 0, std::memory_order_relaxed);

@@ -305,6 +305,19 @@ __device__ inline float group_sum(float v) {
     return v;
 }
 
+// Maximum over aligned groups of G lanes (G = 1..64), in every lane of the
+// group (the same butterfly as group_sum).
+template <int G>
+__device__ inline float group_max(float v) {
+    if constexpr (G >= 2) v = fmaxf(v, partner<1>(v));
+    if constexpr (G >= 4) v = fmaxf(v, partner<2>(v));
+    if constexpr (G >= 8) v = fmaxf(v, partner<4>(v));
+    if constexpr (G >= 16) v = fmaxf(v, partner<8>(v));
+    if constexpr (G >= 32) v = fmaxf(v, partner<16>(v));
+    if constexpr (G >= 64) v = fmaxf(lane_read(v, 0), lane_read(v, 32));
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // Row statistics.  Each lane holds (n, s, q): its element count, the sum of
 // its values minus a shift c shared by the whole group, and the sum of

@@ -115,6 +115,36 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t blocks);
 hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(Dt dt, const Path& p, BwdMode mode, const BwdArgs& a, hipStream_t s);
 hipError_t launch_dropout_mask(const FwdArgs& a, hipStream_t s);   // a.mask_out, rows, m, thr, seed
+// Attention softmax over rows of `m` scores.
+struct SmArgs {
+    const void* x;          // forward: scores; backward: gradient of the output
+    const void* mask;       // forward: additive mask rows, or NULL
+    const void* y;          // backward: the forward's softmax output
+    void* out;              // forward: y; backward: dx
+    void* out2;             // forward: dropped output, or NULL
+    int64_t rows;
+    int64_t m;
+    int64_t nslots;
+    int64_t rows_per_mask;  // row r adds mask row r / rows_per_mask
+    float scale;            // forward: multiplies x; backward: multiplies dx
+    float pscale;           // 1 / (1 - p)
+    uint32_t thr;           // keep iff 16-bit uniform >= thr
+    uint32_t seed_lo;
+    uint32_t seed_hi;
+    int causal;             // keys j > r mod m masked (square score blocks)
+};
+
+// Row layouts of the softmax kernels.
+#define MBROW_SM_LAYOUTS_F32(X)                                             \
+    X(16, 1) X(16, 2) X(16, 4) X(32, 2) X(32, 4) X(64, 2) X(64, 4) X(64, 8) \
+    X(128, 4) X(256, 4) X(512, 4) X(1024, 4)
+#define MBROW_SM_LAYOUTS_16(X)                                              \
+    X(16, 1) X(16, 2) X(32, 1) X(32, 2) X(64, 1) X(64, 2) X(64, 4)          \
+    X(128, 4) X(256, 4) X(512, 4)
+
+Path pick_softmax_path(Dt dt, int64_t cols, bool vec);
+hipError_t launch_softmax(Dt dt, const Path& p, bool backward, const SmArgs& a, hipStream_t s);
+
 // Fold of [P][kinds][m] partials (kinds = 2 or 3) into out[0..kinds-1].
 struct FoldOut {
     float* p[3];

@@ -1,0 +1,291 @@
+// softmax.hip -- attention softmax forward and backward for gfx950.
+// Compiled once per storage type (-DMBROW_DT=0 fp32, 1 fp16, 2 bf16).
+//
+// Forward ("Accelerating Transformer on GPU (I)" §4.1): every row of scores
+// is scaled and gets its additive mask row and the causal mask; then the row
+// maximum (one butterfly), exp of the difference and the row sum (a second
+// butterfly), and the normalised row is written.  With dropout the dropped
+// copy (keep ? y / (1 - p) : 0, keep from the same Philox mask as the
+// LayerNorm prologue) is written as well.  One row per group of G lanes,
+// held in registers, as in the LayerNorm forward; under the causal mask a
+// slot that lies wholly past the query is never read (its buffer offset is
+// out of range), so the masked half of the scores costs no reads.
+//
+// Backward ("Accelerating Transformer on GPU (II)" §3): the dropout backward
+// first, in registers (g = keep ? dy / (1 - p) : 0, the mask regenerated from
+// the seed), then one dot product s = sum g * y and dx = scale * y * (g - s).
+#include "ln_device.hpp"
+#include "ln_launch.hpp"
+
+#ifndef MBROW_DT
+#error "compile with -DMBROW_DT=0|1|2"
+#endif
+
+namespace mbrow {
+
+#if MBROW_DT == 0
+using St = StF32;
+#define MBROW_SUFFIX f32
+#elif MBROW_DT == 1
+using St = StF16;
+#define MBROW_SUFFIX f16
+#else
+using St = StBF16;
+#define MBROW_SUFFIX bf16
+#endif
+
+template <int G>
+struct SmGeometry {
+    static constexpr int NT = G <= 256 ? 256 : G;   // threads per workgroup
+    static constexpr int ROWS = NT / G;              // rows per block
+    static constexpr int WPR = G > 64 ? G / 64 : 1;  // waves per row
+};
+
+template <class S, int G, int V, bool VEC, bool BWD>
+__global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
+    constexpr int E = S::E;
+    constexpr int ROWS = SmGeometry<G>::ROWS;
+    constexpr int WPR = SmGeometry<G>::WPR;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int lg = tid % G;
+    const int rloc = tid / G;
+    const int m = (int)a.m;
+    const int nslots = (int)a.nslots;
+    const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
+
+    // slot i of this lane covers columns (i*G + lg)*E .. +E-1
+    bool ok[V];
+    uint32_t vo[VEC ? V : 1];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        ok[i] = i * G + lg < nslots;
+        if constexpr (VEC) vo[i] = slot_offset<S, G>(tid, i, m, ok[i]);
+    }
+    const int wrow = wave_first_row<G>(tid);
+    constexpr int64_t N = WaveRows<G>::N;   // rows of one wave
+    auto view = [&](const void* t, int64_t blk) {
+        const int64_t row0 = blk * ROWS + wrow;
+        const int64_t left = a.rows - row0;
+        return row_view<S>(t, row0, left < N ? left : N, m);
+    };
+    // cross-wave exchange of multi-wave rows: [buffer][max, sum][row][wave]
+    __shared__ float red[2][2][ROWS][WPR];
+    auto reduce_max = [&](float v, int buf) {
+        if constexpr (G <= 64) {
+            return group_max<G>(v);
+        } else {
+            v = group_max<64>(v);
+            if (lane == 0) red[buf][0][rloc][lg / 64] = v;
+            __syncthreads();
+            float r = red[buf][0][rloc][0];
+#pragma unroll
+            for (int k = 1; k < WPR; ++k) r = fmaxf(r, red[buf][0][rloc][k]);
+            return r;
+        }
+    };
+    auto reduce_sum = [&](float v, int buf) {
+        if constexpr (G <= 64) {
+            return group_sum<G>(v);
+        } else {
+            v = group_sum<64>(v);
+            if (lane == 0) red[buf][1][rloc][lg / 64] = v;
+            __syncthreads();
+            float r = red[buf][1][rloc][0];
+#pragma unroll
+            for (int k = 1; k < WPR; ++k) r = r + red[buf][1][rloc][k];
+            return r;
+        }
+    };
+
+    // Persistent walk over row blocks, uniform per workgroup (so the barriers
+    // of multi-wave rows are reached by all), one block at a time.
+    int it = 0;
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x, ++it) {
+        const int64_t row = blk * ROWS + rloc;
+        const bool rok = row < a.rows;
+        const int64_t r = rok ? row : 0;
+        const int q = (int)(r % m);   // query position under the causal mask
+        const int buf = it & 1;
+        // a slot is read unless it is past the row or wholly past the query
+        bool live[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) live[i] = ok[i] && (!a.causal || (i * G + lg) * E <= q);
+        // element e of slot i takes part: inside the row and not causally masked
+        auto valid = [&](int i, int e) {
+            const int col = (i * G + lg) * E + e;
+            return ok[i] && (VEC || col < m) && (!a.causal || col <= q);
+        };
+
+        u32x4 xr[V], yr[BWD ? V : 1], mr[BWD ? 1 : V];
+        const bool has_mask = !BWD && a.mask != nullptr;   // uniform
+        if constexpr (VEC) {
+            const rsrc_t vx = view(a.x, blk);
+            const rsrc_t vy = view(BWD ? a.y : a.x, blk);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const uint32_t off = live[i] ? vo[i] : kOob;
+                xr[i] = buf_load_nt(vx, off);
+                if constexpr (BWD) yr[i] = buf_load_nt(vy, off);
+            }
+            if constexpr (!BWD) {
+                if (has_mask) {
+                    // mask rows of this wave's rows: a contiguous range
+                    const int64_t row0 = blk * ROWS + wrow;
+                    const int64_t last = (row0 + N - 1 < a.rows ? row0 + N - 1 : a.rows - 1);
+                    const int64_t m0 = row0 / a.rows_per_mask;
+                    const int64_t nm = row0 < a.rows ? last / a.rows_per_mask - m0 + 1 : 0;
+                    const rsrc_t vm = row_view<S>(a.mask, m0, nm, m);
+                    const uint32_t mrow = (uint32_t)(r / a.rows_per_mask - m0);
+#pragma unroll
+                    for (int i = 0; i < V; ++i) {
+                        const uint32_t off = (live[i] && rok)
+                                                 ? mrow * (uint32_t)m * S::BYTES +
+                                                       (uint32_t)(i * G + lg) * 16u
+                                                 : kOob;
+                        mr[i] = buf_load(vm, off);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                const int col0 = (i * G + lg) * E;
+                load_elems<S>(a.x, r, m, col0, live[i] && rok, f);
+                xr[i] = S::pack(f);
+                if constexpr (BWD) {
+                    load_elems<S>(a.y, r, m, col0, live[i] && rok, f);
+                    yr[i] = S::pack(f);
+                } else if (has_mask) {
+                    load_elems<S>(a.mask, r / a.rows_per_mask, m, col0, live[i] && rok, f);
+                    mr[i] = S::pack(f);
+                }
+            }
+        }
+
+        if constexpr (!BWD) {
+            // scores: scale, mask, -inf where masked; the row maximum
+            float t[V][E];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float xv[E], mv[E];
+                S::unpack(xr[i], xv);
+                if (has_mask) S::unpack(mr[i], mv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float v = a.scale * xv[e];
+                    if (has_mask) v = v + mv[e];
+                    t[i][e] = valid(i, e) ? v : -INFINITY;
+                    mx = fmaxf(mx, t[i][e]);
+                }
+            }
+            mx = reduce_max(mx, buf);
+            // exp of the difference and the row sum (a row with every key
+            // masked has mx = -inf and gives zeros)
+            const bool live_row = mx != -INFINITY;
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    t[i][e] = live_row ? __expf(t[i][e] - mx) : 0.0f;
+                    s += t[i][e];
+                }
+            s = reduce_sum(s, buf);
+            const float inv = live_row ? 1.0f / s : 0.0f;
+            const rsrc_t vy = view(a.out, blk);
+            const rsrc_t vd = view(a.out2 ? a.out2 : a.out, blk);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int col0 = (i * G + lg) * E;
+                float yv[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) yv[e] = t[i][e] * inv;
+                if constexpr (VEC) {
+                    buf_store_nt(S::pack(yv), vy, vo[i]);
+                } else {
+                    store_elems<S>(a.out, r, m, col0, ok[i] && rok, yv);
+                }
+                if (a.out2) {
+                    const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                    float dv[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        dv[e] = kept<E>(w, col0, e, a.thr) ? yv[e] * a.pscale : 0.0f;
+                    if constexpr (VEC) {
+                        buf_store_nt(S::pack(dv), vd, vo[i]);
+                    } else {
+                        store_elems<S>(a.out2, r, m, col0, ok[i] && rok, dv);
+                    }
+                }
+            }
+        } else {
+            // dropout backward, then s = sum g * y and dx = scale * y * (g - s)
+            float g[V][E], y[V][E];
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int col0 = (i * G + lg) * E;
+                float dv[E];
+                S::unpack(xr[i], dv);
+                S::unpack(yr[i], y[i]);
+                const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    g[i][e] = kept<E>(w, col0, e, a.thr) ? dv[e] * a.pscale : 0.0f;
+                    s = fmaf(g[i][e], y[i][e], s);
+                }
+            }
+            s = reduce_sum(s, buf);
+            const rsrc_t vdx = view(a.out, blk);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float dx[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) dx[e] = a.scale * (y[i][e] * (g[i][e] - s));
+                if constexpr (VEC) {
+                    buf_store_nt(S::pack(dx), vdx, vo[i]);
+                } else {
+                    store_elems<S>(a.out, r, m, (i * G + lg) * E, ok[i] && rok, dx);
+                }
+            }
+        }
+    }
+}
+
+template <int G, int V, bool VEC, bool BWD>
+static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
+    constexpr int ROWS = SmGeometry<G>::ROWS;
+    const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
+    const void* k = reinterpret_cast<const void*>(&softmax_kernel<St, G, V, VEC, BWD>);
+    const int64_t grid = persistent_grid(k, SmGeometry<G>::NT, nblk);
+    hipLaunchKernelGGL((softmax_kernel<St, G, V, VEC, BWD>), dim3((unsigned)grid),
+                       dim3(SmGeometry<G>::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <bool VEC, bool BWD>
+static hipError_t dispatch(const Path& p, const SmArgs& a, hipStream_t s) {
+#define MBROW_CASE(GG, VV) \
+    if (p.g == GG && p.v == VV) return launch_one<GG, VV, VEC, BWD>(a, s);
+#if MBROW_DT == 0
+    MBROW_SM_LAYOUTS_F32(MBROW_CASE)
+#else
+    MBROW_SM_LAYOUTS_16(MBROW_CASE)
+#endif
+#undef MBROW_CASE
+    return hipErrorInvalidValue;
+}
+
+#define MBROW_CAT2(a, b) a##b
+#define MBROW_CAT(a, b) MBROW_CAT2(a, b)
+hipError_t MBROW_CAT(launch_softmax_, MBROW_SUFFIX)(const Path& p, bool backward,
+                                                    const SmArgs& a, hipStream_t s) {
+    if (backward)
+        return p.vec ? dispatch<true, true>(p, a, s) : dispatch<false, true>(p, a, s);
+    return p.vec ? dispatch<true, false>(p, a, s) : dispatch<false, false>(p, a, s);
+}
+
+}  // namespace mbrow

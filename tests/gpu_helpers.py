@@ -119,6 +119,55 @@ def check_dropout_bwd(orc, dy, dz_extra, z, gamma, mean, rstd, p, seed, dres, dx
     return assert_reports(*reps)
 
 
+def softmax_refs(orc, x, mask, rows_per_mask, causal, scale):
+    """Oracle y of the stored scores and the size of the float32 terms behind
+    each y_j (|t_j| + |max t| + 1 in units of y_j: the exponent's rounding and
+    the exp, sum and divide), for the arithmetic clause."""
+    rows, cols = x.shape
+    x64 = f64(x)
+    m64 = None if mask is None else f64(mask).reshape(-1, cols)
+    y_ref = orc.attn_softmax_fwd(x64, scale=scale, mask=m64, rows_per_mask=rows_per_mask,
+                                 causal=causal)
+    t = np.float64(np.float32(scale)) * x64
+    if m64 is not None:
+        t = t + np.repeat(m64, rows_per_mask, axis=0)[:rows]
+    finite = np.where(np.isfinite(t), t, 0.0)
+    mx = np.max(np.where(y_ref > 0, finite, -np.inf), axis=1, keepdims=True)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    y_scale = y_ref * (1.0 + np.abs(finite) + np.abs(mx))
+    return y_ref, y_scale
+
+
+def check_softmax_fwd(orc, x, y, y_dropped, fmt, scale=1.0, mask=None, rows_per_mask=1,
+                      causal=False, p=0.0, seed=0, name="softmax"):
+    rows, cols = x.shape
+    y_ref, y_scale = softmax_refs(orc, x, mask, rows_per_mask, causal, scale)
+    reps = [cmp.check_elementwise(f"{name}.y", f64(y), y_ref, fmt, term_scale=y_scale,
+                                  row_len=cols)]
+    if y_dropped is not None:
+        keep = orc.dropout_keep(seed, p, rows, cols)
+        s = 1.0 / (1.0 - np.float64(np.float32(p)))
+        reps.append(cmp.check_elementwise(f"{name}.y_dropped", f64(y_dropped),
+                                          np.where(keep == 1, y_ref * s, 0.0), fmt,
+                                          term_scale=y_scale * s * keep, row_len=cols))
+        yd = f64(y_dropped)
+        assert np.all(yd[keep == 0] == 0.0), f"{name}: dropped positions not zero"
+    return assert_reports(*reps)
+
+
+def check_softmax_bwd(orc, dy, y, dx, fmt, scale=1.0, p=0.0, seed=0, name="softmax_bwd"):
+    """Reference dx from the stored dy and the GPU's stored y."""
+    rows, cols = y.shape
+    dy64, y64 = f64(dy), f64(y)
+    keep = orc.dropout_keep(seed, p, rows, cols) if p > 0 else None
+    dx_ref = orc.attn_softmax_bwd(dy64, y64, keep=keep, p=p, scale=scale)
+    s = 1.0 / (1.0 - np.float64(np.float32(p)))
+    g = dy64 * s if keep is None else np.where(keep == 1, dy64 * s, 0.0)
+    term = abs(scale) * y64 * (np.abs(g) + np.sum(np.abs(g * y64), axis=1, keepdims=True))
+    return assert_reports(cmp.check_elementwise(f"{name}.dx", f64(dx), dx_ref, fmt,
+                                                term_scale=term, row_len=cols))
+
+
 def run_fwd_bwd(rows, cols, dtype, seed=0, x_mean=0.0, x_std=1.0):
     inp = dev(synth.layer_inputs(rows, cols, dtype, seed=seed, x_mean=x_mean, x_std=x_std,
                                  names=("x", "gamma", "beta", "dy")))

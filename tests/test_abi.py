@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(L):
     names = _declared_functions()
     assert {"ln_fwd", "bias_dropout_residual_ln_fwd", "ln_bwd_dx", "ln_bwd_dgamma_dbeta",
             "ln_bwd_workspace_bytes", "ln_status_string", "bias_dropout_residual_ln_bwd",
-            "bias_dropout_residual_ln_bwd_workspace_bytes"} <= set(names)
+            "bias_dropout_residual_ln_bwd_workspace_bytes", "attn_softmax_fwd",
+            "attn_softmax_bwd"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -205,3 +206,38 @@ def test_dropout_bwd_validation(L):
     assert drop_bwd(L, dbias=H) == LN_ERR_UNSUPPORTED             # dbias over dgamma
     assert drop_bwd(L, ws=B) == LN_ERR_UNSUPPORTED                # workspace over z
     assert drop_bwd(L, rows=0, dx=M, ez=M) == LN_OK               # in place on dz_extra
+
+
+def sm_fwd(L, x=A, mask=None, rpm=1, y=B, yd=None, rows=4, cols=8, scale=1.0, causal=0, p=0.0,
+           seed=0, dt=BF16):
+    return L.attn_softmax_fwd(x, mask, rpm, y, yd, rows, cols, scale, causal, p, seed, dt, None)
+
+
+def sm_bwd(L, dy=A, y=B, dx=C, rows=4, cols=8, scale=1.0, causal=0, p=0.0, seed=0, dt=BF16):
+    return L.attn_softmax_bwd(dy, y, dx, rows, cols, scale, causal, p, seed, dt, None)
+
+
+def test_softmax_validation(L):
+    assert sm_fwd(L, x=None) == LN_ERR_NULL
+    assert sm_fwd(L, y=None) == LN_ERR_NULL
+    assert sm_fwd(L, rows=0) == LN_OK                             # mask, y_dropped nullable
+    assert sm_fwd(L, rows=-1) == LN_ERR_SHAPE
+    assert sm_fwd(L, cols=0) == LN_ERR_SHAPE
+    assert sm_fwd(L, dt=4) == LN_ERR_DTYPE
+    assert sm_fwd(L, cols=16385) == LN_ERR_UNSUPPORTED
+    for kw in ({"scale": float("inf")}, {"scale": float("nan")}, {"causal": 2},
+               {"p": 1.0}, {"p": -0.5}, {"mask": C, "rpm": 0}):
+        assert sm_fwd(L, **kw) == LN_ERR_PARAM, kw
+    assert sm_fwd(L, rows=0, y=A) == LN_OK                        # in place
+    assert sm_fwd(L, yd=B) == LN_ERR_UNSUPPORTED                  # y_dropped over y
+    assert sm_fwd(L, y=A + 2) == LN_ERR_UNSUPPORTED
+    assert sm_fwd(L, mask=C, rpm=2, y=C) == LN_ERR_UNSUPPORTED    # y over the mask
+    for k in ("dy", "y", "dx"):
+        assert sm_bwd(L, **{k: None}) == LN_ERR_NULL, k
+    assert sm_bwd(L, rows=0, dx=A) == LN_OK
+    assert sm_bwd(L, rows=0, dx=B) == LN_OK
+    assert sm_bwd(L, dx=B + 4) == LN_ERR_UNSUPPORTED
+    assert sm_bwd(L, scale=float("inf")) == LN_ERR_PARAM
+    assert sm_bwd(L, p=1.0) == LN_ERR_PARAM
+    assert sm_bwd(L, cols=16385) == LN_ERR_UNSUPPORTED
+

@@ -1,0 +1,144 @@
+"""GPU parity of the attention softmax forward (scale, additive and causal
+masks, dropout output) and of its backward fused with the dropout backward,
+against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_amd as mb
+from memory_bound_row_amd import synth
+from gpu_helpers import FMT, case, check_softmax_bwd, check_softmax_fwd, dev
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [torch.float32, torch.float16, torch.bfloat16]
+SM_LAYOUTS_F32 = [(16, 1), (16, 2), (16, 4), (32, 2), (32, 4), (64, 2), (64, 4), (64, 8),
+                  (128, 4), (256, 4), (512, 4), (1024, 4)]
+SM_LAYOUTS_16 = [(16, 1), (16, 2), (32, 1), (32, 2), (64, 1), (64, 2), (64, 4), (128, 4),
+                 (256, 4), (512, 4)]
+
+
+def scores(rows, cols, dtype, seed=0, std=3.0):
+    """Attention scores ~ N(0, std) and an upstream gradient ~ N(0, 1)."""
+    d = synth.layer_inputs(rows, cols, dtype, seed=seed, x_std=std, names=("x", "dy"))
+    return dev(d)
+
+
+def run(rows, cols, dtype, scale, causal, p, seed, mask=None, rows_per_mask=1, data_seed=0):
+    d = scores(rows, cols, dtype, data_seed)
+    y, yd = mb.attn_softmax_fwd(d["x"], scale, mask=mask, rows_per_mask=rows_per_mask,
+                                causal=causal, p=p, seed=seed, want_dropped=p > 0)
+    dx = mb.attn_softmax_bwd(d["dy"], y, scale, causal=causal, p=p, seed=seed)
+    torch.cuda.synchronize()
+    return d, y, yd, dx
+
+
+def check(orc, d, y, yd, dx, scale, causal, p, seed, mask=None, rows_per_mask=1, name="sm"):
+    fmt = FMT[y.dtype]
+    check_softmax_fwd(orc, d["x"], y, yd, fmt, scale=scale, mask=mask,
+                      rows_per_mask=rows_per_mask, causal=causal, p=p, seed=seed,
+                      name=f"{name}.fwd")
+    check_softmax_bwd(orc, d["dy"], y, dx, fmt, scale=scale, p=p, seed=seed,
+                      name=f"{name}.bwd")
+
+
+@pytest.mark.parametrize("shape", [(2 * 16 * 256, 256), (8 * 16 * 512, 512)])
+def test_pages_attention_shapes(orc, shape):
+    """Batch 2 x 16 heads x 256 x 256 with the causal mask, and 8 x 16 x 512 x
+    512 with dropout, fp16 (the pages' examples)."""
+    rows, cols = shape
+    causal, p = (True, 0.0) if cols == 256 else (False, 0.1)
+    case(f"softmax {rows}x{cols} fp16 causal={causal} p={p}")
+    scale = 1.0 / np.sqrt(64.0)
+    d, y, yd, dx = run(rows, cols, torch.float16, scale, causal, p, 3)
+    check(orc, d, y, yd, dx, scale, causal, p, 3, name=f"sm.{rows}x{cols}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("cols", [1, 7, 8, 31, 32, 33, 100, 256, 1000, 1024, 4096, 8200,
+                                  16384])
+def test_widths(orc, dtype, cols):
+    rows = 96 if cols <= 4096 else 12
+    case(f"softmax {rows}x{cols} {dtype}")
+    d, y, yd, dx = run(rows, cols, dtype, 0.5, False, 0.2, 9, data_seed=cols)
+    check(orc, d, y, yd, dx, 0.5, False, 0.2, 9, name=f"sm.{cols}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("cols", [8, 64, 100, 512, 1024])
+def test_causal(orc, dtype, cols):
+    rows = 2 * cols + 3                      # two score blocks and part of a third
+    case(f"softmax causal {rows}x{cols} {dtype}")
+    d, y, yd, dx = run(rows, cols, dtype, 1.0, True, 0.1, 5, data_seed=7)
+    check(orc, d, y, yd, dx, 1.0, True, 0.1, 5, name=f"sm.causal.{cols}")
+    q = torch.arange(rows, device="cuda") % cols
+    j = torch.arange(cols, device="cuda")
+    assert torch.all(y[j[None, :] > q[:, None]] == 0)
+    assert torch.all(dx[j[None, :] > q[:, None]] == 0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_additive_mask(orc, dtype):
+    rows, cols, rpm = 128, 200, 32
+    case(f"softmax additive mask {rows}x{cols} {dtype}")
+    mk = torch.zeros((rows // rpm, cols), dtype=torch.float32)
+    mk[0, 10:50] = -torch.inf                # padded keys of the first batch
+    mk[1, :] = 2.0                           # a constant shift changes nothing
+    mk[2, 190:] = -torch.inf
+    mk[3, :] = -torch.inf                    # every key masked: zeros
+    mask = mk.to(dtype).cuda()
+    d, y, yd, dx = run(rows, cols, dtype, 0.8, False, 0.15, 2, mask=mask, rows_per_mask=rpm)
+    check(orc, d, y, yd, dx, 0.8, False, 0.15, 2, mask=mask, rows_per_mask=rpm,
+          name="sm.mask")
+    assert torch.all(y[:32, 10:50] == 0) and torch.all(y[96:] == 0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_forced_layouts(orc, dtype):
+    layouts = SM_LAYOUTS_F32 if dtype == torch.float32 else SM_LAYOUTS_16
+    e = 4 if dtype == torch.float32 else 8
+    try:
+        for g, v in layouts:
+            cols = g * v * e - e
+            if cols <= 0:
+                continue
+            case(f"softmax forced {g}x{v} cols={cols} {dtype}")
+            mb.debug_force_path(g, v)
+            d, y, yd, dx = run(40, cols, dtype, 1.0, cols >= 64, 0.3, 4)
+            check(orc, d, y, yd, dx, 1.0, cols >= 64, 0.3, 4, name=f"sm.{g}x{v}")
+    finally:
+        mb.debug_force_path(0)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_per_element_path(orc, dtype):
+    case(f"softmax per-element path {dtype}")
+    try:
+        mb.debug_force_path(0, 0, scalar=True)
+        d, y, yd, dx = run(64, 333, dtype, 0.5, True, 0.1, 8)
+        check(orc, d, y, yd, dx, 0.5, True, 0.1, 8, name="sm.scalar")
+    finally:
+        mb.debug_force_path(0)
+
+
+def test_rows_sum_to_one_and_p_zero():
+    case("softmax row sums, p = 0")
+    d, y, yd, dx = run(1000, 777, torch.float32, 1.0, False, 0.0, 0)
+    assert torch.allclose(y.double().sum(dim=1), torch.ones(1000, dtype=torch.float64,
+                                                            device="cuda"), atol=1e-5)
+    y2, yd2 = mb.attn_softmax_fwd(d["x"], 1.0, p=0.0, want_dropped=True)
+    torch.cuda.synchronize()
+    assert torch.equal(yd2, y2) and torch.equal(y2, y)
+    # each row of dx sums to 0 (softmax ignores a constant added to its input)
+    assert torch.allclose(dx.double().sum(dim=1), torch.zeros(1000, dtype=torch.float64,
+                                                              device="cuda"), atol=1e-5)
+
+
+def test_in_place():
+    case("softmax in place")
+    d, y, yd, dx = run(300, 512, torch.bfloat16, 0.5, True, 0.1, 6)
+    x2, dy2 = d["x"].clone(), d["dy"].clone()
+    y2, _ = mb.attn_softmax_fwd(x2, 0.5, causal=True, p=0.1, seed=6, y=x2)
+    dx2 = mb.attn_softmax_bwd(dy2, y2, 0.5, causal=True, p=0.1, seed=6, dx=dy2)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y) and torch.equal(dx2, dx)
