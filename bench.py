@@ -230,6 +230,8 @@ def configs_report(cpp_launch: bool = True) -> None:
         Python loop through the binding, and a HIP graph of the calls;
       * the fused backward of the whole layer (bias_dropout_residual_ln_bwd)
         at 8192x1280 bf16, alone and after the fused forward;
+      * the attention softmax forward and backward at 8x16x512x512 (dropout)
+        and 2x16x256x256 (causal), fp16;
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
@@ -396,6 +398,58 @@ def configs_report(cpp_launch: bool = True) -> None:
           "pct_of_hbm_peak": round(100.0 * lb / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)})
     del st, wsd
     torch.cuda.empty_cache()
+
+    # attention softmax at the pages' shapes (fp16): batch 8 x 16 heads x
+    # 512 x 512 with attention dropout p = 0.1, and 2 x 16 x 256 x 256 causal
+    def softmax_case(rows, L, causal, p, label):
+        dt = torch.float16
+        d = synth.layer_inputs(rows, L, dt, seed=SEED, x_std=3.0, names=("x", "dy"))
+        sets = []
+        for _ in range(2):
+            a = {"x": d["x"].to(dev), "dy": d["dy"].to(dev)}
+            a["y"] = torch.empty_like(a["x"])
+            a["yd"] = torch.empty_like(a["x"]) if p > 0 else None
+            a["dx"] = torch.empty_like(a["x"])
+            sets.append(a)
+        del d
+        scale = 0.125
+
+        def f(i):
+            a = sets[i % 2]
+            mb.attn_softmax_fwd(a["x"], scale, causal=causal, p=p, seed=SEED, y=a["y"],
+                                y_dropped=a["yd"])
+
+        def b(i):
+            a = sets[(i + 1) % 2]
+            mb.attn_softmax_bwd(a["dy"], a["y"], scale, causal=causal, p=p, seed=SEED,
+                                dx=a["dx"])
+
+        for i in range(2):
+            f(i)
+        torch.cuda.synchronize()
+        n = 50
+        msf = timed(capture(f, n), n)
+        msb = timed(capture(b, n), n)
+        t = rows * L * 2
+        read = t * (L + 1) / (2 * L) if causal else t     # scores past the query are not read
+        fb = read + t * (2 if p > 0 else 1)
+        bb = 2 * read + t
+        emit({"workload": label, "rows": rows, "cols": L, "storage": "float16",
+              "causal": causal, "p": p,
+              "fwd_bytes": int(fb), "fwd_us": round(msf * 1e3, 3),
+              "fwd_GBps": round(fb / (msf * 1e-3) / 1e9, 1),
+              "fwd_pct_of_hbm_peak": round(100.0 * fb / (msf * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+              "bwd_bytes": int(bb), "bwd_us": round(msb * 1e3, 3),
+              "bwd_GBps": round(bb / (msb * 1e-3) / 1e9, 1),
+              "bwd_pct_of_hbm_peak": round(100.0 * bb / (msb * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                           2)})
+        del sets
+        torch.cuda.empty_cache()
+
+    softmax_case(8 * 16 * 512, 512, False, 0.1,
+                 "attention softmax fwd (y and dropped y) + bwd (with dropout), 8x16x512x512")
+    softmax_case(2 * 16 * 256, 256, True, 0.0,
+                 "attention softmax fwd + bwd, causal, 2x16x256x256")
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")
