@@ -391,3 +391,41 @@ void orc_attn_softmax_bwd(const double* dy, const double* y, const uint8_t* keep
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* RMSNorm ([FP] §6: fused add + RMSNorm).                                   */
+/* ------------------------------------------------------------------------ */
+
+void orc_rmsnorm_fwd(const double* x, const double* gamma, int64_t rows, int64_t m,
+                     double eps, double* y, double* rstd) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * m;
+        double ss = 0.0;
+        for (int64_t j = 0; j < m; ++j) ss += xr[j] * xr[j];
+        double rs = 1.0 / sqrt(ss / (double)m + eps);
+        rstd[r] = rs;
+        for (int64_t j = 0; j < m; ++j) y[r * m + j] = gamma[j] * (xr[j] * rs);
+    }
+}
+
+void orc_rmsnorm_bwd(const double* dy, const double* x, const double* gamma,
+                     const double* rstd, int64_t rows, int64_t m, double* dx,
+                     double* dgamma, double* sgamma) {
+    for (int64_t j = 0; j < m; ++j) {
+        dgamma[j] = 0.0;
+        if (sgamma) sgamma[j] = 0.0;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* dyr = dy + r * m;
+        const double* xr = x + r * m;
+        double rs = rstd[r];
+        double b = 0.0;
+        for (int64_t j = 0; j < m; ++j) b += gamma[j] * dyr[j] * (xr[j] * rs);
+        for (int64_t j = 0; j < m; ++j) {
+            double xhat = xr[j] * rs;
+            dx[r * m + j] = rs * (gamma[j] * dyr[j] - xhat * b / (double)m);
+            dgamma[j] += dyr[j] * xhat;
+            if (sgamma) sgamma[j] += fabs(dyr[j] * xhat);
+        }
+    }
+}
+

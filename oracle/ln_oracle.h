@@ -142,6 +142,21 @@ void orc_ln_bwd_params(const double* dy, const double* x, const double* mean,
                        double* dgamma, double* dbeta,
                        double* sgamma, double* sbeta);
 
+/* RMSNorm ([FP] §6, "fused add + RMSNorm": one sum of squares, no mean):
+ *   rstd = 1 / sqrt((1/m) sum_j x_j^2 + eps);  y_j = gamma_j * x_j * rstd.
+ * The fused kernel adds the residual first and normalises the stored sum;
+ * that add is done by the caller here. */
+void orc_rmsnorm_fwd(const double* x, const double* gamma, int64_t rows, int64_t m,
+                     double eps, double* y, double* rstd);
+
+/* RMSNorm backward, the chain rule of the above with xhat = x * rstd and
+ * g = gamma * dy:  dx_j = rstd * (g_j - xhat_j * (sum_k g_k xhat_k) / m);
+ * dgamma_j = sum over rows of dy * xhat (row order), sgamma_j = sum of
+ * |dy * xhat| (may be NULL).  rstd is the saved float32 value. */
+void orc_rmsnorm_bwd(const double* dy, const double* x, const double* gamma,
+                     const double* rstd, int64_t rows, int64_t m, double* dx,
+                     double* dgamma, double* sgamma);
+
 /* Attention softmax forward ([L10] §4.1: per row, scale, add the mask, the
  * row maximum, exp of the difference, the row sum, divide), one row at a
  * time in double:

@@ -63,6 +63,8 @@ def _load():
         getattr(lib, name).argtypes = [dp, dp, dp, dp, dp, i64, i64, dp]
     lib.orc_ln_bwd_params.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, dp, dp]
     lib.orc_dropout_residual_bwd.argtypes = [dp, u8p, ctypes.c_float, i64, i64, dp, dp, dp]
+    lib.orc_rmsnorm_fwd.argtypes = [dp, dp, i64, i64, ctypes.c_double, dp, dp]
+    lib.orc_rmsnorm_bwd.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, dp]
     lib.orc_attn_softmax_fwd.argtypes = [dp, dp, i64, i64, i64, ctypes.c_double, ctypes.c_int,
                                          dp]
     lib.orc_attn_softmax_bwd.argtypes = [dp, dp, u8p, ctypes.c_float, i64, i64, ctypes.c_double,
@@ -258,8 +260,31 @@ def attn_softmax_bwd(dy, y, keep=None, p: float = 0.0, scale: float = 1.0) -> np
     return dx
 
 
+
+def rmsnorm_fwd(x, gamma, eps: float):
+    """RMSNorm: (y, rstd) with rstd = 1/sqrt(mean(x^2) + eps)."""
+    x = _d(x)
+    rows, m = _shape2(x)
+    g = _d(gamma)
+    y = np.empty_like(x)
+    rs = np.empty(rows)
+    _load().orc_rmsnorm_fwd(_ptr(x), _ptr(g), rows, m, float(np.float32(eps)), _ptr(y), _ptr(rs))
+    return y, rs
+
+
+def rmsnorm_bwd(dy, x, gamma, rstd):
+    """(dx, dgamma, sgamma) of RMSNorm given the saved rstd."""
+    dy, x, g, rs = _d(dy), _d(x), _d(gamma), _d(rstd)
+    rows, m = _shape2(x)
+    dx = np.empty_like(x)
+    dg, sg = np.empty(m), np.empty(m)
+    _load().orc_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(g), _ptr(rs), rows, m, _ptr(dx), _ptr(dg),
+                            _ptr(sg))
+    return dx, dg, sg
+
+
 __all__ = ["F32", "F16", "BF16", "build", "round_to", "round_scalar", "ln_fwd",
            "row_stats_welford", "var_naive_f32", "var_chan_f32", "philox4x32_10",
            "dropout_threshold", "dropout_keep", "bias_dropout_residual",
            "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params", "dropout_residual_bwd",
-           "attn_softmax_fwd", "attn_softmax_bwd"]
+           "attn_softmax_fwd", "attn_softmax_bwd", "rmsnorm_fwd", "rmsnorm_bwd"]

@@ -15,6 +15,9 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def orc():
     import oracle
-    oracle.build(force=not os.path.exists(
-        os.path.join(ROOT, "oracle", "liboracle_ln.so")))
+    lib = os.path.join(ROOT, "oracle", "liboracle_ln.so")
+    srcs = [os.path.join(ROOT, "oracle", f) for f in ("ln_oracle.c", "ln_oracle.h")]
+    stale = not os.path.exists(lib) or any(
+        os.path.getmtime(s) > os.path.getmtime(lib) for s in srcs)
+    oracle.build(force=stale)
     return oracle

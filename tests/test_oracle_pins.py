@@ -547,3 +547,63 @@ def test_softmax_backward_finite_differences(orc, m):
     # each row of dx sums to 0 (softmax ignores a constant added to its input)
     assert np.allclose(np.sum(dx, axis=1), 0.0, atol=1e-14)
 
+
+# --------------------------------------------------------------------------
+# RMSNorm: "GPU Performance from First Principles" §6 (fused add + RMSNorm:
+# one sum of squares, no mean)
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_is_layernorm_of_the_centred_row(orc):
+    # LayerNorm(x) with beta = 0 is RMSNorm(x - mean(x)): pins the RMSNorm
+    # oracle against the (separately pinned) LayerNorm oracle
+    rng = np.random.default_rng(31)
+    for m in (1, 3, 64, 1000):
+        x = _rows(rng, 6, m, mean=2.0, std=1.5)
+        gamma = rng.uniform(0.5, 1.5, m)
+        y_ln, mean, rstd_ln = orc.ln_fwd(x, gamma, np.zeros(m), 1e-5)
+        y_rms, rstd_rms = orc.rmsnorm_fwd(x - mean[:, None], gamma, 1e-5)
+        assert np.allclose(y_rms, y_ln, rtol=1e-12, atol=1e-12), m
+        assert np.allclose(rstd_rms, rstd_ln, rtol=1e-12), m
+
+
+def test_rmsnorm_closed_form(orc):
+    rng = np.random.default_rng(32)
+    x = _rows(rng, 5, 300, std=4.0)
+    eps = 1e-5
+    y, rstd = orc.rmsnorm_fwd(x, np.ones(300), eps)
+    ms = np.mean(x * x, axis=1)
+    e32 = float(np.float32(eps))
+    assert np.allclose(np.mean(y * y, axis=1), ms / (ms + e32), rtol=1e-13)
+    assert np.allclose(rstd, 1.0 / np.sqrt(ms + e32), rtol=1e-14)
+
+
+def _rms_loss(orc, x, gamma, dy, eps):
+    y, _ = orc.rmsnorm_fwd(x, gamma, eps)
+    return float(np.sum(dy * y))
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+def test_rmsnorm_backward_finite_differences(orc, m):
+    rng = np.random.default_rng(500 + m)
+    rows, eps = 3, 1e-5
+    x, dy = _rows(rng, rows, m, std=1.5), _rows(rng, rows, m)
+    gamma = rng.uniform(0.5, 1.5, m)
+    _, rstd = orc.rmsnorm_fwd(x, gamma, eps)
+    dx, dg, sg = orc.rmsnorm_bwd(dy, x, gamma, rstd)
+    scale = max(1.0, np.max(np.abs(dx)))
+    for r in range(rows):
+        for j in range(m):
+            h = 1e-6 * max(1.0, abs(x[r, j]))
+            xp, xm = x.copy(), x.copy()
+            xp[r, j] += h
+            xm[r, j] -= h
+            fd = (_rms_loss(orc, xp, gamma, dy, eps) - _rms_loss(orc, xm, gamma, dy, eps)) / (2 * h)
+            assert abs(fd - dx[r, j]) <= 1e-7 * scale, (r, j, fd, dx[r, j])
+    for j in range(m):                       # the loss is linear in gamma
+        gp, gm = gamma.copy(), gamma.copy()
+        gp[j] += 0.5
+        gm[j] -= 0.5
+        fd = _rms_loss(orc, x, gp, dy, eps) - _rms_loss(orc, x, gm, dy, eps)
+        assert abs(fd - dg[j]) <= 1e-12 * max(1.0, abs(dg[j])), j
+    assert np.all(sg >= np.abs(dg))
+
