@@ -8,6 +8,8 @@
  *          (CMU 11-868 lecture-11 notes)
  *   [BLOG] "AI infra 学习记录(2): 从 LayerNorm 算子熟悉常见的算子优化方法"
  *   [LLMC] "02 · llmc/ 的 CUDA kernel 层" (llm.c CUDA kernel walk-through)
+ *   [FP]   "GPU Performance from First Principles" (CS349D prerequisite
+ *          lecture P1)
  *
  * Common conventions for every entry point
  * ----------------------------------------
@@ -256,6 +258,63 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
 ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
                              int64_t cols, float scale, int causal, float p, uint64_t seed,
                              ln_dtype_t dt, hipStream_t stream);
+
+/*
+ * Fused residual add + RMSNorm forward ([FP] §6.1: the residual add and the
+ * next RMSNorm as one kernel that reads x and the residual and writes the new
+ * residual stream and the normalised h).  For each row r with m = cols:
+ *   z_j  = x_j + residual_j, rounded to T (residual NULL: z = x, nothing
+ *          written to residual_out);
+ *   rstd = 1 / sqrt(sum_j z_j^2 / m + eps), on the rounded z, in float32
+ *          ([FP] §7.5: the sum of squares is float32 because squares of
+ *          activation outliers of a few hundred overflow fp16);
+ *   y_j  = z_j * rstd * gamma_j.
+ *   x, residual    [rows, cols] T inputs (residual may be NULL).
+ *   gamma          [cols] T.
+ *   residual_out   [rows, cols] T output z; required with a residual, must be
+ *                  NULL without one (LN_ERR_PARAM); may equal x or residual.
+ *   y              [rows, cols] T output; may equal x or residual, not
+ *                  residual_out.
+ *   rstd           [rows] float32 output, or NULL (inference).
+ * eps >= 0 and finite, else LN_ERR_PARAM.
+ */
+ln_status_t add_rmsnorm_fwd(const void* x, const void* residual, const void* gamma,
+                            void* residual_out, void* y, float* rstd, int64_t rows, int64_t cols,
+                            float eps, ln_dtype_t dt, hipStream_t stream);
+
+/*
+ * Bytes of float32 workspace add_rmsnorm_bwd needs: P * cols * 4 (dgamma
+ * partials per partition), with the same P as ln_bwd_workspace_bytes.
+ * Returns 0 for rows <= 0 or cols <= 0.
+ */
+size_t add_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Backward of add_rmsnorm_fwd.  With g = gamma * dy and xhat = z * rstd
+ * (RMSNorm is the LayerNorm of [L11] §2.1 with the mean fixed at 0, so the
+ * sum of g drops out):
+ *   dz_j     = rstd * (g_j - xhat_j * sum_k g_k xhat_k / m) + dz_extra_j,
+ *              one row sum per row, formed in float32 and rounded to T once;
+ *              it is the gradient of both x and residual of the forward;
+ *   dgamma_j = sum over rows of dy * xhat, float32, by the deterministic
+ *              two-stage reduction of ln_bwd_dgamma_dbeta ([L11] §2.4).
+ *   dy        [rows, cols] T: gradient of y.
+ *   dz_extra  [rows, cols] T or NULL: gradient reaching z from its other
+ *             uses (the residual stream); NULL adds nothing.
+ *   z         [rows, cols] T: residual_out of the forward (x without a
+ *             residual).
+ *   gamma [cols] T;  rstd [rows] float32 as saved by the forward.
+ *   dz        [rows, cols] T output; may equal exactly one of dy, dz_extra
+ *             or z (in place).
+ *   dgamma    [cols] float32 output.
+ *   workspace float32 device buffer of at least
+ *             add_rmsnorm_bwd_workspace_bytes(rows, cols).
+ * Errors as for the other calls.
+ */
+ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
+                            const void* gamma, const float* rstd, void* dz, float* dgamma,
+                            float* workspace, size_t workspace_bytes, int64_t rows, int64_t cols,
+                            ln_dtype_t dt, hipStream_t stream);
 
 /* Static English description of a status code (never NULL). */
 const char* ln_status_string(ln_status_t status);

@@ -59,6 +59,13 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_uint64, i32, vp]
     L.attn_softmax_bwd.restype = i32
     L.attn_softmax_bwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, f32, ctypes.c_uint64, i32, vp]
+    L.add_rmsnorm_fwd.restype = i32
+    L.add_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    L.add_rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.add_rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
+    L.add_rmsnorm_bwd.restype = i32
+    L.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
+                                  i32, vp]
     L.ln_debug_force_path.restype = i32
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
     L.ln_debug_force_grid.restype = i32
@@ -304,6 +311,71 @@ def attn_softmax_bwd(dy, y, scale: float = 1.0, *, causal: bool = False, p: floa
                                   1 if causal else 0, float(p),
                                   int(seed) & 0xFFFFFFFFFFFFFFFF, _dt(y), _stream(y)))
     return dx
+
+
+def add_rmsnorm_fwd(x, gamma, eps: float = 1e-6, *, residual=None, residual_out=None,
+                    y=None, rstd=None, stats: bool = True):
+    """z = x + residual (x alone without one); y = RMSNorm(z) -> (z, y, rstd).
+
+    Without a residual z is x itself (nothing is written); rstd is None when
+    `stats` is false."""
+    rows, cols = _mat(x, "x")
+    if residual is not None:
+        if residual.shape != x.shape or residual.dtype != x.dtype:
+            raise ValueError("residual must match x")
+        _mat(residual, "residual")
+        residual_out = _out(residual_out, x.shape, x.dtype, x.device, "residual_out")
+    elif residual_out is not None:
+        raise ValueError("residual_out needs a residual")
+    _vec(gamma, cols, x.dtype, "gamma")
+    y = _out(y, x.shape, x.dtype, x.device, "y")
+    if stats:
+        rstd = _out(rstd, (rows,), torch.float32, x.device, "rstd")
+    z = residual_out if residual is not None else x
+    if rows == 0:
+        return z, y, rstd
+    _check(lib().add_rmsnorm_fwd(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(residual_out),
+                                 _ptr(y), _ptr(rstd), rows, cols, float(eps), _dt(x),
+                                 _stream(x)))
+    return z, y, rstd
+
+
+def add_rmsnorm_bwd_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().add_rmsnorm_bwd_workspace_bytes(int(rows), int(cols)))
+
+
+def rmsnorm_workspace(rows: int, cols: int, device) -> torch.Tensor:
+    """A float32 workspace of the size add_rmsnorm_bwd needs."""
+    n = add_rmsnorm_bwd_workspace_bytes(rows, cols) // 4
+    return torch.empty(max(n, 1), dtype=torch.float32, device=device)
+
+
+def add_rmsnorm_bwd(dy, z, gamma, rstd, *, dz_extra=None, dz=None, dgamma=None,
+                    workspace=None):
+    """Backward of add_rmsnorm_fwd -> (dz, dgamma).
+
+    dz = RMSNorm dx (from dy) + dz_extra is the gradient of both x and the
+    residual; dgamma (float32) = column sums of dy * z * rstd."""
+    rows, cols = _mat(z, "z")
+    for t, n in ((dy, "dy"), (dz_extra, "dz_extra")):
+        if t is not None and (t.shape != z.shape or t.dtype != z.dtype):
+            raise ValueError(f"{n} must match z")
+        if t is not None:
+            _mat(t, n)
+    _vec(gamma, cols, z.dtype, "gamma")
+    _vec(rstd, rows, torch.float32, "rstd")
+    dz = _out(dz, z.shape, z.dtype, z.device, "dz")
+    dgamma = _out(dgamma, (cols,), torch.float32, z.device, "dgamma")
+    if workspace is None:
+        workspace = rmsnorm_workspace(rows, cols, z.device)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda:
+        raise ValueError("workspace must be a float32 GPU tensor")
+    if rows == 0:
+        return dz, dgamma.zero_()
+    _check(lib().add_rmsnorm_bwd(_ptr(dy), _ptr(dz_extra), _ptr(z), _ptr(gamma), _ptr(rstd),
+                                 _ptr(dz), _ptr(dgamma), _ptr(workspace), workspace.numel() * 4,
+                                 rows, cols, _dt(z), _stream(z)))
+    return dz, dgamma
 
 
 def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,

@@ -24,6 +24,17 @@ hipError_t launch_bwd_bf16(const Path&, BwdMode, const BwdArgs&, hipStream_t);
 hipError_t launch_softmax_f32(const Path&, bool, const SmArgs&, hipStream_t);
 hipError_t launch_softmax_f16(const Path&, bool, const SmArgs&, hipStream_t);
 hipError_t launch_softmax_bf16(const Path&, bool, const SmArgs&, hipStream_t);
+hipError_t launch_rmsnorm_fwd_f32(const Path&, const RmsArgs&, hipStream_t);
+hipError_t launch_rmsnorm_fwd_f16(const Path&, const RmsArgs&, hipStream_t);
+hipError_t launch_rmsnorm_fwd_bf16(const Path&, const RmsArgs&, hipStream_t);
+
+hipError_t launch_rmsnorm_fwd(Dt dt, const Path& p, const RmsArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_rmsnorm_fwd_f32(p, a, s);
+    case Dt::F16: return launch_rmsnorm_fwd_f16(p, a, s);
+    default: return launch_rmsnorm_fwd_bf16(p, a, s);
+    }
+}
 
 hipError_t launch_softmax(Dt dt, const Path& p, bool backward, const SmArgs& a, hipStream_t s) {
     switch (dt) {
@@ -286,6 +297,11 @@ size_t bias_dropout_residual_ln_bwd_workspace_bytes(int64_t rows, int64_t cols) 
     return (size_t)bwd_partitions(rows, cols) * 3u * (size_t)cols * sizeof(float);
 }
 
+size_t add_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)bwd_partitions(rows, cols) * (size_t)cols * sizeof(float);
+}
+
 ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
                    float* rstd, int64_t rows, int64_t cols, float eps, ln_dtype_t dt,
                    hipStream_t stream) {
@@ -478,6 +494,74 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
     out.p[1] = dbeta;
     out.p[2] = dbias;
     return from_hip(launch_fold(workspace, a.parts, cols, 3, out, stream));
+}
+
+ln_status_t add_rmsnorm_fwd(const void* x, const void* residual, const void* gamma,
+                            void* residual_out, void* y, float* rstd, int64_t rows, int64_t cols,
+                            float eps, ln_dtype_t dt, hipStream_t stream) {
+    if (!x || !gamma || !y || (residual && !residual_out)) return LN_ERR_NULL;
+    if (!residual && residual_out) return LN_ERR_PARAM;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    if (!(eps >= 0.0f) || std::isinf(eps)) return LN_ERR_PARAM;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float);
+    const Span outs[] = {{residual_out, residual_out ? tb : 0, true}, {y, tb, true},
+                         {rstd, sb, false}};
+    const Span ins[] = {{x, tb, true}, {residual, residual ? tb : 0, true}, {gamma, vb, false}};
+    st = check_aliasing(outs, 3, ins, 3);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(x) && (!residual || aligned16(residual)) && aligned16(gamma) &&
+                     (!residual_out || aligned16(residual_out)) && aligned16(y) &&
+                     (cols * (int64_t)es) % 16 == 0;
+    RmsArgs a{};
+    a.x = x; a.residual = residual; a.gamma = gamma; a.residual_out = residual_out; a.y = y;
+    a.rstd = rstd;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.eps = eps;
+    a.inv_m = (float)(1.0 / (double)cols);
+    return from_hip(launch_rmsnorm_fwd(d, pick_path(d, cols, vec), a, stream));
+}
+
+ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
+                            const void* gamma, const float* rstd, void* dz, float* dgamma,
+                            float* workspace, size_t workspace_bytes, int64_t rows, int64_t cols,
+                            ln_dtype_t dt, hipStream_t stream) {
+    if (!dy || !z || !gamma || !rstd || !dz || !dgamma || !workspace) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    const size_t need = add_rmsnorm_bwd_workspace_bytes(rows, cols);
+    if (workspace_bytes < need) return LN_ERR_WORKSPACE;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float), cb = (size_t)cols * sizeof(float);
+    const Span outs[] = {{dz, tb, true}, {dgamma, cb, false}, {workspace, need, false}};
+    const Span ins[] = {{dy, tb, true}, {dz_extra, dz_extra ? tb : 0, true}, {z, tb, true},
+                        {gamma, vb, false}, {rstd, sb, false}};
+    st = check_aliasing(outs, 3, ins, 5);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(dy) && (!dz_extra || aligned16(dz_extra)) && aligned16(z) &&
+                     aligned16(gamma) && aligned16(dz) && (cols * (int64_t)es) % 16 == 0;
+    BwdArgs a{};
+    a.dy = dy; a.x = z; a.gamma = gamma; a.rstd = rstd; a.dx = dz; a.dz_extra = dz_extra;
+    a.ws = workspace;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.parts = bwd_partitions(rows, cols);
+    a.inv_m = (float)(1.0 / (double)cols);
+    st = from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::RMS, a, stream));
+    if (st != LN_OK) return st;
+    FoldOut out{};
+    out.p[0] = dgamma;
+    return from_hip(launch_fold(workspace, a.parts, cols, 1, out, stream));
 }
 
 ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,

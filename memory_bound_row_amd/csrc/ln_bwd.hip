@@ -17,6 +17,11 @@
 // small kernel adds the P partials in a fixed order.  No floating-point
 // atomics anywhere, so every run gives the same bits.
 //
+// RMSNorm ("GPU Performance from First Principles" §6): the same kernel with
+// the mean fixed at 0 and no sum of g -- xhat = x*rstd, B = sum g*xhat,
+// dx = rstd*(g - xhat*B/m) -- one column partial (dgamma), and the gradient
+// reaching the normalised input from its other uses added to dx.
+//
 // Schedule.  One row block at a time per workgroup, its loads issued
 // together at the top of the iteration; all P workgroups are resident, so
 // the memory system sees P blocks in flight.  (Measured: prefetching the
@@ -65,7 +70,9 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     constexpr bool DX = MODE != (int)BwdMode::PARTIALS;
     constexpr bool PART = MODE != (int)BwdMode::DX;
     constexpr bool DROP = MODE == (int)BwdMode::DROPOUT;   // prologue backward too
-    constexpr int NK = DROP ? 3 : 2;                        // kinds of column partials
+    constexpr bool RMS = MODE == (int)BwdMode::RMS;         // mean 0, no sum of g
+    constexpr bool EXTRA = DROP || RMS;                     // dz_extra may be given
+    constexpr int NK = DROP ? 3 : (RMS ? 1 : 2);            // kinds of column partials
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int lg = tid % G;
@@ -105,16 +112,16 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     };
 
     // Column accumulators: one per value of the lane's slots and kind
-    // (dgamma, dbeta, and dbias in the prologue mode).
+    // (dgamma, then dbeta, then dbias in the prologue mode; dgamma alone for
+    // RMSNorm).
     constexpr int KA = PART ? V * E : 1;
     float acc[NK][KA];
 #pragma unroll
-    for (int k = 0; k < KA; ++k) acc[0][k] = acc[1][k] = 0.0f;
-    if constexpr (DROP) {
+    for (int kind = 0; kind < NK; ++kind) {
 #pragma unroll
-        for (int k = 0; k < KA; ++k) acc[NK - 1][k] = 0.0f;
+        for (int k = 0; k < KA; ++k) acc[kind][k] = 0.0f;
     }
-    const bool has_extra = DROP && a.dz_extra != nullptr;   // uniform
+    const bool has_extra = EXTRA && a.dz_extra != nullptr;   // uniform
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
     // One block at a time: its loads, the block unpacked once, pass 1 (the
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         const int64_t row = base + grp;
         const bool rok = row < a.rows;
         const int64_t r = rok ? row : 0;   // rows past the end read row 0's statistics
-        u32x4 xr[V], dr[V], er[DROP ? V : 1];
+        u32x4 xr[V], dr[V], er[EXTRA ? V : 1];
         if constexpr (VEC) {
             // rows past the end read 0 and are never stored
             const rsrc_t vd = view(a.dy, base);
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 dr[i] = buf_load_nt(vd, vo[i]);
                 xr[i] = buf_load_nt(vx, vo[i]);
             }
-            if constexpr (DROP) {
+            if constexpr (EXTRA) {
                 if (has_extra) {
                     const rsrc_t ve = view(a.dz_extra, base);
 #pragma unroll
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 dr[i] = S::pack(f);
                 load_elems<S>(a.x, r, m, (i * G + lg) * E, ok[i] && rok, f);
                 xr[i] = S::pack(f);
-                if constexpr (DROP) {
+                if constexpr (EXTRA) {
                     if (has_extra) {
                         load_elems<S>(a.dz_extra, r, m, (i * G + lg) * E, ok[i] && rok, f);
                         er[i] = S::pack(f);
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 }
             }
         }
-        const float mu = a.mean[r], rs = a.rstd[r];
+        const float mu = RMS ? 0.0f : a.mean[r], rs = a.rstd[r];
         // (the per-element path and multi-wave rows of the prologue backward
         // have no registers to spare for gamma unpacked across blocks)
         if constexpr (DX && (!VEC || (DROP && G > 64))) keep_packed(gp);
@@ -174,8 +181,10 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             for (int i = 0; i < V; ++i) {
                 S::unpack(xr[i], xm_[i]);
                 S::unpack(dr[i], d_[i]);
+                if constexpr (!RMS) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) xm_[i][e] = xm_[i][e] - mu;
+                    for (int e = 0; e < E; ++e) xm_[i][e] = xm_[i][e] - mu;
+                }
             }
         }
         // x - mean and dy of slot i
@@ -189,13 +198,16 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             } else {
                 S::unpack(xr[i], xm);
                 S::unpack(dr[i], d);
+                if constexpr (!RMS) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) xm[e] = xm[e] - mu;
+                    for (int e = 0; e < E; ++e) xm[e] = xm[e] - mu;
+                }
             }
         };
         float c1 = 0.0f, c2 = 0.0f;
         if constexpr (DX) {
             // A = sum g, B = sum g * xhat = rstd * sum g * (x - mean)
+            // (RMSNorm: A unused)
             float A = 0.0f, Bm = 0.0f;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float g = ga[e] * d[e];   // zero outside the row
-                    A += g;
+                    if constexpr (!RMS) A += g;
                     Bm = fmaf(g, xm[e], Bm);
                 }
             }
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             // dx = rstd * (g - (A + xhat * B) / m) = rstd * (g - (c1 + xhat * c2));
             // g - (...) cancels exactly where it should (a one-column row
             // gets dx = 0)
-            c1 = A * a.inv_m;
+            c1 = RMS ? 0.0f : A * a.inv_m;
             c2 = (Bm * rs) * a.inv_m;
         }
         // Pass 2, slot by slot: dx (when formed) and the column partials.
@@ -258,16 +270,18 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     out[e] = rs * (ga[e] * d[e] - fmaf(xh[e], c2, c1));
-                if constexpr (DROP) {
-                    // dz = the LayerNorm's dx + the gradient from z's other
-                    // uses; dresidual = dz; dx of the prologue = keep * dz /
-                    // (1 - p) with the forward's mask regenerated; dbias sums it
+                // dz = the norm's dx + the gradient from z's other uses
+                if constexpr (EXTRA) {
                     if (has_extra) {
                         float ez[E];
                         S::unpack(er[i], ez);
 #pragma unroll
                         for (int e = 0; e < E; ++e) out[e] = out[e] + ez[e];
                     }
+                }
+                if constexpr (DROP) {
+                    // dresidual = dz; dx of the prologue = keep * dz / (1 - p)
+                    // with the forward's mask regenerated; dbias sums it
                     const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
                     float din[E];
 #pragma unroll
@@ -291,7 +305,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     acc[0][i * E + e] = fmaf(d[e], xh[e], acc[0][i * E + e]);
-                    acc[1][i * E + e] = acc[1][i * E + e] + d[e];
+                    if constexpr (!RMS) acc[1][i * E + e] = acc[1][i * E + e] + d[e];
                 }
             }
         }
@@ -411,7 +425,8 @@ static hipError_t dispatch_mode(const Path& p, BwdMode mode, const BwdArgs& a, h
     case BwdMode::DX: return dispatch<VEC, 0>(p, a, s);
     case BwdMode::DX_PARTIALS: return dispatch<VEC, 1>(p, a, s);
     case BwdMode::PARTIALS: return dispatch<VEC, 2>(p, a, s);
-    default: return dispatch<VEC, 3>(p, a, s);
+    case BwdMode::DROPOUT: return dispatch<VEC, 3>(p, a, s);
+    default: return dispatch<VEC, 4>(p, a, s);
     }
 }
 

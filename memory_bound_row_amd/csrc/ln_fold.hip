@@ -1,6 +1,6 @@
 // ln_fold.hip -- stage 2 of the dgamma/dbeta(/dbias) column reduction for
-// gfx950: add the P per-partition partials [P][K][m] (K = 2 or 3) in a fixed
-// order
+// gfx950: add the P per-partition partials [P][K][m] (K = 1, 2 or 3) in a
+// fixed order
 // ("Accelerating Transformer on GPU (II)" §2.4: a second small kernel adds
 // the P partial sums).
 //
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(FOLD_COLS* FOLD_SLICES) void ln_fold1_kernel(
 
 hipError_t launch_fold(const float* ws, int64_t parts, int64_t m, int kinds, FoldOut out,
                        hipStream_t s) {
-    if (parts > (int64_t)FOLD_SLICES * FOLD_MAX_PER_SLICE || kinds < 2 || kinds > 3)
+    if (parts > (int64_t)FOLD_SLICES * FOLD_MAX_PER_SLICE || kinds < 1 || kinds > 3)
         return hipErrorInvalidValue;
     const bool vec = (m % 4) == 0 && (reinterpret_cast<uintptr_t>(ws) & 15u) == 0;
     if (vec) {

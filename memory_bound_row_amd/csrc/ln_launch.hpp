@@ -77,8 +77,9 @@ struct BwdArgs {
 };
 
 // DROPOUT: dx of the LayerNorm plus the backward of the bias + dropout +
-// residual prologue, with partials of dgamma, dbeta and dbias.
-enum class BwdMode : int { DX = 0, DX_PARTIALS = 1, PARTIALS = 2, DROPOUT = 3 };
+// residual prologue, with partials of dgamma, dbeta and dbias.  RMS: dx of
+// RMSNorm (mean not read), plus dz_extra, with partials of dgamma.
+enum class BwdMode : int { DX = 0, DX_PARTIALS = 1, PARTIALS = 2, DROPOUT = 3, RMS = 4 };
 
 // Row layouts of the prologue backward: three column accumulators per value
 // leave room for fewer values per lane (multi-wave 16-bit rows take 2 slots
@@ -145,7 +146,23 @@ struct SmArgs {
 Path pick_softmax_path(Dt dt, int64_t cols, bool vec);
 hipError_t launch_softmax(Dt dt, const Path& p, bool backward, const SmArgs& a, hipStream_t s);
 
-// Fold of [P][kinds][m] partials (kinds = 2 or 3) into out[0..kinds-1].
+// Residual add + RMSNorm forward over rows of `m` values.
+struct RmsArgs {
+    const void* x;
+    const void* residual;   // NULL: plain RMSNorm of x
+    const void* gamma;
+    void* residual_out;     // z = x + residual (with a residual)
+    void* y;
+    float* rstd;            // or NULL
+    int64_t rows;
+    int64_t m;
+    int64_t nslots;
+    float eps;
+    float inv_m;
+};
+hipError_t launch_rmsnorm_fwd(Dt dt, const Path& p, const RmsArgs& a, hipStream_t s);
+
+// Fold of [P][kinds][m] partials (kinds = 1, 2 or 3) into out[0..kinds-1].
 struct FoldOut {
     float* p[3];
 };

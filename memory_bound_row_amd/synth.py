@@ -9,7 +9,10 @@ read the identical stored values.
 
 Default distributions (N(a, b) = mean a, standard deviation b):
 x ~ N(0, 1), residual ~ N(0, 1), bias ~ N(0, 0.02), gamma ~ U(0.5, 1.5),
-beta ~ N(0, 0.1), dy ~ N(0, 1).
+beta ~ N(0, 0.1), dy ~ N(0, 1).  With `outlier_frac` > 0, that fraction
+of the x entries (drawn after x from x's stream) is replaced by
++-`outlier_value`: the occasional activation outliers of a few hundred that
+large models carry.
 """
 from __future__ import annotations
 
@@ -31,12 +34,22 @@ def to_storage(a: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
 
 def layer_inputs(rows: int, cols: int, dtype: torch.dtype, seed: int = 0,
                  x_mean: float = 0.0, x_std: float = 1.0,
-                 names=NAMES) -> dict:
+                 names=NAMES, outlier_frac: float = 0.0,
+                 outlier_value: float = 300.0) -> dict:
     """Dict of CPU tensors in `dtype`: [rows, cols] x, residual, dy and
     [cols] bias, gamma, beta (only those listed in `names`)."""
     gens = _generators(seed)
+
+    def draw_x(g):
+        a = g.normal(x_mean, x_std, size=(rows, cols))
+        if outlier_frac > 0.0:
+            hit = g.random(size=(rows, cols)) < outlier_frac
+            sign = np.where(g.random(size=(rows, cols)) < 0.5, -1.0, 1.0)
+            a = np.where(hit, sign * outlier_value, a)
+        return a
+
     draw = {
-        "x": lambda g: g.normal(x_mean, x_std, size=(rows, cols)),
+        "x": draw_x,
         "residual": lambda g: g.normal(0.0, 1.0, size=(rows, cols)),
         "bias": lambda g: g.normal(0.0, 0.02, size=(cols,)),
         "gamma": lambda g: g.uniform(0.5, 1.5, size=(cols,)),

@@ -168,6 +168,47 @@ def check_softmax_bwd(orc, dy, y, dx, fmt, scale=1.0, p=0.0, seed=0, name="softm
                                                 term_scale=term, row_len=cols))
 
 
+def check_rmsnorm_fwd(orc, x, residual, gamma, z, y, rstd, fmt, eps, name="rms"):
+    """Reference z = x + residual (rounded once to T; the GPU adds in float32
+    and rounds, which for two T values stays within the rounding clause) and
+    the RMSNorm of z as stored.  y carries the float32 error of rstd (a sum of
+    m squares), so the arithmetic clause takes |y| as the size of its terms."""
+    rows, cols = x.shape[0], x.shape[-1]
+    reps = []
+    if residual is not None:
+        zero = np.zeros(cols)
+        keep = np.ones((rows, cols), dtype=np.uint8)
+        z_ref = orc.bias_dropout_residual(f64(x), zero, f64(residual), keep, 0.0)
+        reps.append(cmp.check_elementwise(f"{name}.z", f64(z), z_ref, fmt))
+    y_ref, rs_ref = orc.rmsnorm_fwd(f64(z).reshape(rows, cols), f64(gamma), eps)
+    reps.append(cmp.check_elementwise(f"{name}.y", f64(y).reshape(rows, cols), y_ref, fmt,
+                                      term_scale=np.abs(y_ref), row_len=cols))
+    if rstd is not None:
+        reps.append(cmp.check_stats(f"{name}.rstd", f64(rstd), rs_ref))
+    return assert_reports(*reps)
+
+
+def check_rmsnorm_bwd(orc, dy, dz_extra, z, gamma, rstd, dz, dgamma, fmt, name="rms_bwd"):
+    """Reference dz = RMSNorm dx (from the stored dy, z and fp32 rstd the GPU
+    read) + dz_extra, and dgamma.  The size of dx's float32 terms is
+    rstd * (|g| + |xhat| * sum|g * xhat| / m), g = gamma * dy, plus |dz_extra|."""
+    rows, cols = z.shape[0], z.shape[-1]
+    dy64, z64 = f64(dy).reshape(rows, cols), f64(z).reshape(rows, cols)
+    rs64, g64 = f64(rstd), f64(gamma)
+    ez64 = np.zeros_like(dy64) if dz_extra is None else f64(dz_extra).reshape(rows, cols)
+    dx_ref, dg_ref, sg = orc.rmsnorm_bwd(dy64, z64, g64, rs64)
+    g = g64 * dy64
+    xh = z64 * rs64[:, None]
+    scale = rs64[:, None] * (np.abs(g) + np.abs(xh) * np.sum(np.abs(g * xh), axis=1,
+                                                              keepdims=True) / cols)
+    reps = [
+        cmp.check_elementwise(f"{name}.dz", f64(dz).reshape(rows, cols), dx_ref + ez64, fmt,
+                              term_scale=scale + np.abs(ez64), row_len=cols),
+        cmp.check_colsum(f"{name}.dgamma", f64(dgamma), dg_ref, sg, rows, fmt),
+    ]
+    return assert_reports(*reps)
+
+
 def run_fwd_bwd(rows, cols, dtype, seed=0, x_mean=0.0, x_std=1.0):
     inp = dev(synth.layer_inputs(rows, cols, dtype, seed=seed, x_mean=x_mean, x_std=x_std,
                                  names=("x", "gamma", "beta", "dy")))

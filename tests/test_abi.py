@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(L):
     assert {"ln_fwd", "bias_dropout_residual_ln_fwd", "ln_bwd_dx", "ln_bwd_dgamma_dbeta",
             "ln_bwd_workspace_bytes", "ln_status_string", "bias_dropout_residual_ln_bwd",
             "bias_dropout_residual_ln_bwd_workspace_bytes", "attn_softmax_fwd",
-            "attn_softmax_bwd"} <= set(names)
+            "attn_softmax_bwd", "add_rmsnorm_fwd", "add_rmsnorm_bwd",
+            "add_rmsnorm_bwd_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -241,3 +242,53 @@ def test_softmax_validation(L):
     assert sm_bwd(L, p=1.0) == LN_ERR_PARAM
     assert sm_bwd(L, cols=16385) == LN_ERR_UNSUPPORTED
 
+
+
+def rms_fwd(L, x=A, res=B, g=C, z=D, y=E, rstd=None, rows=4, cols=8, eps=1e-6, dt=BF16):
+    return L.add_rmsnorm_fwd(x, res, g, z, y, rstd, rows, cols, eps, dt, None)
+
+
+def rms_bwd(L, dy=A, ez=None, z=B, g=C, rstd=D, dz=E, dg=F, ws=G, wsb=None, rows=4, cols=8,
+            dt=BF16):
+    if wsb is None:
+        wsb = L.add_rmsnorm_bwd_workspace_bytes(rows, cols)
+    return L.add_rmsnorm_bwd(dy, ez, z, g, rstd, dz, dg, ws, wsb, rows, cols, dt, None)
+
+
+def test_rmsnorm_workspace_bytes(L):
+    f = L.add_rmsnorm_bwd_workspace_bytes
+    assert f(0, 10) == 0 and f(10, 0) == 0 and f(-1, 10) == 0
+    # the same P partitions as the LayerNorm backward, one kind of partial
+    assert f(8192, 4096) == 256 * 4096 * 4
+    assert f(5, 7) * 2 == L.ln_bwd_workspace_bytes(5, 7)
+
+
+def test_rmsnorm_validation(L):
+    for k in ("x", "g", "y", "z"):
+        assert rms_fwd(L, **{k: None}) == LN_ERR_NULL, k      # z required with a residual
+    assert rms_fwd(L, res=None, z=None, rows=0) == LN_OK        # plain RMSNorm
+    assert rms_fwd(L, res=None) == LN_ERR_PARAM                 # z without a residual
+    assert rms_fwd(L, rows=0, rstd=F) == LN_OK
+    assert rms_fwd(L, rows=-1) == LN_ERR_SHAPE
+    assert rms_fwd(L, cols=0) == LN_ERR_SHAPE
+    assert rms_fwd(L, dt=3) == LN_ERR_DTYPE
+    assert rms_fwd(L, cols=16385) == LN_ERR_UNSUPPORTED
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert rms_fwd(L, eps=eps) == LN_ERR_PARAM, eps
+    assert rms_fwd(L, rows=0, z=B, y=A) == LN_OK                # in place on both inputs
+    assert rms_fwd(L, y=D) == LN_ERR_UNSUPPORTED                # y over z
+    assert rms_fwd(L, z=A + 2) == LN_ERR_UNSUPPORTED
+    assert rms_fwd(L, rstd=C) == LN_ERR_UNSUPPORTED             # rstd over gamma
+    for k in ("dy", "z", "g", "rstd", "dz", "dg", "ws"):
+        assert rms_bwd(L, **{k: None}) == LN_ERR_NULL, k
+    assert rms_bwd(L, rows=0) == LN_OK                          # dz_extra may be NULL
+    assert rms_bwd(L, rows=0, ez=M, dz=M) == LN_OK              # in place on dz_extra
+    assert rms_bwd(L, rows=0, dz=A) == LN_OK
+    assert rms_bwd(L, rows=-1) == LN_ERR_SHAPE
+    assert rms_bwd(L, dt=7) == LN_ERR_DTYPE
+    assert rms_bwd(L, cols=16385) == LN_ERR_UNSUPPORTED
+    need = L.add_rmsnorm_bwd_workspace_bytes(4, 8)
+    assert rms_bwd(L, wsb=need - 4) == LN_ERR_WORKSPACE
+    assert rms_bwd(L, dz=B + 2) == LN_ERR_UNSUPPORTED
+    assert rms_bwd(L, dg=D) == LN_ERR_UNSUPPORTED               # dgamma over rstd
+    assert rms_bwd(L, ws=F) == LN_ERR_UNSUPPORTED               # workspace over dgamma
