@@ -232,6 +232,9 @@ def configs_report(cpp_launch: bool = True) -> None:
         at 8192x1280 bf16, alone and after the fused forward;
       * the attention softmax forward and backward at 8x16x512x512 (dropout)
         and 2x16x256x256 (causal), fp16;
+      * fused residual add + RMSNorm forward and backward at 2048x4096 bf16
+        (one layer of a 2048-token Llama-3-8B prefill), rotated past the
+        cache, and the forward at 64x4096 (a decode step of 64 requests);
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
@@ -450,6 +453,62 @@ def configs_report(cpp_launch: bool = True) -> None:
                  "attention softmax fwd (y and dropped y) + bwd (with dropout), 8x16x512x512")
     softmax_case(2 * 16 * 256, 256, True, 0.0,
                  "attention softmax fwd + bwd, causal, 2x16x256x256")
+
+    # fused residual add + RMSNorm (bf16): forward reads x and the residual
+    # and writes z and y; backward reads dy, z and dz_extra and writes dz
+    def rmsnorm_case(rows, cols, sets, iters, label, bwd=True):
+        dt = torch.bfloat16
+        d = synth.layer_inputs(rows, cols, dt, seed=SEED, names=("x", "residual", "gamma", "dy"))
+        ez = synth.layer_inputs(rows, cols, dt, seed=SEED + 1, names=("dy",))["dy"]
+        gamma = d["gamma"].to(dev)
+        st = []
+        for _ in range(sets):
+            a = {k: d[k].to(dev) for k in ("x", "residual", "dy")}
+            a["ez"] = ez.to(dev)
+            for k in ("z", "y", "dz"):
+                a[k] = torch.empty((rows, cols), dtype=dt, device=dev)
+            a["rstd"] = torch.empty(rows, dtype=torch.float32, device=dev)
+            st.append(a)
+        del d, ez
+        ws = mb.rmsnorm_workspace(rows, cols, dev)
+        dg = torch.empty(cols, dtype=torch.float32, device=dev)
+
+        def f(i):
+            a = st[i % sets]
+            mb.add_rmsnorm_fwd(a["x"], gamma, 1e-6, residual=a["residual"], residual_out=a["z"],
+                               y=a["y"], rstd=a["rstd"])
+
+        def b(i):
+            a = st[(i + sets // 2) % sets]
+            mb.add_rmsnorm_bwd(a["dy"], a["z"], gamma, a["rstd"], dz_extra=a["ez"], dz=a["dz"],
+                               dgamma=dg, workspace=ws)
+
+        for i in range(sets):
+            f(i)
+        torch.cuda.synchronize()
+        t = rows * cols * 2
+        fb = 4 * t + cols * 2 + 4 * rows
+        msf = timed(capture(f, iters), iters)
+        rec = {"workload": label, "rows": rows, "cols": cols, "storage": "bfloat16",
+               "buffer_sets": sets, "iters": iters,
+               "fwd_bytes": fb, "fwd_us": round(msf * 1e3, 3),
+               "fwd_GBps": round(fb / (msf * 1e-3) / 1e9, 1),
+               "fwd_pct_of_hbm_peak": round(100.0 * fb / (msf * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+        if bwd:
+            bb = 4 * t + cols * 2 + 4 * rows + 4 * cols
+            msb = timed(capture(b, iters), iters)
+            rec.update({"bwd_bytes": bb, "bwd_us": round(msb * 1e3, 3),
+                        "bwd_GBps": round(bb / (msb * 1e-3) / 1e9, 1),
+                        "bwd_pct_of_hbm_peak": round(100.0 * bb / (msb * 1e-3) / 1e9
+                                                     / HBM_PEAK_GBPS, 2)})
+        emit(rec)
+        del st, ws
+        torch.cuda.empty_cache()
+
+    rmsnorm_case(2048, 4096, 4, 100,
+                 "fused residual add + RMSNorm fwd + bwd (dz_extra given), 2048x4096, rotated")
+    rmsnorm_case(64, 4096, 1, 1000, "fused residual add + RMSNorm forward, decode 64x4096",
+                 bwd=False)
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")
