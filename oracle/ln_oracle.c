@@ -429,3 +429,37 @@ void orc_rmsnorm_bwd(const double* dy, const double* x, const double* gamma,
     }
 }
 
+
+/* ------------------------------------------------------------------------ */
+/* Cross-entropy with label smoothing ([L10] §5.2; [LLMC] §6.1).            */
+/* ------------------------------------------------------------------------ */
+
+void orc_cross_entropy(const double* x, const int64_t* labels, int64_t rows, int64_t V,
+                       double alpha, double scale, double* loss, double* dx) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * V;
+        double* dr = dx ? dx + r * V : NULL;
+        const int64_t y = labels[r];
+        if (y < 0 || y >= V) {
+            const double v = y < 0 ? 0.0 : NAN;
+            loss[r] = v;
+            if (dr)
+                for (int64_t j = 0; j < V; ++j) dr[j] = v;
+            continue;
+        }
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < V; ++j)
+            if (xr[j] > mx) mx = xr[j];
+        double z = 0.0;
+        for (int64_t j = 0; j < V; ++j) z += exp(xr[j] - mx);
+        const double logz = log(z);
+        double l = 0.0;
+        for (int64_t j = 0; j < V; ++j) {
+            const double p = (j == y ? 1.0 - alpha : 0.0) + alpha / (double)V;
+            const double logq = (xr[j] - mx) - logz;
+            l -= p * logq;
+            if (dr) dr[j] = scale * (exp(logq) - p);
+        }
+        loss[r] = l;
+    }
+}

@@ -176,6 +176,18 @@ void orc_attn_softmax_fwd(const double* x, const double* mask, int64_t rows_per_
 void orc_attn_softmax_bwd(const double* dy, const double* y, const uint8_t* keep, float p,
                           int64_t rows, int64_t m, double scale, double* dx);
 
+/* Cross-entropy of a row of logits against a class label, with label
+ * smoothing, and its gradient, by the definitions ([L10] §5.2; [LLMC] §6.1
+ * for the fusion of loss and gradient over a vocabulary-wide row):
+ *   q = softmax(x) (computed with the row maximum subtracted),
+ *   p_j = (1 - alpha) [j == label] + alpha / V,
+ *   loss = -sum_j p_j log q_j,   dx_j = scale * (q_j - p_j).
+ * A negative label marks an ignored row: loss 0 and dx 0.  A label >= V has
+ * no target distribution: loss and dx are NaN.  x is [rows, V]; loss is
+ * [rows]; dx [rows, V] may be NULL. */
+void orc_cross_entropy(const double* x, const int64_t* labels, int64_t rows, int64_t V,
+                       double alpha, double scale, double* loss, double* dx);
+
 #ifdef __cplusplus
 }
 #endif

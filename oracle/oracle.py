@@ -65,6 +65,8 @@ def _load():
     lib.orc_dropout_residual_bwd.argtypes = [dp, u8p, ctypes.c_float, i64, i64, dp, dp, dp]
     lib.orc_rmsnorm_fwd.argtypes = [dp, dp, i64, i64, ctypes.c_double, dp, dp]
     lib.orc_rmsnorm_bwd.argtypes = [dp, dp, dp, dp, i64, i64, dp, dp, dp]
+    lib.orc_cross_entropy.argtypes = [dp, ctypes.POINTER(ctypes.c_int64), i64, i64,
+                                      ctypes.c_double, ctypes.c_double, dp, dp]
     lib.orc_attn_softmax_fwd.argtypes = [dp, dp, i64, i64, i64, ctypes.c_double, ctypes.c_int,
                                          dp]
     lib.orc_attn_softmax_bwd.argtypes = [dp, dp, u8p, ctypes.c_float, i64, i64, ctypes.c_double,
@@ -283,8 +285,27 @@ def rmsnorm_bwd(dy, x, gamma, rstd):
     return dx, dg, sg
 
 
+def cross_entropy(x, labels, alpha: float = 0.0, scale: float = 1.0, grad: bool = True):
+    """(loss [rows], dx [rows, V] or None) of label-smoothed cross-entropy.
+
+    alpha and scale are taken as the float32 values the GPU library receives;
+    a negative label is an ignored row (loss 0, dx 0)."""
+    x = _d(x)
+    rows, V = _shape2(x)
+    lab = np.ascontiguousarray(np.asarray(labels, dtype=np.int64))
+    if lab.shape != (rows,):
+        raise ValueError("labels must be [rows]")
+    loss = np.empty(rows)
+    dx = np.empty_like(x) if grad else None
+    _load().orc_cross_entropy(_ptr(x), lab.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                              rows, V, float(np.float32(alpha)), float(np.float32(scale)),
+                              _ptr(loss), None if dx is None else _ptr(dx))
+    return loss, dx
+
+
 __all__ = ["F32", "F16", "BF16", "build", "round_to", "round_scalar", "ln_fwd",
            "row_stats_welford", "var_naive_f32", "var_chan_f32", "philox4x32_10",
            "dropout_threshold", "dropout_keep", "bias_dropout_residual",
            "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params", "dropout_residual_bwd",
-           "attn_softmax_fwd", "attn_softmax_bwd", "rmsnorm_fwd", "rmsnorm_bwd"]
+           "attn_softmax_fwd", "attn_softmax_bwd", "rmsnorm_fwd", "rmsnorm_bwd",
+           "cross_entropy"]

@@ -607,3 +607,80 @@ def test_rmsnorm_backward_finite_differences(orc, m):
         assert abs(fd - dg[j]) <= 1e-12 * max(1.0, abs(dg[j])), j
     assert np.all(sg >= np.abs(dg))
 
+
+
+# --- cross-entropy with label smoothing ([L10] §5.2; [LLMC] §6.1) ----------
+
+def test_cross_entropy_matches_torch_label_smoothing(orc):
+    # the lecture notes state that their target p = (1 - a) y + a / V is the
+    # convention of torch's label_smoothing, and check the gradient q - p
+    # against autograd; both are library special cases here (float64, CPU)
+    import torch
+    rng = np.random.default_rng(41)
+    for V, alpha in ((2, 0.0), (7, 0.1), (300, 0.25), (1000, 0.0)):
+        x = rng.normal(0.0, 3.0, (9, V))
+        lab = rng.integers(0, V, 9)
+        lab[4] = -100                              # torch's ignore_index
+        scale = 0.375
+        loss, dx = orc.cross_entropy(x, lab, alpha, scale)
+        xt = torch.tensor(x, requires_grad=True)
+        lt = torch.nn.functional.cross_entropy(xt, torch.tensor(lab), reduction="none",
+                                               label_smoothing=float(np.float32(alpha)),
+                                               ignore_index=-100)
+        (lt * scale).sum().backward()
+        np.testing.assert_allclose(loss, lt.detach().numpy(), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-15)
+        assert loss[4] == 0.0 and np.all(dx[4] == 0.0)
+
+
+def test_cross_entropy_closed_form(orc):
+    # loss = log Z + m - [(1 - a) x_label + (a / V) sum x]  ([L10] §5.2)
+    rng = np.random.default_rng(42)
+    V, alpha = 513, 0.1
+    x = rng.normal(0.0, 2.0, (6, V))
+    lab = rng.integers(0, V, 6)
+    loss, _ = orc.cross_entropy(x, lab, alpha, 1.0, grad=False)
+    a = float(np.float32(alpha))
+    for r in range(6):
+        m = x[r].max()
+        logz = np.log(np.sum(np.exp(x[r] - m)))
+        ref = logz + m - ((1 - a) * x[r, lab[r]] + a / V * x[r].sum())
+        assert abs(loss[r] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_cross_entropy_special_rows(orc):
+    # uniform logits: q = 1/V, so loss = log V for any smoothing; the gradient
+    # sums to 0 over a row (sum q = sum p = 1) and is negative at the label
+    rng = np.random.default_rng(43)
+    for V in (1, 2, 50, 4096):
+        loss, dx = orc.cross_entropy(np.full((2, V), 3.5), [0, V - 1], 0.2, 1.0)
+        np.testing.assert_allclose(loss, np.log(V), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-14)
+    x = rng.normal(0.0, 1.0, (5, 333))
+    lab = np.array([0, 17, 332, 100, 5])
+    _, dx = orc.cross_entropy(x, lab, 0.05, 2.0)
+    np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-13)
+    assert np.all(dx[np.arange(5), lab] < 0)
+    # one-hot target: loss = -log q_label
+    loss, _ = orc.cross_entropy(x, lab, 0.0, 1.0, grad=False)
+    q = np.exp(x - x.max(axis=1, keepdims=True))
+    q /= q.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(loss, -np.log(q[np.arange(5), lab]), rtol=1e-13)
+    # a label outside the vocabulary has no target: NaN
+    loss, dx = orc.cross_entropy(x[:1], [333], 0.0, 1.0)
+    assert np.isnan(loss[0]) and np.all(np.isnan(dx))
+
+
+def test_cross_entropy_finite_differences(orc):
+    rng = np.random.default_rng(44)
+    V, alpha, h = 11, 0.3, 1e-6
+    x = rng.normal(0.0, 2.0, (1, V))
+    lab = [4]
+    _, dx = orc.cross_entropy(x, lab, alpha, 1.0)
+    for j in range(V):
+        xp, xm = x.copy(), x.copy()
+        xp[0, j] += h
+        xm[0, j] -= h
+        fd = (orc.cross_entropy(xp, lab, alpha, 1.0, grad=False)[0][0]
+              - orc.cross_entropy(xm, lab, alpha, 1.0, grad=False)[0][0]) / (2 * h)
+        assert abs(fd - dx[0, j]) < 1e-8, (j, fd, dx[0, j])
