@@ -77,6 +77,11 @@ typedef enum {
  * three column accumulators per value need the registers of twice as many
  * lanes). */
 #define LN_MAX_COLS_DROPOUT_BWD 8192
+/* Widest padded row (ld) of cross_entropy_fwd_bwd: 53248 fp32 or 57344
+ * fp16/bf16 classes (the row is held in the registers of one 1024-lane
+ * workgroup; GPT-2's 50257-entry vocabulary, padded to 50304, fits). */
+#define LN_MAX_COLS_XENT_F32 53248
+#define LN_MAX_COLS_XENT_16 57344
 
 /*
  * LayerNorm forward.  For each row r with m = cols:
@@ -315,6 +320,35 @@ ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
                             const void* gamma, const float* rstd, void* dz, float* dgamma,
                             float* workspace, size_t workspace_bytes, int64_t rows, int64_t cols,
                             ln_dtype_t dt, hipStream_t stream);
+
+/*
+ * Cross-entropy with label smoothing, forward and backward in one pass over
+ * each row of logits ([L10] §5.2: with q = softmax(x) and the smoothed target
+ * p_j = (1 - a)[j == label] + a/V, the loss is
+ * log Z + m - [(1 - a) x_label + (a/V) sum_j x_j] (m the row maximum,
+ * Z = sum_j exp(x_j - m)) and its gradient is q - p; [LLMC] §6.1: the row's
+ * maximum and exp-sum from one online softmax reduction, the probabilities
+ * never stored, the gradient written over the logits in the same kernel):
+ *   loss_r   = the label-smoothed cross-entropy of row r (float32);
+ *   dlogits  = grad_scale * (q - p), rounded to T.
+ *   logits   [rows, ld] T; columns [0, cols) are the V = cols classes,
+ *            columns [cols, ld) are padding and are never read.
+ *   labels   [rows] int64 class indices.  A negative label marks an ignored
+ *            row: loss 0, gradient 0.  A label >= cols has no target: loss
+ *            and the row's gradient are NaN.
+ *   loss     [rows] float32 output.
+ *   dlogits  [rows, ld] T output or NULL (loss only); may equal logits (in
+ *            place).  Its padding columns are written with 0.
+ *   label_smoothing a in [0, 1];  grad_scale finite (e.g. 1/rows for a mean
+ *            loss).
+ * ld >= cols, else LN_ERR_SHAPE; ld above LN_MAX_COLS_XENT_F32 (fp32) or
+ * LN_MAX_COLS_XENT_16 (fp16/bf16) is LN_ERR_UNSUPPORTED.  Arithmetic in
+ * float32 (exp by the device's exp2).
+ */
+ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, float* loss,
+                                  void* dlogits, int64_t rows, int64_t cols, int64_t ld,
+                                  float label_smoothing, float grad_scale, ln_dtype_t dt,
+                                  hipStream_t stream);
 
 /* Static English description of a status code (never NULL). */
 const char* ln_status_string(ln_status_t status);

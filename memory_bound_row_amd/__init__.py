@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.add_rmsnorm_bwd.restype = i32
     L.add_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                                   i32, vp]
+    L.cross_entropy_fwd_bwd.restype = i32
+    L.cross_entropy_fwd_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, f32, i32, vp]
     L.ln_debug_force_path.restype = i32
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
     L.ln_debug_force_grid.restype = i32
@@ -376,6 +378,31 @@ def add_rmsnorm_bwd(dy, z, gamma, rstd, *, dz_extra=None, dz=None, dgamma=None,
                                  _ptr(dz), _ptr(dgamma), _ptr(workspace), workspace.numel() * 4,
                                  rows, cols, _dt(z), _stream(z)))
     return dz, dgamma
+
+
+def cross_entropy_fwd_bwd(logits, labels, *, cols: int = None, label_smoothing: float = 0.0,
+                          grad_scale: float = 1.0, grad: bool = True, loss=None,
+                          dlogits=None):
+    """Label-smoothed cross-entropy of each row -> (loss float32 [rows], dlogits or None).
+
+    logits is [..., ld]; the first `cols` columns (all by default) are the
+    classes, the rest padding.  labels are int64 (negative: ignored row).
+    dlogits = grad_scale * (softmax - target); pass dlogits=logits to
+    overwrite the logits with it."""
+    rows, ld = _mat(logits, "logits")
+    cols = ld if cols is None else int(cols)
+    if (not labels.is_cuda or not labels.is_contiguous() or labels.dtype != torch.int64
+            or labels.numel() != rows):
+        raise ValueError(f"labels must be a contiguous GPU int64 tensor of {rows} values")
+    loss = _out(loss, (rows,), torch.float32, logits.device, "loss")
+    if grad or dlogits is not None:
+        dlogits = _out(dlogits, logits.shape, logits.dtype, logits.device, "dlogits")
+    if rows == 0:
+        return loss, dlogits
+    _check(lib().cross_entropy_fwd_bwd(_ptr(logits), _ptr(labels), _ptr(loss), _ptr(dlogits),
+                                       rows, cols, ld, float(label_smoothing),
+                                       float(grad_scale), _dt(logits), _stream(logits)))
+    return loss, dlogits
 
 
 def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,

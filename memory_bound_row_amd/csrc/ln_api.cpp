@@ -28,6 +28,18 @@ hipError_t launch_rmsnorm_fwd_f32(const Path&, const RmsArgs&, hipStream_t);
 hipError_t launch_rmsnorm_fwd_f16(const Path&, const RmsArgs&, hipStream_t);
 hipError_t launch_rmsnorm_fwd_bf16(const Path&, const RmsArgs&, hipStream_t);
 
+hipError_t launch_xent_f32(const Path&, const XeArgs&, hipStream_t);
+hipError_t launch_xent_f16(const Path&, const XeArgs&, hipStream_t);
+hipError_t launch_xent_bf16(const Path&, const XeArgs&, hipStream_t);
+
+hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_xent_f32(p, a, s);
+    case Dt::F16: return launch_xent_f16(p, a, s);
+    default: return launch_xent_bf16(p, a, s);
+    }
+}
+
 hipError_t launch_rmsnorm_fwd(Dt dt, const Path& p, const RmsArgs& a, hipStream_t s) {
     switch (dt) {
     case Dt::F32: return launch_rmsnorm_fwd_f32(p, a, s);
@@ -161,6 +173,19 @@ Path pick_softmax_path(Dt dt, int64_t cols, bool vec) {
     const int64_t ns = (cols + E - 1) / E;
     return E == 4 ? pick(true, ns, vec, kSm32, MBROW_N(kSm32), false, true)
                   : pick(false, ns, vec, kSm16, MBROW_N(kSm16), false, true);
+}
+
+static const int kXe32[][2] = {{16, 1}, {16, 2}, {16, 4}, {32, 2}, {32, 4}, {64, 2},
+                               {64, 4}, {64, 8}, {128, 4}, {256, 4}, {512, 4}, {1024, 4},
+                               {1024, 6}, {1024, 8}, {1024, 10}, {1024, 13}};
+static const int kXe16[][2] = {{16, 1}, {16, 2}, {32, 1}, {32, 2}, {64, 1}, {64, 2},
+                               {64, 4}, {128, 4}, {256, 4}, {512, 4}, {1024, 4}, {1024, 5},
+                               {1024, 6}, {1024, 7}};
+
+// `slots`: 16-byte slots of the padded row (ceil(ld / E)).
+Path pick_xent_path(Dt dt, int64_t slots, bool vec) {
+    return dt == Dt::F32 ? pick(true, slots, vec, kXe32, MBROW_N(kXe32), false, true)
+                         : pick(false, slots, vec, kXe16, MBROW_N(kXe16), false, true);
 }
 
 // The same choice with and without partials, so the fused and the
@@ -564,6 +589,40 @@ ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
     return from_hip(launch_fold(workspace, a.parts, cols, 1, out, stream));
 }
 
+ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, float* loss,
+                                  void* dlogits, int64_t rows, int64_t cols, int64_t ld,
+                                  float label_smoothing, float grad_scale, ln_dtype_t dt,
+                                  hipStream_t stream) {
+    if (!logits || !labels || !loss) return LN_ERR_NULL;
+    if (!valid_dtype(dt)) return LN_ERR_DTYPE;
+    if (rows < 0 || cols <= 0 || ld < cols) return LN_ERR_SHAPE;
+    const int64_t max_ld = dt == LN_F32 ? LN_MAX_COLS_XENT_F32 : LN_MAX_COLS_XENT_16;
+    if (ld > max_ld || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
+    if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f)) return LN_ERR_PARAM;
+    if (!std::isfinite(grad_scale)) return LN_ERR_PARAM;
+    if (rows == 0) return LN_OK;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)ld * es;
+    const Span outs[] = {{dlogits, dlogits ? tb : 0, true}, {loss, (size_t)rows * 4, false}};
+    const Span ins[] = {{logits, tb, true}, {labels, (size_t)rows * 8, false}};
+    ln_status_t st = check_aliasing(outs, 2, ins, 2);
+    if (st != LN_OK) return st;
+
+    const Dt d = static_cast<Dt>(dt);
+    const int E = elems_per_slot(d);
+    const bool vec = aligned16(logits) && (!dlogits || aligned16(dlogits)) &&
+                     (ld * (int64_t)es) % 16 == 0;
+    XeArgs a{};
+    a.x = logits; a.labels = labels; a.loss = loss; a.dx = dlogits;
+    a.rows = rows; a.cols = cols; a.ld = ld;
+    a.nvalid = (cols + E - 1) / E;
+    a.nslots = (ld + E - 1) / E;
+    a.alpha = label_smoothing;
+    a.inv_v = (float)(1.0 / (double)cols);
+    a.scale = grad_scale;
+    return from_hip(launch_xent(d, pick_xent_path(d, a.nslots, vec), a, stream));
+}
+
 ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
                              void* y_dropped, int64_t rows, int64_t cols, float scale,
                              int causal, float p, uint64_t seed, ln_dtype_t dt,
@@ -642,7 +701,8 @@ ln_status_t ln_debug_force_path(int lanes_per_row, int slots_per_lane, int scala
     const int g = lanes_per_row, v = slots_per_lane;
     if (g != 0 && !have_instance(true, g, v) && !have_instance(false, g, v) &&
         !in_list(kDrop32, MBROW_N(kDrop32), g, v) && !in_list(kDrop16, MBROW_N(kDrop16), g, v) &&
-        !in_list(kSm32, MBROW_N(kSm32), g, v) && !in_list(kSm16, MBROW_N(kSm16), g, v))
+        !in_list(kSm32, MBROW_N(kSm32), g, v) && !in_list(kSm16, MBROW_N(kSm16), g, v) &&
+        !in_list(kXe32, MBROW_N(kXe32), g, v) && !in_list(kXe16, MBROW_N(kXe16), g, v))
         return LN_ERR_UNSUPPORTED;
     g_force_g.store(lanes_per_row, std::memory_order_relaxed);
     g_force_v.store(lanes_per_row ? slots_per_lane : 0, std::memory_order_relaxed);

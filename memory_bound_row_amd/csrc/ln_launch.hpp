@@ -162,6 +162,38 @@ struct RmsArgs {
 };
 hipError_t launch_rmsnorm_fwd(Dt dt, const Path& p, const RmsArgs& a, hipStream_t s);
 
+// Cross-entropy with label smoothing over rows of `cols` classes stored with
+// a row stride of `ld` elements (columns [cols, ld) are padding).
+struct XeArgs {
+    const void* x;           // logits
+    const int64_t* labels;   // [rows]
+    float* loss;             // [rows]
+    void* dx;                // gradient, or NULL (loss only); may equal x
+    int64_t rows;
+    int64_t cols;
+    int64_t ld;
+    int64_t nvalid;          // ceil(cols / E): slots holding classes
+    int64_t nslots;          // ceil(ld / E): slots of the padded row
+    float alpha;             // label smoothing
+    float inv_v;             // 1 / cols
+    float scale;             // gradient scale
+};
+
+// Row layouts of the cross-entropy kernel: vocabulary-wide rows over up to
+// 1024 lanes.  The widest instances that fit in 128 registers per lane hold
+// 13 fp32 or 7 16-bit slots per lane: 53248 fp32 or 57344 16-bit classes.
+#define MBROW_XE_LAYOUTS_F32(X)                                             \
+    X(16, 1) X(16, 2) X(16, 4) X(32, 2) X(32, 4) X(64, 2) X(64, 4) X(64, 8) \
+    X(128, 4) X(256, 4) X(512, 4) X(1024, 4) X(1024, 6) X(1024, 8)         \
+    X(1024, 10) X(1024, 13)
+#define MBROW_XE_LAYOUTS_16(X)                                              \
+    X(16, 1) X(16, 2) X(32, 1) X(32, 2) X(64, 1) X(64, 2) X(64, 4)          \
+    X(128, 4) X(256, 4) X(512, 4) X(1024, 4) X(1024, 5) X(1024, 6)         \
+    X(1024, 7)
+
+Path pick_xent_path(Dt dt, int64_t slots, bool vec);
+hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s);
+
 // Fold of [P][kinds][m] partials (kinds = 1, 2 or 3) into out[0..kinds-1].
 struct FoldOut {
     float* p[3];

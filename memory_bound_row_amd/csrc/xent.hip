@@ -1,0 +1,275 @@
+// xent.hip -- fused cross-entropy forward and backward for gfx950 (label
+// smoothing, loss and gradient in one pass).  Compiled once per storage type
+// (-DMBROW_DT=0 fp32, 1 fp16, 2 bf16).
+//
+// "Accelerating Transformer on GPU (I)" §5.2: with q = softmax(x) and the
+// smoothed target p = (1 - a)[j == label] + a/V, the loss is
+// log Z + m - [(1 - a) x_label + (a/V) sum x] (m the row maximum,
+// Z = sum exp(x - m)) and its gradient is q - p, an elementwise difference,
+// so one kernel reduces the row and writes the gradient.  "02 · llmc/ 的 CUDA
+// kernel 层" §6.1: over a vocabulary-wide row the probabilities are never
+// stored; the row's max and sum come from one online softmax reduction and
+// the logits can be overwritten by the gradient in the same kernel.
+//
+// Here a row is held in registers across G lanes (up to 1024 lanes of one
+// workgroup: GPT-2's 50304-column padded vocabulary fits in fp32 and bf16),
+// so it is read from HBM once and written once.  Each lane reduces its own
+// values to (max, sum of exp(x - max), sum x), the lanes merge those states
+// in one butterfly (and one LDS exchange across the waves of a row), x at the
+// label is read directly, and the gradient pass re-reads the registers.
+// Columns in [V, ld) are padding: not used, and written as 0 in the gradient.
+#include "ln_device.hpp"
+#include "ln_launch.hpp"
+
+#ifndef MBROW_DT
+#error "compile with -DMBROW_DT=0|1|2"
+#endif
+
+namespace mbrow {
+
+#if MBROW_DT == 0
+using St = StF32;
+#define MBROW_SUFFIX f32
+#elif MBROW_DT == 1
+using St = StF16;
+#define MBROW_SUFFIX f16
+#else
+using St = StBF16;
+#define MBROW_SUFFIX bf16
+#endif
+
+template <int G>
+struct XeGeometry {
+    static constexpr int NT = G <= 256 ? 256 : G;   // threads per workgroup
+    static constexpr int ROWS = NT / G;              // rows per block
+    static constexpr int WPR = G > 64 ? G / 64 : 1;  // waves per row
+};
+
+// Online softmax state of a set of values: their maximum, the sum of
+// exp(x - max) and the sum of x.
+struct XeState {
+    float mx, z, sx;
+};
+
+// Merge of two states.  Every operation is commutative in (a, b), so both
+// partners of a butterfly step get the same bits.  A side with no values
+// (max -inf, sum 0) contributes 0 without forming exp(-inf + inf).
+__device__ inline XeState xe_merge(const XeState& a, const XeState& b) {
+    XeState r;
+    r.mx = fmaxf(a.mx, b.mx);
+    const float ta = a.mx == r.mx ? a.z : a.z * __expf(a.mx - r.mx);
+    const float tb = b.mx == r.mx ? b.z : b.z * __expf(b.mx - r.mx);
+    r.z = ta + tb;
+    r.sx = a.sx + b.sx;
+    return r;
+}
+
+template <int D>
+__device__ inline XeState xe_partner(const XeState& s) {
+    return XeState{partner<D>(s.mx), partner<D>(s.z), partner<D>(s.sx)};
+}
+
+// Merge over aligned groups of G lanes (G = 1..64), result in every lane.
+template <int G>
+__device__ inline XeState xe_group(XeState s) {
+    if constexpr (G >= 2) s = xe_merge(s, xe_partner<1>(s));
+    if constexpr (G >= 4) s = xe_merge(s, xe_partner<2>(s));
+    if constexpr (G >= 8) s = xe_merge(s, xe_partner<4>(s));
+    if constexpr (G >= 16) s = xe_merge(s, xe_partner<8>(s));
+    if constexpr (G >= 32) s = xe_merge(s, xe_partner<16>(s));
+    if constexpr (G >= 64) {
+        const XeState lo{lane_read(s.mx, 0), lane_read(s.z, 0), lane_read(s.sx, 0)};
+        const XeState hi{lane_read(s.mx, 32), lane_read(s.z, 32), lane_read(s.sx, 32)};
+        s = xe_merge(lo, hi);
+    }
+    return s;
+}
+
+// An integer the compiler must treat as changed: per-element comparisons
+// against it are formed where they are used instead of being hoisted out of
+// the row loop and held (one lane mask per element) across the passes.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <class S, int G, int V, bool VEC>
+__global__ __launch_bounds__(XeGeometry<G>::NT) void xent_kernel(XeArgs a) {
+    constexpr int E = S::E;
+    constexpr int ROWS = XeGeometry<G>::ROWS;
+    constexpr int WPR = XeGeometry<G>::WPR;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int lg = tid % G;
+    const int rloc = tid / G;
+    const int ld = (int)a.ld;
+    const int cols = (int)a.cols;
+    const int nv = (int)a.nvalid;    // slots holding at least one class
+    const int ns = (int)a.nslots;    // slots of the padded row
+    const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
+    const bool grad = a.dx != nullptr;   // uniform
+
+    // Slot i of this lane covers columns (i*G + lg)*E + e, e < E: column
+    // c(i, e) = base + i*G*E + e with base = lg*E, so "column < cols" is
+    // "i*G*E + e < cols - base" against a compile-time left side.
+    const int base = lg * E;
+    // vector path: byte offset of slot i in the wave's row view is
+    // rbase + i*G*16 (rbase: the lane's row within the wave and its first
+    // slot); slots past the classes are not read (kOob), slots past the
+    // padded row are not written
+    const uint32_t rbase = slot_offset<S, G>(tid, 0, ld, true);
+    auto slot_off = [&](uint32_t rb, int i, int nslot) {
+        return i * G + lg < nslot ? rb + (uint32_t)(i * G * 16) : kOob;
+    };
+    const int wrow = wave_first_row<G>(tid);
+    auto view = [&](const void* t, int64_t blk) {
+        const int64_t row0 = blk * ROWS + wrow;
+        const int64_t left = a.rows - row0;
+        return row_view<S>(t, row0, left < WaveRows<G>::N ? left : WaveRows<G>::N, ld);
+    };
+    __shared__ XeState red[2][ROWS][WPR];   // cross-wave exchange, double-buffered
+    const float inv_v = a.inv_v;
+    const float alpha = a.alpha;
+
+    int it = 0;
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x, ++it) {
+        const int64_t row = blk * ROWS + rloc;
+        const bool rok = row < a.rows;
+        const int64_t r = rok ? row : 0;
+        const int64_t off = r * (int64_t)ld;
+        const int64_t label = rok ? a.labels[row] : -1;
+        const bool ignored = label < 0;
+        const bool bad = label >= cols;
+        // x at the label, read directly (one element per row)
+        const float xl = (ignored || bad) ? 0.0f : S::load1(a.x, off + label);
+        u32x4 xr[V];
+        if constexpr (VEC) {
+            const rsrc_t vx = view(a.x, blk);
+            const uint32_t rb = (uint32_t)opaque((int)rbase);
+#pragma unroll
+            for (int i = 0; i < V; ++i) xr[i] = buf_load_nt(vx, slot_off(rb, i, nv));
+        } else {
+            const int lim = opaque(cols - base);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    f[e] = (rok && i * G * E + e < lim) ? S::load1(a.x, off + base + i * G * E + e)
+                                                         : 0.0f;
+                xr[i] = S::pack(f);
+            }
+        }
+        // this lane's state: max and sum of x, then the exp-sum against the max
+        XeState st{-INFINITY, 0.0f, 0.0f};
+        {
+            const int lim = opaque(cols - base);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                S::unpack(xr[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const bool in = i * G * E + e < lim;
+                    st.mx = fmaxf(st.mx, in ? f[e] : -INFINITY);
+                    st.sx += in ? f[e] : 0.0f;
+                }
+            }
+        }
+        keep_packed(xr);
+        {
+            const int lim = opaque(cols - base);
+            const float m0 = st.mx == -INFINITY ? 0.0f : st.mx;   // lanes past the row
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                S::unpack(xr[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    st.z += i * G * E + e < lim ? __expf(f[e] - m0) : 0.0f;
+            }
+        }
+        if constexpr (G <= 64) {
+            st = xe_group<G>(st);
+        } else {
+            st = xe_group<64>(st);
+            const int buf = it & 1;
+            if (lane == 0) red[buf][rloc][lg / 64] = st;
+            __syncthreads();
+            st = red[buf][rloc][0];
+#pragma unroll
+            for (int k = 1; k < WPR; ++k) st = xe_merge(st, red[buf][rloc][k]);
+        }
+        // loss = log Z + (1 - a)(m - x_label) + a (m - sum x / V)
+        if (lg == 0 && rok) {
+            const float l = logf(st.z) + (1.0f - alpha) * (st.mx - xl) +
+                            alpha * (st.mx - st.sx * inv_v);
+            a.loss[row] = ignored ? 0.0f : (bad ? NAN : l);
+        }
+        if (grad) {
+            // dx = scale * (q - p): q = exp(x - m) / Z, p = a/V + (1 - a)[j == label]
+            keep_packed(xr);
+            const float iz = 1.0f / st.z;
+            const float pa = alpha * inv_v;
+            const float fill = ignored ? 0.0f : NAN;   // rows without a target
+            const bool no_target = ignored || bad;
+            const int lim = opaque(cols - base);
+            const int rel = opaque((int)(ignored || bad ? -1 : label) - base);
+            const rsrc_t vd = view(a.dx, blk);
+            const uint32_t rb = (uint32_t)opaque((int)rbase);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E], out[E];
+                S::unpack(xr[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int c = i * G * E + e;
+                    const float q = __expf(f[e] - st.mx) * iz;
+                    const float p = c == rel ? pa + (1.0f - alpha) : pa;
+                    const float d = no_target ? fill : a.scale * (q - p);
+                    out[e] = c < lim ? d : 0.0f;   // padding columns get 0
+                }
+                if constexpr (VEC) {
+                    buf_store_nt(S::pack(out), vd, slot_off(rb, i, ns));
+                } else {
+                    const int wl = opaque(ld - base);
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (rok && i * G * E + e < wl) S::store1(a.dx, off + base + i * G * E + e, out[e]);
+                }
+            }
+        }
+    }
+}
+
+template <int G, int V, bool VEC>
+static hipError_t launch_one(const XeArgs& a, hipStream_t s) {
+    constexpr int ROWS = XeGeometry<G>::ROWS;
+    const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
+    const void* k = reinterpret_cast<const void*>(&xent_kernel<St, G, V, VEC>);
+    const int64_t grid = persistent_grid(k, XeGeometry<G>::NT, nblk);
+    hipLaunchKernelGGL((xent_kernel<St, G, V, VEC>), dim3((unsigned)grid),
+                       dim3(XeGeometry<G>::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <bool VEC>
+static hipError_t dispatch(const Path& p, const XeArgs& a, hipStream_t s) {
+#define MBROW_CASE(GG, VV) \
+    if (p.g == GG && p.v == VV) return launch_one<GG, VV, VEC>(a, s);
+#if MBROW_DT == 0
+    MBROW_XE_LAYOUTS_F32(MBROW_CASE)
+#else
+    MBROW_XE_LAYOUTS_16(MBROW_CASE)
+#endif
+#undef MBROW_CASE
+    return hipErrorInvalidValue;
+}
+
+#define MBROW_CAT2(a, b) a##b
+#define MBROW_CAT(a, b) MBROW_CAT2(a, b)
+hipError_t MBROW_CAT(launch_xent_, MBROW_SUFFIX)(const Path& p, const XeArgs& a, hipStream_t s) {
+    return p.vec ? dispatch<true>(p, a, s) : dispatch<false>(p, a, s);
+}
+
+}  // namespace mbrow

@@ -59,6 +59,27 @@ def layer_inputs(rows: int, cols: int, dtype: torch.dtype, seed: int = 0,
     return {n: to_storage(draw[n](gens[n]), dtype) for n in names}
 
 
+def class_labels(rows: int, classes: int, seed: int = 0, ignore_frac: float = 0.0,
+                 ignore_index: int = -100) -> torch.Tensor:
+    """[rows] int64 class indices, uniform over [0, classes), from their own
+    PCG64 stream; with `ignore_frac` > 0 that fraction of the rows (drawn
+    after the labels) is set to `ignore_index`."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 7919])))
+    lab = g.integers(0, classes, size=rows, dtype=np.int64)
+    if ignore_frac > 0.0:
+        lab = np.where(g.random(rows) < ignore_frac, np.int64(ignore_index), lab)
+    return torch.from_numpy(np.ascontiguousarray(lab))
+
+
+def logits(rows: int, ld: int, dtype: torch.dtype, seed: int = 0, mean: float = 0.0,
+           std: float = 2.0) -> torch.Tensor:
+    """[rows, ld] logits ~ N(mean, std) in `dtype` (CPU), from their own
+    PCG64 stream (columns past the classes, if any, hold values too: padding
+    a kernel must not use)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 104729])))
+    return to_storage(g.normal(mean, std, size=(rows, ld)), dtype)
+
+
 def as_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 numpy copy of a (CPU or GPU) tensor."""
     return t.detach().to("cpu", torch.float64).numpy()

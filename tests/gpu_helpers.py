@@ -209,6 +209,49 @@ def check_rmsnorm_bwd(orc, dy, dz_extra, z, gamma, rstd, dz, dgamma, fmt, name="
     return assert_reports(*reps)
 
 
+def check_xent(orc, logits, labels, cols, alpha, scale, loss, dx, fmt, rows_sel=None,
+               name="xent"):
+    """Reference loss and gradient of the stored logits (the first `cols`
+    columns of each row; rows_sel restricts the check to those rows).  The
+    kernel's float32 terms: the exp-sum over V values and the exp arguments
+    x - m (up to max|x - m|), the sums of x; so the loss is checked against
+    the arithmetic clause with S = 1 + |log Z| + |m - x_label| + a (|m| +
+    sum|x| / V) + max|x - m|, and q_j against q_j (1 + |x_j - m| + max|x - m|)
+    + p_j.  The gradient's padding columns must be exactly 0."""
+    x_all = f64(logits)
+    lab_all = labels.cpu().numpy()
+    rows_idx = np.arange(x_all.shape[0]) if rows_sel is None else np.asarray(rows_sel)
+    x64 = np.ascontiguousarray(x_all[rows_idx, :cols])
+    lab = lab_all[rows_idx]
+    loss_ref, dx_ref = orc.cross_entropy(x64, lab, alpha, scale, grad=dx is not None)
+    a = float(np.float32(alpha))
+    valid = (lab >= 0) & (lab < cols)
+    m = x64.max(axis=1)
+    spread = np.max(np.abs(x64 - m[:, None]), axis=1)
+    z = np.sum(np.exp(x64 - m[:, None]), axis=1)
+    xl = np.where(valid, x64[np.arange(len(lab)), np.clip(lab, 0, cols - 1)], 0.0)
+    s_loss = (1.0 + np.abs(np.log(z)) + np.abs(m - xl)
+              + a * (np.abs(m) + np.sum(np.abs(x64), axis=1) / cols) + spread)
+    s_loss = np.where(valid, s_loss, 0.0)
+    got_loss = f64(loss)[rows_idx]
+    reps = [cmp.check_elementwise(f"{name}.loss", got_loss, loss_ref, cmp.F32,
+                                  term_scale=s_loss, row_len=cols)]
+    if dx is not None:
+        q = np.exp(x64 - m[:, None]) / z[:, None]
+        p = np.full_like(q, a / cols)
+        p[np.arange(len(lab))[valid], lab[valid]] += 1.0 - a
+        term = abs(float(np.float32(scale))) * (
+            q * (1.0 + np.abs(x64 - m[:, None]) + spread[:, None]) + p)
+        term = np.where(valid[:, None], term, 0.0)
+        d_all = f64(dx)
+        reps.append(cmp.check_elementwise(f"{name}.dx", d_all[rows_idx, :cols], dx_ref, fmt,
+                                          term_scale=term, row_len=cols))
+        if d_all.shape[1] > cols:
+            pad = d_all[rows_idx, cols:]
+            assert np.all(pad == 0.0), f"{name}: nonzero gradient in padding columns"
+    return assert_reports(*reps)
+
+
 def run_fwd_bwd(rows, cols, dtype, seed=0, x_mean=0.0, x_std=1.0):
     inp = dev(synth.layer_inputs(rows, cols, dtype, seed=seed, x_mean=x_mean, x_std=x_std,
                                  names=("x", "gamma", "beta", "dy")))

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(L):
             "ln_bwd_workspace_bytes", "ln_status_string", "bias_dropout_residual_ln_bwd",
             "bias_dropout_residual_ln_bwd_workspace_bytes", "attn_softmax_fwd",
             "attn_softmax_bwd", "add_rmsnorm_fwd", "add_rmsnorm_bwd",
-            "add_rmsnorm_bwd_workspace_bytes"} <= set(names)
+            "add_rmsnorm_bwd_workspace_bytes", "cross_entropy_fwd_bwd"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -161,7 +161,8 @@ def test_debug_force_path_validation(L):
     assert L.ln_debug_force_path(128, 3, 0) == LN_ERR_UNSUPPORTED
     assert L.ln_debug_force_path(128, 2, 0) == LN_OK          # prologue-backward layout
     assert L.ln_debug_force_path(0, 0, 0) == LN_OK
-    assert L.ln_debug_force_path(1024, 8, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(1024, 9, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(1024, 13, 0) == LN_OK        # cross-entropy layout
     assert L.ln_debug_force_path(64, 3, 0) == LN_OK
     assert L.ln_debug_force_path(0, 0, 0) == LN_OK
 
@@ -292,3 +293,33 @@ def test_rmsnorm_validation(L):
     assert rms_bwd(L, dz=B + 2) == LN_ERR_UNSUPPORTED
     assert rms_bwd(L, dg=D) == LN_ERR_UNSUPPORTED               # dgamma over rstd
     assert rms_bwd(L, ws=F) == LN_ERR_UNSUPPORTED               # workspace over dgamma
+
+
+def xent(L, x=A, lab=B, loss=C, dx=None, rows=4, cols=8, ld=8, alpha=0.0, scale=1.0, dt=BF16):
+    return L.cross_entropy_fwd_bwd(x, lab, loss, dx, rows, cols, ld, alpha, scale, dt, None)
+
+
+def test_cross_entropy_validation(L):
+    for k in ("x", "lab", "loss"):
+        assert xent(L, **{k: None}) == LN_ERR_NULL, k
+    assert xent(L, rows=0) == LN_OK                             # dlogits may be NULL
+    assert xent(L, rows=0, dx=A) == LN_OK                       # in place on the logits
+    assert xent(L, rows=0, dx=D) == LN_OK
+    assert xent(L, rows=-1) == LN_ERR_SHAPE
+    assert xent(L, cols=0) == LN_ERR_SHAPE
+    assert xent(L, cols=9, ld=8) == LN_ERR_SHAPE                # ld < cols
+    assert xent(L, dt=3) == LN_ERR_DTYPE
+    assert xent(L, cols=53248, ld=53248, rows=0, dt=F32) == LN_OK
+    assert xent(L, cols=53249, ld=53249, dt=F32) == LN_ERR_UNSUPPORTED
+    assert xent(L, cols=100, ld=53249, dt=F32) == LN_ERR_UNSUPPORTED
+    for dt in (F16, BF16):
+        assert xent(L, cols=57344, ld=57344, rows=0, dt=dt) == LN_OK
+        assert xent(L, cols=57345, ld=57345, dt=dt) == LN_ERR_UNSUPPORTED
+    for kw in ({"alpha": -0.1}, {"alpha": 1.5}, {"alpha": float("nan")},
+               {"scale": float("inf")}, {"scale": float("nan")}):
+        assert xent(L, **kw) == LN_ERR_PARAM, kw
+    assert xent(L, rows=0, alpha=1.0) == LN_OK
+    assert xent(L, dx=A + 2) == LN_ERR_UNSUPPORTED              # partial overlap of logits
+    assert xent(L, dx=B) == LN_ERR_UNSUPPORTED                  # dlogits over the labels
+    assert xent(L, loss=B) == LN_ERR_UNSUPPORTED                # loss over the labels
+    assert xent(L, loss=A) == LN_ERR_UNSUPPORTED                # loss over the logits
