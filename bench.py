@@ -235,6 +235,9 @@ def configs_report(cpp_launch: bool = True) -> None:
       * fused residual add + RMSNorm forward and backward at 2048x4096 bf16
         (one layer of a 2048-token Llama-3-8B prefill), rotated past the
         cache, and the forward at 64x4096 (a decode step of 64 requests);
+      * fused cross-entropy loss + gradient over GPT-2's vocabulary (50257
+        classes in rows padded to 50304), 8x1024 tokens, bf16 and fp32, with
+        the gradient in its own buffer and over the logits;
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
@@ -509,6 +512,42 @@ def configs_report(cpp_launch: bool = True) -> None:
                  "fused residual add + RMSNorm fwd + bwd (dz_extra given), 2048x4096, rotated")
     rmsnorm_case(64, 4096, 1, 1000, "fused residual add + RMSNorm forward, decode 64x4096",
                  bwd=False)
+
+    # fused cross-entropy (loss + gradient) over a vocabulary-wide row
+    def xent_case(rows, cols, ld, dt, label):
+        x = synth.logits(rows, ld, dt, seed=SEED).to(dev)
+        lab = synth.class_labels(rows, cols, seed=SEED).to(dev)
+        loss = torch.empty(rows, dtype=torch.float32, device=dev)
+        dx = torch.empty_like(x)
+        s = x.element_size()
+
+        def f(i):
+            mb.cross_entropy_fwd_bwd(x, lab, cols=cols, label_smoothing=0.1,
+                                     grad_scale=1.0 / rows, loss=loss, dlogits=dx)
+
+        def g(i):
+            # the gradient over the logits (values change, the work does not)
+            mb.cross_entropy_fwd_bwd(x, lab, cols=cols, label_smoothing=0.1,
+                                     grad_scale=1.0 / rows, loss=loss, dlogits=x)
+
+        f(0)
+        torch.cuda.synchronize()
+        n = 20
+        ms = timed(capture(f, n), n)
+        ms_ip = timed(capture(g, n), n)
+        b = 2 * rows * cols * s + 12 * rows
+        emit({"workload": label, "rows": rows, "cols": cols, "ld": ld,
+              "storage": str(dt)[6:], "bytes_per_pass": b, "iters": n,
+              "us_per_pass": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+              "pct_of_hbm_peak": round(100.0 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+              "in_place_us": round(ms_ip * 1e3, 3),
+              "in_place_GBps": round(b / (ms_ip * 1e-3) / 1e9, 1)})
+        del x, dx, lab, loss
+        torch.cuda.empty_cache()
+
+    for dt in (torch.bfloat16, torch.float32):
+        xent_case(8192, 50257, 50304, dt,
+                  "fused cross-entropy loss + gradient, GPT-2 vocabulary, 8x1024 tokens")
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")

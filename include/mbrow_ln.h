@@ -77,11 +77,11 @@ typedef enum {
  * three column accumulators per value need the registers of twice as many
  * lanes). */
 #define LN_MAX_COLS_DROPOUT_BWD 8192
-/* Widest padded row (ld) of cross_entropy_fwd_bwd: 53248 fp32 or 57344
+/* Widest padded row (ld) of cross_entropy_fwd_bwd: 65536 fp32 or 131072
  * fp16/bf16 classes (the row is held in the registers of one 1024-lane
- * workgroup; GPT-2's 50257-entry vocabulary, padded to 50304, fits). */
-#define LN_MAX_COLS_XENT_F32 53248
-#define LN_MAX_COLS_XENT_16 57344
+ * workgroup; GPT-2's 50257 and Llama-3's 128256 classes fit in bf16). */
+#define LN_MAX_COLS_XENT_F32 65536
+#define LN_MAX_COLS_XENT_16 131072
 
 /*
  * LayerNorm forward.  For each row r with m = cols:

@@ -12,7 +12,7 @@
 // the logits can be overwritten by the gradient in the same kernel.
 //
 // Here a row is held in registers across G lanes (up to 1024 lanes of one
-// workgroup: GPT-2's 50304-column padded vocabulary fits in fp32 and bf16),
+// workgroup: 65536 fp32 or 131072 16-bit classes),
 // so it is read from HBM once and written once.  Each lane reduces its own
 // values to (max, sum of exp(x - max), sum x), the lanes merge those states
 // in one butterfly (and one LDS exchange across the waves of a row), x at the
@@ -85,6 +85,50 @@ __device__ inline XeState xe_group(XeState s) {
     return s;
 }
 
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// 2^x by the hardware exp2 (v_exp_f32).
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per-element access for rows that are not 16-byte aligned: one 2- or
+// 4-byte buffer access per element through the same wave row views (a 32-bit
+// offset per element instead of a 64-bit address; offsets past the view read
+// 0 and drop stores).
+template <class S>
+__device__ __forceinline__ float elem_load(rsrc_t r, uint32_t off) {
+    if constexpr (S::BYTES == 4) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    } else {
+        const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+        if constexpr (std::is_same<S, StBF16>::value) {
+            return __uint_as_float((uint32_t)b << 16);
+        } else {
+            return (float)__builtin_bit_cast(_Float16, b);
+        }
+    }
+}
+template <class S>
+__device__ __forceinline__ void elem_store(rsrc_t r, uint32_t off, float f) {
+    if constexpr (S::BYTES == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, (int)off, 0, 0);
+    } else if constexpr (std::is_same<S, StBF16>::value) {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)f), r,
+                                              (int)off, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)f), r,
+                                              (int)off, 0, 0);
+    }
+}
+
+// Packed slots that must be formed before any later memory access is issued
+// (the memory clobber orders them): bounds the per-element loads in flight
+// to one group of slots, each of which holds a whole register until packed.
+__device__ __forceinline__ void hold_packed(u32x4& v) {
+    uint32_t a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3) : : "memory");
+    v = u32x4{a0, a1, a2, a3};
+}
+
 // An integer the compiler must treat as changed: per-element comparisons
 // against it are formed where they are used instead of being hoisted out of
 // the row loop and held (one lane mask per element) across the passes.
@@ -118,6 +162,8 @@ __global__ __launch_bounds__(XeGeometry<G>::NT) void xent_kernel(XeArgs a) {
     // slot); slots past the classes are not read (kOob), slots past the
     // padded row are not written
     const uint32_t rbase = slot_offset<S, G>(tid, 0, ld, true);
+    // per-element path: byte offset of the lane's first column in the view
+    const uint32_t ebase = (uint32_t)((G <= 64 ? (tid & 63) / G : 0) * ld + base) * S::BYTES;
     auto slot_off = [&](uint32_t rb, int i, int nslot) {
         return i * G + lg < nslot ? rb + (uint32_t)(i * G * 16) : kOob;
     };
@@ -149,44 +195,74 @@ __global__ __launch_bounds__(XeGeometry<G>::NT) void xent_kernel(XeArgs a) {
 #pragma unroll
             for (int i = 0; i < V; ++i) xr[i] = buf_load_nt(vx, slot_off(rb, i, nv));
         } else {
+            const rsrc_t vx = view(a.x, blk);
             const int lim = opaque(cols - base);
+            const uint32_t eb = (uint32_t)opaque((int)ebase);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 float f[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    f[e] = (rok && i * G * E + e < lim) ? S::load1(a.x, off + base + i * G * E + e)
-                                                         : 0.0f;
+                for (int e = 0; e < E; ++e) {
+                    const int c = i * G * E + e;
+                    f[e] = elem_load<S>(vx, c < lim ? eb + (uint32_t)c * S::BYTES : kOob);
+                }
                 xr[i] = S::pack(f);
+                // wide rows: at most four slots of element loads in flight
+                if constexpr (V * E > 32) {
+                    if (i % 4 == 3 || i == V - 1) {
+#pragma unroll
+                        for (int k = i - i % 4; k <= i; ++k) hold_packed(xr[k]);
+                    }
+                }
             }
         }
-        // this lane's state: max and sum of x, then the exp-sum against the max
+        // This lane's state: max and sum of x, then the exp-sum against the
+        // max.  Slots wholly inside the classes take no per-element test; at
+        // most one slot of a row is partial, and slots past the classes are
+        // skipped (per-slot branches, taken by few waves).
         XeState st{-INFINITY, 0.0f, 0.0f};
         {
             const int lim = opaque(cols - base);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
+                constexpr int W = G * E;
                 float f[E];
                 S::unpack(xr[i], f);
+                if (i * W + E <= lim) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const bool in = i * G * E + e < lim;
-                    st.mx = fmaxf(st.mx, in ? f[e] : -INFINITY);
-                    st.sx += in ? f[e] : 0.0f;
+                    for (int e = 0; e < E; ++e) {
+                        st.mx = fmaxf(st.mx, f[e]);
+                        st.sx += f[e];
+                    }
+                } else if (i * W < lim) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        if (i * W + e < lim) {
+                            st.mx = fmaxf(st.mx, f[e]);
+                            st.sx += f[e];
+                        }
+                    }
                 }
             }
         }
         keep_packed(xr);
         {
             const int lim = opaque(cols - base);
-            const float m0 = st.mx == -INFINITY ? 0.0f : st.mx;   // lanes past the row
+            // exp(x - m) = exp2(x log2(e) - m log2(e)), one fma and one exp2
+            const float nm = st.mx == -INFINITY ? 0.0f : -st.mx * kLog2e;   // lanes past the row
 #pragma unroll
             for (int i = 0; i < V; ++i) {
+                constexpr int W = G * E;
                 float f[E];
                 S::unpack(xr[i], f);
+                if (i * W + E <= lim) {
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    st.z += i * G * E + e < lim ? __expf(f[e] - m0) : 0.0f;
+                    for (int e = 0; e < E; ++e) st.z += exp2_(fmaf(f[e], kLog2e, nm));
+                } else if (i * W < lim) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (i * W + e < lim) st.z += exp2_(fmaf(f[e], kLog2e, nm));
+                }
             }
         }
         if constexpr (G <= 64) {
@@ -207,35 +283,54 @@ __global__ __launch_bounds__(XeGeometry<G>::NT) void xent_kernel(XeArgs a) {
             a.loss[row] = ignored ? 0.0f : (bad ? NAN : l);
         }
         if (grad) {
-            // dx = scale * (q - p): q = exp(x - m) / Z, p = a/V + (1 - a)[j == label]
+            // dx = scale * (q - p) = exp(x - m) * (scale / Z) - scale * p with
+            // p = a/V off the label and a/V + 1 - a at it
             keep_packed(xr);
-            const float iz = 1.0f / st.z;
+            const float nm = -st.mx * kLog2e;
+            const float siz = a.scale * (1.0f / st.z);
             const float pa = alpha * inv_v;
-            const float fill = ignored ? 0.0f : NAN;   // rows without a target
+            const float nsp = -(a.scale * pa);
+            const float nsl = -(a.scale * (pa + (1.0f - alpha)));
             const bool no_target = ignored || bad;
+            const float fill = ignored ? 0.0f : NAN;   // rows without a target
             const int lim = opaque(cols - base);
-            const int rel = opaque((int)(ignored || bad ? -1 : label) - base);
+            const int rel = opaque((int)(no_target ? -1 : label) - base);
             const rsrc_t vd = view(a.dx, blk);
             const uint32_t rb = (uint32_t)opaque((int)rbase);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
+                constexpr int W = G * E;
                 float f[E], out[E];
                 S::unpack(xr[i], f);
+                if (!no_target) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int c = i * G * E + e;
-                    const float q = __expf(f[e] - st.mx) * iz;
-                    const float p = c == rel ? pa + (1.0f - alpha) : pa;
-                    const float d = no_target ? fill : a.scale * (q - p);
-                    out[e] = c < lim ? d : 0.0f;   // padding columns get 0
+                    for (int e = 0; e < E; ++e)
+                        out[e] = fmaf(exp2_(fmaf(f[e], kLog2e, nm)), siz, nsp);
+                    if ((unsigned)(rel - i * W) < (unsigned)E) {   // the label is here
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (i * W + e == rel)
+                                out[e] = fmaf(exp2_(fmaf(f[e], kLog2e, nm)), siz, nsl);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) out[e] = fill;
+                }
+                if (!(i * W + E <= lim)) {   // padding columns get 0
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (i * W + e >= lim) out[e] = 0.0f;
                 }
                 if constexpr (VEC) {
                     buf_store_nt(S::pack(out), vd, slot_off(rb, i, ns));
                 } else {
                     const int wl = opaque(ld - base);
+                    const uint32_t eb = (uint32_t)opaque((int)ebase);
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        if (rok && i * G * E + e < wl) S::store1(a.dx, off + base + i * G * E + e, out[e]);
+                    for (int e = 0; e < E; ++e) {
+                        const int c = i * W + e;
+                        elem_store<S>(vd, c < wl ? eb + (uint32_t)c * S::BYTES : kOob, out[e]);
+                    }
                 }
             }
         }

@@ -162,6 +162,7 @@ def test_debug_force_path_validation(L):
     assert L.ln_debug_force_path(128, 2, 0) == LN_OK          # prologue-backward layout
     assert L.ln_debug_force_path(0, 0, 0) == LN_OK
     assert L.ln_debug_force_path(1024, 9, 0) == LN_ERR_UNSUPPORTED
+    assert L.ln_debug_force_path(1024, 16, 0) == LN_OK
     assert L.ln_debug_force_path(1024, 13, 0) == LN_OK        # cross-entropy layout
     assert L.ln_debug_force_path(64, 3, 0) == LN_OK
     assert L.ln_debug_force_path(0, 0, 0) == LN_OK
@@ -309,12 +310,12 @@ def test_cross_entropy_validation(L):
     assert xent(L, cols=0) == LN_ERR_SHAPE
     assert xent(L, cols=9, ld=8) == LN_ERR_SHAPE                # ld < cols
     assert xent(L, dt=3) == LN_ERR_DTYPE
-    assert xent(L, cols=53248, ld=53248, rows=0, dt=F32) == LN_OK
-    assert xent(L, cols=53249, ld=53249, dt=F32) == LN_ERR_UNSUPPORTED
-    assert xent(L, cols=100, ld=53249, dt=F32) == LN_ERR_UNSUPPORTED
+    assert xent(L, cols=65536, ld=65536, rows=0, dt=F32) == LN_OK
+    assert xent(L, cols=65537, ld=65537, dt=F32) == LN_ERR_UNSUPPORTED
+    assert xent(L, cols=100, ld=65537, dt=F32) == LN_ERR_UNSUPPORTED
     for dt in (F16, BF16):
-        assert xent(L, cols=57344, ld=57344, rows=0, dt=dt) == LN_OK
-        assert xent(L, cols=57345, ld=57345, dt=dt) == LN_ERR_UNSUPPORTED
+        assert xent(L, cols=131072, ld=131072, rows=0, dt=dt) == LN_OK
+        assert xent(L, cols=131073, ld=131073, dt=dt) == LN_ERR_UNSUPPORTED
     for kw in ({"alpha": -0.1}, {"alpha": 1.5}, {"alpha": float("nan")},
                {"scale": float("inf")}, {"scale": float("nan")}):
         assert xent(L, **kw) == LN_ERR_PARAM, kw

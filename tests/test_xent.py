@@ -14,9 +14,10 @@ pytestmark = pytest.mark.gpu
 DTYPES = [torch.float32, torch.float16, torch.bfloat16]
 LAYOUTS_F32 = [(16, 1), (16, 2), (16, 4), (32, 2), (32, 4), (64, 2), (64, 4), (64, 8),
                (128, 4), (256, 4), (512, 4), (1024, 4), (1024, 6), (1024, 8), (1024, 10),
-               (1024, 13)]
+               (1024, 13), (1024, 16)]
 LAYOUTS_16 = [(16, 1), (16, 2), (32, 1), (32, 2), (64, 1), (64, 2), (64, 4), (128, 4),
-              (256, 4), (512, 4), (1024, 4), (1024, 5), (1024, 6), (1024, 7)]
+              (256, 4), (512, 4), (1024, 4), (1024, 5), (1024, 6), (1024, 7), (1024, 8),
+              (1024, 10), (1024, 12), (1024, 14), (1024, 16)]
 GPT2_V, GPT2_VP = 50257, 50304   # GPT-2's vocabulary and its padded row
 
 
@@ -46,6 +47,15 @@ def test_gpt2_full_batch_sampled(orc):
     sel = np.random.default_rng(5).choice(8192, 48, replace=False)
     sel = np.concatenate([sel, [0, 8191]])
     run(orc, 8192, GPT2_V, GPT2_VP, torch.bfloat16, 1, rows_sel=sel, name="xent.8192")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("cols,ld", [(128256, 128256), (128255, 128255)])
+def test_llama3_vocabulary(orc, dtype, cols, ld):
+    # a 128K vocabulary (the lecture notes' example of logits outgrowing the
+    # weights); the odd width takes the per-element path at 16 slots per lane
+    case(f"cross-entropy 40x{cols} ld {ld} {dtype}")
+    run(orc, 40, cols, ld, dtype, 12, name=f"xent.{cols}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
