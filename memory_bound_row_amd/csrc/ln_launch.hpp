@@ -184,12 +184,13 @@ struct XeArgs {
 // classes.
 #define MBROW_XE_LAYOUTS_F32(X)                                             \
     X(16, 1) X(16, 2) X(16, 4) X(32, 2) X(32, 4) X(64, 2) X(64, 4) X(64, 8) \
-    X(128, 4) X(256, 4) X(512, 4) X(1024, 4) X(1024, 6) X(1024, 8)         \
-    X(1024, 10) X(1024, 13) X(1024, 16)
+    X(128, 4) X(256, 4) X(512, 4) X(512, 8) X(512, 13) X(1024, 4)          \
+    X(1024, 6) X(1024, 8) X(1024, 10) X(1024, 13) X(1024, 16)
 #define MBROW_XE_LAYOUTS_16(X)                                              \
     X(16, 1) X(16, 2) X(32, 1) X(32, 2) X(64, 1) X(64, 2) X(64, 4)          \
-    X(128, 4) X(256, 4) X(512, 4) X(1024, 4) X(1024, 5) X(1024, 6)         \
-    X(1024, 7) X(1024, 8) X(1024, 10) X(1024, 12) X(1024, 14) X(1024, 16)
+    X(128, 4) X(256, 4) X(512, 4) X(512, 7) X(512, 10) X(512, 13)          \
+    X(1024, 4) X(1024, 5) X(1024, 6) X(1024, 7) X(1024, 8) X(1024, 10)     \
+    X(1024, 12) X(1024, 14) X(1024, 16)
 
 Path pick_xent_path(Dt dt, int64_t slots, bool vec);
 hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s);

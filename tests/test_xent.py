@@ -13,11 +13,12 @@ pytestmark = pytest.mark.gpu
 
 DTYPES = [torch.float32, torch.float16, torch.bfloat16]
 LAYOUTS_F32 = [(16, 1), (16, 2), (16, 4), (32, 2), (32, 4), (64, 2), (64, 4), (64, 8),
-               (128, 4), (256, 4), (512, 4), (1024, 4), (1024, 6), (1024, 8), (1024, 10),
-               (1024, 13), (1024, 16)]
+               (128, 4), (256, 4), (512, 4), (512, 8), (512, 13), (1024, 4), (1024, 6),
+               (1024, 8), (1024, 10), (1024, 13), (1024, 16)]
 LAYOUTS_16 = [(16, 1), (16, 2), (32, 1), (32, 2), (64, 1), (64, 2), (64, 4), (128, 4),
-              (256, 4), (512, 4), (1024, 4), (1024, 5), (1024, 6), (1024, 7), (1024, 8),
-              (1024, 10), (1024, 12), (1024, 14), (1024, 16)]
+              (256, 4), (512, 4), (512, 7), (512, 10), (512, 13), (1024, 4), (1024, 5),
+              (1024, 6), (1024, 7), (1024, 8), (1024, 10), (1024, 12), (1024, 14),
+              (1024, 16)]
 GPT2_V, GPT2_VP = 50257, 50304   # GPT-2's vocabulary and its padded row
 
 
