@@ -335,13 +335,16 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         // order (0, 1, ...) column by column, consecutive threads taking
         // consecutive columns, and writes the workgroup's partial.  The
         // accumulators go through LDS in chunks of CI slot indices so the
-        // footprint stays within 64 KB.
-        constexpr int KF = 65536 / (NU * NK * UT * 4);          // floats per lane that fit
+        // footprint stays within kStage bytes (gfx950 has 160 KB of LDS per
+        // workgroup; most layouts then stage every accumulator in one chunk:
+        // one barrier instead of one per chunk).
+        constexpr int kStage = 156 * 1024;
+        constexpr int KF = kStage / (NU * NK * UT * 4);          // floats per lane that fit
         constexpr int CI = (KF - 1) / E < 1 ? 1 : ((KF - 1) / E < V ? (KF - 1) / E : V);
         constexpr int CK = CI * E + 1;                          // padded lane stride
         constexpr int CW = CI * G * E;                          // columns per chunk
         float* const pw = a.ws + part * NK * a.m;   // this partition's [NK][m] partial
-        constexpr bool DIRECT = NU == 1 && NK * UT * CK * 4 > 65536;
+        constexpr bool DIRECT = NU == 1 && NK * UT * CK * 4 > kStage;
         if constexpr (DIRECT) {
             // one unit too wide to stage: every column is held by exactly
             // one lane, which writes it
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             }
             return;
         }
-        static_assert(DIRECT || NU * NK * UT * CK * 4 <= 65536, "stage exceeds 64 KB");
+        static_assert(DIRECT || NU * NK * UT * CK * 4 <= kStage, "stage exceeds its budget");
         __shared__ float stage[DIRECT ? 1 : NU][NK][DIRECT ? 1 : UT][DIRECT ? 1 : CK];
         const int unit = tid / UT;
         const int pos = tid % UT;
