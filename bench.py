@@ -69,10 +69,16 @@ def parse():
     return ap.parse_args()
 
 
+# Sources the step's kernels are compiled from (forward, backward, fold, their
+# shared device code) and launched by (argument checks, layout choice, grid).
+STEP_SOURCES = ("ln_api.cpp", "ln_bwd.hip", "ln_device.hpp", "ln_fold.hip", "ln_fwd.hip",
+                "ln_launch.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "memory_bound_row_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in STEP_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
