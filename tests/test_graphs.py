@@ -1,0 +1,157 @@
+"""Every entry point captured into a HIP graph: replays, separated by eager
+work on the same buffers and synchronisations, give the eager result bit for
+bit (the calls enqueue only kernels: no memsets, copies or allocations)."""
+import pytest
+import torch
+
+import memory_bound_row_amd as mb
+from memory_bound_row_amd import synth
+from gpu_helpers import case, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t
+
+
+def check_replays(run, outputs, inputs_reset=None, replays=4):
+    """run() enqueues the call into preallocated outputs; compare each graph
+    replay with the eager result."""
+    run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outputs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for k in range(replays):
+        for o in outputs:
+            o.fill_(float("nan") if o.is_floating_point() else 0)   # eager work in between
+        if inputs_reset:
+            inputs_reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outputs, ref):
+            assert torch.equal(bits(o), bits(r)), f"replay {k} differs"
+
+
+def test_layernorm_step_in_a_graph():
+    case("graph: fused forward, backward with partials, fold")
+    R, C = 1000, 1280
+    d = dev(synth.layer_inputs(R, C, torch.bfloat16, seed=3))
+    z, y = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+    mean = torch.empty(R, dtype=torch.float32, device="cuda")
+    rstd = torch.empty_like(mean)
+    dx = torch.empty_like(d["x"])
+    ws = mb.workspace(R, C, "cuda")
+    dg = torch.empty(C, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dg)
+
+    def run():
+        mb.bias_dropout_residual_ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"], d["beta"],
+                                        0.1, 5, 1e-5, residual_out=z, y=y, mean=mean, rstd=rstd)
+        mb.ln_bwd_dx(d["dy"], z, d["gamma"], mean, rstd, dx=dx, workspace=ws)
+        mb.ln_bwd_dgamma_dbeta(ws, R, C, torch.bfloat16, partials_ready=True, dgamma=dg,
+                               dbeta=db)
+
+    check_replays(run, [z, y, mean, rstd, dx, dg, db])
+
+
+def test_prologue_backward_in_a_graph():
+    case("graph: prologue backward")
+    R, C = 600, 1024
+    d = dev(synth.layer_inputs(R, C, torch.float16, seed=4))
+    z, _, mean, rstd, _ = mb.bias_dropout_residual_ln_fwd(
+        d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 0.2, 9, 1e-5)
+    outs = [torch.empty_like(z), torch.empty_like(z)] + \
+        [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = mb.dropout_workspace(R, C, "cuda")
+
+    def run():
+        mb.bias_dropout_residual_ln_bwd(d["dy"], z, d["gamma"], mean, rstd, 0.2, 9,
+                                        dz_extra=d["residual"], dresidual=outs[0], dx=outs[1],
+                                        dgamma=outs[2], dbeta=outs[3], dbias=outs[4],
+                                        workspace=ws)
+
+    check_replays(run, outs)
+
+
+def test_softmax_in_a_graph():
+    case("graph: attention softmax forward and backward")
+    d = dev(synth.layer_inputs(4 * 256, 256, torch.bfloat16, seed=5, x_std=3.0,
+                               names=("x", "dy")))
+    y, yd, dx = (torch.empty_like(d["x"]) for _ in range(3))
+
+    def run():
+        mb.attn_softmax_fwd(d["x"], 0.125, causal=True, p=0.1, seed=2, y=y, y_dropped=yd)
+        mb.attn_softmax_bwd(d["dy"], y, 0.125, causal=True, p=0.1, seed=2, dx=dx)
+
+    check_replays(run, [y, yd, dx])
+
+
+def test_rmsnorm_in_a_graph():
+    case("graph: add + RMSNorm forward and backward")
+    R, C = 512, 4096
+    d = dev(synth.layer_inputs(R, C, torch.bfloat16, seed=6,
+                               names=("x", "residual", "gamma", "dy")))
+    z, y, dz = (torch.empty_like(d["x"]) for _ in range(3))
+    rstd = torch.empty(R, dtype=torch.float32, device="cuda")
+    dg = torch.empty(C, dtype=torch.float32, device="cuda")
+    ws = mb.rmsnorm_workspace(R, C, "cuda")
+
+    def run():
+        mb.add_rmsnorm_fwd(d["x"], d["gamma"], 1e-6, residual=d["residual"], residual_out=z,
+                           y=y, rstd=rstd)
+        mb.add_rmsnorm_bwd(d["dy"], z, d["gamma"], rstd, dz_extra=d["dy"], dz=dz, dgamma=dg,
+                           workspace=ws)
+
+    check_replays(run, [z, y, rstd, dz, dg])
+
+
+def test_cross_entropy_in_a_graph():
+    case("graph: cross-entropy, gradient over the logits")
+    R, V, LD = 256, 50257, 50304
+    x0 = synth.logits(R, LD, torch.bfloat16, seed=7).to("cuda")
+    lab = synth.class_labels(R, V, seed=7).to("cuda")
+    x = x0.clone()
+    loss = torch.empty(R, dtype=torch.float32, device="cuda")
+
+    def reset():
+        x.copy_(x0)
+
+    def run():
+        mb.cross_entropy_fwd_bwd(x, lab, cols=V, label_smoothing=0.1, grad_scale=1.0 / R,
+                                 loss=loss, dlogits=x)
+
+    # the call overwrites its input: restore the logits before every run
+    reset()
+    run()
+    torch.cuda.synchronize()
+    ref = [loss.clone(), x.clone()]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for k in range(4):
+        loss.fill_(float("nan"))
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss, ref[0]), f"replay {k}: loss differs"
+        assert torch.equal(bits(x), bits(ref[1])), f"replay {k}: gradient differs"
