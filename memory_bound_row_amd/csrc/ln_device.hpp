@@ -237,6 +237,11 @@ __device__ __forceinline__ u32x4 load_param(const void* base, int s, int m, bool
     }
 }
 
+// exp(x - m) as exp2(x log2(e) - m log2(e)): one fma and the hardware exp2
+// (v_exp_f32) per element, with -m log2(e) formed once per row.
+constexpr float kLog2e = 1.44269504088896340736f;
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Keep a packed register array packed: the empty asm tells the compiler the
 // values may have changed, so unpacking them is not hoisted out of a loop
 // (which would hold the unpacked floats, twice the registers, across it).

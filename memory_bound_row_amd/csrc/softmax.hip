@@ -183,18 +183,20 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
             }
             mx = reduce_max(mx, buf);
             // exp of the difference and the row sum (a row with every key
-            // masked has mx = -inf and gives zeros)
+            // masked has mx = -inf: its scores are all -inf and exp2 gives 0)
             const bool live_row = mx != -INFINITY;
+            const float nm = live_row ? -mx * kLog2e : 0.0f;
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < V; ++i)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    t[i][e] = live_row ? __expf(t[i][e] - mx) : 0.0f;
+                    t[i][e] = exp2_(fmaf(t[i][e], kLog2e, nm));
                     s += t[i][e];
                 }
             s = reduce_sum(s, buf);
             const float inv = live_row ? 1.0f / s : 0.0f;
+            const float inv_kept = inv * a.pscale;   // dropped copy: y / (1 - p)
             const rsrc_t vy = view(a.out, blk);
             const rsrc_t vd = view(a.out2 ? a.out2 : a.out, blk);
 #pragma unroll
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
                     float dv[E];
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        dv[e] = kept<E>(w, col0, e, a.thr) ? yv[e] * a.pscale : 0.0f;
+                        dv[e] = kept<E>(w, col0, e, a.thr) ? t[i][e] * inv_kept : 0.0f;
                     if constexpr (VEC) {
                         buf_store_nt(S::pack(dv), vd, vo[i]);
                     } else {

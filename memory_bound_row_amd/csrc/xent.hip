@@ -85,11 +85,6 @@ __device__ inline XeState xe_group(XeState s) {
     return s;
 }
 
-constexpr float kLog2e = 1.44269504088896340736f;
-
-// 2^x by the hardware exp2 (v_exp_f32).
-__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Per-element access for rows that are not 16-byte aligned: one 2- or
 // 4-byte buffer access per element through the same wave row views (a 32-bit
 // offset per element instead of a 64-bit address; offsets past the view read
