@@ -166,6 +166,17 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 }
             }
         }
+        // The prologue's mask words depend only on (row, column): formed while
+        // the block's loads are in flight (layouts with room for them; wider
+        // ones form each slot's words where they are used).
+        constexpr bool EARLY = DROP && V <= 4;
+        u32x4 dw[EARLY ? V : 1];
+        if constexpr (EARLY) {
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                dw[i] = dropout_words(row, (i * G + lg) * E, a.seed_lo, a.seed_hi, a.thr);
+            keep_packed(dw);
+        }
         const float mu = RMS ? 0.0f : a.mean[r], rs = a.rstd[r];
         // (the per-element path and multi-wave rows of the prologue backward
         // have no registers to spare for gamma unpacked across blocks)
@@ -282,7 +293,12 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 if constexpr (DROP) {
                     // dresidual = dz; dx of the prologue = keep * dz / (1 - p)
                     // with the forward's mask regenerated; dbias sums it
-                    const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                    u32x4 w;
+                    if constexpr (EARLY) {
+                        w = dw[i];
+                    } else {
+                        w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                    }
                     float din[E];
 #pragma unroll
                     for (int e = 0; e < E; ++e) {

@@ -155,6 +155,13 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
         auto inside = [&](int i, int e) { return ok[i] && (VEC || (i * G + lg) * E + e < m); };
         if constexpr (FUSED) {
             if constexpr (PREG) keep_packed(bip);
+            // the mask words depend only on (row, column): formed before the
+            // block's data is waited for
+            u32x4 dw[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                dw[i] = dropout_words(row, (i * G + lg) * E, a.seed_lo, a.seed_hi, a.thr);
+            keep_packed(dw);
             const rsrc_t vz = view(a.residual_out, blk);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(Geometry<G>::NT) void ln_fwd_kernel(FwdArgs a) {
                 S::unpack(param(a.bias, bip, i), bv);
                 // (slots outside the tensor are never stored, so their
                 // uniforms do not matter)
-                const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                const u32x4 w = dw[i];
                 float z[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {

@@ -164,6 +164,16 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
             }
         }
 
+        // The dropout mask words depend only on (row, column): formed while
+        // the block's loads are in flight (forward: only with a dropped copy).
+        u32x4 dw[V];
+        const bool drop = BWD || a.out2 != nullptr;   // uniform
+        if (drop) {
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                dw[i] = dropout_words(row, (i * G + lg) * E, a.seed_lo, a.seed_hi, a.thr);
+            keep_packed(dw);
+        }
         if constexpr (!BWD) {
             // scores: scale, mask, -inf where masked; the row maximum
             float t[V][E];
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
                     store_elems<S>(a.out, r, m, col0, ok[i] && rok, yv);
                 }
                 if (a.out2) {
-                    const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                    const u32x4 w = dw[i];
                     float dv[E];
 #pragma unroll
                     for (int e = 0; e < E; ++e)
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
                 float dv[E];
                 S::unpack(xr[i], dv);
                 S::unpack(yr[i], y[i]);
-                const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                const u32x4 w = dw[i];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     g[i][e] = kept<E>(w, col0, e, a.thr) ? dv[e] * a.pscale : 0.0f;
