@@ -208,25 +208,31 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t blocks) {
     const int forced = g_force_grid.load(std::memory_order_relaxed);
     if (forced < 0) return blocks;
     static std::mutex mu;
-    static std::unordered_map<const void*, int> per_cu;   // resident workgroups per CU
-    static int cus = 0;
-    int n = 0;
+    // per device: its CU count, and resident workgroups per CU of each kernel
+    static std::unordered_map<int, int> cu_count;
+    static std::unordered_map<int, std::unordered_map<const void*, int>> per_cu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return blocks;
+    int cus = 0, n = 0;
     {
         std::lock_guard<std::mutex> lock(mu);
-        if (cus == 0) {
-            int dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                    hipSuccess || cus <= 0)
-                cus = 0;
+        auto c = cu_count.find(dev);
+        if (c == cu_count.end()) {
+            int v = 0;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) !=
+                    hipSuccess || v <= 0)
+                v = 0;
+            c = cu_count.emplace(dev, v).first;
         }
-        auto it = per_cu.find(kernel);
-        if (it == per_cu.end()) {
+        cus = c->second;
+        auto& kmap = per_cu[dev];
+        auto it = kmap.find(kernel);
+        if (it == kmap.end()) {
             int b = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, threads, 0) !=
                     hipSuccess || b <= 0)
                 b = 0;
-            it = per_cu.emplace(kernel, b).first;
+            it = kmap.emplace(kernel, b).first;
         }
         n = it->second;
     }

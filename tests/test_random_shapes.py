@@ -1,0 +1,106 @@
+"""GPU parity on seeded random shapes: every entry point on widths drawn
+log-uniformly over its supported range, random row counts, all storage types,
+and tensors that start one element into their allocation (base addresses not
+16-byte aligned, which forces the per-element paths).  Each case is checked
+against the float64 oracle with the same helpers as the targeted tests."""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_amd as mb
+from memory_bound_row_amd import synth
+from gpu_helpers import (EPS, FMT, case, check_bwd, check_dropout_bwd, check_fused, check_fwd,
+                         check_rmsnorm_bwd, check_rmsnorm_fwd, check_softmax_bwd,
+                         check_softmax_fwd, check_xent)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [torch.float32, torch.float16, torch.bfloat16]
+KINDS = ["layernorm", "fused", "prologue_bwd", "softmax", "rmsnorm", "xent"]
+MAX_COLS = {"layernorm": 16384, "fused": 16384, "prologue_bwd": 8192, "softmax": 16384,
+            "rmsnorm": 16384, "xent": 60000}
+N_CASES = 36
+
+
+def draw(idx):
+    """Shape of case idx: (kind, dtype, rows, cols, misaligned)."""
+    g = np.random.default_rng([2024, idx])
+    kind = KINDS[idx % len(KINDS)]
+    dtype = DTYPES[int(g.integers(0, 3))]
+    cols = int(np.exp(g.uniform(0.0, np.log(MAX_COLS[kind]))))
+    cols = max(1, cols)
+    budget = 3_000_000 if kind == "xent" else 1_500_000
+    rows = int(g.integers(1, max(2, min(400, budget // cols))))
+    misaligned = bool(g.integers(0, 4) == 0)
+    return kind, dtype, rows, cols, misaligned
+
+
+def place(t, misaligned):
+    """t on the GPU, optionally starting one element into a larger buffer."""
+    if not misaligned:
+        return t.to("cuda")
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+    out = buf[1:].view(t.shape)
+    out.copy_(t.to("cuda"))
+    return out
+
+
+@pytest.mark.parametrize("idx", range(N_CASES))
+def test_random_shape(orc, idx):
+    kind, dtype, rows, cols, mis = draw(idx)
+    case(f"random case {idx}: {kind} {rows}x{cols} {dtype} misaligned={mis}")
+    fmt = FMT[dtype]
+    seed = 1000 + idx
+    if kind in ("layernorm", "fused", "prologue_bwd"):
+        cpu = synth.layer_inputs(rows, cols, dtype, seed=seed)
+        d = {k: place(v, mis) for k, v in cpu.items()}
+        if kind == "layernorm":
+            y, mean, rstd = mb.ln_fwd(d["x"], d["gamma"], d["beta"], EPS)
+            dx, dg, db = mb.ln_bwd(d["dy"], d["x"], d["gamma"], mean, rstd)
+            torch.cuda.synchronize()
+            check_fwd(orc, d["x"], d["gamma"], d["beta"], y, mean, rstd, fmt, name="rnd.fwd")
+            check_bwd(orc, d["dy"], d["x"], d["gamma"], mean, rstd, dx, dg, db, fmt,
+                      name="rnd.bwd")
+        elif kind == "fused":
+            z, y, mean, rstd, mask = mb.bias_dropout_residual_ln_fwd(
+                d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 0.15, seed, EPS,
+                want_mask=True)
+            torch.cuda.synchronize()
+            check_fused(orc, d, 0.15, seed, z, y, mean, rstd, mask, fmt, name="rnd.fused")
+        else:
+            z, _, mean, rstd, _ = mb.bias_dropout_residual_ln_fwd(
+                d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 0.15, seed, EPS)
+            ez = place(synth.layer_inputs(rows, cols, dtype, seed=seed + 1,
+                                          names=("dy",))["dy"], mis)
+            dres, dx, dg, db, dbias = mb.bias_dropout_residual_ln_bwd(
+                d["dy"], z, d["gamma"], mean, rstd, 0.15, seed, dz_extra=ez)
+            torch.cuda.synchronize()
+            check_dropout_bwd(orc, d["dy"], ez, z, d["gamma"], mean, rstd, 0.15, seed, dres,
+                              dx, dg, db, dbias, fmt, name="rnd.drop_bwd")
+    elif kind == "softmax":
+        cpu = synth.layer_inputs(rows, cols, dtype, seed=seed, x_std=3.0, names=("x", "dy"))
+        x, dy = place(cpu["x"], mis), place(cpu["dy"], mis)
+        y, yd = mb.attn_softmax_fwd(x, 0.5, p=0.1, seed=seed, want_dropped=True)
+        dx = mb.attn_softmax_bwd(dy, y, 0.5, p=0.1, seed=seed)
+        torch.cuda.synchronize()
+        check_softmax_fwd(orc, x, y, yd, fmt, scale=0.5, p=0.1, seed=seed, name="rnd.sm")
+        check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, p=0.1, seed=seed, name="rnd.sm_bwd")
+    elif kind == "rmsnorm":
+        cpu = synth.layer_inputs(rows, cols, dtype, seed=seed,
+                                 names=("x", "residual", "gamma", "dy"))
+        d = {k: place(v, mis) for k, v in cpu.items()}
+        z, y, rstd = mb.add_rmsnorm_fwd(d["x"], d["gamma"], 1e-6, residual=d["residual"])
+        dz, dg = mb.add_rmsnorm_bwd(d["dy"], z, d["gamma"], rstd, dz_extra=d["residual"])
+        torch.cuda.synchronize()
+        check_rmsnorm_fwd(orc, d["x"], d["residual"], d["gamma"], z, y, rstd, fmt, 1e-6,
+                          name="rnd.rms")
+        check_rmsnorm_bwd(orc, d["dy"], d["residual"], z, d["gamma"], rstd, dz, dg, fmt,
+                          name="rnd.rms_bwd")
+    else:
+        ld = cols + int(np.random.default_rng([7, idx]).integers(0, 9))
+        x = place(synth.logits(rows, ld, dtype, seed=seed), mis)
+        lab = synth.class_labels(rows, cols, seed=seed, ignore_frac=0.05).to("cuda")
+        loss, dx = mb.cross_entropy_fwd_bwd(x, lab, cols=cols, label_smoothing=0.1,
+                                            grad_scale=0.25)
+        torch.cuda.synchronize()
+        check_xent(orc, x, lab, cols, 0.1, 0.25, loss, dx, fmt, name="rnd.xent")
