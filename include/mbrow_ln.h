@@ -82,6 +82,11 @@ typedef enum {
  * workgroup; GPT-2's 50257 and Llama-3's 128256 classes fit in bf16). */
 #define LN_MAX_COLS_XENT_F32 65536
 #define LN_MAX_COLS_XENT_16 131072
+/* Widest row of attn_softmax_fwd / attn_softmax_bwd / cross_entropy_fwd_bwd:
+ * rows wider than their register path (LN_MAX_COLS for the softmax,
+ * LN_MAX_COLS_XENT_* for the cross-entropy) take a two-pass path that reads
+ * the row twice. */
+#define LN_MAX_COLS_STREAM (1 << 24)
 
 /*
  * LayerNorm forward.  For each row r with m = cols:
@@ -242,7 +247,10 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
  *   NULL;  y [rows, cols] T output (may equal x);  y_dropped [rows, cols] T
  *   output or NULL (may equal x, not y).
  * scale must be finite; causal 0 or 1; p in [0, 1); rows_per_mask >= 1 when
- * mask is given.  Arithmetic in float32 (exp by the device's exp2).
+ * mask is given.  Arithmetic in float32 (exp by the device's exp2).  Rows of
+ * up to LN_MAX_COLS columns are held in registers (read once); wider rows, up
+ * to LN_MAX_COLS_STREAM, are read twice: an online maximum/sum pass
+ * ([LLMC] §6.1), then the output pass.
  */
 ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
                              void* y_dropped, int64_t rows, int64_t cols, float scale,
@@ -258,7 +266,8 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
  *   dy [rows, cols] T: gradient of y_dropped (of y when p = 0).
  *   y  [rows, cols] T: the forward's y.   dx [rows, cols] T output (may equal
  *   dy or y).  causal = 1 skips reading the keys past the query (y = 0
- *   there, so dx = 0).
+ *   there, so dx = 0).  Rows wider than LN_MAX_COLS (up to
+ *   LN_MAX_COLS_STREAM) read dy and y twice: the dot product, then dx.
  */
 ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
                              int64_t cols, float scale, int causal, float p, uint64_t seed,
@@ -341,9 +350,11 @@ ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
  *            place).  Its padding columns are written with 0.
  *   label_smoothing a in [0, 1];  grad_scale finite (e.g. 1/rows for a mean
  *            loss).
- * ld >= cols, else LN_ERR_SHAPE; ld above LN_MAX_COLS_XENT_F32 (fp32) or
- * LN_MAX_COLS_XENT_16 (fp16/bf16) is LN_ERR_UNSUPPORTED.  Arithmetic in
- * float32 (exp by the device's exp2).
+ * ld >= cols, else LN_ERR_SHAPE.  Rows of up to LN_MAX_COLS_XENT_F32 (fp32) or
+ * LN_MAX_COLS_XENT_16 (fp16/bf16) columns are held in registers and read
+ * once; wider rows, up to LN_MAX_COLS_STREAM (else LN_ERR_UNSUPPORTED), are
+ * read twice: an online maximum/sum pass, then the gradient pass.
+ * Arithmetic in float32 (exp by the device's exp2).
  */
 ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, float* loss,
                                   void* dlogits, int64_t rows, int64_t cols, int64_t ld,

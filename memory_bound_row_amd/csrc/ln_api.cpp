@@ -32,6 +32,29 @@ hipError_t launch_xent_f32(const Path&, const XeArgs&, hipStream_t);
 hipError_t launch_xent_f16(const Path&, const XeArgs&, hipStream_t);
 hipError_t launch_xent_bf16(const Path&, const XeArgs&, hipStream_t);
 
+hipError_t launch_softmax_stream_f32(bool, bool, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_stream_f16(bool, bool, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_stream_bf16(bool, bool, const SmArgs&, hipStream_t);
+hipError_t launch_xent_stream_f32(bool, const XeArgs&, hipStream_t);
+hipError_t launch_xent_stream_f16(bool, const XeArgs&, hipStream_t);
+hipError_t launch_xent_stream_bf16(bool, const XeArgs&, hipStream_t);
+
+hipError_t launch_softmax_stream(Dt dt, bool vec, bool backward, const SmArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_softmax_stream_f32(vec, backward, a, s);
+    case Dt::F16: return launch_softmax_stream_f16(vec, backward, a, s);
+    default: return launch_softmax_stream_bf16(vec, backward, a, s);
+    }
+}
+
+hipError_t launch_xent_stream(Dt dt, bool vec, const XeArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_xent_stream_f32(vec, a, s);
+    case Dt::F16: return launch_xent_stream_f16(vec, a, s);
+    default: return launch_xent_stream_bf16(vec, a, s);
+    }
+}
+
 hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s) {
     switch (dt) {
     case Dt::F32: return launch_xent_f32(p, a, s);
@@ -87,6 +110,9 @@ static bool have_instance(bool f32, int g, int v) {
 }
 
 static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0}, g_force_grid{0};
+
+// The test-only override that forces the per-element path (no vector access).
+bool force_scalar() { return g_force_scalar.load(std::memory_order_relaxed) != 0; }
 
 // Row layout: among the candidate layouts, the one with the fewest slots
 // (used or not); ties go to the earlier candidate.  With `wave_rows`, slots
@@ -300,6 +326,14 @@ ln_status_t check_shape(int64_t rows, int64_t cols, ln_dtype_t dt) {
 }
 
 ln_status_t from_hip(hipError_t e) { return e == hipSuccess ? LN_OK : LN_ERR_HIP; }
+
+// Shape check of the calls with a two-pass path for long rows.
+ln_status_t check_shape_stream(int64_t rows, int64_t cols, ln_dtype_t dt) {
+    if (!valid_dtype(dt)) return LN_ERR_DTYPE;
+    if (rows < 0 || cols <= 0) return LN_ERR_SHAPE;
+    if (cols > LN_MAX_COLS_STREAM || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
+    return LN_OK;
+}
 
 }  // namespace
 
@@ -605,8 +639,8 @@ ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, flo
     if (!logits || !labels || !loss) return LN_ERR_NULL;
     if (!valid_dtype(dt)) return LN_ERR_DTYPE;
     if (rows < 0 || cols <= 0 || ld < cols) return LN_ERR_SHAPE;
+    if (ld > LN_MAX_COLS_STREAM || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
     const int64_t max_ld = dt == LN_F32 ? LN_MAX_COLS_XENT_F32 : LN_MAX_COLS_XENT_16;
-    if (ld > max_ld || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
     if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f)) return LN_ERR_PARAM;
     if (!std::isfinite(grad_scale)) return LN_ERR_PARAM;
     if (rows == 0) return LN_OK;
@@ -629,6 +663,7 @@ ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, flo
     a.alpha = label_smoothing;
     a.inv_v = (float)(1.0 / (double)cols);
     a.scale = grad_scale;
+    if (ld > max_ld) return from_hip(launch_xent_stream(d, vec && !force_scalar(), a, stream));
     return from_hip(launch_xent(d, pick_xent_path(d, a.nslots, vec), a, stream));
 }
 
@@ -637,7 +672,7 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
                              int causal, float p, uint64_t seed, ln_dtype_t dt,
                              hipStream_t stream) {
     if (!x || !y) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape_stream(rows, cols, dt);
     if (st != LN_OK) return st;
     if (!std::isfinite(scale) || (causal != 0 && causal != 1)) return LN_ERR_PARAM;
     if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
@@ -665,6 +700,8 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
     a.pscale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
+    if (cols > LN_MAX_COLS)
+        return from_hip(launch_softmax_stream(d, vec && !force_scalar(), false, a, stream));
     return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec), false, a, stream));
 }
 
@@ -672,7 +709,7 @@ ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t ro
                              int64_t cols, float scale, int causal, float p, uint64_t seed,
                              ln_dtype_t dt, hipStream_t stream) {
     if (!dy || !y || !dx) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape_stream(rows, cols, dt);
     if (st != LN_OK) return st;
     if (!std::isfinite(scale) || (causal != 0 && causal != 1)) return LN_ERR_PARAM;
     if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
@@ -698,6 +735,8 @@ ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t ro
     a.pscale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
+    if (cols > LN_MAX_COLS)
+        return from_hip(launch_softmax_stream(d, vec && !force_scalar(), true, a, stream));
     return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec), true, a, stream));
 }
 

@@ -195,6 +195,11 @@ struct XeArgs {
 Path pick_xent_path(Dt dt, int64_t slots, bool vec);
 hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s);
 
+// Rows too long for the register layouts: one workgroup per row, two passes
+// over the row (stream.hip).
+hipError_t launch_softmax_stream(Dt dt, bool vec, bool backward, const SmArgs& a, hipStream_t s);
+hipError_t launch_xent_stream(Dt dt, bool vec, const XeArgs& a, hipStream_t s);
+
 // Fold of [P][kinds][m] partials (kinds = 1, 2 or 3) into out[0..kinds-1].
 struct FoldOut {
     float* p[3];

@@ -1,0 +1,383 @@
+// stream.hip -- attention softmax (forward, backward) and cross-entropy over
+// rows too long to hold in one workgroup's registers, for gfx950.  Compiled
+// once per storage type (-DMBROW_DT=0 fp32, 1 fp16, 2 bf16).
+//
+// One workgroup of 1024 lanes per row walks the row in chunks of 64 KB
+// (four 16-byte slots per lane) twice.  Pass A reduces: the online softmax
+// state of "02 · llmc/ 的 CUDA kernel 层" §6.1 (a running maximum and a sum of
+// exp(x - max) rescaled when the maximum grows, plus sum x for the
+// cross-entropy), or the dot product sum g * y of the softmax backward
+// ("Accelerating Transformer on GPU (II)" §3).  The lanes' states are merged
+// in a fixed order (one butterfly per wave, then the waves in order through
+// LDS).  Pass B re-reads the row and writes the output exactly as the
+// register kernels do (the same mask words, exp2 form and dropout).  Cost:
+// the row is read twice (the backward reads dy and y twice), against once for
+// rows that fit in registers.
+#include "ln_device.hpp"
+#include "ln_launch.hpp"
+#include "online_softmax.hpp"
+
+#ifndef MBROW_DT
+#error "compile with -DMBROW_DT=0|1|2"
+#endif
+
+namespace mbrow {
+
+#if MBROW_DT == 0
+using St = StF32;
+#define MBROW_SUFFIX f32
+#elif MBROW_DT == 1
+using St = StF16;
+#define MBROW_SUFFIX f16
+#else
+using St = StBF16;
+#define MBROW_SUFFIX bf16
+#endif
+
+constexpr int kSnt = 1024;            // lanes per row (one workgroup)
+constexpr int kSu = 4;                // 16-byte slots per lane per chunk
+constexpr int kSnw = kSnt / 64;       // waves per row
+constexpr int kSchunk = kSnt * kSu;   // slots per chunk
+
+// Merge of the row's lane states: a butterfly per wave, then the waves in
+// order through LDS.  Every lane gets the row's state.
+__device__ inline XeState row_merge(XeState st, XeState* lds) {
+    st = xe_group<64>(st);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[w] = st;
+    __syncthreads();
+    XeState r = lds[0];
+#pragma unroll
+    for (int k = 1; k < kSnw; ++k) r = xe_merge(r, lds[k]);
+    __syncthreads();   // the next row reuses lds
+    return r;
+}
+__device__ inline float row_sum(float v, float* lds) {
+    v = group_sum<64>(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[w] = v;
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int k = 1; k < kSnw; ++k) r = r + lds[k];
+    __syncthreads();
+    return r;
+}
+
+// One chunk of a row: slot k of this lane is s = chunk*kSchunk + k*kSnt +
+// lane (a wave covers 1 KB contiguous per k).  Slots at or past `nslot` read
+// 0; on the per-element path, columns at or past `lim` read 0.
+template <class S, bool VEC>
+__device__ inline void load_chunk(rsrc_t v, int64_t chunk, int nslot, int lim, u32x4 (&out)[kSu]) {
+    constexpr int E = S::E;
+#pragma unroll
+    for (int k = 0; k < kSu; ++k) {
+        const int s = (int)(chunk * kSchunk) + k * kSnt + (int)threadIdx.x;
+        if constexpr (VEC) {
+            out[k] = buf_load_nt(v, s < nslot ? (uint32_t)s * 16u : kOob);
+        } else {
+            float f[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int col = s * E + e;
+                f[e] = elem_load<S>(v, col < lim ? (uint32_t)col * S::BYTES : kOob);
+            }
+            out[k] = S::pack(f);
+            hold_packed(out[k]);   // one slot of element loads in flight at a time
+        }
+    }
+}
+template <class S, bool VEC>
+__device__ inline void store_slot(rsrc_t v, int s, int nslot, int lim, const float* f) {
+    constexpr int E = S::E;
+    if constexpr (VEC) {
+        buf_store_nt(S::pack(f), v, s < nslot ? (uint32_t)s * 16u : kOob);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int col = s * E + e;
+            elem_store<S>(v, col < lim ? (uint32_t)col * S::BYTES : kOob, f[e]);
+        }
+    }
+}
+
+// Online update of a lane's (max, sum of exp(x - max)) by a chunk whose
+// values in play have maximum cm: rescale the sum when the maximum grows.
+__device__ inline void rescale(XeState& st, float cm) {
+    if (cm > st.mx) {
+        if (st.mx != -INFINITY) st.z = st.z * exp2_((st.mx - cm) * kLog2e);
+        st.mx = cm;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Softmax forward: y = softmax(scale * x + mask, causal), optional dropped y.
+// ---------------------------------------------------------------------------
+template <class S, bool VEC>
+__global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
+    constexpr int E = S::E;
+    __shared__ XeState lds[kSnw];
+    const int m = (int)a.m;
+    const int ns = (int)a.nslots;
+    const bool has_mask = a.mask != nullptr;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const rsrc_t vx = row_view<S>(a.x, row, 1, m);
+        const rsrc_t vm = has_mask ? row_view<S>(a.mask, row / a.rows_per_mask, 1, m) : vx;
+        // columns in play: all, or up to the query under the causal mask
+        const int lim = a.causal ? (int)(row % m) + 1 : m;
+        const int nlive = (lim + E - 1) / E;                       // slots in play
+        const int64_t clive = (nlive + kSchunk - 1) / kSchunk;      // chunks in play
+        const int64_t call = (ns + kSchunk - 1) / kSchunk;
+        auto scores = [&](int64_t c, float (&t)[kSu][E]) {
+            u32x4 xr[kSu], mr[kSu];
+            load_chunk<S, VEC>(vx, c, nlive, lim, xr);
+            if (has_mask) load_chunk<S, VEC>(vm, c, nlive, lim, mr);
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
+                float xv[E], mv[E];
+                S::unpack(xr[k], xv);
+                if (has_mask) S::unpack(mr[k], mv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float v = a.scale * xv[e];
+                    if (has_mask) v = v + mv[e];
+                    t[k][e] = s * E + e < lim ? v : -INFINITY;
+                }
+            }
+        };
+        XeState st{-INFINITY, 0.0f, 0.0f};
+        for (int64_t c = 0; c < clive; ++c) {
+            float t[kSu][E];
+            scores(c, t);
+            float cm = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kSu; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) cm = fmaxf(cm, t[k][e]);
+            rescale(st, cm);
+            const float nm = st.mx == -INFINITY ? 0.0f : -st.mx * kLog2e;
+#pragma unroll
+            for (int k = 0; k < kSu; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) st.z += exp2_(fmaf(t[k][e], kLog2e, nm));
+        }
+        st = row_merge(st, lds);
+        const bool live_row = st.mx != -INFINITY;
+        const float nm = live_row ? -st.mx * kLog2e : 0.0f;
+        const float inv = live_row ? 1.0f / st.z : 0.0f;
+        const float inv_kept = inv * a.pscale;
+        const rsrc_t vy = row_view<S>(a.out, row, 1, m);
+        const rsrc_t vd = row_view<S>(a.out2 ? a.out2 : a.out, row, 1, m);
+        for (int64_t c = 0; c < call; ++c) {
+            float t[kSu][E];
+            if (c < clive) {
+                scores(c, t);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kSu; ++k)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) t[k][e] = -INFINITY;   // past the query: y = 0
+            }
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
+                float yv[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    t[k][e] = exp2_(fmaf(t[k][e], kLog2e, nm));
+                    yv[e] = t[k][e] * inv;
+                }
+                store_slot<S, VEC>(vy, s, ns, m, yv);
+                if (a.out2) {
+                    const u32x4 w = dropout_words(row, s * E, a.seed_lo, a.seed_hi, a.thr);
+                    float dv[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        dv[e] = kept<E>(w, s * E, e, a.thr) ? t[k][e] * inv_kept : 0.0f;
+                    store_slot<S, VEC>(vd, s, ns, m, dv);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Softmax backward: g = keep ? dy / (1 - p) : 0, s = sum g * y,
+// dx = scale * y * (g - s).
+// ---------------------------------------------------------------------------
+template <class S, bool VEC>
+__global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
+    constexpr int E = S::E;
+    __shared__ float lds[kSnw];
+    const int m = (int)a.m;
+    const int ns = (int)a.nslots;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const rsrc_t vdy = row_view<S>(a.x, row, 1, m);
+        const rsrc_t vyy = row_view<S>(a.y, row, 1, m);
+        const int lim = a.causal ? (int)(row % m) + 1 : m;   // y = 0 past the query
+        const int nlive = (lim + E - 1) / E;
+        const int64_t clive = (nlive + kSchunk - 1) / kSchunk;
+        const int64_t call = (ns + kSchunk - 1) / kSchunk;
+        // g and y of one chunk
+        auto grads = [&](int64_t c, float (&g)[kSu][E], float (&y)[kSu][E]) {
+            u32x4 dr[kSu], yr[kSu];
+            load_chunk<S, VEC>(vdy, c, nlive, lim, dr);
+            load_chunk<S, VEC>(vyy, c, nlive, lim, yr);
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
+                const u32x4 w = dropout_words(row, s * E, a.seed_lo, a.seed_hi, a.thr);
+                float dv[E];
+                S::unpack(dr[k], dv);
+                S::unpack(yr[k], y[k]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const bool in = s * E + e < lim;
+                    g[k][e] = (in && kept<E>(w, s * E, e, a.thr)) ? dv[e] * a.pscale : 0.0f;
+                    if (!in) y[k][e] = 0.0f;
+                }
+            }
+        };
+        float sum = 0.0f;
+        for (int64_t c = 0; c < clive; ++c) {
+            float g[kSu][E], y[kSu][E];
+            grads(c, g, y);
+#pragma unroll
+            for (int k = 0; k < kSu; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) sum = fmaf(g[k][e], y[k][e], sum);
+        }
+        sum = row_sum(sum, lds);
+        const rsrc_t vdx = row_view<S>(a.out, row, 1, m);
+        for (int64_t c = 0; c < call; ++c) {
+            float g[kSu][E], y[kSu][E];
+            if (c < clive) {
+                grads(c, g, y);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kSu; ++k)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) g[k][e] = y[k][e] = 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
+                float dx[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) dx[e] = a.scale * (y[k][e] * (g[k][e] - sum));
+                store_slot<S, VEC>(vdx, s, ns, m, dx);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-entropy with label smoothing: loss and dx = scale * (q - p).
+// ---------------------------------------------------------------------------
+template <class S, bool VEC>
+__global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
+    constexpr int E = S::E;
+    __shared__ XeState lds[kSnw];
+    const int cols = (int)a.cols;
+    const int ld = (int)a.ld;
+    const int nv = (int)a.nvalid;
+    const int ns = (int)a.nslots;
+    const int64_t cv = (nv + kSchunk - 1) / kSchunk;
+    const int64_t call = (ns + kSchunk - 1) / kSchunk;
+    const float alpha = a.alpha;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const rsrc_t vx = row_view<S>(a.x, row, 1, ld);
+        const int64_t label = a.labels[row];
+        const bool ignored = label < 0;
+        const bool bad = label >= cols;
+        const bool no_target = ignored || bad;
+        const float xl = no_target ? 0.0f : elem_load<S>(vx, (uint32_t)label * S::BYTES);
+        XeState st{-INFINITY, 0.0f, 0.0f};
+        for (int64_t c = 0; c < cv; ++c) {
+            u32x4 xr[kSu];
+            load_chunk<S, VEC>(vx, c, nv, cols, xr);
+            float cm = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
+                float f[E];
+                S::unpack(xr[k], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const bool in = s * E + e < cols;
+                    cm = fmaxf(cm, in ? f[e] : -INFINITY);
+                    st.sx += in ? f[e] : 0.0f;
+                }
+            }
+            rescale(st, cm);
+            const float nm = st.mx == -INFINITY ? 0.0f : -st.mx * kLog2e;
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
+                float f[E];
+                S::unpack(xr[k], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    st.z += s * E + e < cols ? exp2_(fmaf(f[e], kLog2e, nm)) : 0.0f;
+            }
+        }
+        st = row_merge(st, lds);
+        if (threadIdx.x == 0) {
+            const float l = logf(st.z) + (1.0f - alpha) * (st.mx - xl) +
+                            alpha * (st.mx - st.sx * a.inv_v);
+            a.loss[row] = ignored ? 0.0f : (bad ? NAN : l);
+        }
+        if (a.dx == nullptr) continue;   // uniform
+        const float nm = -st.mx * kLog2e;
+        const float siz = a.scale * (1.0f / st.z);
+        const float pa = alpha * a.inv_v;
+        const float nsp = -(a.scale * pa);
+        const float nsl = -(a.scale * (pa + (1.0f - alpha)));
+        const float fill = ignored ? 0.0f : NAN;
+        const rsrc_t vd = row_view<S>(a.dx, row, 1, ld);
+        for (int64_t c = 0; c < call; ++c) {
+            u32x4 xr[kSu];
+            load_chunk<S, VEC>(vx, c, nv, cols, xr);
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
+                float f[E], out[E];
+                S::unpack(xr[k], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int col = s * E + e;
+                    const float q = exp2_(fmaf(f[e], kLog2e, nm));
+                    float d = fmaf(q, siz, col == label ? nsl : nsp);
+                    if (no_target) d = fill;
+                    out[e] = col < cols ? d : 0.0f;   // padding columns get 0
+                }
+                store_slot<S, VEC>(vd, s, ns, ld, out);
+            }
+        }
+    }
+}
+
+template <class K, class A>
+static hipError_t launch_rows(K kernel, const A& a, hipStream_t s) {
+    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kernel), kSnt, a.rows);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kSnt), 0, s, a);
+    return hipGetLastError();
+}
+
+#define MBROW_CAT2(a, b) a##b
+#define MBROW_CAT(a, b) MBROW_CAT2(a, b)
+hipError_t MBROW_CAT(launch_softmax_stream_, MBROW_SUFFIX)(bool vec, bool backward,
+                                                           const SmArgs& a, hipStream_t s) {
+    if (backward)
+        return vec ? launch_rows(softmax_stream_bwd<St, true>, a, s)
+                   : launch_rows(softmax_stream_bwd<St, false>, a, s);
+    return vec ? launch_rows(softmax_stream_fwd<St, true>, a, s)
+               : launch_rows(softmax_stream_fwd<St, false>, a, s);
+}
+hipError_t MBROW_CAT(launch_xent_stream_, MBROW_SUFFIX)(bool vec, const XeArgs& a,
+                                                        hipStream_t s) {
+    return vec ? launch_rows(xent_stream<St, true>, a, s) : launch_rows(xent_stream<St, false>, a, s);
+}
+
+}  // namespace mbrow

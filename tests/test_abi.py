@@ -18,6 +18,7 @@ F32, F16, BF16 = 0, 1, 2
 
 # fake but non-NULL device addresses: validation never dereferences them
 A, B, C, D, E, F, G, H, I, J, K, M = (0x10000000 * k for k in range(1, 13))
+STREAM_MAX = 1 << 24   # LN_MAX_COLS_STREAM
 
 
 @pytest.fixture(scope="module")
@@ -227,7 +228,8 @@ def test_softmax_validation(L):
     assert sm_fwd(L, rows=-1) == LN_ERR_SHAPE
     assert sm_fwd(L, cols=0) == LN_ERR_SHAPE
     assert sm_fwd(L, dt=4) == LN_ERR_DTYPE
-    assert sm_fwd(L, cols=16385) == LN_ERR_UNSUPPORTED
+    assert sm_fwd(L, cols=STREAM_MAX + 1) == LN_ERR_UNSUPPORTED
+    assert sm_fwd(L, cols=16385, rows=0) == LN_OK                 # long rows: two-pass path
     for kw in ({"scale": float("inf")}, {"scale": float("nan")}, {"causal": 2},
                {"p": 1.0}, {"p": -0.5}, {"mask": C, "rpm": 0}):
         assert sm_fwd(L, **kw) == LN_ERR_PARAM, kw
@@ -242,7 +244,8 @@ def test_softmax_validation(L):
     assert sm_bwd(L, dx=B + 4) == LN_ERR_UNSUPPORTED
     assert sm_bwd(L, scale=float("inf")) == LN_ERR_PARAM
     assert sm_bwd(L, p=1.0) == LN_ERR_PARAM
-    assert sm_bwd(L, cols=16385) == LN_ERR_UNSUPPORTED
+    assert sm_bwd(L, cols=STREAM_MAX + 1) == LN_ERR_UNSUPPORTED
+    assert sm_bwd(L, cols=STREAM_MAX, rows=0) == LN_OK
 
 
 
@@ -311,11 +314,13 @@ def test_cross_entropy_validation(L):
     assert xent(L, cols=9, ld=8) == LN_ERR_SHAPE                # ld < cols
     assert xent(L, dt=3) == LN_ERR_DTYPE
     assert xent(L, cols=65536, ld=65536, rows=0, dt=F32) == LN_OK
-    assert xent(L, cols=65537, ld=65537, dt=F32) == LN_ERR_UNSUPPORTED
-    assert xent(L, cols=100, ld=65537, dt=F32) == LN_ERR_UNSUPPORTED
+    assert xent(L, cols=65537, ld=65537, rows=0, dt=F32) == LN_OK     # two-pass path
+    assert xent(L, cols=STREAM_MAX + 1, ld=STREAM_MAX + 1, dt=F32) == LN_ERR_UNSUPPORTED
+    assert xent(L, cols=100, ld=STREAM_MAX + 1, dt=F32) == LN_ERR_UNSUPPORTED
     for dt in (F16, BF16):
         assert xent(L, cols=131072, ld=131072, rows=0, dt=dt) == LN_OK
-        assert xent(L, cols=131073, ld=131073, dt=dt) == LN_ERR_UNSUPPORTED
+        assert xent(L, cols=131073, ld=131073, rows=0, dt=dt) == LN_OK
+        assert xent(L, cols=STREAM_MAX + 1, ld=STREAM_MAX + 1, dt=dt) == LN_ERR_UNSUPPORTED
     for kw in ({"alpha": -0.1}, {"alpha": 1.5}, {"alpha": float("nan")},
                {"scale": float("inf")}, {"scale": float("nan")}):
         assert xent(L, **kw) == LN_ERR_PARAM, kw
