@@ -66,15 +66,19 @@ __device__ inline float row_sum(float v, float* lds) {
 
 // One chunk of a row: slot k of this lane is s = chunk*kSchunk + k*kSnt +
 // lane (a wave covers 1 KB contiguous per k).  Slots at or past `nslot` read
-// 0; on the per-element path, columns at or past `lim` read 0.
-template <class S, bool VEC>
+// 0; on the per-element path, columns at or past `lim` read 0.  The first
+// pass reads through the caches (LAST = false) so that the second pass, the
+// row's last use, finds it in the 256 MB Infinity Cache; the second pass
+// reads nontemporally.
+template <class S, bool VEC, bool LAST>
 __device__ inline void load_chunk(rsrc_t v, int64_t chunk, int nslot, int lim, u32x4 (&out)[kSu]) {
     constexpr int E = S::E;
 #pragma unroll
     for (int k = 0; k < kSu; ++k) {
         const int s = (int)(chunk * kSchunk) + k * kSnt + (int)threadIdx.x;
         if constexpr (VEC) {
-            out[k] = buf_load_nt(v, s < nslot ? (uint32_t)s * 16u : kOob);
+            const uint32_t off = s < nslot ? (uint32_t)s * 16u : kOob;
+            out[k] = LAST ? buf_load_nt(v, off) : buf_load(v, off);
         } else {
             float f[E];
 #pragma unroll
@@ -128,10 +132,10 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         const int nlive = (lim + E - 1) / E;                       // slots in play
         const int64_t clive = (nlive + kSchunk - 1) / kSchunk;      // chunks in play
         const int64_t call = (ns + kSchunk - 1) / kSchunk;
-        auto scores = [&](int64_t c, float (&t)[kSu][E]) {
+        auto scores = [&](int64_t c, float (&t)[kSu][E], auto last) {
             u32x4 xr[kSu], mr[kSu];
-            load_chunk<S, VEC>(vx, c, nlive, lim, xr);
-            if (has_mask) load_chunk<S, VEC>(vm, c, nlive, lim, mr);
+            load_chunk<S, VEC, decltype(last)::value>(vx, c, nlive, lim, xr);
+            if (has_mask) load_chunk<S, VEC, false>(vm, c, nlive, lim, mr);
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         XeState st{-INFINITY, 0.0f, 0.0f};
         for (int64_t c = 0; c < clive; ++c) {
             float t[kSu][E];
-            scores(c, t);
+            scores(c, t, std::false_type{});
             float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSu; ++k)
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         for (int64_t c = 0; c < call; ++c) {
             float t[kSu][E];
             if (c < clive) {
-                scores(c, t);
+                scores(c, t, std::true_type{});
             } else {
 #pragma unroll
                 for (int k = 0; k < kSu; ++k)
@@ -220,10 +224,10 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         const int64_t clive = (nlive + kSchunk - 1) / kSchunk;
         const int64_t call = (ns + kSchunk - 1) / kSchunk;
         // g and y of one chunk
-        auto grads = [&](int64_t c, float (&g)[kSu][E], float (&y)[kSu][E]) {
+        auto grads = [&](int64_t c, float (&g)[kSu][E], float (&y)[kSu][E], auto last) {
             u32x4 dr[kSu], yr[kSu];
-            load_chunk<S, VEC>(vdy, c, nlive, lim, dr);
-            load_chunk<S, VEC>(vyy, c, nlive, lim, yr);
+            load_chunk<S, VEC, decltype(last)::value>(vdy, c, nlive, lim, dr);
+            load_chunk<S, VEC, decltype(last)::value>(vyy, c, nlive, lim, yr);
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         float sum = 0.0f;
         for (int64_t c = 0; c < clive; ++c) {
             float g[kSu][E], y[kSu][E];
-            grads(c, g, y);
+            grads(c, g, y, std::false_type{});
 #pragma unroll
             for (int k = 0; k < kSu; ++k)
 #pragma unroll
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         for (int64_t c = 0; c < call; ++c) {
             float g[kSu][E], y[kSu][E];
             if (c < clive) {
-                grads(c, g, y);
+                grads(c, g, y, std::true_type{});
             } else {
 #pragma unroll
                 for (int k = 0; k < kSu; ++k)
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         XeState st{-INFINITY, 0.0f, 0.0f};
         for (int64_t c = 0; c < cv; ++c) {
             u32x4 xr[kSu];
-            load_chunk<S, VEC>(vx, c, nv, cols, xr);
+            load_chunk<S, VEC, false>(vx, c, nv, cols, xr);
             float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         const rsrc_t vd = row_view<S>(a.dx, row, 1, ld);
         for (int64_t c = 0; c < call; ++c) {
             u32x4 xr[kSu];
-            load_chunk<S, VEC>(vx, c, nv, cols, xr);
+            load_chunk<S, VEC, true>(vx, c, nv, cols, xr);
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
