@@ -35,9 +35,11 @@ using St = StBF16;
 #endif
 
 constexpr int kSnt = 1024;            // lanes per row (one workgroup)
-constexpr int kSu = 4;                // 16-byte slots per lane per chunk
 constexpr int kSnw = kSnt / 64;       // waves per row
-constexpr int kSchunk = kSnt * kSu;   // slots per chunk
+// 16-byte slots per lane per chunk: four when one tensor is walked, two when
+// two are (the next chunk is in flight as well, in 128 registers per lane)
+constexpr int kSu1 = 4;
+constexpr int kSu2 = 2;
 
 // Merge of the row's lane states: a butterfly per wave, then the waves in
 // order through LDS.  Every lane gets the row's state.
@@ -64,18 +66,18 @@ __device__ inline float row_sum(float v, float* lds) {
     return r;
 }
 
-// One chunk of a row: slot k of this lane is s = chunk*kSchunk + k*kSnt +
+// One chunk of a row: slot k of this lane is s = chunk*kSnt*U + k*kSnt +
 // lane (a wave covers 1 KB contiguous per k).  Slots at or past `nslot` read
 // 0; on the per-element path, columns at or past `lim` read 0.  The first
 // pass reads through the caches (LAST = false) so that the second pass, the
 // row's last use, finds it in the 256 MB Infinity Cache; the second pass
 // reads nontemporally.
-template <class S, bool VEC, bool LAST>
-__device__ inline void load_chunk(rsrc_t v, int64_t chunk, int nslot, int lim, u32x4 (&out)[kSu]) {
+template <class S, bool VEC, bool LAST, int U>
+__device__ inline void load_chunk(rsrc_t v, int64_t chunk, int nslot, int lim, u32x4 (&out)[U]) {
     constexpr int E = S::E;
 #pragma unroll
-    for (int k = 0; k < kSu; ++k) {
-        const int s = (int)(chunk * kSchunk) + k * kSnt + (int)threadIdx.x;
+    for (int k = 0; k < U; ++k) {
+        const int s = (int)(chunk * (kSnt * U)) + k * kSnt + (int)threadIdx.x;
         if constexpr (VEC) {
             const uint32_t off = s < nslot ? (uint32_t)s * 16u : kOob;
             out[k] = LAST ? buf_load_nt(v, off) : buf_load(v, off);
@@ -114,46 +116,96 @@ __device__ inline void rescale(XeState& st, float cm) {
     }
 }
 
+// Walk chunks [0, n) with the next chunk's loads in flight while one is used
+// (two register buffers, used alternately).  A chunk at or past the end
+// reads nothing (its slots are outside the row's view), so the prefetch is
+// unconditional: a conditional one would make the wait for the current
+// chunk also wait for it, since loads retire in order.
+// (The per-element path, PREFETCH = false, has no registers for a second
+// buffer and walks the chunks one at a time.)
+template <class B, bool PREFETCH, class Fetch, class Use>
+__device__ inline void pipelined(int64_t n, Fetch&& fetch, Use&& use) {
+    if constexpr (PREFETCH) {
+        B b0, b1;
+        fetch(int64_t(0), b0);
+        for (int64_t c = 0; c < n; c += 2) {
+            fetch(c + 1, b1);
+            use(c, b0);
+            if (c + 1 >= n) break;
+            fetch(c + 2, b0);
+            use(c + 1, b1);
+        }
+    } else {
+        B b;
+        for (int64_t c = 0; c < n; ++c) {
+            fetch(c, b);
+            use(c, b);
+        }
+    }
+}
+
+template <bool MASK>
+struct SmChunk {
+    static constexpr int U = MASK ? kSu2 : kSu1;
+    u32x4 x[U];
+    u32x4 m[MASK ? U : 1];
+};
+struct DyChunk {
+    static constexpr int U = kSu2;
+    u32x4 d[U];
+    u32x4 y[U];
+};
+struct XChunk {
+    static constexpr int U = kSu1;
+    u32x4 x[U];
+};
+
 // ---------------------------------------------------------------------------
 // Softmax forward: y = softmax(scale * x + mask, causal), optional dropped y.
 // ---------------------------------------------------------------------------
-template <class S, bool VEC>
+template <class S, bool VEC, bool MASK>
 __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
     constexpr int E = S::E;
+    constexpr int kSu = SmChunk<MASK>::U;
+    constexpr int kSchunk = kSnt * kSu;
     __shared__ XeState lds[kSnw];
     const int m = (int)a.m;
     const int ns = (int)a.nslots;
-    const bool has_mask = a.mask != nullptr;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const rsrc_t vx = row_view<S>(a.x, row, 1, m);
-        const rsrc_t vm = has_mask ? row_view<S>(a.mask, row / a.rows_per_mask, 1, m) : vx;
+        const rsrc_t vm = MASK ? row_view<S>(a.mask, row / a.rows_per_mask, 1, m) : vx;
         // columns in play: all, or up to the query under the causal mask
         const int lim = a.causal ? (int)(row % m) + 1 : m;
         const int nlive = (lim + E - 1) / E;                       // slots in play
         const int64_t clive = (nlive + kSchunk - 1) / kSchunk;      // chunks in play
         const int64_t call = (ns + kSchunk - 1) / kSchunk;
-        auto scores = [&](int64_t c, float (&t)[kSu][E], auto last) {
-            u32x4 xr[kSu], mr[kSu];
-            load_chunk<S, VEC, decltype(last)::value>(vx, c, nlive, lim, xr);
-            if (has_mask) load_chunk<S, VEC, false>(vm, c, nlive, lim, mr);
+        auto fetch = [&](auto last) {
+            return [&, last](int64_t c, SmChunk<MASK>& b) {
+                load_chunk<S, VEC, decltype(last)::value, kSu>(vx, c, nlive, lim, b.x);
+                if constexpr (MASK) load_chunk<S, VEC, false, kSu>(vm, c, nlive, lim, b.m);
+            };
+        };
+        // scaled, masked scores of a chunk (-inf outside the columns in play)
+        auto scores = [&](int64_t c, const SmChunk<MASK>& b, float (&t)[kSu][E]) {
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
                 float xv[E], mv[E];
-                S::unpack(xr[k], xv);
-                if (has_mask) S::unpack(mr[k], mv);
+                S::unpack(b.x[k], xv);
+                if constexpr (MASK) S::unpack(b.m[k], mv);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     float v = a.scale * xv[e];
-                    if (has_mask) v = v + mv[e];
+                    if constexpr (MASK) v = v + mv[e];
                     t[k][e] = s * E + e < lim ? v : -INFINITY;
                 }
             }
         };
         XeState st{-INFINITY, 0.0f, 0.0f};
-        for (int64_t c = 0; c < clive; ++c) {
+        pipelined<SmChunk<MASK>, VEC>(clive, fetch(std::false_type{}),
+                                 [&](int64_t c, const SmChunk<MASK>& b) {
             float t[kSu][E];
-            scores(c, t, std::false_type{});
+            scores(c, b, t);
             float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSu; ++k)
@@ -165,7 +217,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
             for (int k = 0; k < kSu; ++k)
 #pragma unroll
                 for (int e = 0; e < E; ++e) st.z += exp2_(fmaf(t[k][e], kLog2e, nm));
-        }
+        });
         st = row_merge(st, lds);
         const bool live_row = st.mx != -INFINITY;
         const float nm = live_row ? -st.mx * kLog2e : 0.0f;
@@ -173,16 +225,12 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         const float inv_kept = inv * a.pscale;
         const rsrc_t vy = row_view<S>(a.out, row, 1, m);
         const rsrc_t vd = row_view<S>(a.out2 ? a.out2 : a.out, row, 1, m);
-        for (int64_t c = 0; c < call; ++c) {
+        // every chunk of the row is written; chunks past the query read
+        // nothing and give y = 0
+        pipelined<SmChunk<MASK>, VEC>(call, fetch(std::true_type{}),
+                                 [&](int64_t c, const SmChunk<MASK>& b) {
             float t[kSu][E];
-            if (c < clive) {
-                scores(c, t, std::true_type{});
-            } else {
-#pragma unroll
-                for (int k = 0; k < kSu; ++k)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) t[k][e] = -INFINITY;   // past the query: y = 0
-            }
+            scores(c, b, t);
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
@@ -202,7 +250,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
                     store_slot<S, VEC>(vd, s, ns, m, dv);
                 }
             }
-        }
+        });
     }
 }
 
@@ -213,6 +261,8 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
 template <class S, bool VEC>
 __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
     constexpr int E = S::E;
+    constexpr int kSu = DyChunk::U;
+    constexpr int kSchunk = kSnt * kSu;
     __shared__ float lds[kSnw];
     const int m = (int)a.m;
     const int ns = (int)a.nslots;
@@ -223,18 +273,21 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         const int nlive = (lim + E - 1) / E;
         const int64_t clive = (nlive + kSchunk - 1) / kSchunk;
         const int64_t call = (ns + kSchunk - 1) / kSchunk;
-        // g and y of one chunk
-        auto grads = [&](int64_t c, float (&g)[kSu][E], float (&y)[kSu][E], auto last) {
-            u32x4 dr[kSu], yr[kSu];
-            load_chunk<S, VEC, decltype(last)::value>(vdy, c, nlive, lim, dr);
-            load_chunk<S, VEC, decltype(last)::value>(vyy, c, nlive, lim, yr);
+        auto fetch = [&](auto last) {
+            return [&, last](int64_t c, DyChunk& b) {
+                load_chunk<S, VEC, decltype(last)::value, kSu>(vdy, c, nlive, lim, b.d);
+                load_chunk<S, VEC, decltype(last)::value, kSu>(vyy, c, nlive, lim, b.y);
+            };
+        };
+        // g and y of one chunk (0 outside the columns in play)
+        auto grads = [&](int64_t c, const DyChunk& b, float (&g)[kSu][E], float (&y)[kSu][E]) {
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
                 const u32x4 w = dropout_words(row, s * E, a.seed_lo, a.seed_hi, a.thr);
                 float dv[E];
-                S::unpack(dr[k], dv);
-                S::unpack(yr[k], y[k]);
+                S::unpack(b.d[k], dv);
+                S::unpack(b.y[k], y[k]);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const bool in = s * E + e < lim;
@@ -244,26 +297,19 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
             }
         };
         float sum = 0.0f;
-        for (int64_t c = 0; c < clive; ++c) {
+        pipelined<DyChunk, VEC>(clive, fetch(std::false_type{}), [&](int64_t c, const DyChunk& b) {
             float g[kSu][E], y[kSu][E];
-            grads(c, g, y, std::false_type{});
+            grads(c, b, g, y);
 #pragma unroll
             for (int k = 0; k < kSu; ++k)
 #pragma unroll
                 for (int e = 0; e < E; ++e) sum = fmaf(g[k][e], y[k][e], sum);
-        }
+        });
         sum = row_sum(sum, lds);
         const rsrc_t vdx = row_view<S>(a.out, row, 1, m);
-        for (int64_t c = 0; c < call; ++c) {
+        pipelined<DyChunk, VEC>(call, fetch(std::true_type{}), [&](int64_t c, const DyChunk& b) {
             float g[kSu][E], y[kSu][E];
-            if (c < clive) {
-                grads(c, g, y, std::true_type{});
-            } else {
-#pragma unroll
-                for (int k = 0; k < kSu; ++k)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) g[k][e] = y[k][e] = 0.0f;
-            }
+            grads(c, b, g, y);
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
@@ -272,7 +318,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
                 for (int e = 0; e < E; ++e) dx[e] = a.scale * (y[k][e] * (g[k][e] - sum));
                 store_slot<S, VEC>(vdx, s, ns, m, dx);
             }
-        }
+        });
     }
 }
 
@@ -282,6 +328,8 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
 template <class S, bool VEC>
 __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
     constexpr int E = S::E;
+    constexpr int kSu = XChunk::U;
+    constexpr int kSchunk = kSnt * kSu;
     __shared__ XeState lds[kSnw];
     const int cols = (int)a.cols;
     const int ld = (int)a.ld;
@@ -297,16 +345,19 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         const bool bad = label >= cols;
         const bool no_target = ignored || bad;
         const float xl = no_target ? 0.0f : elem_load<S>(vx, (uint32_t)label * S::BYTES);
+        auto fetch = [&](auto last) {
+            return [&, last](int64_t c, XChunk& b) {
+                load_chunk<S, VEC, decltype(last)::value, kSu>(vx, c, nv, cols, b.x);
+            };
+        };
         XeState st{-INFINITY, 0.0f, 0.0f};
-        for (int64_t c = 0; c < cv; ++c) {
-            u32x4 xr[kSu];
-            load_chunk<S, VEC, false>(vx, c, nv, cols, xr);
+        pipelined<XChunk, VEC>(cv, fetch(std::false_type{}), [&](int64_t c, const XChunk& b) {
             float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
                 float f[E];
-                S::unpack(xr[k], f);
+                S::unpack(b.x[k], f);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const bool in = s * E + e < cols;
@@ -320,12 +371,12 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
                 float f[E];
-                S::unpack(xr[k], f);
+                S::unpack(b.x[k], f);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     st.z += s * E + e < cols ? exp2_(fmaf(f[e], kLog2e, nm)) : 0.0f;
             }
-        }
+        });
         st = row_merge(st, lds);
         if (threadIdx.x == 0) {
             const float l = logf(st.z) + (1.0f - alpha) * (st.mx - xl) +
@@ -340,14 +391,12 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         const float nsl = -(a.scale * (pa + (1.0f - alpha)));
         const float fill = ignored ? 0.0f : NAN;
         const rsrc_t vd = row_view<S>(a.dx, row, 1, ld);
-        for (int64_t c = 0; c < call; ++c) {
-            u32x4 xr[kSu];
-            load_chunk<S, VEC, true>(vx, c, nv, cols, xr);
+        pipelined<XChunk, VEC>(call, fetch(std::true_type{}), [&](int64_t c, const XChunk& b) {
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;
                 float f[E], out[E];
-                S::unpack(xr[k], f);
+                S::unpack(b.x[k], f);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const int col = s * E + e;
@@ -358,7 +407,7 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
                 }
                 store_slot<S, VEC>(vd, s, ns, ld, out);
             }
-        }
+        });
     }
 }
 
@@ -376,8 +425,11 @@ hipError_t MBROW_CAT(launch_softmax_stream_, MBROW_SUFFIX)(bool vec, bool backwa
     if (backward)
         return vec ? launch_rows(softmax_stream_bwd<St, true>, a, s)
                    : launch_rows(softmax_stream_bwd<St, false>, a, s);
-    return vec ? launch_rows(softmax_stream_fwd<St, true>, a, s)
-               : launch_rows(softmax_stream_fwd<St, false>, a, s);
+    if (a.mask)
+        return vec ? launch_rows(softmax_stream_fwd<St, true, true>, a, s)
+                   : launch_rows(softmax_stream_fwd<St, false, true>, a, s);
+    return vec ? launch_rows(softmax_stream_fwd<St, true, false>, a, s)
+               : launch_rows(softmax_stream_fwd<St, false, false>, a, s);
 }
 hipError_t MBROW_CAT(launch_xent_stream_, MBROW_SUFFIX)(bool vec, const XeArgs& a,
                                                         hipStream_t s) {
