@@ -610,7 +610,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method's rows "
               "shard across GPUs with no communication except a [2, cols] dgamma/dbeta "
-              "exchange, which this build does not run.", file=sys.stderr)
+              "exchange, which this benchmark does not run.", file=sys.stderr)
         sys.exit(2)
     import torch
     import memory_bound_row_amd as mb

@@ -30,7 +30,7 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
-            f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+            f"{LIB_PATH} is not built: run `python -m memory_bound_row_amd.build` "
             "(the HIP library is required; there is no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int

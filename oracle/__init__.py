@@ -6,7 +6,7 @@ never imports, links or calls it, and it shares no code with the GPU library.
 
 The arithmetic lives in ``ln_oracle.c`` (plain C, float64); this module only
 builds it with gcc and marshals numpy arrays through ctypes.  ``compare``
-holds the tolerance rule used to judge GPU outputs against it.
+holds the tolerance rule used to check GPU outputs against it.
 
 Parity unpinned: the Philox-based dropout mask is pinned by published
 known-answer values of Philox4x32-10 and by statistics, but the choice of
