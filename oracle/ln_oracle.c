@@ -192,10 +192,15 @@ uint32_t orc_dropout_threshold(float p) {
 
 void orc_dropout_keep(uint64_t seed, float p, int64_t rows, int64_t m,
                       uint8_t* keep) {
+    orc_dropout_keep_rows(seed, p, 0, rows, m, keep);
+}
+
+void orc_dropout_keep_rows(uint64_t seed, float p, int64_t row0, int64_t rows, int64_t m,
+                           uint8_t* keep) {
     uint32_t thr = orc_dropout_threshold(p);
     uint32_t key[2] = { (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32) };
     for (int64_t r = 0; r < rows; ++r) {
-        uint64_t ur = (uint64_t)r;
+        uint64_t ur = (uint64_t)(row0 + r);
         for (int64_t j = 0; j < m; ++j) {
             uint64_t uj = (uint64_t)j;
             uint32_t ctr[4] = { (uint32_t)(uj >> 3), (uint32_t)(ur & 0xFFFFFFFFu),

@@ -87,6 +87,10 @@ uint32_t orc_dropout_threshold(float p);
  * (col & 1) of output word (col & 7) >> 1. */
 void orc_dropout_keep(uint64_t seed, float p, int64_t rows, int64_t m,
                       uint8_t* keep);
+/* The same mask for rows [row0, row0 + rows) of a tensor (keep holds
+ * rows x m entries): for checking sampled rows of very large tensors. */
+void orc_dropout_keep_rows(uint64_t seed, float p, int64_t row0, int64_t rows, int64_t m,
+                           uint8_t* keep);
 
 /* Bias + dropout + residual, [L10] §2.3 (bias add, dropout, then residual):
  * t = x + bias; d = keep ? t / (1 - p) : 0; z = residual + d.  Exact in

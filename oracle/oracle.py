@@ -57,6 +57,7 @@ def _load():
     lib.orc_dropout_threshold.restype = ctypes.c_uint32
     lib.orc_dropout_threshold.argtypes = [ctypes.c_float]
     lib.orc_dropout_keep.argtypes = [ctypes.c_uint64, ctypes.c_float, i64, i64, u8p]
+    lib.orc_dropout_keep_rows.argtypes = [ctypes.c_uint64, ctypes.c_float, i64, i64, i64, u8p]
     lib.orc_bias_dropout_residual.argtypes = [dp, dp, dp, u8p, ctypes.c_float,
                                               i64, i64, dp]
     for name in ("orc_ln_bwd_dx_hw4", "orc_ln_bwd_dx_slides", "orc_ln_bwd_dx_scale"):
@@ -163,6 +164,14 @@ def dropout_keep(seed: int, p: float, rows: int, cols: int) -> np.ndarray:
     keep = np.empty((rows, cols), dtype=np.uint8)
     _load().orc_dropout_keep(ctypes.c_uint64(seed), ctypes.c_float(p), rows, cols,
                              _ptr(keep, ctypes.c_uint8))
+    return keep
+
+
+def dropout_keep_rows(seed: int, p: float, row0: int, rows: int, cols: int) -> np.ndarray:
+    """The keep mask of rows [row0, row0 + rows) of a tensor."""
+    keep = np.empty((rows, cols), dtype=np.uint8)
+    _load().orc_dropout_keep_rows(ctypes.c_uint64(seed), ctypes.c_float(p), row0, rows, cols,
+                                  _ptr(keep, ctypes.c_uint8))
     return keep
 
 
@@ -305,7 +314,7 @@ def cross_entropy(x, labels, alpha: float = 0.0, scale: float = 1.0, grad: bool 
 
 __all__ = ["F32", "F16", "BF16", "build", "round_to", "round_scalar", "ln_fwd",
            "row_stats_welford", "var_naive_f32", "var_chan_f32", "philox4x32_10",
-           "dropout_threshold", "dropout_keep", "bias_dropout_residual",
+           "dropout_threshold", "dropout_keep", "dropout_keep_rows", "bias_dropout_residual",
            "ln_bwd_dx", "ln_bwd_dx_scale", "ln_bwd_params", "dropout_residual_bwd",
            "attn_softmax_fwd", "attn_softmax_bwd", "rmsnorm_fwd", "rmsnorm_bwd",
            "cross_entropy"]

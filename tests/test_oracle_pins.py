@@ -684,3 +684,14 @@ def test_cross_entropy_finite_differences(orc):
         fd = (orc.cross_entropy(xp, lab, alpha, 1.0, grad=False)[0][0]
               - orc.cross_entropy(xm, lab, alpha, 1.0, grad=False)[0][0]) / (2 * h)
         assert abs(fd - dx[0, j]) < 1e-8, (j, fd, dx[0, j])
+
+
+def test_dropout_keep_rows_is_the_same_mask(orc):
+    # the row-range form of the mask equals the corresponding rows of the
+    # whole-tensor form (including rows past 2^32, where the row's high word
+    # enters the counter)
+    full = orc.dropout_keep(123, 0.3, 40, 77)
+    assert np.array_equal(orc.dropout_keep_rows(123, 0.3, 7, 20, 77), full[7:27])
+    hi = orc.dropout_keep_rows(5, 0.5, (1 << 32) + 3, 2, 64)
+    lo = orc.dropout_keep_rows(5, 0.5, 3, 2, 64)
+    assert not np.array_equal(hi, lo)
