@@ -192,6 +192,57 @@ def timed(g, n):
     return start.elapsed_time(end) / n
 
 
+def step_distribution(g, n, reps):
+    """Microseconds per step over `reps` further replays of the n-step graph
+    g, each between its own pair of HIP events: p10 / median / p90 of the
+    per-replay averages."""
+    import torch
+    t = sorted(timed(g, n) * 1e3 for _ in range(reps))
+
+    def q(f):
+        return round(t[min(reps - 1, int(f * reps))], 2)
+    return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9), "replays": reps,
+            "steps_per_replay": n}
+
+
+def copy_rates(sizes_mb, S, dev, K):
+    """Attainable bandwidth: the library's plain 16-byte copy (`hbm_copy`)
+    moving `mb` MB in total (half read, half written), rotated over S buffer
+    pairs like the step, timed as a K-copy graph.  GB/s per size."""
+    import torch
+    import memory_bound_row_amd as mb_lib
+    out = {}
+    for mb in sizes_mb:
+        n = (int(mb * 1e6) // 2) // 16 * 4           # int32 elements per side, 16 B multiple
+        pairs = [(torch.ones(n, dtype=torch.int32, device=dev),
+                  torch.empty(n, dtype=torch.int32, device=dev)) for _ in range(S)]
+        ms = timed(capture(lambda i: mb_lib.hbm_copy(pairs[i % S][0], pairs[i % S][1]), K), K)
+        out[f"{mb}MB"] = round(8 * n / (ms * 1e-3) / 1e9, 1)
+        del pairs
+    return out
+
+
+def host_threads() -> int:
+    """Threads the host leg may use: the process's CPU affinity, capped by
+    OMP_NUM_THREADS when that is set."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def plain_bytes(rows: int, cols: int, s: int) -> dict:
     """Algorithmic bytes of ln_fwd and of the backward (dx, dgamma, dbeta)."""
     fwd = 2 * rows * cols * s + 2 * cols * s + 8 * rows
@@ -199,33 +250,63 @@ def plain_bytes(rows: int, cols: int, s: int) -> dict:
     return {"fwd": fwd, "bwd": bwd, "step": fwd + bwd}
 
 
+def _oracle_step(orc, d, row0, rows):
+    """The oracle's whole step over rows [row0, row0 + rows) of the workload;
+    returns the column sums (dgamma, dbeta) of that range."""
+    import numpy as np
+    sl = slice(row0, row0 + rows)
+    keep = orc.dropout_keep_rows(SEED, P_DROP, row0, rows, COLS)
+    z = orc.round_to(orc.bias_dropout_residual(d["x"][sl], d["bias"], d["residual"][sl], keep,
+                                               P_DROP), "bf16")
+    _, mu, rs = orc.ln_fwd(z, d["gamma"], d["beta"], EPS)
+    mu, rs = np.float64(np.float32(mu)), np.float64(np.float32(rs))
+    orc.ln_bwd_dx(d["dy"][sl], z, d["gamma"], mu, rs)
+    return orc.ln_bwd_params(d["dy"][sl], z, mu, rs)
+
+
 def cpu_baseline(inp_cpu, target_s: float):
     """The float64 oracle, as it stands, on the host: the same step on the
-    same stored values (single thread)."""
-    import numpy as np
+    same stored values, single-threaded (the reported baseline), and for
+    context the same calls on row ranges split over the host's threads (the
+    oracle's C routines release the interpreter lock), their column sums
+    added in range order."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle as orc
     from memory_bound_row_amd import synth
 
-    rows_s = ROWS
     d = {k: synth.as_f64(v) for k, v in inp_cpu.items()}
+    b = algorithmic_bytes(ROWS, COLS, 2)["step"]
+
     reps, t_total = 0, 0.0
     while reps == 0 or (t_total < target_s and reps < 50):
         t0 = time.perf_counter()
-        keep = orc.dropout_keep(SEED, P_DROP, rows_s, COLS)
-        z = orc.round_to(orc.bias_dropout_residual(d["x"], d["bias"], d["residual"], keep,
-                                                   P_DROP), "bf16")
-        _, mu, rs = orc.ln_fwd(z, d["gamma"], d["beta"], EPS)
-        mu, rs = np.float64(np.float32(mu)), np.float64(np.float32(rs))
-        orc.ln_bwd_dx(d["dy"], z, d["gamma"], mu, rs)
-        orc.ln_bwd_params(d["dy"], z, mu, rs)
+        _oracle_step(orc, d, 0, ROWS)
         t_total += time.perf_counter() - t0
         reps += 1
-    b = algorithmic_bytes(rows_s, COLS, 2)["step"]
-    return {"value": round(b * reps / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{reps} full step(s) of the workload ({rows_s}x{COLS}, float64 oracle "
-                      f"on bf16-stored inputs), {t_total:.1f} s single-threaded",
-            "rows_per_s": round(rows_s * reps / t_total, 1)}
+    out = {"value": round(b * reps / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"{reps} full step(s) of the workload ({ROWS}x{COLS}, float64 oracle "
+                     f"on bf16-stored inputs), {t_total:.1f} s single-threaded",
+           "rows_per_s": round(ROWS * reps / t_total, 1), "cpu_model": cpu_model()}
+
+    nt = host_threads()
+    if nt > 1:
+        bounds = [(ROWS * i // nt, ROWS * (i + 1) // nt) for i in range(nt)]
+        with ThreadPoolExecutor(nt) as pool:
+            reps_p, t_par = 0, 0.0
+            while reps_p == 0 or (t_par < target_s / 2 and reps_p < 50):
+                t0 = time.perf_counter()
+                parts = list(pool.map(lambda r: _oracle_step(orc, d, r[0], r[1] - r[0]), bounds))
+                dg, db = parts[0][0], parts[0][1]
+                for part in parts[1:]:
+                    dg, db = dg + part[0], db + part[1]
+                t_par += time.perf_counter() - t0
+                reps_p += 1
+        out["all_threads"] = {"value": round(b * reps_p / t_par / 1e9, 3), "unit": "GB/s",
+                              "cores": nt,
+                              "sample": f"{reps_p} full step(s), rows split over {nt} threads, "
+                                        f"{t_par:.1f} s"}
+    return out
 
 
 def configs_report(cpp_launch: bool = True) -> None:
@@ -659,15 +740,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # attainable bandwidth: a plain copy of the forward's input size, rotated
-    # like the step, and a large copy (also the PMC calibration kernel)
-    ms_copy = timed(capture(lambda i: sets[i % S]["y"].copy_(sets[i % S]["x"]), K), K)
-    big_src = torch.empty(COPY_BYTES // 2, dtype=dtype, device=dev)
-    big_dst = torch.empty_like(big_src)
-    ms_bigcopy = timed(capture(lambda i: big_dst.copy_(big_src), 4), 4)
-
     g_step = capture(step, K)
     ms_step = timed(g_step, K)
+    dist = step_distribution(g_step, K, 20)
     # per-kernel launches over the same rotation, for the roofline
     ms_fwd = timed(capture(lambda i: fwd(sets[i % S]), K), K)
     ms_bwd = timed(capture(lambda i: bwd(sets[(i + S // 2) % S]), K), K)
@@ -687,12 +762,25 @@ def main():
     ms_plain = timed(capture(plain_step, K), K)
     pb = plain_bytes(ROWS, COLS, 2)["step"]
 
+    # attainable bandwidth: plain copies moving the kernels' and the step's
+    # byte counts, rotated like the step, and a large copy (also the PMC
+    # calibration kernel)
+    nb = algorithmic_bytes(ROWS, COLS, 2)
+    copy_mb = {"fused_fwd": round(nb["fused_fwd"] / 1e6), "bwd": round(nb["bwd"] / 1e6),
+               "step": round(nb["step"] / 1e6)}
+    copies = copy_rates(sorted(set(copy_mb.values())), S, dev, K)
+    big_src = torch.empty(COPY_BYTES // 2, dtype=dtype, device=dev)
+    big_dst = torch.empty_like(big_src)
+    ms_bigcopy = timed(capture(lambda i: big_dst.copy_(big_src), 4), 4)
+
     nbytes = algorithmic_bytes(ROWS, COLS, 2)
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
     per_kernel = {
         "ln_fwd_kernel(fused)": (ms_fwd, nbytes["fused_fwd"]),
         "ln_bwd_kernel(dx+partials)": (ms_bwd, nbytes["bwd"] - 8 * COLS),
     }
+    bwd_gbps = per_kernel["ln_bwd_kernel(dx+partials)"][1] / (ms_bwd * 1e-3) / 1e9
+    fwd_gbps = nbytes["fused_fwd"] / (ms_fwd * 1e-3) / 1e9
     dom = max(per_kernel, key=lambda k: per_kernel[k][0])
     ms_dom, b_dom = per_kernel[dom]
     achieved = b_dom / (ms_dom * 1e-3) / 1e9
@@ -720,8 +808,13 @@ def main():
         "bytes_per_step": nbytes["step"],
         "kernel_us": {"fused_fwd": round(ms_fwd * 1e3, 3), "bwd_dx_partials": round(ms_bwd * 1e3, 3),
                       "fold": round(ms_fold * 1e3, 3)},
-        "copy_GBps": {"21MB_rotated": round(2 * ROWS * COLS * 2 / (ms_copy * 1e-3) / 1e9, 1),
-                      "256MiB": round(2 * COPY_BYTES / (ms_bigcopy * 1e-3) / 1e9, 1)},
+        "step_us": dist,
+        "copy_GBps": dict(copies, **{
+            "256MiB_torch": round(2 * COPY_BYTES / (ms_bigcopy * 1e-3) / 1e9, 1)}),
+        "pct_of_copy": {
+            "step": round(100.0 * value / copies[f"{copy_mb['step']}MB"], 1),
+            "fused_fwd": round(100.0 * fwd_gbps / copies[f"{copy_mb['fused_fwd']}MB"], 1),
+            "bwd": round(100.0 * bwd_gbps / copies[f"{copy_mb['bwd']}MB"], 1)},
         "plain_fwd_step": {"workload": "ln_fwd then the same backward and fold, 8192x1280 bf16",
                            "bytes_per_step": pb, "ms_per_step": round(ms_plain, 5),
                            "GBps": round(pb / (ms_plain * 1e-3) / 1e9, 1),

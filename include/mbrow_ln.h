@@ -361,6 +361,16 @@ ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, flo
                                   float label_smoothing, float grad_scale, ln_dtype_t dt,
                                   hipStream_t stream);
 
+/*
+ * Measurement reference, not a step of any method: copies `bytes` bytes from
+ * src to dst (device pointers) in 16-byte vectors with nontemporal loads and
+ * stores, the attainable-bandwidth figure that the row kernels' rates are
+ * compared against.  bytes, src and dst must be multiples of 16 and the two
+ * ranges must not overlap, else LN_ERR_PARAM; NULL with bytes > 0 is
+ * LN_ERR_NULL; bytes == 0 is a no-op.  Enqueued on `stream`; no allocation.
+ */
+ln_status_t hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
 /* Static English description of a status code (never NULL). */
 const char* ln_status_string(ln_status_t status);
 

@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
                                   i32, vp]
     L.cross_entropy_fwd_bwd.restype = i32
     L.cross_entropy_fwd_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, f32, i32, vp]
+    L.hbm_copy.restype = i32
+    L.hbm_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     L.ln_debug_force_path.restype = i32
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
     L.ln_debug_force_grid.restype = i32
@@ -403,6 +405,18 @@ def cross_entropy_fwd_bwd(logits, labels, *, cols: int = None, label_smoothing: 
                                        rows, cols, ld, float(label_smoothing),
                                        float(grad_scale), _dt(logits), _stream(logits)))
     return loss, dlogits
+
+
+def hbm_copy(src, dst) -> None:
+    """Copy src into dst (same byte size, device tensors, 16-byte aligned and
+    sized, not overlapping) with the library's plain 16-byte copy kernel: the
+    attainable-bandwidth reference for measurements."""
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("hbm_copy needs contiguous GPU tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("hbm_copy: src and dst differ in size")
+    _check(lib().hbm_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)))
 
 
 def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,

@@ -329,3 +329,15 @@ def test_cross_entropy_validation(L):
     assert xent(L, dx=B) == LN_ERR_UNSUPPORTED                  # dlogits over the labels
     assert xent(L, loss=B) == LN_ERR_UNSUPPORTED                # loss over the labels
     assert xent(L, loss=A) == LN_ERR_UNSUPPORTED                # loss over the logits
+
+
+def test_hbm_copy_validation(L):
+    assert L.hbm_copy(A, B, 0, None) == LN_OK             # no-op, nothing launched
+    assert L.hbm_copy(None, B, 16, None) == LN_ERR_NULL
+    assert L.hbm_copy(A, None, 16, None) == LN_ERR_NULL
+    assert L.hbm_copy(A, B, 17, None) == LN_ERR_PARAM     # not a whole number of vectors
+    assert L.hbm_copy(A + 8, B, 16, None) == LN_ERR_PARAM
+    assert L.hbm_copy(A, B + 4, 16, None) == LN_ERR_PARAM
+    assert L.hbm_copy(A, A + 16, 64, None) == LN_ERR_PARAM   # overlapping ranges
+    assert L.hbm_copy(A + 16, A, 64, None) == LN_ERR_PARAM
+    assert L.hbm_copy(A, A, 16, None) == LN_ERR_PARAM
