@@ -93,6 +93,15 @@ def test_xent_long_rows_per_element_and_invalid_label(orc):
     assert torch.isnan(loss2[2]) and torch.isnan(dx2[2]).all()
 
 
+def test_widest_rows(orc):
+    # LN_MAX_COLS_STREAM columns: the widest row the library takes (the next
+    # width up is rejected on the host, tests/test_abi.py)
+    cols = 1 << 24
+    case(f"stream softmax and cross-entropy 2x{cols} bf16")
+    softmax_run(orc, 2, cols, torch.bfloat16, p=0.1, name="stream.sm.widest")
+    xent_run(orc, 2, cols, cols, torch.bfloat16, name="stream.xent.widest")
+
+
 def test_stream_in_a_graph():
     case("stream paths under graph capture")
     d = dev(synth.layer_inputs(8, 40000, torch.bfloat16, seed=9, x_std=3.0, names=("x", "dy")))
