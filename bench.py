@@ -351,7 +351,34 @@ def configs_report(cpp_launch: bool = True) -> None:
     torch.cuda.init()
     dev = torch.device("cuda", 0)
 
+    copy_cache = {}
+
+    def copy_gbps(nbytes):
+        """GB/s of the library's plain copy (`hbm_copy`) moving nbytes (half
+        read, half written), rotated over enough buffer pairs to exceed the
+        Infinity Cache: the attainable rate at that byte count."""
+        key = int(round(nbytes / 1e6))
+        if key not in copy_cache:
+            n = (int(nbytes) // 2) // 16 * 4            # int32 elements per side
+            pairs = max(2, -(-1_100_000_000 // (8 * n)))
+            bufs = [(torch.ones(n, dtype=torch.int32, device=dev),
+                     torch.empty(n, dtype=torch.int32, device=dev)) for _ in range(pairs)]
+            k = 20
+            ms = timed(capture(lambda i: mb.hbm_copy(bufs[i % pairs][0], bufs[i % pairs][1]),
+                               k), k)
+            copy_cache[key] = 8 * n / (ms * 1e-3) / 1e9
+            del bufs
+            torch.cuda.empty_cache()
+        return copy_cache[key]
+
     def emit(rec):
+        # each rate of at least 16 MB next to the copy rate at its byte count
+        for pre, bkey in (("", "bytes_per_pass"), ("fwd_", "fwd_bytes"), ("bwd_", "bwd_bytes")):
+            rate, nb = rec.get(pre + "GBps"), rec.get(bkey)
+            if rate is not None and nb and nb >= 16_000_000:
+                c = copy_gbps(nb)
+                rec[pre + "copy_GBps"] = round(c, 1)
+                rec[pre + "pct_of_copy"] = round(100.0 * rate / c, 1)
         print(json.dumps(rec), flush=True)
 
     # decode-shaped launch cost
@@ -427,9 +454,11 @@ def configs_report(cpp_launch: bool = True) -> None:
         rec["pct_of_hbm_peak"] = round(100.0 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
         if fwd:
             msf = timed(capture(f, iters), iters)
+            rec["fwd_bytes"] = pb["fwd"]
             rec["fwd_us"] = round(msf * 1e3, 3)
             rec["fwd_GBps"] = round(pb["fwd"] / (msf * 1e-3) / 1e9, 1)
         msb = timed(capture(bw, iters), iters)
+        rec["bwd_bytes"] = pb["bwd"]
         rec["bwd_fold_us"] = round(msb * 1e3, 3)
         rec["bwd_GBps"] = round(pb["bwd"] / (msb * 1e-3) / 1e9, 1)
         emit(rec)
