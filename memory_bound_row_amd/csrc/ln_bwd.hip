@@ -24,8 +24,9 @@
 //
 // Schedule.  One row block at a time per workgroup, its loads issued
 // together at the top of the iteration; all P workgroups are resident, so
-// the memory system sees P blocks in flight.  (Measured: prefetching the
-// next block as well slows this kernel down on gfx950.)
+// the memory system sees P blocks in flight.  The prologue backward (16-bit
+// rows of one wave or less) also loads the next block while it computes the
+// current one; the plain modes measured no faster with that.
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 
@@ -59,6 +60,16 @@ struct BwdGeometry {
 };
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// a or b, chosen at compile time (arrays of different lengths)
+template <bool C, class A, class B>
+__device__ __forceinline__ auto& select(A& a, B& b) {
+    if constexpr (C) {
+        return a;
+    } else {
+        return b;
+    }
+}
 
 template <class S, int G, int V, bool VEC, int MODE>
 __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
@@ -124,17 +135,52 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     const bool has_extra = EXTRA && a.dz_extra != nullptr;   // uniform
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
-    // One block at a time: its loads, the block unpacked once, pass 1 (the
-    // two row sums), pass 2 (dx and the column partials).  The walk is
-    // uniform per workgroup, so the barrier of a multi-wave row is reached
-    // by all.
-    int it = 0;
-    for (int64_t base = first; base < a.rows; base += stride, ++it) {
+    // The block is unpacked once (x - mean in place, dy as is), except in
+    // multi-wave rows of the prologue backward, which have no registers to
+    // spare for that and unpack in each pass.
+    constexpr bool ONCE = !(DROP && G > 64);
+    // With a 16-bit block unpacked once, its packed registers are free during
+    // the two passes: the prologue backward loads the next block's dy, z and
+    // row statistics into them there, so each block's loads are in flight
+    // while the previous block's Philox rounds and sums run.  (The plain
+    // backward, with less arithmetic per block, measured no faster so.)
+    constexpr bool PF = DROP && VEC && ONCE && E == 8 && V <= 3;
+    u32x4 xp[PF ? V : 1], dp[PF ? V : 1];   // the prefetched block
+    float mu_n = 0.0f, rs_n = 0.0f;
+    auto issue = [&](int64_t b) {
+        const rsrc_t vd = view(a.dy, b);
+        const rsrc_t vx = view(a.x, b);
+#pragma unroll
+        for (int i = 0; i < (PF ? V : 1); ++i) {
+            dp[i] = buf_load_nt(vd, vo[i]);
+            xp[i] = buf_load_nt(vx, vo[i]);
+        }
+        const int64_t rw = b + grp < a.rows ? b + grp : 0;
+        if constexpr (!RMS) mu_n = a.mean[rw];
+        rs_n = a.rstd[rw];
+    };
+
+    // One block: its loads, the block unpacked once, pass 1 (the two row
+    // sums), pass 2 (dx and the column partials).  The walk is uniform per
+    // workgroup, so the barrier of a multi-wave row is reached by all.
+    auto block = [&](const int64_t base, const int it) __attribute__((always_inline)) {
+        // the block's dy and x: the prefetched registers, or its own
+        u32x4 xr_b[PF ? 1 : V], dr_b[PF ? 1 : V];
+        auto& xr = select<PF>(xp, xr_b);
+        auto& dr = select<PF>(dp, dr_b);
         const int64_t row = base + grp;
         const bool rok = row < a.rows;
         const int64_t r = rok ? row : 0;   // rows past the end read row 0's statistics
-        u32x4 xr[V], dr[V], er[EXTRA ? V : 1];
-        if constexpr (VEC) {
+        u32x4 er[EXTRA ? V : 1];
+        if constexpr (PF) {
+            if constexpr (EXTRA) {
+                if (has_extra) {
+                    const rsrc_t ve = view(a.dz_extra, base);
+#pragma unroll
+                    for (int i = 0; i < V; ++i) er[i] = buf_load_nt(ve, vo[i]);
+                }
+            }
+        } else if constexpr (VEC) {
             // rows past the end read 0 and are never stored
             const rsrc_t vd = view(a.dy, base);
             const rsrc_t vx = view(a.x, base);
@@ -177,15 +223,17 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 dw[i] = dropout_words(row, (i * G + lg) * E, a.seed_lo, a.seed_hi, a.thr);
             keep_packed(dw);
         }
-        const float mu = RMS ? 0.0f : a.mean[r], rs = a.rstd[r];
+        float mu, rs;
+        if constexpr (PF) {
+            mu = RMS ? 0.0f : mu_n;
+            rs = rs_n;
+        } else {
+            mu = RMS ? 0.0f : a.mean[r];
+            rs = a.rstd[r];
+        }
         // (the per-element path and multi-wave rows of the prologue backward
         // have no registers to spare for gamma unpacked across blocks)
         if constexpr (DX && (!VEC || (DROP && G > 64))) keep_packed(gp);
-        // The block is unpacked once: x becomes x - mean in place, dy stays.
-        // (Multi-wave rows of the prologue backward have no registers to
-        // spare for that: they keep the block packed and unpack it in each
-        // pass.)
-        constexpr bool ONCE = !(DROP && G > 64);
         float xm_[ONCE ? V : 1][E], d_[ONCE ? V : 1][E];
         if constexpr (ONCE) {
 #pragma unroll
@@ -197,6 +245,13 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                     for (int e = 0; e < E; ++e) xm_[i][e] = xm_[i][e] - mu;
                 }
             }
+        }
+        if constexpr (PF) {
+            // the next block's loads, into the registers just unpacked
+            // (uniform per workgroup)
+            asm volatile("" ::: "memory");
+            if (base + stride < a.rows) issue(base + stride);
+            asm volatile("" ::: "memory");
         }
         // x - mean and dy of slot i
         auto slot = [&](int i, float* xm, float* d) {
@@ -325,6 +380,21 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
                 }
             }
         }
+    };
+    if constexpr (PF) {
+        // the first block outside the loop, so that every entry to the loop
+        // has the same memory operations in flight (the wait for a block's
+        // prefetched loads then leaves the previous block's stores alone)
+        if (first < a.rows) {
+            issue(first);
+            block(first, 0);
+            int it = 1;
+            for (int64_t base = first + stride; base < a.rows; base += stride, ++it)
+                block(base, it);
+        }
+    } else {
+        int it = 0;
+        for (int64_t base = first; base < a.rows; base += stride, ++it) block(base, it);
     }
 
     if constexpr (PART) {
