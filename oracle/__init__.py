@@ -8,10 +8,12 @@ The arithmetic lives in ``ln_oracle.c`` (plain C, float64); this module only
 builds it with gcc and marshals numpy arrays through ctypes.  ``compare``
 holds the tolerance rule used to check GPU outputs against it.
 
-Parity unpinned: the Philox-based dropout mask is pinned by published
-known-answer values of Philox4x32-10 and by statistics, but the choice of
-counter/key layout is this library's own (the pages only say the mask is
-regenerated from a seed); the GPU and oracle implementations of that layout
-are written independently and checked against each other.
+Parity unpinned: the Philox-based dropout mask.  Philox4x32-10 is written
+here from its published definition (Salmon et al., SC'11), and the pages
+print no known-answer values for it; the counter/key layout is this
+library's own (the pages only say the mask is regenerated from a seed).  The
+tests pin the layout and the keep statistics, and the GPU and oracle
+implementations, written independently, are checked against each other bit
+for bit.
 """
 from .oracle import *  # noqa: F401,F403

@@ -24,7 +24,9 @@
  *
  * Pins: every function is checked in tests/test_oracle_pins.py against
  * something other than itself (worked examples printed on the pages, closed
- * forms, identities, finite differences, published known-answer values).
+ * forms, identities, finite differences), except the Philox4x32-10 round
+ * function: parity unpinned (no known-answer values on the pages; its
+ * layout and statistics are pinned, its bits checked against the GPU's).
  */
 #ifndef MBROW_LN_ORACLE_H
 #define MBROW_LN_ORACLE_H

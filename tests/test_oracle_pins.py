@@ -2,8 +2,10 @@
 
 CPU only.  Each test checks the oracle against something other than itself:
 values printed on the pages (tests/golden), closed forms, identities, finite
-differences, an independent algorithm, a library routine for a special case,
-or published known-answer values.
+differences, an independent algorithm, or a library routine for a special
+case.  The Philox4x32-10 function itself is parity unpinned: no known-answer
+values for it are on the pages, so only its layout and statistics are pinned
+here and its bits are checked GPU against oracle.
 """
 import math
 import os
@@ -369,22 +371,6 @@ def test_params_abs_sums_bound_sums(orc):
 # --------------------------------------------------------------------------
 # Dropout mask (Philox4x32-10) and the fused prologue ("(I)" §2.3)
 # --------------------------------------------------------------------------
-
-def _kat():
-    out = []
-    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
-        for line in f:
-            if line.startswith("#") or not line.strip():
-                continue
-            v = [int(t, 16) for t in line.split()]
-            out.append((v[0:4], v[4:6], v[6:10]))
-    return out
-
-
-@pytest.mark.parametrize("ctr,key,expect", _kat())
-def test_philox_known_answers(orc, ctr, key, expect):
-    assert orc.philox4x32_10(ctr, key).tolist() == expect
-
 
 def test_dropout_threshold(orc):
     assert orc.dropout_threshold(0.0) == 0
