@@ -325,10 +325,12 @@ def configs_report(cpp_launch: bool = True) -> None:
       * fused cross-entropy loss + gradient over GPT-2's vocabulary (50257
         classes in rows padded to 50304), 8x1024 tokens, bf16 and fp32, with
         the gradient in its own buffer and over the logits;
-      * the two-pass paths for rows beyond the register layouts: the softmax
-        over 16x256 rows of 65536 fp16 keys, and the cross-entropy over a
-        256000-class bf16 vocabulary at 2048 tokens (algorithmic bytes: one
-        read and one write; these paths read the row twice);
+      * long softmax rows, fp16: 16x256 rows of 32768 keys in the register
+        layouts and forced onto the two-pass path, and 8x256 rows of
+        131072 keys (two-pass path), and the cross-entropy over a
+        256000-class bf16 vocabulary at 2048 tokens (two-pass path); the
+        algorithmic bytes count one read and one write, though the two-pass
+        path reads each row twice;
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
@@ -671,34 +673,47 @@ def configs_report(cpp_launch: bool = True) -> None:
     xent_case(2048, 256000, 256000, torch.bfloat16,
               "fused cross-entropy, 256000-class vocabulary (two-pass path), 2048 tokens")
 
-    # softmax over rows longer than the register layouts (two-pass path)
-    rows, L = 16 * 256, 65536
-    d = synth.layer_inputs(rows, L, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
-    a = {"x": d["x"].to(dev), "dy": d["dy"].to(dev)}
-    del d
-    a["y"] = torch.empty_like(a["x"])
-    a["dx"] = torch.empty_like(a["x"])
+    # softmax over long rows: the register layouts (32768 keys; also forced
+    # onto the two-pass path, for comparison) and the two-pass path past them
+    # (131072 keys)
+    def long_softmax(rows, L, label, two_pass=False):
+        d = synth.layer_inputs(rows, L, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
+        a = {"x": d["x"].to(dev), "dy": d["dy"].to(dev)}
+        del d
+        a["y"] = torch.empty_like(a["x"])
+        a["dx"] = torch.empty_like(a["x"])
 
-    def lf(i):
-        mb.attn_softmax_fwd(a["x"], 0.125, y=a["y"])
+        def lf(i):
+            mb.attn_softmax_fwd(a["x"], 0.125, y=a["y"])
 
-    def lb(i):
-        mb.attn_softmax_bwd(a["dy"], a["y"], 0.125, dx=a["dx"])
+        def lb(i):
+            mb.attn_softmax_bwd(a["dy"], a["y"], 0.125, dx=a["dx"])
 
-    lf(0)
-    torch.cuda.synchronize()
-    n = 10
-    msf = timed(capture(lf, n), n)
-    msb = timed(capture(lb, n), n)
-    t = rows * L * 2
-    emit({"workload": "attention softmax fwd + bwd, 16x256 rows of 65536 keys (two-pass path)",
-          "rows": rows, "cols": L, "storage": "float16",
-          "fwd_bytes": 2 * t, "fwd_us": round(msf * 1e3, 3),
-          "fwd_GBps": round(2 * t / (msf * 1e-3) / 1e9, 1),
-          "bwd_bytes": 3 * t, "bwd_us": round(msb * 1e3, 3),
-          "bwd_GBps": round(3 * t / (msb * 1e-3) / 1e9, 1)})
-    del a
-    torch.cuda.empty_cache()
+        mb.debug_force_two_pass(two_pass)
+        try:
+            lf(0)
+            torch.cuda.synchronize()
+            n = 10
+            msf = timed(capture(lf, n), n)
+            msb = timed(capture(lb, n), n)
+        finally:
+            mb.debug_force_two_pass(False)
+        t = rows * L * 2
+        emit({"workload": label, "rows": rows, "cols": L, "storage": "float16",
+              "fwd_bytes": 2 * t, "fwd_us": round(msf * 1e3, 3),
+              "fwd_GBps": round(2 * t / (msf * 1e-3) / 1e9, 1),
+              "bwd_bytes": 3 * t, "bwd_us": round(msb * 1e3, 3),
+              "bwd_GBps": round(3 * t / (msb * 1e-3) / 1e9, 1)})
+        del a
+        torch.cuda.empty_cache()
+
+    long_softmax(16 * 256, 32768,
+                 "attention softmax fwd + bwd, 16x256 rows of 32768 keys (register layouts)")
+    long_softmax(16 * 256, 32768,
+                 "attention softmax fwd + bwd, 16x256 rows of 32768 keys, forced onto the "
+                 "two-pass path", two_pass=True)
+    long_softmax(8 * 256, 131072,
+                 "attention softmax fwd + bwd, 8x256 rows of 131072 keys (two-pass path)")
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")

@@ -82,10 +82,18 @@ typedef enum {
  * workgroup; GPT-2's 50257 and Llama-3's 128256 classes fit in bf16). */
 #define LN_MAX_COLS_XENT_F32 65536
 #define LN_MAX_COLS_XENT_16 131072
+/* Widest row of attn_softmax_fwd / attn_softmax_bwd held in registers (and
+ * so read once): 32768 fp32 or 65536 fp16/bf16 scores (one 1024-lane
+ * workgroup per row beyond 16384). */
+#define LN_MAX_COLS_SOFTMAX_F32 32768
+#define LN_MAX_COLS_SOFTMAX_16 65536
+/* The same for attn_softmax_bwd with fp16/bf16 storage (it holds two
+ * tensors, dy and y, per row). */
+#define LN_MAX_COLS_SOFTMAX_BWD_16 49152
 /* Widest row of attn_softmax_fwd / attn_softmax_bwd / cross_entropy_fwd_bwd:
- * rows wider than their register path (LN_MAX_COLS for the softmax,
- * LN_MAX_COLS_XENT_* for the cross-entropy) take a two-pass path that reads
- * the row twice. */
+ * rows wider than their register path (LN_MAX_COLS_SOFTMAX_* for the
+ * softmax, LN_MAX_COLS_XENT_* for the cross-entropy) take a two-pass path
+ * that reads the row twice. */
 #define LN_MAX_COLS_STREAM (1 << 24)
 
 /*
@@ -248,8 +256,9 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
  *   output or NULL (may equal x, not y).
  * scale must be finite; causal 0 or 1; p in [0, 1); rows_per_mask >= 1 when
  * mask is given.  Arithmetic in float32 (exp by the device's exp2).  Rows of
- * up to LN_MAX_COLS columns are held in registers (read once); wider rows, up
- * to LN_MAX_COLS_STREAM, are read twice: an online maximum/sum pass
+ * up to LN_MAX_COLS_SOFTMAX_F32 (fp32) or LN_MAX_COLS_SOFTMAX_16 (fp16/bf16)
+ * columns are held in registers (read once); wider rows, up to
+ * LN_MAX_COLS_STREAM, are read twice: an online maximum/sum pass
  * ([LLMC] §6.1), then the output pass.
  */
 ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
@@ -266,8 +275,9 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
  *   dy [rows, cols] T: gradient of y_dropped (of y when p = 0).
  *   y  [rows, cols] T: the forward's y.   dx [rows, cols] T output (may equal
  *   dy or y).  causal = 1 skips reading the keys past the query (y = 0
- *   there, so dx = 0).  Rows wider than LN_MAX_COLS (up to
- *   LN_MAX_COLS_STREAM) read dy and y twice: the dot product, then dx.
+ *   there, so dx = 0).  Rows wider than LN_MAX_COLS_SOFTMAX_F32 (fp32) or
+ *   LN_MAX_COLS_SOFTMAX_BWD_16 (fp16/bf16), up to LN_MAX_COLS_STREAM, read dy
+ *   and y twice: the dot product, then dx.
  */
 ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
                              int64_t cols, float scale, int causal, float p, uint64_t seed,

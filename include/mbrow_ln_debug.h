@@ -22,7 +22,10 @@ extern "C" {
  *                  library's own choice (and ignores slots_per_lane).
  *   slots_per_lane 16-byte slots per lane.  Built layouts: fp32 16x{1,2,4,8},
  *                  32x1-8, 64x1-8, {128,256,512,1024}x4; fp16/bf16
- *                  16x{1,2,4}, 32x1-5, 64x1-5, {128,256,512}x4.  The prologue
+ *                  16x{1,2,4}, 32x1-5, 64x1-5, {128,256,512}x4.  The attention
+ *                  softmax also has 1024x5-8 (fp32) and 512x{6,8}, 1024x3-8
+ *                  (fp16/bf16; its backward 1024x3-6), the cross-entropy its
+ *                  own set (1024 x up to 16).  The prologue
  *                  backward (bias_dropout_residual_ln_bwd) has its own set:
  *                  fp32 16x{1,2,4}, 32x1-4, 64x1-6, {128,256,512}x4;
  *                  fp16/bf16 16x{1,2}, 32x1-3, 64x1-3, {128,256,512}x2.
@@ -42,6 +45,14 @@ ln_status_t ln_debug_force_path(int lanes_per_row, int slots_per_lane, int scala
  * Results do not depend on it.
  */
 ln_status_t ln_debug_force_grid(int workgroups_per_cu);
+
+/*
+ * on != 0: every later attn_softmax_fwd / attn_softmax_bwd /
+ * cross_entropy_fwd_bwd call takes the two-pass path (the one for rows wider
+ * than the register layouts) whatever its width; 0 restores the width-based
+ * choice.  Results are within the same tolerances either way.
+ */
+ln_status_t ln_debug_force_two_pass(int on);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
     L.ln_debug_force_grid.restype = i32
     L.ln_debug_force_grid.argtypes = [i32]
+    L.ln_debug_force_two_pass.restype = i32
+    L.ln_debug_force_two_pass.argtypes = [i32]
     _lib = L
     return L
 
@@ -424,6 +426,12 @@ def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,
     """Test-only: force the row layout of later calls (0 restores the default)."""
     _check(lib().ln_debug_force_path(int(lanes_per_row), int(slots_per_lane),
                                      1 if scalar else 0))
+
+
+def debug_force_two_pass(on: bool = False) -> None:
+    """Test-only: softmax and cross-entropy calls take the two-pass path at
+    every width (False restores the width-based choice)."""
+    _check(lib().ln_debug_force_two_pass(1 if on else 0))
 
 
 def debug_force_grid(workgroups_per_cu: int = 0) -> None:

@@ -109,10 +109,12 @@ static bool have_instance(bool f32, int g, int v) {
     return false;
 }
 
-static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0}, g_force_grid{0};
+static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0}, g_force_grid{0},
+    g_force_two_pass{0};
 
 // The test-only override that forces the per-element path (no vector access).
 bool force_scalar() { return g_force_scalar.load(std::memory_order_relaxed) != 0; }
+bool force_two_pass() { return g_force_two_pass.load(std::memory_order_relaxed) != 0; }
 
 // Row layout: among the candidate layouts, the one with the fewest slots
 // (used or not); ties go to the earlier candidate.  With `wave_rows`, slots
@@ -190,15 +192,20 @@ Path pick_path(Dt dt, int64_t cols, bool vec) {
 }
 
 static const int kSm32[][2] = {{16, 1}, {16, 2}, {16, 4}, {32, 2}, {32, 4}, {64, 2}, {64, 4},
-                               {64, 8}, {128, 4}, {256, 4}, {512, 4}, {1024, 4}};
+                               {64, 8}, {128, 4}, {256, 4}, {512, 4}, {1024, 4}, {1024, 5},
+                               {1024, 6}, {1024, 7}, {1024, 8}};
 static const int kSm16[][2] = {{16, 1}, {16, 2}, {32, 1}, {32, 2}, {64, 1}, {64, 2}, {64, 4},
-                               {128, 4}, {256, 4}, {512, 4}};
+                               {128, 4}, {256, 4}, {512, 4}, {512, 6}, {512, 8}, {1024, 3},
+                               {1024, 4}, {1024, 5}, {1024, 6}, {1024, 7}, {1024, 8}};
 
-Path pick_softmax_path(Dt dt, int64_t cols, bool vec) {
+// (the 16-bit backward stops at 1024 x kSmWideBwdV16: the last entries of
+// kSm16 are forward-only)
+Path pick_softmax_path(Dt dt, int64_t cols, bool vec, bool backward) {
     const int E = elems_per_slot(dt);
     const int64_t ns = (cols + E - 1) / E;
+    const int n16 = backward ? MBROW_N(kSm16) - (8 - kSmWideBwdV16) : MBROW_N(kSm16);
     return E == 4 ? pick(true, ns, vec, kSm32, MBROW_N(kSm32), false, true)
-                  : pick(false, ns, vec, kSm16, MBROW_N(kSm16), false, true);
+                  : pick(false, ns, vec, kSm16, n16, false, true);
 }
 
 static const int kXe32[][2] = {{16, 1}, {16, 2}, {16, 4}, {32, 2}, {32, 4}, {64, 2},
@@ -287,6 +294,12 @@ bool valid_dtype(ln_dtype_t dt) { return dt == LN_F32 || dt == LN_F16 || dt == L
 size_t elem_bytes(ln_dtype_t dt) { return dt == LN_F32 ? 4 : 2; }
 
 int64_t max_cols(ln_dtype_t) { return LN_MAX_COLS; }
+
+// widest softmax row held in registers (wider rows take the two-pass path)
+int64_t softmax_max_cols(ln_dtype_t dt, bool backward) {
+    if (dt == LN_F32) return LN_MAX_COLS_SOFTMAX_F32;
+    return backward ? LN_MAX_COLS_SOFTMAX_BWD_16 : LN_MAX_COLS_SOFTMAX_16;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -663,7 +676,8 @@ ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, flo
     a.alpha = label_smoothing;
     a.inv_v = (float)(1.0 / (double)cols);
     a.scale = grad_scale;
-    if (ld > max_ld) return from_hip(launch_xent_stream(d, vec && !force_scalar(), a, stream));
+    if (ld > max_ld || force_two_pass())
+        return from_hip(launch_xent_stream(d, vec && !force_scalar(), a, stream));
     return from_hip(launch_xent(d, pick_xent_path(d, a.nslots, vec), a, stream));
 }
 
@@ -700,9 +714,9 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
     a.pscale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
-    if (cols > LN_MAX_COLS)
+    if (cols > softmax_max_cols(dt, false) || force_two_pass())
         return from_hip(launch_softmax_stream(d, vec && !force_scalar(), false, a, stream));
-    return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec), false, a, stream));
+    return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec, false), false, a, stream));
 }
 
 ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
@@ -735,9 +749,14 @@ ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t ro
     a.pscale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
-    if (cols > LN_MAX_COLS)
+    if (cols > softmax_max_cols(dt, true) || force_two_pass())
         return from_hip(launch_softmax_stream(d, vec && !force_scalar(), true, a, stream));
-    return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec), true, a, stream));
+    return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec, true), true, a, stream));
+}
+
+ln_status_t ln_debug_force_two_pass(int on) {
+    g_force_two_pass.store(on ? 1 : 0, std::memory_order_relaxed);
+    return LN_OK;
 }
 
 ln_status_t ln_debug_force_grid(int workgroups_per_cu) {

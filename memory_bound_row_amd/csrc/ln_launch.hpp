@@ -135,15 +135,27 @@ struct SmArgs {
     int causal;             // keys j > r mod m masked (square score blocks)
 };
 
-// Row layouts of the softmax kernels.
+// Row layouts of the softmax kernels (1024 x 5-8 fp32, 512 x 6, 8 and
+// 1024 x 3-8 16-bit keep the block packed: softmax_wide_kernel).
 #define MBROW_SM_LAYOUTS_F32(X)                                             \
     X(16, 1) X(16, 2) X(16, 4) X(32, 2) X(32, 4) X(64, 2) X(64, 4) X(64, 8) \
-    X(128, 4) X(256, 4) X(512, 4) X(1024, 4)
+    X(128, 4) X(256, 4) X(512, 4) X(1024, 4) X(1024, 5) X(1024, 6)          \
+    X(1024, 7) X(1024, 8)
 #define MBROW_SM_LAYOUTS_16(X)                                              \
     X(16, 1) X(16, 2) X(32, 1) X(32, 2) X(64, 1) X(64, 2) X(64, 4)          \
-    X(128, 4) X(256, 4) X(512, 4)
+    X(128, 4) X(256, 4) X(512, 4) X(512, 6) X(512, 8) X(1024, 3) X(1024, 4) \
+    X(1024, 5) X(1024, 6) X(1024, 7) X(1024, 8)
 
-Path pick_softmax_path(Dt dt, int64_t cols, bool vec);
+// Widest 16-bit backward layout of the softmax (1024 x this many slots).
+constexpr int kSmWideBwdV16 = 6;
+
+// Softmax layouts that keep the block packed (softmax_wide_kernel): those
+// whose unpacked scores would not fit a lane's registers.
+constexpr bool sm_wide_layout(int g, int v, int e) {
+    return (g == 1024 && v * e > 16) || (g == 512 && v > 4);
+}
+
+Path pick_softmax_path(Dt dt, int64_t cols, bool vec, bool backward);
 hipError_t launch_softmax(Dt dt, const Path& p, bool backward, const SmArgs& a, hipStream_t s);
 
 // Residual add + RMSNorm forward over rows of `m` values.

@@ -14,12 +14,23 @@
 // Backward ("Accelerating Transformer on GPU (II)" §3): the dropout backward
 // first, in registers (g = keep ? dy / (1 - p) : 0, the mask regenerated from
 // the seed), then one dot product s = sum g * y and dx = scale * y * (g - s).
+//
+// Rows wider than the generic kernel's registers hold unpacked (up to 65536
+// 16-bit or 32768 fp32 columns, over 512 or 1024 lanes) take
+// softmax_wide_kernel: it holds the block packed, not its unpacked scores,
+// and each pass recomputes what it needs from the packed block (the scores;
+// in the backward g, from dy and one keep bit per value kept from the first
+// pass).  The row is still read once and written once.  Being lean in
+// registers it also keeps more rows in flight per CU, which makes it the
+// faster forward for 16-bit rows of 512 lanes (16384 columns) as well.
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
+#include "online_softmax.hpp"
 
 #ifndef MBROW_DT
 #error "compile with -DMBROW_DT=0|1|2"
 #endif
+
 
 namespace mbrow {
 
@@ -267,15 +278,267 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
     }
 }
 
+// One row per workgroup of G lanes, the block packed in registers (V slots of
+// 16 bytes per lane).  Slot i of lane t covers columns (i*G + t)*E ..+E-1;
+// element e of it is in play iff i*G*E + e < rel, rel = the columns in
+// play (all, or up to the query under the causal mask) minus the lane's first
+// column.  Each pass takes rel and the lane's byte offset through opaque(), so
+// the compiler keeps no per-slot masks or offsets across passes, and only the
+// lane's one partial slot tests elements.
+template <class S, int G, int V, bool VEC, bool BWD, bool MASK>
+__global__ __launch_bounds__(G) void softmax_wide_kernel(SmArgs a) {
+    constexpr int E = S::E, W = G * E, NW = G / 64;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int m = (int)a.m;
+    const int ns = (int)a.nslots;
+    const int base = tid * E;                       // the lane's first column
+    const uint32_t rb0 = (uint32_t)tid * 16u;       // ... and its byte offset (vector path)
+    const uint32_t eb0 = (uint32_t)base * S::BYTES;
+    __shared__ float red[2][2][NW];                 // [buffer][max, sum][wave]
+    auto reduce = [&](float v, int buf, int k) {
+        v = k == 0 ? group_max<64>(v) : group_sum<64>(v);
+        if (lane == 0) red[buf][k][tid / 64] = v;
+        __syncthreads();
+        float r = red[buf][k][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = k == 0 ? fmaxf(r, red[buf][k][w]) : r + red[buf][k][w];
+        return r;
+    };
+    // the lane's slots of one tensor row: slot i is read iff it holds a
+    // column in play (i*G + tid < nlive); others read 0
+    auto load = [&](const void* t, int64_t trow, int nlive, int lim, u32x4 (&out)[V], bool cached) {
+        const rsrc_t v = row_view<S>(t, trow, 1, m);
+        if constexpr (VEC) {
+            const uint32_t rb = (uint32_t)opaque((int)rb0);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const uint32_t off = i * G + tid < nlive ? rb + (uint32_t)(i * G * 16) : kOob;
+                out[i] = cached ? buf_load(v, off) : buf_load_nt(v, off);
+            }
+        } else {
+            const int rel = opaque(lim - base);
+            const uint32_t eb = (uint32_t)opaque((int)eb0);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int c = i * W + e;
+                    f[e] = elem_load<S>(v, c < rel ? eb + (uint32_t)c * S::BYTES : kOob);
+                }
+                out[i] = S::pack(f);
+                hold_packed(out[i]);   // one slot of element loads in flight at a time
+            }
+        }
+    };
+    // writes slot i of a row: every slot of the row (i*G + tid < ns), and on
+    // the per-element path only its columns < m
+    auto store = [&](const rsrc_t v, int i, const float* f) {
+        if constexpr (VEC) {
+            const uint32_t rb = (uint32_t)opaque((int)rb0);
+            buf_store_nt(S::pack(f), v, i * G + tid < ns ? rb + (uint32_t)(i * G * 16) : kOob);
+        } else {
+            const int wl = opaque(m - base);
+            const uint32_t eb = (uint32_t)opaque((int)eb0);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int c = i * W + e;
+                elem_store<S>(v, c < wl ? eb + (uint32_t)c * S::BYTES : kOob, f[e]);
+            }
+        }
+    };
+
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const int buf = it & 1;
+        const int q = a.causal ? (int)(row % m) : m - 1;   // last key in play
+        const int lim = q + 1 < m ? q + 1 : m;
+        const int nlive = (lim + E - 1) / E;
+        u32x4 xr[V];
+        if constexpr (!BWD) {
+            u32x4 mr[MASK ? V : 1];
+            load(a.x, row, nlive, lim, xr, false);
+            if constexpr (MASK) load(a.mask, row / a.rows_per_mask, nlive, lim, mr, true);
+            // scores of slot i: scale, mask; elements out of play are skipped
+            // by the callers
+            auto score = [&](int i, float (&t)[E]) {
+                float xv[E];
+                S::unpack(xr[i], xv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) t[e] = a.scale * xv[e];
+                if constexpr (MASK) {
+                    float mv[E];
+                    S::unpack(mr[i], mv);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) t[e] = t[e] + mv[e];
+                }
+            };
+            auto repack = [&]() {
+                keep_packed(xr);
+                if constexpr (MASK) keep_packed(mr);
+            };
+            // the row maximum, then the sum of exp(score - maximum)
+            float mx = -INFINITY;
+            {
+                const int rel = opaque(lim - base);
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    float t[E];
+                    score(i, t);
+                    if (i * W + E <= rel) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) mx = fmaxf(mx, t[e]);
+                    } else if (i * W < rel) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (i * W + e < rel) mx = fmaxf(mx, t[e]);
+                    }
+                }
+            }
+            mx = reduce(mx, buf, 0);
+            const bool live_row = mx != -INFINITY;   // every key masked: y = 0
+            const float nm = live_row ? -mx * kLog2e : 0.0f;
+            repack();
+            float z = 0.0f;
+            {
+                const int rel = opaque(lim - base);
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    float t[E];
+                    score(i, t);
+                    if (i * W + E <= rel) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) z += exp2_(fmaf(t[e], kLog2e, nm));
+                    } else if (i * W < rel) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (i * W + e < rel) z += exp2_(fmaf(t[e], kLog2e, nm));
+                    }
+                }
+            }
+            z = reduce(z, buf, 1);
+            const float inv = live_row ? 1.0f / z : 0.0f;
+            const float inv_kept = inv * a.pscale;   // dropped copy: y / (1 - p)
+            repack();
+            const rsrc_t vy = row_view<S>(a.out, row, 1, m);
+            const rsrc_t vd = row_view<S>(a.out2 ? a.out2 : a.out, row, 1, m);
+            const int rel = opaque(lim - base);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float t[E], yv[E];
+                score(i, t);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    t[e] = exp2_(fmaf(t[e], kLog2e, nm));
+                    yv[e] = t[e] * inv;
+                }
+                if (!(i * W + E <= rel)) {   // keys out of play get y = 0
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        if (i * W + e >= rel) {
+                            t[e] = 0.0f;
+                            yv[e] = 0.0f;
+                        }
+                    }
+                }
+                store(vy, i, yv);
+                if (a.out2) {
+                    const int col0 = i * W + base;
+                    const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                    float dv[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        dv[e] = kept<E>(w, col0, e, a.thr) ? t[e] * inv_kept : 0.0f;
+                    store(vd, i, dv);
+                }
+            }
+        } else {
+            // dy in xr, y in yr; keys out of play read 0 (y = 0 there, so
+            // they add nothing and get dx = 0)
+            u32x4 yr[V];
+            load(a.x, row, nlive, lim, xr, false);
+            load(a.y, row, nlive, lim, yr, false);
+            // pass 1: g = keep ? dy / (1 - p) : 0 and s = sum g * y, with the
+            // keep bits of the slots in play kept for pass 2
+            constexpr int NB = (V * E + 31) / 32;
+            uint32_t kb[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) kb[k] = 0u;
+            float sg = 0.0f;
+            const int live = opaque(nlive - tid);   // slot i in play iff i*G < live
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                if (i * G < live) {
+                    const int col0 = i * W + base;
+                    float dv[E], yv[E];
+                    S::unpack(xr[i], dv);
+                    S::unpack(yr[i], yv);
+                    const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int b = i * E + e;
+                        const bool keep = kept<E>(w, col0, e, a.thr);
+                        kb[b >> 5] |= keep ? (1u << (b & 31)) : 0u;
+                        sg = fmaf(keep ? dv[e] * a.pscale : 0.0f, yv[e], sg);
+                    }
+                }
+            }
+            sg = reduce(sg, buf, 1);
+            keep_packed(xr);
+            keep_packed(yr);
+            const rsrc_t vdx = row_view<S>(a.out, row, 1, m);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float dv[E], yv[E], dx[E];
+                S::unpack(xr[i], dv);
+                S::unpack(yr[i], yv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int b = i * E + e;
+                    const float g = ((kb[b >> 5] >> (b & 31)) & 1u) ? dv[e] * a.pscale : 0.0f;
+                    dx[e] = a.scale * (yv[e] * (g - sg));
+                }
+                store(vdx, i, dx);
+            }
+        }
+    }
+}
+
+// The 16-bit backward holds dy and y packed (two tensors): up to 6 slots per
+// lane fit its registers, 8 in the forward (the scores and a mask row).
+template <int G, int V, bool VEC, bool BWD, bool MASK>
+static hipError_t launch_wide(const SmArgs& a, hipStream_t s) {
+    if constexpr (BWD && St::E == 8 && G == 1024 && V > kSmWideBwdV16) {
+        return hipErrorInvalidValue;   // callers send such rows to the two-pass path
+    } else {
+        const void* k =
+            reinterpret_cast<const void*>(&softmax_wide_kernel<St, G, V, VEC, BWD, MASK>);
+        const int64_t grid = persistent_grid(k, G, a.rows);
+        hipLaunchKernelGGL((softmax_wide_kernel<St, G, V, VEC, BWD, MASK>),
+                           dim3((unsigned)grid), dim3(G), 0, s, a);
+        return hipGetLastError();
+    }
+}
+
 template <int G, int V, bool VEC, bool BWD>
 static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
-    constexpr int ROWS = SmGeometry<G>::ROWS;
-    const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
-    const void* k = reinterpret_cast<const void*>(&softmax_kernel<St, G, V, VEC, BWD>);
-    const int64_t grid = persistent_grid(k, SmGeometry<G>::NT, nblk);
-    hipLaunchKernelGGL((softmax_kernel<St, G, V, VEC, BWD>), dim3((unsigned)grid),
-                       dim3(SmGeometry<G>::NT), 0, s, a);
-    return hipGetLastError();
+    // (the 16-bit forward over 512-lane rows also measured faster lean:
+    // 16384 columns 4.2 -> 5.6 TB/s; narrower rows and fp32 did not)
+    if constexpr (sm_wide_layout(G, V, St::E) || (!BWD && St::E == 8 && G == 512)) {
+        if constexpr (!BWD) {
+            if (a.mask) return launch_wide<G, V, VEC, BWD, true>(a, s);
+        }
+        return launch_wide<G, V, VEC, BWD, false>(a, s);
+    } else {
+        constexpr int ROWS = SmGeometry<G>::ROWS;
+        const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
+        const void* k = reinterpret_cast<const void*>(&softmax_kernel<St, G, V, VEC, BWD>);
+        const int64_t grid = persistent_grid(k, SmGeometry<G>::NT, nblk);
+        hipLaunchKernelGGL((softmax_kernel<St, G, V, VEC, BWD>), dim3((unsigned)grid),
+                           dim3(SmGeometry<G>::NT), 0, s, a);
+        return hipGetLastError();
+    }
 }
 
 template <bool VEC, bool BWD>

@@ -13,9 +13,14 @@ pytestmark = pytest.mark.gpu
 
 DTYPES = [torch.float32, torch.float16, torch.bfloat16]
 SM_LAYOUTS_F32 = [(16, 1), (16, 2), (16, 4), (32, 2), (32, 4), (64, 2), (64, 4), (64, 8),
-                  (128, 4), (256, 4), (512, 4), (1024, 4)]
+                  (128, 4), (256, 4), (512, 4), (1024, 4), (1024, 5), (1024, 6), (1024, 7),
+                  (1024, 8)]
 SM_LAYOUTS_16 = [(16, 1), (16, 2), (32, 1), (32, 2), (64, 1), (64, 2), (64, 4), (128, 4),
-                 (256, 4), (512, 4)]
+                 (256, 4), (512, 4), (512, 6), (512, 8), (1024, 3), (1024, 4), (1024, 5),
+                 (1024, 6), (1024, 7), (1024, 8)]
+# the register layouts' widest rows (LN_MAX_COLS_SOFTMAX_*)
+MAX_FWD = {torch.float32: 32768, torch.float16: 65536, torch.bfloat16: 65536}
+MAX_BWD = {torch.float32: 32768, torch.float16: 49152, torch.bfloat16: 49152}
 
 
 def scores(rows, cols, dtype, seed=0, std=3.0):
@@ -108,6 +113,47 @@ def test_forced_layouts(orc, dtype):
             check(orc, d, y, yd, dx, 1.0, cols >= 64, 0.3, 4, name=f"sm.{g}x{v}")
     finally:
         mb.debug_force_path(0)
+
+
+WIDE = {torch.float32: [16385, 20000, 32767, 32768],
+        torch.float16: [16385, 24577, 49152, 65536],
+        torch.bfloat16: [16392, 40000, 49153, 65536]}
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_wide_rows(orc, dtype):
+    """Rows past 16384 columns in the lean 1024-lane register layouts (each
+    pass recomputes from the packed row), with dropout; up to the widest row
+    each direction holds (wider 16-bit backward rows take the two-pass path)."""
+    for cols in WIDE[dtype]:
+        assert cols <= MAX_FWD[dtype]
+        case(f"softmax wide {6}x{cols} {dtype} (backward in registers: {cols <= MAX_BWD[dtype]})")
+        d, y, yd, dx = run(6, cols, dtype, 0.5, False, 0.1, 11, data_seed=cols)
+        check(orc, d, y, yd, dx, 0.5, False, 0.1, 11, name=f"sm.wide.{cols}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_wide_rows_mask_causal_and_per_element(orc, dtype):
+    cols = 20000 if dtype == torch.float32 else 30000   # rows of whole 16-byte slots
+    case(f"softmax wide additive mask {6}x{cols} {dtype}")
+    mk = torch.zeros((3, cols), dtype=torch.float32)
+    mk[0, 100:9000] = -torch.inf             # padded keys
+    mk[1, :] = 1.5
+    mk[2, :] = -torch.inf                    # every key masked: zeros
+    mask = mk.to(dtype).cuda()
+    d, y, yd, dx = run(6, cols, dtype, 0.7, False, 0.2, 12, mask=mask, rows_per_mask=2)
+    check(orc, d, y, yd, dx, 0.7, False, 0.2, 12, mask=mask, rows_per_mask=2,
+          name="sm.wide.mask")
+    assert torch.all(y[4:] == 0)
+    # causal rows 0-47 of a wide row (keys past the query are not read)
+    case(f"softmax wide causal 48x{cols} {dtype}")
+    d, y, yd, dx = run(48, cols, dtype, 1.0, True, 0.1, 13)
+    check(orc, d, y, yd, dx, 1.0, True, 0.1, 13, name="sm.wide.causal")
+    # rows that are not a whole number of 16-byte slots: per-element loads
+    # and stores
+    case(f"softmax wide per-element path 5x{cols + 1} {dtype}")
+    d, y, yd, dx = run(5, cols + 1, dtype, 0.5, True, 0.1, 14)
+    check(orc, d, y, yd, dx, 0.5, True, 0.1, 14, name="sm.wide.odd")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

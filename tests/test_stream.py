@@ -1,6 +1,8 @@
 """GPU parity of the two-pass paths for rows too long for the register
-layouts: the attention softmax beyond 16384 columns and the cross-entropy
-beyond 65536 fp32 / 131072 16-bit classes, against the float64 oracle."""
+layouts (the attention softmax beyond 32768 fp32 / 65536 16-bit columns, the
+cross-entropy beyond 65536 fp32 / 131072 16-bit classes), against the float64
+oracle.  The module forces the two-pass path, so it is also checked at
+narrower widths."""
 import pytest
 import torch
 
@@ -11,6 +13,16 @@ from gpu_helpers import FMT, case, check_softmax_bwd, check_softmax_fwd, check_x
 pytestmark = pytest.mark.gpu
 
 DTYPES = [torch.float32, torch.float16, torch.bfloat16]
+
+
+@pytest.fixture(autouse=True)
+def two_pass():
+    """Every call in this module takes the two-pass path, also at widths the
+    register layouts hold (rows of 16385-65536 columns would otherwise go to
+    the wide register kernels)."""
+    mb.debug_force_two_pass(True)
+    yield
+    mb.debug_force_two_pass(False)
 
 
 def softmax_run(orc, rows, cols, dtype, scale=0.5, causal=False, p=0.0, seed=3, mask_rows=0,
