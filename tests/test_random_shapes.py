@@ -104,3 +104,32 @@ def test_random_shape(orc, idx):
                                             grad_scale=0.25)
         torch.cuda.synchronize()
         check_xent(orc, x, lab, cols, 0.1, 0.25, loss, dx, fmt, name="rnd.xent")
+
+
+@pytest.mark.parametrize("idx", range(10))
+def test_random_long_softmax_rows(orc, idx):
+    """The softmax's long-row register layouts (16385-65536 columns) on
+    seeded random widths, dtypes, scales, dropout rates and masks."""
+    g = np.random.default_rng([4711, idx])
+    dtype = DTYPES[int(g.integers(0, 3))]
+    top = 32768 if dtype == torch.float32 else 65536
+    cols = int(g.integers(16385, top + 1))
+    rows = int(g.integers(1, 9))
+    mis = bool(g.integers(0, 3) == 0)
+    p = float(g.choice([0.0, 0.1, 0.3]))
+    scale = float(g.uniform(0.05, 1.0))
+    case(f"random long softmax {idx}: {rows}x{cols} {dtype} misaligned={mis} p={p}")
+    cpu = synth.layer_inputs(rows, cols, dtype, seed=idx, x_std=3.0, names=("x", "dy"))
+    x, dy = place(cpu["x"], mis), place(cpu["dy"], mis)
+    mask = None
+    if idx % 3 == 0:
+        mk = synth.layer_inputs(1, cols, dtype, seed=idx + 50, x_std=2.0, names=("x",))["x"]
+        mask = place(mk, mis)
+    y, yd = mb.attn_softmax_fwd(x, scale, mask=mask, rows_per_mask=rows, p=p, seed=idx,
+                                want_dropped=p > 0)
+    dx = mb.attn_softmax_bwd(dy, y, scale, p=p, seed=idx)
+    torch.cuda.synchronize()
+    fmt = FMT[dtype]
+    check_softmax_fwd(orc, x, y, yd, fmt, scale=scale, mask=mask, rows_per_mask=rows, p=p,
+                      seed=idx, name="rnd.long_sm")
+    check_softmax_bwd(orc, dy, y, dx, fmt, scale=scale, p=p, seed=idx, name="rnd.long_sm_bwd")
