@@ -806,13 +806,13 @@ def main():
     ms_plain = timed(capture(plain_step, K), K)
     pb = plain_bytes(ROWS, COLS, 2)["step"]
 
-    # attainable bandwidth: plain copies moving the kernels' and the step's
-    # byte counts, rotated like the step, and a large copy (also the PMC
-    # calibration kernel)
+    # attainable bandwidth: plain copies moving 21 and 42 MB and the kernels'
+    # and the step's byte counts, rotated like the step, and a large copy
+    # (also the PMC calibration kernel)
     nb = algorithmic_bytes(ROWS, COLS, 2)
     copy_mb = {"fused_fwd": round(nb["fused_fwd"] / 1e6), "bwd": round(nb["bwd"] / 1e6),
                "step": round(nb["step"] / 1e6)}
-    copies = copy_rates(sorted(set(copy_mb.values())), S, dev, K)
+    copies = copy_rates(sorted(set(copy_mb.values()) | {21, 42}), S, dev, K)
     big_src = torch.empty(COPY_BYTES // 2, dtype=dtype, device=dev)
     big_dst = torch.empty_like(big_src)
     ms_bigcopy = timed(capture(lambda i: big_dst.copy_(big_src), 4), 4)
