@@ -77,11 +77,12 @@ typedef enum {
  * three column accumulators per value need the registers of twice as many
  * lanes). */
 #define LN_MAX_COLS_DROPOUT_BWD 8192
-/* Widest padded row (ld) of cross_entropy_fwd_bwd: 65536 fp32 or 131072
- * fp16/bf16 classes (the row is held in the registers of one 1024-lane
- * workgroup; GPT-2's 50257 and Llama-3's 128256 classes fit in bf16). */
+/* Widest padded row (ld) of cross_entropy_fwd_bwd held in registers (and so
+ * read once): 65536 fp32 or 163840 fp16/bf16 classes (the row is held in
+ * the registers of one 1024-lane workgroup; GPT-2's 50257, Llama-3's 128256
+ * and Qwen-2's 151936 classes fit in bf16). */
 #define LN_MAX_COLS_XENT_F32 65536
-#define LN_MAX_COLS_XENT_16 131072
+#define LN_MAX_COLS_XENT_16 163840
 /* Widest row of attn_softmax_fwd / attn_softmax_bwd held in registers (and
  * so read once): 32768 fp32 or 65536 fp16/bf16 scores (one 1024-lane
  * workgroup per row beyond 16384). */

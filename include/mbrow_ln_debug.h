@@ -25,7 +25,7 @@ extern "C" {
  *                  16x{1,2,4}, 32x1-5, 64x1-5, {128,256,512}x4.  The attention
  *                  softmax also has 1024x5-8 (fp32) and 512x{6,8}, 1024x3-8
  *                  (fp16/bf16; its backward 1024x3-6), the cross-entropy its
- *                  own set (1024 x up to 16).  The prologue
+ *                  own set (1024 x up to 16 fp32, 20 fp16/bf16).  The prologue
  *                  backward (bias_dropout_residual_ln_bwd) has its own set:
  *                  fp32 16x{1,2,4}, 32x1-4, 64x1-6, {128,256,512}x4;
  *                  fp16/bf16 16x{1,2}, 32x1-3, 64x1-3, {128,256,512}x2.

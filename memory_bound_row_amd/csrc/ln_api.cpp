@@ -216,7 +216,7 @@ static const int kXe16[][2] = {{16, 1}, {16, 2}, {32, 1}, {32, 2}, {64, 1}, {64,
                                {64, 4}, {128, 4}, {256, 4}, {512, 4}, {512, 7}, {512, 10},
                                {512, 13}, {1024, 4}, {1024, 5},
                                {1024, 6}, {1024, 7}, {1024, 8}, {1024, 10}, {1024, 12},
-                               {1024, 14}, {1024, 16}};
+                               {1024, 14}, {1024, 16}, {1024, 18}, {1024, 20}};
 
 // `slots`: 16-byte slots of the padded row (ceil(ld / E)).
 Path pick_xent_path(Dt dt, int64_t slots, bool vec) {

@@ -202,7 +202,7 @@ struct XeArgs {
     X(16, 1) X(16, 2) X(32, 1) X(32, 2) X(64, 1) X(64, 2) X(64, 4)          \
     X(128, 4) X(256, 4) X(512, 4) X(512, 7) X(512, 10) X(512, 13)          \
     X(1024, 4) X(1024, 5) X(1024, 6) X(1024, 7) X(1024, 8) X(1024, 10)     \
-    X(1024, 12) X(1024, 14) X(1024, 16)
+    X(1024, 12) X(1024, 14) X(1024, 16) X(1024, 18) X(1024, 20)
 
 Path pick_xent_path(Dt dt, int64_t slots, bool vec);
 hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s);

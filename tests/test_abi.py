@@ -319,6 +319,7 @@ def test_cross_entropy_validation(L):
     assert xent(L, cols=100, ld=STREAM_MAX + 1, dt=F32) == LN_ERR_UNSUPPORTED
     for dt in (F16, BF16):
         assert xent(L, cols=131072, ld=131072, rows=0, dt=dt) == LN_OK
+        assert xent(L, cols=163840, ld=163840, rows=0, dt=dt) == LN_OK
         assert xent(L, cols=131073, ld=131073, rows=0, dt=dt) == LN_OK
         assert xent(L, cols=STREAM_MAX + 1, ld=STREAM_MAX + 1, dt=dt) == LN_ERR_UNSUPPORTED
     for kw in ({"alpha": -0.1}, {"alpha": 1.5}, {"alpha": float("nan")},

@@ -1,6 +1,6 @@
 """GPU parity of the two-pass paths for rows too long for the register
 layouts (the attention softmax beyond 32768 fp32 / 65536 16-bit columns, the
-cross-entropy beyond 65536 fp32 / 131072 16-bit classes), against the float64
+cross-entropy beyond 65536 fp32 / 163840 16-bit classes), against the float64
 oracle.  The module forces the two-pass path, so it is also checked at
 narrower widths."""
 import pytest

@@ -18,7 +18,7 @@ LAYOUTS_F32 = [(16, 1), (16, 2), (16, 4), (32, 2), (32, 4), (64, 2), (64, 4), (6
 LAYOUTS_16 = [(16, 1), (16, 2), (32, 1), (32, 2), (64, 1), (64, 2), (64, 4), (128, 4),
               (256, 4), (512, 4), (512, 7), (512, 10), (512, 13), (1024, 4), (1024, 5),
               (1024, 6), (1024, 7), (1024, 8), (1024, 10), (1024, 12), (1024, 14),
-              (1024, 16)]
+              (1024, 16), (1024, 18), (1024, 20)]
 GPT2_V, GPT2_VP = 50257, 50304   # GPT-2's vocabulary and its padded row
 
 
@@ -51,10 +51,12 @@ def test_gpt2_full_batch_sampled(orc):
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
-@pytest.mark.parametrize("cols,ld", [(128256, 128256), (128255, 128255)])
+@pytest.mark.parametrize("cols,ld", [(128256, 128256), (128255, 128255), (151936, 151936),
+                                     (163840, 163840)])
 def test_llama3_vocabulary(orc, dtype, cols, ld):
     # a 128K vocabulary (the lecture notes' example of logits outgrowing the
-    # weights); the odd width takes the per-element path at 16 slots per lane
+    # weights); the odd width takes the per-element path at 16 slots per lane;
+    # 151936 classes (Qwen-2) and the widest 16-bit register row, 163840
     case(f"cross-entropy 40x{cols} ld {ld} {dtype}")
     run(orc, 40, cols, ld, dtype, 12, name=f"xent.{cols}")
 
