@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--no-cpp-launch", action="store_true",
                     help="with --configs: skip the C++ launch-loop child process (for runs "
                          "under a profiler, whose preloaded library the child inherits)")
+    ap.add_argument("--two-pass-kernels", action="store_true",
+                    help="launch each two-pass kernel (cross-entropy over 2048 x 256000 bf16, "
+                         "softmax forward and backward over 2048 x 131072 fp16) three times "
+                         "and exit: a short program for hardware-counter runs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "this benchmark into profiles/traffic.json and exit")
@@ -307,6 +311,32 @@ def cpu_baseline(inp_cpu, target_s: float):
                               "sample": f"{reps_p} full step(s), rows split over {nt} threads, "
                                         f"{t_par:.1f} s"}
     return out
+
+
+def two_pass_kernels() -> None:
+    """Three launches of each two-pass kernel on rows past the register
+    layouts, nothing else timed or printed (for rocprofv3 --pmc)."""
+    import torch
+    import memory_bound_row_amd as mb
+    from memory_bound_row_amd import synth
+    dev = torch.device("cuda", 0)
+    x = synth.logits(2048, 256000, torch.bfloat16, seed=SEED).to(dev)
+    lab = synth.class_labels(2048, 256000, seed=SEED).to(dev)
+    loss = torch.empty(2048, dtype=torch.float32, device=dev)
+    dx = torch.empty_like(x)
+    for _ in range(3):
+        mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0, loss=loss,
+                                 dlogits=dx)
+    torch.cuda.synchronize()
+    del x, dx
+    d = synth.layer_inputs(2048, 131072, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
+    s, dy = d["x"].to(dev), d["dy"].to(dev)
+    y, ds = torch.empty_like(s), torch.empty_like(s)
+    for _ in range(3):
+        mb.attn_softmax_fwd(s, 0.125, y=y)
+        mb.attn_softmax_bwd(dy, y, 0.125, dx=ds)
+    torch.cuda.synchronize()
+    print("two-pass kernels: done", flush=True)
 
 
 def configs_report(cpp_launch: bool = True) -> None:
@@ -731,6 +761,9 @@ def main():
         return
     if args.configs:
         configs_report(cpp_launch=not args.no_cpp_launch)
+        return
+    if args.two_pass_kernels:
+        two_pass_kernels()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method's rows "
