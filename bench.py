@@ -313,6 +313,25 @@ def cpu_baseline(inp_cpu, target_s: float):
     return out
 
 
+def oracle_rate(prep, work, row_bytes, max_rows, target_s=0.5):
+    """CPU baseline of a workload: the float64 oracle's rate on a sample of
+    its rows.  prep(n) builds the oracle's inputs for the first n rows
+    (untimed); work(args) runs the oracle's computation of the workload on
+    them (timed, single thread).  n doubles until one run takes target_s or
+    reaches max_rows."""
+    n = 1
+    while True:
+        args = prep(n)
+        t0 = time.perf_counter()
+        work(args)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= max_rows:
+            return {"value": round(n * row_bytes / dt / 1e9, 3), "unit": "GB/s",
+                    "cores": 1, "kind": "oracle",
+                    "sample": f"the first {n} rows, {dt:.2f} s single-threaded"}
+        n = min(max_rows, n * 2)
+
+
 def two_pass_kernels() -> None:
     """Three launches of each two-pass kernel on rows past the register
     layouts, nothing else timed or printed (for rocprofv3 --pmc)."""
@@ -364,7 +383,11 @@ def configs_report(cpp_launch: bool = True) -> None:
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
-        forward + backward (each pass moves more than the cache holds)."""
+        forward + backward (each pass moves more than the cache holds).
+    Rates of 16 MB or more come with the plain copy's rate at the same byte
+    count; the prologue backward, the softmax with dropout, add + RMSNorm and
+    the cross-entropy also with a CPU baseline (the float64 oracle on a
+    sample of the rows, one thread)."""
     import subprocess
     tool = os.path.join(ROOT, "memory_bound_row_amd", "launch_bench")
     if not os.path.exists(tool):
@@ -377,8 +400,10 @@ def configs_report(cpp_launch: bool = True) -> None:
             raise RuntimeError(f"launch_bench failed: {r.stderr.strip()}")
         cpp[rows] = json.loads(r.stdout)
 
+    import numpy as np
     import torch
     import memory_bound_row_amd as mb
+    import oracle as orc   # the CPU baselines only
     from memory_bound_row_amd import synth
     torch.cuda.init()
     dev = torch.device("cuda", 0)
@@ -544,11 +569,29 @@ def configs_report(cpp_launch: bool = True) -> None:
     ms_l = timed(capture(layer, n), n)
     bb = 5 * R * C * 2 + C * 2 + 8 * R + 12 * C
     lb = algorithmic_bytes(R, C, 2)["fused_fwd"] + bb
+    def pro_prep(n):
+        i = {k: synth.as_f64(v) for k, v in synth.layer_inputs(n, C, dt16, seed=SEED).items()}
+        ez = synth.as_f64(synth.layer_inputs(n, C, dt16, seed=SEED + 1, names=("dy",))["dy"])
+        keep = orc.dropout_keep_rows(SEED, P_DROP, 0, n, C)
+        z = orc.round_to(orc.bias_dropout_residual(i["x"], i["bias"], i["residual"], keep,
+                                                   P_DROP), "bf16")
+        _, mu, rs = orc.ln_fwd(z, i["gamma"], i["beta"], EPS)
+        return i, ez, keep, z, np.float64(np.float32(mu)), np.float64(np.float32(rs))
+
+    def pro_work(args):
+        i, ez, keep, z, mu, rs = args
+        dz = orc.ln_bwd_dx(i["dy"], z, i["gamma"], mu, rs) + ez
+        orc.round_to(dz, "bf16")
+        dxin, _, _ = orc.dropout_residual_bwd(dz, keep, P_DROP)
+        orc.round_to(dxin, "bf16")
+        orc.ln_bwd_params(i["dy"], z, mu, rs)
+
     emit({"workload": "fused backward of bias+dropout(p=0.1)+residual+LayerNorm "
                       "(dz_extra given), 8192x1280 bf16, rotated",
           "bytes_per_pass": bb, "us_per_pass": round(ms_b * 1e3, 3),
           "GBps": round(bb / (ms_b * 1e-3) / 1e9, 1),
-          "pct_of_hbm_peak": round(100.0 * bb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)})
+          "pct_of_hbm_peak": round(100.0 * bb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+          "cpu_baseline": oracle_rate(pro_prep, pro_work, 5 * C * 2, R)})
     emit({"workload": "training layer: fused forward + fused backward (p=0.1), "
                       "8192x1280 bf16, rotated",
           "bytes_per_pass": lb, "us_per_pass": round(ms_l * 1e3, 3),
@@ -592,8 +635,21 @@ def configs_report(cpp_launch: bool = True) -> None:
         read = t * (L + 1) / (2 * L) if causal else t     # scores past the query are not read
         fb = read + t * (2 if p > 0 else 1)
         bb = 2 * read + t
+        def sm_prep(n):
+            i = synth.layer_inputs(n, L, dt, seed=SEED, x_std=3.0, names=("x", "dy"))
+            keep = orc.dropout_keep_rows(SEED, p, 0, n, L) if p > 0 else None
+            return synth.as_f64(i["x"]), synth.as_f64(i["dy"]), keep
+
+        def sm_work(args):
+            x, dy, keep = args
+            y = orc.attn_softmax_fwd(x, scale, causal=causal)
+            if keep is not None:
+                orc.round_to(np.where(keep == 1, y / (1.0 - p), 0.0), "f16")
+            orc.attn_softmax_bwd(dy, orc.round_to(y, "f16"), keep, p, scale)
+
+        cpu = None if causal else oracle_rate(sm_prep, sm_work, (fb + bb) / rows, rows)
         emit({"workload": label, "rows": rows, "cols": L, "storage": "float16",
-              "causal": causal, "p": p,
+              "causal": causal, "p": p, "cpu_baseline": cpu,
               "fwd_bytes": int(fb), "fwd_us": round(msf * 1e3, 3),
               "fwd_GBps": round(fb / (msf * 1e-3) / 1e9, 1),
               "fwd_pct_of_hbm_peak": round(100.0 * fb / (msf * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
@@ -656,6 +712,23 @@ def configs_report(cpp_launch: bool = True) -> None:
                         "bwd_GBps": round(bb / (msb * 1e-3) / 1e9, 1),
                         "bwd_pct_of_hbm_peak": round(100.0 * bb / (msb * 1e-3) / 1e9
                                                      / HBM_PEAK_GBPS, 2)})
+
+            def rms_prep(n):
+                i = {k: synth.as_f64(v) for k, v in synth.layer_inputs(
+                    n, cols, dt, seed=SEED, names=("x", "residual", "gamma", "dy")).items()}
+                ez = synth.as_f64(synth.layer_inputs(n, cols, dt, seed=SEED + 1,
+                                                     names=("dy",))["dy"])
+                return i, ez
+
+            def rms_work(args):
+                i, ez = args
+                z = orc.round_to(i["x"] + i["residual"], "bf16")
+                y, rs = orc.rmsnorm_fwd(z, i["gamma"], 1e-6)
+                orc.round_to(y, "bf16")
+                dz, _, _ = orc.rmsnorm_bwd(i["dy"], z, i["gamma"], np.float64(np.float32(rs)))
+                orc.round_to(dz + ez, "bf16")
+
+            rec["cpu_baseline"] = oracle_rate(rms_prep, rms_work, 8 * cols * 2, rows)
         emit(rec)
         del st, ws
         torch.cuda.empty_cache()
@@ -688,12 +761,21 @@ def configs_report(cpp_launch: bool = True) -> None:
         ms = timed(capture(f, n), n)
         ms_ip = timed(capture(g, n), n)
         b = 2 * rows * cols * s + 12 * rows
+
+        def xe_prep(k):
+            xs = synth.as_f64(synth.logits(k, ld, dt, seed=SEED))[:, :cols]
+            return np.ascontiguousarray(xs), synth.class_labels(k, cols, seed=SEED).numpy()
+
+        def xe_work(args):
+            orc.cross_entropy(args[0], args[1], 0.1, 1.0 / rows)
+
         emit({"workload": label, "rows": rows, "cols": cols, "ld": ld,
               "storage": str(dt)[6:], "bytes_per_pass": b, "iters": n,
               "us_per_pass": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
               "pct_of_hbm_peak": round(100.0 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
               "in_place_us": round(ms_ip * 1e3, 3),
-              "in_place_GBps": round(b / (ms_ip * 1e-3) / 1e9, 1)})
+              "in_place_GBps": round(b / (ms_ip * 1e-3) / 1e9, 1),
+              "cpu_baseline": oracle_rate(xe_prep, xe_work, b / rows, rows)})
         del x, dx, lab, loss
         torch.cuda.empty_cache()
 
