@@ -755,7 +755,8 @@ def configs_report(cpp_launch: bool = True) -> None:
             mb.cross_entropy_fwd_bwd(x, lab, cols=cols, label_smoothing=0.1,
                                      grad_scale=1.0 / rows, loss=loss, dlogits=x)
 
-        f(0)
+        for i in range(3):   # first touches of the fresh 0.4-3 GB buffers
+            f(i)
         torch.cuda.synchronize()
         n = 20
         ms = timed(capture(f, n), n)
@@ -803,7 +804,9 @@ def configs_report(cpp_launch: bool = True) -> None:
 
         mb.debug_force_two_pass(two_pass)
         try:
-            lf(0)
+            for i in range(3):
+                lf(i)
+                lb(i)
             torch.cuda.synchronize()
             n = 10
             msf = timed(capture(lf, n), n)
