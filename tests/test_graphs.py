@@ -96,6 +96,21 @@ def test_softmax_in_a_graph():
     check_replays(run, [y, yd, dx])
 
 
+def test_long_softmax_rows_in_a_graph():
+    case("graph: attention softmax over 40000-key bf16 rows (lean register layouts)")
+    d = dev(synth.layer_inputs(12, 40000, torch.bfloat16, seed=6, x_std=3.0,
+                               names=("x", "dy")))
+    mk = dev(synth.layer_inputs(3, 40000, torch.bfloat16, seed=7, names=("x",)))["x"]
+    y, yd, dx = (torch.empty_like(d["x"]) for _ in range(3))
+
+    def run():
+        mb.attn_softmax_fwd(d["x"], 0.25, mask=mk, rows_per_mask=4, p=0.1, seed=3, y=y,
+                            y_dropped=yd)
+        mb.attn_softmax_bwd(d["dy"], y, 0.25, p=0.1, seed=3, dx=dx)
+
+    check_replays(run, [y, yd, dx])
+
+
 def test_rmsnorm_in_a_graph():
     case("graph: add + RMSNorm forward and backward")
     R, C = 512, 4096
