@@ -19,7 +19,7 @@ DTYPES = [torch.float32, torch.float16, torch.bfloat16]
 KINDS = ["layernorm", "fused", "prologue_bwd", "softmax", "rmsnorm", "xent"]
 MAX_COLS = {"layernorm": 16384, "fused": 16384, "prologue_bwd": 8192, "softmax": 16384,
             "rmsnorm": 16384, "xent": 60000}
-N_CASES = 36
+N_CASES = 72
 
 
 def draw(idx):
