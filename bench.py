@@ -63,10 +63,11 @@ def parse():
     ap.add_argument("--no-cpp-launch", action="store_true",
                     help="with --configs: skip the C++ launch-loop child process (for runs "
                          "under a profiler, whose preloaded library the child inherits)")
-    ap.add_argument("--two-pass-kernels", action="store_true",
-                    help="launch each two-pass kernel (cross-entropy over 2048 x 256000 bf16, "
-                         "softmax forward and backward over 2048 x 131072 fp16) three times "
-                         "and exit: a short program for hardware-counter runs")
+    ap.add_argument("--counter-sample", action="store_true",
+                    help="launch the other operators' kernels three times each at their "
+                         "workloads (prologue backward, attention softmax, add + RMSNorm, "
+                         "cross-entropy, and the two-pass paths) and exit: a short program "
+                         "for hardware-counter runs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "this benchmark into profiles/traffic.json and exit")
@@ -332,13 +333,48 @@ def oracle_rate(prep, work, row_bytes, max_rows, target_s=0.5):
         n = min(max_rows, n * 2)
 
 
-def two_pass_kernels() -> None:
-    """Three launches of each two-pass kernel on rows past the register
-    layouts, nothing else timed or printed (for rocprofv3 --pmc)."""
+def counter_sample() -> None:
+    """Three launches of each of the other operators' kernels at their
+    workloads, nothing timed (for rocprofv3 --pmc): the prologue backward
+    (8192 x 1280 bf16, dz_extra given), the attention softmax forward (y and
+    dropped y) and backward (8 x 16 x 512 x 512 fp16, p = 0.1), add + RMSNorm
+    forward and backward (2048 x 4096 bf16), the cross-entropy (8192 x 50257
+    bf16, rows of 50304), and the two-pass paths (cross-entropy over 2048 x
+    256000 bf16, softmax over 2048 x 131072 fp16)."""
     import torch
     import memory_bound_row_amd as mb
     from memory_bound_row_amd import synth
     dev = torch.device("cuda", 0)
+    bf, hf = torch.bfloat16, torch.float16
+
+    d = {k: v.to(dev) for k, v in synth.layer_inputs(ROWS, COLS, bf, seed=SEED).items()}
+    ez = synth.layer_inputs(ROWS, COLS, bf, seed=SEED + 1, names=("dy",))["dy"].to(dev)
+    z, _, mean, rstd, _ = mb.bias_dropout_residual_ln_fwd(d["x"], d["bias"], d["residual"],
+                                                          d["gamma"], d["beta"], P_DROP, SEED,
+                                                          EPS)
+    for _ in range(3):
+        mb.bias_dropout_residual_ln_bwd(d["dy"], z, d["gamma"], mean, rstd, P_DROP, SEED,
+                                        dz_extra=ez)
+    del d, ez, z
+    d = {k: v.to(dev) for k, v in synth.layer_inputs(8 * 16 * 512, 512, hf, seed=SEED,
+                                                     x_std=3.0, names=("x", "dy")).items()}
+    for _ in range(3):
+        y, _ = mb.attn_softmax_fwd(d["x"], 0.125, p=0.1, seed=SEED, want_dropped=True)
+        mb.attn_softmax_bwd(d["dy"], y, 0.125, p=0.1, seed=SEED)
+    del d, y
+    d = {k: v.to(dev) for k, v in synth.layer_inputs(
+        2048, 4096, bf, seed=SEED, names=("x", "residual", "gamma", "dy")).items()}
+    for _ in range(3):
+        z, _, rs = mb.add_rmsnorm_fwd(d["x"], d["gamma"], 1e-6, residual=d["residual"])
+        mb.add_rmsnorm_bwd(d["dy"], z, d["gamma"], rs, dz_extra=d["residual"])
+    del d, z
+    x = synth.logits(8192, 50304, bf, seed=SEED).to(dev)
+    lab = synth.class_labels(8192, 50257, seed=SEED).to(dev)
+    for _ in range(3):
+        mb.cross_entropy_fwd_bwd(x, lab, cols=50257, label_smoothing=0.1, grad_scale=1.0 / 8192)
+    torch.cuda.synchronize()
+    del x
+
     x = synth.logits(2048, 256000, torch.bfloat16, seed=SEED).to(dev)
     lab = synth.class_labels(2048, 256000, seed=SEED).to(dev)
     loss = torch.empty(2048, dtype=torch.float32, device=dev)
@@ -355,7 +391,7 @@ def two_pass_kernels() -> None:
         mb.attn_softmax_fwd(s, 0.125, y=y)
         mb.attn_softmax_bwd(dy, y, 0.125, dx=ds)
     torch.cuda.synchronize()
-    print("two-pass kernels: done", flush=True)
+    print("counter sample: done", flush=True)
 
 
 def configs_report(cpp_launch: bool = True) -> None:
@@ -847,8 +883,8 @@ def main():
     if args.configs:
         configs_report(cpp_launch=not args.no_cpp_launch)
         return
-    if args.two_pass_kernels:
-        two_pass_kernels()
+    if args.counter_sample:
+        counter_sample()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method's rows "
