@@ -47,6 +47,9 @@ int main(void) {
     expect("cross_entropy_fwd_bwd ld",
            cross_entropy_fwd_bwd(a, lab, f, NULL, 4, 8, 7, 0.0f, 1.0f, LN_BF16, s), LN_ERR_SHAPE);
     expect("empty call", ln_fwd(a, a, a, a, NULL, NULL, 0, 8, 1e-5f, LN_BF16, s), LN_OK);
+    expect("hbm_copy size", hbm_copy(a, f, 20, s), LN_ERR_PARAM);
+    expect("hbm_copy null", hbm_copy(NULL, f, 16, s), LN_ERR_NULL);
+    expect("hbm_copy empty", hbm_copy(a, f, 0, s), LN_OK);
 
     if (ln_bwd_workspace_bytes(8192, 1280) != (size_t)256 * 2 * 1280 * 4) ++fails;
     if (bias_dropout_residual_ln_bwd_workspace_bytes(8192, 1280) != (size_t)256 * 3 * 1280 * 4)
