@@ -8,12 +8,13 @@ The arithmetic lives in ``ln_oracle.c`` (plain C, float64); this module only
 builds it with gcc and marshals numpy arrays through ctypes.  ``compare``
 holds the tolerance rule used to check GPU outputs against it.
 
-Parity unpinned: the Philox-based dropout mask.  Philox4x32-10 is written
-here from its published definition (Salmon et al., SC'11), and the pages
-print no known-answer values for it; the counter/key layout is this
-library's own (the pages only say the mask is regenerated from a seed).  The
-tests pin the layout and the keep statistics, and the GPU and oracle
-implementations, written independently, are checked against each other bit
-for bit.
+The Philox-based dropout mask: Philox4x32-10 is written here from its
+published definition (Salmon et al., SC'11); the pages print no known-answer
+values for it, so its round function is pinned against an independent
+implementation of the same generator (rocRAND's host engine, in
+tests/test_philox_pin.py).  The counter/key layout is this library's own
+(the pages only say the mask is regenerated from a seed); the tests pin the
+layout and the keep statistics, and the GPU and oracle implementations,
+written independently, are checked against each other bit for bit.
 """
 from .oracle import *  # noqa: F401,F403

@@ -24,9 +24,10 @@
  *
  * Pins: every function is checked in tests/test_oracle_pins.py against
  * something other than itself (worked examples printed on the pages, closed
- * forms, identities, finite differences), except the Philox4x32-10 round
- * function: parity unpinned (no known-answer values on the pages; its
- * layout and statistics are pinned, its bits checked against the GPU's).
+ * forms, identities, finite differences); the Philox4x32-10 round function,
+ * for which the pages print no known-answer values, is pinned against an
+ * independent implementation of the published generator (rocRAND's host
+ * engine) in tests/test_philox_pin.py.
  */
 #ifndef MBROW_LN_ORACLE_H
 #define MBROW_LN_ORACLE_H

@@ -3,9 +3,9 @@
 CPU only.  Each test checks the oracle against something other than itself:
 values printed on the pages (tests/golden), closed forms, identities, finite
 differences, an independent algorithm, or a library routine for a special
-case.  The Philox4x32-10 function itself is parity unpinned: no known-answer
-values for it are on the pages, so only its layout and statistics are pinned
-here and its bits are checked GPU against oracle.
+case.  The Philox4x32-10 function itself is pinned in tests/test_philox_pin.py
+against an independent implementation of the published generator; its
+layout and statistics are pinned here.
 """
 import math
 import os
