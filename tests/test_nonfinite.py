@@ -1,0 +1,172 @@
+"""Row isolation under non-finite inputs (GPU).
+
+A few rows of each input hold +Inf, NaN or -Inf in one element.  Every other
+row -- including rows that share a wave, a workgroup and a reduction tree
+with a poisoned one -- must still equal the float64 oracle under the usual
+tolerance, and each poisoned row must be finite exactly where the oracle's
+is: a reduction that mixed rows, or masked another row's lanes by
+multiplying with 0, would spread the NaN.  The column sums show the same
+separation: dbeta sums dy alone and stays finite and exact, while dgamma
+(which sums dy * xhat) is non-finite in every column, as in the oracle.
+Where a -Inf is a legal value (a masked score for the softmax, a logit of
+probability 0), the row stays finite and is checked like the others; in the
+fused forward a poisoned element that the mask drops adds exactly 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_amd as mb
+from memory_bound_row_amd import synth
+from oracle import compare as cmp
+from gpu_helpers import (EPS, FMT, assert_reports, case, check_bwd, check_fwd,
+                         check_rmsnorm_fwd, check_softmax_bwd, check_softmax_fwd, check_xent,
+                         dev, f64)
+
+pytestmark = pytest.mark.gpu
+
+ROWS = 48
+POISON = ((5, 3, np.inf), (17, -1, np.nan), (30, 0, -np.inf))   # (row, column, value)
+
+
+def poison(t):
+    for r, c, v in POISON:
+        t[r, c] = v
+
+
+def split(ref):
+    """Rows where the oracle's output is finite throughout, and the rest."""
+    ok = np.isfinite(ref.reshape(ref.shape[0], -1)).all(axis=1)
+    return np.nonzero(ok)[0].tolist(), np.nonzero(~ok)[0].tolist()
+
+
+def same_finiteness(name, got, ref):
+    g = f64(got).reshape(ref.shape)
+    bad = np.isfinite(g) != np.isfinite(ref)
+    assert not bad.any(), f"{name}: {int(bad.sum())} elements differ in finiteness"
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("cols", [64, 1000, 1280, 4096])
+def test_layernorm(orc, dtype, cols):
+    case(f"LayerNorm fwd + bwd with non-finite rows {ROWS}x{cols} {dtype}")
+    inp = dev(synth.layer_inputs(ROWS, cols, dtype, seed=31, names=("x", "gamma", "beta", "dy")))
+    x = inp["x"]
+    poison(x)
+    y, mean, rstd = mb.ln_fwd(x, inp["gamma"], inp["beta"], EPS)
+    dx, dg, db = mb.ln_bwd(inp["dy"], x, inp["gamma"], mean, rstd)
+    torch.cuda.synchronize()
+    y_ref, _, _ = orc.ln_fwd(f64(x), f64(inp["gamma"]), f64(inp["beta"]), EPS)
+    good, bad = split(y_ref)
+    assert sorted(bad) == sorted(r for r, _, _ in POISON)
+    g = torch.as_tensor(good, device="cuda")
+    check_fwd(orc, x[g], inp["gamma"], inp["beta"], y[g], mean[g], rstd[g], FMT[dtype],
+              name="nonfinite.ln")
+    same_finiteness("nonfinite.ln.y", y[bad], y_ref[bad])
+    # dx from the stored statistics of each row (non-finite in the poisoned ones)
+    check_bwd(orc, inp["dy"][g], x[g], inp["gamma"], mean[g], rstd[g], dx[g], None, None,
+              FMT[dtype], name="nonfinite.ln_bwd")
+    dx_ref = orc.ln_bwd_dx(f64(inp["dy"])[bad], f64(x)[bad], f64(inp["gamma"]),
+                           f64(mean)[bad], f64(rstd)[bad])
+    same_finiteness("nonfinite.ln_bwd.dx", dx[bad], dx_ref)
+    dg_ref, db_ref, _, sb = orc.ln_bwd_params(f64(inp["dy"]), f64(x), f64(mean), f64(rstd))
+    same_finiteness("nonfinite.dgamma", dg, dg_ref)
+    assert not np.isfinite(dg_ref).any()
+    assert_reports(cmp.check_colsum("nonfinite.dbeta", f64(db), db_ref, sb, ROWS, FMT[dtype]))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+@pytest.mark.parametrize("cols", [64, 1000, 4096])
+def test_softmax(orc, dtype, cols):
+    case(f"softmax fwd + bwd with non-finite rows {ROWS}x{cols} {dtype}")
+    d = dev(synth.layer_inputs(ROWS, cols, dtype, seed=32, names=("x", "dy")))
+    x = d["x"]
+    poison(x)
+    y, _ = mb.attn_softmax_fwd(x, 0.5)
+    dx = mb.attn_softmax_bwd(d["dy"], y, 0.5)
+    torch.cuda.synchronize()
+    y_ref = orc.attn_softmax_fwd(f64(x), scale=0.5, mask=None, rows_per_mask=1, causal=False)
+    good, bad = split(y_ref)
+    assert sorted(bad) == [5, 17]          # the -Inf score is a masked key
+    g = torch.as_tensor(good, device="cuda")
+    check_softmax_fwd(orc, x[g], y[g], None, FMT[dtype], scale=0.5, name="nonfinite.sm")
+    same_finiteness("nonfinite.sm.y", y[bad], y_ref[bad])
+    check_softmax_bwd(orc, d["dy"][g], y[g], dx[g], FMT[dtype], scale=0.5,
+                      name="nonfinite.sm_bwd")
+    dx_ref = orc.attn_softmax_bwd(f64(d["dy"])[bad], f64(y)[bad], keep=None, p=0.0, scale=0.5)
+    same_finiteness("nonfinite.sm_bwd.dx", dx[bad], dx_ref)
+
+
+@pytest.mark.parametrize("cols", [1280, 4096])
+def test_add_rmsnorm(orc, cols):
+    case(f"add + RMSNorm fwd with non-finite rows {ROWS}x{cols} bf16")
+    dt = torch.bfloat16
+    d = dev(synth.layer_inputs(ROWS, cols, dt, seed=33, names=("x", "residual", "gamma")))
+    x = d["x"]
+    poison(x)
+    z, y, rstd = mb.add_rmsnorm_fwd(x, d["gamma"], 1e-6, residual=d["residual"])
+    torch.cuda.synchronize()
+    y_ref, rs_ref = orc.rmsnorm_fwd(f64(z), f64(d["gamma"]), 1e-6)
+    good, bad = split(y_ref)
+    assert sorted(bad) == sorted(r for r, _, _ in POISON)
+    g = torch.as_tensor(good, device="cuda")
+    check_rmsnorm_fwd(orc, x[g], d["residual"][g], d["gamma"], z[g], y[g], rstd[g], FMT[dt],
+                      1e-6, name="nonfinite.rms")
+    # an infinite element: rstd = 0, the rest of its row exactly 0, the element NaN
+    same_finiteness("nonfinite.rms.y", y[bad], y_ref[bad])
+    same_finiteness("nonfinite.rms.rstd", rstd[bad], rs_ref[bad])
+    yb, rb = f64(y[bad]), y_ref[bad]
+    both = np.isfinite(yb) & np.isfinite(rb)
+    assert np.array_equal(yb[both], rb[both])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("cols", [1000, 50257])
+def test_cross_entropy(orc, dtype, cols):
+    case(f"cross-entropy with non-finite rows {ROWS}x{cols} {dtype}")
+    x = dev(synth.layer_inputs(ROWS, cols, dtype, seed=34, names=("x",)))["x"]
+    poison(x)
+    lab = torch.randint(0, cols, (ROWS,), device="cuda",
+                        generator=torch.Generator(device="cuda").manual_seed(35))
+    loss, dx = mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0)
+    torch.cuda.synchronize()
+    loss_ref, dx_ref = orc.cross_entropy(f64(x), lab.cpu().numpy(), 0.1, 1.0, grad=True)
+    bad = sorted(r for r, _, _ in POISON)
+    good = [r for r in range(ROWS) if r not in bad]
+    check_xent(orc, x, lab, cols, 0.1, 1.0, loss, dx, FMT[dtype], rows_sel=good,
+               name="nonfinite.xent")
+    # a -Inf logit has probability 0: the smoothed loss is +Inf, the gradient finite
+    same_finiteness("nonfinite.xent.loss", loss[bad], loss_ref[bad])
+    same_finiteness("nonfinite.xent.dx", dx[bad], dx_ref[bad])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("cols", [64, 1280])
+def test_fused_forward(orc, dtype, cols):
+    """A dropped element contributes exactly 0 whatever its value: a poisoned
+    row whose poisoned element the mask drops stays finite (z = residual
+    there), one whose element is kept turns non-finite."""
+    case(f"fused forward with non-finite rows {ROWS}x{cols} {dtype}")
+    p, seed = 0.5, 4242
+    d = dev(synth.layer_inputs(ROWS, cols, dtype, seed=36,
+                               names=("x", "residual", "bias", "gamma", "beta")))
+    x = d["x"]
+    # every row poisoned at its own column, so some elements are kept and some dropped
+    for r in range(ROWS):
+        x[r, (7 * r) % cols] = (np.inf, np.nan, -np.inf)[r % 3]
+    z, y, mean, rstd, _ = mb.bias_dropout_residual_ln_fwd(x, d["bias"], d["residual"],
+                                                          d["gamma"], d["beta"], p, seed, EPS)
+    torch.cuda.synchronize()
+    keep = orc.dropout_keep(seed, p, ROWS, cols)
+    z_ref = orc.bias_dropout_residual(f64(x), f64(d["bias"]), f64(d["residual"]), keep, p)
+    good, bad = split(z_ref)
+    hit = keep[np.arange(ROWS), (7 * np.arange(ROWS)) % cols] == 1
+    assert bad == np.nonzero(hit)[0].tolist() and len(good) > 0 and len(bad) > 0
+    g = torch.as_tensor(good, device="cuda")
+    assert_reports(cmp.check_elementwise("nonfinite.fused.z", f64(z)[good], z_ref[good],
+                                         FMT[dtype]))
+    check_fwd(orc, z[g], d["gamma"], d["beta"], y[g], mean[g], rstd[g], FMT[dtype],
+              name="nonfinite.fused.ln")
+    same_finiteness("nonfinite.fused.z", z[bad], z_ref[bad])
+    y_ref, _, _ = orc.ln_fwd(f64(z)[bad], f64(d["gamma"]), f64(d["beta"]), EPS)
+    same_finiteness("nonfinite.fused.y", y[bad], y_ref)
