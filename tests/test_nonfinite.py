@@ -170,3 +170,88 @@ def test_fused_forward(orc, dtype, cols):
     same_finiteness("nonfinite.fused.z", z[bad], z_ref[bad])
     y_ref, _, _ = orc.ln_fwd(f64(z)[bad], f64(d["gamma"]), f64(d["beta"]), EPS)
     same_finiteness("nonfinite.fused.y", y[bad], y_ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("cols", [64, 1280])
+def test_prologue_backward(orc, dtype, cols):
+    """Poisoned rows of z: their dz is non-finite throughout, their dx only
+    where the mask keeps; dbias is non-finite exactly in the columns where a
+    poisoned row is kept, dgamma everywhere, dbeta nowhere."""
+    import math
+    case(f"prologue backward with non-finite rows {ROWS}x{cols} {dtype}")
+    p, seed = 0.3, 99
+    d = dev(synth.layer_inputs(ROWS, cols, dtype, seed=37,
+                               names=("x", "residual", "gamma", "beta", "dy")))
+    z, ez = d["x"], d["residual"]
+    poison(z)
+    _, mean, rstd = mb.ln_fwd(z, d["gamma"], d["beta"], EPS)
+    dres, dx, dg, db, dbias = mb.bias_dropout_residual_ln_bwd(d["dy"], z, d["gamma"], mean,
+                                                              rstd, p, seed, dz_extra=ez)
+    torch.cuda.synchronize()
+    dy64, z64, g64 = f64(d["dy"]), f64(z), f64(d["gamma"])
+    mu64, rs64, ez64 = f64(mean), f64(rstd), f64(ez)
+    dz_ref = orc.ln_bwd_dx(dy64, z64, g64, mu64, rs64) + ez64
+    scale = orc.ln_bwd_dx_scale(dy64, z64, g64, mu64, rs64) + np.abs(ez64)
+    keep = orc.dropout_keep(seed, p, ROWS, cols)
+    dx_ref, dbias_ref, sbias = orc.dropout_residual_bwd(dz_ref, keep, p)
+    good, bad = split(dz_ref)
+    assert sorted(bad) == sorted(r for r, _, _ in POISON)
+    s = 1.0 / (1.0 - np.float64(np.float32(p)))
+    dx_scale = np.where(keep == 1, scale * s, 0.0)
+    fmt = FMT[dtype]
+    assert_reports(
+        cmp.check_elementwise("nonfinite.drop.dresidual", f64(dres)[good], dz_ref[good], fmt,
+                              term_scale=scale[good], row_len=cols),
+        cmp.check_elementwise("nonfinite.drop.dx", f64(dx)[good], dx_ref[good], fmt,
+                              term_scale=dx_scale[good], row_len=cols))
+    same_finiteness("nonfinite.drop.dresidual", dres[bad], dz_ref[bad])
+    same_finiteness("nonfinite.drop.dx", dx[bad], dx_ref[bad])
+    assert np.all(f64(dx)[keep == 0] == 0.0)
+    same_finiteness("nonfinite.drop.dbias", dbias, dbias_ref)
+    fin = np.isfinite(dbias_ref)
+    k = 4 + math.ceil(math.log2(max(cols, 2)))
+    bias_err = np.sum(k * 2.0 ** -24 * np.where(np.isfinite(dx_scale), dx_scale, 0.0), axis=0)
+    reps = []
+    if fin.any():
+        reps.append(cmp.check_colsum("nonfinite.drop.dbias", f64(dbias)[fin], dbias_ref[fin],
+                                     sbias[fin], ROWS, fmt, term_err=bias_err[fin]))
+    dg_ref, db_ref, _, sb = orc.ln_bwd_params(dy64, z64, mu64, rs64)
+    same_finiteness("nonfinite.drop.dgamma", dg, dg_ref)
+    reps.append(cmp.check_colsum("nonfinite.drop.dbeta", f64(db), db_ref, sb, ROWS, fmt))
+    assert_reports(*reps)
+
+
+@pytest.mark.parametrize("cols", [1280, 4096])
+def test_add_rmsnorm_backward(orc, cols):
+    """An infinite element of z: rstd = 0, so its row's xhat is NaN at that
+    element and 0 elsewhere; dz is non-finite across the row, dgamma only in
+    the poisoned columns."""
+    case(f"add + RMSNorm bwd with non-finite rows {ROWS}x{cols} bf16")
+    dt = torch.bfloat16
+    d = dev(synth.layer_inputs(ROWS, cols, dt, seed=38, names=("x", "residual", "gamma", "dy")))
+    z0, ez = d["x"], d["residual"]
+    z0[5, 3] = np.inf
+    z0[30, 0] = -np.inf
+    z, _, rstd = mb.add_rmsnorm_fwd(z0, d["gamma"], 1e-6)
+    dz, dg = mb.add_rmsnorm_bwd(d["dy"], z, d["gamma"], rstd, dz_extra=ez)
+    torch.cuda.synchronize()
+    dy64, z64, g64, rs64, ez64 = f64(d["dy"]), f64(z), f64(d["gamma"]), f64(rstd), f64(ez)
+    dx_ref, dg_ref, sg = orc.rmsnorm_bwd(dy64, z64, g64, rs64)
+    dz_ref = dx_ref + ez64
+    good, bad = split(dz_ref)
+    assert bad == [5, 30]
+    g = g64 * dy64
+    with np.errstate(invalid="ignore"):   # inf * 0 in the poisoned rows
+        xh = z64 * rs64[:, None]
+        scale = rs64[:, None] * (np.abs(g) + np.abs(xh) * np.sum(np.abs(g * xh), axis=1,
+                                                                  keepdims=True) / cols)
+    scale = scale + np.abs(ez64)
+    assert_reports(cmp.check_elementwise("nonfinite.rms_bwd.dz", f64(dz)[good], dz_ref[good],
+                                         cmp.BF16, term_scale=scale[good], row_len=cols))
+    same_finiteness("nonfinite.rms_bwd.dz", dz[bad], dz_ref[bad])
+    same_finiteness("nonfinite.rms_bwd.dgamma", dg, dg_ref)
+    fin = np.isfinite(dg_ref)
+    assert sorted(np.nonzero(~fin)[0].tolist()) == [0, 3]
+    assert_reports(cmp.check_colsum("nonfinite.rms_bwd.dgamma", f64(dg)[fin], dg_ref[fin],
+                                    sg[fin], ROWS, cmp.BF16))
