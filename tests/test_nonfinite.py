@@ -75,10 +75,19 @@ def test_layernorm(orc, dtype, cols):
     assert_reports(cmp.check_colsum("nonfinite.dbeta", f64(db), db_ref, sb, ROWS, FMT[dtype]))
 
 
+@pytest.fixture(params=[False, True], ids=["registers", "two_pass"])
+def two_pass(request):
+    """The register-resident kernels, or the two-pass long-row path forced
+    at these widths."""
+    mb.debug_force_two_pass(request.param)
+    yield request.param
+    mb.debug_force_two_pass(False)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
 @pytest.mark.parametrize("cols", [64, 1000, 4096])
-def test_softmax(orc, dtype, cols):
-    case(f"softmax fwd + bwd with non-finite rows {ROWS}x{cols} {dtype}")
+def test_softmax(orc, dtype, cols, two_pass):
+    case(f"softmax fwd + bwd with non-finite rows {ROWS}x{cols} {dtype} two_pass={two_pass}")
     d = dev(synth.layer_inputs(ROWS, cols, dtype, seed=32, names=("x", "dy")))
     x = d["x"]
     poison(x)
@@ -122,8 +131,8 @@ def test_add_rmsnorm(orc, cols):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("cols", [1000, 50257])
-def test_cross_entropy(orc, dtype, cols):
-    case(f"cross-entropy with non-finite rows {ROWS}x{cols} {dtype}")
+def test_cross_entropy(orc, dtype, cols, two_pass):
+    case(f"cross-entropy with non-finite rows {ROWS}x{cols} {dtype} two_pass={two_pass}")
     x = dev(synth.layer_inputs(ROWS, cols, dtype, seed=34, names=("x",)))["x"]
     poison(x)
     lab = torch.randint(0, cols, (ROWS,), device="cuda",
