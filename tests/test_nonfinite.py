@@ -12,6 +12,8 @@ Where a -Inf is a legal value (a masked score for the softmax, a logit of
 probability 0), the row stays finite and is checked like the others; in the
 fused forward a poisoned element that the mask drops adds exactly 0.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -187,7 +189,6 @@ def test_prologue_backward(orc, dtype, cols):
     """Poisoned rows of z: their dz is non-finite throughout, their dx only
     where the mask keeps; dbias is non-finite exactly in the columns where a
     poisoned row is kept, dgamma everywhere, dbeta nowhere."""
-    import math
     case(f"prologue backward with non-finite rows {ROWS}x{cols} {dtype}")
     p, seed = 0.3, 99
     d = dev(synth.layer_inputs(ROWS, cols, dtype, seed=37,
