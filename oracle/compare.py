@@ -22,6 +22,16 @@ arithmetic; every use of the wider clause is counted in the report:
   bound of a balanced summation tree over `rows` terms ("GPU Performance
   from First Principles", §7.4: a tree sum rounds each term log2(n) times).
 * mean / rstd (float32): pass iff |o - r| <= 1e-5 * max(1, |r|).
+* probability-sized outputs (softmax y, its dropped copy and dx; the
+  cross-entropy gradient): these are far below 1 (about 1/L for a row of L
+  keys), so an absolute floor of 2e-2 or 1e-5 would pass an all-zero output.
+  They take no absolute floor: pass iff
+  |o - r| <= 0.5 * ulp_T(r) * (1 + 2^-8) + k * 2^-24 * scale + 2^-126, the
+  storage rounding, the float32 arithmetic clause above with the size of the
+  terms behind each value, and float32's smallest normal (below it the
+  arithmetic itself is denormal).  An exact 0 of the reference (a masked or
+  dropped position) must be an exact 0.  `n_wide` counts the elements that
+  needed more than the storage rounding.
 """
 from __future__ import annotations
 
@@ -96,6 +106,22 @@ def check_elementwise(name, out, ref, fmt, term_scale=None, row_len: int = 1) ->
     return _finish(name, out, ref, err, tol, atol)
 
 
+def check_scaled(name, out, ref, fmt, term_scale, row_len: int) -> Report:
+    """Value-scaled rule of probability-sized outputs (no absolute floor)."""
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    k = 4 + math.ceil(math.log2(max(row_len, 2)))
+    store = 0.5 * ulp(ref, fmt) * (1.0 + 2.0 ** -8)
+    store = np.where(ref == 0, 0.0, store)
+    arith = k * 2.0 ** -24 * np.asarray(term_scale, np.float64)
+    tol = store + arith + np.where(ref == 0, 0.0, 2.0 ** -126)
+    err = np.abs(out - ref)
+    rep = _finish(name, out, ref, err, tol, 0.0)
+    rep.n_wide = int(np.count_nonzero((err > store) & (err <= tol)))
+    return rep
+
+
 def check_colsum(name, out, ref, abs_sum, rows: int, fmt, term_err=None) -> Report:
     """Column sums: |o - r| <= atol, or <= half an fp32 step + the rounding of
     a depth-ceil(log2 rows) summation of |terms| (abs_sum).  `term_err`, when
@@ -111,6 +137,29 @@ def check_colsum(name, out, ref, abs_sum, rows: int, fmt, term_err=None) -> Repo
         tol = tol + np.asarray(term_err, dtype=np.float64)
     err = np.abs(out - ref)
     return _finish(name, out, ref, err, tol, atol)
+
+
+def check_colsum_stat(name, out, ref, sq_sum, rows: int) -> Report:
+    """Column sums against the random-rounding model of float32 summation
+    (the rule of thumb that rounding errors of a long sum grow like the square
+    root of the number of roundings, not linearly): each addition rounds its
+    partial sum s_k with an error of at most 2^-24 |s_k|, so the error is
+    about 2^-24/sqrt(3) * sqrt(sum_k s_k^2).  For terms of random sign summed
+    in any order whose partial sums carry no more than D = 4 ceil(log2 rows)
+    times the terms' own energy (sum_k s_k^2 <= D * sum_i t_i^2; a balanced
+    tree has D = log2 rows, runs of a few dozen sequential adds per level stay
+    well inside), the bound is six standard deviations:
+    |o - r| <= 0.5 ulp_f32(r) + 6 * 2^-24/sqrt(3) * sqrt(D * sum_i t_i^2).
+    It is far tighter than the worst-case tree clause of check_colsum, so a
+    change that loses accuracy (a worse order, a term rounded twice, a lost
+    row) fails it.  `sq_sum` is sum_r t_rj^2 per column."""
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    depth = 4 * math.ceil(math.log2(max(rows, 2)))
+    sd = 2.0 ** -24 / math.sqrt(3.0) * np.sqrt(depth * np.asarray(sq_sum, np.float64))
+    tol = 0.5 * ulp(ref, F32) + 6.0 * sd
+    err = np.abs(out - ref)
+    return _finish(name, out, ref, err, tol, 0.0)
 
 
 def check_stats(name, out, ref) -> Report:

@@ -35,19 +35,32 @@ def assert_reports(*reports):
     return reports
 
 
-def check_fwd(orc, x, gamma, beta, y, mean, rstd, fmt, eps=EPS, name="fwd"):
+def assert_no_wide(reports):
+    """No output needed a clause wider than the headline max-abs bound."""
+    wide = [str(r) for r in reports if r.n_wide]
+    assert not wide, "wider tolerance clause used:\n" + "\n".join(wide)
+
+
+def check_fwd(orc, x, gamma, beta, y, mean, rstd, fmt, eps=EPS, name="fwd", strict=False):
+    """`strict`: also require that no element needed a wider clause than the
+    headline max-abs bound (the fp32 configurations meet it outright)."""
     y_ref, mu_ref, rs_ref = orc.ln_fwd(f64(x).reshape(-1, x.shape[-1]), f64(gamma),
                                        f64(beta), eps)
     reps = [cmp.check_elementwise(f"{name}.y", f64(y).reshape(y_ref.shape), y_ref, fmt)]
     if mean is not None:
         reps.append(cmp.check_stats(f"{name}.mean", f64(mean), mu_ref))
         reps.append(cmp.check_stats(f"{name}.rstd", f64(rstd), rs_ref))
-    return assert_reports(*reps)
+    assert_reports(*reps)
+    if strict:
+        assert_no_wide(reps)
+    return reps
 
 
-def check_bwd(orc, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, fmt, name="bwd"):
+def check_bwd(orc, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, fmt, name="bwd",
+              strict=False):
     """Reference dx, dgamma, dbeta from the stored inputs and the stored fp32
-    mean/rstd the GPU read."""
+    mean/rstd the GPU read.  `strict`: dx needs no wider clause, and the
+    column sums also meet the statistical bound of cmp.check_colsum_stat."""
     rows, cols = x.shape[0], x.shape[-1]
     dy64, x64 = f64(dy).reshape(rows, cols), f64(x).reshape(rows, cols)
     mu64, rs64 = f64(mean), f64(rstd)
@@ -61,7 +74,18 @@ def check_bwd(orc, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, fmt, name="bwd")
         dg, db, sg, sb = orc.ln_bwd_params(dy64, x64, mu64, rs64)
         reps.append(cmp.check_colsum(f"{name}.dgamma", f64(dgamma), dg, sg, rows, fmt))
         reps.append(cmp.check_colsum(f"{name}.dbeta", f64(dbeta), db, sb, rows, fmt))
-    return assert_reports(*reps)
+    assert_reports(*reps)
+    if strict:
+        if dx is not None:
+            assert_no_wide(reps[:1])
+        if dgamma is not None:
+            xh = (x64 - mu64[:, None]) * rs64[:, None]
+            assert_reports(
+                cmp.check_colsum_stat(f"{name}.dgamma.stat", f64(dgamma), dg,
+                                      np.sum((dy64 * xh) ** 2, axis=0), rows),
+                cmp.check_colsum_stat(f"{name}.dbeta.stat", f64(dbeta), db,
+                                      np.sum(dy64 ** 2, axis=0), rows))
+    return reps
 
 
 def check_fused(orc, inp, p, seed, z, y, mean, rstd, mask, fmt, eps=EPS, name="fused"):
@@ -142,14 +166,14 @@ def check_softmax_fwd(orc, x, y, y_dropped, fmt, scale=1.0, mask=None, rows_per_
                       causal=False, p=0.0, seed=0, name="softmax"):
     rows, cols = x.shape
     y_ref, y_scale = softmax_refs(orc, x, mask, rows_per_mask, causal, scale)
-    reps = [cmp.check_elementwise(f"{name}.y", f64(y), y_ref, fmt, term_scale=y_scale,
-                                  row_len=cols)]
+    reps = [cmp.check_scaled(f"{name}.y", f64(y), y_ref, fmt, term_scale=y_scale,
+                             row_len=cols)]
     if y_dropped is not None:
         keep = orc.dropout_keep(seed, p, rows, cols)
         s = 1.0 / (1.0 - np.float64(np.float32(p)))
-        reps.append(cmp.check_elementwise(f"{name}.y_dropped", f64(y_dropped),
-                                          np.where(keep == 1, y_ref * s, 0.0), fmt,
-                                          term_scale=y_scale * s * keep, row_len=cols))
+        reps.append(cmp.check_scaled(f"{name}.y_dropped", f64(y_dropped),
+                                     np.where(keep == 1, y_ref * s, 0.0), fmt,
+                                     term_scale=y_scale * s * keep, row_len=cols))
         yd = f64(y_dropped)
         assert np.all(yd[keep == 0] == 0.0), f"{name}: dropped positions not zero"
     return assert_reports(*reps)
@@ -164,8 +188,8 @@ def check_softmax_bwd(orc, dy, y, dx, fmt, scale=1.0, p=0.0, seed=0, name="softm
     s = 1.0 / (1.0 - np.float64(np.float32(p)))
     g = dy64 * s if keep is None else np.where(keep == 1, dy64 * s, 0.0)
     term = abs(scale) * y64 * (np.abs(g) + np.sum(np.abs(g * y64), axis=1, keepdims=True))
-    return assert_reports(cmp.check_elementwise(f"{name}.dx", f64(dx), dx_ref, fmt,
-                                                term_scale=term, row_len=cols))
+    return assert_reports(cmp.check_scaled(f"{name}.dx", f64(dx), dx_ref, fmt,
+                                           term_scale=term, row_len=cols))
 
 
 def check_rmsnorm_fwd(orc, x, residual, gamma, z, y, rstd, fmt, eps, name="rms"):
@@ -244,8 +268,8 @@ def check_xent(orc, logits, labels, cols, alpha, scale, loss, dx, fmt, rows_sel=
             q * (1.0 + np.abs(x64 - m[:, None]) + spread[:, None]) + p)
         term = np.where(valid[:, None], term, 0.0)
         d_all = f64(dx)
-        reps.append(cmp.check_elementwise(f"{name}.dx", d_all[rows_idx, :cols], dx_ref, fmt,
-                                          term_scale=term, row_len=cols))
+        reps.append(cmp.check_scaled(f"{name}.dx", d_all[rows_idx, :cols], dx_ref, fmt,
+                                     term_scale=term, row_len=cols))
         if d_all.shape[1] > cols:
             pad = d_all[rows_idx, cols:]
             assert np.all(pad == 0.0), f"{name}: nonzero gradient in padding columns"

@@ -433,6 +433,44 @@ def test_fused_prologue_definition(orc):
     assert np.array_equal(z0, res + (x + bias))
 
 
+@pytest.mark.parametrize("p", [0.1, 0.3, 0.5, 0.9])
+def test_fused_prologue_keeps_the_expectation(orc, p):
+    """Dropout followed by the residual add ("(I)" §2.3) must leave the
+    expected value of z unchanged: averaged over dropout seeds, z - residual
+    equals x + bias.  The oracle's prologue, driven by its own keep masks, is
+    fitted with one scale s in z - residual = s * (x + bias) over 2^20
+    (element, seed) pairs; s must be 1 within the binomial band plus the
+    quantisation of p to a 16-bit threshold (|thr/65536 - p| <= 2^-17).  A
+    scale of (1 - p), or none, moves s by at least 0.1 at every p here (the
+    band is below 3e-3).  Dropped positions hold exactly the residual: the
+    bias is dropped with x, and the residual is never dropped."""
+    rng = np.random.default_rng(31)
+    rows, m, seeds = 64, 256, 64
+    x, res = _rows(rng, rows, m), _rows(rng, rows, m)
+    bias = rng.normal(0, 0.5, m)
+    t = x + bias
+    num = den = 0.0
+    for s in range(seeds):
+        keep = orc.dropout_keep(1000 + s, p, rows, m)
+        z = orc.bias_dropout_residual(x, bias, res, keep, p)
+        assert np.array_equal(z[keep == 0], res[keep == 0])
+        d = z - res
+        num += float(np.sum(d * t))
+        den += float(np.sum(t * t))
+    s_fit = num / den
+    n = rows * m * seeds
+    q = 1.0 - orc.dropout_threshold(p) / 65536.0
+    pf = float(np.float32(p))
+    # Var of sum(keep t^2)/sum(t^2) for Bernoulli(q) keeps: q(1-q) sum t^4 / (sum t^2)^2
+    t4 = float(np.sum(t ** 4)) * seeds
+    sd = math.sqrt(q * (1 - q) * t4) / den / (1 - pf)
+    assert abs(s_fit - 1.0) <= 6 * sd + 2.0 ** -17 / (1 - pf) + 1e-12, (s_fit, sd)
+    # the band excludes the other readings: kept values scaled by (1 - p), or
+    # not scaled at all, would give s = q (1 - p) or s = q
+    for wrong in (q * (1 - pf), q):
+        assert abs(wrong - 1.0) > 6 * sd + 2.0 ** -17 / (1 - pf) + 0.05
+
+
 def test_dx_term_scale_bounds_dx(orc):
     # |dx_j| = r |g_j - (A + xhat_j B)/m| <= r (|g_j| + (sum|g| + |xhat_j| sum|g xhat|)/m)
     rng = np.random.default_rng(12)

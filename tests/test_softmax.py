@@ -47,15 +47,17 @@ def check(orc, d, y, yd, dx, scale, causal, p, seed, mask=None, rows_per_mask=1,
                       name=f"{name}.bwd")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape", [(2 * 16 * 256, 256), (8 * 16 * 512, 512)])
-def test_pages_attention_shapes(orc, shape):
+def test_pages_attention_shapes(orc, shape, dtype):
     """Batch 2 x 16 heads x 256 x 256 with the causal mask, and 8 x 16 x 512 x
-    512 with dropout, fp16 (the pages' examples)."""
+    512 with dropout (the pages' examples), in every storage type, under the
+    value-scaled rule (y is about 1/512 here)."""
     rows, cols = shape
     causal, p = (True, 0.0) if cols == 256 else (False, 0.1)
-    case(f"softmax {rows}x{cols} fp16 causal={causal} p={p}")
+    case(f"softmax {rows}x{cols} {dtype} causal={causal} p={p}")
     scale = 1.0 / np.sqrt(64.0)
-    d, y, yd, dx = run(rows, cols, torch.float16, scale, causal, p, 3)
+    d, y, yd, dx = run(rows, cols, dtype, scale, causal, p, 3)
     check(orc, d, y, yd, dx, scale, causal, p, 3, name=f"sm.{rows}x{cols}")
 
 

@@ -36,10 +36,13 @@ def run(orc, rows, cols, ld, dtype, seed, alpha=0.1, scale=None, grad=True, igno
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_gpt2_vocabulary(orc, dtype):
-    # llm.c's fused classifier shape: V = 50257 classes in rows padded to 50304
-    case(f"cross-entropy 256x{GPT2_V} (ld {GPT2_VP}) {dtype}")
-    run(orc, 256, GPT2_V, GPT2_VP, dtype, 0, name="xent.gpt2")
+@pytest.mark.parametrize("scale", [None, 1.0], ids=["mean", "unit"])
+def test_gpt2_vocabulary(orc, dtype, scale):
+    # llm.c's fused classifier shape: V = 50257 classes in rows padded to 50304;
+    # with the mean loss's 1/rows and with a unit gradient scale (the
+    # gradient checked under the value-scaled rule either way)
+    case(f"cross-entropy 256x{GPT2_V} (ld {GPT2_VP}) {dtype} scale={scale}")
+    run(orc, 256, GPT2_V, GPT2_VP, dtype, 0, scale=scale, name="xent.gpt2")
 
 
 def test_gpt2_full_batch_sampled(orc):
