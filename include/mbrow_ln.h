@@ -67,8 +67,15 @@ typedef enum {
     LN_ERR_WORKSPACE = 5,   /* workspace smaller than ln_bwd_workspace_bytes   */
     LN_ERR_UNSUPPORTED = 6, /* cols above LN_MAX_COLS, or an aliasing form
                                the call does not allow                        */
-    LN_ERR_HIP = 7          /* a HIP launch or query failed                    */
+    LN_ERR_HIP = 7,         /* a HIP launch or query failed                    */
+    LN_ERR_SCRATCH = 8      /* ln_bwd_noalloc: the shape needs more than the
+                               library's static scratch of
+                               LN_NOALLOC_SCRATCH_BYTES                       */
 } ln_status_t;
+
+/* Size of the static device scratch that ln_bwd_noalloc uses (per GPU, held
+ * until the process ends). */
+#define LN_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Widest row supported, for every storage type (the whole row is held in
  * registers of one workgroup). */
@@ -196,6 +203,29 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x,
                                 int partials_ready, int64_t rows,
                                 int64_t cols, ln_dtype_t dt,
                                 hipStream_t stream);
+
+/*
+ * The whole LayerNorm backward -- dx, dgamma and dbeta -- for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments and results as
+ * ln_bwd_dx with a workspace followed by ln_bwd_dgamma_dbeta with
+ * partials_ready = 1 (the same kernels: results are bitwise identical), but
+ * the column partials live in a static device array of the library,
+ * LN_NOALLOC_SCRATCH_BYTES per GPU, instead of a caller workspace.  The call
+ * allocates nothing and calls no allocating routine.
+ *   Shapes whose partials need more than LN_NOALLOC_SCRATCH_BYTES
+ *   (ln_bwd_workspace_bytes(rows, cols) > LN_NOALLOC_SCRATCH_BYTES, e.g. more
+ *   than 8192 columns at 256 rows or more) return LN_ERR_SCRATCH and enqueue
+ *   nothing.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on one
+ *   GPU (concurrent streams, or host threads on the same device) race and
+ *   must be serialised by the caller.  Nothing in the array needs clearing:
+ *   each call writes every partial it later reads.
+ */
+ln_status_t ln_bwd_noalloc(const void* dy, const void* x, const void* gamma,
+                           const float* mean, const float* rstd, void* dx,
+                           float* dgamma, float* dbeta, int64_t rows, int64_t cols,
+                           ln_dtype_t dt, hipStream_t stream);
 
 /*
  * Bytes of float32 workspace bias_dropout_residual_ln_bwd needs: P * 3 * cols

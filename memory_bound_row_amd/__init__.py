@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
     L.ln_bwd_dgamma_dbeta.restype = i32
     L.ln_bwd_dgamma_dbeta.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i32,
                                       i64, i64, i32, vp]
+    L.ln_bwd_noalloc.restype = i32
+    L.ln_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]
     L.bias_dropout_residual_ln_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.bias_dropout_residual_ln_bwd_workspace_bytes.argtypes = [i64, i64]
     L.bias_dropout_residual_ln_bwd.restype = i32
@@ -233,6 +235,29 @@ def ln_bwd(dy, x, gamma, mean, rstd, *, dx=None, workspace_buf=None, dgamma=None
     dx = ln_bwd_dx(dy, x, gamma, mean, rstd, dx=dx, workspace=ws)
     dgamma, dbeta = ln_bwd_dgamma_dbeta(ws, rows, cols, x.dtype, partials_ready=True,
                                         dgamma=dgamma, dbeta=dbeta)
+    return dx, dgamma, dbeta
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # LN_NOALLOC_SCRATCH_BYTES
+
+
+def ln_bwd_noalloc(dy, x, gamma, mean, rstd, *, dx, dgamma, dbeta):
+    """Whole LayerNorm backward with the library's static scratch for the
+    column partials: the C call allocates nothing, and neither does this
+    wrapper (every output is the caller's)."""
+    rows, cols = _mat(x, "x")
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x")
+    _mat(dy, "dy")
+    _vec(gamma, cols, x.dtype, "gamma")
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        _vec(t, rows, torch.float32, n)
+    dx = _out(dx, x.shape, x.dtype, x.device, "dx")
+    dgamma = _out(dgamma, (cols,), torch.float32, x.device, "dgamma")
+    dbeta = _out(dbeta, (cols,), torch.float32, x.device, "dbeta")
+    _check(lib().ln_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd),
+                                _ptr(dx), _ptr(dgamma), _ptr(dbeta), rows, cols, _dt(x),
+                                _stream(x)))
     return dx, dgamma, dbeta
 
 

@@ -275,6 +275,9 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t blocks) {
     return g < blocks ? g : blocks;
 }
 
+// ln_bwd_noalloc's static device scratch (noalloc.hip).
+hipError_t noalloc_scratch(float** out);
+
 int64_t bwd_partitions(int64_t rows, int64_t cols) {
     (void)cols;
     const int64_t kParts = 256;
@@ -364,6 +367,9 @@ const char* ln_status_string(ln_status_t status) {
         return "LN_ERR_UNSUPPORTED: shape too large or buffers overlap in a way the call "
                "does not allow";
     case LN_ERR_HIP: return "LN_ERR_HIP: a HIP launch failed";
+    case LN_ERR_SCRATCH:
+        return "LN_ERR_SCRATCH: the shape needs more than the library's static scratch "
+               "(LN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown ln_status_t";
     }
 }
@@ -524,6 +530,44 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
     out.p[0] = dgamma;
     out.p[1] = dbeta;
     return from_hip(launch_fold(workspace, parts, cols, 2, out, stream));
+}
+
+ln_status_t ln_bwd_noalloc(const void* dy, const void* x, const void* gamma, const float* mean,
+                           const float* rstd, void* dx, float* dgamma, float* dbeta,
+                           int64_t rows, int64_t cols, ln_dtype_t dt, hipStream_t stream) {
+    if (!dy || !x || !gamma || !mean || !rstd || !dx || !dgamma || !dbeta) return LN_ERR_NULL;
+    ln_status_t st = check_shape(rows, cols, dt);
+    if (st != LN_OK) return st;
+    if (rows == 0) return LN_OK;
+    const size_t need = ln_bwd_workspace_bytes(rows, cols);
+    if (need > LN_NOALLOC_SCRATCH_BYTES) return LN_ERR_SCRATCH;
+    const size_t es = elem_bytes(dt);
+    const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
+    const size_t sb = (size_t)rows * sizeof(float), cb = (size_t)cols * sizeof(float);
+    const Span outs[] = {{dx, tb, true}, {dgamma, cb, false}, {dbeta, cb, false}};
+    const Span ins[] = {{dy, tb, true}, {x, tb, true}, {gamma, vb, false},
+                        {mean, sb, false}, {rstd, sb, false}};
+    st = check_aliasing(outs, 3, ins, 5);
+    if (st != LN_OK) return st;
+    float* ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess || !ws) return LN_ERR_HIP;
+
+    const Dt d = static_cast<Dt>(dt);
+    const bool vec = aligned16(dy) && aligned16(x) && aligned16(gamma) && aligned16(dx) &&
+                     (cols * (int64_t)es) % 16 == 0;
+    BwdArgs a{};
+    a.dy = dy; a.x = x; a.gamma = gamma; a.mean = mean; a.rstd = rstd; a.dx = dx;
+    a.ws = ws;
+    a.rows = rows; a.m = cols;
+    a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
+    a.parts = bwd_partitions(rows, cols);
+    a.inv_m = (float)(1.0 / (double)cols);
+    st = from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::DX_PARTIALS, a, stream));
+    if (st != LN_OK) return st;
+    FoldOut out{};
+    out.p[0] = dgamma;
+    out.p[1] = dbeta;
+    return from_hip(launch_fold(ws, a.parts, cols, 2, out, stream));
 }
 
 ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, const void* z,

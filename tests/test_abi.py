@@ -13,7 +13,7 @@ import memory_bound_row_amd as mb
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 LN_OK, LN_ERR_NULL, LN_ERR_SHAPE, LN_ERR_DTYPE, LN_ERR_PARAM = 0, 1, 2, 3, 4
-LN_ERR_WORKSPACE, LN_ERR_UNSUPPORTED, LN_ERR_HIP = 5, 6, 7
+LN_ERR_WORKSPACE, LN_ERR_UNSUPPORTED, LN_ERR_HIP, LN_ERR_SCRATCH = 5, 6, 7, 8
 F32, F16, BF16 = 0, 1, 2
 
 # fake but non-NULL device addresses: validation never dereferences them
@@ -48,7 +48,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(8):
+    for code in range(9):
         s = mb.status_string(code)
         assert s and s != "unknown ln_status_t"
     assert mb.status_string(99) == "unknown ln_status_t"
