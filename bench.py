@@ -1,11 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of the fused LayerNorm hot path on one MI355X.
 
-One step = the whole path over one batch of synthetic rows:
-  bias_dropout_residual_ln_fwd (bias add, dropout p, residual add, LayerNorm,
-  z and y written, mean/rstd saved)  ->  ln_bwd_dx with the dgamma/dbeta
-  stage-1 partials  ->  ln_bwd_dgamma_dbeta fold,
-at 8192 x 1280 bf16 storage, float32 arithmetic.
+One step = one training pass of the path over one batch of synthetic rows,
+at 8192 x 1280 bf16 storage with float32 arithmetic:
+  bias_dropout_residual_ln_fwd (bias add, dropout p, residual add, LayerNorm;
+  z and y written, mean/rstd saved)  ->  bias_dropout_residual_ln_bwd_dx (the
+  LayerNorm dx from two row sums, the gradient from the residual stream added,
+  the dropout/residual backward with the mask regenerated from the seed, and
+  the stage-1 column partials of dgamma, dbeta, dbias)  ->
+  bias_dropout_residual_ln_bwd_fold (the fixed-order fold of the partials).
+The same line reports the plain LayerNorm step the hot-path scope table
+defines as the metric case (ln_fwd -> ln_bwd_dx with partials -> fold) and
+the fused forward followed by the plain LayerNorm backward.
 
 The timed region replays K steps captured in one HIP graph, on inputs that
 are already resident in device memory.  K steps rotate over buffer sets whose
@@ -14,7 +20,8 @@ backward reads a set written half a rotation earlier, so every byte comes
 from HBM as it would in training (the backward of a layer runs long after
 its forward).  `value` is algorithmic bytes (what the method must move) per
 second over the whole step.  The `roofline` object reports the dominant
-kernel alone; the CPU baseline times the float64 oracle on the host.
+kernel alone, timed with HIP events on the stream it runs on; the CPU
+baseline times the float64 oracle on the host.
 
 Prints one JSON line.
 """
@@ -33,16 +40,26 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 ROWS, COLS, P_DROP, EPS, SEED = 8192, 1280, 0.1, 1e-5, 0
-WORKLOAD = ("bias+dropout(p=0.1)+residual+LayerNorm fwd, then LayerNorm bwd "
-            "(dx + dgamma/dbeta), 8192x1280 bf16 storage")
+WORKLOAD = ("training step of the fused LayerNorm, 8192x1280 bf16 storage: "
+            "bias+dropout(p=0.1)+residual+LayerNorm forward, then its backward (LayerNorm "
+            "dx and dgamma/dbeta, residual-stream gradient added, dropout/residual/bias "
+            "backward with dbias)")
 
 
 def algorithmic_bytes(rows: int, cols: int, s: int) -> dict:
-    """Bytes each call must move at minimum: every tensor read or written
-    once; gamma/beta/bias once; mean/rstd as float32."""
+    """Bytes each call of the step must move at minimum: every [rows, cols]
+    tensor read or written once, gamma/beta/bias once, mean/rstd and the
+    parameter gradients as float32 (the column partials are not counted)."""
     fwd = 4 * rows * cols * s + 3 * cols * s + 8 * rows        # x, res -> z, y
-    bwd = 3 * rows * cols * s + cols * s + 8 * rows + 8 * cols  # dy, x -> dx; dg, db
-    return {"fused_fwd": fwd, "bwd": bwd, "step": fwd + bwd}
+    bwd = 5 * rows * cols * s + cols * s + 8 * rows            # dy, dz_extra, z -> dres, dx
+    fold = 12 * cols                                           # dgamma, dbeta, dbias
+    return {"fused_fwd": fwd, "prologue_bwd": bwd, "fold": fold,
+            "step": fwd + bwd + fold}
+
+
+def ln_bwd_bytes(rows: int, cols: int, s: int) -> int:
+    """The LayerNorm backward (dx, dgamma, dbeta): dy, x read, dx written."""
+    return 3 * rows * cols * s + cols * s + 8 * rows + 8 * cols
 
 
 def parse():
@@ -122,6 +139,20 @@ def _read_counters(path: str) -> dict:
     return out
 
 
+BWD_MODES = {"0": "dx", "1": "dx+partials", "2": "partials", "3": "prologue", "4": "rms"}
+
+
+def kernel_short_name(name: str) -> str:
+    """A library kernel's demangled name -> the short name used in reports."""
+    base = name.split("(")[0].replace("void ", "").replace("mbrow::", "")
+    if base.startswith("ln_fwd_kernel"):
+        return "ln_fwd_kernel(fused)" if base.rstrip(">").endswith("true") else "ln_fwd_kernel"
+    if base.startswith("ln_bwd_kernel"):
+        mode = base.rstrip(">").split(",")[-1].strip()
+        return f"ln_bwd_kernel({BWD_MODES.get(mode, mode)})"
+    return base.split("<")[0]
+
+
 def pmc_summary(fetch_csv: str, write_csv: str) -> None:
     """HBM bytes per launch of each library kernel from FETCH_SIZE/WRITE_SIZE
     (KiB per dispatch), scaled so that the calibration copy of COPY_BYTES reads
@@ -129,9 +160,10 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> None:
     fetch, write = _read_counters(fetch_csv), _read_counters(write_csv)
 
     def copy_kib(d):
+        # the calibration copy: the largest one-source, one-destination stream
         best = 0.0
         for name, vals in d.items():
-            if "copy" in name.lower():
+            if "hbm_stream_kernel<1, 1>" in name:
                 best = max(best, max(vals))
         return best
     fcopy, wcopy = copy_kib(fetch), copy_kib(write)
@@ -145,10 +177,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> None:
             continue
         f_kib = sum(fetch[name]) / len(fetch[name])
         w_kib = sum(write.get(name, [0.0])) / max(1, len(write.get(name, [0.0])))
-        short = ("ln_fwd_kernel(fused)" if "ln_fwd_kernel" in name and "true>" in name
-                 else "ln_fwd_kernel" if "ln_fwd_kernel" in name
-                 else "ln_bwd_kernel(dx+partials)" if "ln_bwd_kernel" in name
-                 else name.split("(")[0].replace("mbrow::", ""))
+        short = kernel_short_name(name)
         kernels[short] = {
             "kernel_name": name,
             "fetch_bytes_per_launch": round(f_kib * 1024 * fscale),
@@ -210,20 +239,25 @@ def step_distribution(g, n, reps):
             "steps_per_replay": n}
 
 
-def copy_rates(sizes_mb, S, dev, K):
-    """Attainable bandwidth: the library's plain 16-byte copy (`hbm_copy`)
-    moving `mb` MB in total (half read, half written), rotated over S buffer
-    pairs like the step, timed as a K-copy graph.  GB/s per size."""
+def stream_rates(cases, S, dev, K):
+    """Attainable bandwidth of each kernel's mix of reads and writes: the
+    library's streaming reference (`hbm_stream`) reading `nsrc` and writing
+    `ndst` tensors that together hold `nbytes`, on incompressible data,
+    rotated over S buffer sets like the step, timed as a K-launch graph.
+    cases: {name: (nsrc, ndst, nbytes)} -> {name: (GB/s, microseconds)}."""
     import torch
     import memory_bound_row_amd as mb_lib
     out = {}
-    for mb in sizes_mb:
-        n = (int(mb * 1e6) // 2) // 16 * 4           # int32 elements per side, 16 B multiple
-        pairs = [(torch.ones(n, dtype=torch.int32, device=dev),
-                  torch.empty(n, dtype=torch.int32, device=dev)) for _ in range(S)]
-        ms = timed(capture(lambda i: mb_lib.hbm_copy(pairs[i % S][0], pairs[i % S][1]), K), K)
-        out[f"{mb}MB"] = round(8 * n / (ms * 1e-3) / 1e9, 1)
-        del pairs
+    g = torch.Generator(device=dev).manual_seed(7)
+    for name, (nsrc, ndst, nbytes) in cases.items():
+        n = (nbytes // (nsrc + ndst)) // 16 * 4        # int32 elements per tensor
+        sets = [[torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, device=dev,
+                               generator=g) for _ in range(nsrc + ndst)] for _ in range(S)]
+        ms = timed(capture(lambda i: mb_lib.hbm_stream(sets[i % S][:nsrc],
+                                                       sets[i % S][nsrc:]), K), K)
+        moved = 4 * n * (nsrc + ndst)
+        out[name] = (round(moved / (ms * 1e-3) / 1e9, 1), round(ms * 1e3 * nbytes / moved, 3))
+        del sets
     return out
 
 
@@ -256,8 +290,9 @@ def plain_bytes(rows: int, cols: int, s: int) -> dict:
 
 
 def _oracle_step(orc, d, row0, rows):
-    """The oracle's whole step over rows [row0, row0 + rows) of the workload;
-    returns the column sums (dgamma, dbeta) of that range."""
+    """The oracle's whole step over rows [row0, row0 + rows) of the workload:
+    the fused forward, then its backward; returns the column sums (dgamma,
+    dbeta, dbias) of that range."""
     import numpy as np
     sl = slice(row0, row0 + rows)
     keep = orc.dropout_keep_rows(SEED, P_DROP, row0, rows, COLS)
@@ -265,8 +300,10 @@ def _oracle_step(orc, d, row0, rows):
                                                P_DROP), "bf16")
     _, mu, rs = orc.ln_fwd(z, d["gamma"], d["beta"], EPS)
     mu, rs = np.float64(np.float32(mu)), np.float64(np.float32(rs))
-    orc.ln_bwd_dx(d["dy"][sl], z, d["gamma"], mu, rs)
-    return orc.ln_bwd_params(d["dy"][sl], z, mu, rs)
+    dz = orc.ln_bwd_dx(d["dy"][sl], z, d["gamma"], mu, rs) + d["ez"][sl]
+    _, dbias, _ = orc.dropout_residual_bwd(dz, keep, P_DROP)
+    dg, db, _, _ = orc.ln_bwd_params(d["dy"][sl], z, mu, rs)
+    return dg, db, dbias
 
 
 def cpu_baseline(inp_cpu, target_s: float):
@@ -302,9 +339,9 @@ def cpu_baseline(inp_cpu, target_s: float):
             while reps_p == 0 or (t_par < target_s / 2 and reps_p < 50):
                 t0 = time.perf_counter()
                 parts = list(pool.map(lambda r: _oracle_step(orc, d, r[0], r[1] - r[0]), bounds))
-                dg, db = parts[0][0], parts[0][1]
+                sums = list(parts[0])
                 for part in parts[1:]:
-                    dg, db = dg + part[0], db + part[1]
+                    sums = [a + b for a, b in zip(sums, part)]
                 t_par += time.perf_counter() - t0
                 reps_p += 1
         out["all_threads"] = {"value": round(b * reps_p / t_par / 1e9, 3), "unit": "GB/s",
@@ -454,7 +491,7 @@ def configs_report(cpp_launch: bool = True) -> None:
         if key not in copy_cache:
             n = (int(nbytes) // 2) // 16 * 4            # int32 elements per side
             pairs = max(2, -(-1_100_000_000 // (8 * n)))
-            bufs = [(torch.ones(n, dtype=torch.int32, device=dev),
+            bufs = [(torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, device=dev),
                      torch.empty(n, dtype=torch.int32, device=dev)) for _ in range(pairs)]
             k = 20
             ms = timed(capture(lambda i: mb.hbm_copy(bufs[i % pairs][0], bufs[i % pairs][1]),
@@ -888,7 +925,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method's rows "
-              "shard across GPUs with no communication except a [2, cols] dgamma/dbeta "
+              "shard across GPUs with no communication except a [3, cols] parameter-gradient "
               "exchange, which this benchmark does not run.", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -900,19 +937,22 @@ def main():
     dtype = torch.bfloat16
     K, W = args.steps, args.warmup
     S = 1 if args.warm_cache else max(2, args.sets)
+    H = S // 2
     inp_cpu = synth.layer_inputs(ROWS, COLS, dtype, seed=SEED)
+    # the gradient reaching z from the residual stream (drawn like dy)
+    inp_cpu["ez"] = synth.layer_inputs(ROWS, COLS, dtype, seed=SEED + 1, names=("dy",))["dy"]
     shared = {k: inp_cpu[k].to(dev) for k in ("bias", "gamma", "beta")}
     sets = []
     for _ in range(S):
-        st = {k: inp_cpu[k].to(dev) for k in ("x", "residual", "dy")}
-        for k in ("z", "y", "dx"):
+        st = {k: inp_cpu[k].to(dev) for k in ("x", "residual", "dy", "ez")}
+        for k in ("z", "y", "dres", "dxin", "dx"):
             st[k] = torch.empty((ROWS, COLS), dtype=dtype, device=dev)
         st["mean"] = torch.empty(ROWS, dtype=torch.float32, device=dev)
         st["rstd"] = torch.empty(ROWS, dtype=torch.float32, device=dev)
         sets.append(st)
+    wsd = mb.dropout_workspace(ROWS, COLS, dev)
     ws = mb.workspace(ROWS, COLS, dev)
-    dg = torch.empty(COLS, dtype=torch.float32, device=dev)
-    db = torch.empty(COLS, dtype=torch.float32, device=dev)
+    pg = [torch.empty(COLS, dtype=torch.float32, device=dev) for _ in range(3)]
 
     def fwd(a):
         mb.bias_dropout_residual_ln_fwd(a["x"], shared["bias"], a["residual"], shared["gamma"],
@@ -920,15 +960,17 @@ def main():
                                         y=a["y"], mean=a["mean"], rstd=a["rstd"])
 
     def bwd(b):
-        mb.ln_bwd_dx(b["dy"], b["z"], shared["gamma"], b["mean"], b["rstd"], dx=b["dx"],
-                     workspace=ws)
+        mb.bias_dropout_residual_ln_bwd_dx(b["dy"], b["z"], shared["gamma"], b["mean"],
+                                           b["rstd"], P_DROP, SEED, workspace=wsd,
+                                           dz_extra=b["ez"], dresidual=b["dres"], dx=b["dxin"])
 
     def fold():
-        mb.ln_bwd_dgamma_dbeta(ws, ROWS, COLS, dtype, partials_ready=True, dgamma=dg, dbeta=db)
+        mb.bias_dropout_residual_ln_bwd_fold(wsd, ROWS, COLS, dgamma=pg[0], dbeta=pg[1],
+                                             dbias=pg[2])
 
     def step(i):
         fwd(sets[i % S])
-        bwd(sets[(i + S // 2) % S])
+        bwd(sets[(i + H) % S])
         fold()
 
     # every set gets valid z/mean/rstd before any backward reads it
@@ -941,49 +983,67 @@ def main():
     g_step = capture(step, K)
     ms_step = timed(g_step, K)
     dist = step_distribution(g_step, K, 20)
-    # per-kernel launches over the same rotation, for the roofline
+    # each kernel alone over the same rotation, timed with HIP events on the
+    # stream it is launched on (the graph's)
     ms_fwd = timed(capture(lambda i: fwd(sets[i % S]), K), K)
-    ms_bwd = timed(capture(lambda i: bwd(sets[(i + S // 2) % S]), K), K)
+    ms_bwd = timed(capture(lambda i: bwd(sets[(i + H) % S]), K), K)
     ms_fold = timed(capture(lambda i: fold(), K), K)
 
-    # the same step with the plain forward (ln_fwd of x, no bias/dropout/
-    # residual), whose backward reads x
+    # the metric case of the hot-path scope table: ln_fwd of x, then the
+    # LayerNorm backward on x (dx with partials, then the fold)
+    def ln_bwd_call(b, xk):
+        mb.ln_bwd_dx(b["dy"], b[xk], shared["gamma"], b["mean"], b["rstd"], dx=b["dx"],
+                     workspace=ws)
+        mb.ln_bwd_dgamma_dbeta(ws, ROWS, COLS, dtype, partials_ready=True, dgamma=pg[0],
+                               dbeta=pg[1])
+
     def plain_step(i):
         a = sets[i % S]
         mb.ln_fwd(a["x"], shared["gamma"], shared["beta"], EPS, y=a["y"], mean=a["mean"],
                   rstd=a["rstd"])
-        b = sets[(i + S // 2) % S]
-        mb.ln_bwd_dx(b["dy"], b["x"], shared["gamma"], b["mean"], b["rstd"], dx=b["dx"],
-                     workspace=ws)
-        fold()
+        ln_bwd_call(sets[(i + H) % S], "x")
 
     ms_plain = timed(capture(plain_step, K), K)
-    pb = plain_bytes(ROWS, COLS, 2)["step"]
 
-    # attainable bandwidth: plain copies moving 21 and 42 MB and the kernels'
-    # and the step's byte counts, rotated like the step, and a large copy
-    # (also the PMC calibration kernel)
+    # the fused forward followed by the plain LayerNorm backward of z
+    def mixed_step(i):
+        fwd(sets[i % S])
+        ln_bwd_call(sets[(i + H) % S], "z")
+
+    for a in sets:
+        fwd(a)
+    torch.cuda.synchronize()
+    ms_mixed = timed(capture(mixed_step, K), K)
+    ms_lnbwd = timed(capture(lambda i: ln_bwd_call(sets[(i + H) % S], "z"), K), K)
+
     nb = algorithmic_bytes(ROWS, COLS, 2)
-    copy_mb = {"fused_fwd": round(nb["fused_fwd"] / 1e6), "bwd": round(nb["bwd"] / 1e6),
-               "step": round(nb["step"] / 1e6)}
-    copies = copy_rates(sorted(set(copy_mb.values()) | {21, 42}), S, dev, K)
-    big_src = torch.empty(COPY_BYTES // 2, dtype=dtype, device=dev)
-    big_dst = torch.empty_like(big_src)
-    ms_bigcopy = timed(capture(lambda i: big_dst.copy_(big_src), 4), 4)
+    pb = plain_bytes(ROWS, COLS, 2)
+    lb = ln_bwd_bytes(ROWS, COLS, 2)
+    t = ROWS * COLS * 2
+    # attainable bandwidth of each kernel's mix of reads and writes
+    refs = stream_rates({"fused_fwd": (2, 2, 4 * t), "prologue_bwd": (3, 2, 5 * t),
+                         "ln_fwd": (1, 1, 2 * t), "ln_bwd": (2, 1, 3 * t)}, S, dev, K)
+    # calibration copy for the HBM traffic counters (256 MiB each way)
+    big = [torch.randint(-2**31, 2**31 - 1, (COPY_BYTES // 4,), dtype=torch.int32, device=dev)
+           for _ in range(2)]
+    mb.hbm_copy(big[0], big[1])
+    torch.cuda.synchronize()
+    del big
 
-    nbytes = algorithmic_bytes(ROWS, COLS, 2)
-    value = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    value = nb["step"] / (ms_step * 1e-3) / 1e9
     per_kernel = {
-        "ln_fwd_kernel(fused)": (ms_fwd, nbytes["fused_fwd"]),
-        "ln_bwd_kernel(dx+partials)": (ms_bwd, nbytes["bwd"] - 8 * COLS),
+        "ln_fwd_kernel(fused)": (ms_fwd, nb["fused_fwd"]),
+        "ln_bwd_kernel(prologue)": (ms_bwd, nb["prologue_bwd"]),
     }
-    bwd_gbps = per_kernel["ln_bwd_kernel(dx+partials)"][1] / (ms_bwd * 1e-3) / 1e9
-    fwd_gbps = nbytes["fused_fwd"] / (ms_fwd * 1e-3) / 1e9
     dom = max(per_kernel, key=lambda k: per_kernel[k][0])
     ms_dom, b_dom = per_kernel[dom]
     achieved = b_dom / (ms_dom * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = load_traffic(dom, src_hash)
+    ref_step_us = refs["fused_fwd"][1] + refs["prologue_bwd"][1]
+
+    def gbps(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
     out = {
         "metric": "achieved HBM GB/s (% of peak) for fused LayerNorm fwd+bwd, 8192x1280 bf16",
@@ -999,29 +1059,38 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "rows": ROWS, "cols": COLS, "storage": "bf16",
-                   "p": P_DROP, "buffer_sets": S,
+                   "arithmetic": "f32", "p": P_DROP, "buffer_sets": S,
                    "cache": "warm (one set)" if args.warm_cache else "rotated past 256 MB"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "rows_per_s": round(ROWS / (ms_step * 1e-3), 1),
-        "bytes_per_step": nbytes["step"],
-        "kernel_us": {"fused_fwd": round(ms_fwd * 1e3, 3), "bwd_dx_partials": round(ms_bwd * 1e3, 3),
+        "bytes_per_step": nb["step"],
+        "kernel_us": {"fused_fwd": round(ms_fwd * 1e3, 3), "prologue_bwd": round(ms_bwd * 1e3, 3),
                       "fold": round(ms_fold * 1e3, 3)},
         "step_us": dist,
-        "copy_GBps": dict(copies, **{
-            "256MiB_torch": round(2 * COPY_BYTES / (ms_bigcopy * 1e-3) / 1e9, 1)}),
-        "pct_of_copy": {
-            "step": round(100.0 * value / copies[f"{copy_mb['step']}MB"], 1),
-            "fused_fwd": round(100.0 * fwd_gbps / copies[f"{copy_mb['fused_fwd']}MB"], 1),
-            "bwd": round(100.0 * bwd_gbps / copies[f"{copy_mb['bwd']}MB"], 1)},
-        "plain_fwd_step": {"workload": "ln_fwd then the same backward and fold, 8192x1280 bf16",
-                           "bytes_per_step": pb, "ms_per_step": round(ms_plain, 5),
-                           "GBps": round(pb / (ms_plain * 1e-3) / 1e9, 1),
-                           "pct_of_hbm_peak": round(100.0 * pb / (ms_plain * 1e-3) / 1e9
-                                                    / HBM_PEAK_GBPS, 2)},
+        "reference_GBps": {k: v[0] for k, v in refs.items()},
+        "pct_of_reference": {
+            "step": round(100.0 * ref_step_us / (ms_step * 1e3), 1),
+            "fused_fwd": round(100.0 * refs["fused_fwd"][1] / (ms_fwd * 1e3), 1),
+            "prologue_bwd": round(100.0 * refs["prologue_bwd"][1] / (ms_bwd * 1e3), 1)},
+        "metric_case": {"workload": "ln_fwd, then ln_bwd_dx with partials and the fold, "
+                                    "8192x1280 bf16 (the scope table's metric case)",
+                        "bytes_per_step": pb["step"], "ms_per_step": round(ms_plain, 5),
+                        "GBps": gbps(pb["step"], ms_plain),
+                        "pct_of_hbm_peak": round(100.0 * pb["step"] / (ms_plain * 1e-3) / 1e9
+                                                 / HBM_PEAK_GBPS, 2),
+                        "pct_of_reference": round(
+                            100.0 * (refs["ln_fwd"][1] + refs["ln_bwd"][1]) / (ms_plain * 1e3),
+                            1)},
+        "mixed_step": {"workload": "the fused forward, then the LayerNorm backward of z "
+                                   "(dx with partials, fold)",
+                       "bytes_per_step": nb["fused_fwd"] + lb, "ms_per_step": round(ms_mixed, 5),
+                       "GBps": gbps(nb["fused_fwd"] + lb, ms_mixed),
+                       "ln_bwd_with_fold_us": round(ms_lnbwd * 1e3, 3)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "source_hash": src_hash},
+                     "traffic": traffic, "bytes_per_launch": b_dom,
+                     "event_us": round(ms_dom * 1e3, 3), "source_hash": src_hash},
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inp_cpu, args.cpu_seconds)

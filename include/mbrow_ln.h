@@ -271,6 +271,29 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
                                          ln_dtype_t dt, hipStream_t stream);
 
 /*
+ * The two stages of bias_dropout_residual_ln_bwd as separate calls (as
+ * ln_bwd_dx and ln_bwd_dgamma_dbeta split the LayerNorm backward), for callers
+ * that schedule the small second stage themselves:
+ *   bias_dropout_residual_ln_bwd_dx writes dresidual, dx and the column
+ *     partials of dgamma, dbeta and dbias into the workspace (arguments and
+ *     errors as for bias_dropout_residual_ln_bwd, without the [cols] outputs);
+ *   bias_dropout_residual_ln_bwd_fold adds those partials for the same
+ *     (rows, cols) in the fixed order into dgamma, dbeta, dbias ([cols]
+ *     float32).  rows < 0 or cols <= 0 is LN_ERR_SHAPE, cols above
+ *     LN_MAX_COLS_DROPOUT_BWD LN_ERR_UNSUPPORTED.
+ * The two calls in turn give bitwise the results of the combined call.
+ */
+ln_status_t bias_dropout_residual_ln_bwd_dx(const void* dy, const void* dz_extra, const void* z,
+                                            const void* gamma, const float* mean,
+                                            const float* rstd, void* dresidual, void* dx,
+                                            float* workspace, size_t workspace_bytes,
+                                            int64_t rows, int64_t cols, float p, uint64_t seed,
+                                            ln_dtype_t dt, hipStream_t stream);
+ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t workspace_bytes,
+                                              float* dgamma, float* dbeta, float* dbias,
+                                              int64_t rows, int64_t cols, hipStream_t stream);
+
+/*
  * Attention softmax forward over rows of `cols` scores ([L10] §4.1: per row,
  * scale, add the mask, subtract the row maximum, exp, divide by the row sum;
  * one row per group of lanes, held in registers):
@@ -405,12 +428,29 @@ ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, flo
 /*
  * Measurement reference, not a step of any method: copies `bytes` bytes from
  * src to dst (device pointers) in 16-byte vectors with nontemporal loads and
- * stores, the attainable-bandwidth figure that the row kernels' rates are
- * compared against.  bytes, src and dst must be multiples of 16 and the two
+ * stores (hbm_stream with one source and one destination), the
+ * attainable-bandwidth figure that the row kernels' rates are compared
+ * against.  bytes, src and dst must be multiples of 16 and the two
  * ranges must not overlap, else LN_ERR_PARAM; NULL with bytes > 0 is
  * LN_ERR_NULL; bytes == 0 is a no-op.  Enqueued on `stream`; no allocation.
  */
 ln_status_t hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+/*
+ * Measurement reference, not a step of any method: reads nsrc (1..3) tensors
+ * of `bytes` bytes each and writes ndst (0..2) tensors of the same size (the
+ * xor and the sum of the sources' 16-byte vectors), one 16-byte vector per
+ * tensor per thread with nontemporal accesses -- the attainable bandwidth of
+ * a kernel that streams the same mix of reads and writes (a LayerNorm
+ * forward reads 1 tensor and writes 1; the fused forward 2 and 2; the
+ * backward 2 and 1; the prologue backward 3 and 2).  src and dst are HOST
+ * arrays of nsrc and ndst device pointers.  nsrc or ndst out of range, bytes
+ * or a pointer not a multiple of 16, or a destination overlapping a source or
+ * another destination is LN_ERR_PARAM; a NULL array or pointer LN_ERR_NULL;
+ * bytes == 0 a no-op.  Enqueued on `stream`; no allocation.
+ */
+ln_status_t hbm_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
+                       size_t bytes, hipStream_t stream);
 
 /* Static English description of a status code (never NULL). */
 const char* ln_status_string(ln_status_t status);

@@ -56,6 +56,13 @@ def lib() -> ctypes.CDLL:
     L.bias_dropout_residual_ln_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                ctypes.c_size_t, i64, i64, f32, ctypes.c_uint64,
                                                i32, vp]
+    L.bias_dropout_residual_ln_bwd_dx.restype = i32
+    L.bias_dropout_residual_ln_bwd_dx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  ctypes.c_size_t, i64, i64, f32,
+                                                  ctypes.c_uint64, i32, vp]
+    L.bias_dropout_residual_ln_bwd_fold.restype = i32
+    L.bias_dropout_residual_ln_bwd_fold.argtypes = [vp, ctypes.c_size_t, vp, vp, vp, i64, i64,
+                                                    vp]
     L.attn_softmax_fwd.restype = i32
     L.attn_softmax_fwd.argtypes = [vp, vp, i64, vp, vp, i64, i64, f32, i32, f32,
                                    ctypes.c_uint64, i32, vp]
@@ -72,6 +79,9 @@ def lib() -> ctypes.CDLL:
     L.cross_entropy_fwd_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, f32, i32, vp]
     L.hbm_copy.restype = i32
     L.hbm_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    L.hbm_stream.restype = i32
+    L.hbm_stream.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(vp), i32, ctypes.c_size_t,
+                             vp]
     L.ln_debug_force_path.restype = i32
     L.ln_debug_force_path.argtypes = [i32, i32, i32]
     L.ln_debug_force_grid.restype = i32
@@ -306,6 +316,49 @@ def bias_dropout_residual_ln_bwd(dy, z, gamma, mean, rstd, p: float, seed: int, 
     return dresidual, dx, dgamma, dbeta, dbias
 
 
+def bias_dropout_residual_ln_bwd_dx(dy, z, gamma, mean, rstd, p: float, seed: int, *,
+                                    workspace, dz_extra=None, dresidual=None, dx=None):
+    """Stage 1 of bias_dropout_residual_ln_bwd -> (dresidual, dx); the column
+    partials go to `workspace` (finish with bias_dropout_residual_ln_bwd_fold)."""
+    rows, cols = _mat(z, "z")
+    for t, n in ((dy, "dy"), (dz_extra, "dz_extra")):
+        if t is not None and (t.shape != z.shape or t.dtype != z.dtype):
+            raise ValueError(f"{n} must match z")
+        if t is not None:
+            _mat(t, n)
+    _vec(gamma, cols, z.dtype, "gamma")
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        _vec(t, rows, torch.float32, n)
+    dresidual = _out(dresidual, z.shape, z.dtype, z.device, "dresidual")
+    dx = _out(dx, z.shape, z.dtype, z.device, "dx")
+    if workspace.dtype != torch.float32 or not workspace.is_cuda:
+        raise ValueError("workspace must be a float32 GPU tensor")
+    if rows == 0:
+        return dresidual, dx
+    _check(lib().bias_dropout_residual_ln_bwd_dx(
+        _ptr(dy), _ptr(dz_extra), _ptr(z), _ptr(gamma), _ptr(mean), _ptr(rstd),
+        _ptr(dresidual), _ptr(dx), _ptr(workspace), workspace.numel() * 4, rows, cols,
+        float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, _dt(z), _stream(z)))
+    return dresidual, dx
+
+
+def bias_dropout_residual_ln_bwd_fold(workspace, rows: int, cols: int, *, dgamma=None,
+                                      dbeta=None, dbias=None):
+    """Stage 2 of bias_dropout_residual_ln_bwd -> (dgamma, dbeta, dbias) float32."""
+    device = workspace.device
+    dgamma = _out(dgamma, (cols,), torch.float32, device, "dgamma")
+    dbeta = _out(dbeta, (cols,), torch.float32, device, "dbeta")
+    dbias = _out(dbias, (cols,), torch.float32, device, "dbias")
+    if workspace.dtype != torch.float32 or not workspace.is_cuda:
+        raise ValueError("workspace must be a float32 GPU tensor")
+    if rows == 0:
+        return dgamma.zero_(), dbeta.zero_(), dbias.zero_()
+    _check(lib().bias_dropout_residual_ln_bwd_fold(
+        _ptr(workspace), workspace.numel() * 4, _ptr(dgamma), _ptr(dbeta), _ptr(dbias),
+        int(rows), int(cols), _stream(workspace)))
+    return dgamma, dbeta, dbias
+
+
 def attn_softmax_fwd(x, scale: float = 1.0, *, mask=None, rows_per_mask: int = 1,
                      causal: bool = False, p: float = 0.0, seed: int = 0, y=None,
                      y_dropped=None, want_dropped: bool = False):
@@ -444,6 +497,20 @@ def hbm_copy(src, dst) -> None:
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("hbm_copy: src and dst differ in size")
     _check(lib().hbm_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)))
+
+
+def hbm_stream(srcs, dsts) -> None:
+    """Measurement reference: read every tensor of `srcs` (1-3) and write every
+    tensor of `dsts` (0-2), all contiguous GPU tensors of one byte size."""
+    ts = list(srcs) + list(dsts)
+    if not ts or any(not t.is_cuda or not t.is_contiguous() for t in ts):
+        raise ValueError("hbm_stream takes contiguous GPU tensors")
+    nbytes = srcs[0].numel() * srcs[0].element_size()
+    if any(t.numel() * t.element_size() != nbytes for t in ts):
+        raise ValueError("hbm_stream tensors must have one byte size")
+    s = (ctypes.c_void_p * max(1, len(srcs)))(*[t.data_ptr() for t in srcs])
+    d = (ctypes.c_void_p * max(1, len(dsts)))(*[t.data_ptr() for t in dsts])
+    _check(lib().hbm_stream(s, len(srcs), d, len(dsts), nbytes, _stream(srcs[0])))
 
 
 def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,

@@ -481,7 +481,7 @@ ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const fl
                      (cols * (int64_t)es) % 16 == 0;
     BwdArgs a{};
     a.dy = dy; a.x = x; a.gamma = gamma; a.mean = mean; a.rstd = rstd; a.dx = dx;
-    a.ws = workspace;
+    a.ws = workspace; a.ws_vec = aligned16(workspace);
     a.rows = rows; a.m = cols;
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.parts = bwd_partitions(rows, cols);
@@ -518,6 +518,7 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
         const bool vec = aligned16(dy) && aligned16(x) && (cols * (int64_t)es) % 16 == 0;
         BwdArgs a{};
         a.dy = dy; a.x = x; a.mean = mean; a.rstd = rstd; a.ws = workspace;
+        a.ws_vec = aligned16(workspace);
         a.rows = rows; a.m = cols;
         a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
         a.parts = parts;
@@ -557,7 +558,7 @@ ln_status_t ln_bwd_noalloc(const void* dy, const void* x, const void* gamma, con
                      (cols * (int64_t)es) % 16 == 0;
     BwdArgs a{};
     a.dy = dy; a.x = x; a.gamma = gamma; a.mean = mean; a.rstd = rstd; a.dx = dx;
-    a.ws = ws;
+    a.ws = ws; a.ws_vec = aligned16(ws);
     a.rows = rows; a.m = cols;
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.parts = bwd_partitions(rows, cols);
@@ -570,16 +571,17 @@ ln_status_t ln_bwd_noalloc(const void* dy, const void* x, const void* gamma, con
     return from_hip(launch_fold(ws, a.parts, cols, 2, out, stream));
 }
 
-ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, const void* z,
-                                         const void* gamma, const float* mean,
-                                         const float* rstd, void* dresidual, void* dx,
-                                         float* dgamma, float* dbeta, float* dbias,
-                                         float* workspace, size_t workspace_bytes, int64_t rows,
-                                         int64_t cols, float p, uint64_t seed, ln_dtype_t dt,
-                                         hipStream_t stream) {
-    if (!dy || !z || !gamma || !mean || !rstd || !dresidual || !dx || !dgamma || !dbeta ||
-        !dbias || !workspace)
+// Stage 1 of the prologue backward (dresidual, dx and the three kinds of
+// column partials); with `fold`, also stage 2 into dgamma/dbeta/dbias.
+static ln_status_t prologue_bwd(const void* dy, const void* dz_extra, const void* z,
+                                const void* gamma, const float* mean, const float* rstd,
+                                void* dresidual, void* dx, float* dgamma, float* dbeta,
+                                float* dbias, float* workspace, size_t workspace_bytes,
+                                int64_t rows, int64_t cols, float p, uint64_t seed,
+                                ln_dtype_t dt, hipStream_t stream, bool fold) {
+    if (!dy || !z || !gamma || !mean || !rstd || !dresidual || !dx || !workspace)
         return LN_ERR_NULL;
+    if (fold && (!dgamma || !dbeta || !dbias)) return LN_ERR_NULL;
     ln_status_t st = check_shape(rows, cols, dt);
     if (st != LN_OK) return st;
     if (cols > LN_MAX_COLS_DROPOUT_BWD) return LN_ERR_UNSUPPORTED;
@@ -589,7 +591,7 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
     if (rows == 0) return LN_OK;
     const size_t es = elem_bytes(dt);
     const size_t tb = (size_t)rows * (size_t)cols * es, vb = (size_t)cols * es;
-    const size_t sb = (size_t)rows * sizeof(float), cb = (size_t)cols * sizeof(float);
+    const size_t sb = (size_t)rows * sizeof(float), cb = fold ? (size_t)cols * sizeof(float) : 0;
     const Span outs[] = {{dresidual, tb, true}, {dx, tb, true}, {dgamma, cb, false},
                          {dbeta, cb, false}, {dbias, cb, false}, {workspace, need, false}};
     const Span ins[] = {{dy, tb, true}, {dz_extra, dz_extra ? tb : 0, true}, {z, tb, true},
@@ -604,6 +606,7 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
     BwdArgs a{};
     a.dy = dy; a.x = z; a.gamma = gamma; a.mean = mean; a.rstd = rstd; a.dx = dresidual;
     a.dz_extra = dz_extra; a.dx_in = dx; a.ws = workspace;
+    a.ws_vec = aligned16(workspace);
     a.rows = rows; a.m = cols;
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.parts = bwd_partitions(rows, cols);
@@ -613,12 +616,55 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
     st = from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec, true), BwdMode::DROPOUT, a, stream));
-    if (st != LN_OK) return st;
+    if (st != LN_OK || !fold) return st;
     FoldOut out{};
     out.p[0] = dgamma;
     out.p[1] = dbeta;
     out.p[2] = dbias;
     return from_hip(launch_fold(workspace, a.parts, cols, 3, out, stream));
+}
+
+ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, const void* z,
+                                         const void* gamma, const float* mean,
+                                         const float* rstd, void* dresidual, void* dx,
+                                         float* dgamma, float* dbeta, float* dbias,
+                                         float* workspace, size_t workspace_bytes, int64_t rows,
+                                         int64_t cols, float p, uint64_t seed, ln_dtype_t dt,
+                                         hipStream_t stream) {
+    return prologue_bwd(dy, dz_extra, z, gamma, mean, rstd, dresidual, dx, dgamma, dbeta, dbias,
+                        workspace, workspace_bytes, rows, cols, p, seed, dt, stream, true);
+}
+
+ln_status_t bias_dropout_residual_ln_bwd_dx(const void* dy, const void* dz_extra, const void* z,
+                                            const void* gamma, const float* mean,
+                                            const float* rstd, void* dresidual, void* dx,
+                                            float* workspace, size_t workspace_bytes,
+                                            int64_t rows, int64_t cols, float p, uint64_t seed,
+                                            ln_dtype_t dt, hipStream_t stream) {
+    return prologue_bwd(dy, dz_extra, z, gamma, mean, rstd, dresidual, dx, nullptr, nullptr,
+                        nullptr, workspace, workspace_bytes, rows, cols, p, seed, dt, stream,
+                        false);
+}
+
+ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t workspace_bytes,
+                                              float* dgamma, float* dbeta, float* dbias,
+                                              int64_t rows, int64_t cols, hipStream_t stream) {
+    if (!workspace || !dgamma || !dbeta || !dbias) return LN_ERR_NULL;
+    if (rows < 0 || cols <= 0) return LN_ERR_SHAPE;
+    if (cols > LN_MAX_COLS_DROPOUT_BWD || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
+    const size_t need = bias_dropout_residual_ln_bwd_workspace_bytes(rows, cols);
+    if (workspace_bytes < need) return LN_ERR_WORKSPACE;
+    if (rows == 0) return LN_OK;
+    const size_t cb = (size_t)cols * sizeof(float);
+    const Span outs[] = {{dgamma, cb, false}, {dbeta, cb, false}, {dbias, cb, false}};
+    const Span ins[] = {{workspace, need, false}};
+    const ln_status_t st = check_aliasing(outs, 3, ins, 1);
+    if (st != LN_OK) return st;
+    FoldOut out{};
+    out.p[0] = dgamma;
+    out.p[1] = dbeta;
+    out.p[2] = dbias;
+    return from_hip(launch_fold(workspace, bwd_partitions(rows, cols), cols, 3, out, stream));
 }
 
 ln_status_t add_rmsnorm_fwd(const void* x, const void* residual, const void* gamma,
@@ -677,7 +723,7 @@ ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
                      aligned16(gamma) && aligned16(dz) && (cols * (int64_t)es) % 16 == 0;
     BwdArgs a{};
     a.dy = dy; a.x = z; a.gamma = gamma; a.rstd = rstd; a.dx = dz; a.dz_extra = dz_extra;
-    a.ws = workspace;
+    a.ws = workspace; a.ws_vec = aligned16(workspace);
     a.rows = rows; a.m = cols;
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.parts = bwd_partitions(rows, cols);

@@ -416,65 +416,85 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
             }
         }
         // Then the units whose lanes own the same columns (the waves of the
-        // workgroup for G <= 64, its row groups otherwise): every unit stages
-        // its sums in LDS, one barrier, then the workgroup adds them in unit
-        // order (0, 1, ...) column by column, consecutive threads taking
-        // consecutive columns, and writes the workgroup's partial.  The
-        // accumulators go through LDS in chunks of CI slot indices so the
-        // footprint stays within kStage bytes (gfx950 has 160 KB of LDS per
-        // workgroup; most layouts then stage every accumulator in one chunk:
-        // one barrier instead of one per chunk).
+        // workgroup for G <= 64, its row groups otherwise) are added in unit
+        // order 0, 1, ... and the workgroup writes its partition's [NK][m]
+        // partial.  Lane l of a unit holds, for slot i of its row, all E
+        // values of that slot, so the thread that adds slot i of lane
+        // position l over the units writes E consecutive columns at once:
+        // 16-byte stores, half the write time of one 4-byte store per column
+        // at the end of the kernel.  Units stage their sums in LDS (lane
+        // position fastest: conflict-free), in chunks of CI slot indices
+        // that fit kStage bytes (gfx950 has 160 KB of LDS per workgroup);
+        // unit u adds the (kind, slot) pairs u, u + NU, ...  A workgroup of
+        // a single unit writes its sums directly.
+        constexpr int NT = BwdGeometry<G>::NT;
         constexpr int kStage = 156 * 1024;
-        constexpr int KF = kStage / (NU * NK * UT * 4);          // floats per lane that fit
-        constexpr int CI = (KF - 1) / E < 1 ? 1 : ((KF - 1) / E < V ? (KF - 1) / E : V);
-        constexpr int CK = CI * E + 1;                          // padded lane stride
-        constexpr int CW = CI * G * E;                          // columns per chunk
+        constexpr int CI0 = kStage / (NT * NK * E * 4);
+        constexpr int CI = CI0 < 1 ? 1 : (CI0 < V ? CI0 : V);
+        static_assert(NU == 1 || NT * NK * CI * E * 4 <= kStage, "stage exceeds its budget");
         float* const pw = a.ws + part * NK * a.m;   // this partition's [NK][m] partial
-        constexpr bool DIRECT = NU == 1 && NK * UT * CK * 4 > kStage;
-        if constexpr (DIRECT) {
-            // one unit too wide to stage: every column is held by exactly
-            // one lane, which writes it
+        // 16-byte partial stores need the partial rows 16-byte aligned
+        const bool wvec = VEC && a.ws_vec;          // uniform
+        const int unit = tid / UT;
+        const int pos = tid % UT;                    // lane position within the unit's row(s)
+        // write the E sums of slot `sl` of one kind
+        auto put = [&](int kind, int sl, const float* t) {
+            float* dst = pw + kind * a.m + sl * E;
+            if (wvec) {
 #pragma unroll
-            for (int k = 0; k < KA; ++k) {
-                const int col = ((k / E) * G + lg) * E + k % E;
-                if ((k / E) * G + lg < nslots && col < m) {
+                for (int e = 0; e < E; e += 4) {
+                    f32x4 v = {t[e], t[e + 1], t[e + 2], t[e + 3]};
+                    *reinterpret_cast<f32x4*>(dst + e) = v;
+                }
+            } else {
 #pragma unroll
-                    for (int kind = 0; kind < NK; ++kind) pw[kind * a.m + col] = acc[kind][k];
+                for (int e = 0; e < E; ++e)
+                    if (sl * E + e < m) dst[e] = t[e];
+            }
+        };
+        if constexpr (NU == 1) {
+            // one unit: lane position lg alone holds its columns
+#pragma unroll
+            for (int kind = 0; kind < NK; ++kind) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    if (i * G + lg < nslots) put(kind, i * G + lg, &acc[kind][i * E]);
                 }
             }
             return;
-        }
-        static_assert(DIRECT || NU * NK * UT * CK * 4 <= kStage, "stage exceeds its budget");
-        __shared__ float stage[DIRECT ? 1 : NU][NK][DIRECT ? 1 : UT][DIRECT ? 1 : CK];
-        const int unit = tid / UT;
-        const int pos = tid % UT;
+        } else {
+            __shared__ float stage[NU][NK][CI * E][UT];
 #pragma unroll
-        for (int i0 = 0; i0 < V; i0 += CI) {
-            if (i0 > 0) __syncthreads();   // previous chunk fully read
+            for (int i0 = 0; i0 < V; i0 += CI) {
+                if (i0 > 0) __syncthreads();   // previous chunk fully read
 #pragma unroll
-            for (int c = 0; c < CI * E; ++c) {
-                const int k = i0 * E + c;
-                if (k < KA) {
+                for (int c = 0; c < CI * E; ++c) {
+                    if (i0 * E + c < KA) {
 #pragma unroll
-                    for (int kind = 0; kind < NK; ++kind) stage[unit][kind][pos][c] = acc[kind][k];
+                        for (int kind = 0; kind < NK; ++kind)
+                            stage[unit][kind][c][pos] = acc[kind][i0 * E + c];
+                    }
                 }
-            }
-            __syncthreads();
-            const int col0 = i0 * G * E;
-            for (int q = tid; q < NK * CW; q += BwdGeometry<G>::NT) {
-                const int kind = q / CW;
-                const int cl = q - kind * CW;
-                const int col = col0 + cl;
-                if (col >= m) continue;
-                // lane (of the first row group) and accumulator holding
-                // column col: slot col/E, element col%E
-                const int sl = cl / E, ee = cl % E;
-                const int il = sl / G, lig = sl % G;
-                const int c = il * E + ee;
-                float t = stage[0][kind][lig][c];
+                __syncthreads();
+                // positions past the row group's lanes (G < 64) hold copies
+                if (pos < G) {
+                    for (int cb = unit; cb < NK * CI; cb += NU) {
+                        const int kind = cb / CI;
+                        const int i = i0 + cb % CI;
+                        const int sl = i * G + pos;
+                        if (i >= V || sl >= nslots) continue;
+                        float t[E];
 #pragma unroll
-                for (int u = 1; u < NU; ++u) t = t + stage[u][kind][lig][c];
-                pw[kind * a.m + col] = t;
+                        for (int e = 0; e < E; ++e) {
+                            const int c = (i - i0) * E + e;
+                            float sum = stage[0][kind][c][pos];
+#pragma unroll
+                            for (int u = 1; u < NU; ++u) sum = sum + stage[u][kind][c][pos];
+                            t[e] = sum;
+                        }
+                        put(kind, sl, t);
+                    }
+                }
             }
         }
     }

@@ -30,6 +30,7 @@
 namespace mbrow {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Call f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time
 // indices, e.g. to pick a packed element).

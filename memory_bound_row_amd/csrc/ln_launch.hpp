@@ -65,6 +65,7 @@ struct BwdArgs {
     const void* dz_extra;   // prologue mode: gradient reaching z from its other uses, or NULL
     void* dx_in;            // prologue mode: gradient of the prologue's x
     float* ws;              // [P][K][m] partials (K = 2, or 3 with dbias)
+    int ws_vec;             // ws 16-byte aligned (16-byte partial stores on the vector path)
     int64_t rows;
     int64_t m;
     int64_t nslots;

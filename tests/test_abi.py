@@ -342,3 +342,36 @@ def test_hbm_copy_validation(L):
     assert L.hbm_copy(A, A + 16, 64, None) == LN_ERR_PARAM   # overlapping ranges
     assert L.hbm_copy(A + 16, A, 64, None) == LN_ERR_PARAM
     assert L.hbm_copy(A, A, 16, None) == LN_ERR_PARAM
+
+
+def test_prologue_backward_stage_validation(L):
+    # stage 1: the combined call's checks without the [cols] outputs
+    ws = 1 << 40
+    args = dict(dy=A, ez=None, z=B, g=C, mean=D, rstd=E, dres=F, dx=G, ws=ws, wsb=1 << 30,
+                rows=4, cols=8, p=0.1, seed=1, dt=BF16)
+
+    def st1(**kw):
+        a = dict(args, **kw)
+        return L.bias_dropout_residual_ln_bwd_dx(a["dy"], a["ez"], a["z"], a["g"], a["mean"],
+                                                 a["rstd"], a["dres"], a["dx"], a["ws"],
+                                                 a["wsb"], a["rows"], a["cols"], a["p"],
+                                                 a["seed"], a["dt"], None)
+    assert st1(dy=None) == LN_ERR_NULL
+    assert st1(ws=None) == LN_ERR_NULL
+    assert st1(rows=-1) == LN_ERR_SHAPE
+    assert st1(p=1.0) == LN_ERR_PARAM
+    assert st1(wsb=4) == LN_ERR_WORKSPACE
+    assert st1(cols=8193) == LN_ERR_UNSUPPORTED
+    assert st1(dt=9) == LN_ERR_DTYPE
+    assert st1(rows=0) == LN_OK
+
+    def fold(ws=ws, wsb=1 << 30, dg=D, db=E, dbias=F, rows=4, cols=8):
+        return L.bias_dropout_residual_ln_bwd_fold(ws, wsb, dg, db, dbias, rows, cols, None)
+    assert fold(ws=None) == LN_ERR_NULL
+    assert fold(dbias=None) == LN_ERR_NULL
+    assert fold(rows=-1) == LN_ERR_SHAPE
+    assert fold(cols=0) == LN_ERR_SHAPE
+    assert fold(cols=8193) == LN_ERR_UNSUPPORTED
+    assert fold(wsb=8) == LN_ERR_WORKSPACE
+    assert fold(dg=ws) == LN_ERR_UNSUPPORTED            # output over the partials
+    assert fold(rows=0) == LN_OK

@@ -170,3 +170,20 @@ def test_seed_changes_mask():
     # p = 0.5: about half the positions differ between independent masks
     frac = (a != b).float().mean().item()
     assert 0.4 < frac < 0.6, frac
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,cols", [(8192, 1280), (37, 1001)])
+def test_two_stage_calls_equal_the_combined_call(dtype, rows, cols):
+    # bias_dropout_residual_ln_bwd_dx then _fold give the combined call's bits
+    case(f"prologue backward split stages {dtype} {rows}x{cols}")
+    inp, z, mean, rstd, _, ez = forward(rows, cols, dtype, 0.1, 21)
+    want = backward(inp, z, mean, rstd, 0.1, 21, ez)
+    ws = mb.dropout_workspace(rows, cols, z.device)
+    dres, dx = mb.bias_dropout_residual_ln_bwd_dx(inp["dy"], z, inp["gamma"], mean, rstd, 0.1,
+                                                  21, workspace=ws, dz_extra=ez)
+    dg, db, dbias = mb.bias_dropout_residual_ln_bwd_fold(ws, rows, cols)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dresidual", "dx", "dgamma", "dbeta", "dbias"),
+                          (dres, dx, dg, db, dbias), want):
+        assert torch.equal(a, b), name
