@@ -537,7 +537,7 @@ def configs_report(cpp_launch: bool = True) -> None:
               "cpp_loop_us": cpp[rows].get("cpp_loop_us"), "cpp_graph_us": cpp[rows].get("graph_us"),
               "python_loop_us": round(py_us, 3), "torch_graph_us": round(g_us, 3)})
 
-    def fwd_bwd(rows, cols, dtype, sets, iters, label, fwd=True):
+    def fwd_bwd(rows, cols, dtype, sets, iters, label, fwd=True, bwd=True):
         s = torch.tensor([], dtype=dtype).element_size()
         inp = synth.layer_inputs(rows, cols, dtype, names=("x", "gamma", "beta", "dy"))
         gamma, beta = inp["gamma"].to(dev), inp["beta"].to(dev)
@@ -568,7 +568,8 @@ def configs_report(cpp_launch: bool = True) -> None:
         def both(i):
             if fwd:
                 f(i)
-            bw(i)
+            if bwd:
+                bw(i)
 
         for i in range(sets):
             f(i)
@@ -577,20 +578,21 @@ def configs_report(cpp_launch: bool = True) -> None:
         ms = timed(capture(both, iters), iters)
         rec = {"workload": label, "rows": rows, "cols": cols, "storage": str(dtype)[6:],
                "buffer_sets": sets, "iters": iters}
-        nb = pb["step"] if fwd else pb["bwd"]
+        nb = (pb["step"] if fwd else pb["bwd"]) if bwd else pb["fwd"]
         rec["bytes_per_pass"] = nb
         rec["us_per_pass"] = round(ms * 1e3, 3)
         rec["GBps"] = round(nb / (ms * 1e-3) / 1e9, 1)
         rec["pct_of_hbm_peak"] = round(100.0 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
-        if fwd:
+        if fwd and bwd:
             msf = timed(capture(f, iters), iters)
             rec["fwd_bytes"] = pb["fwd"]
             rec["fwd_us"] = round(msf * 1e3, 3)
             rec["fwd_GBps"] = round(pb["fwd"] / (msf * 1e-3) / 1e9, 1)
-        msb = timed(capture(bw, iters), iters)
-        rec["bwd_bytes"] = pb["bwd"]
-        rec["bwd_fold_us"] = round(msb * 1e3, 3)
-        rec["bwd_GBps"] = round(pb["bwd"] / (msb * 1e-3) / 1e9, 1)
+        if bwd:
+            msb = timed(capture(bw, iters), iters)
+            rec["bwd_bytes"] = pb["bwd"]
+            rec["bwd_fold_us"] = round(msb * 1e3, 3)
+            rec["bwd_GBps"] = round(pb["bwd"] / (msb * 1e-3) / 1e9, 1)
         emit(rec)
         del st, ws
         torch.cuda.empty_cache()
@@ -910,6 +912,14 @@ def configs_report(cpp_launch: bool = True) -> None:
     for dtype in (torch.float32, torch.bfloat16):
         for rows, cols in ((4096, 16384), (65536, 1000)):
             fwd_bwd(rows, cols, dtype, 2, 20, "LayerNorm forward + backward, wide/ragged rows")
+    # rows past the register layouts, staged in LDS
+    fwd_bwd(4096, 32768, torch.bfloat16, 2, 20,
+            "LayerNorm forward + backward, LDS-staged rows (widest 16-bit backward)")
+    fwd_bwd(4096, 19968, torch.float32, 2, 20,
+            "LayerNorm forward + backward, LDS-staged rows (widest fp32 backward)")
+    for dtype in (torch.float32, torch.bfloat16):
+        fwd_bwd(2048, 65536, dtype, 2, 20, "LayerNorm forward, LDS-staged rows (widest; fp32 "
+                "rows past the stage read again)", bwd=False)
 
 
 def main():

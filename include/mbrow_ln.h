@@ -65,8 +65,8 @@ typedef enum {
     LN_ERR_DTYPE = 3,       /* unknown ln_dtype_t                              */
     LN_ERR_PARAM = 4,       /* eps < 0 or NaN; p outside [0, 1) or NaN         */
     LN_ERR_WORKSPACE = 5,   /* workspace smaller than ln_bwd_workspace_bytes   */
-    LN_ERR_UNSUPPORTED = 6, /* cols above LN_MAX_COLS, or an aliasing form
-                               the call does not allow                        */
+    LN_ERR_UNSUPPORTED = 6, /* cols above the call's LN_MAX_COLS*, or an
+                               aliasing form the call does not allow          */
     LN_ERR_HIP = 7,         /* a HIP launch or query failed                    */
     LN_ERR_SCRATCH = 8      /* ln_bwd_noalloc: the shape needs more than the
                                library's static scratch of
@@ -77,9 +77,19 @@ typedef enum {
  * until the process ends). */
 #define LN_NOALLOC_SCRATCH_BYTES (16u << 20)
 
-/* Widest row supported, for every storage type (the whole row is held in
- * registers of one workgroup). */
-#define LN_MAX_COLS 16384
+/* Widest row of ln_fwd and bias_dropout_residual_ln_fwd, for every storage
+ * type.  Rows of up to 16384 columns are held in registers; wider rows are
+ * staged in the LDS of one workgroup (read from global memory once while
+ * they fit it: 39936 fp32 or 65536 16-bit columns; the rest of a wider fp32
+ * row is read again in each later pass). */
+#define LN_MAX_COLS 65536
+/* Widest row of ln_bwd_dx, ln_bwd_dgamma_dbeta and ln_bwd_noalloc: past
+ * 16384 columns both dy and x are staged in LDS, which holds 19968 fp32 or
+ * (capped here) 32768 16-bit columns of each. */
+#define LN_MAX_COLS_BWD_F32 19968
+#define LN_MAX_COLS_BWD_16 32768
+/* Widest row of add_rmsnorm_fwd and add_rmsnorm_bwd (registers only). */
+#define LN_MAX_COLS_RMSNORM 16384
 /* Widest row of bias_dropout_residual_ln_bwd, for every storage type (its
  * three column accumulators per value need the registers of twice as many
  * lanes). */

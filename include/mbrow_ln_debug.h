@@ -54,6 +54,14 @@ ln_status_t ln_debug_force_grid(int workgroups_per_cu);
  */
 ln_status_t ln_debug_force_two_pass(int on);
 
+/*
+ * on != 0: every later ln_fwd, bias_dropout_residual_ln_fwd, ln_bwd_dx,
+ * ln_bwd_dgamma_dbeta and ln_bwd_noalloc call takes the LDS-staged path (the
+ * one for rows wider than 16384 columns) whatever its width; 0 restores the
+ * width-based choice.  Results are within the same tolerances either way.
+ */
+ln_status_t ln_debug_force_staged(int on);
+
 #ifdef __cplusplus
 }
 #endif

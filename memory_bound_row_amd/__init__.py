@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.ln_debug_force_grid.argtypes = [i32]
     L.ln_debug_force_two_pass.restype = i32
     L.ln_debug_force_two_pass.argtypes = [i32]
+    L.ln_debug_force_staged.restype = i32
+    L.ln_debug_force_staged.argtypes = [i32]
     _lib = L
     return L
 
@@ -518,6 +520,11 @@ def debug_force_path(lanes_per_row: int = 0, slots_per_lane: int = 0,
     """Test-only: force the row layout of later calls (0 restores the default)."""
     _check(lib().ln_debug_force_path(int(lanes_per_row), int(slots_per_lane),
                                      1 if scalar else 0))
+
+
+def debug_force_staged(on: bool = False) -> None:
+    """Test hook: route every LayerNorm call through the LDS-staged path."""
+    _check(lib().ln_debug_force_staged(1 if on else 0))
 
 
 def debug_force_two_pass(on: bool = False) -> None:

@@ -36,6 +36,7 @@ UNITS = (
     + [("rmsnorm.hip", ["-DMBROW_DT=%d" % d], "rmsnorm_%d.o" % d) for d in range(3)]
     + [("xent.hip", ["-DMBROW_DT=%d" % d], "xent_%d.o" % d) for d in range(3)]
     + [("stream.hip", ["-DMBROW_DT=%d" % d], "stream_%d.o" % d) for d in range(3)]
+    + [("ln_wide.hip", ["-DMBROW_DT=%d" % d], "ln_wide_%d.o" % d) for d in range(3)]
     + [("ln_fold.hip", [], "ln_fold.o"), ("copy.hip", [], "copy.o"),
        ("noalloc.hip", [], "noalloc.o"),
        ("ln_api.cpp", [], "ln_api.o")]

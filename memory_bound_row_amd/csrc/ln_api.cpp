@@ -87,6 +87,29 @@ hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStr
     }
 }
 
+hipError_t launch_wide_fwd_f32(bool, bool, const FwdArgs&, hipStream_t);
+hipError_t launch_wide_fwd_f16(bool, bool, const FwdArgs&, hipStream_t);
+hipError_t launch_wide_fwd_bf16(bool, bool, const FwdArgs&, hipStream_t);
+hipError_t launch_wide_bwd_f32(bool, BwdMode, const BwdArgs&, hipStream_t);
+hipError_t launch_wide_bwd_f16(bool, BwdMode, const BwdArgs&, hipStream_t);
+hipError_t launch_wide_bwd_bf16(bool, BwdMode, const BwdArgs&, hipStream_t);
+
+hipError_t launch_wide_fwd(Dt dt, bool vec, bool fused, const FwdArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_wide_fwd_f32(vec, fused, a, s);
+    case Dt::F16: return launch_wide_fwd_f16(vec, fused, a, s);
+    default: return launch_wide_fwd_bf16(vec, fused, a, s);
+    }
+}
+
+hipError_t launch_wide_bwd(Dt dt, bool vec, BwdMode mode, const BwdArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_wide_bwd_f32(vec, mode, a, s);
+    case Dt::F16: return launch_wide_bwd_f16(vec, mode, a, s);
+    default: return launch_wide_bwd_bf16(vec, mode, a, s);
+    }
+}
+
 hipError_t launch_bwd(Dt dt, const Path& p, BwdMode mode, const BwdArgs& a, hipStream_t s) {
     switch (dt) {
     case Dt::F32: return launch_bwd_f32(p, mode, a, s);
@@ -110,11 +133,12 @@ static bool have_instance(bool f32, int g, int v) {
 }
 
 static std::atomic<int> g_force_g{0}, g_force_v{0}, g_force_scalar{0}, g_force_grid{0},
-    g_force_two_pass{0};
+    g_force_two_pass{0}, g_force_staged{0};
 
 // The test-only override that forces the per-element path (no vector access).
 bool force_scalar() { return g_force_scalar.load(std::memory_order_relaxed) != 0; }
 bool force_two_pass() { return g_force_two_pass.load(std::memory_order_relaxed) != 0; }
+bool force_staged() { return g_force_staged.load(std::memory_order_relaxed) != 0; }
 
 // Row layout: among the candidate layouts, the one with the fewest slots
 // (used or not); ties go to the earlier candidate.  With `wave_rows`, slots
@@ -296,7 +320,15 @@ bool valid_dtype(ln_dtype_t dt) { return dt == LN_F32 || dt == LN_F16 || dt == L
 
 size_t elem_bytes(ln_dtype_t dt) { return dt == LN_F32 ? 4 : 2; }
 
-int64_t max_cols(ln_dtype_t) { return LN_MAX_COLS; }
+enum class Kind { FWD, BWD, RMS };
+
+int64_t max_cols(ln_dtype_t dt, Kind k) {
+    switch (k) {
+    case Kind::FWD: return LN_MAX_COLS;
+    case Kind::BWD: return dt == LN_F32 ? LN_MAX_COLS_BWD_F32 : LN_MAX_COLS_BWD_16;
+    default: return LN_MAX_COLS_RMSNORM;
+    }
+}
 
 // widest softmax row held in registers (wider rows take the two-pass path)
 int64_t softmax_max_cols(ln_dtype_t dt, bool backward) {
@@ -334,12 +366,16 @@ ln_status_t check_aliasing(const Span* outs, int nout, const Span* ins, int nin)
     return LN_OK;
 }
 
-ln_status_t check_shape(int64_t rows, int64_t cols, ln_dtype_t dt) {
+ln_status_t check_shape(int64_t rows, int64_t cols, ln_dtype_t dt, Kind k) {
     if (!valid_dtype(dt)) return LN_ERR_DTYPE;
     if (rows < 0 || cols <= 0) return LN_ERR_SHAPE;
-    if (cols > max_cols(dt) || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
+    if (cols > max_cols(dt, k) || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
     return LN_OK;
 }
+
+// LayerNorm rows past the register layouts, or every row under the test hook,
+// take the LDS-staged kernels.
+bool staged(int64_t cols) { return cols > kRegisterMaxCols || force_staged(); }
 
 ln_status_t from_hip(hipError_t e) { return e == hipSuccess ? LN_OK : LN_ERR_HIP; }
 
@@ -393,7 +429,7 @@ ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, 
                    float* rstd, int64_t rows, int64_t cols, float eps, ln_dtype_t dt,
                    hipStream_t stream) {
     if (!x || !gamma || !beta || !y) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::FWD);
     if (st != LN_OK) return st;
     if (!(eps >= 0.0f) || std::isinf(eps)) return LN_ERR_PARAM;
     if (rows == 0) return LN_OK;
@@ -414,6 +450,7 @@ ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, 
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.eps = eps;
     a.inv_m = (float)(1.0 / (double)cols);
+    if (staged(cols)) return from_hip(launch_wide_fwd(d, vec && !force_scalar(), false, a, stream));
     return from_hip(launch_fwd(d, pick_path(d, cols, vec), false, a, stream));
 }
 
@@ -423,7 +460,7 @@ ln_status_t bias_dropout_residual_ln_fwd(const void* x, const void* bias, const 
                                          int64_t rows, int64_t cols, float eps, float p,
                                          uint64_t seed, ln_dtype_t dt, hipStream_t stream) {
     if (!x || !bias || !residual || !gamma || !beta || !residual_out || !y) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::FWD);
     if (st != LN_OK) return st;
     if (!(eps >= 0.0f) || std::isinf(eps)) return LN_ERR_PARAM;
     if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
@@ -453,7 +490,8 @@ ln_status_t bias_dropout_residual_ln_fwd(const void* x, const void* bias, const 
     a.scale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
-    st = from_hip(launch_fwd(d, pick_path(d, cols, vec), true, a, stream));
+    st = staged(cols) ? from_hip(launch_wide_fwd(d, vec && !force_scalar(), true, a, stream))
+                      : from_hip(launch_fwd(d, pick_path(d, cols, vec), true, a, stream));
     if (st == LN_OK && mask_out) st = from_hip(launch_dropout_mask(a, stream));
     return st;
 }
@@ -462,7 +500,7 @@ ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const fl
                       const float* rstd, void* dx, float* workspace, size_t workspace_bytes,
                       int64_t rows, int64_t cols, ln_dtype_t dt, hipStream_t stream) {
     if (!dy || !x || !gamma || !mean || !rstd || !dx) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::BWD);
     if (st != LN_OK) return st;
     const size_t need = ln_bwd_workspace_bytes(rows, cols);
     if (workspace && workspace_bytes < need) return LN_ERR_WORKSPACE;
@@ -487,6 +525,7 @@ ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const fl
     a.parts = bwd_partitions(rows, cols);
     a.inv_m = (float)(1.0 / (double)cols);
     const BwdMode mode = workspace ? BwdMode::DX_PARTIALS : BwdMode::DX;
+    if (staged(cols)) return from_hip(launch_wide_bwd(d, vec && !force_scalar(), mode, a, stream));
     return from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec), mode, a,
                                stream));
 }
@@ -497,7 +536,7 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
                                 int64_t cols, ln_dtype_t dt, hipStream_t stream) {
     if (!dgamma || !dbeta || !workspace) return LN_ERR_NULL;
     if (!partials_ready && (!dy || !x || !mean || !rstd)) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::BWD);
     if (st != LN_OK) return st;
     const size_t need = ln_bwd_workspace_bytes(rows, cols);
     if (workspace_bytes < need) return LN_ERR_WORKSPACE;
@@ -523,8 +562,11 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
         a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
         a.parts = parts;
         a.inv_m = (float)(1.0 / (double)cols);
-        st = from_hip(
-            launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::PARTIALS, a, stream));
+        st = staged(cols)
+                 ? from_hip(launch_wide_bwd(d, vec && !force_scalar(), BwdMode::PARTIALS, a,
+                                            stream))
+                 : from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::PARTIALS, a,
+                                       stream));
         if (st != LN_OK) return st;
     }
     FoldOut out{};
@@ -537,7 +579,7 @@ ln_status_t ln_bwd_noalloc(const void* dy, const void* x, const void* gamma, con
                            const float* rstd, void* dx, float* dgamma, float* dbeta,
                            int64_t rows, int64_t cols, ln_dtype_t dt, hipStream_t stream) {
     if (!dy || !x || !gamma || !mean || !rstd || !dx || !dgamma || !dbeta) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::BWD);
     if (st != LN_OK) return st;
     if (rows == 0) return LN_OK;
     const size_t need = ln_bwd_workspace_bytes(rows, cols);
@@ -563,7 +605,11 @@ ln_status_t ln_bwd_noalloc(const void* dy, const void* x, const void* gamma, con
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.parts = bwd_partitions(rows, cols);
     a.inv_m = (float)(1.0 / (double)cols);
-    st = from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::DX_PARTIALS, a, stream));
+    st = staged(cols)
+             ? from_hip(launch_wide_bwd(d, vec && !force_scalar(), BwdMode::DX_PARTIALS, a,
+                                        stream))
+             : from_hip(launch_bwd(d, pick_bwd_path(d, cols, vec), BwdMode::DX_PARTIALS, a,
+                                   stream));
     if (st != LN_OK) return st;
     FoldOut out{};
     out.p[0] = dgamma;
@@ -582,7 +628,7 @@ static ln_status_t prologue_bwd(const void* dy, const void* dz_extra, const void
     if (!dy || !z || !gamma || !mean || !rstd || !dresidual || !dx || !workspace)
         return LN_ERR_NULL;
     if (fold && (!dgamma || !dbeta || !dbias)) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::FWD);
     if (st != LN_OK) return st;
     if (cols > LN_MAX_COLS_DROPOUT_BWD) return LN_ERR_UNSUPPORTED;
     if (!(p >= 0.0f && p < 1.0f)) return LN_ERR_PARAM;
@@ -672,7 +718,7 @@ ln_status_t add_rmsnorm_fwd(const void* x, const void* residual, const void* gam
                             float eps, ln_dtype_t dt, hipStream_t stream) {
     if (!x || !gamma || !y || (residual && !residual_out)) return LN_ERR_NULL;
     if (!residual && residual_out) return LN_ERR_PARAM;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::RMS);
     if (st != LN_OK) return st;
     if (!(eps >= 0.0f) || std::isinf(eps)) return LN_ERR_PARAM;
     if (rows == 0) return LN_OK;
@@ -704,7 +750,7 @@ ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
                             float* workspace, size_t workspace_bytes, int64_t rows, int64_t cols,
                             ln_dtype_t dt, hipStream_t stream) {
     if (!dy || !z || !gamma || !rstd || !dz || !dgamma || !workspace) return LN_ERR_NULL;
-    ln_status_t st = check_shape(rows, cols, dt);
+    ln_status_t st = check_shape(rows, cols, dt, Kind::RMS);
     if (st != LN_OK) return st;
     const size_t need = add_rmsnorm_bwd_workspace_bytes(rows, cols);
     if (workspace_bytes < need) return LN_ERR_WORKSPACE;
@@ -842,6 +888,11 @@ ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t ro
     if (cols > softmax_max_cols(dt, true) || force_two_pass())
         return from_hip(launch_softmax_stream(d, vec && !force_scalar(), true, a, stream));
     return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec, true), true, a, stream));
+}
+
+ln_status_t ln_debug_force_staged(int on) {
+    g_force_staged.store(on ? 1 : 0, std::memory_order_relaxed);
+    return LN_OK;
 }
 
 ln_status_t ln_debug_force_two_pass(int on) {

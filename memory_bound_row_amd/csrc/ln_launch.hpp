@@ -208,6 +208,13 @@ struct XeArgs {
 Path pick_xent_path(Dt dt, int64_t slots, bool vec);
 hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s);
 
+// LayerNorm rows wider than the register layouts (ln_wide.hip): one 1024-lane
+// workgroup per row, the row staged in LDS.  The backward takes modes DX,
+// DX_PARTIALS and PARTIALS.
+constexpr int64_t kRegisterMaxCols = 16384;   // widest LayerNorm row of the register kernels
+hipError_t launch_wide_fwd(Dt dt, bool vec, bool fused, const FwdArgs& a, hipStream_t s);
+hipError_t launch_wide_bwd(Dt dt, bool vec, BwdMode mode, const BwdArgs& a, hipStream_t s);
+
 // Rows too long for the register layouts: one workgroup per row, two passes
 // over the row (stream.hip).
 hipError_t launch_softmax_stream(Dt dt, bool vec, bool backward, const SmArgs& a, hipStream_t s);

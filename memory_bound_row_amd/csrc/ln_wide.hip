@@ -1,0 +1,419 @@
+// ln_wide.hip -- LayerNorm forward (plain and fused with bias + dropout +
+// residual) and backward for rows wider than the register layouts hold
+// (more than 16384 columns), for gfx950.  Compiled once per storage type
+// (-DMBROW_DT=0 fp32, 1 fp16, 2 bf16).
+//
+// One 1024-lane workgroup owns a row at a time.  The row is staged in LDS as
+// it is read ("02 · llmc/ 的 CUDA kernel 层" §3.1: a row past the register
+// budget goes to shared memory, so global memory is read once), and the
+// statistics, the normalisation and, in the backward, the dx pass read it
+// back from there.  160 KB of LDS hold 9984 16-byte slots: 39936 fp32 or
+// 79872 16-bit columns of one tensor, half that per tensor for the backward's
+// two (dy and x).  Slots past that capacity are read again from global memory
+// in each later pass (the fused forward recomputes z for them from x, the
+// residual, the bias and the mask, bit for bit as first stored).
+//
+// Lane t owns the 16-byte slots t, t + 1024, t + 2048, ... of the row, so
+// each wave-wide access covers 1 KB of consecutive bytes.  Reductions: a
+// butterfly within each wave, then the 16 wave sums added through LDS in wave
+// order, the same bits in every lane.  Arithmetic follows the register
+// kernels: statistics of values shifted by the row's first value, two exact
+// passes (mean, then squared deviations), y = ((v - c - mean) * rstd) * gamma
+// + beta; dx = rstd * (gamma*dy - (A + xhat * B) / m) from the two row sums
+// reduced together ("Accelerating Transformer on GPU (II)" §2.1-§2.2).
+//
+// The backward's workgroup is a row partition (rows p, p + P, ...), as in the
+// register kernel: each lane accumulates dgamma and dbeta for the columns of
+// its slots over the partition's rows, and, every column being owned by one
+// lane, writes its partial directly ("(II)" §2.4, stage 1 of two).
+#include "ln_device.hpp"
+#include "ln_launch.hpp"
+
+#ifndef MBROW_DT
+#error "compile with -DMBROW_DT=0|1|2"
+#endif
+
+namespace mbrow {
+
+#if MBROW_DT == 0
+using St = StF32;
+#define MBROW_SUFFIX f32
+#elif MBROW_DT == 1
+using St = StF16;
+#define MBROW_SUFFIX f16
+#else
+using St = StBF16;
+#define MBROW_SUFFIX bf16
+#endif
+
+constexpr int kWideT = 1024;                 // lanes per workgroup (and per row)
+constexpr int kWideW = kWideT / 64;          // waves
+constexpr int kWideLds = 156 * 1024;         // LDS bytes for staged slots
+constexpr int kWideGroup = 4;                // slots whose loads are issued together
+
+// Slot s of a row of a [rows, m] tensor, packed in T: one 16-byte load on the
+// vector path, else per element (columns past m read 0).
+template <class S, bool VEC>
+__device__ __forceinline__ u32x4 wide_load(const void* base, int64_t row, int m, int s) {
+    if constexpr (VEC) {
+        const char* p = static_cast<const char*>(base) +
+                        (row * (int64_t)m + (int64_t)s * S::E) * S::BYTES;
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    } else {
+        float f[S::E];
+        load_elems<S>(base, row, m, s * S::E, true, f);
+        return S::pack(f);   // exact: the values are representable in T
+    }
+}
+
+template <class S, bool VEC>
+__device__ __forceinline__ void wide_store(void* base, int64_t row, int m, int s,
+                                           const float* f) {
+    if constexpr (VEC) {
+        char* p = static_cast<char*>(base) + (row * (int64_t)m + (int64_t)s * S::E) * S::BYTES;
+        __builtin_nontemporal_store(S::pack(f), reinterpret_cast<u32x4*>(p));
+    } else {
+        store_elems<S>(base, row, m, s * S::E, true, f);
+    }
+}
+
+// Sum of one value per lane over the workgroup, identical in every lane:
+// wave butterflies, then the wave sums in wave order.  `red` is [kWideW]
+// floats of LDS that no other reduction in flight uses.
+__device__ __forceinline__ float wide_sum(float v, float* red, int tid) {
+    v = group_sum<64>(v);
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    float t = red[0];
+#pragma unroll
+    for (int w = 1; w < kWideW; ++w) t = t + red[w];
+    return t;
+}
+
+// Columns of slot s inside the row (E for every slot but a partial last one).
+template <int E>
+__device__ __forceinline__ int wide_cols(int s, int m) {
+    const int left = m - s * E;
+    return left < E ? left : E;
+}
+
+// ---------------------------------------------------------------------------
+// Forward.
+// ---------------------------------------------------------------------------
+template <class S, bool VEC, bool FUSED>
+__global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
+    constexpr int E = S::E;
+    constexpr int LCAP = kWideLds / 16;
+    __shared__ u32x4 stage[LCAP];
+    __shared__ float red[2][kWideW];
+    const int tid = threadIdx.x;
+    const int m = (int)a.m;
+    const int nslots = (int)a.nslots;
+    const int J = (nslots + kWideT - 1) / kWideT;   // slots per lane (at most)
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        __syncthreads();   // the previous row's reads of the stage are done
+
+        // The values of slot s being normalised, packed in T: x, or z as
+        // stored (formed here from x, the residual, the bias and the mask).
+        // `store` writes z out (the first time only).
+        auto fetch = [&](int j0, u32x4 (&v)[kWideGroup], bool first) {
+            u32x4 xv[kWideGroup], rv[FUSED ? kWideGroup : 1];
+#pragma unroll
+            for (int u = 0; u < kWideGroup; ++u) {
+                const int s = tid + (j0 + u) * kWideT;
+                const bool need = j0 + u < J && s < nslots && (first || s >= LCAP);
+                if (need) {
+                    xv[u] = wide_load<S, VEC>(a.x, row, m, s);
+                    if constexpr (FUSED) rv[u] = wide_load<S, VEC>(a.residual, row, m, s);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kWideGroup; ++u) {
+                const int s = tid + (j0 + u) * kWideT;
+                if (!(j0 + u < J && s < nslots)) continue;
+                if (!first && s < LCAP) {
+                    v[u] = stage[s];
+                    continue;
+                }
+                if constexpr (FUSED) {
+                    float xf[E], rf[E], bf[E], z[E];
+                    S::unpack(xv[u], xf);
+                    S::unpack(rv[u], rf);
+                    S::unpack(load_param<S, VEC>(a.bias, s, m, true), bf);
+                    const u32x4 w =
+                        dropout_words(row, s * E, a.seed_lo, a.seed_hi, a.thr);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float t = kept<E>(w, s * E, e, a.thr) ? xf[e] + bf[e] : 0.0f;
+                        z[e] = fmaf(t, a.scale, rf[e]);
+                    }
+                    v[u] = S::pack(z);
+                    if (first) {
+                        float zs[E];
+                        S::unpack(v[u], zs);
+                        wide_store<S, VEC>(a.residual_out, row, m, s, zs);
+                    }
+                } else {
+                    v[u] = xv[u];
+                }
+            }
+        };
+
+        // pass 1: read (and form z), stage
+        for (int j0 = 0; j0 < J; j0 += kWideGroup) {
+            u32x4 v[kWideGroup];
+            fetch(j0, v, true);
+#pragma unroll
+            for (int u = 0; u < kWideGroup; ++u) {
+                const int s = tid + (j0 + u) * kWideT;
+                if (j0 + u < J && s < nslots && s < LCAP) stage[s] = v[u];
+            }
+        }
+        __syncthreads();
+        // shift: the row's first value (fp32 rows whose mean dwarfs their
+        // spread keep their precision; harmless for 16-bit rows)
+        const float c = S::template elem<0>(stage[0]);
+
+        // passes 2-4 over the lane's slots: f(s, values, columns)
+        auto over = [&](auto&& f) {
+            for (int j0 = 0; j0 < J; j0 += kWideGroup) {
+                u32x4 v[kWideGroup];
+                fetch(j0, v, false);
+#pragma unroll
+                for (int u = 0; u < kWideGroup; ++u) {
+                    const int s = tid + (j0 + u) * kWideT;
+                    if (!(j0 + u < J && s < nslots)) continue;
+                    float fv[E];
+                    S::unpack(v[u], fv);
+                    f(s, fv, wide_cols<E>(s, m));
+                }
+            }
+        };
+        float sl = 0.0f;
+        over([&](int, const float* fv, int n) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) sl += e < n ? fv[e] - c : 0.0f;
+        });
+        const float mu = wide_sum(sl, red[0], tid) * a.inv_m;   // mean of v - c
+        float ql = 0.0f;
+        over([&](int, const float* fv, int n) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float d = (fv[e] - c) - mu;
+                ql = e < n ? fmaf(d, d, ql) : ql;
+            }
+        });
+        const float var = wide_sum(ql, red[1], tid) * a.inv_m;
+        const float rs = 1.0f / sqrtf(var + a.eps);
+        if (tid == 0) {
+            if (a.mean) a.mean[row] = c + mu;
+            if (a.rstd) a.rstd[row] = rs;
+        }
+        over([&](int s, const float* fv, int) {
+            float ga[E], be[E], out[E];
+            S::unpack(load_param<S, VEC>(a.gamma, s, m, true), ga);
+            S::unpack(load_param<S, VEC>(a.beta, s, m, true), be);
+#pragma unroll
+            for (int e = 0; e < E; ++e) out[e] = fmaf(((fv[e] - c) - mu) * rs, ga[e], be[e]);
+            wide_store<S, VEC>(a.y, row, m, s, out);
+        });
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward.
+// ---------------------------------------------------------------------------
+// The backward holds both dy and x in LDS (no second read from global
+// memory), so its rows stop at what the stage holds: 4992 slots of each,
+// 19968 fp32 or 39936 16-bit columns (the library caps 16-bit rows at 32768).
+// Slots per lane:
+template <class S>
+struct WideBwd {
+    static constexpr int LCAP = kWideLds / 32;
+    static constexpr int J = S::E == 4 ? (LCAP + kWideT - 1) / kWideT : 32768 / 8 / kWideT;
+};
+
+template <class S, bool VEC, int MODE>
+__global__ __launch_bounds__(kWideT) void ln_wide_bwd_kernel(BwdArgs a) {
+    constexpr int E = S::E;
+    constexpr int JM = WideBwd<S>::J;
+    constexpr bool DX = MODE != (int)BwdMode::PARTIALS;
+    constexpr bool PART = MODE != (int)BwdMode::DX;
+    constexpr int LCAP = WideBwd<S>::LCAP;       // slots of each of dy and x
+    __shared__ u32x4 sdy[LCAP], sx[LCAP];
+    __shared__ float red[2][2][kWideW];
+    const int tid = threadIdx.x;
+    const int m = (int)a.m;
+    const int nslots = (int)a.nslots;
+    const int64_t part = blockIdx.x;
+
+    constexpr int KA = PART ? JM * E : 1;
+    float acc[2][KA];
+#pragma unroll
+    for (int k = 0; k < KA; ++k) {
+        acc[0][k] = 0.0f;
+        acc[1][k] = 0.0f;
+    }
+    int it = 0;
+    for (int64_t row = part; row < a.rows; row += a.parts, ++it) {
+        __syncthreads();   // the previous row's reads of the stage are done
+        const float mu = a.mean[row];
+        const float rs = a.rstd[row];
+        // pass 1: dy and x read (the loads of a group of slots issued
+        // together) and staged; A = sum g, Bm = sum g (x - mean)
+        // (groups of two slots: with the accumulators live, four would not
+        // fit a lane's 128 registers)
+        constexpr int GB = 2;
+        float A = 0.0f, Bm = 0.0f;
+#pragma unroll
+        for (int j0 = 0; j0 < JM; j0 += GB) {
+            u32x4 d[GB], x[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+                const int s = tid + (j0 + u) * kWideT;
+                if (j0 + u < JM && s < nslots) {
+                    d[u] = wide_load<S, VEC>(a.dy, row, m, s);
+                    x[u] = wide_load<S, VEC>(a.x, row, m, s);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+                const int s = tid + (j0 + u) * kWideT;
+                if (!(j0 + u < JM && s < nslots)) continue;
+                sdy[s] = d[u];
+                sx[s] = x[u];
+                if constexpr (DX) {
+                    float ga[E], df[E], xf[E];
+                    S::unpack(load_param<S, VEC>(a.gamma, s, m, true), ga);
+                    S::unpack(d[u], df);
+                    S::unpack(x[u], xf);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float g = ga[e] * df[e];   // zero outside the row
+                        A += g;
+                        Bm = fmaf(g, xf[e] - mu, Bm);
+                    }
+                }
+            }
+        }
+        float c1 = 0.0f, c2 = 0.0f;
+        if constexpr (DX) {
+            A = group_sum<64>(A);
+            Bm = group_sum<64>(Bm);
+            float(*r)[kWideW] = red[it & 1];
+            if ((tid & 63) == 0) {
+                r[0][tid >> 6] = A;
+                r[1][tid >> 6] = Bm;
+            }
+        }
+        __syncthreads();   // the stage (and the row sums) are complete
+        if constexpr (DX) {
+            const float(*r)[kWideW] = red[it & 1];
+            A = r[0][0];
+            Bm = r[1][0];
+#pragma unroll
+            for (int w = 1; w < kWideW; ++w) {
+                A = A + r[0][w];
+                Bm = Bm + r[1][w];
+            }
+            c1 = A * a.inv_m;
+            c2 = (Bm * rs) * a.inv_m;
+        }
+        // pass 2, from the stage: dx and the column partials
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            {
+                const int s = tid + j * kWideT;
+                if (s >= nslots) continue;
+                float df[E], xf[E], xh[E];
+                S::unpack(sdy[s], df);
+                S::unpack(sx[s], xf);
+#pragma unroll
+                for (int e = 0; e < E; ++e) xh[e] = (xf[e] - mu) * rs;
+                if constexpr (DX) {
+                    float ga[E], out[E];
+                    S::unpack(load_param<S, VEC>(a.gamma, s, m, true), ga);
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        out[e] = rs * (ga[e] * df[e] - fmaf(xh[e], c2, c1));
+                    wide_store<S, VEC>(a.dx, row, m, s, out);
+                }
+                if constexpr (PART) {
+                    // zero past the row (df is 0 there), so no test per element
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        acc[0][j * E + e] = fmaf(df[e], xh[e], acc[0][j * E + e]);
+                        acc[1][j * E + e] = acc[1][j * E + e] + df[e];
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (PART) {
+        // every column is owned by one lane: the partition's partial directly
+        float* const pw = a.ws + part * 2 * a.m;
+        const bool wvec = VEC && a.ws_vec;
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int s = tid + j * kWideT;
+            if (s >= nslots) continue;
+#pragma unroll
+            for (int kind = 0; kind < 2; ++kind) {
+                float* dst = pw + kind * a.m + s * E;
+                if (wvec) {
+#pragma unroll
+                    for (int e = 0; e < E; e += 4) {
+                        f32x4 v = {acc[kind][j * E + e], acc[kind][j * E + e + 1],
+                                   acc[kind][j * E + e + 2], acc[kind][j * E + e + 3]};
+                        *reinterpret_cast<f32x4*>(dst + e) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (s * E + e < m) dst[e] = acc[kind][j * E + e];
+                }
+            }
+        }
+    }
+}
+
+template <bool VEC, bool FUSED>
+static hipError_t launch_fwd_one(const FwdArgs& a, hipStream_t s) {
+    auto kern = ln_wide_fwd_kernel<St, VEC, FUSED>;
+    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), kWideT, a.rows);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWideT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <bool VEC, int MODE>
+static hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((ln_wide_bwd_kernel<St, VEC, MODE>), dim3((unsigned)a.parts),
+                       dim3(kWideT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <bool VEC>
+static hipError_t bwd_mode(BwdMode mode, const BwdArgs& a, hipStream_t s) {
+    switch (mode) {
+    case BwdMode::DX: return launch_bwd_one<VEC, 0>(a, s);
+    case BwdMode::DX_PARTIALS: return launch_bwd_one<VEC, 1>(a, s);
+    case BwdMode::PARTIALS: return launch_bwd_one<VEC, 2>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+#define MBROW_CAT2(a, b) a##b
+#define MBROW_CAT(a, b) MBROW_CAT2(a, b)
+hipError_t MBROW_CAT(launch_wide_fwd_, MBROW_SUFFIX)(bool vec, bool fused, const FwdArgs& a,
+                                                      hipStream_t s) {
+    if (vec) return fused ? launch_fwd_one<true, true>(a, s) : launch_fwd_one<true, false>(a, s);
+    return fused ? launch_fwd_one<false, true>(a, s) : launch_fwd_one<false, false>(a, s);
+}
+
+hipError_t MBROW_CAT(launch_wide_bwd_, MBROW_SUFFIX)(bool vec, BwdMode mode, const BwdArgs& a,
+                                                      hipStream_t s) {
+    return vec ? bwd_mode<true>(mode, a, s) : bwd_mode<false>(mode, a, s);
+}
+
+}  // namespace mbrow

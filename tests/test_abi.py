@@ -81,9 +81,10 @@ def test_ln_fwd_validation(L):
     assert fwd(L, eps=-1e-6) == LN_ERR_PARAM
     assert fwd(L, eps=float("nan")) == LN_ERR_PARAM
     assert fwd(L, eps=float("inf")) == LN_ERR_PARAM
-    assert fwd(L, cols=16385, dt=F32) == LN_ERR_UNSUPPORTED
-    assert fwd(L, cols=16385, dt=BF16) == LN_ERR_UNSUPPORTED
-    assert fwd(L, cols=16384, dt=F16, rows=0) == LN_OK
+    assert fwd(L, cols=65537, dt=F32) == LN_ERR_UNSUPPORTED     # LN_MAX_COLS
+    assert fwd(L, cols=65537, dt=BF16) == LN_ERR_UNSUPPORTED
+    assert fwd(L, cols=65536, dt=F16, rows=0) == LN_OK
+    assert fwd(L, cols=16385, dt=F32, rows=0) == LN_OK           # the LDS-staged path
     assert fwd(L, rows=2 ** 31) == LN_ERR_UNSUPPORTED
     assert fwd(L, rows=0) == LN_OK            # no-op, nothing enqueued
     # y may be x exactly, but not a partial overlap of it
@@ -134,6 +135,12 @@ def test_bwd_dx_validation(L):
     assert bwd_dx(L, rows=0, dx=A) == LN_OK                     # dx == dy in place
     assert bwd_dx(L, dx=A + 4) == LN_ERR_UNSUPPORTED
     assert bwd_dx(L, ws=A, wsb=need) == LN_ERR_UNSUPPORTED      # workspace over dy
+    # widest rows: LN_MAX_COLS_BWD_F32 / LN_MAX_COLS_BWD_16 (staged in LDS)
+    assert bwd_dx(L, cols=19969, dt=F32) == LN_ERR_UNSUPPORTED
+    assert bwd_dx(L, cols=32769, dt=BF16) == LN_ERR_UNSUPPORTED
+    assert bwd_dx(L, cols=32769, dt=F16) == LN_ERR_UNSUPPORTED
+    assert bwd_dx(L, cols=19968, dt=F32, rows=0) == LN_OK
+    assert bwd_dx(L, cols=32768, dt=BF16, rows=0) == LN_OK
 
 
 def dgdb(L, dy=A, x=B, mean=C, rstd=D, dg=E, db=F, ws=G, wsb=None, ready=0, rows=4, cols=8,
