@@ -9,10 +9,13 @@
 // cross-entropy), or the dot product sum g * y of the softmax backward
 // ("Accelerating Transformer on GPU (II)" §3).  The lanes' states are merged
 // in a fixed order (one butterfly per wave, then the waves in order through
-// LDS).  Pass B re-reads the row and writes the output exactly as the
-// register kernels do (the same mask words, exp2 form and dropout).  Cost:
-// the row is read twice (the backward reads dy and y twice), against once for
-// rows that fit in registers.
+// LDS).  Pass B writes the output exactly as the register kernels do (the
+// same mask words, exp2 form and dropout).  Pass A keeps the row's first two
+// chunks (128 KB) in LDS, each lane its own slots, so pass B reads them back
+// from there and re-reads only the rest of the row from global memory
+// ("02 · llmc/ 的 CUDA kernel 层" §3.1: what fits on chip is read once).  The
+// rest is read twice (the backward reads dy and y), against once for rows
+// that fit in registers.
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 #include "online_softmax.hpp"
@@ -40,6 +43,9 @@ constexpr int kSnw = kSnt / 64;       // waves per row
 // two are (the next chunk is in flight as well, in 128 registers per lane)
 constexpr int kSu1 = 4;
 constexpr int kSu2 = 2;
+// Chunks of a row kept in LDS between the passes (64 KB each: four slots of
+// one tensor or two slots of two, per lane).
+constexpr int kStaged = 2;
 
 // Merge of the row's lane states: a butterfly per wave, then the waves in
 // order through LDS.  Every lane gets the row's state.
@@ -144,6 +150,43 @@ __device__ inline void pipelined(int64_t n, Fetch&& fetch, Use&& use) {
     }
 }
 
+// Pass B's walk.  Chunks [0, nst) are read back from the LDS stage by
+// `stage`, the rest fetched from global memory.  With prefetch, the walk takes
+// the last chunk first, since the chunks pass A read last are the ones most
+// likely still in L2, and the staged chunks at the end; a prefetch that would
+// fall on a staged chunk is sent to chunk n instead, which reads nothing.
+// (The per-element path walks in order: the reverse walk costs it a spill.)
+template <class B, bool PREFETCH, class Stage, class Fetch, class Use>
+__device__ inline void pipelined_staged(int64_t nst, int64_t n, Stage&& stage, Fetch&& fetch,
+                                        Use&& use) {
+    auto next = [&](int64_t c) { return c >= nst ? c : n; };
+    if constexpr (PREFETCH) {
+        B b0, b1;
+        fetch(next(n - 1), b0);
+        for (int64_t c = n - 1; c >= nst; c -= 2) {
+            fetch(next(c - 1), b1);
+            use(c, b0);
+            if (c - 1 < nst) break;
+            fetch(next(c - 2), b0);
+            use(c - 1, b1);
+        }
+        for (int64_t c = nst - 1; c >= 0; --c) {
+            stage(c, b1);
+            use(c, b1);
+        }
+    } else {
+        B b;
+        for (int64_t c = 0; c < nst; ++c) {
+            stage(c, b);
+            use(c, b);
+        }
+        for (int64_t c = nst; c < n; ++c) {
+            fetch(c, b);
+            use(c, b);
+        }
+    }
+}
+
 template <bool MASK>
 struct SmChunk {
     static constexpr int U = MASK ? kSu2 : kSu1;
@@ -169,6 +212,9 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
     constexpr int kSu = SmChunk<MASK>::U;
     constexpr int kSchunk = kSnt * kSu;
     __shared__ XeState lds[kSnw];
+    // pass A's first chunks, each lane its own slots (x, then the mask's)
+    __shared__ u32x4 stg[kStaged][MASK ? 2 * kSu : kSu][kSnt];
+    const int tid = threadIdx.x;
     const int m = (int)a.m;
     const int ns = (int)a.nslots;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
@@ -204,6 +250,13 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         XeState st{-INFINITY, 0.0f, 0.0f};
         pipelined<SmChunk<MASK>, VEC>(clive, fetch(std::false_type{}),
                                  [&](int64_t c, const SmChunk<MASK>& b) {
+            if (c < kStaged) {   // read back by this lane only: no barrier
+#pragma unroll
+                for (int k = 0; k < kSu; ++k) {
+                    stg[c][k][tid] = b.x[k];
+                    if constexpr (MASK) stg[c][kSu + k][tid] = b.m[k];
+                }
+            }
             float t[kSu][E];
             scores(c, b, t);
             float cm = -INFINITY;
@@ -227,8 +280,16 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         const rsrc_t vd = row_view<S>(a.out2 ? a.out2 : a.out, row, 1, m);
         // every chunk of the row is written; chunks past the query read
         // nothing and give y = 0
-        pipelined<SmChunk<MASK>, VEC>(call, fetch(std::true_type{}),
-                                 [&](int64_t c, const SmChunk<MASK>& b) {
+        auto staged = [&](int64_t c, SmChunk<MASK>& b) {
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                b.x[k] = stg[c][k][tid];
+                if constexpr (MASK) b.m[k] = stg[c][kSu + k][tid];
+            }
+        };
+        pipelined_staged<SmChunk<MASK>, VEC>(clive < kStaged ? clive : kStaged, call, staged,
+                                             fetch(std::true_type{}),
+                                             [&](int64_t c, const SmChunk<MASK>& b) {
             float t[kSu][E];
             scores(c, b, t);
 #pragma unroll
@@ -264,6 +325,8 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
     constexpr int kSu = DyChunk::U;
     constexpr int kSchunk = kSnt * kSu;
     __shared__ float lds[kSnw];
+    __shared__ u32x4 stg[kStaged][2 * kSu][kSnt];   // pass A's first chunks: dy, then y
+    const int tid = threadIdx.x;
     const int m = (int)a.m;
     const int ns = (int)a.nslots;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
@@ -298,6 +361,13 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         };
         float sum = 0.0f;
         pipelined<DyChunk, VEC>(clive, fetch(std::false_type{}), [&](int64_t c, const DyChunk& b) {
+            if (c < kStaged) {   // read back by this lane only: no barrier
+#pragma unroll
+                for (int k = 0; k < kSu; ++k) {
+                    stg[c][k][tid] = b.d[k];
+                    stg[c][kSu + k][tid] = b.y[k];
+                }
+            }
             float g[kSu][E], y[kSu][E];
             grads(c, b, g, y);
 #pragma unroll
@@ -307,7 +377,16 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         });
         sum = row_sum(sum, lds);
         const rsrc_t vdx = row_view<S>(a.out, row, 1, m);
-        pipelined<DyChunk, VEC>(call, fetch(std::true_type{}), [&](int64_t c, const DyChunk& b) {
+        auto staged = [&](int64_t c, DyChunk& b) {
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) {
+                b.d[k] = stg[c][k][tid];
+                b.y[k] = stg[c][kSu + k][tid];
+            }
+        };
+        pipelined_staged<DyChunk, VEC>(clive < kStaged ? clive : kStaged, call, staged,
+                                       fetch(std::true_type{}),
+                                       [&](int64_t c, const DyChunk& b) {
             float g[kSu][E], y[kSu][E];
             grads(c, b, g, y);
 #pragma unroll
@@ -331,6 +410,8 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
     constexpr int kSu = XChunk::U;
     constexpr int kSchunk = kSnt * kSu;
     __shared__ XeState lds[kSnw];
+    __shared__ u32x4 stg[kStaged][kSu][kSnt];   // pass A's first chunks
+    const int tid = threadIdx.x;
     const int cols = (int)a.cols;
     const int ld = (int)a.ld;
     const int nv = (int)a.nvalid;
@@ -352,6 +433,10 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         };
         XeState st{-INFINITY, 0.0f, 0.0f};
         pipelined<XChunk, VEC>(cv, fetch(std::false_type{}), [&](int64_t c, const XChunk& b) {
+            if (c < kStaged) {   // read back by this lane only: no barrier
+#pragma unroll
+                for (int k = 0; k < kSu; ++k) stg[c][k][tid] = b.x[k];
+            }
             float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
@@ -391,7 +476,12 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         const float nsl = -(a.scale * (pa + (1.0f - alpha)));
         const float fill = ignored ? 0.0f : NAN;
         const rsrc_t vd = row_view<S>(a.dx, row, 1, ld);
-        pipelined<XChunk, VEC>(call, fetch(std::true_type{}), [&](int64_t c, const XChunk& b) {
+        auto staged = [&](int64_t c, XChunk& b) {
+#pragma unroll
+            for (int k = 0; k < kSu; ++k) b.x[k] = stg[c][k][tid];
+        };
+        pipelined_staged<XChunk, VEC>(cv < kStaged ? cv : kStaged, call, staged,
+                                      fetch(std::true_type{}), [&](int64_t c, const XChunk& b) {
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
                 const int s = (int)(c * kSchunk) + k * kSnt + (int)threadIdx.x;

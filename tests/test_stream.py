@@ -75,6 +75,45 @@ def test_softmax_long_rows_per_element(orc, dtype):
         mb.debug_force_path(0)
 
 
+# Columns per chunk of a row (1024 lanes x 4 16-byte slots without a mask, x 2
+# with one); pass A keeps the first two chunks in LDS for pass B.
+CHUNK = {torch.float32: 16384, torch.float16: 32768, torch.bfloat16: 32768}
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("k,d", [(1, 0), (2, -1), (2, 0), (2, 1), (3, 0), (4, 1)])
+def test_staged_chunk_boundaries(orc, dtype, k, d):
+    # rows of k chunks (d columns more or fewer): all staged, the last slot of
+    # the stage, one slot past it
+    cols = k * CHUNK[dtype] + d
+    case(f"stream softmax + cross-entropy {dtype} 6x{cols} ({k} chunks {d:+d})")
+    softmax_run(orc, 6, cols, dtype, p=0.1, name=f"stream.sm.k{k}{d:+d}")
+    xent_run(orc, 6, cols, cols, dtype, name=f"stream.xent.k{k}{d:+d}")
+
+
+def test_causal_rows_across_the_stage(orc):
+    # causal fp32 rows with a mask (chunks of 8192 columns): row r reads its
+    # first r + 1 columns, so the rows below end in chunk 1, 2, 3 and 4, and
+    # each equals the softmax of its prefix, zeros after it
+    rows = cols = 24600
+    case(f"stream causal softmax fp32 {rows}x{cols} with a mask, sampled rows")
+    g = torch.Generator(device="cuda").manual_seed(21)
+    x = torch.randn((rows, cols), device="cuda", generator=g) * 3.0
+    mask = torch.randn((1, cols), device="cuda", generator=g)
+    dy = torch.randn((rows, cols), device="cuda", generator=g)
+    y, _ = mb.attn_softmax_fwd(x, 0.5, mask=mask, rows_per_mask=rows, causal=True)
+    dx = mb.attn_softmax_bwd(dy, y, 0.5, causal=True)
+    torch.cuda.synchronize()
+    for r in (0, 8191, 8192, 16383, 16384, 24575, 24576, rows - 1):
+        n = r + 1
+        fmt = FMT[torch.float32]
+        check_softmax_fwd(orc, x[r:r + 1, :n], y[r:r + 1, :n], None, fmt, scale=0.5,
+                          mask=mask[:, :n], name=f"stream.causal.r{r}")
+        check_softmax_bwd(orc, dy[r:r + 1, :n], y[r:r + 1, :n], dx[r:r + 1, :n], fmt,
+                          scale=0.5, name=f"stream.causal.r{r}.bwd")
+        assert torch.all(y[r, n:] == 0) and torch.all(dx[r, n:] == 0)
+
+
 def xent_run(orc, rows, cols, ld, dtype, seed=5, name="stream.xent"):
     x = synth.logits(rows, ld, dtype, seed=seed).to("cuda")
     lab = synth.class_labels(rows, cols, seed=seed, ignore_frac=0.1).to("cuda")
