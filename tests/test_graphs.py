@@ -170,3 +170,65 @@ def test_cross_entropy_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(loss, ref[0]), f"replay {k}: loss differs"
         assert torch.equal(bits(x), bits(ref[1])), f"replay {k}: gradient differs"
+
+
+def test_training_step_split_stages_in_a_graph():
+    # the benchmarked step: fused forward, prologue backward stage 1, fold
+    case("graph: fused forward, prologue backward stages, fold")
+    R, C = 1000, 1280
+    d = dev(synth.layer_inputs(R, C, torch.bfloat16, seed=4))
+    ez = dev(synth.layer_inputs(R, C, torch.bfloat16, seed=5, names=("dy",)))["dy"]
+    z, y = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+    mean = torch.empty(R, dtype=torch.float32, device="cuda")
+    rstd = torch.empty_like(mean)
+    dres, dxin = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+    ws = mb.dropout_workspace(R, C, "cuda")
+    pg = [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(3)]
+
+    def run():
+        mb.bias_dropout_residual_ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"], d["beta"],
+                                        0.1, 5, 1e-5, residual_out=z, y=y, mean=mean, rstd=rstd)
+        mb.bias_dropout_residual_ln_bwd_dx(d["dy"], z, d["gamma"], mean, rstd, 0.1, 5,
+                                           workspace=ws, dz_extra=ez, dresidual=dres, dx=dxin)
+        mb.bias_dropout_residual_ln_bwd_fold(ws, R, C, dgamma=pg[0], dbeta=pg[1], dbias=pg[2])
+
+    check_replays(run, [z, y, mean, rstd, dres, dxin] + pg)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_staged_rows_in_a_graph(dtype):
+    case(f"graph: LDS-staged forward, fused forward and backward {dtype}")
+    R, C = 40, 20000 if dtype == torch.bfloat16 else 19000
+    d = dev(synth.layer_inputs(R, C, dtype, seed=6))
+    y, z, y2 = (torch.empty_like(d["x"]) for _ in range(3))
+    mean = torch.empty(R, dtype=torch.float32, device="cuda")
+    rstd, mean2, rstd2 = (torch.empty_like(mean) for _ in range(3))
+    dx = torch.empty_like(d["x"])
+    ws = mb.workspace(R, C, "cuda")
+    dg = torch.empty(C, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dg)
+
+    def run():
+        mb.ln_fwd(d["x"], d["gamma"], d["beta"], 1e-5, y=y, mean=mean, rstd=rstd)
+        mb.bias_dropout_residual_ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"], d["beta"],
+                                        0.2, 8, 1e-5, residual_out=z, y=y2, mean=mean2,
+                                        rstd=rstd2)
+        mb.ln_bwd(d["dy"], d["x"], d["gamma"], mean, rstd, dx=dx, workspace_buf=ws, dgamma=dg,
+                  dbeta=db)
+
+    check_replays(run, [y, z, y2, mean, rstd, mean2, rstd2, dx, dg, db])
+
+
+def test_noalloc_backward_in_a_graph():
+    case("graph: ln_bwd_noalloc")
+    R, C = 1000, 1280
+    d = dev(synth.layer_inputs(R, C, torch.bfloat16, seed=7))
+    _, mean, rstd = mb.ln_fwd(d["x"], d["gamma"], d["beta"], 1e-5)
+    dx = torch.empty_like(d["x"])
+    dg = torch.empty(C, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dg)
+
+    def run():
+        mb.ln_bwd_noalloc(d["dy"], d["x"], d["gamma"], mean, rstd, dx=dx, dgamma=dg, dbeta=db)
+
+    check_replays(run, [dx, dg, db])
