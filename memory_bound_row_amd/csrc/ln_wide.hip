@@ -3,19 +3,22 @@
 // (more than 16384 columns), for gfx950.  Compiled once per storage type
 // (-DMBROW_DT=0 fp32, 1 fp16, 2 bf16).
 //
-// One 1024-lane workgroup owns a row at a time.  The row is staged in LDS as
-// it is read ("02 · llmc/ 的 CUDA kernel 层" §3.1: a row past the register
-// budget goes to shared memory, so global memory is read once), and the
-// statistics, the normalisation and, in the backward, the dx pass read it
-// back from there.  160 KB of LDS hold 9984 16-byte slots: 39936 fp32 or
-// 79872 16-bit columns of one tensor, half that per tensor for the backward's
-// two (dy and x).  Slots past that capacity are read again from global memory
-// in each later pass (the fused forward recomputes z for them from x, the
-// residual, the bias and the mask, bit for bit as first stored).
+// One workgroup owns a row at a time.  The row is staged in LDS as it is
+// read ("02 · llmc/ 的 CUDA kernel 层" §3.1: a row past the register budget
+// goes to shared memory, so global memory is read once), and the statistics,
+// the normalisation and, in the backward, the dx pass read it back from
+// there.  160 KB of LDS hold 9984 16-byte slots: 39936 fp32 or 79872 16-bit
+// columns of one tensor, half that per tensor for the backward's two (dy and
+// x).  Slots past that capacity are read again from global memory in each
+// later pass (the fused forward recomputes z for them from x, the residual,
+// the bias and the mask, bit for bit as first stored).  The forward's
+// workgroup has 1024 lanes and the whole LDS, or, for rows of at most 4992
+// slots, 512 lanes and half of it, so that two workgroups share a compute
+// unit and one reads its row while the other normalises and writes its own.
 //
-// Lane t owns the 16-byte slots t, t + 1024, t + 2048, ... of the row, so
+// Lane t of T owns the 16-byte slots t, t + T, t + 2T, ... of the row, so
 // each wave-wide access covers 1 KB of consecutive bytes.  Reductions: a
-// butterfly within each wave, then the 16 wave sums added through LDS in wave
+// butterfly within each wave, then the wave sums added through LDS in wave
 // order, the same bits in every lane.  Arithmetic follows the register
 // kernels: statistics of values shifted by the row's first value, two exact
 // passes (mean, then squared deviations), y = ((v - c - mean) * rstd) * gamma
@@ -26,6 +29,8 @@
 // register kernel: each lane accumulates dgamma and dbeta for the columns of
 // its slots over the partition's rows, and, every column being owned by one
 // lane, writes its partial directly ("(II)" §2.4, stage 1 of two).
+#include <type_traits>
+
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 
@@ -77,16 +82,17 @@ __device__ __forceinline__ void wide_store(void* base, int64_t row, int m, int s
     }
 }
 
-// Sum of one value per lane over the workgroup, identical in every lane:
-// wave butterflies, then the wave sums in wave order.  `red` is [kWideW]
+// Sum of one value per lane over a workgroup of W waves, identical in every
+// lane: wave butterflies, then the wave sums in wave order.  `red` is [W]
 // floats of LDS that no other reduction in flight uses.
+template <int W>
 __device__ __forceinline__ float wide_sum(float v, float* red, int tid) {
     v = group_sum<64>(v);
     if ((tid & 63) == 0) red[tid >> 6] = v;
     __syncthreads();
     float t = red[0];
 #pragma unroll
-    for (int w = 1; w < kWideW; ++w) t = t + red[w];
+    for (int w = 1; w < W; ++w) t = t + red[w];
     return t;
 }
 
@@ -100,16 +106,23 @@ __device__ __forceinline__ int wide_cols(int s, int m) {
 // ---------------------------------------------------------------------------
 // Forward.
 // ---------------------------------------------------------------------------
-template <class S, bool VEC, bool FUSED>
-__global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
+// T lanes per workgroup, LB bytes of LDS for the stage: 1024 lanes and the
+// whole LDS, or, for rows that fit half of it, 512 lanes and half, so that two
+// workgroups share a compute unit and one reads its row while the other
+// normalises and writes its own (four waves per SIMD either way: at most 128
+// registers per lane).
+template <class S, bool FUSED, int T, int LB>
+__global__ __launch_bounds__(T, 4) void ln_wide_fwd_kernel(FwdArgs a) {
+    constexpr bool VEC = false;   // the per-element path (rows of any width and alignment)
     constexpr int E = S::E;
-    constexpr int LCAP = kWideLds / 16;
+    constexpr int W = T / 64;
+    constexpr int LCAP = LB / 16;
     __shared__ u32x4 stage[LCAP];
-    __shared__ float red[2][kWideW];
+    __shared__ float red[2][W];
     const int tid = threadIdx.x;
     const int m = (int)a.m;
     const int nslots = (int)a.nslots;
-    const int J = (nslots + kWideT - 1) / kWideT;   // slots per lane (at most)
+    const int J = (nslots + T - 1) / T;   // slots per lane (at most)
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         __syncthreads();   // the previous row's reads of the stage are done
@@ -121,7 +134,7 @@ __global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
             u32x4 xv[kWideGroup], rv[FUSED ? kWideGroup : 1];
 #pragma unroll
             for (int u = 0; u < kWideGroup; ++u) {
-                const int s = tid + (j0 + u) * kWideT;
+                const int s = tid + (j0 + u) * T;
                 const bool need = j0 + u < J && s < nslots && (first || s >= LCAP);
                 if (need) {
                     xv[u] = wide_load<S, VEC>(a.x, row, m, s);
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < kWideGroup; ++u) {
-                const int s = tid + (j0 + u) * kWideT;
+                const int s = tid + (j0 + u) * T;
                 if (!(j0 + u < J && s < nslots)) continue;
                 if (!first && s < LCAP) {
                     v[u] = stage[s];
@@ -166,7 +179,7 @@ __global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
             fetch(j0, v, true);
 #pragma unroll
             for (int u = 0; u < kWideGroup; ++u) {
-                const int s = tid + (j0 + u) * kWideT;
+                const int s = tid + (j0 + u) * T;
                 if (j0 + u < J && s < nslots && s < LCAP) stage[s] = v[u];
             }
         }
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
                 fetch(j0, v, false);
 #pragma unroll
                 for (int u = 0; u < kWideGroup; ++u) {
-                    const int s = tid + (j0 + u) * kWideT;
+                    const int s = tid + (j0 + u) * T;
                     if (!(j0 + u < J && s < nslots)) continue;
                     float fv[E];
                     S::unpack(v[u], fv);
@@ -195,7 +208,7 @@ __global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int e = 0; e < E; ++e) sl += e < n ? fv[e] - c : 0.0f;
         });
-        const float mu = wide_sum(sl, red[0], tid) * a.inv_m;   // mean of v - c
+        const float mu = wide_sum<W>(sl, red[0], tid) * a.inv_m;   // mean of v - c
         float ql = 0.0f;
         over([&](int, const float* fv, int n) {
 #pragma unroll
@@ -204,7 +217,7 @@ __global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
                 ql = e < n ? fmaf(d, d, ql) : ql;
             }
         });
-        const float var = wide_sum(ql, red[1], tid) * a.inv_m;
+        const float var = wide_sum<W>(ql, red[1], tid) * a.inv_m;
         const float rs = 1.0f / sqrtf(var + a.eps);
         if (tid == 0) {
             if (a.mean) a.mean[row] = c + mu;
@@ -217,6 +230,169 @@ __global__ __launch_bounds__(kWideT) void ln_wide_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int e = 0; e < E; ++e) out[e] = fmaf(((fv[e] - c) - mu) * rs, ga[e], be[e]);
             wide_store<S, VEC>(a.y, row, m, s, out);
+        });
+    }
+}
+
+// The vector path (rows of whole 16-byte slots): the same passes with loads
+// and stores through buffer views of the row, where a slot past the row
+// reads 0 and its store is dropped, so no lane branches on its own slot.
+// Whether a slot is in the stage is the same for its whole wave (the stage
+// holds whole waves of slots), so that test is a uniform branch.  A lane's
+// slots are walked in groups of G, then one at a time for the last J mod G.
+// Every load of a group is issued before the group's first store (a store
+// may alias a later load, so loads are not moved above it).
+template <class S, bool FUSED, int T, int LB>
+__global__ __launch_bounds__(T, 4) void ln_wide_fwd_vec_kernel(FwdArgs a) {
+    constexpr int E = S::E;
+    constexpr int W = T / 64;
+    constexpr int G = kWideGroup;
+    constexpr int LCAP = LB / 16;
+    static_assert(LCAP % 64 == 0, "the stage holds whole waves of slots");
+    __shared__ u32x4 stage[LCAP];
+    __shared__ float red[2][W];
+    const int tid = threadIdx.x;
+    const int wbase = tid & ~63;   // the wave's first lane
+    const int m = (int)a.m;
+    const int nslots = (int)a.nslots;
+    const int J = (nslots + T - 1) / T;   // slots per lane (at most)
+    const rsrc_t vg = row_view<S>(a.gamma, 0, 1, m);
+    const rsrc_t vbe = row_view<S>(a.beta, 0, 1, m);
+    const rsrc_t vbi = row_view<S>(FUSED ? a.bias : a.gamma, 0, 1, m);
+    auto off = [&](int s) { return s < nslots ? (uint32_t)s * 16u : kOob; };
+    auto staged = [&](int j) { return wbase + j * T < LCAP; };   // uniform
+    // body(j0, N) over the lane's slots j0 .. j0+N-1
+    auto groups = [&](auto&& body) {
+        int j0 = 0;
+        for (; j0 + G <= J; j0 += G) body(j0, std::integral_constant<int, G>{});
+        for (; j0 < J; ++j0) body(j0, std::integral_constant<int, 1>{});
+    };
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        __syncthreads();   // the previous row's reads of the stage are done
+        const rsrc_t vx = row_view<S>(a.x, row, 1, m);
+        const rsrc_t vr = row_view<S>(FUSED ? a.residual : a.x, row, 1, m);
+        const rsrc_t vz = row_view<S>(FUSED ? a.residual_out : a.y, row, 1, m);
+        const rsrc_t vy = row_view<S>(a.y, row, 1, m);
+
+        // The values of the lane's slots j0 .. j0+N-1 being normalised,
+        // packed in T: x, or z as stored (formed from x, the residual, the
+        // bias and the mask); `first` reads every slot and writes z out,
+        // later passes read the staged slots from LDS and the rest again.
+        auto values = [&](int j0, auto& v, bool first) {
+            constexpr int N = sizeof(v) / sizeof(v[0]);
+            u32x4 xv[N], rv[FUSED ? N : 1], bv[FUSED ? N : 1];
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                const int s = tid + (j0 + u) * T;
+                if (first || !staged(j0 + u)) {
+                    xv[u] = buf_load_nt(vx, off(s));
+                    if constexpr (FUSED) {
+                        rv[u] = buf_load_nt(vr, off(s));
+                        bv[u] = buf_load(vbi, off(s));
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                const int s = tid + (j0 + u) * T;
+                if (!first && staged(j0 + u)) {
+                    v[u] = stage[s];
+                    continue;
+                }
+                if constexpr (FUSED) {
+                    float xf[E], rf[E], bf[E], z[E];
+                    S::unpack(xv[u], xf);
+                    S::unpack(rv[u], rf);
+                    S::unpack(bv[u], bf);
+                    const u32x4 w = dropout_words(row, s * E, a.seed_lo, a.seed_hi, a.thr);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float t = kept<E>(w, s * E, e, a.thr) ? xf[e] + bf[e] : 0.0f;
+                        z[e] = fmaf(t, a.scale, rf[e]);
+                    }
+                    v[u] = S::pack(z);
+                    if (first) buf_store_nt(v[u], vz, off(s));
+                } else {
+                    v[u] = xv[u];
+                }
+            }
+        };
+
+        // pass 1: read (and form z), stage (slots past the row stage 0)
+        groups([&](int j0, auto n) {
+            constexpr int N = decltype(n)::value;
+            u32x4 v[N];
+            values(j0, v, true);
+#pragma unroll
+            for (int u = 0; u < N; ++u)
+                if (staged(j0 + u)) stage[tid + (j0 + u) * T] = v[u];
+        });
+        __syncthreads();
+        // shift: the row's first value (fp32 rows whose mean dwarfs their
+        // spread keep their precision; harmless for 16-bit rows)
+        const float c = S::template elem<0>(stage[0]);
+
+        // passes 2-3: f(values, in row) over the lane's slots
+        auto over = [&](auto&& f) {
+            groups([&](int j0, auto n) {
+                constexpr int N = decltype(n)::value;
+                u32x4 v[N];
+                values(j0, v, false);
+#pragma unroll
+                for (int u = 0; u < N; ++u) {
+                    float fv[E];
+                    S::unpack(v[u], fv);
+                    f(fv, tid + (j0 + u) * T < nslots);
+                }
+            });
+        };
+        float sl = 0.0f;
+        over([&](const float* fv, bool in) {
+            float t = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) t += fv[e] - c;
+            sl += in ? t : 0.0f;
+        });
+        const float mu = wide_sum<W>(sl, red[0], tid) * a.inv_m;   // mean of v - c
+        float ql = 0.0f;
+        over([&](const float* fv, bool in) {
+            float t = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float d = (fv[e] - c) - mu;
+                t = fmaf(d, d, t);
+            }
+            ql += in ? t : 0.0f;
+        });
+        const float var = wide_sum<W>(ql, red[1], tid) * a.inv_m;
+        const float rs = 1.0f / sqrtf(var + a.eps);
+        if (tid == 0) {
+            if (a.mean) a.mean[row] = c + mu;
+            if (a.rstd) a.rstd[row] = rs;
+        }
+        // pass 4: y, with gamma and beta loaded with the group
+        groups([&](int j0, auto n) {
+            constexpr int N = decltype(n)::value;
+            u32x4 gv[N], bv[N], v[N];
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                const int s = tid + (j0 + u) * T;
+                gv[u] = buf_load(vg, off(s));
+                bv[u] = buf_load(vbe, off(s));
+            }
+            values(j0, v, false);
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                const int s = tid + (j0 + u) * T;
+                float fv[E], ga[E], be[E], out[E];
+                S::unpack(v[u], fv);
+                S::unpack(gv[u], ga);
+                S::unpack(bv[u], be);
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[e] = fmaf(((fv[e] - c) - mu) * rs, ga[e], be[e]);
+                buf_store_nt(S::pack(out), vy, off(s));
+            }
         });
     }
 }
@@ -378,11 +554,23 @@ __global__ __launch_bounds__(kWideT) void ln_wide_bwd_kernel(BwdArgs a) {
     }
 }
 
+template <class K>
+static void launch_rows(K kern, int threads, const FwdArgs& a, hipStream_t s) {
+    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), threads, a.rows);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, s, a);
+}
+
 template <bool VEC, bool FUSED>
 static hipError_t launch_fwd_one(const FwdArgs& a, hipStream_t s) {
-    auto kern = ln_wide_fwd_kernel<St, VEC, FUSED>;
-    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), kWideT, a.rows);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWideT), 0, s, a);
+    constexpr int kHalf = kWideLds / 2;
+    const bool half = a.nslots <= kHalf / 16;
+    if constexpr (VEC) {
+        if (half) launch_rows(ln_wide_fwd_vec_kernel<St, FUSED, kWideT / 2, kHalf>, kWideT / 2, a, s);
+        else launch_rows(ln_wide_fwd_vec_kernel<St, FUSED, kWideT, kWideLds>, kWideT, a, s);
+    } else {
+        if (half) launch_rows(ln_wide_fwd_kernel<St, FUSED, kWideT / 2, kHalf>, kWideT / 2, a, s);
+        else launch_rows(ln_wide_fwd_kernel<St, FUSED, kWideT, kWideLds>, kWideT, a, s);
+    }
     return hipGetLastError();
 }
 
