@@ -456,7 +456,9 @@ def configs_report(cpp_launch: bool = True) -> None:
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
-        forward + backward (each pass moves more than the cache holds).
+        forward + backward (each pass moves more than the cache holds);
+      * rows past the register layouts, staged in LDS: 4096x32768 bf16 and
+        4096x19968 fp32 forward + backward, 2048x65536 forward in both.
     Rates of 16 MB or more come with the plain copy's rate at the same byte
     count; the prologue backward, the softmax with dropout, add + RMSNorm and
     the cross-entropy also with a CPU baseline (the float64 oracle on a
