@@ -10,11 +10,11 @@
 // there.  160 KB of LDS hold 9984 16-byte slots: 39936 fp32 or 79872 16-bit
 // columns of one tensor, half that per tensor for the backward's two (dy and
 // x).  Slots past that capacity are read again from global memory in each
-// later pass (the fused forward recomputes z for them from x, the residual,
-// the bias and the mask, bit for bit as first stored).  The forward's
-// workgroup has 1024 lanes and the whole LDS, or, for rows of at most 4992
-// slots, 512 lanes and half of it, so that two workgroups share a compute
-// unit and one reads its row while the other normalises and writes its own.
+// later pass (the fused forward reads back the z it wrote for them).  The
+// forward's workgroup has 1024 lanes and the whole LDS, or, for rows of at
+// most 4992 slots, 512 lanes and half of it, so that two workgroups share a
+// compute unit and one reads its row while the other normalises and writes
+// its own.
 //
 // Lane t of T owns the 16-byte slots t, t + T, t + 2T, ... of the row, so
 // each wave-wide access covers 1 KB of consecutive bytes.  Reductions: a
@@ -115,6 +115,7 @@ template <class S, bool FUSED, int T, int LB>
 __global__ __launch_bounds__(T, 4) void ln_wide_fwd_kernel(FwdArgs a) {
     constexpr bool VEC = false;   // the per-element path (rows of any width and alignment)
     constexpr int E = S::E;
+    constexpr int G = 2;          // slots per group (E loads each)
     constexpr int W = T / 64;
     constexpr int LCAP = LB / 16;
     __shared__ u32x4 stage[LCAP];
@@ -128,25 +129,35 @@ __global__ __launch_bounds__(T, 4) void ln_wide_fwd_kernel(FwdArgs a) {
         __syncthreads();   // the previous row's reads of the stage are done
 
         // The values of slot s being normalised, packed in T: x, or z as
-        // stored (formed here from x, the residual, the bias and the mask).
-        // `store` writes z out (the first time only).
-        auto fetch = [&](int j0, u32x4 (&v)[kWideGroup], bool first) {
-            u32x4 xv[kWideGroup], rv[FUSED ? kWideGroup : 1];
+        // stored.  The first pass forms z from x, the residual, the bias and
+        // the mask and writes it out; later passes read the staged slots from
+        // LDS and the rest back from global memory (z as written: with
+        // residual_out == residual the residual is gone by then).
+        auto fetch = [&](int j0, u32x4 (&v)[G], bool first) {
+            u32x4 xv[G], rv[FUSED ? G : 1];
 #pragma unroll
-            for (int u = 0; u < kWideGroup; ++u) {
+            for (int u = 0; u < G; ++u) {
                 const int s = tid + (j0 + u) * T;
                 const bool need = j0 + u < J && s < nslots && (first || s >= LCAP);
                 if (need) {
-                    xv[u] = wide_load<S, VEC>(a.x, row, m, s);
-                    if constexpr (FUSED) rv[u] = wide_load<S, VEC>(a.residual, row, m, s);
+                    if (FUSED && !first) {
+                        xv[u] = wide_load<S, VEC>(a.residual_out, row, m, s);
+                    } else {
+                        xv[u] = wide_load<S, VEC>(a.x, row, m, s);
+                        if constexpr (FUSED) rv[u] = wide_load<S, VEC>(a.residual, row, m, s);
+                    }
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kWideGroup; ++u) {
+            for (int u = 0; u < G; ++u) {
                 const int s = tid + (j0 + u) * T;
                 if (!(j0 + u < J && s < nslots)) continue;
                 if (!first && s < LCAP) {
                     v[u] = stage[s];
+                    continue;
+                }
+                if (FUSED && !first) {
+                    v[u] = xv[u];
                     continue;
                 }
                 if constexpr (FUSED) {
@@ -174,11 +185,11 @@ __global__ __launch_bounds__(T, 4) void ln_wide_fwd_kernel(FwdArgs a) {
         };
 
         // pass 1: read (and form z), stage
-        for (int j0 = 0; j0 < J; j0 += kWideGroup) {
-            u32x4 v[kWideGroup];
+        for (int j0 = 0; j0 < J; j0 += G) {
+            u32x4 v[G];
             fetch(j0, v, true);
 #pragma unroll
-            for (int u = 0; u < kWideGroup; ++u) {
+            for (int u = 0; u < G; ++u) {
                 const int s = tid + (j0 + u) * T;
                 if (j0 + u < J && s < nslots && s < LCAP) stage[s] = v[u];
             }
@@ -190,11 +201,11 @@ __global__ __launch_bounds__(T, 4) void ln_wide_fwd_kernel(FwdArgs a) {
 
         // passes 2-4 over the lane's slots: f(s, values, columns)
         auto over = [&](auto&& f) {
-            for (int j0 = 0; j0 < J; j0 += kWideGroup) {
-                u32x4 v[kWideGroup];
+            for (int j0 = 0; j0 < J; j0 += G) {
+                u32x4 v[G];
                 fetch(j0, v, false);
 #pragma unroll
-                for (int u = 0; u < kWideGroup; ++u) {
+                for (int u = 0; u < G; ++u) {
                     const int s = tid + (j0 + u) * T;
                     if (!(j0 + u < J && s < nslots)) continue;
                     float fv[E];
@@ -276,16 +287,20 @@ __global__ __launch_bounds__(T, 4) void ln_wide_fwd_vec_kernel(FwdArgs a) {
         const rsrc_t vy = row_view<S>(a.y, row, 1, m);
 
         // The values of the lane's slots j0 .. j0+N-1 being normalised,
-        // packed in T: x, or z as stored (formed from x, the residual, the
-        // bias and the mask); `first` reads every slot and writes z out,
-        // later passes read the staged slots from LDS and the rest again.
+        // packed in T: x, or z as stored.  `first` reads every slot, forms z
+        // from x, the residual, the bias and the mask and writes it out;
+        // later passes read the staged slots from LDS and the rest back from
+        // global memory (z as written: with residual_out == residual the
+        // residual is gone by then).
         auto values = [&](int j0, auto& v, bool first) {
             constexpr int N = sizeof(v) / sizeof(v[0]);
             u32x4 xv[N], rv[FUSED ? N : 1], bv[FUSED ? N : 1];
 #pragma unroll
             for (int u = 0; u < N; ++u) {
                 const int s = tid + (j0 + u) * T;
-                if (first || !staged(j0 + u)) {
+                if (FUSED && !first && !staged(j0 + u)) {
+                    xv[u] = buf_load_nt(vz, off(s));
+                } else if (first || !staged(j0 + u)) {
                     xv[u] = buf_load_nt(vx, off(s));
                     if constexpr (FUSED) {
                         rv[u] = buf_load_nt(vr, off(s));
@@ -298,6 +313,10 @@ __global__ __launch_bounds__(T, 4) void ln_wide_fwd_vec_kernel(FwdArgs a) {
                 const int s = tid + (j0 + u) * T;
                 if (!first && staged(j0 + u)) {
                     v[u] = stage[s];
+                    continue;
+                }
+                if (FUSED && !first) {
+                    v[u] = xv[u];
                     continue;
                 }
                 if constexpr (FUSED) {

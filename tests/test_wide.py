@@ -175,3 +175,23 @@ def test_widest_rows_large_batch_sampled(orc, dtype):
     dy64 = f64(inp["dy"])
     assert_reports(cmp.check_colsum("wide.dbeta", f64(db), dy64.sum(axis=0),
                                     np.abs(dy64).sum(axis=0), rows, FMT[dtype]))
+
+
+@pytest.mark.parametrize("cols", [40001, 65536])
+def test_fused_forward_wide_in_place(orc, cols):
+    # fp32 rows past the stage: the slots beyond it are read again in later
+    # passes, also when z overwrites the residual (residual_out == residual)
+    rows, dtype = 6, torch.float32
+    case(f"staged fused forward in place fp32 {rows}x{cols}")
+    inp = dev(synth.layer_inputs(rows, cols, dtype, seed=cols + 4))
+    z, y, mean, rstd, mask = mb.bias_dropout_residual_ln_fwd(
+        inp["x"], inp["bias"], inp["residual"], inp["gamma"], inp["beta"], 0.1, 17, EPS,
+        want_mask=True)
+    res = inp["residual"].clone()
+    z2, y2, mean2, rstd2, _ = mb.bias_dropout_residual_ln_fwd(
+        inp["x"], inp["bias"], res, inp["gamma"], inp["beta"], 0.1, 17, EPS, residual_out=res)
+    torch.cuda.synchronize()
+    assert z2.data_ptr() == res.data_ptr()
+    for a, b in ((z, z2), (y, y2), (mean, mean2), (rstd, rstd2)):
+        assert torch.equal(a, b)
+    check_fused(orc, inp, 0.1, 17, z, y, mean, rstd, mask, FMT[dtype])
