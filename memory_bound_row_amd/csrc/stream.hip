@@ -46,6 +46,13 @@ constexpr int kSu2 = 2;
 // Chunks of a row kept in LDS between the passes (64 KB each: four slots of
 // one tensor or two slots of two, per lane).
 constexpr int kStaged = 2;
+// Further chunks kept in registers, after the LDS-staged ones, by the 16-bit
+// vector-path kernels whose registers allow it (16 per lane per chunk): two
+// in the softmax backward, one in the cross-entropy.
+template <class S>
+constexpr int kRegStagedBwd = S::E == 8 ? 2 : 0;   // at most 2
+template <class S>
+constexpr int kRegStagedXent = S::E == 8 ? 1 : 0;  // at most 1
 
 // Merge of the row's lane states: a butterfly per wave, then the waves in
 // order through LDS.  Every lane gets the row's state.
@@ -326,6 +333,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
     constexpr int kSchunk = kSnt * kSu;
     __shared__ float lds[kSnw];
     __shared__ u32x4 stg[kStaged][2 * kSu][kSnt];   // pass A's first chunks: dy, then y
+    constexpr int R = VEC ? kRegStagedBwd<S> : 0;    // and the next R, in registers
     const int tid = threadIdx.x;
     const int m = (int)a.m;
     const int ns = (int)a.nslots;
@@ -360,6 +368,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
             }
         };
         float sum = 0.0f;
+        DyChunk k0, k1;   // the chunks after the staged ones (R of them used)
         pipelined<DyChunk, VEC>(clive, fetch(std::false_type{}), [&](int64_t c, const DyChunk& b) {
             if (c < kStaged) {   // read back by this lane only: no barrier
 #pragma unroll
@@ -368,6 +377,8 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
                     stg[c][kSu + k][tid] = b.y[k];
                 }
             }
+            if (R > 0 && c == kStaged) k0 = b;   // uniform
+            if (R > 1 && c == kStaged + 1) k1 = b;
             float g[kSu][E], y[kSu][E];
             grads(c, b, g, y);
 #pragma unroll
@@ -378,13 +389,17 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         sum = row_sum(sum, lds);
         const rsrc_t vdx = row_view<S>(a.out, row, 1, m);
         auto staged = [&](int64_t c, DyChunk& b) {
+            if (R == 0 || c < kStaged) {   // uniform
 #pragma unroll
-            for (int k = 0; k < kSu; ++k) {
-                b.d[k] = stg[c][k][tid];
-                b.y[k] = stg[c][kSu + k][tid];
+                for (int k = 0; k < kSu; ++k) {
+                    b.d[k] = stg[c][k][tid];
+                    b.y[k] = stg[c][kSu + k][tid];
+                }
             }
+            if (R > 0 && c == kStaged) b = k0;
+            if (R > 1 && c == kStaged + 1) b = k1;
         };
-        pipelined_staged<DyChunk, VEC>(clive < kStaged ? clive : kStaged, call, staged,
+        pipelined_staged<DyChunk, VEC>(clive < kStaged + R ? clive : kStaged + R, call, staged,
                                        fetch(std::true_type{}),
                                        [&](int64_t c, const DyChunk& b) {
             float g[kSu][E], y[kSu][E];
@@ -411,6 +426,7 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
     constexpr int kSchunk = kSnt * kSu;
     __shared__ XeState lds[kSnw];
     __shared__ u32x4 stg[kStaged][kSu][kSnt];   // pass A's first chunks
+    constexpr int R = VEC ? kRegStagedXent<S> : 0;   // and the next R, in registers
     const int tid = threadIdx.x;
     const int cols = (int)a.cols;
     const int ld = (int)a.ld;
@@ -432,11 +448,13 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
             };
         };
         XeState st{-INFINITY, 0.0f, 0.0f};
+        XChunk k0;   // the chunk after the staged ones (if R = 1)
         pipelined<XChunk, VEC>(cv, fetch(std::false_type{}), [&](int64_t c, const XChunk& b) {
             if (c < kStaged) {   // read back by this lane only: no barrier
 #pragma unroll
                 for (int k = 0; k < kSu; ++k) stg[c][k][tid] = b.x[k];
             }
+            if (R > 0 && c == kStaged) k0 = b;   // uniform
             float cm = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
@@ -477,10 +495,13 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         const float fill = ignored ? 0.0f : NAN;
         const rsrc_t vd = row_view<S>(a.dx, row, 1, ld);
         auto staged = [&](int64_t c, XChunk& b) {
+            if (R == 0 || c < kStaged) {   // uniform
 #pragma unroll
-            for (int k = 0; k < kSu; ++k) b.x[k] = stg[c][k][tid];
+                for (int k = 0; k < kSu; ++k) b.x[k] = stg[c][k][tid];
+            }
+            if (R > 0 && c == kStaged) b = k0;
         };
-        pipelined_staged<XChunk, VEC>(cv < kStaged ? cv : kStaged, call, staged,
+        pipelined_staged<XChunk, VEC>(cv < kStaged + R ? cv : kStaged + R, call, staged,
                                       fetch(std::true_type{}), [&](int64_t c, const XChunk& b) {
 #pragma unroll
             for (int k = 0; k < kSu; ++k) {
