@@ -101,3 +101,43 @@ def test_rmsnorm_and_xent_beyond_2g_elements(orc):
     loss, dx = mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0)
     torch.cuda.synchronize()
     check_xent(orc, x[i], lab[i], COLS, 0.1, 1.0, loss[i], dx[i], FMT[dt], name="big.xent")
+
+
+def test_staged_layernorm_beyond_2g_elements(orc):
+    # rows past the register layouts, staged in LDS: 2^31 + 32768 elements
+    rows, cols = (1 << 16) + 1, 32768
+    case(f"LDS-staged LayerNorm fwd + bwd {rows}x{cols} bf16")
+    dt = torch.bfloat16
+    x, dy = big(rows, cols, dt, 13), big(rows, cols, dt, 14)
+    p = {k: v.to("cuda") for k, v in synth.layer_inputs(1, cols, dt, seed=15,
+                                                         names=("gamma", "beta")).items()}
+    y, mean, rstd = mb.ln_fwd(x, p["gamma"], p["beta"], EPS)
+    dx, dg, db = mb.ln_bwd(dy, x, p["gamma"], mean, rstd)
+    torch.cuda.synchronize()
+    i = torch.as_tensor([0, 1, rows // 2, (1 << 16) - 1, 1 << 16], device="cuda")
+    check_fwd(orc, x[i], p["gamma"], p["beta"], y[i], mean[i], rstd[i], FMT[dt],
+              name="big.staged")
+    check_bwd(orc, dy[i], x[i], p["gamma"], mean[i], rstd[i], dx[i], None, None, FMT[dt],
+              name="big.staged_bwd")
+    assert torch.isfinite(dg).all() and torch.isfinite(db).all()
+
+
+def test_two_pass_beyond_2g_elements(orc):
+    # the widest rows (2^24 columns) on the two-pass path: 2^31 + 2^24 elements
+    rows, cols = 129, 1 << 24
+    case(f"two-pass softmax fwd + bwd, cross-entropy {rows}x{cols}")
+    dt = torch.float16
+    x, dy = big(rows, cols, dt, 16), big(rows, cols, dt, 17)
+    y, _ = mb.attn_softmax_fwd(x, 0.5)
+    dx = mb.attn_softmax_bwd(dy, y, 0.5)
+    torch.cuda.synchronize()
+    i = torch.as_tensor([0, 64, rows - 1], device="cuda")
+    check_softmax_fwd(orc, x[i], y[i], None, FMT[dt], scale=0.5, name="big.stream.sm")
+    check_softmax_bwd(orc, dy[i], y[i], dx[i], FMT[dt], scale=0.5, name="big.stream.sm_bwd")
+    del y, dy, dx
+    lab = torch.randint(0, cols, (rows,), device="cuda",
+                        generator=torch.Generator(device="cuda").manual_seed(18))
+    loss, dl = mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0)
+    torch.cuda.synchronize()
+    check_xent(orc, x[i], lab[i], cols, 0.1, 1.0, loss[i], dl[i], FMT[dt],
+               name="big.stream.xent")
