@@ -140,11 +140,11 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     // spare for that and unpack in each pass.
     constexpr bool ONCE = !(DROP && G > 64);
     // With a 16-bit block unpacked once, its packed registers are free during
-    // the two passes: the prologue backward loads the next block's dy, z and
-    // row statistics into them there, so each block's loads are in flight
-    // while the previous block's Philox rounds and sums run.  (The plain
-    // backward, with less arithmetic per block, measured no faster so.)
-    constexpr bool PF = DROP && VEC && ONCE && E == 8 && V <= 3;
+    // the two passes: the prologue and RMSNorm backwards load the next
+    // block's dy, z and row statistics into them there, so each block's loads
+    // are in flight while the previous block's arithmetic runs (the Philox
+    // rounds, the sums).  (The plain backward measured no faster so.)
+    constexpr bool PF = (DROP || RMS) && VEC && ONCE && E == 8 && V <= 4;
     u32x4 xp[PF ? V : 1], dp[PF ? V : 1];   // the prefetched block
     float mu_n = 0.0f, rs_n = 0.0f;
     auto issue = [&](int64_t b) {
