@@ -20,6 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmbrow_ln.so")
 LAUNCH_BENCH = os.path.join(HERE, "launch_bench")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -79,7 +80,9 @@ def build(jobs: int | None = None, verbose: bool = False, extra_flags=(), out_li
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda u: _compile(u, build_dir, tuple(extra_flags), csrc), UNITS))
     tmp = out_lib + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp,
+           "-L", os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx",
+           "-Wl,-rpath," + os.path.join(ROCM, "lib")]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))

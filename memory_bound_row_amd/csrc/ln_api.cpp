@@ -4,9 +4,12 @@
 #include "mbrow_ln.h"
 #include "mbrow_ln_debug.h"
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <limits>
 #include <mutex>
 #include <unordered_map>
@@ -387,6 +390,29 @@ ln_status_t check_shape_stream(int64_t rows, int64_t cols, ln_dtype_t dt) {
     return LN_OK;
 }
 
+// A roctx range around each entry point, for timelines from rocprofv3
+// --marker-trace: on when the environment has MBROW_ROCTX=1 (read once per
+// process), off otherwise, so that by default a call costs nothing extra.
+bool roctx_on() {
+    static const bool on = [] {
+        const char* v = std::getenv("MBROW_ROCTX");
+        return v != nullptr && v[0] == '1';
+    }();
+    return on;
+}
+
+struct Range {
+    const bool on;
+    explicit Range(const char* name) : on(roctx_on()) {
+        if (on) roctxRangePushA(name);
+    }
+    ~Range() {
+        if (on) roctxRangePop();
+    }
+    Range(const Range&) = delete;
+    Range& operator=(const Range&) = delete;
+};
+
 }  // namespace
 
 extern "C" {
@@ -428,6 +454,7 @@ size_t add_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t cols) {
 ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
                    float* rstd, int64_t rows, int64_t cols, float eps, ln_dtype_t dt,
                    hipStream_t stream) {
+    const Range range("ln_fwd");
     if (!x || !gamma || !beta || !y) return LN_ERR_NULL;
     ln_status_t st = check_shape(rows, cols, dt, Kind::FWD);
     if (st != LN_OK) return st;
@@ -459,6 +486,7 @@ ln_status_t bias_dropout_residual_ln_fwd(const void* x, const void* bias, const 
                                          void* y, float* mean, float* rstd, uint8_t* mask_out,
                                          int64_t rows, int64_t cols, float eps, float p,
                                          uint64_t seed, ln_dtype_t dt, hipStream_t stream) {
+    const Range range("bias_dropout_residual_ln_fwd");
     if (!x || !bias || !residual || !gamma || !beta || !residual_out || !y) return LN_ERR_NULL;
     ln_status_t st = check_shape(rows, cols, dt, Kind::FWD);
     if (st != LN_OK) return st;
@@ -499,6 +527,7 @@ ln_status_t bias_dropout_residual_ln_fwd(const void* x, const void* bias, const 
 ln_status_t ln_bwd_dx(const void* dy, const void* x, const void* gamma, const float* mean,
                       const float* rstd, void* dx, float* workspace, size_t workspace_bytes,
                       int64_t rows, int64_t cols, ln_dtype_t dt, hipStream_t stream) {
+    const Range range("ln_bwd_dx");
     if (!dy || !x || !gamma || !mean || !rstd || !dx) return LN_ERR_NULL;
     ln_status_t st = check_shape(rows, cols, dt, Kind::BWD);
     if (st != LN_OK) return st;
@@ -534,6 +563,7 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
                                 const float* rstd, float* dgamma, float* dbeta, float* workspace,
                                 size_t workspace_bytes, int partials_ready, int64_t rows,
                                 int64_t cols, ln_dtype_t dt, hipStream_t stream) {
+    const Range range("ln_bwd_dgamma_dbeta");
     if (!dgamma || !dbeta || !workspace) return LN_ERR_NULL;
     if (!partials_ready && (!dy || !x || !mean || !rstd)) return LN_ERR_NULL;
     ln_status_t st = check_shape(rows, cols, dt, Kind::BWD);
@@ -578,6 +608,7 @@ ln_status_t ln_bwd_dgamma_dbeta(const void* dy, const void* x, const float* mean
 ln_status_t ln_bwd_noalloc(const void* dy, const void* x, const void* gamma, const float* mean,
                            const float* rstd, void* dx, float* dgamma, float* dbeta,
                            int64_t rows, int64_t cols, ln_dtype_t dt, hipStream_t stream) {
+    const Range range("ln_bwd_noalloc");
     if (!dy || !x || !gamma || !mean || !rstd || !dx || !dgamma || !dbeta) return LN_ERR_NULL;
     ln_status_t st = check_shape(rows, cols, dt, Kind::BWD);
     if (st != LN_OK) return st;
@@ -677,6 +708,7 @@ ln_status_t bias_dropout_residual_ln_bwd(const void* dy, const void* dz_extra, c
                                          float* workspace, size_t workspace_bytes, int64_t rows,
                                          int64_t cols, float p, uint64_t seed, ln_dtype_t dt,
                                          hipStream_t stream) {
+    const Range range("bias_dropout_residual_ln_bwd");
     return prologue_bwd(dy, dz_extra, z, gamma, mean, rstd, dresidual, dx, dgamma, dbeta, dbias,
                         workspace, workspace_bytes, rows, cols, p, seed, dt, stream, true);
 }
@@ -687,6 +719,7 @@ ln_status_t bias_dropout_residual_ln_bwd_dx(const void* dy, const void* dz_extra
                                             float* workspace, size_t workspace_bytes,
                                             int64_t rows, int64_t cols, float p, uint64_t seed,
                                             ln_dtype_t dt, hipStream_t stream) {
+    const Range range("bias_dropout_residual_ln_bwd_dx");
     return prologue_bwd(dy, dz_extra, z, gamma, mean, rstd, dresidual, dx, nullptr, nullptr,
                         nullptr, workspace, workspace_bytes, rows, cols, p, seed, dt, stream,
                         false);
@@ -695,6 +728,7 @@ ln_status_t bias_dropout_residual_ln_bwd_dx(const void* dy, const void* dz_extra
 ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t workspace_bytes,
                                               float* dgamma, float* dbeta, float* dbias,
                                               int64_t rows, int64_t cols, hipStream_t stream) {
+    const Range range("bias_dropout_residual_ln_bwd_fold");
     if (!workspace || !dgamma || !dbeta || !dbias) return LN_ERR_NULL;
     if (rows < 0 || cols <= 0) return LN_ERR_SHAPE;
     if (cols > LN_MAX_COLS_DROPOUT_BWD || rows > kMaxRows) return LN_ERR_UNSUPPORTED;
@@ -716,6 +750,7 @@ ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t wor
 ln_status_t add_rmsnorm_fwd(const void* x, const void* residual, const void* gamma,
                             void* residual_out, void* y, float* rstd, int64_t rows, int64_t cols,
                             float eps, ln_dtype_t dt, hipStream_t stream) {
+    const Range range("add_rmsnorm_fwd");
     if (!x || !gamma || !y || (residual && !residual_out)) return LN_ERR_NULL;
     if (!residual && residual_out) return LN_ERR_PARAM;
     ln_status_t st = check_shape(rows, cols, dt, Kind::RMS);
@@ -749,6 +784,7 @@ ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
                             const void* gamma, const float* rstd, void* dz, float* dgamma,
                             float* workspace, size_t workspace_bytes, int64_t rows, int64_t cols,
                             ln_dtype_t dt, hipStream_t stream) {
+    const Range range("add_rmsnorm_bwd");
     if (!dy || !z || !gamma || !rstd || !dz || !dgamma || !workspace) return LN_ERR_NULL;
     ln_status_t st = check_shape(rows, cols, dt, Kind::RMS);
     if (st != LN_OK) return st;
@@ -785,6 +821,7 @@ ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, flo
                                   void* dlogits, int64_t rows, int64_t cols, int64_t ld,
                                   float label_smoothing, float grad_scale, ln_dtype_t dt,
                                   hipStream_t stream) {
+    const Range range("cross_entropy_fwd_bwd");
     if (!logits || !labels || !loss) return LN_ERR_NULL;
     if (!valid_dtype(dt)) return LN_ERR_DTYPE;
     if (rows < 0 || cols <= 0 || ld < cols) return LN_ERR_SHAPE;
@@ -821,6 +858,7 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
                              void* y_dropped, int64_t rows, int64_t cols, float scale,
                              int causal, float p, uint64_t seed, ln_dtype_t dt,
                              hipStream_t stream) {
+    const Range range("attn_softmax_fwd");
     if (!x || !y) return LN_ERR_NULL;
     ln_status_t st = check_shape_stream(rows, cols, dt);
     if (st != LN_OK) return st;
@@ -858,6 +896,7 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
 ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
                              int64_t cols, float scale, int causal, float p, uint64_t seed,
                              ln_dtype_t dt, hipStream_t stream) {
+    const Range range("attn_softmax_bwd");
     if (!dy || !y || !dx) return LN_ERR_NULL;
     ln_status_t st = check_shape_stream(rows, cols, dt);
     if (st != LN_OK) return st;

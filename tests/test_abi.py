@@ -382,3 +382,19 @@ def test_prologue_backward_stage_validation(L):
     assert fold(wsb=8) == LN_ERR_WORKSPACE
     assert fold(dg=ws) == LN_ERR_UNSUPPORTED            # output over the partials
     assert fold(rows=0) == LN_OK
+
+
+def test_roctx_ranges_switched_on_do_not_change_results():
+    # MBROW_ROCTX=1 wraps every entry point in a roctx range (no tool attached
+    # here): the calls still validate and return as without it
+    import subprocess
+    import sys
+    code = ("import ctypes, memory_bound_row_amd as mb; L = mb.lib(); "
+            "print(L.ln_fwd(None, None, None, None, None, None, 4, 8, ctypes.c_float(1e-5), 0, None), "
+            "L.attn_softmax_fwd(None, None, 1, None, None, 4, 8, ctypes.c_float(1.0), 0, "
+            "ctypes.c_float(0.0), ctypes.c_uint64(0), 0, None))")
+    env = dict(os.environ, MBROW_ROCTX="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == [str(LN_ERR_NULL), str(LN_ERR_NULL)]
