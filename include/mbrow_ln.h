@@ -44,6 +44,10 @@
  *   partition of rows (a pure function of rows and cols) and a fixed-order
  *   fold, never floating-point atomics ([L11] §2.4 and [L10] §5.1 note that
  *   atomic accumulation order varies from run to run).
+ * Tracing.  With MBROW_ROCTX=1 in the environment (read once per process),
+ *   every entry point below that enqueues work opens a roctx range named
+ *   after itself and closes it on return (rocprofv3 --marker-trace shows
+ *   them); otherwise the library makes no roctx call.
  */
 #ifndef MBROW_LN_H
 #define MBROW_LN_H
