@@ -45,7 +45,8 @@
  *   fold, never floating-point atomics ([L11] §2.4 and [L10] §5.1 note that
  *   atomic accumulation order varies from run to run).
  * Tracing.  With MBROW_ROCTX=1 in the environment (read once per process),
- *   every entry point below that enqueues work opens a roctx range named
+ *   every entry point below that runs the library's row kernels (all but the
+ *   streaming references hbm_copy and hbm_stream) opens a roctx range named
  *   after itself and closes it on return (rocprofv3 --marker-trace shows
  *   them); otherwise the library makes no roctx call.
  */
