@@ -380,6 +380,17 @@ ln_status_t check_shape(int64_t rows, int64_t cols, ln_dtype_t dt, Kind k) {
 // take the LDS-staged kernels.
 bool staged(int64_t cols) { return cols > kRegisterMaxCols || force_staged(); }
 
+// The plain forward of fp32 rows of 8193-16384 columns on the vector path
+// runs faster staged (512 lanes x up to 8 slots, two workgroups per CU) than
+// in the register layout that holds them (1024 lanes x 4 slots, one
+// workgroup per CU, its last slot partly idle below 16384): measured 175 ->
+// 149 us at 8192x12288, 102.7 -> 100.2 us at 4096x16384.  The fused forward,
+// 16-bit rows and the backward measured as fast or faster in registers.
+// A layout forced through the test hook keeps the register kernel.
+bool staged_plain_fwd(Dt d, int64_t cols, bool vec) {
+    return d == Dt::F32 && vec && cols > 8192 && g_force_g.load(std::memory_order_relaxed) == 0;
+}
+
 ln_status_t from_hip(hipError_t e) { return e == hipSuccess ? LN_OK : LN_ERR_HIP; }
 
 // Shape check of the calls with a two-pass path for long rows.
@@ -477,7 +488,9 @@ ln_status_t ln_fwd(const void* x, const void* gamma, const void* beta, void* y, 
     a.nslots = (cols + elems_per_slot(d) - 1) / elems_per_slot(d);
     a.eps = eps;
     a.inv_m = (float)(1.0 / (double)cols);
-    if (staged(cols)) return from_hip(launch_wide_fwd(d, vec && !force_scalar(), false, a, stream));
+    const bool v = vec && !force_scalar();
+    if (staged(cols) || staged_plain_fwd(d, cols, v))
+        return from_hip(launch_wide_fwd(d, v, false, a, stream));
     return from_hip(launch_fwd(d, pick_path(d, cols, vec), false, a, stream));
 }
 

@@ -195,3 +195,24 @@ def test_fused_forward_wide_in_place(orc, cols):
     for a, b in ((z, z2), (y, y2), (mean, mean2), (rstd, rstd2)):
         assert torch.equal(a, b)
     check_fused(orc, inp, 0.1, 17, z, y, mean, rstd, mask, FMT[dtype])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_wide_config_shape_on_the_staged_path(orc, dtype):
+    # the wide-rows workload (4096 x 16384) forced onto the LDS-staged kernels
+    # (the register layouts take it by default), checked on sampled rows; the
+    # column sums over all rows through dbeta
+    rows, cols = 4096, 16384
+    case(f"forced staged path {dtype} {rows}x{cols}")
+    mb.debug_force_staged(True)
+    inp, y, mean, rstd, (dx, dg, db) = fwd_bwd(rows, cols, dtype, seed=21)
+    mb.debug_force_staged(False)
+    sel = np.concatenate([np.random.default_rng(2).choice(rows, 10, replace=False),
+                          [0, rows - 1]])
+    t = torch.as_tensor(sel, device="cuda")
+    check_fwd(orc, inp["x"][t], inp["gamma"], inp["beta"], y[t], mean[t], rstd[t], FMT[dtype])
+    check_bwd(orc, inp["dy"][t], inp["x"][t], inp["gamma"], mean[t], rstd[t], dx[t], None,
+              None, FMT[dtype])
+    dy64 = f64(inp["dy"])
+    assert_reports(cmp.check_colsum("wide.cfg.dbeta", f64(db), dy64.sum(axis=0),
+                                    np.abs(dy64).sum(axis=0), rows, FMT[dtype]))
