@@ -380,15 +380,17 @@ ln_status_t check_shape(int64_t rows, int64_t cols, ln_dtype_t dt, Kind k) {
 // take the LDS-staged kernels.
 bool staged(int64_t cols) { return cols > kRegisterMaxCols || force_staged(); }
 
-// The plain forward of fp32 rows of 8193-16384 columns on the vector path
+// The plain forward of fp32 rows of 6145-16384 columns on the vector path
 // runs faster staged (512 lanes x up to 8 slots, two workgroups per CU) than
-// in the register layout that holds them (1024 lanes x 4 slots, one
-// workgroup per CU, its last slot partly idle below 16384): measured 175 ->
-// 149 us at 8192x12288, 102.7 -> 100.2 us at 4096x16384.  The fused forward,
-// 16-bit rows and the backward measured as fast or faster in registers.
-// A layout forced through the test hook keeps the register kernel.
+// in the register layouts that hold them (512 or 1024 lanes x 4 slots, their
+// last slot partly idle): measured 101.8 -> 96.4 us at 9362x7168, 98.7 ->
+// 96.4 us at 8192x8192, 175 -> 149 us at 8192x12288, 102.7 -> 100.2 us at
+// 4096x16384; at 6144 columns and below the registers win (105.6 against
+// 128.3 us at 10922x6144).  The fused forward, 16-bit rows and the backward
+// measured as fast or faster in registers.  A layout forced through the
+// test hook keeps the register kernel.
 bool staged_plain_fwd(Dt d, int64_t cols, bool vec) {
-    return d == Dt::F32 && vec && cols > 8192 && g_force_g.load(std::memory_order_relaxed) == 0;
+    return d == Dt::F32 && vec && cols > 6144 && g_force_g.load(std::memory_order_relaxed) == 0;
 }
 
 ln_status_t from_hip(hipError_t e) { return e == hipSuccess ? LN_OK : LN_ERR_HIP; }
