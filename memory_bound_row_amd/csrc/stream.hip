@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         const int64_t clive = (nlive + kSchunk - 1) / kSchunk;      // chunks in play
         const int64_t call = (ns + kSchunk - 1) / kSchunk;
         auto fetch = [&](auto last) {
-            return [&, last](int64_t c, SmChunk<MASK>& b) {
+            return [&](int64_t c, SmChunk<MASK>& b) {
                 load_chunk<S, VEC, decltype(last)::value, kSu>(vx, c, nlive, lim, b.x);
                 if constexpr (MASK) load_chunk<S, VEC, false, kSu>(vm, c, nlive, lim, b.m);
             };
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_bwd(SmArgs a) {
         const int64_t clive = (nlive + kSchunk - 1) / kSchunk;
         const int64_t call = (ns + kSchunk - 1) / kSchunk;
         auto fetch = [&](auto last) {
-            return [&, last](int64_t c, DyChunk& b) {
+            return [&](int64_t c, DyChunk& b) {
                 load_chunk<S, VEC, decltype(last)::value, kSu>(vdy, c, nlive, lim, b.d);
                 load_chunk<S, VEC, decltype(last)::value, kSu>(vyy, c, nlive, lim, b.y);
             };
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kSnt) void xent_stream(XeArgs a) {
         const bool no_target = ignored || bad;
         const float xl = no_target ? 0.0f : elem_load<S>(vx, (uint32_t)label * S::BYTES);
         auto fetch = [&](auto last) {
-            return [&, last](int64_t c, XChunk& b) {
+            return [&](int64_t c, XChunk& b) {
                 load_chunk<S, VEC, decltype(last)::value, kSu>(vx, c, nv, cols, b.x);
             };
         };
