@@ -338,35 +338,59 @@ __global__ __launch_bounds__(T, 4) void ln_wide_fwd_vec_kernel(FwdArgs a) {
             }
         };
 
-        // pass 1: read (and form z), stage (slots past the row stage 0)
+        // pass 1: read (and form z), stage (slots past the row stage 0).
+        // Slots past the stage are not read again for the statistics: pass
+        // 1 keeps their count, sum and sum of squares shifted by the wave's
+        // first value cw (on the row's scale, so the sums stay small), and
+        // passes 2 and 3 add them in with the shift moved to c and mean.
+        float cw = 0.0f, s_ov = 0.0f, q_ov = 0.0f, n_ov = 0.0f;
         groups([&](int j0, auto n) {
             constexpr int N = decltype(n)::value;
             u32x4 v[N];
             values(j0, v, true);
+            if (j0 == 0) cw = lane_read(S::template elem<0>(v[0]), 0);   // uniform
 #pragma unroll
-            for (int u = 0; u < N; ++u)
-                if (staged(j0 + u)) stage[tid + (j0 + u) * T] = v[u];
+            for (int u = 0; u < N; ++u) {
+                if (staged(j0 + u)) {
+                    stage[tid + (j0 + u) * T] = v[u];
+                } else {
+                    float fv[E];
+                    S::unpack(v[u], fv);
+                    float t = 0.0f, q = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float d = fv[e] - cw;
+                        t += d;
+                        q = fmaf(d, d, q);
+                    }
+                    const bool in = tid + (j0 + u) * T < nslots;
+                    s_ov += in ? t : 0.0f;
+                    q_ov += in ? q : 0.0f;
+                    n_ov += in ? (float)E : 0.0f;
+                }
+            }
         });
         __syncthreads();
         // shift: the row's first value (fp32 rows whose mean dwarfs their
         // spread keep their precision; harmless for 16-bit rows)
         const float c = S::template elem<0>(stage[0]);
 
-        // passes 2-3: f(values, in row) over the lane's slots
+        // passes 2-3: f(values, in row) over the lane's staged slots
         auto over = [&](auto&& f) {
             groups([&](int j0, auto n) {
                 constexpr int N = decltype(n)::value;
-                u32x4 v[N];
-                values(j0, v, false);
 #pragma unroll
                 for (int u = 0; u < N; ++u) {
+                    if (!staged(j0 + u)) continue;
                     float fv[E];
-                    S::unpack(v[u], fv);
+                    S::unpack(stage[tid + (j0 + u) * T], fv);
                     f(fv, tid + (j0 + u) * T < nslots);
                 }
             });
         };
-        float sl = 0.0f;
+        // the slots past the stage: sum of (v - c) = s_ov + n_ov (cw - c)
+        // (lanes without such slots start from 0, as rows within the stage)
+        float sl = n_ov > 0.0f ? fmaf(n_ov, cw - c, s_ov) : 0.0f;
         over([&](const float* fv, bool in) {
             float t = 0.0f;
 #pragma unroll
@@ -374,7 +398,10 @@ __global__ __launch_bounds__(T, 4) void ln_wide_fwd_vec_kernel(FwdArgs a) {
             sl += in ? t : 0.0f;
         });
         const float mu = wide_sum<W>(sl, red[0], tid) * a.inv_m;   // mean of v - c
-        float ql = 0.0f;
+        // and sum of (v - c - mu)^2 = q_ov - 2 dc s_ov + n_ov dc^2,
+        // dc = c + mu - cw
+        const float dc = (c - cw) + mu;
+        float ql = n_ov > 0.0f ? fmaf(n_ov * dc, dc, fmaf(-2.0f * dc, s_ov, q_ov)) : 0.0f;
         over([&](const float* fv, bool in) {
             float t = 0.0f;
 #pragma unroll

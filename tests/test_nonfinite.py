@@ -77,6 +77,26 @@ def test_layernorm(orc, dtype, cols):
     assert_reports(cmp.check_colsum("nonfinite.dbeta", f64(db), db_ref, sb, ROWS, FMT[dtype]))
 
 
+@pytest.mark.parametrize("dtype,cols", [(torch.float32, 20000), (torch.float32, 65536),
+                                        (torch.bfloat16, 40000)])
+def test_layernorm_staged_rows(orc, dtype, cols):
+    # rows staged in LDS; fp32 65536: the last column lies past the stage, in
+    # the slots whose statistics pass 1 keeps apart
+    case(f"staged LayerNorm fwd with non-finite rows {ROWS}x{cols} {dtype}")
+    inp = dev(synth.layer_inputs(ROWS, cols, dtype, seed=33, names=("x", "gamma", "beta")))
+    x = inp["x"]
+    poison(x)
+    y, mean, rstd = mb.ln_fwd(x, inp["gamma"], inp["beta"], EPS)
+    torch.cuda.synchronize()
+    y_ref, _, _ = orc.ln_fwd(f64(x), f64(inp["gamma"]), f64(inp["beta"]), EPS)
+    good, bad = split(y_ref)
+    assert sorted(bad) == sorted(r for r, _, _ in POISON)
+    g = torch.as_tensor(good, device="cuda")
+    check_fwd(orc, x[g], inp["gamma"], inp["beta"], y[g], mean[g], rstd[g], FMT[dtype],
+              name="nonfinite.staged")
+    same_finiteness("nonfinite.staged.y", y[bad], y_ref[bad])
+
+
 @pytest.fixture(params=[False, True], ids=["registers", "two_pass"])
 def two_pass(request):
     """The register-resident kernels, or the two-pass long-row path forced
