@@ -48,11 +48,14 @@ constexpr int kSu2 = 2;
 constexpr int kStaged = 2;
 // Further chunks kept in registers, after the LDS-staged ones, by the 16-bit
 // vector-path kernels whose registers allow it (16 per lane per chunk): two
-// in the softmax backward, one in the cross-entropy.
+// in the softmax backward, one in the cross-entropy and in the softmax
+// forward without a mask.
 template <class S>
 constexpr int kRegStagedBwd = S::E == 8 ? 2 : 0;   // at most 2
 template <class S>
 constexpr int kRegStagedXent = S::E == 8 ? 1 : 0;  // at most 1
+template <class S, bool MASK>
+constexpr int kRegStagedFwd = S::E == 8 && !MASK ? 1 : 0;   // at most 1
 
 // Merge of the row's lane states: a butterfly per wave, then the waves in
 // order through LDS.  Every lane gets the row's state.
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
     __shared__ XeState lds[kSnw];
     // pass A's first chunks, each lane its own slots (x, then the mask's)
     __shared__ u32x4 stg[kStaged][MASK ? 2 * kSu : kSu][kSnt];
+    constexpr int R = VEC ? kRegStagedFwd<S, MASK> : 0;   // and the next R, in registers
     const int tid = threadIdx.x;
     const int m = (int)a.m;
     const int ns = (int)a.nslots;
@@ -255,6 +259,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
             }
         };
         XeState st{-INFINITY, 0.0f, 0.0f};
+        SmChunk<MASK> k0;   // the chunk after the staged ones (if R = 1)
         pipelined<SmChunk<MASK>, VEC>(clive, fetch(std::false_type{}),
                                  [&](int64_t c, const SmChunk<MASK>& b) {
             if (c < kStaged) {   // read back by this lane only: no barrier
@@ -264,6 +269,7 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
                     if constexpr (MASK) stg[c][kSu + k][tid] = b.m[k];
                 }
             }
+            if (R > 0 && c == kStaged) k0 = b;   // uniform
             float t[kSu][E];
             scores(c, b, t);
             float cm = -INFINITY;
@@ -288,13 +294,17 @@ __global__ __launch_bounds__(kSnt) void softmax_stream_fwd(SmArgs a) {
         // every chunk of the row is written; chunks past the query read
         // nothing and give y = 0
         auto staged = [&](int64_t c, SmChunk<MASK>& b) {
+            if (R == 0 || c < kStaged) {   // uniform
 #pragma unroll
-            for (int k = 0; k < kSu; ++k) {
-                b.x[k] = stg[c][k][tid];
-                if constexpr (MASK) b.m[k] = stg[c][kSu + k][tid];
+                for (int k = 0; k < kSu; ++k) {
+                    b.x[k] = stg[c][k][tid];
+                    if constexpr (MASK) b.m[k] = stg[c][kSu + k][tid];
+                }
             }
+            if (R > 0 && c == kStaged) b = k0;
         };
-        pipelined_staged<SmChunk<MASK>, VEC>(clive < kStaged ? clive : kStaged, call, staged,
+        pipelined_staged<SmChunk<MASK>, VEC>(clive < kStaged + R ? clive : kStaged + R, call,
+                                             staged,
                                              fetch(std::true_type{}),
                                              [&](int64_t c, const SmChunk<MASK>& b) {
             float t[kSu][E];
