@@ -921,7 +921,7 @@ def configs_report(cpp_launch: bool = True) -> None:
             "LayerNorm forward + backward, LDS-staged rows (widest fp32 backward)")
     for dtype in (torch.float32, torch.bfloat16):
         fwd_bwd(2048, 65536, dtype, 2, 20, "LayerNorm forward, LDS-staged rows (widest; fp32 "
-                "rows past the stage read again)", bwd=False)
+                "slots past the stage read again for the output)", bwd=False)
 
 
 def main():
