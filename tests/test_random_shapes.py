@@ -133,3 +133,55 @@ def test_random_long_softmax_rows(orc, idx):
     check_softmax_fwd(orc, x, y, yd, fmt, scale=scale, mask=mask, rows_per_mask=rows, p=p,
                       seed=idx, name="rnd.long_sm")
     check_softmax_bwd(orc, dy, y, dx, fmt, scale=scale, p=p, seed=idx, name="rnd.long_sm_bwd")
+
+
+@pytest.mark.parametrize("idx", range(12))
+def test_random_staged_and_two_pass_rows(orc, idx):
+    """Rows the staged LayerNorm and the two-pass softmax / cross-entropy
+    take by default, on seeded random widths, dtypes and alignments: the
+    LayerNorm forward + backward (fp32 forwards from 6145 columns, every
+    dtype past 16384, up to the backward's limit), the fused forward up to
+    65536 columns, the two-pass rows up to 300000 columns."""
+    g = np.random.default_rng([9001, idx])
+    dtype = DTYPES[int(g.integers(0, 3))]
+    mis = bool(g.integers(0, 3) == 0)
+    fmt = FMT[dtype]
+    seed = 5000 + idx
+    kind = ("layernorm", "fused", "stream")[idx % 3]
+    if kind == "layernorm":
+        lo = 6145 if dtype == torch.float32 else 16385
+        hi = 19968 if dtype == torch.float32 else 32768
+        cols = int(g.integers(lo, hi + 1))
+        rows = int(g.integers(1, 40))
+        case(f"random staged LayerNorm {idx}: {rows}x{cols} {dtype} misaligned={mis}")
+        d = {k: place(v, mis) for k, v in synth.layer_inputs(rows, cols, dtype, seed=seed).items()}
+        y, mean, rstd = mb.ln_fwd(d["x"], d["gamma"], d["beta"], EPS)
+        dx, dg, db = mb.ln_bwd(d["dy"], d["x"], d["gamma"], mean, rstd)
+        torch.cuda.synchronize()
+        check_fwd(orc, d["x"], d["gamma"], d["beta"], y, mean, rstd, fmt, name="rnd.staged")
+        check_bwd(orc, d["dy"], d["x"], d["gamma"], mean, rstd, dx, dg, db, fmt,
+                  name="rnd.staged_bwd")
+    elif kind == "fused":
+        cols = int(g.integers(16385, 65537))
+        rows = int(g.integers(1, 12))
+        case(f"random staged fused forward {idx}: {rows}x{cols} {dtype} misaligned={mis}")
+        d = {k: place(v, mis) for k, v in synth.layer_inputs(rows, cols, dtype, seed=seed).items()}
+        z, y, mean, rstd, mask = mb.bias_dropout_residual_ln_fwd(
+            d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 0.2, seed, EPS,
+            want_mask=True)
+        torch.cuda.synchronize()
+        check_fused(orc, d, 0.2, seed, z, y, mean, rstd, mask, fmt, name="rnd.staged_fused")
+    else:
+        cols = int(g.integers(65537, 300001))
+        rows = int(g.integers(1, 6))
+        case(f"random two-pass rows {idx}: {rows}x{cols} {dtype} misaligned={mis}")
+        cpu = synth.layer_inputs(rows, cols, dtype, seed=seed, x_std=3.0, names=("x", "dy"))
+        x, dy = place(cpu["x"], mis), place(cpu["dy"], mis)
+        y, yd = mb.attn_softmax_fwd(x, 0.5, p=0.1, seed=seed, want_dropped=True)
+        dx = mb.attn_softmax_bwd(dy, y, 0.5, p=0.1, seed=seed)
+        lab = synth.class_labels(rows, cols, seed=seed, ignore_frac=0.1).to("cuda")
+        loss, dl = mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0)
+        torch.cuda.synchronize()
+        check_softmax_fwd(orc, x, y, yd, fmt, scale=0.5, p=0.1, seed=seed, name="rnd.tp_sm")
+        check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, p=0.1, seed=seed, name="rnd.tp_sm_bwd")
+        check_xent(orc, x, lab, cols, 0.1, 1.0, loss, dl, fmt, name="rnd.tp_xent")
