@@ -11,11 +11,13 @@
 // in a fixed order (one butterfly per wave, then the waves in order through
 // LDS).  Pass B writes the output exactly as the register kernels do (the
 // same mask words, exp2 form and dropout).  Pass A keeps the row's first two
-// chunks (128 KB) in LDS, each lane its own slots, so pass B reads them back
-// from there and re-reads only the rest of the row from global memory
-// ("02 · llmc/ 的 CUDA kernel 层" §3.1: what fits on chip is read once).  The
-// rest is read twice (the backward reads dy and y), against once for rows
-// that fit in registers.
+// chunks (128 KB) in LDS, each lane its own slots, and the 16-bit kernels
+// with registers to spare one or two more chunks in registers, so pass B
+// takes those from on chip and re-reads only the rest of the row from global
+// memory ("02 · llmc/ 的 CUDA kernel 层" §3.1: what fits on chip is read
+// once), last chunk first, while L2 may still hold it.  The rest is read
+// twice (the backward reads dy and y), against once for rows that fit in
+// registers.
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 #include "online_softmax.hpp"
