@@ -24,9 +24,9 @@
 //
 // Schedule.  One row block at a time per workgroup, its loads issued
 // together at the top of the iteration; all P workgroups are resident, so
-// the memory system sees P blocks in flight.  The prologue backward (16-bit
-// rows of one wave or less) also loads the next block while it computes the
-// current one; the plain modes measured no faster with that.
+// the memory system sees P blocks in flight.  With 16-bit storage, the
+// prologue and RMSNorm backwards, and the plain one for rows of more than
+// one wave, also load the next block while they compute the current one.
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 
@@ -140,11 +140,14 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     // spare for that and unpack in each pass.
     constexpr bool ONCE = !(DROP && G > 64);
     // With a 16-bit block unpacked once, its packed registers are free during
-    // the two passes: the prologue and RMSNorm backwards load the next
-    // block's dy, z and row statistics into them there, so each block's loads
-    // are in flight while the previous block's arithmetic runs (the Philox
-    // rounds, the sums).  (The plain backward measured no faster so.)
-    constexpr bool PF = (DROP || RMS) && VEC && ONCE && E == 8 && V <= 4;
+    // the two passes: the next block's dy, x and row statistics are loaded
+    // into them there, so each block's loads are in flight while the
+    // previous block's arithmetic runs (the Philox rounds, the sums, the
+    // cross-wave exchange).  The prologue and RMSNorm backwards do this at
+    // every layout; the plain backward only for rows of more than one wave
+    // (a workgroup walks one to four rows per block there; with one-wave
+    // rows, eight per block, it measured no faster).
+    constexpr bool PF = (DROP || RMS || (DX && G > 64)) && VEC && ONCE && E == 8 && V <= 4;
     u32x4 xp[PF ? V : 1], dp[PF ? V : 1];   // the prefetched block
     float mu_n = 0.0f, rs_n = 0.0f;
     auto issue = [&](int64_t b) {
