@@ -135,19 +135,16 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     const bool has_extra = EXTRA && a.dz_extra != nullptr;   // uniform
     __shared__ float red[2][NG][WPR][2];   // cross-wave A/B exchange (multi-wave rows)
 
-    // The block is unpacked once (x - mean in place, dy as is), except in
-    // multi-wave rows of the prologue backward, which have no registers to
-    // spare for that and unpack in each pass.
-    constexpr bool ONCE = !(DROP && G > 64);
-    // With a 16-bit block unpacked once, its packed registers are free during
-    // the two passes: the next block's dy, x and row statistics are loaded
-    // into them there, so each block's loads are in flight while the
-    // previous block's arithmetic runs (the Philox rounds, the sums, the
-    // cross-wave exchange).  The prologue and RMSNorm backwards do this at
-    // every layout; the plain backward only for rows of more than one wave
-    // (a workgroup walks one to four rows per block there; with one-wave
-    // rows, eight per block, it measured no faster).
-    constexpr bool PF = (DROP || RMS || (DX && G > 64)) && VEC && ONCE && E == 8 && V <= 4;
+    // The block is unpacked once (x - mean in place, dy as is).  With 16-bit
+    // storage its packed registers are then free during the two passes: the
+    // next block's dy, x and row statistics are loaded into them there, so
+    // each block's loads are in flight while the previous block's arithmetic
+    // runs (the Philox rounds, the sums, the cross-wave exchange).  The
+    // prologue and RMSNorm backwards do this at every layout; the plain
+    // backward only for rows of more than one wave (a workgroup walks one to
+    // four rows per block there; with one-wave rows, eight per block, it
+    // measured no faster).
+    constexpr bool PF = (DROP || RMS || (DX && G > 64)) && VEC && E == 8 && V <= 4;
     u32x4 xp[PF ? V : 1], dp[PF ? V : 1];   // the prefetched block
     float mu_n = 0.0f, rs_n = 0.0f;
     auto issue = [&](int64_t b) {
@@ -237,16 +234,14 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         // (the per-element path and multi-wave rows of the prologue backward
         // have no registers to spare for gamma unpacked across blocks)
         if constexpr (DX && (!VEC || (DROP && G > 64))) keep_packed(gp);
-        float xm_[ONCE ? V : 1][E], d_[ONCE ? V : 1][E];
-        if constexpr (ONCE) {
+        float xm_[V][E], d_[V][E];
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                S::unpack(xr[i], xm_[i]);
-                S::unpack(dr[i], d_[i]);
-                if constexpr (!RMS) {
+        for (int i = 0; i < V; ++i) {
+            S::unpack(xr[i], xm_[i]);
+            S::unpack(dr[i], d_[i]);
+            if constexpr (!RMS) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) xm_[i][e] = xm_[i][e] - mu;
-                }
+                for (int e = 0; e < E; ++e) xm_[i][e] = xm_[i][e] - mu;
             }
         }
         if constexpr (PF) {
@@ -258,19 +253,10 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         }
         // x - mean and dy of slot i
         auto slot = [&](int i, float* xm, float* d) {
-            if constexpr (ONCE) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    xm[e] = xm_[i][e];
-                    d[e] = d_[i][e];
-                }
-            } else {
-                S::unpack(xr[i], xm);
-                S::unpack(dr[i], d);
-                if constexpr (!RMS) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) xm[e] = xm[e] - mu;
-                }
+            for (int e = 0; e < E; ++e) {
+                xm[e] = xm_[i][e];
+                d[e] = d_[i][e];
             }
         };
         float c1 = 0.0f, c2 = 0.0f;
@@ -322,10 +308,6 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
         // and the partials-only passes produce the same bits.
         const rsrc_t vdx = view(DX ? a.dx : a.dy, base);
         const rsrc_t vdi = view(DROP ? a.dx_in : a.dy, base);
-        if constexpr (!ONCE) {
-            keep_packed(xr);
-            keep_packed(dr);
-        }
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const int col0 = (i * G + lg) * E;
