@@ -25,8 +25,8 @@
 // Schedule.  One row block at a time per workgroup, its loads issued
 // together at the top of the iteration; all P workgroups are resident, so
 // the memory system sees P blocks in flight.  With 16-bit storage, the
-// prologue and RMSNorm backwards, and the plain one for rows of more than
-// one wave, also load the next block while they compute the current one.
+// prologue and RMSNorm backwards, and every mode for rows of two to eight
+// waves, also load the next block while they compute the current one.
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 
@@ -143,8 +143,11 @@ __global__ __launch_bounds__(BwdGeometry<G>::NT) void ln_bwd_kernel(BwdArgs a) {
     // prologue and RMSNorm backwards do this at every layout; the plain
     // backward only for rows of more than one wave (a workgroup walks one to
     // four rows per block there; with one-wave rows, eight per block, it
-    // measured no faster).
-    constexpr bool PF = (DROP || RMS || (DX && G > 64)) && VEC && E == 8 && V <= 4;
+    // measured no faster).  fp32 rows free nothing by unpacking (dy is kept
+    // as loaded), so their prefetch costs registers: taken for rows of two
+    // to eight waves, where it measured faster and fits 256 registers.
+    constexpr bool MULTI = DX && G > 64 && G <= 512;
+    constexpr bool PF = VEC && V <= 4 && (E == 8 ? (DROP || RMS || MULTI) : MULTI);
     u32x4 xp[PF ? V : 1], dp[PF ? V : 1];   // the prefetched block
     float mu_n = 0.0f, rs_n = 0.0f;
     auto issue = [&](int64_t b) {
