@@ -264,7 +264,7 @@ Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool dropout) {
                   : pick(false, ns, vec, kBwd16, MBROW_N(kBwd16), true);
 }
 
-int64_t persistent_grid(const void* kernel, int threads, int64_t blocks) {
+static int64_t grid_for(const void* kernel, int threads, int64_t blocks, int dyn_per_cu) {
     const int forced = g_force_grid.load(std::memory_order_relaxed);
     if (forced < 0) return blocks;
     static std::mutex mu;
@@ -299,7 +299,16 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t blocks) {
     if (cus <= 0 || n <= 0) return blocks;   // unknown: one workgroup per block
     const int64_t per = forced > 0 ? forced : n;
     const int64_t g = (int64_t)cus * per;
+    if (forced == 0 && dyn_per_cu > 0 && n >= dyn_per_cu && blocks >= 3 * g) return blocks;
     return g < blocks ? g : blocks;
+}
+
+int64_t persistent_grid(const void* kernel, int threads, int64_t blocks, int dyn_per_cu) {
+    // a dispatch counts its work-items in 32 bits; every kernel walks its
+    // blocks with a stride of the grid, so a smaller grid only loops more
+    const int64_t cap = std::numeric_limits<int32_t>::max() / threads;
+    const int64_t g = grid_for(kernel, threads, blocks, dyn_per_cu);
+    return g < cap ? g : cap;
 }
 
 // ln_bwd_noalloc's static device scratch (noalloc.hip).

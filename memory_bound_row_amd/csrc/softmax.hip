@@ -514,7 +514,7 @@ static hipError_t launch_wide(const SmArgs& a, hipStream_t s) {
     } else {
         const void* k =
             reinterpret_cast<const void*>(&softmax_wide_kernel<St, G, V, VEC, BWD, MASK>);
-        const int64_t grid = persistent_grid(k, G, a.rows);
+        const int64_t grid = persistent_grid(k, G, a.rows, 1);
         hipLaunchKernelGGL((softmax_wide_kernel<St, G, V, VEC, BWD, MASK>),
                            dim3((unsigned)grid), dim3(G), 0, s, a);
         return hipGetLastError();
@@ -534,7 +534,9 @@ static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
         constexpr int ROWS = SmGeometry<G>::ROWS;
         const int64_t nblk = (a.rows + ROWS - 1) / ROWS;
         const void* k = reinterpret_cast<const void*>(&softmax_kernel<St, G, V, VEC, BWD>);
-        const int64_t grid = persistent_grid(k, SmGeometry<G>::NT, nblk);
+        // one workgroup per block when there are three rounds of them:
+        // 3-10 % faster at every width measured
+        const int64_t grid = persistent_grid(k, SmGeometry<G>::NT, nblk, 1);
         hipLaunchKernelGGL((softmax_kernel<St, G, V, VEC, BWD>), dim3((unsigned)grid),
                            dim3(SmGeometry<G>::NT), 0, s, a);
         return hipGetLastError();
