@@ -376,8 +376,9 @@ def counter_sample() -> None:
     (8192 x 1280 bf16, dz_extra given), the attention softmax forward (y and
     dropped y) and backward (8 x 16 x 512 x 512 fp16, p = 0.1), add + RMSNorm
     forward and backward (2048 x 4096 bf16), the cross-entropy (8192 x 50257
-    bf16, rows of 50304), and the two-pass paths (cross-entropy over 2048 x
-    256000 bf16, softmax over 2048 x 131072 fp16)."""
+    bf16, rows of 50304), the cross-entropy over 2048 x 256000 bf16 (rows held
+    in registers and LDS, then forced onto the two-pass path), and the
+    two-pass softmax over 2048 x 131072 fp16."""
     import torch
     import memory_bound_row_amd as mb
     from memory_bound_row_amd import synth
@@ -416,10 +417,13 @@ def counter_sample() -> None:
     lab = synth.class_labels(2048, 256000, seed=SEED).to(dev)
     loss = torch.empty(2048, dtype=torch.float32, device=dev)
     dx = torch.empty_like(x)
-    for _ in range(3):
-        mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0, loss=loss,
-                                 dlogits=dx)
-    torch.cuda.synchronize()
+    for two_pass in (False, True):
+        mb.debug_force_two_pass(two_pass)
+        for _ in range(3):
+            mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0, loss=loss,
+                                     dlogits=dx)
+        torch.cuda.synchronize()
+    mb.debug_force_two_pass(False)
     del x, dx
     d = synth.layer_inputs(2048, 131072, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
     s, dy = d["x"].to(dev), d["dy"].to(dev)
@@ -816,7 +820,7 @@ def configs_report(cpp_launch: bool = True) -> None:
                  bwd=False)
 
     # fused cross-entropy (loss + gradient) over a vocabulary-wide row
-    def xent_case(rows, cols, ld, dt, label):
+    def xent_case(rows, cols, ld, dt, label, two_pass=False, cpu=True):
         x = synth.logits(rows, ld, dt, seed=SEED).to(dev)
         lab = synth.class_labels(rows, cols, seed=SEED).to(dev)
         loss = torch.empty(rows, dtype=torch.float32, device=dev)
@@ -832,12 +836,16 @@ def configs_report(cpp_launch: bool = True) -> None:
             mb.cross_entropy_fwd_bwd(x, lab, cols=cols, label_smoothing=0.1,
                                      grad_scale=1.0 / rows, loss=loss, dlogits=x)
 
-        for i in range(3):   # first touches of the fresh 0.4-3 GB buffers
-            f(i)
-        torch.cuda.synchronize()
-        n = 20
-        ms = timed(capture(f, n), n)
-        ms_ip = timed(capture(g, n), n)
+        mb.debug_force_two_pass(two_pass)
+        try:
+            for i in range(3):   # first touches of the fresh 0.4-3 GB buffers
+                f(i)
+            torch.cuda.synchronize()
+            n = 20
+            ms = timed(capture(f, n), n)
+            ms_ip = timed(capture(g, n), n)
+        finally:
+            mb.debug_force_two_pass(False)
         b = 2 * rows * cols * s + 12 * rows
 
         def xe_prep(k):
@@ -853,7 +861,7 @@ def configs_report(cpp_launch: bool = True) -> None:
               "pct_of_hbm_peak": round(100.0 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
               "in_place_us": round(ms_ip * 1e3, 3),
               "in_place_GBps": round(b / (ms_ip * 1e-3) / 1e9, 1),
-              "cpu_baseline": oracle_rate(xe_prep, xe_work, b / rows, rows)})
+              **({"cpu_baseline": oracle_rate(xe_prep, xe_work, b / rows, rows)} if cpu else {})})
         del x, dx, lab, loss
         torch.cuda.empty_cache()
 
@@ -861,7 +869,11 @@ def configs_report(cpp_launch: bool = True) -> None:
         xent_case(8192, 50257, 50304, dt,
                   "fused cross-entropy loss + gradient, GPT-2 vocabulary, 8x1024 tokens")
     xent_case(2048, 256000, 256000, torch.bfloat16,
-              "fused cross-entropy, 256000-class vocabulary (two-pass path), 2048 tokens")
+              "fused cross-entropy, 256000-class vocabulary (row held in registers and LDS), "
+              "2048 tokens")
+    xent_case(2048, 256000, 256000, torch.bfloat16,
+              "fused cross-entropy, 256000-class vocabulary, forced onto the two-pass path, "
+              "2048 tokens", two_pass=True, cpu=False)
 
     # softmax over long rows: the register layouts (32768 keys; also forced
     # onto the two-pass path, for comparison) and the two-pass path past them

@@ -105,6 +105,14 @@ typedef enum {
  * and Qwen-2's 151936 classes fit in bf16). */
 #define LN_MAX_COLS_XENT_F32 65536
 #define LN_MAX_COLS_XENT_16 163840
+/* Widest padded row (ld) of cross_entropy_fwd_bwd held on chip by one
+ * workgroup, part in registers and part in LDS, and so still read once:
+ * 131072 fp32 or 262144 fp16/bf16 classes (Llama-3's 128256 in fp32, a
+ * 256000-class vocabulary in bf16).  Only rows on the 16-byte vector path (logits and dlogits
+ * 16-byte aligned, ld * sizeof(T) a multiple of 16); other rows past
+ * LN_MAX_COLS_XENT_* take the two-pass path. */
+#define LN_MAX_COLS_XENT_LDS_F32 131072
+#define LN_MAX_COLS_XENT_LDS_16 262144
 /* Widest row of attn_softmax_fwd / attn_softmax_bwd held in registers (and
  * so read once): 32768 fp32 or 65536 fp16/bf16 scores (one 1024-lane
  * workgroup per row beyond 16384). */
@@ -114,9 +122,10 @@ typedef enum {
  * tensors, dy and y, per row). */
 #define LN_MAX_COLS_SOFTMAX_BWD_16 49152
 /* Widest row of attn_softmax_fwd / attn_softmax_bwd / cross_entropy_fwd_bwd:
- * rows wider than their register path (LN_MAX_COLS_SOFTMAX_* for the
- * softmax, LN_MAX_COLS_XENT_* for the cross-entropy) take a two-pass path
- * that reads the row twice. */
+ * rows wider than their on-chip paths (LN_MAX_COLS_SOFTMAX_* for the
+ * softmax, LN_MAX_COLS_XENT_LDS_* on the vector path and LN_MAX_COLS_XENT_*
+ * otherwise for the cross-entropy) take a two-pass path that reads the rest
+ * of the row twice. */
 #define LN_MAX_COLS_STREAM (1 << 24)
 
 /*
@@ -431,8 +440,11 @@ ln_status_t add_rmsnorm_bwd(const void* dy, const void* dz_extra, const void* z,
  *            loss).
  * ld >= cols, else LN_ERR_SHAPE.  Rows of up to LN_MAX_COLS_XENT_F32 (fp32) or
  * LN_MAX_COLS_XENT_16 (fp16/bf16) columns are held in registers and read
- * once; wider rows, up to LN_MAX_COLS_STREAM (else LN_ERR_UNSUPPORTED), are
- * read twice: an online maximum/sum pass, then the gradient pass.
+ * once; on the 16-byte vector path, rows of up to LN_MAX_COLS_XENT_LDS_F32 /
+ * LN_MAX_COLS_XENT_LDS_16 are held in the registers and LDS of one workgroup
+ * and still read once; wider rows, up to LN_MAX_COLS_STREAM (else
+ * LN_ERR_UNSUPPORTED), are read twice: an online maximum/sum pass, then the
+ * gradient pass.
  * Arithmetic in float32 (exp by the device's exp2).
  */
 ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, float* loss,

@@ -41,6 +41,9 @@ hipError_t launch_softmax_stream_bf16(bool, bool, const SmArgs&, hipStream_t);
 hipError_t launch_xent_stream_f32(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_f16(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_bf16(bool, const XeArgs&, hipStream_t);
+hipError_t launch_xent_lds_f32(const XeArgs&, hipStream_t);
+hipError_t launch_xent_lds_f16(const XeArgs&, hipStream_t);
+hipError_t launch_xent_lds_bf16(const XeArgs&, hipStream_t);
 
 hipError_t launch_softmax_stream(Dt dt, bool vec, bool backward, const SmArgs& a, hipStream_t s) {
     switch (dt) {
@@ -55,6 +58,18 @@ hipError_t launch_xent_stream(Dt dt, bool vec, const XeArgs& a, hipStream_t s) {
     case Dt::F32: return launch_xent_stream_f32(vec, a, s);
     case Dt::F16: return launch_xent_stream_f16(vec, a, s);
     default: return launch_xent_stream_bf16(vec, a, s);
+    }
+}
+
+static_assert(LN_MAX_COLS_XENT_LDS_F32 / 4 == kXeLdsMaxSlots &&
+                  LN_MAX_COLS_XENT_LDS_16 / 8 == kXeLdsMaxSlots,
+              "the header's on-chip cross-entropy widths are the kernel's slots");
+
+hipError_t launch_xent_lds(Dt dt, const XeArgs& a, hipStream_t s) {
+    switch (dt) {
+    case Dt::F32: return launch_xent_lds_f32(a, s);
+    case Dt::F16: return launch_xent_lds_f16(a, s);
+    default: return launch_xent_lds_bf16(a, s);
     }
 }
 
@@ -873,8 +888,15 @@ ln_status_t cross_entropy_fwd_bwd(const void* logits, const int64_t* labels, flo
     a.alpha = label_smoothing;
     a.inv_v = (float)(1.0 / (double)cols);
     a.scale = grad_scale;
-    if (ld > max_ld || force_two_pass())
-        return from_hip(launch_xent_stream(d, vec && !force_scalar(), a, stream));
+    if (ld > max_ld || force_two_pass()) {
+        // past the register layouts: rows that the registers and LDS of one
+        // workgroup hold (vector path) are still read once; the rest take
+        // the two-pass walk
+        const bool vec_ok = vec && !force_scalar();
+        if (vec_ok && !force_two_pass() && a.nslots <= kXeLdsMaxSlots)
+            return from_hip(launch_xent_lds(d, a, stream));
+        return from_hip(launch_xent_stream(d, vec_ok, a, stream));
+    }
     return from_hip(launch_xent(d, pick_xent_path(d, a.nslots, vec), a, stream));
 }
 

@@ -215,6 +215,23 @@ struct XeArgs {
 Path pick_xent_path(Dt dt, int64_t slots, bool vec);
 hipError_t launch_xent(Dt dt, const Path& p, const XeArgs& a, hipStream_t s);
 
+// Cross-entropy rows past the register layouts on the vector path
+// (xent_lds_kernel): one workgroup per row holds the padded row, part of
+// each lane's slots in registers and the rest in LDS, so rows of up to
+// 32768 slots (131072 fp32, 262144 16-bit classes) are read once.  16-bit
+// rows: 1024 lanes x (23 + 9) slots; fp32 rows: 512 lanes x (45 + 19) slots
+// (fp32 needs the 256 registers a lane of a 512-lane workgroup has).
+template <int E>
+struct XeLds {
+    static constexpr int LANES = E == 8 ? 1024 : 512;
+    static constexpr int REG = E == 8 ? 23 : 45;   // slots per lane in registers
+    static constexpr int LDS = E == 8 ? 9 : 19;    // slots per lane in LDS
+};
+constexpr int64_t kXeLdsMaxSlots = 32768;
+static_assert(XeLds<8>::LANES * (XeLds<8>::REG + XeLds<8>::LDS) == kXeLdsMaxSlots, "16-bit");
+static_assert(XeLds<4>::LANES * (XeLds<4>::REG + XeLds<4>::LDS) == kXeLdsMaxSlots, "fp32");
+hipError_t launch_xent_lds(Dt dt, const XeArgs& a, hipStream_t s);
+
 // LayerNorm rows wider than the register layouts (ln_wide.hip): one 1024-lane
 // workgroup per row, the row staged in LDS.  The backward takes modes DX,
 // DX_PARTIALS and PARTIALS.

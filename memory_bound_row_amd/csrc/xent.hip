@@ -272,10 +272,217 @@ static hipError_t dispatch(const Path& p, const XeArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// Rows past the register layouts, on the vector path: one workgroup per row
+// holds the whole row, each lane's first REG slots in registers and its
+// next LDS slots in LDS (XeLds), so the row is still
+// read from global memory once ("02 · llmc/ 的 CUDA kernel 层" §3.1: what
+// fits on chip is read once; §6.1: the vocabulary-wide row reduced by one
+// online softmax and overwritten by its gradient).  The LDS slots are loaded
+// straight into LDS (buffer loads with an LDS destination), so all slots
+// of a lane are in flight together without staging registers; each wave's
+// lanes land in consecutive 16-byte cells, and each lane reads back only the
+// cells its own loads wrote.  The arithmetic is the register kernel's, slot
+// by slot, in the same order.
+template <class S>
+__global__ __launch_bounds__(XeLds<S::E>::LANES) void xent_lds_kernel(XeArgs a) {
+    constexpr int E = S::E;
+    constexpr int G = XeLds<E>::LANES;
+    constexpr int VR = XeLds<E>::REG;
+    constexpr int VL = XeLds<E>::LDS;
+    constexpr int NW = G / 64;
+    constexpr int W = G * E;   // columns between consecutive slots of a lane
+    __shared__ __attribute__((aligned(16))) u32x4 stage[VL][G];
+    __shared__ XeState red[2][NW];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ld = (int)a.ld;
+    const int cols = (int)a.cols;
+    const int nv = (int)a.nvalid;
+    const int ns = (int)a.nslots;
+    const bool grad = a.dx != nullptr;   // uniform
+    const int base = tid * E;            // first column of the lane's slot 0
+    // Byte offset of slot i of this lane in its row's view, or kOob past
+    // `nslot`: formed where it is used from an opaque copy of the lane index,
+    // so that no slot's offset stays live between the loads and the stores
+    // (32 of them would not fit beside the row).
+    auto slot_off = [&](int i, int nslot) {
+        const int t = opaque(tid);
+        return i * G + t < nslot ? (uint32_t)(t * 16 + i * G * 16) : kOob;
+    };
+    // LDS slot j of this lane, read where it is used: one slot's registers
+    // at a time (the next read is not hoisted above this one)
+    auto lds_slot = [&](int j) {
+        u32x4 v = stage[j][tid];
+        hold_packed(v);
+        return v;
+    };
+    // The per-row constants are formed inside the row loop from opaque
+    // scalar copies of the arguments, so they are not hoisted out of it into
+    // vector registers that would stay live beside the row.
+    auto sreg = [](float v) {
+        asm volatile("" : "+s"(v));
+        return v;
+    };
+
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const int64_t label = a.labels[row];
+        const bool ignored = label < 0;
+        const bool bad = label >= cols;
+        // x at the label (one element, uniform per row), loaded before the
+        // row and moved to a scalar register once it arrives
+        const float xl_v = (ignored || bad) ? 0.0f : S::load1(a.x, row * (int64_t)ld + label);
+        const rsrc_t vx = row_view<S>(a.x, row, 1, ld);
+        u32x4 xr[VR];
+#pragma unroll
+        for (int i = 0; i < VR; ++i) xr[i] = buf_load_nt(vx, slot_off(i, nv));
+        // the wave's 64 cells of LDS slot j start at stage[j][64 * wave]
+        // (the previous row's cells were consumed before its stores)
+#pragma unroll
+        for (int j = 0; j < VL; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vx, (__attribute__((address_space(3))) void*)&stage[j][64 * wave], 16,
+                (int)slot_off(VR + j, nv), 0, 0, kNt);
+        const float xl = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, xl_v)));
+
+        // Pass 1: max and sum of x; pass 2: sum of exp(x - max).  Slots
+        // wholly inside the classes take no per-element test; slots past
+        // them are skipped (their values are not used).
+        XeState st{-INFINITY, 0.0f, 0.0f};
+        // The lane's L = cols - base columns from its first one: slots
+        // i < nfull lie wholly inside the classes, slot i < npart holds at
+        // least one (columns e < L - i*W of it).  Each pass forms these from
+        // its own opaque copy of L, so the per-slot tests are made again
+        // against small inline constants rather than kept live.
+        int L, nfull, npart;
+        auto limits = [&]() {
+            L = opaque(cols - base);
+            nfull = L >= E ? (L - E) / W + 1 : 0;
+            npart = L > 0 ? (L - 1) / W + 1 : 0;
+        };
+        limits();
+        auto sums = [&](int i, const u32x4& v) {
+            float f[E];
+            S::unpack(v, f);
+            if (i < nfull) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    st.mx = fmaxf(st.mx, f[e]);
+                    st.sx += f[e];
+                }
+            } else if (i < npart) {
+                const int r = L - i * W;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if (e < r) {
+                        st.mx = fmaxf(st.mx, f[e]);
+                        st.sx += f[e];
+                    }
+                }
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < VR; ++i) sums(i, xr[i]);
+#pragma unroll
+        for (int j = 0; j < VL; ++j) sums(VR + j, lds_slot(j));
+        keep_packed(xr);
+        limits();
+        {
+            // exp(x - m) = exp2(x log2(e) - m log2(e)), one fma and one exp2
+            const float nm = st.mx == -INFINITY ? 0.0f : -st.mx * kLog2e;   // lanes past the row
+            auto expsum = [&](int i, const u32x4& v) {
+                float f[E];
+                S::unpack(v, f);
+                if (i < nfull) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) st.z += exp2_(fmaf(f[e], kLog2e, nm));
+                } else if (i < npart) {
+                    const int r = L - i * W;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (e < r) st.z += exp2_(fmaf(f[e], kLog2e, nm));
+                }
+            };
+#pragma unroll
+            for (int i = 0; i < VR; ++i) expsum(i, xr[i]);
+#pragma unroll
+            for (int j = 0; j < VL; ++j) expsum(VR + j, lds_slot(j));
+        }
+        // the lanes' states: a butterfly per wave, then the waves in order
+        // through LDS (double-buffered: one barrier per row)
+        st = xe_group<64>(st);
+        const int buf = it & 1;
+        if (lane == 0) red[buf][wave] = st;
+        __syncthreads();
+        st = red[buf][0];
+#pragma unroll
+        for (int k = 1; k < NW; ++k) st = xe_merge(st, red[buf][k]);
+        // loss = log Z + (1 - a)(m - x_label) + a (m - sum x / V)
+        if (tid == 0) {
+            const float alpha = sreg(a.alpha);
+            const float l = logf(st.z) + (1.0f - alpha) * (st.mx - xl) +
+                            alpha * (st.mx - st.sx * sreg(a.inv_v));
+            a.loss[row] = ignored ? 0.0f : (bad ? NAN : l);
+        }
+        if (!grad) continue;
+        // dx = scale * (q - p) = exp(x - m) * (scale / Z) - scale * p with
+        // p = a/V off the label and a/V + 1 - a at it
+        keep_packed(xr);
+        const float nm = -st.mx * kLog2e;
+        const float alpha = sreg(a.alpha);
+        const float scale = sreg(a.scale);
+        const float siz = scale * (1.0f / st.z);
+        const float pa = alpha * sreg(a.inv_v);
+        const float nsp = -(scale * pa);
+        const float nsl = -(scale * (pa + (1.0f - alpha)));
+        const bool no_target = ignored || bad;
+        const float fill = ignored ? 0.0f : NAN;   // rows without a target
+        const int rel = opaque((int)(no_target ? -1 : label) - base);
+        limits();
+        const rsrc_t vd = row_view<S>(a.dx, row, 1, ld);
+        auto grad_slot = [&](int i, const u32x4& v) {
+            float f[E], out[E];
+            S::unpack(v, f);
+            if (!no_target) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[e] = fmaf(exp2_(fmaf(f[e], kLog2e, nm)), siz, nsp);
+                if ((unsigned)(rel - i * W) < (unsigned)E) {   // the label is here
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (i * W + e == rel) out[e] = fmaf(exp2_(fmaf(f[e], kLog2e, nm)), siz, nsl);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[e] = fill;
+            }
+            if (i >= nfull) {   // padding columns get 0
+                const int r = L - i * W;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (e >= r) out[e] = 0.0f;
+            }
+            buf_store_nt(S::pack(out), vd, slot_off(i, ns));
+        };
+#pragma unroll
+        for (int i = 0; i < VR; ++i) grad_slot(i, xr[i]);
+#pragma unroll
+        for (int j = 0; j < VL; ++j) grad_slot(VR + j, lds_slot(j));
+    }
+}
+
 #define MBROW_CAT2(a, b) a##b
 #define MBROW_CAT(a, b) MBROW_CAT2(a, b)
 hipError_t MBROW_CAT(launch_xent_, MBROW_SUFFIX)(const Path& p, const XeArgs& a, hipStream_t s) {
     return p.vec ? dispatch<true>(p, a, s) : dispatch<false>(p, a, s);
+}
+hipError_t MBROW_CAT(launch_xent_lds_, MBROW_SUFFIX)(const XeArgs& a, hipStream_t s) {
+    const void* k = reinterpret_cast<const void*>(&xent_lds_kernel<St>);
+    constexpr int lanes = XeLds<St::E>::LANES;
+    const int64_t grid = persistent_grid(k, lanes, a.rows);
+    hipLaunchKernelGGL((xent_lds_kernel<St>), dim3((unsigned)grid), dim3(lanes), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace mbrow

@@ -152,8 +152,10 @@ def test_add_rmsnorm(orc, cols):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("cols", [1000, 50257])
+@pytest.mark.parametrize("cols", [1000, 50257, 120000, 200000])
 def test_cross_entropy(orc, dtype, cols, two_pass):
+    # 120000 fp32 and 200000 bf16 columns: rows held in registers and LDS
+    # (column -1 of a poisoned row lies in an LDS slot)
     case(f"cross-entropy with non-finite rows {ROWS}x{cols} {dtype} two_pass={two_pass}")
     x = dev(synth.layer_inputs(ROWS, cols, dtype, seed=34, names=("x",)))["x"]
     poison(x)

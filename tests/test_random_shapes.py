@@ -141,7 +141,9 @@ def test_random_staged_and_two_pass_rows(orc, idx):
     take by default, on seeded random widths, dtypes and alignments: the
     LayerNorm forward + backward (fp32 forwards from 6145 columns, every
     dtype past 16384, up to the backward's limit), the fused forward up to
-    65536 columns, the two-pass rows up to 300000 columns."""
+    65536 columns, the rows past the register layouts up to 300000 columns
+    (aligned cross-entropy rows of up to 131072 fp32 / 262144 16-bit classes
+    are held in registers and LDS, the rest take the two-pass walk)."""
     g = np.random.default_rng([9001, idx])
     dtype = DTYPES[int(g.integers(0, 3))]
     mis = bool(g.integers(0, 3) == 0)

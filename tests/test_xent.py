@@ -163,3 +163,113 @@ def test_empty():
     loss, dx = mb.cross_entropy_fwd_bwd(x, lab)
     torch.cuda.synchronize()
     assert loss.shape == (0,) and dx.shape == (0, 100)
+
+
+# Rows past the register layouts on the vector path are held by one workgroup,
+# part of each lane's slots in registers and the rest in LDS: 16-bit rows
+# 1024 lanes x (23 + 9) slots of 8 values, fp32 rows 512 lanes x (45 + 19)
+# slots of 4.  Columns held in the register slots, and the widest row held:
+REG_COLS = {torch.float32: 512 * 45 * 4, torch.float16: 1024 * 23 * 8,
+            torch.bfloat16: 1024 * 23 * 8}
+ONCHIP_MAX = {torch.float32: 131072, torch.float16: 262144, torch.bfloat16: 262144}
+
+
+@pytest.mark.parametrize("dtype,cols,ld", [
+    (torch.float32, 65537, 65540),     # the first fp32 width past the register layouts
+    (torch.float32, 92160, 92160),     # the register slots exactly
+    (torch.float32, 92161, 92164),     # one class in an LDS slot
+    (torch.float32, 128256, 128256),   # Llama-3's vocabulary
+    (torch.float32, 131071, 131072),   # the widest fp32 row held on chip
+    (torch.bfloat16, 163841, 163848),  # the first 16-bit width past the register layouts
+    (torch.float16, 188416, 188416),   # the register slots exactly
+    (torch.bfloat16, 188417, 188424),  # one class in an LDS slot
+    (torch.bfloat16, 256000, 256000),
+    (torch.float16, 250001, 262144),   # padding up to the widest 16-bit row
+    (torch.bfloat16, 262144, 262144),
+])
+def test_onchip_rows(orc, dtype, cols, ld):
+    case(f"cross-entropy on chip {dtype} 24x{cols} ld {ld}")
+    run(orc, 24, cols, ld, dtype, 13, ignore=0.1, name=f"xent.onchip.{cols}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_onchip_many_rows_per_workgroup(orc, dtype):
+    # one workgroup per compute unit walks three or four rows: each row's LDS
+    # slots and cross-wave exchange reuse the previous row's
+    rows = 3 * 256 + 7
+    cols = REG_COLS[dtype] + 20000   # rows of whole 16-byte slots: the vector path
+    case(f"cross-entropy on chip {dtype} {rows}x{cols}, sampled rows")
+    g = torch.Generator(device="cuda").manual_seed(14)
+    x = (torch.randn((rows, cols), device="cuda", generator=g) * 2.0).to(dtype)
+    lab = torch.randint(0, cols, (rows,), device="cuda", generator=g, dtype=torch.int64)
+    loss, dx = mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0)
+    torch.cuda.synchronize()
+    sel = [0, 1, 255, 256, 257, 511, 512, 767, 768, rows - 1]
+    check_xent(orc, x, lab, cols, 0.1, 1.0, loss, dx, FMT[dtype], rows_sel=sel,
+               name="xent.onchip.rows")
+    # every row's loss, against the oracle's loss alone
+    loss_ref, _ = orc.cross_entropy(synth.as_f64(x), lab.cpu().numpy(), 0.1, 1.0, grad=False)
+    err = np.abs(synth.as_f64(loss) - loss_ref) / np.maximum(1.0, np.abs(loss_ref))
+    assert err.max() < 1e-4, err.max()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_onchip_label_and_maximum_in_lds_slots(orc, dtype):
+    # rows whose maximum and label lie in the LDS slots, in the register
+    # slots, and one of each
+    rows, cols = 8, ONCHIP_MAX[dtype]
+    case(f"cross-entropy on chip {dtype} {rows}x{cols}, label and maximum placed")
+    x = synth.logits(rows, cols, dtype, seed=15)
+    lab = synth.class_labels(rows, cols, seed=15)
+    hi, lo = cols - 5, REG_COLS[dtype] // 3   # an LDS column and a register column
+    for r, (cmax, clab) in enumerate([(hi, hi), (lo, lo), (hi, lo), (lo, hi)]):
+        x[r, cmax] = 12.0
+        lab[r] = clab
+    x, lab = x.to("cuda"), lab.to("cuda")
+    loss, dx = mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0)
+    torch.cuda.synchronize()
+    check_xent(orc, x, lab, cols, 0.1, 1.0, loss, dx, FMT[dtype], name="xent.onchip.placed")
+
+
+def test_onchip_ignored_invalid_in_place_and_loss_only(orc):
+    rows, cols, ld = 40, 230001, 230008
+    case(f"cross-entropy on chip bf16 {rows}x{cols}: ignored, invalid, in place, loss only")
+    x, lab, loss, dx = run(orc, rows, cols, ld, torch.bfloat16, 16, ignore=0.25,
+                           scale=1.0, name="xent.onchip.ignore")
+    ign = (lab < 0).cpu()
+    assert ign.any()
+    assert torch.all(loss.cpu()[ign] == 0) and torch.all(dx.cpu()[ign] == 0)
+    lab2 = lab.clone()
+    lab2[3] = cols
+    loss2, dx2 = mb.cross_entropy_fwd_bwd(x, lab2, cols=cols, label_smoothing=0.1,
+                                          grad_scale=1.0)
+    loss_only, none = mb.cross_entropy_fwd_bwd(x, lab, cols=cols, label_smoothing=0.1,
+                                               grad=False)
+    x3 = x.clone()
+    loss3, dx3 = mb.cross_entropy_fwd_bwd(x3, lab, cols=cols, label_smoothing=0.1,
+                                          grad_scale=1.0, dlogits=x3)
+    torch.cuda.synchronize()
+    assert torch.isnan(loss2[3]) and torch.isnan(dx2[3, :cols]).all()
+    assert torch.all(dx2[3, cols:] == 0)
+    keep = torch.ones(rows, dtype=torch.bool)
+    keep[3] = False
+    assert torch.equal(loss2.cpu()[keep], loss.cpu()[keep])
+    assert none is None and torch.equal(loss, loss_only) and torch.equal(loss, loss3)
+    assert dx3.data_ptr() == x3.data_ptr()
+    assert torch.equal(dx.view(torch.int16), dx3.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,cols", [(torch.float32, 120000), (torch.bfloat16, 240000)])
+def test_onchip_and_two_pass_paths_agree(orc, dtype, cols):
+    # the same rows on the on-chip path and forced onto the two-pass walk:
+    # both against the oracle, and their losses within float32 rounding
+    case(f"cross-entropy {dtype} 16x{cols}: on chip and two-pass")
+    x, lab, loss, dx = run(orc, 16, cols, cols, dtype, 17, scale=1.0, name="xent.onchip.ab")
+    mb.debug_force_two_pass(True)
+    try:
+        loss2, dx2 = mb.cross_entropy_fwd_bwd(x, lab, label_smoothing=0.1, grad_scale=1.0)
+        torch.cuda.synchronize()
+    finally:
+        mb.debug_force_two_pass(False)
+    check_xent(orc, x, lab, cols, 0.1, 1.0, loss2, dx2, FMT[dtype], name="xent.twopass.ab")
+    assert torch.allclose(loss, loss2, rtol=1e-5, atol=1e-5)
