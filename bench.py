@@ -917,7 +917,11 @@ def configs_report(cpp_launch: bool = True) -> None:
                  "attention softmax fwd + bwd, 16x256 rows of 32768 keys, forced onto the "
                  "two-pass path", two_pass=True)
     long_softmax(8 * 256, 131072,
-                 "attention softmax fwd + bwd, 8x256 rows of 131072 keys (two-pass path)")
+                 "attention softmax fwd + bwd, 8x256 rows of 131072 keys (forward without a mask "
+                 "or dropped copy in registers, backward two-pass)")
+    long_softmax(8 * 256, 131072,
+                 "attention softmax fwd + bwd, 8x256 rows of 131072 keys, forced onto the "
+                 "two-pass path", two_pass=True)
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")

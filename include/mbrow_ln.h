@@ -118,6 +118,12 @@ typedef enum {
  * workgroup per row beyond 16384). */
 #define LN_MAX_COLS_SOFTMAX_F32 32768
 #define LN_MAX_COLS_SOFTMAX_16 65536
+/* Widest fp16/bf16 row of attn_softmax_fwd still held in registers when the
+ * call has no mask row and no dropped copy and its rows are on the 16-byte
+ * vector path (x and y 16-byte aligned, cols * 2 a multiple of 16): 131072
+ * scores (1024 lanes x 16 slots).  Other rows past LN_MAX_COLS_SOFTMAX_16
+ * take the two-pass path. */
+#define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 131072
 /* The same for attn_softmax_bwd with fp16/bf16 storage (it holds two
  * tensors, dy and y, per row). */
 #define LN_MAX_COLS_SOFTMAX_BWD_16 49152
@@ -335,9 +341,10 @@ ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t wor
  * scale must be finite; causal 0 or 1; p in [0, 1); rows_per_mask >= 1 when
  * mask is given.  Arithmetic in float32 (exp by the device's exp2).  Rows of
  * up to LN_MAX_COLS_SOFTMAX_F32 (fp32) or LN_MAX_COLS_SOFTMAX_16 (fp16/bf16)
- * columns are held in registers (read once); wider rows, up to
- * LN_MAX_COLS_STREAM, are read twice: an online maximum/sum pass
- * ([LLMC] §6.1), then the output pass.
+ * columns are held in registers (read once), and so are fp16/bf16 rows of up
+ * to LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 columns on the vector path when mask
+ * and y_dropped are NULL; wider rows, up to LN_MAX_COLS_STREAM, are read
+ * twice: an online maximum/sum pass ([LLMC] §6.1), then the output pass.
  */
 ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
                              void* y_dropped, int64_t rows, int64_t cols, float scale,

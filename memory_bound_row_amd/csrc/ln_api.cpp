@@ -41,6 +41,8 @@ hipError_t launch_softmax_stream_bf16(bool, bool, const SmArgs&, hipStream_t);
 hipError_t launch_xent_stream_f32(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_f16(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_bf16(bool, const XeArgs&, hipStream_t);
+hipError_t launch_softmax_long_fwd_f16(int, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_long_fwd_bf16(int, const SmArgs&, hipStream_t);
 hipError_t launch_xent_lds_f32(const XeArgs&, hipStream_t);
 hipError_t launch_xent_lds_f16(const XeArgs&, hipStream_t);
 hipError_t launch_xent_lds_bf16(const XeArgs&, hipStream_t);
@@ -934,8 +936,21 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
     a.pscale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
-    if (cols > softmax_max_cols(dt, false) || force_two_pass())
-        return from_hip(launch_softmax_stream(d, vec && !force_scalar(), false, a, stream));
+    if (cols > softmax_max_cols(dt, false) || force_two_pass()) {
+        // past the register layouts: a 16-bit row without a mask row or a
+        // dropped copy is still held in registers (vector path), up to
+        // LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 columns; the rest take the
+        // two-pass walk
+        const bool vec_ok = vec && !force_scalar();
+        if (vec_ok && !force_two_pass() && dt != LN_F32 && !mask && !y_dropped &&
+            cols <= LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16) {
+            const int64_t per_lane = (a.nslots + 1023) / 1024;
+            const int v = per_lane <= 10 ? 10 : per_lane <= 12 ? 12 : per_lane <= 14 ? 14 : 16;
+            return from_hip(d == Dt::F16 ? launch_softmax_long_fwd_f16(v, a, stream)
+                                         : launch_softmax_long_fwd_bf16(v, a, stream));
+        }
+        return from_hip(launch_softmax_stream(d, vec_ok, false, a, stream));
+    }
     return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec, false), false, a, stream));
 }
 

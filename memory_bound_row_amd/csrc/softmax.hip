@@ -285,7 +285,9 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
 // column.  Each pass takes rel and the lane's byte offset through opaque(), so
 // the compiler keeps no per-slot masks or offsets across passes, and only the
 // lane's one partial slot tests elements.
-template <class S, int G, int V, bool VEC, bool BWD, bool MASK>
+// DROP = false: a forward built without the dropped copy (a.out2 must be
+// NULL), whose Philox rounds would otherwise need registers beside the row.
+template <class S, int G, int V, bool VEC, bool BWD, bool MASK, bool DROP = true>
 __global__ __launch_bounds__(G) void softmax_wide_kernel(SmArgs a) {
     constexpr int E = S::E, W = G * E, NW = G / 64;
     const int tid = threadIdx.x;
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(G) void softmax_wide_kernel(SmArgs a) {
                     }
                 }
                 store(vy, i, yv);
-                if (a.out2) {
+                if (DROP && a.out2) {
                     const int col0 = i * W + base;
                     const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
                     float dv[E];
@@ -507,15 +509,15 @@ __global__ __launch_bounds__(G) void softmax_wide_kernel(SmArgs a) {
 
 // The 16-bit backward holds dy and y packed (two tensors): up to 6 slots per
 // lane fit its registers, 8 in the forward (the scores and a mask row).
-template <int G, int V, bool VEC, bool BWD, bool MASK>
+template <int G, int V, bool VEC, bool BWD, bool MASK, bool DROP = true>
 static hipError_t launch_wide(const SmArgs& a, hipStream_t s) {
     if constexpr (BWD && St::E == 8 && G == 1024 && V > kSmWideBwdV16) {
         return hipErrorInvalidValue;   // callers send such rows to the two-pass path
     } else {
-        const void* k =
-            reinterpret_cast<const void*>(&softmax_wide_kernel<St, G, V, VEC, BWD, MASK>);
+        const void* k = reinterpret_cast<const void*>(
+            &softmax_wide_kernel<St, G, V, VEC, BWD, MASK, DROP>);
         const int64_t grid = persistent_grid(k, G, a.rows, 1);
-        hipLaunchKernelGGL((softmax_wide_kernel<St, G, V, VEC, BWD, MASK>),
+        hipLaunchKernelGGL((softmax_wide_kernel<St, G, V, VEC, BWD, MASK, DROP>),
                            dim3((unsigned)grid), dim3(G), 0, s, a);
         return hipGetLastError();
     }
@@ -528,6 +530,13 @@ static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
     if constexpr (sm_wide_layout(G, V, St::E) || (!BWD && St::E == 8 && G == 512)) {
         if constexpr (!BWD) {
             if (a.mask) return launch_wide<G, V, VEC, BWD, true>(a, s);
+            // fp32 rows without a dropped copy: the instance without Philox,
+            // in fewer registers, so two 1024-lane rows share a compute unit
+            // (1024 x 6 fp32: 148 -> 139 us at 4096 x 24576; the 16-bit
+            // layouts up to 8 slots measured 1-3 % slower so)
+            if constexpr (St::E == 4) {
+                if (!a.out2) return launch_wide<G, V, VEC, BWD, false, false>(a, s);
+            }
         }
         return launch_wide<G, V, VEC, BWD, false>(a, s);
     } else {
@@ -541,6 +550,16 @@ static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
                            dim3(SmGeometry<G>::NT), 0, s, a);
         return hipGetLastError();
     }
+}
+
+// The 16-bit forward without a mask row or a dropped copy holds one tensor
+// and needs no Philox rounds, so its rows fit 1024 lanes x up to 16 slots
+// (131072 columns) packed in registers; past LN_MAX_COLS_SOFTMAX_16 such
+// rows (vector path) take these layouts.
+template <int V>
+static hipError_t launch_long_fwd(const SmArgs& a, hipStream_t s) {
+    if (a.mask || a.out2) return hipErrorInvalidValue;   // callers send such rows elsewhere
+    return launch_wide<1024, V, true, false, false, false>(a, s);
 }
 
 template <bool VEC, bool BWD>
@@ -563,6 +582,22 @@ hipError_t MBROW_CAT(launch_softmax_, MBROW_SUFFIX)(const Path& p, bool backward
     if (backward)
         return p.vec ? dispatch<true, true>(p, a, s) : dispatch<false, true>(p, a, s);
     return p.vec ? dispatch<true, false>(p, a, s) : dispatch<false, false>(p, a, s);
+}
+// `v`: slots per lane (10, 12, 14 or 16); 16-bit storage only
+hipError_t MBROW_CAT(launch_softmax_long_fwd_, MBROW_SUFFIX)(int v, const SmArgs& a,
+                                                             hipStream_t s) {
+#if MBROW_DT == 0
+    (void)v; (void)a; (void)s;
+    return hipErrorInvalidValue;
+#else
+    switch (v) {
+    case 10: return launch_long_fwd<10>(a, s);
+    case 12: return launch_long_fwd<12>(a, s);
+    case 14: return launch_long_fwd<14>(a, s);
+    case 16: return launch_long_fwd<16>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+#endif
 }
 
 }  // namespace mbrow

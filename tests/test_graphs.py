@@ -130,10 +130,14 @@ def test_rmsnorm_in_a_graph():
     check_replays(run, [z, y, rstd, dz, dg])
 
 
-def test_cross_entropy_in_a_graph():
-    case("graph: cross-entropy, gradient over the logits")
-    R, V, LD = 256, 50257, 50304
-    x0 = synth.logits(R, LD, torch.bfloat16, seed=7).to("cuda")
+@pytest.mark.parametrize("R,V,LD,dtype", [
+    (256, 50257, 50304, torch.bfloat16),    # rows in registers
+    (520, 192000, 192000, torch.bfloat16),  # rows held in registers and LDS, 2-3 per workgroup
+    (300, 100000, 100000, torch.float32),   # the same, fp32
+])
+def test_cross_entropy_in_a_graph(R, V, LD, dtype):
+    case(f"graph: cross-entropy {R}x{V} {dtype}, gradient over the logits")
+    x0 = synth.logits(R, LD, dtype, seed=7).to("cuda")
     lab = synth.class_labels(R, V, seed=7).to("cuda")
     x = x0.clone()
     loss = torch.empty(R, dtype=torch.float32, device="cuda")

@@ -117,6 +117,27 @@ def test_forced_layouts(orc, dtype):
         mb.debug_force_path(0)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_forced_wide_layouts_without_dropped_copy(orc, dtype):
+    # forwards that write no dropped copy (fp32 wide rows take an instance
+    # built without the dropout rounds), causal and not, with the backward
+    layouts = SM_LAYOUTS_F32 if dtype == torch.float32 else SM_LAYOUTS_16
+    e = 4 if dtype == torch.float32 else 8
+    try:
+        for g, v in layouts:
+            if g < 512:
+                continue
+            cols = g * v * e - 3 * e
+            causal = v % 2 == 1
+            case(f"softmax forced {g}x{v} cols={cols} {dtype}, no dropped copy, causal={causal}")
+            mb.debug_force_path(g, v)
+            d, y, yd, dx = run(24, cols, dtype, 0.7, causal, 0.0, 5)
+            assert yd is None
+            check(orc, d, y, yd, dx, 0.7, causal, 0.0, 5, name=f"sm.plain.{g}x{v}")
+    finally:
+        mb.debug_force_path(0)
+
+
 WIDE = {torch.float32: [16385, 20000, 32767, 32768],
         torch.float16: [16385, 24577, 49152, 65536],
         torch.bfloat16: [16392, 40000, 49153, 65536]}
@@ -190,3 +211,65 @@ def test_in_place():
     dx2 = mb.attn_softmax_bwd(dy2, y2, 0.5, causal=True, p=0.1, seed=6, dx=dy2)
     torch.cuda.synchronize()
     assert torch.equal(y2, y) and torch.equal(dx2, dx)
+
+
+# 16-bit forwards without a mask row or a dropped copy stay in registers past
+# LN_MAX_COLS_SOFTMAX_16, up to LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 (1024 lanes x
+# 10, 12, 14 or 16 slots); their backward takes the two-pass path.
+PLAIN_FWD_MAX = 131072
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("cols", [65544, 81920, 98312, 114688, 120008, PLAIN_FWD_MAX])
+def test_plain_forward_long_rows(orc, dtype, cols):
+    case(f"softmax plain forward 6x{cols} {dtype} (registers), backward two-pass")
+    d, y, yd, dx = run(6, cols, dtype, 0.5, False, 0.0, 0, data_seed=cols)
+    assert yd is None
+    check(orc, d, y, yd, dx, 0.5, False, 0.0, 0, name=f"sm.plain.{cols}")
+
+
+def test_plain_forward_long_rows_many_per_workgroup_and_causal(orc):
+    # three or four rows per workgroup (one workgroup per compute unit), rows
+    # sampled; then causal rows (keys past the query are not read)
+    rows, cols = 3 * 256 + 9, 100000
+    case(f"softmax plain forward {rows}x{cols} fp16, sampled rows")
+    g = torch.Generator(device="cuda").manual_seed(31)
+    x = (torch.randn((rows, cols), device="cuda", generator=g) * 3.0).to(torch.float16)
+    y, _ = mb.attn_softmax_fwd(x, 0.25)
+    torch.cuda.synchronize()
+    sel = torch.as_tensor([0, 1, 255, 256, 511, 512, 767, 768, rows - 1], device="cuda")
+    check_softmax_fwd(orc, x[sel], y[sel], None, FMT[torch.float16], scale=0.25,
+                      name="sm.plain.rows")
+    case(f"softmax plain forward causal 40x{cols} bf16")
+    d = scores(40, cols, torch.bfloat16, 32)
+    y, _ = mb.attn_softmax_fwd(d["x"], 0.5, causal=True)
+    torch.cuda.synchronize()
+    check_softmax_fwd(orc, d["x"], y, None, FMT[torch.bfloat16], scale=0.5, causal=True,
+                      name="sm.plain.causal")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
+    # the same rows in registers and forced onto the two-pass walk; masked or
+    # dropped calls at this width take the two-pass path and are checked too
+    cols = 110000
+    case(f"softmax plain forward 8x{cols} {dtype}: registers, two-pass, mask, dropout")
+    d = scores(8, cols, dtype, 33)
+    y, _ = mb.attn_softmax_fwd(d["x"], 0.5)
+    mb.debug_force_two_pass(True)
+    try:
+        y2, _ = mb.attn_softmax_fwd(d["x"], 0.5)
+    finally:
+        mb.debug_force_two_pass(False)
+    mask = (torch.randn((1, cols), device="cuda",
+                        generator=torch.Generator(device="cuda").manual_seed(34))).to(dtype)
+    y3, _ = mb.attn_softmax_fwd(d["x"], 0.5, mask=mask, rows_per_mask=8)
+    y4, yd4 = mb.attn_softmax_fwd(d["x"], 0.5, p=0.1, seed=35, want_dropped=True)
+    torch.cuda.synchronize()
+    fmt = FMT[dtype]
+    check_softmax_fwd(orc, d["x"], y, None, fmt, scale=0.5, name="sm.plain.reg")
+    check_softmax_fwd(orc, d["x"], y2, None, fmt, scale=0.5, name="sm.plain.2pass")
+    check_softmax_fwd(orc, d["x"], y3, None, fmt, scale=0.5, mask=mask, rows_per_mask=8,
+                      name="sm.plain.mask")
+    check_softmax_fwd(orc, d["x"], y4, yd4, fmt, scale=0.5, p=0.1, seed=35,
+                      name="sm.plain.drop")
