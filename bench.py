@@ -378,7 +378,8 @@ def counter_sample() -> None:
     forward and backward (2048 x 4096 bf16), the cross-entropy (8192 x 50257
     bf16, rows of 50304), the cross-entropy over 2048 x 256000 bf16 (rows held
     in registers and LDS, then forced onto the two-pass path), and the
-    two-pass softmax over 2048 x 131072 fp16."""
+    softmax over 2048 x 131072 fp16 (the forward in registers, the backward
+    two-pass; then both forced onto the two-pass path)."""
     import torch
     import memory_bound_row_amd as mb
     from memory_bound_row_amd import synth
@@ -428,10 +429,13 @@ def counter_sample() -> None:
     d = synth.layer_inputs(2048, 131072, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
     s, dy = d["x"].to(dev), d["dy"].to(dev)
     y, ds = torch.empty_like(s), torch.empty_like(s)
-    for _ in range(3):
-        mb.attn_softmax_fwd(s, 0.125, y=y)
-        mb.attn_softmax_bwd(dy, y, 0.125, dx=ds)
-    torch.cuda.synchronize()
+    for two_pass in (False, True):
+        mb.debug_force_two_pass(two_pass)
+        for _ in range(3):
+            mb.attn_softmax_fwd(s, 0.125, y=y)
+            mb.attn_softmax_bwd(dy, y, 0.125, dx=ds)
+        torch.cuda.synchronize()
+    mb.debug_force_two_pass(False)
     print("counter sample: done", flush=True)
 
 
