@@ -42,6 +42,8 @@ hipError_t launch_xent_stream_f32(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_f16(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_bf16(bool, const XeArgs&, hipStream_t);
 hipError_t launch_softmax_long_fwd_f16(int, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_bwd_lds_f16(const SmArgs&, hipStream_t);
+hipError_t launch_softmax_bwd_lds_bf16(const SmArgs&, hipStream_t);
 hipError_t launch_softmax_long_fwd_bf16(int, const SmArgs&, hipStream_t);
 hipError_t launch_xent_lds_f32(const XeArgs&, hipStream_t);
 hipError_t launch_xent_lds_f16(const XeArgs&, hipStream_t);
@@ -985,8 +987,18 @@ ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t ro
     a.pscale = (float)(1.0 / (1.0 - (double)p));
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
-    if (cols > softmax_max_cols(dt, true) || force_two_pass())
-        return from_hip(launch_softmax_stream(d, vec && !force_scalar(), true, a, stream));
+    if (cols > softmax_max_cols(dt, true) || force_two_pass()) {
+        // past the register layouts: 16-bit rows without dropout (p rounds to
+        // 0) on the vector path are still held on chip, dy and y read once,
+        // up to LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16 columns; the rest take the
+        // two-pass walk
+        const bool vec_ok = vec && !force_scalar();
+        if (vec_ok && !force_two_pass() && dt != LN_F32 && a.thr == 0u &&
+            cols <= LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16)
+            return from_hip(d == Dt::F16 ? launch_softmax_bwd_lds_f16(a, stream)
+                                         : launch_softmax_bwd_lds_bf16(a, stream));
+        return from_hip(launch_softmax_stream(d, vec_ok, true, a, stream));
+    }
     return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec, true), true, a, stream));
 }
 

@@ -562,6 +562,116 @@ static hipError_t launch_long_fwd(const SmArgs& a, hipStream_t s) {
     return launch_wide<1024, V, true, false, false, false>(a, s);
 }
 
+// Backward rows past the register layouts without dropout (p rounds to 0:
+// every key kept), 16-bit, vector path: one 1024-lane workgroup per row
+// holds dy and y on chip and reads each once ("02 · llmc/ 的 CUDA kernel 层"
+// §3.1: what fits on chip is read once).  dy's 16 slots per lane and y's
+// first kSbYReg in registers, y's last kSbYLds in LDS, loaded straight into
+// LDS (each wave's lanes fill 64 consecutive 16-byte cells and each lane
+// reads back only its own).  The arithmetic and its order are the register
+// kernel's: s = sum g * y per lane in slot order, one butterfly per wave,
+// the waves in order; dx = scale * (y * (g - s)).  Slots out of play (past
+// the query of a causal row) read as 0 in registers and are zeroed in LDS,
+// whose cells may still hold another row's values.
+constexpr int kSbSlots = 16;   // slots per lane of each tensor (131072 16-bit keys)
+constexpr int kSbYReg = 7;     // y's slots in registers
+constexpr int kSbYLds = kSbSlots - kSbYReg;   // y's slots in LDS (144 KB)
+template <class S>
+__global__ __launch_bounds__(1024) void softmax_bwd_lds_kernel(SmArgs a) {
+    constexpr int E = S::E, G = 1024, V = kSbSlots, VY = kSbYReg, VL = kSbYLds, NW = G / 64;
+    static_assert(VY + VL == V, "y's slots: registers, then LDS");
+    __shared__ __attribute__((aligned(16))) u32x4 stage[VL][G];
+    __shared__ float red[2][NW];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = (int)a.m;
+    const int ns = (int)a.nslots;
+    // byte offset of slot i of this lane, or kOob past `nslot`, formed where
+    // it is used from an opaque copy of the lane index
+    auto slot_off = [&](int i, int nslot) {
+        const int t = opaque(tid);
+        return i * G + t < nslot ? (uint32_t)(t * 16 + i * G * 16) : kOob;
+    };
+    auto lds_slot = [&](int j) {
+        u32x4 v = stage[j][tid];
+        hold_packed(v);
+        return v;
+    };
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const int buf = it & 1;
+        // (the division by m set up per row from an opaque scalar copy, not
+        // hoisted into a vector register kept beside the row)
+        int mq = m;
+        asm volatile("" : "+s"(mq));
+        const int q = a.causal ? (int)(row % mq) : m - 1;   // last key in play
+        const int lim = q + 1 < m ? q + 1 : m;
+        const int nlive = (lim + E - 1) / E;
+        const rsrc_t vdy = row_view<S>(a.x, row, 1, m);
+        const rsrc_t vy = row_view<S>(a.y, row, 1, m);
+        u32x4 dr[V], yr[VY];
+#pragma unroll
+        for (int i = 0; i < V; ++i) dr[i] = buf_load_nt(vdy, slot_off(i, nlive));
+#pragma unroll
+        for (int i = 0; i < VY; ++i) yr[i] = buf_load_nt(vy, slot_off(i, nlive));
+        // (the previous row's cells were consumed before its stores)
+#pragma unroll
+        for (int j = 0; j < VL; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vy, (__attribute__((address_space(3))) void*)&stage[j][64 * wave], 16,
+                (int)slot_off(VY + j, nlive), 0, 0, kNt);
+        // pass 1: g = dy / (1 - p) (every key kept) and s = sum g * y over the
+        // slots in play
+        float sg = 0.0f;
+        int live = opaque(nlive - tid);   // slot i in play iff i*G < live
+        auto pass1 = [&](int i, const u32x4& y4) {
+            if (i * G < live) {
+                float dv[E], yv[E];
+                S::unpack(dr[i], dv);
+                S::unpack(y4, yv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) sg = fmaf(dv[e] * a.pscale, yv[e], sg);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < VY; ++i) pass1(i, yr[i]);
+#pragma unroll
+        for (int j = 0; j < VL; ++j) pass1(VY + j, lds_slot(j));
+        sg = group_sum<64>(sg);
+        if (lane == 0) red[buf][wave] = sg;
+        __syncthreads();
+        float r = red[buf][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = r + red[buf][w];
+        sg = r;
+        keep_packed(dr);
+        keep_packed(yr);
+        // pass 2: dx = scale * (y * (g - s)), every slot of the row written
+        const rsrc_t vdx = row_view<S>(a.out, row, 1, m);
+        live = opaque(nlive - tid);
+        auto pass2 = [&](int i, const u32x4& y4) {
+            float dv[E], yv[E], dx[E];
+            S::unpack(dr[i], dv);
+            S::unpack(y4, yv);
+            if (!(i * G < live)) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    dv[e] = 0.0f;
+                    yv[e] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) dx[e] = a.scale * (yv[e] * (dv[e] * a.pscale - sg));
+            buf_store_nt(S::pack(dx), vdx, slot_off(i, ns));
+        };
+#pragma unroll
+        for (int i = 0; i < VY; ++i) pass2(i, yr[i]);
+#pragma unroll
+        for (int j = 0; j < VL; ++j) pass2(VY + j, lds_slot(j));
+    }
+}
+
 template <bool VEC, bool BWD>
 static hipError_t dispatch(const Path& p, const SmArgs& a, hipStream_t s) {
 #define MBROW_CASE(GG, VV) \
@@ -582,6 +692,19 @@ hipError_t MBROW_CAT(launch_softmax_, MBROW_SUFFIX)(const Path& p, bool backward
     if (backward)
         return p.vec ? dispatch<true, true>(p, a, s) : dispatch<false, true>(p, a, s);
     return p.vec ? dispatch<true, false>(p, a, s) : dispatch<false, false>(p, a, s);
+}
+// the backward rows held on chip without dropout; 16-bit storage only
+hipError_t MBROW_CAT(launch_softmax_bwd_lds_, MBROW_SUFFIX)(const SmArgs& a, hipStream_t s) {
+#if MBROW_DT == 0
+    (void)a; (void)s;
+    return hipErrorInvalidValue;
+#else
+    if (a.thr != 0u) return hipErrorInvalidValue;   // callers send dropout rows elsewhere
+    const void* k = reinterpret_cast<const void*>(&softmax_bwd_lds_kernel<St>);
+    const int64_t grid = persistent_grid(k, 1024, a.rows);
+    hipLaunchKernelGGL((softmax_bwd_lds_kernel<St>), dim3((unsigned)grid), dim3(1024), 0, s, a);
+    return hipGetLastError();
+#endif
 }
 // `v`: slots per lane (10, 12, 14 or 16); 16-bit storage only
 hipError_t MBROW_CAT(launch_softmax_long_fwd_, MBROW_SUFFIX)(int v, const SmArgs& a,

@@ -215,14 +215,16 @@ def test_in_place():
 
 # 16-bit forwards without a mask row or a dropped copy stay in registers past
 # LN_MAX_COLS_SOFTMAX_16, up to LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 (1024 lanes x
-# 10, 12, 14 or 16 slots); their backward takes the two-pass path.
+# 10, 12, 14 or 16 slots); backwards without dropout are held on chip (dy in
+# registers, y in registers and LDS) past LN_MAX_COLS_SOFTMAX_BWD_16, up to
+# LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16.
 PLAIN_FWD_MAX = 131072
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("cols", [65544, 81920, 98312, 114688, 120008, PLAIN_FWD_MAX])
 def test_plain_forward_long_rows(orc, dtype, cols):
-    case(f"softmax plain forward 6x{cols} {dtype} (registers), backward two-pass")
+    case(f"softmax plain forward 6x{cols} {dtype} (registers), backward on chip")
     d, y, yd, dx = run(6, cols, dtype, 0.5, False, 0.0, 0, data_seed=cols)
     assert yd is None
     check(orc, d, y, yd, dx, 0.5, False, 0.0, 0, name=f"sm.plain.{cols}")
@@ -240,12 +242,21 @@ def test_plain_forward_long_rows_many_per_workgroup_and_causal(orc):
     sel = torch.as_tensor([0, 1, 255, 256, 511, 512, 767, 768, rows - 1], device="cuda")
     check_softmax_fwd(orc, x[sel], y[sel], None, FMT[torch.float16], scale=0.25,
                       name="sm.plain.rows")
-    case(f"softmax plain forward causal 40x{cols} bf16")
+    dy = (torch.randn((rows, cols), device="cuda", generator=g)).to(torch.float16)
+    dx = mb.attn_softmax_bwd(dy, y, 0.25)
+    torch.cuda.synchronize()
+    check_softmax_bwd(orc, dy[sel], y[sel], dx[sel], FMT[torch.float16], scale=0.25,
+                      name="sm.plain.rows.bwd")
+    case(f"softmax plain forward and backward, causal 40x{cols} bf16")
     d = scores(40, cols, torch.bfloat16, 32)
     y, _ = mb.attn_softmax_fwd(d["x"], 0.5, causal=True)
+    dx = mb.attn_softmax_bwd(d["dy"], y, 0.5, causal=True)
     torch.cuda.synchronize()
     check_softmax_fwd(orc, d["x"], y, None, FMT[torch.bfloat16], scale=0.5, causal=True,
                       name="sm.plain.causal")
+    check_softmax_bwd(orc, d["dy"], y, dx, FMT[torch.bfloat16], scale=0.5,
+                      name="sm.plain.causal.bwd")
+    assert torch.all(dx[:, 64:] == 0)
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
@@ -273,3 +284,33 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
                       name="sm.plain.mask")
     check_softmax_fwd(orc, d["x"], y4, yd4, fmt, scale=0.5, p=0.1, seed=35,
                       name="sm.plain.drop")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_plain_backward_long_rows_in_place_and_two_pass(orc, dtype):
+    # the backward held on chip: in place over dy and over y, the same rows
+    # forced onto the two-pass walk, and a call with dropout at this width
+    # (two-pass)
+    rows, cols = 10, 98304
+    case(f"softmax backward on chip {rows}x{cols} {dtype}: in place, two-pass, dropout")
+    d = scores(rows, cols, dtype, 36)
+    y, _ = mb.attn_softmax_fwd(d["x"], 0.5)
+    dx = mb.attn_softmax_bwd(d["dy"], y, 0.5)
+    dy2, y3 = d["dy"].clone(), y.clone()
+    dx2 = mb.attn_softmax_bwd(dy2, y, 0.5, dx=dy2)
+    dx3 = mb.attn_softmax_bwd(d["dy"], y3, 0.5, dx=y3)
+    mb.debug_force_two_pass(True)
+    try:
+        dx4 = mb.attn_softmax_bwd(d["dy"], y, 0.5)
+    finally:
+        mb.debug_force_two_pass(False)
+    dx5 = mb.attn_softmax_bwd(d["dy"], y, 0.5, p=0.1, seed=37)
+    torch.cuda.synchronize()
+    fmt = FMT[dtype]
+    check_softmax_bwd(orc, d["dy"], y, dx, fmt, scale=0.5, name="sm.plainbwd")
+    check_softmax_bwd(orc, d["dy"], y, dx4, fmt, scale=0.5, name="sm.plainbwd.2pass")
+    check_softmax_bwd(orc, d["dy"], y, dx5, fmt, scale=0.5, p=0.1, seed=37,
+                      name="sm.plainbwd.drop")
+    assert dx2.data_ptr() == dy2.data_ptr() and dx3.data_ptr() == y3.data_ptr()
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dx.view(torch.int16), dx3.view(torch.int16))

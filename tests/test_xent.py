@@ -222,7 +222,9 @@ def test_onchip_label_and_maximum_in_lds_slots(orc, dtype):
     x = synth.logits(rows, cols, dtype, seed=15)
     lab = synth.class_labels(rows, cols, seed=15)
     hi, lo = cols - 5, REG_COLS[dtype] // 3   # an LDS column and a register column
-    for r, (cmax, clab) in enumerate([(hi, hi), (lo, lo), (hi, lo), (lo, hi)]):
+    b = REG_COLS[dtype]                        # the first column of the first LDS slot
+    for r, (cmax, clab) in enumerate([(hi, hi), (lo, lo), (hi, lo), (lo, hi),
+                                      (b, b), (b - 1, b - 1), (b - 1, b), (cols - 1, 0)]):
         x[r, cmax] = 12.0
         lab[r] = clab
     x, lab = x.to("cuda"), lab.to("cuda")
