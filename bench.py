@@ -922,7 +922,7 @@ def configs_report(cpp_launch: bool = True) -> None:
                  "two-pass path", two_pass=True)
     long_softmax(8 * 256, 131072,
                  "attention softmax fwd + bwd, 8x256 rows of 131072 keys (forward without a mask "
-                 "or dropped copy in registers, backward two-pass)")
+                 "or dropped copy in registers, backward without dropout on chip)")
     long_softmax(8 * 256, 131072,
                  "attention softmax fwd + bwd, 8x256 rows of 131072 keys, forced onto the "
                  "two-pass path", two_pass=True)
