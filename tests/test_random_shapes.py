@@ -187,3 +187,52 @@ def test_random_staged_and_two_pass_rows(orc, idx):
         check_softmax_fwd(orc, x, y, yd, fmt, scale=0.5, p=0.1, seed=seed, name="rnd.tp_sm")
         check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, p=0.1, seed=seed, name="rnd.tp_sm_bwd")
         check_xent(orc, x, lab, cols, 0.1, 1.0, loss, dl, fmt, name="rnd.tp_xent")
+
+
+@pytest.mark.parametrize("idx", range(10))
+def test_random_rows_held_on_chip(orc, idx):
+    """Rows past the register layouts that one workgroup still holds on chip
+    and reads once, on seeded random widths (rows of whole 16-byte slots):
+    the cross-entropy in registers and LDS (up to 131072 fp32 / 262144 16-bit
+    classes), the 16-bit softmax forward without a mask or dropped copy and
+    its backward without dropout (up to 131072 columns), causal or not."""
+    g = np.random.default_rng([9100, idx])
+    rows = int(g.integers(1, 40)) if idx % 3 else int(g.integers(257, 300))
+    if idx % 2 == 0:
+        dtype = DTYPES[int(g.integers(0, 3))]
+        e = 4 if dtype == torch.float32 else 8
+        lo, hi = (65537, 131072) if e == 4 else (163841, 262144)
+        cols = int(g.integers(lo // e + 1, hi // e + 1)) * e
+        ld = min(cols + e * int(g.integers(0, 3)), hi)   # padded rows, still on chip
+        alpha = float(g.choice([0.0, 0.1, 0.5]))
+        case(f"random on-chip cross-entropy {idx}: {rows}x{cols} ld {ld} {dtype} a={alpha}")
+        x = synth.logits(rows, ld, dtype, seed=9100 + idx).to("cuda")
+        lab = synth.class_labels(rows, cols, seed=9100 + idx, ignore_frac=0.1).to("cuda")
+        loss, dl = mb.cross_entropy_fwd_bwd(x, lab, cols=cols, label_smoothing=alpha,
+                                            grad_scale=1.0)
+        torch.cuda.synchronize()
+        sel = None if rows < 64 else [0, 1, 255, 256, rows - 1]
+        check_xent(orc, x, lab, cols, alpha, 1.0, loss, dl, FMT[dtype], rows_sel=sel,
+                   name="rnd.oc_xent")
+    else:
+        dtype = (torch.float16, torch.bfloat16)[int(g.integers(0, 2))]
+        cols = int(g.integers(49153 // 8 + 1, 131072 // 8 + 1)) * 8
+        causal = bool(g.integers(0, 2))
+        case(f"random on-chip softmax {idx}: {rows}x{cols} {dtype} causal={causal}")
+        cpu = synth.layer_inputs(rows, cols, dtype, seed=9100 + idx, x_std=3.0,
+                                 names=("x", "dy"))
+        x, dy = cpu["x"].to("cuda"), cpu["dy"].to("cuda")
+        y, _ = mb.attn_softmax_fwd(x, 0.5, causal=causal)
+        dx = mb.attn_softmax_bwd(dy, y, 0.5, causal=causal)
+        torch.cuda.synchronize()
+        fmt = FMT[dtype]
+        if rows < 64:
+            check_softmax_fwd(orc, x, y, None, fmt, scale=0.5, causal=causal, name="rnd.oc_sm")
+            check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, name="rnd.oc_sm_bwd")
+        else:
+            # sampled rows (the oracle's causal query is a row's index in the
+            # tensor it is given, so causal forwards are checked whole only)
+            i = torch.as_tensor([0, 1, 255, 256, rows - 1], device="cuda")
+            if not causal:
+                check_softmax_fwd(orc, x[i], y[i], None, fmt, scale=0.5, name="rnd.oc_sm")
+            check_softmax_bwd(orc, dy[i], y[i], dx[i], fmt, scale=0.5, name="rnd.oc_sm_bwd")
