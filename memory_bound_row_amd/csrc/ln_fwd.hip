@@ -372,11 +372,14 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t s) {
     const int64_t nblk = (a.rows + Geo::ROWS - 1) / Geo::ROWS;
     // one workgroup per block for rows of one wave or less with up to 4
     // slots per lane, where three or more workgroups fit a compute unit
-    // (narrow rows: 512-1024 columns 3-12 % faster so; wider rows, and
-    // the fused kernel, whose workgroups load gamma, beta and bias once,
-    // keep the persistent walk)
-    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), Geo::NT, nblk,
-                                         G <= 64 && V <= 4 ? 3 : 0);
+    // (narrow rows: 512-1024 columns 3-12 % faster so), and for the plain
+    // forward's rows of two or four waves with every slot used (4096 16-bit
+    // / 2048 fp32 columns and twice that: 3-8 % faster so; 512-lane rows,
+    // rows with a partly used slot, and the fused kernel, whose workgroups
+    // load gamma, beta and bias once, measured slower and keep the
+    // persistent walk)
+    constexpr int dyn = G <= 64 && V <= 4 ? 3 : (!FUSED && (G == 128 || G == 256) && V == 4 ? 1 : 0);
+    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kern), Geo::NT, nblk, dyn);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Geo::NT), 0, s, a);
     return hipGetLastError();
 }
