@@ -118,17 +118,20 @@ typedef enum {
  * workgroup per row beyond 16384). */
 #define LN_MAX_COLS_SOFTMAX_F32 32768
 #define LN_MAX_COLS_SOFTMAX_16 65536
-/* Widest fp16/bf16 row of attn_softmax_fwd still held in registers when the
- * call has no mask row and no dropped copy and its rows are on the 16-byte
- * vector path (x and y 16-byte aligned, cols * 2 a multiple of 16): 131072
- * scores (1024 lanes x 16 slots).  Other rows past LN_MAX_COLS_SOFTMAX_16
- * take the two-pass path. */
+/* Widest row of attn_softmax_fwd still held in registers when the call has
+ * no mask row and no dropped copy and its rows are on the 16-byte vector
+ * path (x and y 16-byte aligned, cols * sizeof(T) a multiple of 16): 65536
+ * fp32 / 131072 fp16/bf16 scores (1024 lanes x 16 slots).  Other rows past
+ * LN_MAX_COLS_SOFTMAX_F32 / _16 take the two-pass path. */
+#define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 65536
 #define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 131072
-/* Widest fp16/bf16 row of attn_softmax_bwd held on chip (dy in registers, y
- * in registers and LDS, each read once) when the call has no dropout (p
- * below 2^-17, so that every key is kept) and its rows are on the 16-byte
- * vector path: 131072 scores.  Other rows past LN_MAX_COLS_SOFTMAX_BWD_16
- * take the two-pass path. */
+/* Widest row of attn_softmax_bwd held on chip (dy in registers, y in
+ * registers and LDS, each read once) when the call has no dropout (p below
+ * 2^-17, so that every key is kept) and its rows are on the 16-byte vector
+ * path: 65536 fp32 / 131072 fp16/bf16 scores.  Other rows past
+ * LN_MAX_COLS_SOFTMAX_F32 / LN_MAX_COLS_SOFTMAX_BWD_16 take the two-pass
+ * path. */
+#define LN_MAX_COLS_SOFTMAX_PLAIN_BWD_F32 65536
 #define LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16 131072
 /* The same for attn_softmax_bwd with fp16/bf16 storage (it holds two
  * tensors, dy and y, per row). */
@@ -347,8 +350,8 @@ ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t wor
  * scale must be finite; causal 0 or 1; p in [0, 1); rows_per_mask >= 1 when
  * mask is given.  Arithmetic in float32 (exp by the device's exp2).  Rows of
  * up to LN_MAX_COLS_SOFTMAX_F32 (fp32) or LN_MAX_COLS_SOFTMAX_16 (fp16/bf16)
- * columns are held in registers (read once), and so are fp16/bf16 rows of up
- * to LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 columns on the vector path when mask
+ * columns are held in registers (read once), and so are rows of up to
+ * LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 / _16 columns on the vector path when mask
  * and y_dropped are NULL; wider rows, up to LN_MAX_COLS_STREAM, are read
  * twice: an online maximum/sum pass ([LLMC] §6.1), then the output pass.
  */
@@ -368,9 +371,9 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
  *   dy or y).  causal = 1 skips reading the keys past the query (y = 0
  *   there, so dx = 0).  Rows wider than LN_MAX_COLS_SOFTMAX_F32 (fp32) or
  *   LN_MAX_COLS_SOFTMAX_BWD_16 (fp16/bf16), up to LN_MAX_COLS_STREAM, read dy
- *   and y twice: the dot product, then dx; fp16/bf16 rows without dropout on
- *   the vector path are held on chip and read once up to
- *   LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16.
+ *   and y twice: the dot product, then dx; rows without dropout on the
+ *   vector path are held on chip and read once up to
+ *   LN_MAX_COLS_SOFTMAX_PLAIN_BWD_F32 / _16.
  */
 ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
                              int64_t cols, float scale, int causal, float p, uint64_t seed,

@@ -41,10 +41,12 @@ hipError_t launch_softmax_stream_bf16(bool, bool, const SmArgs&, hipStream_t);
 hipError_t launch_xent_stream_f32(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_f16(bool, const XeArgs&, hipStream_t);
 hipError_t launch_xent_stream_bf16(bool, const XeArgs&, hipStream_t);
+hipError_t launch_softmax_long_fwd_f32(int, const SmArgs&, hipStream_t);
 hipError_t launch_softmax_long_fwd_f16(int, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_long_fwd_bf16(int, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_bwd_lds_f32(const SmArgs&, hipStream_t);
 hipError_t launch_softmax_bwd_lds_f16(const SmArgs&, hipStream_t);
 hipError_t launch_softmax_bwd_lds_bf16(const SmArgs&, hipStream_t);
-hipError_t launch_softmax_long_fwd_bf16(int, const SmArgs&, hipStream_t);
 hipError_t launch_xent_lds_f32(const XeArgs&, hipStream_t);
 hipError_t launch_xent_lds_f16(const XeArgs&, hipStream_t);
 hipError_t launch_xent_lds_bf16(const XeArgs&, hipStream_t);
@@ -939,17 +941,19 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
     if (cols > softmax_max_cols(dt, false) || force_two_pass()) {
-        // past the register layouts: a 16-bit row without a mask row or a
-        // dropped copy is still held in registers (vector path), up to
-        // LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 columns; the rest take the
+        // past the register layouts: a row without a mask row or a dropped
+        // copy is still held in registers (vector path), up to
+        // LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 / _F32 columns; the rest take the
         // two-pass walk
         const bool vec_ok = vec && !force_scalar();
-        if (vec_ok && !force_two_pass() && dt != LN_F32 && !mask && !y_dropped &&
-            cols <= LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16) {
+        const int64_t plain_max =
+            dt == LN_F32 ? LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 : LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16;
+        if (vec_ok && !force_two_pass() && !mask && !y_dropped && cols <= plain_max) {
             const int64_t per_lane = (a.nslots + 1023) / 1024;
             const int v = per_lane <= 10 ? 10 : per_lane <= 12 ? 12 : per_lane <= 14 ? 14 : 16;
-            return from_hip(d == Dt::F16 ? launch_softmax_long_fwd_f16(v, a, stream)
-                                         : launch_softmax_long_fwd_bf16(v, a, stream));
+            return from_hip(d == Dt::F32   ? launch_softmax_long_fwd_f32(v, a, stream)
+                            : d == Dt::F16 ? launch_softmax_long_fwd_f16(v, a, stream)
+                                           : launch_softmax_long_fwd_bf16(v, a, stream));
         }
         return from_hip(launch_softmax_stream(d, vec_ok, false, a, stream));
     }
@@ -988,15 +992,17 @@ ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t ro
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
     if (cols > softmax_max_cols(dt, true) || force_two_pass()) {
-        // past the register layouts: 16-bit rows without dropout (p rounds to
-        // 0) on the vector path are still held on chip, dy and y read once,
-        // up to LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16 columns; the rest take the
+        // past the register layouts: rows without dropout (p rounds to 0) on
+        // the vector path are still held on chip, dy and y read once, up to
+        // LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16 / _F32 columns; the rest take the
         // two-pass walk
         const bool vec_ok = vec && !force_scalar();
-        if (vec_ok && !force_two_pass() && dt != LN_F32 && a.thr == 0u &&
-            cols <= LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16)
-            return from_hip(d == Dt::F16 ? launch_softmax_bwd_lds_f16(a, stream)
-                                         : launch_softmax_bwd_lds_bf16(a, stream));
+        const int64_t plain_max =
+            dt == LN_F32 ? LN_MAX_COLS_SOFTMAX_PLAIN_BWD_F32 : LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16;
+        if (vec_ok && !force_two_pass() && a.thr == 0u && cols <= plain_max)
+            return from_hip(d == Dt::F32   ? launch_softmax_bwd_lds_f32(a, stream)
+                            : d == Dt::F16 ? launch_softmax_bwd_lds_f16(a, stream)
+                                           : launch_softmax_bwd_lds_bf16(a, stream));
         return from_hip(launch_softmax_stream(d, vec_ok, true, a, stream));
     }
     return from_hip(launch_softmax(d, pick_softmax_path(d, cols, vec, true), true, a, stream));

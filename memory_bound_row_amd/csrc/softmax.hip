@@ -552,10 +552,10 @@ static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
     }
 }
 
-// The 16-bit forward without a mask row or a dropped copy holds one tensor
-// and needs no Philox rounds, so its rows fit 1024 lanes x up to 16 slots
-// (131072 columns) packed in registers; past LN_MAX_COLS_SOFTMAX_16 such
-// rows (vector path) take these layouts.
+// The forward without a mask row or a dropped copy holds one tensor and
+// needs no Philox rounds, so its rows fit 1024 lanes x up to 16 slots
+// (131072 16-bit / 65536 fp32 columns) packed in registers; past
+// LN_MAX_COLS_SOFTMAX_16 / _F32 such rows (vector path) take these layouts.
 template <int V>
 static hipError_t launch_long_fwd(const SmArgs& a, hipStream_t s) {
     if (a.mask || a.out2) return hipErrorInvalidValue;   // callers send such rows elsewhere
@@ -563,7 +563,7 @@ static hipError_t launch_long_fwd(const SmArgs& a, hipStream_t s) {
 }
 
 // Backward rows past the register layouts without dropout (p rounds to 0:
-// every key kept), 16-bit, vector path: one 1024-lane workgroup per row
+// every key kept), vector path: one 1024-lane workgroup per row
 // holds dy and y on chip and reads each once ("02 · llmc/ 的 CUDA kernel 层"
 // §3.1: what fits on chip is read once).  dy's 16 slots per lane and y's
 // first kSbYReg in registers, y's last kSbYLds in LDS, loaded straight into
@@ -573,7 +573,7 @@ static hipError_t launch_long_fwd(const SmArgs& a, hipStream_t s) {
 // the waves in order; dx = scale * (y * (g - s)).  Slots out of play (past
 // the query of a causal row) read as 0 in registers and are zeroed in LDS,
 // whose cells may still hold another row's values.
-constexpr int kSbSlots = 16;   // slots per lane of each tensor (131072 16-bit keys)
+constexpr int kSbSlots = 16;   // slots per lane of each tensor (131072 16-bit / 65536 fp32 keys)
 constexpr int kSbYReg = 7;     // y's slots in registers
 constexpr int kSbYLds = kSbSlots - kSbYReg;   // y's slots in LDS (144 KB)
 template <class S>
@@ -693,26 +693,17 @@ hipError_t MBROW_CAT(launch_softmax_, MBROW_SUFFIX)(const Path& p, bool backward
         return p.vec ? dispatch<true, true>(p, a, s) : dispatch<false, true>(p, a, s);
     return p.vec ? dispatch<true, false>(p, a, s) : dispatch<false, false>(p, a, s);
 }
-// the backward rows held on chip without dropout; 16-bit storage only
+// the backward rows held on chip without dropout
 hipError_t MBROW_CAT(launch_softmax_bwd_lds_, MBROW_SUFFIX)(const SmArgs& a, hipStream_t s) {
-#if MBROW_DT == 0
-    (void)a; (void)s;
-    return hipErrorInvalidValue;
-#else
     if (a.thr != 0u) return hipErrorInvalidValue;   // callers send dropout rows elsewhere
     const void* k = reinterpret_cast<const void*>(&softmax_bwd_lds_kernel<St>);
     const int64_t grid = persistent_grid(k, 1024, a.rows);
     hipLaunchKernelGGL((softmax_bwd_lds_kernel<St>), dim3((unsigned)grid), dim3(1024), 0, s, a);
     return hipGetLastError();
-#endif
 }
-// `v`: slots per lane (10, 12, 14 or 16); 16-bit storage only
+// `v`: slots per lane (10, 12, 14 or 16)
 hipError_t MBROW_CAT(launch_softmax_long_fwd_, MBROW_SUFFIX)(int v, const SmArgs& a,
                                                              hipStream_t s) {
-#if MBROW_DT == 0
-    (void)v; (void)a; (void)s;
-    return hipErrorInvalidValue;
-#else
     switch (v) {
     case 10: return launch_long_fwd<10>(a, s);
     case 12: return launch_long_fwd<12>(a, s);
@@ -720,7 +711,6 @@ hipError_t MBROW_CAT(launch_softmax_long_fwd_, MBROW_SUFFIX)(int v, const SmArgs
     case 16: return launch_long_fwd<16>(a, s);
     default: return hipErrorInvalidValue;
     }
-#endif
 }
 
 }  // namespace mbrow

@@ -194,8 +194,9 @@ def test_random_rows_held_on_chip(orc, idx):
     """Rows past the register layouts that one workgroup still holds on chip
     and reads once, on seeded random widths (rows of whole 16-byte slots):
     the cross-entropy in registers and LDS (up to 131072 fp32 / 262144 16-bit
-    classes), the 16-bit softmax forward without a mask or dropped copy and
-    its backward without dropout (up to 131072 columns), causal or not."""
+    classes), the softmax forward without a mask or dropped copy and its
+    backward without dropout (up to 65536 fp32 / 131072 16-bit columns),
+    causal or not."""
     g = np.random.default_rng([9100, idx])
     rows = int(g.integers(1, 40)) if idx % 3 else int(g.integers(257, 300))
     if idx % 2 == 0:
@@ -215,8 +216,10 @@ def test_random_rows_held_on_chip(orc, idx):
         check_xent(orc, x, lab, cols, alpha, 1.0, loss, dl, FMT[dtype], rows_sel=sel,
                    name="rnd.oc_xent")
     else:
-        dtype = (torch.float16, torch.bfloat16)[int(g.integers(0, 2))]
-        cols = int(g.integers(49153 // 8 + 1, 131072 // 8 + 1)) * 8
+        dtype = DTYPES[int(g.integers(0, 3))]
+        e = 4 if dtype == torch.float32 else 8
+        lo, hi = (32768, 65536) if e == 4 else (49152, 131072)
+        cols = int(g.integers(lo // e + 1, hi // e + 1)) * e
         causal = bool(g.integers(0, 2))
         case(f"random on-chip softmax {idx}: {rows}x{cols} {dtype} causal={causal}")
         cpu = synth.layer_inputs(rows, cols, dtype, seed=9100 + idx, x_std=3.0,

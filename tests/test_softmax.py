@@ -230,6 +230,15 @@ def test_plain_forward_long_rows(orc, dtype, cols):
     check(orc, d, y, yd, dx, 0.5, False, 0.0, 0, name=f"sm.plain.{cols}")
 
 
+@pytest.mark.parametrize("cols", [32772, 40960, 49152, 57344, 60004, 65536])
+def test_plain_long_rows_fp32(orc, cols):
+    # fp32 rows past LN_MAX_COLS_SOFTMAX_F32: forward in registers without a
+    # mask or dropped copy, backward on chip without dropout (up to 65536)
+    case(f"softmax plain fp32 6x{cols}: forward in registers, backward on chip")
+    d, y, yd, dx = run(6, cols, torch.float32, 0.5, False, 0.0, 0, data_seed=cols)
+    check(orc, d, y, yd, dx, 0.5, False, 0.0, 0, name=f"sm.plain32.{cols}")
+
+
 def test_plain_forward_long_rows_many_per_workgroup_and_causal(orc):
     # three or four rows per workgroup (one workgroup per compute unit), rows
     # sampled; then causal rows (keys past the query are not read)
@@ -286,12 +295,12 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
                       name="sm.plain.drop")
 
 
-@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_plain_backward_long_rows_in_place_and_two_pass(orc, dtype):
     # the backward held on chip: in place over dy and over y, the same rows
     # forced onto the two-pass walk, and a call with dropout at this width
     # (two-pass)
-    rows, cols = 10, 98304
+    rows, cols = 10, (49152 if dtype == torch.float32 else 98304)
     case(f"softmax backward on chip {rows}x{cols} {dtype}: in place, two-pass, dropout")
     d = scores(rows, cols, dtype, 36)
     y, _ = mb.attn_softmax_fwd(d["x"], 0.5)
@@ -312,5 +321,6 @@ def test_plain_backward_long_rows_in_place_and_two_pass(orc, dtype):
     check_softmax_bwd(orc, d["dy"], y, dx5, fmt, scale=0.5, p=0.1, seed=37,
                       name="sm.plainbwd.drop")
     assert dx2.data_ptr() == dy2.data_ptr() and dx3.data_ptr() == y3.data_ptr()
-    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
-    assert torch.equal(dx.view(torch.int16), dx3.view(torch.int16))
+    ibits = torch.int32 if dtype == torch.float32 else torch.int16
+    assert torch.equal(dx.view(ibits), dx2.view(ibits))
+    assert torch.equal(dx.view(ibits), dx3.view(ibits))
