@@ -379,7 +379,8 @@ def counter_sample() -> None:
     bf16, rows of 50304), the cross-entropy over 2048 x 256000 bf16 (rows held
     in registers and LDS, then forced onto the two-pass path), and the
     softmax over 2048 x 131072 fp16 (the forward in registers, the backward
-    two-pass; then both forced onto the two-pass path)."""
+    without and with dropout, p = 0.1, held on chip; then all three forced
+    onto the two-pass path)."""
     import torch
     import memory_bound_row_amd as mb
     from memory_bound_row_amd import synth
@@ -434,6 +435,8 @@ def counter_sample() -> None:
         for _ in range(3):
             mb.attn_softmax_fwd(s, 0.125, y=y)
             mb.attn_softmax_bwd(dy, y, 0.125, dx=ds)
+        for _ in range(3):
+            mb.attn_softmax_bwd(dy, y, 0.125, p=0.1, seed=SEED, dx=ds)
         torch.cuda.synchronize()
     mb.debug_force_two_pass(False)
     print("counter sample: done", flush=True)
@@ -457,10 +460,11 @@ def configs_report(cpp_launch: bool = True) -> None:
         the gradient in its own buffer and over the logits;
       * long softmax rows, fp16: 16x256 rows of 32768 keys in the register
         layouts and forced onto the two-pass path, and 8x256 rows of
-        131072 keys (two-pass path), and the cross-entropy over a
-        256000-class bf16 vocabulary at 2048 tokens (two-pass path); the
-        algorithmic bytes count one read and one write, though the two-pass
-        path reads each row twice;
+        131072 keys (held on chip; the backward also with dropout) and
+        forced onto the two-pass path, and the cross-entropy over a
+        256000-class bf16 vocabulary at 2048 tokens (held on chip, then
+        forced onto the two-pass path); the algorithmic bytes count one read
+        and one write, though the two-pass path reads each row twice;
       * 64x768 fp32 forward + backward (launch-bound): microseconds per pass;
       * 16384x1024 bf16 backward (dx, dgamma, dbeta), rotated past the cache;
       * wide and ragged rows, fp32 and bf16: 4096x16384 and 65536x1000
@@ -882,7 +886,7 @@ def configs_report(cpp_launch: bool = True) -> None:
     # softmax over long rows: the register layouts (32768 keys; also forced
     # onto the two-pass path, for comparison) and the two-pass path past them
     # (131072 keys)
-    def long_softmax(rows, L, label, two_pass=False):
+    def long_softmax(rows, L, label, two_pass=False, p=0.0):
         d = synth.layer_inputs(rows, L, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
         a = {"x": d["x"].to(dev), "dy": d["dy"].to(dev)}
         del d
@@ -893,7 +897,7 @@ def configs_report(cpp_launch: bool = True) -> None:
             mb.attn_softmax_fwd(a["x"], 0.125, y=a["y"])
 
         def lb(i):
-            mb.attn_softmax_bwd(a["dy"], a["y"], 0.125, dx=a["dx"])
+            mb.attn_softmax_bwd(a["dy"], a["y"], 0.125, p=p, seed=SEED, dx=a["dx"])
 
         mb.debug_force_two_pass(two_pass)
         try:
@@ -908,7 +912,7 @@ def configs_report(cpp_launch: bool = True) -> None:
             mb.debug_force_two_pass(False)
         t = rows * L * 2
         emit({"workload": label, "rows": rows, "cols": L, "storage": "float16",
-              "fwd_bytes": 2 * t, "fwd_us": round(msf * 1e3, 3),
+              "bwd_dropout": p, "fwd_bytes": 2 * t, "fwd_us": round(msf * 1e3, 3),
               "fwd_GBps": round(2 * t / (msf * 1e-3) / 1e9, 1),
               "bwd_bytes": 3 * t, "bwd_us": round(msb * 1e3, 3),
               "bwd_GBps": round(3 * t / (msb * 1e-3) / 1e9, 1)})
@@ -926,6 +930,12 @@ def configs_report(cpp_launch: bool = True) -> None:
     long_softmax(8 * 256, 131072,
                  "attention softmax fwd + bwd, 8x256 rows of 131072 keys, forced onto the "
                  "two-pass path", two_pass=True)
+    long_softmax(8 * 256, 131072,
+                 "attention softmax fwd + bwd with dropout p = 0.1 in the backward, 8x256 rows "
+                 "of 131072 keys (both on chip)", p=0.1)
+    long_softmax(8 * 256, 131072,
+                 "attention softmax fwd + bwd with dropout p = 0.1 in the backward, 8x256 rows "
+                 "of 131072 keys, forced onto the two-pass path", two_pass=True, p=0.1)
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")

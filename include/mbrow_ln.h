@@ -126,11 +126,10 @@ typedef enum {
 #define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 65536
 #define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 131072
 /* Widest row of attn_softmax_bwd held on chip (dy in registers, y in
- * registers and LDS, each read once) when the call has no dropout (p below
- * 2^-17, so that every key is kept) and its rows are on the 16-byte vector
- * path: 65536 fp32 / 131072 fp16/bf16 scores.  Other rows past
- * LN_MAX_COLS_SOFTMAX_F32 / LN_MAX_COLS_SOFTMAX_BWD_16 take the two-pass
- * path. */
+ * registers and LDS, each read once, with or without dropout) when its rows
+ * are on the 16-byte vector path: 65536 fp32 / 131072 fp16/bf16 scores.
+ * Other rows past LN_MAX_COLS_SOFTMAX_F32 / LN_MAX_COLS_SOFTMAX_BWD_16 take
+ * the two-pass path. */
 #define LN_MAX_COLS_SOFTMAX_PLAIN_BWD_F32 65536
 #define LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16 131072
 /* The same for attn_softmax_bwd with fp16/bf16 storage (it holds two
@@ -371,9 +370,9 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
  *   dy or y).  causal = 1 skips reading the keys past the query (y = 0
  *   there, so dx = 0).  Rows wider than LN_MAX_COLS_SOFTMAX_F32 (fp32) or
  *   LN_MAX_COLS_SOFTMAX_BWD_16 (fp16/bf16), up to LN_MAX_COLS_STREAM, read dy
- *   and y twice: the dot product, then dx; rows without dropout on the
- *   vector path are held on chip and read once up to
- *   LN_MAX_COLS_SOFTMAX_PLAIN_BWD_F32 / _16.
+ *   and y twice: the dot product, then dx; rows on the vector path are
+ *   held on chip and read once up to LN_MAX_COLS_SOFTMAX_PLAIN_BWD_F32 / _16
+ *   (with dropout, the keep bits are regenerated from the seed on chip).
  */
 ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t rows,
                              int64_t cols, float scale, int causal, float p, uint64_t seed,

@@ -992,14 +992,13 @@ ln_status_t attn_softmax_bwd(const void* dy, const void* y, void* dx, int64_t ro
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
     if (cols > softmax_max_cols(dt, true) || force_two_pass()) {
-        // past the register layouts: rows without dropout (p rounds to 0) on
-        // the vector path are still held on chip, dy and y read once, up to
-        // LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16 / _F32 columns; the rest take the
-        // two-pass walk
+        // past the register layouts: rows on the vector path are still held
+        // on chip, dy and y read once, up to LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16
+        // / _F32 columns; the rest take the two-pass walk
         const bool vec_ok = vec && !force_scalar();
         const int64_t plain_max =
             dt == LN_F32 ? LN_MAX_COLS_SOFTMAX_PLAIN_BWD_F32 : LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16;
-        if (vec_ok && !force_two_pass() && a.thr == 0u && cols <= plain_max)
+        if (vec_ok && !force_two_pass() && cols <= plain_max)
             return from_hip(d == Dt::F32   ? launch_softmax_bwd_lds_f32(a, stream)
                             : d == Dt::F16 ? launch_softmax_bwd_lds_f16(a, stream)
                                            : launch_softmax_bwd_lds_bf16(a, stream));

@@ -562,21 +562,37 @@ static hipError_t launch_long_fwd(const SmArgs& a, hipStream_t s) {
     return launch_wide<1024, V, true, false, false, false>(a, s);
 }
 
-// Backward rows past the register layouts without dropout (p rounds to 0:
-// every key kept), vector path: one 1024-lane workgroup per row
-// holds dy and y on chip and reads each once ("02 · llmc/ 的 CUDA kernel 层"
-// §3.1: what fits on chip is read once).  dy's 16 slots per lane and y's
-// first kSbYReg in registers, y's last kSbYLds in LDS, loaded straight into
-// LDS (each wave's lanes fill 64 consecutive 16-byte cells and each lane
-// reads back only its own).  The arithmetic and its order are the register
-// kernel's: s = sum g * y per lane in slot order, one butterfly per wave,
-// the waves in order; dx = scale * (y * (g - s)).  Slots out of play (past
-// the query of a causal row) read as 0 in registers and are zeroed in LDS,
-// whose cells may still hold another row's values.
+// dy's packed slot with the elements that dropout dropped set to +0 (the
+// keep bits from the words of the slot's 8-column group), so that
+// dy * (1/(1-p)) afterwards is exactly keep ? dy / (1 - p) : 0.
+template <class S>
+__device__ __forceinline__ u32x4 zero_dropped(u32x4 v, const u32x4& w, int col0, uint32_t thr) {
+    constexpr int E = S::E, PER = E / 4;   // elements per 32-bit word
+    constexpr uint32_t FIELD = PER == 1 ? ~0u : 0xffffu;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (!kept<E>(w, col0, e, thr)) v[e / PER] &= ~(FIELD << ((e % PER) * (32 / PER)));
+    return v;
+}
+
+// Backward rows past the register layouts, vector path: one 1024-lane
+// workgroup per row holds dy and y on chip and reads each once
+// ("02 · llmc/ 的 CUDA kernel 层" §3.1: what fits on chip is read once).
+// dy's 16 slots per lane and y's first kSbYReg in registers, y's last
+// kSbYLds in LDS, loaded straight into LDS (each wave's lanes fill 64
+// consecutive 16-byte cells and each lane reads back only its own).  The
+// arithmetic and its order are the register kernel's: s = sum g * y per lane
+// in slot order, one butterfly per wave, the waves in order;
+// dx = scale * (y * (g - s)).  With dropout (DROP), pass 1 regenerates each
+// slot's keep bits from the seed and clears the dropped elements of dy in
+// its registers, which then give g = 0 in both passes: no keep bits are held
+// beside the row.  Slots out of play (past the query of a causal row) read
+// as 0 in registers and are zeroed in LDS, whose cells may still hold
+// another row's values.
 constexpr int kSbSlots = 16;   // slots per lane of each tensor (131072 16-bit / 65536 fp32 keys)
 constexpr int kSbYReg = 7;     // y's slots in registers
 constexpr int kSbYLds = kSbSlots - kSbYReg;   // y's slots in LDS (144 KB)
-template <class S>
+template <class S, bool DROP>
 __global__ __launch_bounds__(1024) void softmax_bwd_lds_kernel(SmArgs a) {
     constexpr int E = S::E, G = 1024, V = kSbSlots, VY = kSbYReg, VL = kSbYLds, NW = G / 64;
     static_assert(VY + VL == V, "y's slots: registers, then LDS");
@@ -621,10 +637,24 @@ __global__ __launch_bounds__(1024) void softmax_bwd_lds_kernel(SmArgs a) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 vy, (__attribute__((address_space(3))) void*)&stage[j][64 * wave], 16,
                 (int)slot_off(VY + j, nlive), 0, 0, kNt);
-        // pass 1: g = dy / (1 - p) (every key kept) and s = sum g * y over the
+        // pass 1: g = keep ? dy / (1 - p) : 0 and s = sum g * y over the
         // slots in play
         float sg = 0.0f;
         int live = opaque(nlive - tid);   // slot i in play iff i*G < live
+        if constexpr (DROP) {
+            // (seed and threshold from opaque scalar copies per row, so that
+            // no vector copy of them is hoisted out of the row loop)
+            uint32_t slo = a.seed_lo, shi = a.seed_hi, thr = a.thr;
+            asm volatile("" : "+s"(slo), "+s"(shi), "+s"(thr));
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                if (i * G < live) {
+                    const int col0 = (i * G + opaque(tid)) * E;
+                    const u32x4 w = dropout_words(row, col0, slo, shi, thr);
+                    dr[i] = zero_dropped<S>(dr[i], w, col0, thr);
+                }
+            }
+        }
         auto pass1 = [&](int i, const u32x4& y4) {
             if (i * G < live) {
                 float dv[E], yv[E];
@@ -693,13 +723,17 @@ hipError_t MBROW_CAT(launch_softmax_, MBROW_SUFFIX)(const Path& p, bool backward
         return p.vec ? dispatch<true, true>(p, a, s) : dispatch<false, true>(p, a, s);
     return p.vec ? dispatch<true, false>(p, a, s) : dispatch<false, false>(p, a, s);
 }
-// the backward rows held on chip without dropout
-hipError_t MBROW_CAT(launch_softmax_bwd_lds_, MBROW_SUFFIX)(const SmArgs& a, hipStream_t s) {
-    if (a.thr != 0u) return hipErrorInvalidValue;   // callers send dropout rows elsewhere
-    const void* k = reinterpret_cast<const void*>(&softmax_bwd_lds_kernel<St>);
+// the backward rows held on chip, with or without dropout
+template <bool DROP>
+static hipError_t launch_bwd_lds(const SmArgs& a, hipStream_t s) {
+    const void* k = reinterpret_cast<const void*>(&softmax_bwd_lds_kernel<St, DROP>);
     const int64_t grid = persistent_grid(k, 1024, a.rows);
-    hipLaunchKernelGGL((softmax_bwd_lds_kernel<St>), dim3((unsigned)grid), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL((softmax_bwd_lds_kernel<St, DROP>), dim3((unsigned)grid), dim3(1024), 0, s,
+                       a);
     return hipGetLastError();
+}
+hipError_t MBROW_CAT(launch_softmax_bwd_lds_, MBROW_SUFFIX)(const SmArgs& a, hipStream_t s) {
+    return a.thr != 0u ? launch_bwd_lds<true>(a, s) : launch_bwd_lds<false>(a, s);
 }
 // `v`: slots per lane (10, 12, 14 or 16)
 hipError_t MBROW_CAT(launch_softmax_long_fwd_, MBROW_SUFFIX)(int v, const SmArgs& a,

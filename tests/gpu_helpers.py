@@ -179,11 +179,18 @@ def check_softmax_fwd(orc, x, y, y_dropped, fmt, scale=1.0, mask=None, rows_per_
     return assert_reports(*reps)
 
 
-def check_softmax_bwd(orc, dy, y, dx, fmt, scale=1.0, p=0.0, seed=0, name="softmax_bwd"):
-    """Reference dx from the stored dy and the GPU's stored y."""
+def check_softmax_bwd(orc, dy, y, dx, fmt, scale=1.0, p=0.0, seed=0, name="softmax_bwd",
+                      row_ids=None):
+    """Reference dx from the stored dy and the GPU's stored y.  row_ids: the
+    rows' indices in the tensor the kernel ran on, when these are sampled
+    rows (the dropout mask depends on the row index)."""
     rows, cols = y.shape
     dy64, y64 = f64(dy), f64(y)
-    keep = orc.dropout_keep(seed, p, rows, cols) if p > 0 else None
+    keep = None
+    if p > 0:
+        keep = (orc.dropout_keep(seed, p, rows, cols) if row_ids is None else
+                np.concatenate([orc.dropout_keep_rows(seed, p, int(r), 1, cols)
+                                for r in row_ids]))
     dx_ref = orc.attn_softmax_bwd(dy64, y64, keep=keep, p=p, scale=scale)
     s = 1.0 / (1.0 - np.float64(np.float32(p)))
     g = dy64 * s if keep is None else np.where(keep == 1, dy64 * s, 0.0)

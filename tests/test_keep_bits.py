@@ -20,7 +20,8 @@ kept it, independently of any tolerance:
 
 Every storage type, the full configuration shape 8192 x 1280 with the seeds 0,
 1 and 2^63 + 5, and every row layout each kernel is built with, on the vector
-and the per-element path (ragged widths)."""
+and the per-element path (ragged widths); and the softmax rows past the
+register layouts (held on chip, or read twice)."""
 import numpy as np
 import pytest
 import torch
@@ -174,3 +175,32 @@ def test_keep_bits_every_layout(orc, kernel, dtype, scalar):
                 mb.debug_force_path(0)
             _assert_bits(got, orc.dropout_keep(seed, p, rows, cols),
                          f"{kernel} {g}x{v} scalar={scalar} {dtype} seed {seed}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f16", "bf16"])
+def test_keep_bits_long_rows(orc, dtype):
+    # rows past the register layouts: the softmax backward held on chip (more
+    # rows than workgroups, so each walks several; a full row of 1024 lanes x
+    # 16 slots, one slot short, and a shorter row), then the two-pass forward
+    # and backward (forced) on the same widths
+    e = _elems(dtype)
+    full = 65536 if dtype == torch.float32 else 131072
+    shorter = 40000 if dtype == torch.float32 else 70000
+    p = 0.25
+    for rows, cols in ((2 * 256 + 3, full), (9, full - e), (9, shorter)):
+        for seed in (5, 2 ** 63 + 5):
+            case(f"keep bits softmax_bwd on chip {dtype} {rows}x{cols} seed={seed}")
+            got = softmax_backward_bits(rows, cols, dtype, p, seed)
+            _assert_bits(got, orc.dropout_keep(seed, p, rows, cols),
+                         f"softmax_bwd on chip {dtype} {rows}x{cols} seed {seed}")
+    for kernel in ("softmax_fwd", "softmax_bwd"):
+        for cols in (full - e, shorter):
+            rows, seed = 9, 2 ** 63 + 5
+            case(f"keep bits {kernel} two-pass {dtype} {rows}x{cols} seed={seed}")
+            mb.debug_force_two_pass(True)
+            try:
+                got = KERNELS[kernel](rows, cols, dtype, p, seed)
+            finally:
+                mb.debug_force_two_pass(False)
+            _assert_bits(got, orc.dropout_keep(seed, p, rows, cols),
+                         f"{kernel} two-pass {dtype} {rows}x{cols} seed {seed}")

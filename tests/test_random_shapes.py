@@ -195,8 +195,8 @@ def test_random_rows_held_on_chip(orc, idx):
     and reads once, on seeded random widths (rows of whole 16-byte slots):
     the cross-entropy in registers and LDS (up to 131072 fp32 / 262144 16-bit
     classes), the softmax forward without a mask or dropped copy and its
-    backward without dropout (up to 65536 fp32 / 131072 16-bit columns),
-    causal or not."""
+    backward with or without dropout (up to 65536 fp32 / 131072 16-bit
+    columns), causal or not."""
     g = np.random.default_rng([9100, idx])
     rows = int(g.integers(1, 40)) if idx % 3 else int(g.integers(257, 300))
     if idx % 2 == 0:
@@ -221,21 +221,27 @@ def test_random_rows_held_on_chip(orc, idx):
         lo, hi = (32768, 65536) if e == 4 else (49152, 131072)
         cols = int(g.integers(lo // e + 1, hi // e + 1)) * e
         causal = bool(g.integers(0, 2))
-        case(f"random on-chip softmax {idx}: {rows}x{cols} {dtype} causal={causal}")
+        p = float(g.choice([0.0, 0.1, 0.3]))
+        seed = int(g.integers(0, 2 ** 63)) * 2 + 1
+        case(f"random on-chip softmax {idx}: {rows}x{cols} {dtype} causal={causal} "
+             f"bwd p={p} seed={seed}")
         cpu = synth.layer_inputs(rows, cols, dtype, seed=9100 + idx, x_std=3.0,
                                  names=("x", "dy"))
         x, dy = cpu["x"].to("cuda"), cpu["dy"].to("cuda")
         y, _ = mb.attn_softmax_fwd(x, 0.5, causal=causal)
-        dx = mb.attn_softmax_bwd(dy, y, 0.5, causal=causal)
+        dx = mb.attn_softmax_bwd(dy, y, 0.5, causal=causal, p=p, seed=seed)
         torch.cuda.synchronize()
         fmt = FMT[dtype]
         if rows < 64:
             check_softmax_fwd(orc, x, y, None, fmt, scale=0.5, causal=causal, name="rnd.oc_sm")
-            check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, name="rnd.oc_sm_bwd")
+            check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, p=p, seed=seed,
+                              name="rnd.oc_sm_bwd")
         else:
             # sampled rows (the oracle's causal query is a row's index in the
             # tensor it is given, so causal forwards are checked whole only)
-            i = torch.as_tensor([0, 1, 255, 256, rows - 1], device="cuda")
+            ids = [0, 1, 255, 256, rows - 1]
+            i = torch.as_tensor(ids, device="cuda")
             if not causal:
                 check_softmax_fwd(orc, x[i], y[i], None, fmt, scale=0.5, name="rnd.oc_sm")
-            check_softmax_bwd(orc, dy[i], y[i], dx[i], fmt, scale=0.5, name="rnd.oc_sm_bwd")
+            check_softmax_bwd(orc, dy[i], y[i], dx[i], fmt, scale=0.5, p=p, seed=seed,
+                              name="rnd.oc_sm_bwd", row_ids=ids)

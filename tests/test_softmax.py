@@ -266,6 +266,12 @@ def test_plain_forward_long_rows_many_per_workgroup_and_causal(orc):
     check_softmax_bwd(orc, d["dy"], y, dx, FMT[torch.bfloat16], scale=0.5,
                       name="sm.plain.causal.bwd")
     assert torch.all(dx[:, 64:] == 0)
+    case(f"softmax backward on chip with dropout, causal 40x{cols} bf16")
+    dx = mb.attn_softmax_bwd(d["dy"], y, 0.5, causal=True, p=0.2, seed=2 ** 63 + 11)
+    torch.cuda.synchronize()
+    check_softmax_bwd(orc, d["dy"], y, dx, FMT[torch.bfloat16], scale=0.5, p=0.2,
+                      seed=2 ** 63 + 11, name="sm.plain.causal.bwd.drop")
+    assert torch.all(dx[:, 64:] == 0)
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
@@ -297,9 +303,8 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_plain_backward_long_rows_in_place_and_two_pass(orc, dtype):
-    # the backward held on chip: in place over dy and over y, the same rows
-    # forced onto the two-pass walk, and a call with dropout at this width
-    # (two-pass)
+    # the backward held on chip, without and with dropout: in place over dy
+    # and over y, and the same rows forced onto the two-pass walk
     rows, cols = 10, (49152 if dtype == torch.float32 else 98304)
     case(f"softmax backward on chip {rows}x{cols} {dtype}: in place, two-pass, dropout")
     d = scores(rows, cols, dtype, 36)
@@ -308,19 +313,28 @@ def test_plain_backward_long_rows_in_place_and_two_pass(orc, dtype):
     dy2, y3 = d["dy"].clone(), y.clone()
     dx2 = mb.attn_softmax_bwd(dy2, y, 0.5, dx=dy2)
     dx3 = mb.attn_softmax_bwd(d["dy"], y3, 0.5, dx=y3)
+    dx5 = mb.attn_softmax_bwd(d["dy"], y, 0.5, p=0.1, seed=37)
+    dy6, y7 = d["dy"].clone(), y.clone()
+    dx6 = mb.attn_softmax_bwd(dy6, y, 0.5, p=0.1, seed=37, dx=dy6)
+    dx7 = mb.attn_softmax_bwd(d["dy"], y7, 0.5, p=0.1, seed=37, dx=y7)
     mb.debug_force_two_pass(True)
     try:
         dx4 = mb.attn_softmax_bwd(d["dy"], y, 0.5)
+        dx8 = mb.attn_softmax_bwd(d["dy"], y, 0.5, p=0.1, seed=37)
     finally:
         mb.debug_force_two_pass(False)
-    dx5 = mb.attn_softmax_bwd(d["dy"], y, 0.5, p=0.1, seed=37)
     torch.cuda.synchronize()
     fmt = FMT[dtype]
     check_softmax_bwd(orc, d["dy"], y, dx, fmt, scale=0.5, name="sm.plainbwd")
     check_softmax_bwd(orc, d["dy"], y, dx4, fmt, scale=0.5, name="sm.plainbwd.2pass")
     check_softmax_bwd(orc, d["dy"], y, dx5, fmt, scale=0.5, p=0.1, seed=37,
                       name="sm.plainbwd.drop")
+    check_softmax_bwd(orc, d["dy"], y, dx8, fmt, scale=0.5, p=0.1, seed=37,
+                      name="sm.plainbwd.drop.2pass")
     assert dx2.data_ptr() == dy2.data_ptr() and dx3.data_ptr() == y3.data_ptr()
+    assert dx6.data_ptr() == dy6.data_ptr() and dx7.data_ptr() == y7.data_ptr()
     ibits = torch.int32 if dtype == torch.float32 else torch.int16
     assert torch.equal(dx.view(ibits), dx2.view(ibits))
     assert torch.equal(dx.view(ibits), dx3.view(ibits))
+    assert torch.equal(dx5.view(ibits), dx6.view(ibits))
+    assert torch.equal(dx5.view(ibits), dx7.view(ibits))
