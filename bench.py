@@ -378,9 +378,9 @@ def counter_sample() -> None:
     forward and backward (2048 x 4096 bf16), the cross-entropy (8192 x 50257
     bf16, rows of 50304), the cross-entropy over 2048 x 256000 bf16 (rows held
     in registers and LDS, then forced onto the two-pass path), and the
-    softmax over 2048 x 131072 fp16 (the forward in registers, the backward
-    without and with dropout, p = 0.1, held on chip; then all three forced
-    onto the two-pass path)."""
+    softmax over 2048 x 131072 fp16 (the forward in registers, without and
+    with the dropped copy, and the backward without and with dropout,
+    p = 0.1, held on chip; then all four forced onto the two-pass path)."""
     import torch
     import memory_bound_row_amd as mb
     from memory_bound_row_amd import synth
@@ -429,13 +429,14 @@ def counter_sample() -> None:
     del x, dx
     d = synth.layer_inputs(2048, 131072, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
     s, dy = d["x"].to(dev), d["dy"].to(dev)
-    y, ds = torch.empty_like(s), torch.empty_like(s)
+    y, ds, yd = torch.empty_like(s), torch.empty_like(s), torch.empty_like(s)
     for two_pass in (False, True):
         mb.debug_force_two_pass(two_pass)
         for _ in range(3):
             mb.attn_softmax_fwd(s, 0.125, y=y)
             mb.attn_softmax_bwd(dy, y, 0.125, dx=ds)
         for _ in range(3):
+            mb.attn_softmax_fwd(s, 0.125, p=0.1, seed=SEED, y=y, y_dropped=yd)
             mb.attn_softmax_bwd(dy, y, 0.125, p=0.1, seed=SEED, dx=ds)
         torch.cuda.synchronize()
     mb.debug_force_two_pass(False)
@@ -892,9 +893,10 @@ def configs_report(cpp_launch: bool = True) -> None:
         del d
         a["y"] = torch.empty_like(a["x"])
         a["dx"] = torch.empty_like(a["x"])
+        a["yd"] = torch.empty_like(a["x"]) if p > 0 else None
 
         def lf(i):
-            mb.attn_softmax_fwd(a["x"], 0.125, y=a["y"])
+            mb.attn_softmax_fwd(a["x"], 0.125, p=p, seed=SEED, y=a["y"], y_dropped=a["yd"])
 
         def lb(i):
             mb.attn_softmax_bwd(a["dy"], a["y"], 0.125, p=p, seed=SEED, dx=a["dx"])
@@ -911,9 +913,10 @@ def configs_report(cpp_launch: bool = True) -> None:
         finally:
             mb.debug_force_two_pass(False)
         t = rows * L * 2
+        nf = 3 if p > 0 else 2   # x read; y (and the dropped copy) written
         emit({"workload": label, "rows": rows, "cols": L, "storage": "float16",
-              "bwd_dropout": p, "fwd_bytes": 2 * t, "fwd_us": round(msf * 1e3, 3),
-              "fwd_GBps": round(2 * t / (msf * 1e-3) / 1e9, 1),
+              "dropout": p, "fwd_bytes": nf * t, "fwd_us": round(msf * 1e3, 3),
+              "fwd_GBps": round(nf * t / (msf * 1e-3) / 1e9, 1),
               "bwd_bytes": 3 * t, "bwd_us": round(msb * 1e3, 3),
               "bwd_GBps": round(3 * t / (msb * 1e-3) / 1e9, 1)})
         del a
@@ -931,11 +934,11 @@ def configs_report(cpp_launch: bool = True) -> None:
                  "attention softmax fwd + bwd, 8x256 rows of 131072 keys, forced onto the "
                  "two-pass path", two_pass=True)
     long_softmax(8 * 256, 131072,
-                 "attention softmax fwd + bwd with dropout p = 0.1 in the backward, 8x256 rows "
-                 "of 131072 keys (both on chip)", p=0.1)
+                 "attention softmax fwd (y and the dropped copy) + bwd with dropout p = 0.1, "
+                 "8x256 rows of 131072 keys (both on chip)", p=0.1)
     long_softmax(8 * 256, 131072,
-                 "attention softmax fwd + bwd with dropout p = 0.1 in the backward, 8x256 rows "
-                 "of 131072 keys, forced onto the two-pass path", two_pass=True, p=0.1)
+                 "attention softmax fwd (y and the dropped copy) + bwd with dropout p = 0.1, "
+                 "8x256 rows of 131072 keys, forced onto the two-pass path", two_pass=True, p=0.1)
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")

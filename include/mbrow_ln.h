@@ -119,10 +119,11 @@ typedef enum {
 #define LN_MAX_COLS_SOFTMAX_F32 32768
 #define LN_MAX_COLS_SOFTMAX_16 65536
 /* Widest row of attn_softmax_fwd still held in registers when the call has
- * no mask row and no dropped copy and its rows are on the 16-byte vector
- * path (x and y 16-byte aligned, cols * sizeof(T) a multiple of 16): 65536
- * fp32 / 131072 fp16/bf16 scores (1024 lanes x 16 slots).  Other rows past
- * LN_MAX_COLS_SOFTMAX_F32 / _16 take the two-pass path. */
+ * no mask row (with or without the dropped copy) and its rows are on the
+ * 16-byte vector path (x, y and y_dropped 16-byte aligned, cols * sizeof(T)
+ * a multiple of 16): 65536 fp32 / 131072 fp16/bf16 scores (1024 lanes x 16
+ * slots).  Other rows past LN_MAX_COLS_SOFTMAX_F32 / _16 take the two-pass
+ * path. */
 #define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 65536
 #define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 131072
 /* Widest row of attn_softmax_bwd held on chip (dy in registers, y in
@@ -351,8 +352,8 @@ ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t wor
  * up to LN_MAX_COLS_SOFTMAX_F32 (fp32) or LN_MAX_COLS_SOFTMAX_16 (fp16/bf16)
  * columns are held in registers (read once), and so are rows of up to
  * LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 / _16 columns on the vector path when mask
- * and y_dropped are NULL; wider rows, up to LN_MAX_COLS_STREAM, are read
- * twice: an online maximum/sum pass ([LLMC] §6.1), then the output pass.
+ * is NULL; wider rows, up to LN_MAX_COLS_STREAM, are read twice: an online
+ * maximum/sum pass ([LLMC] §6.1), then the output pass.
  */
 ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
                              void* y_dropped, int64_t rows, int64_t cols, float scale,

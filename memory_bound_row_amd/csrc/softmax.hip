@@ -286,7 +286,7 @@ __global__ __launch_bounds__(SmGeometry<G>::NT) void softmax_kernel(SmArgs a) {
 // the compiler keeps no per-slot masks or offsets across passes, and only the
 // lane's one partial slot tests elements.
 // DROP = false: a forward built without the dropped copy (a.out2 must be
-// NULL), whose Philox rounds would otherwise need registers beside the row.
+// NULL) and so without Philox code, a few registers leaner.
 template <class S, int G, int V, bool VEC, bool BWD, bool MASK, bool DROP = true>
 __global__ __launch_bounds__(G) void softmax_wide_kernel(SmArgs a) {
     constexpr int E = S::E, W = G * E, NW = G / 64;
@@ -426,6 +426,12 @@ __global__ __launch_bounds__(G) void softmax_wide_kernel(SmArgs a) {
             const rsrc_t vy = row_view<S>(a.out, row, 1, m);
             const rsrc_t vd = row_view<S>(a.out2 ? a.out2 : a.out, row, 1, m);
             const int rel = opaque(lim - base);
+            // (seed and threshold from opaque scalar copies per row, and each
+            // slot's column from an opaque lane index where it is used, so
+            // that neither is hoisted out of the row loop into registers
+            // held beside the row)
+            uint32_t slo = a.seed_lo, shi = a.seed_hi, thr = a.thr;
+            asm volatile("" : "+s"(slo), "+s"(shi), "+s"(thr));
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 float t[E], yv[E];
@@ -446,12 +452,12 @@ __global__ __launch_bounds__(G) void softmax_wide_kernel(SmArgs a) {
                 }
                 store(vy, i, yv);
                 if (DROP && a.out2) {
-                    const int col0 = i * W + base;
-                    const u32x4 w = dropout_words(row, col0, a.seed_lo, a.seed_hi, a.thr);
+                    const int col0 = i * W + opaque(tid) * E;
+                    const u32x4 w = dropout_words(row, col0, slo, shi, thr);
                     float dv[E];
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        dv[e] = kept<E>(w, col0, e, a.thr) ? t[e] * inv_kept : 0.0f;
+                        dv[e] = kept<E>(w, col0, e, thr) ? t[e] * inv_kept : 0.0f;
                     store(vd, i, dv);
                 }
             }
@@ -530,9 +536,8 @@ static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
     if constexpr (sm_wide_layout(G, V, St::E) || (!BWD && St::E == 8 && G == 512)) {
         if constexpr (!BWD) {
             if (a.mask) return launch_wide<G, V, VEC, BWD, true>(a, s);
-            // fp32 rows without a dropped copy: the instance without Philox,
-            // in fewer registers, so two 1024-lane rows share a compute unit
-            // (1024 x 6 fp32: 148 -> 139 us at 4096 x 24576; the 16-bit
+            // fp32 rows without a dropped copy: the instance without Philox
+            // code (1024 x 6 fp32: 148 -> 139 us at 4096 x 24576; the 16-bit
             // layouts up to 8 slots measured 1-3 % slower so)
             if constexpr (St::E == 4) {
                 if (!a.out2) return launch_wide<G, V, VEC, BWD, false, false>(a, s);
@@ -552,14 +557,16 @@ static hipError_t launch_one(const SmArgs& a, hipStream_t s) {
     }
 }
 
-// The forward without a mask row or a dropped copy holds one tensor and
-// needs no Philox rounds, so its rows fit 1024 lanes x up to 16 slots
-// (131072 16-bit / 65536 fp32 columns) packed in registers; past
-// LN_MAX_COLS_SOFTMAX_16 / _F32 such rows (vector path) take these layouts.
+// The forward without a mask row holds one tensor, so its rows fit 1024
+// lanes x up to 16 slots (131072 16-bit / 65536 fp32 columns) packed in
+// registers, with or without the dropped copy (whose Philox rounds run one
+// slot at a time in the output pass); past LN_MAX_COLS_SOFTMAX_16 / _F32
+// such rows (vector path) take these layouts.
 template <int V>
 static hipError_t launch_long_fwd(const SmArgs& a, hipStream_t s) {
-    if (a.mask || a.out2) return hipErrorInvalidValue;   // callers send such rows elsewhere
-    return launch_wide<1024, V, true, false, false, false>(a, s);
+    if (a.mask) return hipErrorInvalidValue;   // callers send masked rows elsewhere
+    return a.out2 ? launch_wide<1024, V, true, false, false, true>(a, s)
+                  : launch_wide<1024, V, true, false, false, false>(a, s);
 }
 
 // dy's packed slot with the elements that dropout dropped set to +0 (the

@@ -179,20 +179,21 @@ def test_keep_bits_every_layout(orc, kernel, dtype, scalar):
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f16", "bf16"])
 def test_keep_bits_long_rows(orc, dtype):
-    # rows past the register layouts: the softmax backward held on chip (more
-    # rows than workgroups, so each walks several; a full row of 1024 lanes x
-    # 16 slots, one slot short, and a shorter row), then the two-pass forward
-    # and backward (forced) on the same widths
+    # rows past the register layouts: the softmax forward and backward held on
+    # chip (more rows than workgroups, so each walks several; a full row of
+    # 1024 lanes x 16 slots, one slot short, and a shorter row), then the
+    # two-pass forward and backward (forced) on the same widths
     e = _elems(dtype)
     full = 65536 if dtype == torch.float32 else 131072
     shorter = 40000 if dtype == torch.float32 else 70000
     p = 0.25
     for rows, cols in ((2 * 256 + 3, full), (9, full - e), (9, shorter)):
         for seed in (5, 2 ** 63 + 5):
-            case(f"keep bits softmax_bwd on chip {dtype} {rows}x{cols} seed={seed}")
-            got = softmax_backward_bits(rows, cols, dtype, p, seed)
-            _assert_bits(got, orc.dropout_keep(seed, p, rows, cols),
-                         f"softmax_bwd on chip {dtype} {rows}x{cols} seed {seed}")
+            want = orc.dropout_keep(seed, p, rows, cols)
+            for kernel in ("softmax_fwd", "softmax_bwd"):
+                case(f"keep bits {kernel} on chip {dtype} {rows}x{cols} seed={seed}")
+                got = KERNELS[kernel](rows, cols, dtype, p, seed)
+                _assert_bits(got, want, f"{kernel} on chip {dtype} {rows}x{cols} seed {seed}")
     for kernel in ("softmax_fwd", "softmax_bwd"):
         for cols in (full - e, shorter):
             rows, seed = 9, 2 ** 63 + 5

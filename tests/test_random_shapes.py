@@ -194,9 +194,9 @@ def test_random_rows_held_on_chip(orc, idx):
     """Rows past the register layouts that one workgroup still holds on chip
     and reads once, on seeded random widths (rows of whole 16-byte slots):
     the cross-entropy in registers and LDS (up to 131072 fp32 / 262144 16-bit
-    classes), the softmax forward without a mask or dropped copy and its
-    backward with or without dropout (up to 65536 fp32 / 131072 16-bit
-    columns), causal or not."""
+    classes), the softmax forward without a mask and its backward, with or
+    without dropout (up to 65536 fp32 / 131072 16-bit columns), causal or
+    not."""
     g = np.random.default_rng([9100, idx])
     rows = int(g.integers(1, 40)) if idx % 3 else int(g.integers(257, 300))
     if idx % 2 == 0:
@@ -224,16 +224,17 @@ def test_random_rows_held_on_chip(orc, idx):
         p = float(g.choice([0.0, 0.1, 0.3]))
         seed = int(g.integers(0, 2 ** 63)) * 2 + 1
         case(f"random on-chip softmax {idx}: {rows}x{cols} {dtype} causal={causal} "
-             f"bwd p={p} seed={seed}")
+             f"p={p} seed={seed}")
         cpu = synth.layer_inputs(rows, cols, dtype, seed=9100 + idx, x_std=3.0,
                                  names=("x", "dy"))
         x, dy = cpu["x"].to("cuda"), cpu["dy"].to("cuda")
-        y, _ = mb.attn_softmax_fwd(x, 0.5, causal=causal)
+        y, yd = mb.attn_softmax_fwd(x, 0.5, causal=causal, p=p, seed=seed, want_dropped=p > 0)
         dx = mb.attn_softmax_bwd(dy, y, 0.5, causal=causal, p=p, seed=seed)
         torch.cuda.synchronize()
         fmt = FMT[dtype]
         if rows < 64:
-            check_softmax_fwd(orc, x, y, None, fmt, scale=0.5, causal=causal, name="rnd.oc_sm")
+            check_softmax_fwd(orc, x, y, yd, fmt, scale=0.5, causal=causal, p=p, seed=seed,
+                              name="rnd.oc_sm")
             check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, p=p, seed=seed,
                               name="rnd.oc_sm_bwd")
         else:

@@ -213,30 +213,35 @@ def test_in_place():
     assert torch.equal(y2, y) and torch.equal(dx2, dx)
 
 
-# 16-bit forwards without a mask row or a dropped copy stay in registers past
+# 16-bit forwards without a mask row stay in registers past
 # LN_MAX_COLS_SOFTMAX_16, up to LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 (1024 lanes x
-# 10, 12, 14 or 16 slots); backwards without dropout are held on chip (dy in
-# registers, y in registers and LDS) past LN_MAX_COLS_SOFTMAX_BWD_16, up to
-# LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16.
+# 10, 12, 14 or 16 slots), with or without the dropped copy; backwards are
+# held on chip (dy in registers, y in registers and LDS) past
+# LN_MAX_COLS_SOFTMAX_BWD_16, up to LN_MAX_COLS_SOFTMAX_PLAIN_BWD_16, with or
+# without dropout.
 PLAIN_FWD_MAX = 131072
 
 
+@pytest.mark.parametrize("p", [0.0, 0.1])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("cols", [65544, 81920, 98312, 114688, 120008, PLAIN_FWD_MAX])
-def test_plain_forward_long_rows(orc, dtype, cols):
-    case(f"softmax plain forward 6x{cols} {dtype} (registers), backward on chip")
-    d, y, yd, dx = run(6, cols, dtype, 0.5, False, 0.0, 0, data_seed=cols)
-    assert yd is None
-    check(orc, d, y, yd, dx, 0.5, False, 0.0, 0, name=f"sm.plain.{cols}")
+def test_plain_forward_long_rows(orc, dtype, cols, p):
+    seed = 2 ** 63 + cols
+    case(f"softmax plain forward 6x{cols} {dtype} p={p} (registers), backward on chip")
+    d, y, yd, dx = run(6, cols, dtype, 0.5, False, p, seed, data_seed=cols)
+    assert (yd is None) == (p == 0)
+    check(orc, d, y, yd, dx, 0.5, False, p, seed, name=f"sm.plain.{cols}")
 
 
+@pytest.mark.parametrize("p", [0.0, 0.1])
 @pytest.mark.parametrize("cols", [32772, 40960, 49152, 57344, 60004, 65536])
-def test_plain_long_rows_fp32(orc, cols):
+def test_plain_long_rows_fp32(orc, cols, p):
     # fp32 rows past LN_MAX_COLS_SOFTMAX_F32: forward in registers without a
-    # mask or dropped copy, backward on chip without dropout (up to 65536)
-    case(f"softmax plain fp32 6x{cols}: forward in registers, backward on chip")
-    d, y, yd, dx = run(6, cols, torch.float32, 0.5, False, 0.0, 0, data_seed=cols)
-    check(orc, d, y, yd, dx, 0.5, False, 0.0, 0, name=f"sm.plain32.{cols}")
+    # mask, backward on chip (up to 65536), with and without dropout
+    seed = 2 ** 63 + cols
+    case(f"softmax plain fp32 6x{cols} p={p}: forward in registers, backward on chip")
+    d, y, yd, dx = run(6, cols, torch.float32, 0.5, False, p, seed, data_seed=cols)
+    check(orc, d, y, yd, dx, 0.5, False, p, seed, name=f"sm.plain32.{cols}")
 
 
 def test_plain_forward_long_rows_many_per_workgroup_and_causal(orc):
@@ -276,8 +281,9 @@ def test_plain_forward_long_rows_many_per_workgroup_and_causal(orc):
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
-    # the same rows in registers and forced onto the two-pass walk; masked or
-    # dropped calls at this width take the two-pass path and are checked too
+    # the same rows in registers and forced onto the two-pass walk, without
+    # and with the dropped copy (also written over x); masked calls at this
+    # width take the two-pass path and are checked too
     cols = 110000
     case(f"softmax plain forward 8x{cols} {dtype}: registers, two-pass, mask, dropout")
     d = scores(8, cols, dtype, 33)
@@ -291,6 +297,13 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
                         generator=torch.Generator(device="cuda").manual_seed(34))).to(dtype)
     y3, _ = mb.attn_softmax_fwd(d["x"], 0.5, mask=mask, rows_per_mask=8)
     y4, yd4 = mb.attn_softmax_fwd(d["x"], 0.5, p=0.1, seed=35, want_dropped=True)
+    x6 = d["x"].clone()
+    y6, yd6 = mb.attn_softmax_fwd(x6, 0.5, p=0.1, seed=35, y_dropped=x6)
+    mb.debug_force_two_pass(True)
+    try:
+        y5, yd5 = mb.attn_softmax_fwd(d["x"], 0.5, p=0.1, seed=35, want_dropped=True)
+    finally:
+        mb.debug_force_two_pass(False)
     torch.cuda.synchronize()
     fmt = FMT[dtype]
     check_softmax_fwd(orc, d["x"], y, None, fmt, scale=0.5, name="sm.plain.reg")
@@ -299,6 +312,11 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
                       name="sm.plain.mask")
     check_softmax_fwd(orc, d["x"], y4, yd4, fmt, scale=0.5, p=0.1, seed=35,
                       name="sm.plain.drop")
+    check_softmax_fwd(orc, d["x"], y5, yd5, fmt, scale=0.5, p=0.1, seed=35,
+                      name="sm.plain.drop.2pass")
+    assert yd6.data_ptr() == x6.data_ptr()
+    assert torch.equal(y6.view(torch.int16), y4.view(torch.int16))
+    assert torch.equal(yd6.view(torch.int16), yd4.view(torch.int16))
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
