@@ -118,12 +118,12 @@ typedef enum {
  * workgroup per row beyond 16384). */
 #define LN_MAX_COLS_SOFTMAX_F32 32768
 #define LN_MAX_COLS_SOFTMAX_16 65536
-/* Widest row of attn_softmax_fwd still held in registers when the call has
- * no mask row (with or without the dropped copy) and its rows are on the
- * 16-byte vector path (x, y and y_dropped 16-byte aligned, cols * sizeof(T)
- * a multiple of 16): 65536 fp32 / 131072 fp16/bf16 scores (1024 lanes x 16
- * slots).  Other rows past LN_MAX_COLS_SOFTMAX_F32 / _16 take the two-pass
- * path. */
+/* Widest row of attn_softmax_fwd still held on chip (read once) when its
+ * rows are on the 16-byte vector path (x, mask, y and y_dropped 16-byte
+ * aligned, cols * sizeof(T) a multiple of 16), with or without a mask row and
+ * the dropped copy: 65536 fp32 / 131072 fp16/bf16 scores (1024 lanes x 16
+ * slots of scores in registers; a mask row in registers and LDS).  Other
+ * rows past LN_MAX_COLS_SOFTMAX_F32 / _16 take the two-pass path. */
 #define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 65536
 #define LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 131072
 /* Widest row of attn_softmax_bwd held on chip (dy in registers, y in
@@ -350,10 +350,11 @@ ln_status_t bias_dropout_residual_ln_bwd_fold(const float* workspace, size_t wor
  * scale must be finite; causal 0 or 1; p in [0, 1); rows_per_mask >= 1 when
  * mask is given.  Arithmetic in float32 (exp by the device's exp2).  Rows of
  * up to LN_MAX_COLS_SOFTMAX_F32 (fp32) or LN_MAX_COLS_SOFTMAX_16 (fp16/bf16)
- * columns are held in registers (read once), and so are rows of up to
- * LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 / _16 columns on the vector path when mask
- * is NULL; wider rows, up to LN_MAX_COLS_STREAM, are read twice: an online
- * maximum/sum pass ([LLMC] §6.1), then the output pass.
+ * columns are held in registers (read once), and rows of up to
+ * LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 / _16 columns on the vector path are held
+ * on chip (the scores in registers, a mask row in registers and LDS); wider
+ * rows, up to LN_MAX_COLS_STREAM, are read twice: an online maximum/sum pass
+ * ([LLMC] §6.1), then the output pass.
  */
 ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_mask, void* y,
                              void* y_dropped, int64_t rows, int64_t cols, float scale,

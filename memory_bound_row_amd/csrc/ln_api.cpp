@@ -44,6 +44,9 @@ hipError_t launch_xent_stream_bf16(bool, const XeArgs&, hipStream_t);
 hipError_t launch_softmax_long_fwd_f32(int, const SmArgs&, hipStream_t);
 hipError_t launch_softmax_long_fwd_f16(int, const SmArgs&, hipStream_t);
 hipError_t launch_softmax_long_fwd_bf16(int, const SmArgs&, hipStream_t);
+hipError_t launch_softmax_fwd_mask_lds_f32(const SmArgs&, hipStream_t);
+hipError_t launch_softmax_fwd_mask_lds_f16(const SmArgs&, hipStream_t);
+hipError_t launch_softmax_fwd_mask_lds_bf16(const SmArgs&, hipStream_t);
 hipError_t launch_softmax_bwd_lds_f32(const SmArgs&, hipStream_t);
 hipError_t launch_softmax_bwd_lds_f16(const SmArgs&, hipStream_t);
 hipError_t launch_softmax_bwd_lds_bf16(const SmArgs&, hipStream_t);
@@ -941,13 +944,18 @@ ln_status_t attn_softmax_fwd(const void* x, const void* mask, int64_t rows_per_m
     a.seed_lo = (uint32_t)(seed & 0xffffffffu);
     a.seed_hi = (uint32_t)(seed >> 32);
     if (cols > softmax_max_cols(dt, false) || force_two_pass()) {
-        // past the register layouts: a row without a mask row is still held
-        // in registers (vector path), with or without the dropped copy, up to
-        // LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 / _F32 columns; the rest take the
+        // past the register layouts: rows on the vector path are still held
+        // on chip, with or without the dropped copy, up to
+        // LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16 / _F32 columns (the scores in
+        // registers; a mask row in registers and LDS); the rest take the
         // two-pass walk
         const bool vec_ok = vec && !force_scalar();
         const int64_t plain_max =
             dt == LN_F32 ? LN_MAX_COLS_SOFTMAX_PLAIN_FWD_F32 : LN_MAX_COLS_SOFTMAX_PLAIN_FWD_16;
+        if (vec_ok && !force_two_pass() && mask && cols <= plain_max)
+            return from_hip(d == Dt::F32   ? launch_softmax_fwd_mask_lds_f32(a, stream)
+                            : d == Dt::F16 ? launch_softmax_fwd_mask_lds_f16(a, stream)
+                                           : launch_softmax_fwd_mask_lds_bf16(a, stream));
         if (vec_ok && !force_two_pass() && !mask && cols <= plain_max) {
             const int64_t per_lane = (a.nslots + 1023) / 1024;
             const int v = per_lane <= 10 ? 10 : per_lane <= 12 ? 12 : per_lane <= 14 ? 14 : 16;

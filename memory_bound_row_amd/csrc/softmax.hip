@@ -709,6 +709,186 @@ __global__ __launch_bounds__(1024) void softmax_bwd_lds_kernel(SmArgs a) {
     }
 }
 
+// Forward rows with an additive mask row past the register layouts, vector
+// path: one 1024-lane workgroup per row holds the scores (16 slots per lane
+// in registers) and the row's mask (its first kSfMReg slots in registers,
+// its last kSbYLds in LDS, loaded straight into LDS as in the backward
+// above), so scores and mask are each read once ("02 · llmc/ 的 CUDA kernel
+// 层" §3.1).  The arithmetic and its order are the register kernel's: score
+// = scale * x + mask, the row maximum and the sum of exp2(score log2(e) -
+// max log2(e)) per lane in slot order, one butterfly per wave, the waves in
+// order; y = e * (1 / sum), the dropped copy from the same per-slot Philox
+// words (DROP).  Keys out of play (past the row, or past the query of a
+// causal row) take no part and get y = 0, whatever the LDS cells hold.
+constexpr int kSfMReg = 7;   // mask slots in registers (the rest in LDS)
+static_assert(kSfMReg + kSbYLds == kSbSlots, "mask slots: registers, then LDS");
+template <class S, bool DROP>
+__global__ __launch_bounds__(1024) void softmax_fwd_mask_lds_kernel(SmArgs a) {
+    constexpr int E = S::E, G = 1024, V = kSbSlots, VM = kSfMReg, VL = kSbYLds, NW = G / 64;
+    constexpr int W = G * E;   // columns between consecutive slots of a lane
+    __shared__ __attribute__((aligned(16))) u32x4 stage[VL][G];
+    __shared__ float red[2][2][NW];   // [buffer][max, sum][wave]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = (int)a.m;
+    const int ns = (int)a.nslots;
+    auto slot_off = [&](int i, int nslot) {
+        const int t = opaque(tid);
+        return i * G + t < nslot ? (uint32_t)(t * 16 + i * G * 16) : kOob;
+    };
+    auto lds_slot = [&](int j) {
+        u32x4 v = stage[j][tid];
+        hold_packed(v);
+        return v;
+    };
+    auto reduce = [&](float v, int buf, int k) {
+        v = k == 0 ? group_max<64>(v) : group_sum<64>(v);
+        if (lane == 0) red[buf][k][wave] = v;
+        __syncthreads();
+        float r = red[buf][k][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = k == 0 ? fmaxf(r, red[buf][k][w]) : r + red[buf][k][w];
+        return r;
+    };
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const int buf = it & 1;
+        int mq = m;
+        asm volatile("" : "+s"(mq));
+        const int q = a.causal ? (int)(row % mq) : m - 1;   // last key in play
+        const int lim = q + 1 < m ? q + 1 : m;
+        const int nlive = (lim + E - 1) / E;
+        const rsrc_t vx = row_view<S>(a.x, row, 1, m);
+        // (both divisions set up per row from opaque scalar copies, not
+        // hoisted into a vector register kept beside the row)
+        int64_t rpm = a.rows_per_mask;
+        asm volatile("" : "+s"(rpm));
+        const rsrc_t vm = row_view<S>(a.mask, row / rpm, 1, m);
+        u32x4 xr[V], mr[VM];
+#pragma unroll
+        for (int i = 0; i < V; ++i) xr[i] = buf_load_nt(vx, slot_off(i, nlive));
+#pragma unroll
+        for (int i = 0; i < VM; ++i) mr[i] = buf_load(vm, slot_off(i, nlive));
+        // (the previous row's cells were consumed before its stores; the
+        // mask row, which rows_per_mask rows share, is read through the
+        // caches)
+#pragma unroll
+        for (int j = 0; j < VL; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vm, (__attribute__((address_space(3))) void*)&stage[j][64 * wave], 16,
+                (int)slot_off(VM + j, nlive), 0, 0, 0);
+        // score of slot i: scale * x + mask (the mask slot from registers or
+        // LDS, read only where it is used)
+        auto score = [&](int i, float (&t)[E]) {
+            const u32x4 m4 = i < VM ? mr[i < VM ? i : 0] : lds_slot(i < VM ? 0 : i - VM);
+            float xv[E], mv[E];
+            S::unpack(xr[i], xv);
+            S::unpack(m4, mv);
+#pragma unroll
+            for (int e = 0; e < E; ++e) t[e] = a.scale * xv[e] + mv[e];
+        };
+        // rel: columns in play from the lane's first; slot i is wholly in
+        // play iff i*W + E <= rel, partly iff i*W < rel, and takes no work
+        // otherwise (rows shorter than 16 slots per lane skip the rest)
+        int rel = opaque(lim - tid * E);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            if (i * W < rel) {
+                float t[E];
+                score(i, t);
+                if (i * W + E <= rel) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) mx = fmaxf(mx, t[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (i * W + e < rel) mx = fmaxf(mx, t[e]);
+                }
+            }
+        }
+        mx = reduce(mx, buf, 0);
+        const bool live_row = mx != -INFINITY;   // every key masked: y = 0
+        const float nm = live_row ? -mx * kLog2e : 0.0f;
+        keep_packed(xr);
+        keep_packed(mr);
+        rel = opaque(lim - tid * E);
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            if (i * W < rel) {
+                float t[E];
+                score(i, t);
+                if (i * W + E <= rel) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) z += exp2_(fmaf(t[e], kLog2e, nm));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (i * W + e < rel) z += exp2_(fmaf(t[e], kLog2e, nm));
+                }
+            }
+        }
+        z = reduce(z, buf, 1);
+        const float inv = live_row ? 1.0f / z : 0.0f;
+        const float inv_kept = inv * a.pscale;   // dropped copy: y / (1 - p)
+        keep_packed(xr);
+        keep_packed(mr);
+        // output pass: every slot of the row written (i*G < rs), keys out of
+        // play as 0
+        const rsrc_t vy = row_view<S>(a.out, row, 1, m);
+        const rsrc_t vd = row_view<S>(DROP ? a.out2 : a.out, row, 1, m);
+        rel = opaque(lim - tid * E);
+        const int rs = opaque(ns - tid);
+        uint32_t slo = a.seed_lo, shi = a.seed_hi, thr = a.thr;
+        asm volatile("" : "+s"(slo), "+s"(shi), "+s"(thr));
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            if (i * G < rs) {
+                float t[E], yv[E];
+                u32x4 w{};
+                int col0 = 0;
+                if constexpr (DROP) {
+                    col0 = (i * G + opaque(tid)) * E;
+                    w = dropout_words(row, col0, slo, shi, thr);
+                }
+                if (i * W < rel) {
+                    score(i, t);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        t[e] = exp2_(fmaf(t[e], kLog2e, nm));
+                        yv[e] = t[e] * inv;
+                    }
+                    if (!(i * W + E <= rel)) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            if (i * W + e >= rel) {
+                                t[e] = 0.0f;
+                                yv[e] = 0.0f;
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        t[e] = 0.0f;
+                        yv[e] = 0.0f;
+                    }
+                }
+                buf_store_nt(S::pack(yv), vy, slot_off(i, ns));
+                if constexpr (DROP) {
+                    float dv[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        dv[e] = kept<E>(w, col0, e, thr) ? t[e] * inv_kept : 0.0f;
+                    buf_store_nt(S::pack(dv), vd, slot_off(i, ns));
+                }
+            }
+        }
+    }
+}
+
 template <bool VEC, bool BWD>
 static hipError_t dispatch(const Path& p, const SmArgs& a, hipStream_t s) {
 #define MBROW_CASE(GG, VV) \
@@ -741,6 +921,20 @@ static hipError_t launch_bwd_lds(const SmArgs& a, hipStream_t s) {
 }
 hipError_t MBROW_CAT(launch_softmax_bwd_lds_, MBROW_SUFFIX)(const SmArgs& a, hipStream_t s) {
     return a.thr != 0u ? launch_bwd_lds<true>(a, s) : launch_bwd_lds<false>(a, s);
+}
+// the forward rows with a mask row held on chip, with or without the
+// dropped copy
+template <bool DROP>
+static hipError_t launch_fwd_mask_lds(const SmArgs& a, hipStream_t s) {
+    const void* k = reinterpret_cast<const void*>(&softmax_fwd_mask_lds_kernel<St, DROP>);
+    const int64_t grid = persistent_grid(k, 1024, a.rows);
+    hipLaunchKernelGGL((softmax_fwd_mask_lds_kernel<St, DROP>), dim3((unsigned)grid), dim3(1024),
+                       0, s, a);
+    return hipGetLastError();
+}
+hipError_t MBROW_CAT(launch_softmax_fwd_mask_lds_, MBROW_SUFFIX)(const SmArgs& a, hipStream_t s) {
+    if (!a.mask) return hipErrorInvalidValue;   // callers send unmasked rows elsewhere
+    return a.out2 ? launch_fwd_mask_lds<true>(a, s) : launch_fwd_mask_lds<false>(a, s);
 }
 // `v`: slots per lane (10, 12, 14 or 16)
 hipError_t MBROW_CAT(launch_softmax_long_fwd_, MBROW_SUFFIX)(int v, const SmArgs& a,

@@ -110,9 +110,12 @@ def prologue_backward_bits(rows, cols, dtype, p, seed):
     return keep
 
 
-def softmax_forward_bits(rows, cols, dtype, p, seed):
+def softmax_forward_bits(rows, cols, dtype, p, seed, masked=False):
+    # masked: one all-zero mask row for every row, so y is still 1/L
     x = torch.zeros((rows, cols), dtype=dtype, device="cuda")
-    y, yd = mb.attn_softmax_fwd(x, 1.0, p=p, seed=seed, want_dropped=True)
+    mask = torch.zeros((1, cols), dtype=dtype, device="cuda") if masked else None
+    y, yd = mb.attn_softmax_fwd(x, 1.0, mask=mask, rows_per_mask=rows, p=p, seed=seed,
+                                want_dropped=True)
     torch.cuda.synchronize()
     assert torch.all(y > 0)
     return yd != 0
@@ -190,9 +193,12 @@ def test_keep_bits_long_rows(orc, dtype):
     for rows, cols in ((2 * 256 + 3, full), (9, full - e), (9, shorter)):
         for seed in (5, 2 ** 63 + 5):
             want = orc.dropout_keep(seed, p, rows, cols)
-            for kernel in ("softmax_fwd", "softmax_bwd"):
+            for kernel in ("softmax_fwd", "softmax_fwd_masked", "softmax_bwd"):
                 case(f"keep bits {kernel} on chip {dtype} {rows}x{cols} seed={seed}")
-                got = KERNELS[kernel](rows, cols, dtype, p, seed)
+                if kernel == "softmax_fwd_masked":
+                    got = softmax_forward_bits(rows, cols, dtype, p, seed, masked=True)
+                else:
+                    got = KERNELS[kernel](rows, cols, dtype, p, seed)
                 _assert_bits(got, want, f"{kernel} on chip {dtype} {rows}x{cols} seed {seed}")
     for kernel in ("softmax_fwd", "softmax_bwd"):
         for cols in (full - e, shorter):

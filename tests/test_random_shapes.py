@@ -194,9 +194,9 @@ def test_random_rows_held_on_chip(orc, idx):
     """Rows past the register layouts that one workgroup still holds on chip
     and reads once, on seeded random widths (rows of whole 16-byte slots):
     the cross-entropy in registers and LDS (up to 131072 fp32 / 262144 16-bit
-    classes), the softmax forward without a mask and its backward, with or
-    without dropout (up to 65536 fp32 / 131072 16-bit columns), causal or
-    not."""
+    classes), the softmax forward, with or without a mask row, and its
+    backward, with or without dropout (up to 65536 fp32 / 131072 16-bit
+    columns), causal or not."""
     g = np.random.default_rng([9100, idx])
     rows = int(g.integers(1, 40)) if idx % 3 else int(g.integers(257, 300))
     if idx % 2 == 0:
@@ -223,17 +223,24 @@ def test_random_rows_held_on_chip(orc, idx):
         causal = bool(g.integers(0, 2))
         p = float(g.choice([0.0, 0.1, 0.3]))
         seed = int(g.integers(0, 2 ** 63)) * 2 + 1
+        rpm = int(g.integers(1, 5)) if rows < 64 and g.integers(0, 2) else 0   # 0: no mask
         case(f"random on-chip softmax {idx}: {rows}x{cols} {dtype} causal={causal} "
-             f"p={p} seed={seed}")
+             f"p={p} seed={seed} rows_per_mask={rpm}")
         cpu = synth.layer_inputs(rows, cols, dtype, seed=9100 + idx, x_std=3.0,
                                  names=("x", "dy"))
         x, dy = cpu["x"].to("cuda"), cpu["dy"].to("cuda")
-        y, yd = mb.attn_softmax_fwd(x, 0.5, causal=causal, p=p, seed=seed, want_dropped=p > 0)
+        mask = None
+        if rpm:
+            mask = cpu["dy"][:(rows + rpm - 1) // rpm].to("cuda").clone()
+            mask[:, ::7] = float("-inf")
+        y, yd = mb.attn_softmax_fwd(x, 0.5, mask=mask, rows_per_mask=max(rpm, 1), causal=causal,
+                                    p=p, seed=seed, want_dropped=p > 0)
         dx = mb.attn_softmax_bwd(dy, y, 0.5, causal=causal, p=p, seed=seed)
         torch.cuda.synchronize()
         fmt = FMT[dtype]
         if rows < 64:
-            check_softmax_fwd(orc, x, y, yd, fmt, scale=0.5, causal=causal, p=p, seed=seed,
+            check_softmax_fwd(orc, x, y, yd, fmt, scale=0.5, mask=mask,
+                              rows_per_mask=max(rpm, 1), causal=causal, p=p, seed=seed,
                               name="rnd.oc_sm")
             check_softmax_bwd(orc, dy, y, dx, fmt, scale=0.5, p=p, seed=seed,
                               name="rnd.oc_sm_bwd")

@@ -281,9 +281,8 @@ def test_plain_forward_long_rows_many_per_workgroup_and_causal(orc):
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
-    # the same rows in registers and forced onto the two-pass walk, without
-    # and with the dropped copy (also written over x); masked calls at this
-    # width take the two-pass path and are checked too
+    # the same rows on chip and forced onto the two-pass walk, without and
+    # with the dropped copy (also written over x) and with a mask row
     cols = 110000
     case(f"softmax plain forward 8x{cols} {dtype}: registers, two-pass, mask, dropout")
     d = scores(8, cols, dtype, 33)
@@ -297,6 +296,11 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
                         generator=torch.Generator(device="cuda").manual_seed(34))).to(dtype)
     y3, _ = mb.attn_softmax_fwd(d["x"], 0.5, mask=mask, rows_per_mask=8)
     y4, yd4 = mb.attn_softmax_fwd(d["x"], 0.5, p=0.1, seed=35, want_dropped=True)
+    mb.debug_force_two_pass(True)
+    try:
+        y3b, _ = mb.attn_softmax_fwd(d["x"], 0.5, mask=mask, rows_per_mask=8)
+    finally:
+        mb.debug_force_two_pass(False)
     x6 = d["x"].clone()
     y6, yd6 = mb.attn_softmax_fwd(x6, 0.5, p=0.1, seed=35, y_dropped=x6)
     mb.debug_force_two_pass(True)
@@ -310,6 +314,8 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
     check_softmax_fwd(orc, d["x"], y2, None, fmt, scale=0.5, name="sm.plain.2pass")
     check_softmax_fwd(orc, d["x"], y3, None, fmt, scale=0.5, mask=mask, rows_per_mask=8,
                       name="sm.plain.mask")
+    check_softmax_fwd(orc, d["x"], y3b, None, fmt, scale=0.5, mask=mask, rows_per_mask=8,
+                      name="sm.plain.mask.2pass")
     check_softmax_fwd(orc, d["x"], y4, yd4, fmt, scale=0.5, p=0.1, seed=35,
                       name="sm.plain.drop")
     check_softmax_fwd(orc, d["x"], y5, yd5, fmt, scale=0.5, p=0.1, seed=35,
@@ -317,6 +323,75 @@ def test_plain_forward_long_rows_agree_with_two_pass(orc, dtype):
     assert yd6.data_ptr() == x6.data_ptr()
     assert torch.equal(y6.view(torch.int16), y4.view(torch.int16))
     assert torch.equal(yd6.view(torch.int16), yd4.view(torch.int16))
+
+
+def _mask_rows(nmask, cols, dtype, seed, dead=()):
+    """Additive mask rows: N(0, 1), about a tenth of the keys -inf, and the
+    rows in `dead` -inf everywhere (their softmax rows are all 0)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    mask = torch.randn((nmask, cols), device="cuda", generator=g)
+    mask[torch.rand((nmask, cols), device="cuda", generator=g) < 0.1] = float("-inf")
+    for r in dead:
+        mask[r] = float("-inf")
+    return mask.to(dtype)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_masked_forward_long_rows_on_chip(orc, dtype, p):
+    # a mask row past the register layouts: the scores in registers, the mask
+    # row in registers and LDS; one and three rows per mask row (7 rows, so
+    # the last mask row serves one), a mask row that masks every key, the
+    # full width, one slot short and a shorter row
+    e = 4 if dtype == torch.float32 else 8
+    full = 65536 if dtype == torch.float32 else PLAIN_FWD_MAX
+    shorter = 40000 if dtype == torch.float32 else 70000
+    for cols in (full, full - e, shorter):
+        for rpm in (1, 3):
+            rows, seed = 7, 2 ** 63 + cols + rpm
+            case(f"softmax masked forward on chip 7x{cols} {dtype} rows_per_mask={rpm} p={p}")
+            d = scores(rows, cols, dtype, cols + rpm)
+            nmask = (rows + rpm - 1) // rpm
+            mask = _mask_rows(nmask, cols, dtype, cols + 7 * rpm, dead=(1,))
+            y, yd = mb.attn_softmax_fwd(d["x"], 0.5, mask=mask, rows_per_mask=rpm, p=p,
+                                        seed=seed, want_dropped=p > 0)
+            torch.cuda.synchronize()
+            check_softmax_fwd(orc, d["x"], y, yd, FMT[dtype], scale=0.5, mask=mask,
+                              rows_per_mask=rpm, p=p, seed=seed, name=f"sm.mask.{cols}.{rpm}")
+            dead = range(rpm, min(2 * rpm, rows))
+            assert torch.all(y[list(dead)] == 0)
+
+
+def test_masked_forward_long_rows_many_per_workgroup_and_causal(orc):
+    # more rows than workgroups (rows sampled, each with its own mask row
+    # spelled out for the oracle), then causal rows with a mask and the
+    # dropped copy, and the result written over x
+    rows, cols, rpm = 2 * 256 + 5, 100000, 16
+    case(f"softmax masked forward on chip {rows}x{cols} bf16, rows_per_mask={rpm}, sampled")
+    d = scores(rows, cols, torch.bfloat16, 41)
+    mask = _mask_rows((rows + rpm - 1) // rpm, cols, torch.bfloat16, 42, dead=(3,))
+    y, _ = mb.attn_softmax_fwd(d["x"], 0.25, mask=mask, rows_per_mask=rpm)
+    torch.cuda.synchronize()
+    ids = [0, 1, 47, 48, 255, 256, 511, rows - 1]
+    sel = torch.as_tensor(ids, device="cuda")
+    mrows = torch.as_tensor([r // rpm for r in ids], device="cuda")
+    check_softmax_fwd(orc, d["x"][sel], y[sel], None, FMT[torch.bfloat16], scale=0.25,
+                      mask=mask[mrows].contiguous(), rows_per_mask=1, name="sm.mask.rows")
+    assert torch.all(y[48:64] == 0)
+    case(f"softmax masked forward on chip, causal 40x{cols} fp16 with the dropped copy")
+    d = scores(40, cols, torch.float16, 43)
+    mask = _mask_rows(5, cols, torch.float16, 44)
+    x2 = d["x"].clone()
+    y, yd = mb.attn_softmax_fwd(d["x"], 0.5, mask=mask, rows_per_mask=8, causal=True, p=0.2,
+                                seed=45, want_dropped=True)
+    y2, _ = mb.attn_softmax_fwd(x2, 0.5, mask=mask, rows_per_mask=8, causal=True, p=0.2,
+                                seed=45, y=x2)
+    torch.cuda.synchronize()
+    check_softmax_fwd(orc, d["x"], y, yd, FMT[torch.float16], scale=0.5, mask=mask,
+                      rows_per_mask=8, causal=True, p=0.2, seed=45, name="sm.mask.causal")
+    assert torch.all(y[:, 64:] == 0) and torch.all(yd[:, 64:] == 0)
+    assert y2.data_ptr() == x2.data_ptr()
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
