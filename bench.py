@@ -380,7 +380,8 @@ def counter_sample() -> None:
     in registers and LDS, then forced onto the two-pass path), and the
     softmax over 2048 x 131072 fp16 (the forward in registers, without and
     with the dropped copy, and the backward without and with dropout,
-    p = 0.1, held on chip; then all four forced onto the two-pass path)."""
+    p = 0.1, held on chip; the forward with a mask row shared by 16 rows,
+    held on chip; then all five forced onto the two-pass path)."""
     import torch
     import memory_bound_row_amd as mb
     from memory_bound_row_amd import synth
@@ -430,6 +431,8 @@ def counter_sample() -> None:
     d = synth.layer_inputs(2048, 131072, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
     s, dy = d["x"].to(dev), d["dy"].to(dev)
     y, ds, yd = torch.empty_like(s), torch.empty_like(s), torch.empty_like(s)
+    mask = synth.layer_inputs(2048 // 16, 131072, torch.float16, seed=SEED + 1,
+                              names=("dy",))["dy"].to(dev)
     for two_pass in (False, True):
         mb.debug_force_two_pass(two_pass)
         for _ in range(3):
@@ -438,6 +441,8 @@ def counter_sample() -> None:
         for _ in range(3):
             mb.attn_softmax_fwd(s, 0.125, p=0.1, seed=SEED, y=y, y_dropped=yd)
             mb.attn_softmax_bwd(dy, y, 0.125, p=0.1, seed=SEED, dx=ds)
+        for _ in range(3):
+            mb.attn_softmax_fwd(s, 0.125, mask=mask, rows_per_mask=16, y=y)
         torch.cuda.synchronize()
     mb.debug_force_two_pass(False)
     print("counter sample: done", flush=True)
@@ -887,16 +892,21 @@ def configs_report(cpp_launch: bool = True) -> None:
     # softmax over long rows: the register layouts (32768 keys; also forced
     # onto the two-pass path, for comparison) and the two-pass path past them
     # (131072 keys)
-    def long_softmax(rows, L, label, two_pass=False, p=0.0):
+    def long_softmax(rows, L, label, two_pass=False, p=0.0, rows_per_mask=0):
         d = synth.layer_inputs(rows, L, torch.float16, seed=SEED, x_std=3.0, names=("x", "dy"))
         a = {"x": d["x"].to(dev), "dy": d["dy"].to(dev)}
         del d
+        a["mask"] = None
+        if rows_per_mask:
+            a["mask"] = synth.layer_inputs(rows // rows_per_mask, L, torch.float16, seed=SEED + 1,
+                                           names=("dy",))["dy"].to(dev)
         a["y"] = torch.empty_like(a["x"])
         a["dx"] = torch.empty_like(a["x"])
         a["yd"] = torch.empty_like(a["x"]) if p > 0 else None
 
         def lf(i):
-            mb.attn_softmax_fwd(a["x"], 0.125, p=p, seed=SEED, y=a["y"], y_dropped=a["yd"])
+            mb.attn_softmax_fwd(a["x"], 0.125, mask=a["mask"], rows_per_mask=max(rows_per_mask, 1),
+                                p=p, seed=SEED, y=a["y"], y_dropped=a["yd"])
 
         def lb(i):
             mb.attn_softmax_bwd(a["dy"], a["y"], 0.125, p=p, seed=SEED, dx=a["dx"])
@@ -914,9 +924,10 @@ def configs_report(cpp_launch: bool = True) -> None:
             mb.debug_force_two_pass(False)
         t = rows * L * 2
         nf = 3 if p > 0 else 2   # x read; y (and the dropped copy) written
+        fb = nf * t + (t // rows_per_mask if rows_per_mask else 0)   # and the mask rows
         emit({"workload": label, "rows": rows, "cols": L, "storage": "float16",
-              "dropout": p, "fwd_bytes": nf * t, "fwd_us": round(msf * 1e3, 3),
-              "fwd_GBps": round(nf * t / (msf * 1e-3) / 1e9, 1),
+              "dropout": p, "rows_per_mask": rows_per_mask or None, "fwd_bytes": fb,
+              "fwd_us": round(msf * 1e3, 3), "fwd_GBps": round(fb / (msf * 1e-3) / 1e9, 1),
               "bwd_bytes": 3 * t, "bwd_us": round(msb * 1e3, 3),
               "bwd_GBps": round(3 * t / (msb * 1e-3) / 1e9, 1)})
         del a
@@ -939,6 +950,12 @@ def configs_report(cpp_launch: bool = True) -> None:
     long_softmax(8 * 256, 131072,
                  "attention softmax fwd (y and the dropped copy) + bwd with dropout p = 0.1, "
                  "8x256 rows of 131072 keys, forced onto the two-pass path", two_pass=True, p=0.1)
+    long_softmax(8 * 256, 131072,
+                 "attention softmax fwd with a mask row per 16 rows + bwd, 8x256 rows of 131072 "
+                 "keys (both on chip)", rows_per_mask=16)
+    long_softmax(8 * 256, 131072,
+                 "attention softmax fwd with a mask row per 16 rows + bwd, 8x256 rows of 131072 "
+                 "keys, forced onto the two-pass path", two_pass=True, rows_per_mask=16)
 
     fwd_bwd(64, 768, torch.float32, 1, 1000,
             "LayerNorm forward + backward fp32 64x768 (launch-bound)")
