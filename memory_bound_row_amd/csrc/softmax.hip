@@ -23,6 +23,14 @@
 // pass).  The row is still read once and written once.  Being lean in
 // registers it also keeps more rows in flight per CU, which makes it the
 // faster forward for 16-bit rows of 512 lanes (16384 columns) as well.
+//
+// Past those widths, rows on the 16-byte vector path of up to 131072 16-bit
+// / 65536 fp32 columns are still held on chip by one 1024-lane workgroup and
+// read once: the forward without a mask row in registers (16 slots per
+// lane), the forward with a mask row with the mask in registers and LDS
+// (softmax_fwd_mask_lds_kernel), the backward with dy in registers and y in
+// registers and LDS (softmax_bwd_lds_kernel), each with or without dropout.
+// Wider rows take the two-pass walk (stream.hip).
 #include "ln_device.hpp"
 #include "ln_launch.hpp"
 #include "online_softmax.hpp"
